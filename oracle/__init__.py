@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for the Dion3 orthogonalization hot path.
+
+Test infrastructure only: imported by tests/, by the smoke check in
+__graft_entry__.py and by the CPU-baseline leg of bench.py, never by the
+product package.
+"""
+from .dion_oracle import (  # noqa: F401
+    DEFAULT_COEFFS,
+    coefficient_schedule,
+    gram_newton_schulz,
+    momentum_update,
+    orthogonalize,
+    orthogonalize_batch,
+    rel_frobenius,
+    restart_points,
+    row_keys,
+    rowsubset_step,
+    select_rows,
+    selected_count,
+)

@@ -1,0 +1,261 @@
+"""Oracle for the Dion3 orthogonalization hot path: plain, slow, fp64, CPU only.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check and
+the benchmark's CPU-baseline leg may import or run this module.  The product
+path (the HIP library and its Python binding) never imports it, and this module
+imports nothing from the product path.
+
+What it computes, and where the pages state it
+----------------------------------------------
+Pages: "Dion3: Full-Stack Orthogonal Updates" (arXiv abstract mirror), section
+Abstract; and the Chinese summary "Dion3：全栈正交更新", sections 方法 / 核心模块
+(method, core modules), 输入输出流程 (input/output flow), 核心洞察 (insights) and
+局限 (limitations).
+
+* The update rule picks a fraction of the momentum matrix's rows and
+  orthogonalizes only those; the other rows keep the raw momentum update
+  (Abstract; 核心模块, "Dion3 更新规则" bullet).
+* Orthogonalization is Newton-Schulz run on the Gram matrix of the momentum,
+  with restarts and a safety factor (Abstract; 核心模块, "Gram Newton-Schulz"
+  bullet; 局限, first bullet).
+* The flow is: update momentum, select rows, Gram Newton-Schulz, update weights
+  (输入输出流程).  The weight update is outside this path.
+
+The pages print no coefficients, normalization, restart schedule, safety
+formula, selection criterion or worked example.  The readings taken here are:
+
+  R1  Coefficients: the fixed quintic (3.4445, -4.7750, 2.0315) unless a
+      per-iteration list is given.
+  R2  Normalization: X0 = S / ||S||_F (Frobenius norm of the selected rows,
+      no epsilon); a zero matrix gives zero output rows.
+  R3  The Gram matrix is formed on the smaller side (m = min(k, C)); when the
+      selected block is tall it is transposed, processed, and transposed back.
+  R4  Safety factor s scales the polynomial's argument at every iteration:
+      f_s(x) = f(x / s), i.e. (a, b, c) -> (a/s, b/s^3, c/s^5).
+  R5  A restart after iteration k (never after the last) re-forms the Gram
+      matrix from the current iterate X_k = Q X and resets Q to I.
+  R6  Rows are ranked by squared L2 norm (fp64, from the exact stored values),
+      larger first, ties to the lower row index; k = ceil(row_frac * R),
+      clamped to [1, R]; selected rows are processed in ascending order.
+  R7  No output scaling (learning rate and shape factors belong to the
+      weight update).
+  R8  Error feedback / momentum: E is the persistent fp32 momentum buffer;
+      M_t = fl32(fl32(beta * E_{t-1}) + G_t) (two correctly rounded fp32
+      operations, heavy-ball form) and E_t = M_t; unselected rows of the
+      output carry M_t unchanged.
+
+Parity pins (in tests/): SVD closed form U f^K(Sigma) V^T, textbook polar
+factor via the cubic Newton-Schulz map, the NS band invariant, equivalence with
+plain (non-Gram) Newton-Schulz, invariances, exact rank-1 / orthonormal-row
+values, brute-force selection with ties, and bit-exact fp32 momentum.  Every
+function below is pinned by at least one of them.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# R1: the fixed quintic used by every workload unless a schedule is supplied.
+DEFAULT_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+# --------------------------------------------------------------------------
+# Hyperparameter expansion (readings R1, R4, R5)
+# --------------------------------------------------------------------------
+def coefficient_schedule(coeffs, n_iter: int, safety: float = 1.0):
+    """Per-iteration (a, b, c) with the safety factor folded in (R1, R4).
+
+    ``coeffs`` is either one triple (used at every iteration) or a list of
+    ``n_iter`` triples.  The safety factor rescales the polynomial's argument:
+    f_s(x) = a (x/s) + b (x/s)^3 + c (x/s)^5.
+    Pages: Dion3 summary, 核心模块 (safety factors named, no formula); 局限.
+    """
+    arr = np.asarray(coeffs, dtype=np.float64)
+    if arr.ndim == 1:
+        if arr.shape[0] != 3:
+            raise ValueError("a single coefficient set must have 3 entries")
+        arr = np.tile(arr, (n_iter, 1))
+    if arr.shape != (n_iter, 3):
+        raise ValueError(f"need 1 or {n_iter} coefficient triples, got {arr.shape}")
+    s = float(safety)
+    if not s > 0:
+        raise ValueError("safety must be > 0")
+    return [(float(a) / s, float(b) / s ** 3, float(c) / s ** 5) for a, b, c in arr]
+
+
+def restart_points(n_iter: int, restart_every: int = 0, restart_mask: int = 0):
+    """Iterations k (1-based) after which the Gram matrix is re-formed (R5).
+
+    A nonzero ``restart_mask`` wins: bit (k-1) set means restart after k.
+    Otherwise every ``restart_every``-th iteration restarts.  No restart is
+    ever taken after the last iteration.
+    Pages: Dion3 summary, 核心模块 (restart strategy) and 局限 (restart threshold).
+    """
+    if restart_mask:
+        pts = {k for k in range(1, n_iter + 1) if (restart_mask >> (k - 1)) & 1}
+    elif restart_every and restart_every > 0:
+        pts = set(range(restart_every, n_iter + 1, restart_every))
+    else:
+        pts = set()
+    return sorted(k for k in pts if k < n_iter)
+
+
+# --------------------------------------------------------------------------
+# Row selection (reading R6)
+# --------------------------------------------------------------------------
+def row_keys(M) -> np.ndarray:
+    """Squared L2 norm of every row, in fp64, from the exact stored values."""
+    A = np.asarray(M, dtype=np.float64)
+    return np.einsum("ij,ij->i", A, A)
+
+
+def selected_count(n_rows: int, row_frac: float) -> int:
+    """k = ceil(row_frac * R) clamped to [1, R] (R6).
+
+    The fraction arrives as a float; x = row_frac * R is shrunk by a relative
+    1e-6 before the ceiling so that the float rounding of a decimal fraction
+    (0.1f * 1000 = 100.0000015) does not add a row.
+    """
+    if not (0.0 < row_frac <= 1.0):
+        raise ValueError("row_frac must be in (0, 1]")
+    x = float(row_frac) * n_rows
+    k = int(math.ceil(x * (1.0 - 1e-6)))
+    return max(1, min(n_rows, k))
+
+
+def select_rows(M, row_frac: float) -> np.ndarray:
+    """Indices of the selected rows, ascending (R6).
+
+    The top-k rows by squared norm, larger first, ties to the lower index.
+    Pages: Dion3 abstract (select a fraction of the momentum rows);
+    Dion3 summary, 核心模块, "Dion3 更新规则" bullet (e.g. 1/8 of the rows).
+    """
+    R = np.asarray(M).shape[0]
+    k = selected_count(R, row_frac)
+    if k == R:
+        return np.arange(R, dtype=np.int64)
+    keys = row_keys(M)
+    # stable sort on (-key) keeps equal keys in ascending row order
+    order = np.argsort(-keys, kind="stable")
+    return np.sort(order[:k]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Gram Newton-Schulz (readings R2-R5)
+# --------------------------------------------------------------------------
+def gram_newton_schulz(X, coeff_list, restarts) -> np.ndarray:
+    """Gram Newton-Schulz on a wide, already normalized X (m <= n), fp64.
+
+    Plain Newton-Schulz steps X <- (a I + b A + c A^2) X with A = X X^T.  The
+    Gram form never updates X inside a segment: it keeps G (the Gram matrix of
+    the current iterate) and Q (the accumulated left factor, current iterate =
+    Q X), and uses that A_{k+1} = P A_k P because P is a polynomial in A_k.
+    A restart re-forms G from the current iterate and resets Q.
+    Pages: Dion3 summary, 核心模块, "Gram Newton-Schulz" bullet; 核心洞察, third
+    bullet (restarts and safety factors make the Gram form stable).
+    """
+    X = np.array(X, dtype=np.float64)
+    m = X.shape[0]
+    eye = np.eye(m)
+    G = X @ X.T
+    Q = eye.copy()
+    K = len(coeff_list)
+    restart_set = set(restarts)
+    for k in range(1, K + 1):
+        a, b, c = coeff_list[k - 1]
+        P = a * eye + b * G + c * (G @ G)
+        Q = P @ Q
+        if k == K:
+            break
+        if k in restart_set:
+            X = Q @ X
+            G = X @ X.T
+            Q = eye.copy()
+        else:
+            G = P @ G @ P
+    return Q @ X
+
+
+def orthogonalize(M, coeffs=DEFAULT_COEFFS, n_iter: int = 5, restart_every: int = 0,
+                  restart_mask: int = 0, safety: float = 1.0, row_frac: float = 1.0):
+    """One matrix of the hot path.  Returns (out fp64 R x C, idx int64[k]).
+
+    out[idx] is the orthogonalized selected block; the other rows are the
+    input rows unchanged (R6, R8).  Inputs are taken exactly as stored.
+    """
+    M64 = np.asarray(M, dtype=np.float64)
+    if M64.ndim != 2:
+        raise ValueError("M must be 2-D")
+    R, C = M64.shape
+    idx = select_rows(M64, row_frac)
+    S = M64[idx, :]
+    coeff_list = coefficient_schedule(coeffs, n_iter, safety)
+    restarts = restart_points(n_iter, restart_every, restart_mask)
+
+    tall = S.shape[0] > C                       # R3
+    X = S.T if tall else S
+    nu = math.sqrt(float(np.sum(X * X)))        # R2
+    if nu == 0.0:
+        O = np.zeros_like(X)
+    else:
+        O = gram_newton_schulz(X / nu, coeff_list, restarts)
+    if tall:
+        O = O.T
+    out = M64.copy()
+    out[idx, :] = O
+    return out, idx
+
+
+def orthogonalize_batch(Ms, **kw):
+    """The megabatch is just the list of independent per-matrix results."""
+    return [orthogonalize(M, **kw) for M in Ms]
+
+
+# --------------------------------------------------------------------------
+# Error feedback / momentum (reading R8)
+# --------------------------------------------------------------------------
+def momentum_update(E, G, beta: float) -> np.ndarray:
+    """M_t = fl32(fl32(beta * E) + G): two separately rounded fp32 operations.
+
+    ``E`` is the fp32 buffer, ``G`` the gradient (bf16 values held exactly in
+    fp32).  numpy float32 ufuncs are correctly rounded IEEE operations with no
+    contraction, so each line is one rounding.
+    Pages: Dion3 summary, 输入输出流程 (momentum update comes first) and
+    核心模块 ("配合误差反馈与有限精度处理": error feedback, finite precision).
+    """
+    E32 = np.asarray(E, dtype=np.float32)
+    G32 = np.asarray(G, dtype=np.float32)
+    b = np.float32(beta)
+    t = np.multiply(b, E32, dtype=np.float32)
+    return np.add(t, G32, dtype=np.float32)
+
+
+def rowsubset_step(Es, grads, beta: float, **kw):
+    """One step of the row-subset rule over a batch.
+
+    Returns (new E list (fp32), out list (fp64), idx list).  E_t = M_t, and
+    the output is orthogonalize(M_t) with unselected rows = M_t (R8).
+    """
+    newE, outs, idxs = [], [], []
+    for E, G in zip(Es, grads):
+        Mt = momentum_update(E, G, beta)
+        out, idx = orthogonalize(Mt, **kw)
+        newE.append(Mt)
+        outs.append(out)
+        idxs.append(idx)
+    return newE, outs, idxs
+
+
+# --------------------------------------------------------------------------
+# Error metric used by every parity gate
+# --------------------------------------------------------------------------
+def rel_frobenius(approx, exact) -> float:
+    """||approx - exact||_F / ||exact||_F (0 when both are zero)."""
+    A = np.asarray(approx, dtype=np.float64)
+    B = np.asarray(exact, dtype=np.float64)
+    den = float(np.linalg.norm(B))
+    num = float(np.linalg.norm(A - B))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den

@@ -1,0 +1,321 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test names what it pins.  None retypes the oracle's iteration: the
+references are the SVD closed form, a library polar factor, exact rational
+arithmetic, the plain (non-Gram) Newton-Schulz iteration, invariances, brute
+force and scalar IEEE emulation.
+"""
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+from oracle import dion_oracle as O
+from workloads import QUINTIC, fp32_64x128, heavytail_np, lowrank_np, round_bf16
+
+RNG = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- helpers
+def scalar_map(x, coeffs, n_iter, safety=1.0):
+    """The NS polynomial applied to a singular value: x <- f(x / s), K times."""
+    trip = np.tile(np.asarray(coeffs, float), (n_iter, 1)) if np.ndim(coeffs) == 1 else np.asarray(coeffs)
+    y = np.asarray(x, dtype=np.float64)
+    for a, b, c in trip:
+        t = y / safety
+        y = a * t + b * t ** 3 + c * t ** 5
+    return y
+
+
+def svd_closed_form(M, coeffs, n_iter, safety=1.0):
+    """U diag(f^K(sigma / ||M||_F)) V^T, the exact-arithmetic output of NS."""
+    M = np.asarray(M, dtype=np.float64)
+    U, s, Vt = np.linalg.svd(M, full_matrices=False)
+    nu = np.linalg.norm(M)
+    return (U * scalar_map(s / nu, coeffs, n_iter, safety)) @ Vt
+
+
+def exact_f(x: Fraction, coeffs, n_iter, safety=Fraction(1)) -> Fraction:
+    a, b, c = (Fraction(str(v)) for v in coeffs)
+    for _ in range(n_iter):
+        t = x / safety
+        x = a * t + b * t ** 3 + c * t ** 5
+    return x
+
+
+def f32(x: float) -> float:
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def rand_lowrank(R, C, rank, noise, rng=RNG):
+    return rng.standard_normal((R, rank)) @ rng.standard_normal((rank, C)) + noise * rng.standard_normal((R, C))
+
+
+# ------------------------------------------------- P6: exact scalar values
+def test_scalar_map_exact_values():
+    """f^5(1) for the fixed quintic, by exact rational arithmetic, matches the
+    value worked out independently (0.696436409469752), and the fp64 scalar
+    loop used by the SVD pin reproduces it."""
+    v = exact_f(Fraction(1), QUINTIC, 5)
+    assert abs(float(v) - 0.696436409469752) < 1e-14
+    assert abs(scalar_map(1.0, QUINTIC, 5) - float(v)) < 1e-13
+    v101 = exact_f(Fraction(1), QUINTIC, 5, Fraction("1.01"))
+    assert abs(float(v101) - 0.709030164453003) < 1e-14
+    v6 = exact_f(Fraction(1), QUINTIC, 6, Fraction("1.05"))
+    assert abs(float(v6) - 1.136014264217548) < 1e-14
+    v8 = exact_f(Fraction(1, 8), QUINTIC, 5)
+    assert abs(float(v8) - 0.688139855776055) < 1e-14
+
+
+def test_scalar_map_textbook_cubic_converges():
+    """Cubic NS (1.5, -0.5, 0) is the textbook polar iteration: from 0.1 it
+    reaches 1 to 1e-15 within 11 steps, and fixes 1 exactly."""
+    assert abs(float(exact_f(Fraction(1), (1.5, -0.5, 0.0), 7)) - 1.0) == 0.0
+    assert abs(scalar_map(0.1, (1.5, -0.5, 0.0), 11) - 1.0) < 1e-15
+
+
+# -------------------------------------------------- P1: SVD closed form
+@pytest.mark.parametrize("shape", [(64, 128), (128, 64), (48, 48), (7, 33), (33, 7), (1, 9), (9, 1)])
+@pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10),
+                                   dict(restart_every=1)])
+@pytest.mark.parametrize("ns", [(5, 1.0), (5, 1.01), (6, 1.05)])
+def test_svd_closed_form(shape, sched, ns):
+    n_iter, safety = ns
+    M = rand_lowrank(*shape, rank=min(4, *shape), noise=0.1)
+    out, idx = O.orthogonalize(M, n_iter=n_iter, safety=safety, **sched)
+    ref = svd_closed_form(M, QUINTIC, n_iter, safety)
+    assert list(idx) == list(range(shape[0]))
+    assert O.rel_frobenius(out, ref) < 1e-10
+
+
+def test_svd_closed_form_fp32_workload():
+    """The fp32 64x128 workload: oracle vs SVD closed form."""
+    M = fp32_64x128()
+    out, _ = O.orthogonalize(M, n_iter=5)
+    assert O.rel_frobenius(out, svd_closed_form(M, QUINTIC, 5)) < 1e-11
+
+
+def test_per_iteration_coefficients():
+    """A per-iteration schedule is applied in order (closed form per step)."""
+    sched = [(3.4445, -4.7750, 2.0315), (2.0, -1.5, 0.5), (1.5, -0.5, 0.0)]
+    M = rand_lowrank(20, 30, 3, 0.2)
+    out, _ = O.orthogonalize(M, coeffs=sched, n_iter=3, restart_every=1, safety=1.02)
+    assert O.rel_frobenius(out, svd_closed_form(M, sched, 3, 1.02)) < 1e-11
+    out_rev, _ = O.orthogonalize(M, coeffs=sched[::-1], n_iter=3, safety=1.02)
+    assert O.rel_frobenius(out_rev, out) > 1e-3
+
+
+# ------------------------------------------------ P2: textbook polar factor
+@pytest.mark.parametrize("shape", [(6, 10), (10, 6), (8, 8)])
+def test_polar_factor_cubic(shape):
+    """With the cubic (1.5, -0.5, 0) the iteration converges to the polar
+    factor; scipy's polar decomposition is the independent reference."""
+    R, C = shape
+    r = min(R, C)
+    U, _ = np.linalg.qr(RNG.standard_normal((R, r)))
+    V, _ = np.linalg.qr(RNG.standard_normal((C, r)))
+    s = np.linspace(0.2, 1.0, r)
+    M = (U * s) @ V.T          # normalized singular values in [0.1, 0.6]
+    out, _ = O.orthogonalize(M, coeffs=(1.5, -0.5, 0.0), n_iter=40, restart_every=3)
+    if R >= C:
+        Up, _ = scipy.linalg.polar(M, side="right")
+    else:
+        Up, _ = scipy.linalg.polar(M.T, side="right")
+        Up = Up.T
+    assert np.max(np.abs(out - Up)) < 1e-12
+
+
+# ------------------------------------------------------ P3: band invariant
+THR = {(5, 1.0): 1.505e-3, (5, 1.01): 1.582e-3, (5, 1.05): 1.922e-3,
+       (6, 1.0): 4.37e-4, (6, 1.01): 4.64e-4, (6, 1.05): 5.86e-4}
+
+
+@pytest.mark.parametrize("ns", sorted(THR))
+def test_band_invariant(ns):
+    """Output singular values never exceed 1.20237, and those whose
+    normalized input is above the capture threshold land in
+    [0.68183, 1.20237]."""
+    n_iter, safety = ns
+    for shape in [(40, 90), (90, 40)]:
+        r = min(shape)
+        U, _ = np.linalg.qr(RNG.standard_normal((shape[0], r)))
+        V, _ = np.linalg.qr(RNG.standard_normal((shape[1], r)))
+        s = np.geomspace(1e-5, 1.0, r)
+        M = (U * s) @ V.T
+        out, _ = O.orthogonalize(M, n_iter=n_iter, restart_every=2, safety=safety)
+        s0 = np.linalg.svd(M, compute_uv=False) / np.linalg.norm(M)
+        s1 = np.linalg.svd(out, compute_uv=False)
+        assert s1.max() <= 1.20237 + 1e-9
+        # singular values keep their order under the monotone-on-[0,1] map
+        captured = s1[s0 >= THR[ns]]
+        assert captured.size > 0
+        assert captured.min() >= 0.68183 - 1e-9 and captured.max() <= 1.20237 + 1e-9
+
+
+# -------------------------------------------- P4: Gram NS == plain NS
+def plain_ns(M, coeffs, n_iter, safety):
+    """Muon-style Newton-Schulz on the full matrix: X <- aX + (bA + cA^2)X."""
+    X = np.asarray(M, float)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    X = X / np.linalg.norm(X)
+    for _ in range(n_iter):
+        a, b, c = coeffs[0] / safety, coeffs[1] / safety ** 3, coeffs[2] / safety ** 5
+        A = X @ X.T
+        X = a * X + b * (A @ X) + c * (A @ (A @ X))
+    return X.T if tall else X
+
+
+@pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b101)])
+@pytest.mark.parametrize("shape", [(30, 70), (70, 30)])
+def test_gram_equals_plain_ns(sched, shape):
+    M = rand_lowrank(*shape, rank=5, noise=0.05)
+    out, _ = O.orthogonalize(M, n_iter=5, safety=1.01, **sched)
+    assert O.rel_frobenius(out, plain_ns(M, QUINTIC, 5, 1.01)) < 1e-12
+
+
+# ------------------------------------------------------- P5: invariances
+def test_invariances():
+    M = rand_lowrank(24, 40, 3, 0.1)
+    kw = dict(n_iter=5, restart_every=2)
+    base, _ = O.orthogonalize(M, **kw)
+    assert O.rel_frobenius(O.orthogonalize(7.3e-3 * M, **kw)[0], base) < 1e-12
+    assert O.rel_frobenius(O.orthogonalize(-M, **kw)[0], -base) < 1e-12
+    assert O.rel_frobenius(O.orthogonalize(M.T, **kw)[0], base.T) < 1e-12
+    U1, _ = np.linalg.qr(RNG.standard_normal((24, 24)))
+    V1, _ = np.linalg.qr(RNG.standard_normal((40, 40)))
+    rot, _ = O.orthogonalize(U1 @ M @ V1.T, **kw)
+    assert O.rel_frobenius(rot, U1 @ base @ V1.T) < 1e-11
+    perm = RNG.permutation(24)
+    assert O.rel_frobenius(O.orthogonalize(M[perm], **kw)[0], base[perm]) < 1e-12
+
+
+# ------------------------------------------- P6: special cases, exact values
+def test_rank_one_exact():
+    u = RNG.standard_normal(17)
+    v = RNG.standard_normal(29)
+    out, _ = O.orthogonalize(np.outer(u, v), n_iter=5, restart_every=2)
+    expect = 0.696436409469752 * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v))
+    assert np.max(np.abs(out - expect)) < 1e-13
+
+
+def test_orthonormal_rows_exact():
+    Q, _ = np.linalg.qr(RNG.standard_normal((200, 64)))
+    M = 3.0 * Q.T                            # 64 orthonormal rows, scaled
+    out, _ = O.orthogonalize(M, n_iter=5)
+    assert np.max(np.abs(out - 0.688139855776055 * Q.T)) < 1e-13
+
+
+def test_diagonal_worked_example():
+    """[[3,0,0],[0,4,0]]: nu = 5, singular values 0.6, 0.8 map separately."""
+    M = np.array([[3.0, 0, 0], [0, 4.0, 0]])
+    out, _ = O.orthogonalize(M, n_iter=5)
+    e6 = float(exact_f(Fraction(3, 5), QUINTIC, 5))
+    e8 = float(exact_f(Fraction(4, 5), QUINTIC, 5))
+    assert np.max(np.abs(out - np.array([[e6, 0, 0], [0, e8, 0]]))) < 1e-14
+
+
+def test_zero_matrix():
+    out, idx = O.orthogonalize(np.zeros((5, 7)), n_iter=5, row_frac=0.4)
+    assert np.all(out == 0) and list(idx) == [0, 1]
+
+
+# -------------------------------------------------- P7: row selection
+def brute_force_select(M, k):
+    keys = [sum(int(v) * int(v) for v in row) for row in np.asarray(M)]
+    order = sorted(range(len(keys)), key=lambda j: (-keys[j], j))
+    return sorted(order[:k])
+
+
+@pytest.mark.parametrize("R,C,frac", [(16, 5, 0.25), (37, 4, 0.5), (8, 3, 1 / 8), (40, 6, 1.0),
+                                      (9, 9, 1 / 9), (64, 2, 0.125), (12, 30, 0.75)])
+def test_selection_brute_force_with_ties(R, C, frac):
+    rng = np.random.default_rng(R * 100 + C)
+    M = rng.integers(-3, 4, size=(R, C)).astype(np.float64)
+    M[rng.integers(0, R, size=R // 3)] = 0.0           # zero rows
+    M[R // 2] = M[0]                                    # exact duplicates
+    M[R - 1] = M[1]
+    k = O.selected_count(R, frac)
+    assert list(O.select_rows(M, frac)) == brute_force_select(M, k)
+
+
+def test_selected_count():
+    assert O.selected_count(4096, 0.125) == 512
+    assert O.selected_count(14336, 0.125) == 1792
+    assert O.selected_count(28672, 0.25) == 7168
+    assert O.selected_count(1000, float(np.float32(0.1))) == 100
+    assert O.selected_count(7, 0.5) == 4
+    assert O.selected_count(5, 1e-6) == 1
+    assert O.selected_count(5, 1.0) == 5
+
+
+def test_rowsubset_output_structure():
+    """Unselected rows are copied; the selected block (tall here: 12 > 8
+    columns) equals the closed form of that block alone."""
+    M = rand_lowrank(24, 8, 2, 0.3)
+    out, idx = O.orthogonalize(M, n_iter=5, restart_every=2, row_frac=0.5)
+    keys = np.sum(M * M, axis=1)
+    assert set(idx) == set(np.argsort(-keys, kind="stable")[:12])
+    rest = np.setdiff1d(np.arange(24), idx)
+    assert np.array_equal(out[rest], M[rest])
+    assert O.rel_frobenius(out[idx], svd_closed_form(M[idx], QUINTIC, 5)) < 1e-11
+
+
+# ------------------------------------------- P8: fp32 momentum, bit exact
+def test_momentum_bit_exact_scalar_emulation():
+    rng = np.random.default_rng(7)
+    E = (rng.standard_normal(3000) * 10.0 ** rng.uniform(-40, 30, 3000)).astype(np.float32)
+    G = round_bf16((rng.standard_normal(3000) * 10.0 ** rng.uniform(-40, 30, 3000)).astype(np.float32))
+    E[:5] = [0.0, -0.0, 1.0, 1e-45, 3.4e38]
+    got = O.momentum_update(E, G, 0.95)
+    beta = f32(0.95)
+    for e, g, r in zip(E.tolist(), G.tolist(), got.tolist()):
+        want = f32(f32(beta * e) + g)      # each op exact in fp64, rounded once
+        assert struct.pack("f", want) == struct.pack("f", r)
+
+
+def test_momentum_is_not_fma():
+    """Two roundings differ from a fused multiply-add on some inputs."""
+    rng = np.random.default_rng(11)
+    E = rng.standard_normal(200000).astype(np.float32)
+    G = round_bf16(rng.standard_normal(200000).astype(np.float32))
+    got = O.momentum_update(E, G, 0.95)
+    fma = (np.float64(np.float32(0.95)) * E.astype(np.float64) + G.astype(np.float64)).astype(np.float32)
+    assert np.any(got != fma)
+
+
+def test_momentum_steps_recurrence():
+    """Two steps of the batch rule: E_t = M_t and out = orth(M_t)."""
+    E = [np.zeros((16, 24), np.float32)]
+    for t in range(2):
+        G = [round_bf16(lowrank_np((9, t), 16, 24, 2, 0.1))]
+        newE, outs, idxs = O.rowsubset_step(E, G, 0.95, n_iter=5, restart_every=2, row_frac=0.25)
+        Mt = O.momentum_update(E[0], G[0], 0.95)
+        assert np.array_equal(newE[0], Mt)
+        assert np.array_equal(outs[0][np.setdiff1d(np.arange(16), idxs[0])],
+                              Mt[np.setdiff1d(np.arange(16), idxs[0])].astype(np.float64))
+        E = newE
+
+
+# ------------------------------------------ workload shapes and sanity
+def test_heavytail_generator_spectrum():
+    M = heavytail_np((5, 0, 0), 60, 40)
+    s = np.linalg.svd(M.astype(np.float64), compute_uv=False)
+    assert np.allclose(s, np.arange(1, 41) ** -0.5, rtol=1e-5)
+
+
+def test_hyperparameter_expansion():
+    assert O.restart_points(5, restart_every=2) == [2, 4]
+    assert O.restart_points(6, restart_every=2) == [2, 4]
+    assert O.restart_points(5, restart_mask=0b10) == [2]
+    assert O.restart_points(5, restart_mask=0b10000) == []
+    assert O.restart_points(5) == []
+    sch = O.coefficient_schedule(QUINTIC, 2, 1.05)
+    assert sch[0] == (3.4445 / 1.05, -4.7750 / 1.05 ** 3, 2.0315 / 1.05 ** 5)
+    with pytest.raises(ValueError):
+        O.coefficient_schedule([QUINTIC, QUINTIC], 3)
+    assert math.isclose(O.rel_frobenius(np.ones(3), np.ones(3) * 2), 0.5)
