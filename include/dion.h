@@ -1,0 +1,169 @@
+/*
+ * dion.h -- C ABI of the MI355X (gfx950) Gram Newton-Schulz orthogonalization
+ * library: the orthogonalization of momentum matrices inside a Muon-style
+ * optimizer step, done the Dion3 way.
+ *
+ * What is computed, and where it is stated
+ *   "Dion3: Full-Stack Orthogonal Updates" (arXiv abstract): Gram
+ *   Newton-Schulz cuts the FLOPs of orthogonalization, symmetric kernels
+ *   exploit the symmetry of the Gram products, megabatching groups the
+ *   matrices, and the update rule orthogonalizes only a fraction of the
+ *   momentum matrix's rows each step.
+ *   "Dion3：全栈正交更新" (Chinese summary), section 方法 / 核心模块: the Gram
+ *   form with restarts and safety factors; upper-triangle-only symmetric GEMM
+ *   with a transpose epilogue and fused GEMM+add; the row rule (e.g. 1/8 of
+ *   the rows) where the other rows keep the raw momentum update, with error
+ *   feedback and finite-precision handling.  Section 输入输出流程: momentum
+ *   update, then row selection, then Gram Newton-Schulz, then the weight
+ *   update (the weight update is not part of this library).
+ *
+ * Per matrix M (R x C, row-major, densely packed), with k = ceil(row_frac*R)
+ * (clamped to [1, R]; x = row_frac*R is shrunk by a relative 1e-6 first):
+ *   1. rows are ranked by squared L2 norm (fp64 from the stored values),
+ *      larger first, ties to the lower row index; the top k are selected and
+ *      kept in ascending row order (all rows when row_frac = 1);
+ *   2. S = M[selected]; if S is tall (k > C) it is transposed so that the
+ *      Gram matrix is formed on the smaller side m = min(k, C);
+ *   3. X = S / ||S||_F (a zero S gives zero output rows);
+ *   4. K iterations of X <- (a I + b A + c A^2) X with A = X X^T, run in Gram
+ *      form on G = X X^T and the accumulated factor Q; the safety factor s
+ *      rescales the argument at every iteration, (a, b, c) -> (a/s, b/s^3,
+ *      c/s^5); a restart after iteration k (never after the last) re-forms G
+ *      from the current iterate and resets Q;
+ *   5. out[selected] = the result (transposed back if tall),
+ *      out[other rows] = M[other rows], cast to the output dtype
+ *      (round to nearest even for bf16).  No learning-rate or shape scaling.
+ *
+ * Conventions for every entry point
+ *   - Matrix arguments are HOST arrays of `batch` DEVICE pointers.  Every
+ *     device buffer is owned by the caller.  The library allocates no device
+ *     memory and keeps no device state between calls: all scratch lives in
+ *     the caller's `workspace` (device memory, at least
+ *     dion_workspace_size() bytes, 256-byte aligned).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work on it and return without synchronizing; host arrays are only read
+ *     during the call.  Two calls must not share a workspace concurrently.
+ *   - Errors are detected on the host before any launch and returned as a
+ *     negative dion_status; dion_last_error() gives a message for the calling
+ *     thread.  NaN/Inf inputs are not checked: the output is unspecified.
+ */
+#ifndef DION_H
+#define DION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DION_OK = 0,
+  DION_E_INVAL = -1,        /* bad argument (shape, count, fraction, aliasing ...) */
+  DION_E_UNSUPPORTED = -2,  /* valid but not implemented combination */
+  DION_E_WORKSPACE = -3,    /* workspace NULL, too small or misaligned */
+  DION_E_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} dion_status;
+
+/* Storage dtype of the momentum / gradient / output matrices. */
+typedef enum { DION_BF16 = 0, DION_FP32 = 1 } dion_dtype;
+
+/* Arithmetic of the iteration.
+ *   DION_PREC_MFMA16: fp16 MFMA with fp32 accumulation; operands carry
+ *     power-of-two scales, and every product whose rounding the iteration
+ *     amplifies uses a two-term (hi + lo) fp16 split.  Relative Frobenius
+ *     error against the exact result: a few 1e-3 on low-rank-plus-noise
+ *     momentum (gate 2e-2).
+ *   DION_PREC_FP64: fp64 arithmetic throughout (error ~1e-12; gate 1e-4).
+ *   DION_PREC_AUTO: FP64 for DION_FP32 inputs of dion_orth_batched, MFMA16
+ *     otherwise. */
+typedef enum { DION_PREC_AUTO = 0, DION_PREC_MFMA16 = 1, DION_PREC_FP64 = 2 } dion_precision;
+
+typedef struct {
+  int32_t rows;
+  int32_t cols;
+} dion_shape;
+
+/* Hyper-parameters of the orthogonalization (shared by the whole batch).
+ *   ns_coeffs     host array of n_coeff_sets * 3 floats (a, b, c); NULL means
+ *                 the fixed quintic (3.4445, -4.7750, 2.0315)
+ *   n_coeff_sets  1 (same triple every iteration) or n_iter
+ *   n_iter        K >= 1 (at most 64)
+ *   restart_every restart after every restart_every-th iteration (0 = none)
+ *   restart_mask  if nonzero, bit (k-1) set = restart after iteration k;
+ *                 overrides restart_every.  Never applied after iteration K.
+ *   safety        s > 0
+ *   row_frac      in (0, 1]
+ *   precision     a dion_precision value */
+typedef struct {
+  const float* ns_coeffs;
+  int32_t n_coeff_sets;
+  int32_t n_iter;
+  int32_t restart_every;
+  uint32_t restart_mask;
+  float safety;
+  float row_frac;
+  int32_t precision;
+} dion_ns_params;
+
+/* Bytes of device workspace needed by dion_orth_batched for this batch
+ * (pure function of its arguments; 0 on invalid arguments).  For
+ * dion_rowsubset_step pass dtype = DION_FP32 and precision MFMA16 or AUTO. */
+size_t dion_workspace_size(const dion_shape* shapes, int32_t batch, int32_t dtype,
+                           const dion_ns_params* p);
+
+/* Orthogonalize a batch of momentum matrices in one megabatched pass.
+ *   M[i]     device, R_i x C_i of `dtype`, read only
+ *   out[i]   device, R_i x C_i of `dtype`, must not overlap any M[j]
+ *   sel_idx  optional device int32 buffer of sum_i k_i entries: receives each
+ *            matrix's selected rows (ascending), matrices in batch order
+ * Pages: Dion3 abstract (Gram Newton-Schulz, symmetric kernels, megabatching,
+ * row fraction); Dion3 summary, 方法 / 核心模块. */
+int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* shapes,
+                      int32_t batch, int32_t dtype, const dion_ns_params* p,
+                      int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same operation with a flat parameter list: one coefficient triple (NULL =
+ * the fixed quintic), restarts every restart_every iterations, AUTO precision. */
+int dion_orth_batched_simple(const void* const* M, void* const* out, const dion_shape* shapes,
+                             int32_t batch, int32_t dtype, const float* ns_coeffs,
+                             int32_t n_iter, int32_t restart_every, float safety,
+                             float row_frac, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* One step of the row-subset rule with its fp32 momentum / error-feedback
+ * buffer (Dion3 summary, 核心模块 "Dion3 更新规则" bullet and 输入输出流程):
+ *   E[i]     device fp32 R x C, updated in place:
+ *            E <- fl32(fl32(beta * E) + grad), two separately rounded fp32
+ *            operations (no fused multiply-add)
+ *   grad[i]  device R x C of grad_dtype (bf16 or fp32), read only
+ *   out[i]   device bf16 R x C: the orthogonalized selected rows of the new E,
+ *            the raw new E (rounded to bf16) in the other rows
+ *   p        as above; p->precision must be AUTO or MFMA16
+ * Workspace: dion_workspace_size(shapes, batch, DION_FP32, p). */
+int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* out,
+                        const dion_shape* shapes, int32_t batch, int32_t grad_dtype, float beta,
+                        const dion_ns_params* p, int32_t* sel_idx, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Useful floating-point operations of one dion_orth_batched call on this
+ * batch, in the executed formulation, symmetric products counted once:
+ * per matrix and restart segment of length L,
+ *   n*m*(m+1) [Gram] + 2*m*m*n [apply] + (4L-3)*m*m*(m+1) [m x m chain]. */
+double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_params* p);
+
+/* Rows selected from a matrix of `rows` rows: ceil(row_frac * rows) with the
+ * 1e-6 relative shrink described above, clamped to [1, rows]; 0 if invalid. */
+int32_t dion_selected_rows(int32_t rows, float row_frac);
+
+/* Static message for a status code. */
+const char* dion_strerror(int status);
+/* Message describing the last error on the calling thread ("" if none). */
+const char* dion_last_error(void);
+/* ABI version (major * 100 + minor). */
+int dion_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DION_H */

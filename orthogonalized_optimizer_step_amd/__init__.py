@@ -1,0 +1,168 @@
+"""MI355X-native Gram Newton-Schulz orthogonalization (Dion3 hot path).
+
+Thin Python binding over the C ABI in include/dion.h.  Every step of the
+path runs in the HIP kernels of libdion.so; this module only marshals
+pointers, shapes and parameters, and uses PyTorch for device memory and the
+current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import DION_BF16, DION_FP32, PREC, DionError, DionParams, DionShape, check, lib
+
+__all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
+           "DionError", "QUINTIC"]
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision):
+    flat = [float(x) for trip in ([coeffs] if len(coeffs) == 3 and not hasattr(coeffs[0], "__len__")
+                                  else coeffs) for x in trip]
+    arr = (ctypes.c_float * len(flat))(*flat)
+    p = DionParams(ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), len(flat) // 3, int(n_iter),
+                   int(restart_every), int(restart_mask), float(safety), float(row_frac),
+                   PREC[precision] if isinstance(precision, str) else int(precision))
+    return p, arr
+
+
+def _shapes(shapes):
+    arr = (DionShape * len(shapes))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i].rows, arr[i].cols = int(r), int(c)
+    return arr
+
+
+def _dtype_code(dt):
+    import torch
+    if dt == torch.bfloat16:
+        return DION_BF16
+    if dt == torch.float32:
+        return DION_FP32
+    raise DionError(-1, f"unsupported dtype {dt}")
+
+
+def _ptrs(tensors):
+    return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+
+
+def _check_tensors(ts, dtype=None):
+    for t in ts:
+        if t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise DionError(-1, "matrices must be 2-D, contiguous, on the GPU")
+        if dtype is not None and t.dtype != dtype:
+            raise DionError(-1, f"expected {dtype}, got {t.dtype}")
+
+
+def workspace_size(shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
+                   safety=1.0, row_frac=1.0, precision="auto") -> int:
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision)
+    code = DION_BF16 if dtype in ("bf16", DION_BF16) else DION_FP32
+    n = lib.dion_workspace_size(_shapes(shapes), len(shapes), code, ctypes.byref(p))
+    if n == 0:
+        raise DionError(-1, lib.dion_last_error().decode())
+    return int(n)
+
+
+def useful_flops(shapes, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
+                 row_frac=1.0) -> float:
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, "auto")
+    return float(lib.dion_useful_flops(_shapes(shapes), len(shapes), ctypes.byref(p)))
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-workspace.data_ptr()) % 256
+    if workspace.numel() - off < nbytes:
+        raise DionError(-3, f"workspace too small: need {nbytes} bytes")
+    return workspace, workspace.data_ptr() + off, workspace.numel() - off
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Orthogonalizer:
+    """A reusable megabatch: fixed shapes, dtype and hyper-parameters, with
+    its own workspace, so repeated calls only marshal pointers."""
+
+    def __init__(self, shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
+                 safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False):
+        import torch
+        self.shapes = [tuple(int(x) for x in s) for s in shapes]
+        self.dtype = dtype
+        self.step_mode = step_mode
+        self._p, self._keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision)
+        self._shp = _shapes(self.shapes)
+        code = DION_FP32 if (step_mode or dtype == "fp32") else DION_BF16
+        self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
+        if self.ws_bytes == 0:
+            raise DionError(-1, lib.dion_last_error().decode())
+        self._ws_tensor, self._ws, self._ws_len = _workspace(self.ws_bytes, device, None)
+        self.selected = [int(lib.dion_selected_rows(r, ctypes.c_float(float(row_frac)))) for r, _ in self.shapes]
+        self.total_selected = sum(self.selected)
+
+    def useful_flops(self):
+        return float(lib.dion_useful_flops(self._shp, len(self.shapes), ctypes.byref(self._p)))
+
+    def __call__(self, Ms, outs, sel_idx=None, stream=None):
+        code = _dtype_code(Ms[0].dtype)
+        rc = lib.dion_orth_batched(_ptrs(Ms), _ptrs(outs), self._shp, len(self.shapes), code, ctypes.byref(self._p),
+                                   ctypes.c_void_p(sel_idx.data_ptr() if sel_idx is not None else None),
+                                   ctypes.c_void_p(self._ws), self._ws_len, _stream(stream))
+        check(rc)
+        return outs
+
+    def step(self, Es, grads, outs, beta, sel_idx=None, stream=None):
+        code = _dtype_code(grads[0].dtype)
+        rc = lib.dion_rowsubset_step(_ptrs(Es), _ptrs(grads), _ptrs(outs), self._shp, len(self.shapes), code,
+                                     float(beta), ctypes.byref(self._p),
+                                     ctypes.c_void_p(sel_idx.data_ptr() if sel_idx is not None else None),
+                                     ctypes.c_void_p(self._ws), self._ws_len, _stream(stream))
+        check(rc)
+        return outs
+
+
+def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
+                 row_frac=1.0, precision="auto", return_indices=False, stream=None):
+    """Orthogonalize a list of 2-D bf16 or fp32 CUDA tensors in one megabatched call.
+
+    Returns the list of outputs (same shapes and dtype), and with
+    ``return_indices`` also the per-matrix selected rows (int32, ascending).
+    """
+    import torch
+    _check_tensors(Ms, Ms[0].dtype)
+    dt = "bf16" if Ms[0].dtype == torch.bfloat16 else "fp32"
+    orth = Orthogonalizer([tuple(M.shape) for M in Ms], dt, coeffs, n_iter, restart_every, restart_mask,
+                          safety, row_frac, precision, device=Ms[0].device)
+    if outs is None:
+        outs = [torch.empty_like(M) for M in Ms]
+    _check_tensors(outs, Ms[0].dtype)
+    sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Ms[0].device) if return_indices else None
+    orth(Ms, outs, sel, stream)
+    if not return_indices:
+        return outs
+    return outs, list(torch.split(sel, orth.selected))
+
+
+def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
+                   safety=1.0, row_frac=0.125, return_indices=False, stream=None):
+    """One row-subset step: E <- fl32(fl32(beta E) + grad) in place; returns bf16 outputs."""
+    import torch
+    _check_tensors(Es, torch.float32)
+    _check_tensors(grads, grads[0].dtype)
+    orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
+                          safety, row_frac, "mfma16", device=Es[0].device, step_mode=True)
+    if outs is None:
+        outs = [torch.empty(E.shape, dtype=torch.bfloat16, device=E.device) for E in Es]
+    _check_tensors(outs, torch.bfloat16)
+    sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
+    orth.step(Es, grads, outs, beta, sel, stream)
+    if not return_indices:
+        return outs
+    return outs, list(torch.split(sel, orth.selected))

@@ -1,0 +1,85 @@
+"""ctypes loader for libdion.so (the HIP library built in-tree by build.py).
+
+There is no fallback: if the library is missing or fails to load, importing
+the package raises, so nothing can silently run elsewhere.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdion.so")
+
+DION_BF16, DION_FP32 = 0, 1
+PREC = {"auto": 0, "mfma16": 1, "fp64": 2}
+
+
+class DionShape(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class DionParams(ctypes.Structure):
+    _fields_ = [
+        ("ns_coeffs", ctypes.POINTER(ctypes.c_float)),
+        ("n_coeff_sets", ctypes.c_int32),
+        ("n_iter", ctypes.c_int32),
+        ("restart_every", ctypes.c_int32),
+        ("restart_mask", ctypes.c_uint32),
+        ("safety", ctypes.c_float),
+        ("row_frac", ctypes.c_float),
+        ("precision", ctypes.c_int32),
+    ]
+
+
+# every symbol declared in include/dion.h
+EXPORTS = (
+    "dion_workspace_size", "dion_orth_batched", "dion_orth_batched_simple",
+    "dion_rowsubset_step", "dion_useful_flops", "dion_selected_rows", "dion_strerror",
+    "dion_last_error", "dion_version",
+)
+
+
+class DionError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dion error {code}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m orthogonalized_optimizer_step_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    shp = ctypes.POINTER(DionShape)
+    prm = ctypes.POINTER(DionParams)
+    lib.dion_workspace_size.argtypes = [shp, i32, i32, prm]
+    lib.dion_workspace_size.restype = sz
+    lib.dion_orth_batched.argtypes = [pp, pp, shp, i32, i32, prm, vp, vp, sz, vp]
+    lib.dion_orth_batched.restype = ctypes.c_int
+    lib.dion_orth_batched_simple.argtypes = [pp, pp, shp, i32, i32, ctypes.POINTER(ctypes.c_float), i32, i32,
+                                             ctypes.c_float, ctypes.c_float, vp, sz, vp]
+    lib.dion_orth_batched_simple.restype = ctypes.c_int
+    lib.dion_rowsubset_step.argtypes = [pp, pp, pp, shp, i32, i32, ctypes.c_float, prm, vp, vp, sz, vp]
+    lib.dion_rowsubset_step.restype = ctypes.c_int
+    lib.dion_useful_flops.argtypes = [shp, i32, prm]
+    lib.dion_useful_flops.restype = ctypes.c_double
+    lib.dion_selected_rows.argtypes = [i32, ctypes.c_float]
+    lib.dion_selected_rows.restype = i32
+    lib.dion_strerror.argtypes = [ctypes.c_int]
+    lib.dion_strerror.restype = ctypes.c_char_p
+    lib.dion_last_error.argtypes = []
+    lib.dion_last_error.restype = ctypes.c_char_p
+    lib.dion_version.argtypes = []
+    lib.dion_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def check(rc: int):
+    if rc != 0:
+        raise DionError(rc, f"{lib.dion_strerror(rc).decode()}: {lib.dion_last_error().decode()}")

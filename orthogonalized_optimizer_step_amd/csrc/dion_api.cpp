@@ -1,0 +1,726 @@
+// Host side of the library: argument validation, the megabatch plan
+// (workspace layout, per-phase tile tables, operand scales) and the phase
+// sequence of Gram Newton-Schulz, then the C ABI declared in include/dion.h.
+//
+// The phase sequence follows the Gram form of Newton-Schulz described in the
+// Dion3 summary (方法 / 核心模块, "Gram Newton-Schulz" bullet): G = X X^T,
+// then per iteration P = aI + bG + cG^2, Q <- P Q, and either G <- P G P or,
+// at a restart, X <- Q X, G <- X X^T, Q <- I; finally out = Q X.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <functional>
+#include <string>
+#include <vector>
+
+#include "../../include/dion.h"
+#include "dion_internal.h"
+
+namespace dion {
+// launchers (gemm_kernels.hip, stream_kernels.hip)
+bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa,
+                   hipStream_t stream);
+bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream);
+void launch_rowkeys(bool bf16, const MatDesc* descs, int nmat, int64_t rows, double* keys, hipStream_t s);
+void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
+                          double* keys, hipStream_t s);
+void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,
+                   MatScalars* scalars, bool fp64_path, hipStream_t s);
+void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
+                 const int* idx, const MatScalars* scalars, int xterms, bool use_idx, hipStream_t s);
+void launch_transpose(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
+                      int src_slot, int dst_slot, hipStream_t s);
+void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
+                            hipStream_t s);
+}  // namespace dion
+
+using namespace dion;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
+constexpr int kMaxIter = 64;
+
+// ------------------------------------------------------------ parameters
+struct Params {
+  std::vector<double> a, b, c;  // per iteration, safety folded in
+  std::vector<int> restart;     // restart[k-1] = 1: restart after iteration k
+  double row_frac;
+  bool fp64;
+};
+
+int parse_params(const dion_ns_params* p, int dtype, bool step_mode, Params& out) {
+  if (!p) return fail(DION_E_INVAL, "params is NULL");
+  if (dtype != DION_BF16 && dtype != DION_FP32) return fail(DION_E_INVAL, "unknown dtype");
+  if (p->n_iter < 1 || p->n_iter > kMaxIter) return fail(DION_E_INVAL, "n_iter must be in [1, 64]");
+  const int K = p->n_iter;
+  const float* co = p->ns_coeffs ? p->ns_coeffs : kQuintic;
+  const int sets = p->ns_coeffs ? p->n_coeff_sets : 1;
+  if (sets != 1 && sets != K) return fail(DION_E_INVAL, "n_coeff_sets must be 1 or n_iter");
+  if (!(p->safety > 0.f) || !std::isfinite(p->safety)) return fail(DION_E_INVAL, "safety must be finite and > 0");
+  if (!(p->row_frac > 0.f && p->row_frac <= 1.f)) return fail(DION_E_INVAL, "row_frac must be in (0, 1]");
+  if (p->restart_every < 0) return fail(DION_E_INVAL, "restart_every must be >= 0");
+  if (p->precision < DION_PREC_AUTO || p->precision > DION_PREC_FP64) return fail(DION_E_INVAL, "unknown precision");
+  if (step_mode && p->precision == DION_PREC_FP64)
+    return fail(DION_E_UNSUPPORTED, "the row-subset step runs on the MFMA16 path only");
+  out.a.resize(K);
+  out.b.resize(K);
+  out.c.resize(K);
+  out.restart.assign(K, 0);
+  const double s = p->safety;
+  for (int k = 0; k < K; ++k) {
+    const float* t = co + 3 * (sets == 1 ? 0 : k);
+    if (!std::isfinite(t[0]) || !std::isfinite(t[1]) || !std::isfinite(t[2]))
+      return fail(DION_E_INVAL, "coefficients must be finite");
+    out.a[k] = (double)t[0] / s;
+    out.b[k] = (double)t[1] / (s * s * s);
+    out.c[k] = (double)t[2] / (s * s * s * s * s);
+  }
+  for (int k = 1; k < K; ++k) {  // never after the last iteration
+    bool r = p->restart_mask ? ((p->restart_mask >> (k - 1)) & 1u) : (p->restart_every > 0 && k % p->restart_every == 0);
+    out.restart[k - 1] = r ? 1 : 0;
+  }
+  out.row_frac = p->row_frac;
+  out.fp64 = p->precision == DION_PREC_FP64 || (p->precision == DION_PREC_AUTO && dtype == DION_FP32 && !step_mode);
+  return DION_OK;
+}
+
+int selected_count(int R, double frac) {
+  const double x = frac * (double)R;
+  long long k = (long long)std::ceil(x * (1.0 - 1e-6));
+  if (k < 1) k = 1;
+  if (k > R) k = R;
+  return (int)k;
+}
+
+// ----------------------------------------------- scalar bounds (MFMA16)
+// Power-of-two scales keep every stored fp16 operand within range: each
+// quantity's spectral norm (>= its largest entry) is bounded by pushing the
+// singular-value bound of the iterate through the scalar polynomial.
+double poly_max(double a, double b, double c, double lam_max, int mode) {
+  // mode 0: max |a + b l + c l^2|, mode 1: max |l (a + b l + c l^2)|, over l in [0, lam_max]
+  double best = 0.0;
+  const int N = 4096;
+  for (int i = 0; i <= N; ++i) {
+    const double l = lam_max * i / N;
+    double v = a + b * l + c * l * l;
+    if (mode == 1) v *= l;
+    best = std::max(best, std::fabs(v));
+  }
+  return best * 1.02 + 1e-30;
+}
+double sv_max(double a, double b, double c, double s_max) {  // max |f(s)| on [0, s_max]
+  double best = 0.0;
+  const int N = 4096;
+  for (int i = 0; i <= N; ++i) {
+    const double x = s_max * i / N;
+    best = std::max(best, std::fabs(a * x + b * x * x * x + c * x * x * x * x * x));
+  }
+  return best * 1.02 + 1e-30;
+}
+float pow2_scale(double bound) {  // largest 2^j with bound * 2^j <= 2^15
+  int j = (int)std::floor(std::log2(32768.0 / bound));
+  j = std::max(-60, std::min(60, j));
+  return std::ldexp(1.0f, j);
+}
+
+// ------------------------------------------------------------ the plan
+enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY };
+
+struct Step {
+  StepKind kind;
+  int bm = 0, na = 1, nb = 1, epi = 0;
+  bool sym = false;
+  int table = 0;  // index into Plan::tabs
+  PhaseArgs pa{};
+  int src_slot = 0, dst_slot = 0;
+};
+
+struct Table {  // a (matrix list, prefix) pair inside the int blob
+  size_t mats_off = 0, prefix_off = 0;  // in ints
+  int nmat = 0, total = 0;
+};
+
+struct MatPlan {
+  int R, C, k, m, n, m_pad, n_pad, tall;
+  size_t off[N_SLOTS];
+};
+
+struct Plan {
+  bool fp64 = false;
+  bool bf16_in = true;
+  int xterms0 = 1;
+  bool use_idx = false;
+  std::vector<MatPlan> mats;
+  int64_t total_rows = 0, total_sel = 0;
+  size_t off_descs = 0, off_scalars = 0, off_keys = 0, off_flags = 0, off_idx = 0, off_ints = 0,
+         off_data = 0, total = 0, upload_bytes = 0;
+  std::vector<int> ints;
+  std::vector<Table> tabs;
+  std::vector<Step> steps;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int add_table(Plan& P, const std::vector<int>& mats, const std::vector<int>& counts) {
+  Table t;
+  t.nmat = (int)mats.size();
+  t.mats_off = P.ints.size();
+  P.ints.insert(P.ints.end(), mats.begin(), mats.end());
+  t.prefix_off = P.ints.size();
+  int acc = 0;
+  for (int c : counts) {
+    P.ints.push_back(acc);
+    acc += c;
+  }
+  P.ints.push_back(acc);
+  t.total = acc;
+  P.tabs.push_back(t);
+  return (int)P.tabs.size() - 1;
+}
+
+int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm, bool step_mode, Plan& P) {
+  if (!shapes) return fail(DION_E_INVAL, "shapes is NULL");
+  if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
+  P.fp64 = prm.fp64;
+  P.bf16_in = !step_mode && dtype == DION_BF16;
+  P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;  // bf16 values are exact in one fp16 term
+  P.use_idx = prm.row_frac < 1.0;
+  const int K = (int)prm.a.size();
+  bool any_restart = false;
+  for (int r : prm.restart) any_restart |= (r != 0);
+  const size_t es = P.fp64 ? 8 : 2;
+  const size_t mm_terms = P.fp64 ? 1 : 2;
+  const size_t xt_terms = P.fp64 ? 1 : 2;
+
+  P.mats.resize(batch);
+  for (int i = 0; i < batch; ++i) {
+    const int R = shapes[i].rows, C = shapes[i].cols;
+    if (R < 1 || C < 1) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + ": rows and cols must be >= 1");
+    if ((int64_t)R * C > ((int64_t)1 << 40)) return fail(DION_E_INVAL, "matrix too large");
+    MatPlan& mp = P.mats[i];
+    mp.R = R;
+    mp.C = C;
+    mp.k = selected_count(R, prm.row_frac);
+    mp.tall = mp.k > C;
+    mp.m = std::min(mp.k, C);
+    mp.n = std::max(mp.k, C);
+    mp.m_pad = pad_up(mp.m);
+    mp.n_pad = pad_up(mp.n);
+    P.total_rows += R;
+    P.total_sel += mp.k;
+  }
+  size_t off = 0;
+  P.off_descs = off;
+  off = align256(off + sizeof(MatDesc) * batch);
+
+  // tables
+  std::vector<int> all(batch);
+  for (int i = 0; i < batch; ++i) all[i] = i;
+  auto sym_counts = [&](int bm) {
+    std::vector<int> c(batch);
+    for (int i = 0; i < batch; ++i) { int T = P.mats[i].m_pad / bm; c[i] = T * (T + 1) / 2; }
+    return c;
+  };
+  auto rect_counts = [&](const std::vector<int>& ms, int bm, bool rows_n) {
+    std::vector<int> c;
+    for (int i : ms) {
+      const MatPlan& mp = P.mats[i];
+      c.push_back((rows_n ? mp.n_pad : mp.m_pad) / bm * ((rows_n ? mp.m_pad : mp.n_pad) / bm));
+    }
+    return c;
+  };
+  auto total_of = [](const std::vector<int>& c) { long long s = 0; for (int x : c) s += x; return s; };
+  // tile size per phase kind: 256 when it gives at least two waves of blocks
+  auto pick_bm = [&](std::function<std::vector<int>(int)> counts) {
+    if (P.fp64) return 64;
+    return total_of(counts(256)) >= 512 ? 256 : 128;
+  };
+  const int bm_sym = pick_bm([&](int bm) { return sym_counts(bm); });
+  const int bm_xtq = pick_bm([&](int bm) { return rect_counts(all, bm, true); });
+  std::vector<int> wide, tall;
+  for (int i = 0; i < batch; ++i) (P.mats[i].tall ? tall : wide).push_back(i);
+  const int bm_fin = pick_bm([&](int bm) {
+    auto a = rect_counts(wide, bm, false), b = rect_counts(tall, bm, true);
+    a.insert(a.end(), b.begin(), b.end());
+    return a;
+  });
+  const int t_sym = add_table(P, all, sym_counts(bm_sym));
+  const int t_xtq = add_table(P, all, rect_counts(all, bm_xtq, true));
+  const int t_wide = add_table(P, wide, rect_counts(wide, bm_fin, false));
+  const int t_tall = add_table(P, tall, rect_counts(tall, bm_fin, true));
+  std::vector<int> pack_c(batch), tr_c(batch);
+  for (int i = 0; i < batch; ++i) {
+    const MatPlan& mp = P.mats[i];
+    pack_c[i] = (mp.m_pad / 64) * (mp.n_pad / 64);  // k_pad * C_pad = m_pad * n_pad either way
+    tr_c[i] = pack_c[i];
+  }
+  const int t_pack = add_table(P, all, pack_c);
+  const int t_tr = add_table(P, all, tr_c);
+  // uploaded part: descriptors, then tables; then device-written scratch
+  P.off_ints = off;
+  off = align256(off + sizeof(int) * P.ints.size());
+  P.upload_bytes = off;
+  P.off_scalars = off; off = align256(off + sizeof(MatScalars) * batch);
+  P.off_keys = off;    off = align256(off + sizeof(double) * P.total_rows);
+  P.off_flags = off;   off = align256(off + P.total_rows);
+  P.off_idx = off;     off = align256(off + sizeof(int) * P.total_sel);
+
+  // per-matrix buffers
+  P.off_data = off;
+  for (int i = 0; i < batch; ++i) {
+    MatPlan& mp = P.mats[i];
+    const size_t mn = (size_t)mp.m_pad * mp.n_pad, mm = (size_t)mp.m_pad * mp.m_pad;
+    for (int s = 0; s < N_SLOTS; ++s) mp.off[s] = 0;
+    mp.off[SLOT_X] = off;   off = align256(off + mn * es);
+    mp.off[SLOT_XT0] = off; off = align256(off + mn * es * xt_terms);
+    if (any_restart) { mp.off[SLOT_XT1] = off; off = align256(off + mn * es * xt_terms); }
+    for (int s = SLOT_MM0; s <= SLOT_MM3; ++s) { mp.off[s] = off; off = align256(off + mm * es * mm_terms); }
+  }
+  P.total = off;
+
+  // ---------------------------------------------------------- phase list
+  Step st;
+  st.kind = step_mode ? ST_MOMENTUM : ST_KEYS;
+  P.steps.push_back(st);
+  st.kind = ST_SELECT;
+  P.steps.push_back(st);
+  st = Step();
+  st.kind = ST_PACK;
+  st.table = t_pack;
+  P.steps.push_back(st);
+
+  auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, PhaseArgs pa) {
+    Step g;
+    g.kind = ST_GEMM;
+    g.table = table;
+    g.bm = bm;
+    g.sym = sym;
+    g.na = P.fp64 ? 1 : na;
+    g.nb = P.fp64 ? 1 : nb;
+    g.epi = epi;
+    g.pa = pa;
+    P.steps.push_back(g);
+  };
+  auto sc = [&](double bound) { return P.fp64 ? 1.0f : pow2_scale(bound); };
+
+  double sb = 1.0;  // bound on the singular values of the current iterate
+  int g_slot = SLOT_MM0;
+  float sG = sc(sb * sb);
+  {
+    PhaseArgs pa{};
+    pa.a_slot = pa.b_slot = SLOT_X;
+    pa.c_slot = g_slot;
+    pa.k_is_n = 1;
+    pa.alpha = sG;
+    pa.alpha_pow = 2;
+    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa);
+  }
+  std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
+  int q_slot = -1, xt_slot = SLOT_XT0, xterms = P.xterms0;
+  float sQ = 1.f, sXT = 1.f;
+  double qb = 1.0;
+  bool x_is_x0 = true;
+  for (int k = 1; k <= K; ++k) {
+    const double a = prm.a[k - 1], b = prm.b[k - 1], c = prm.c[k - 1];
+    const double gb = sb * sb;
+    const double pb = poly_max(a, b, c, gb, 0), tb = poly_max(a, b, c, gb, 1);
+    const double sb_next = sv_max(a, b, c, sb);
+    const float sP = sc(pb);
+    const int p_slot = freel.back();
+    freel.pop_back();
+    {  // P = a I + b G + c G^2, fused into the G*G epilogue
+      PhaseArgs pa{};
+      pa.a_slot = pa.b_slot = pa.aux_slot = g_slot;
+      pa.c_slot = p_slot;
+      pa.alpha = 1.0f / (sG * sG);
+      pa.poly_a = (float)a;
+      pa.poly_b = (float)b;
+      pa.poly_c = (float)c;
+      pa.aux_inv_scale = 1.0f / sG;
+      pa.out_scale = sP;
+      gemm(t_sym, bm_sym, true, 2, 2, EPI_POLY, pa);
+    }
+    if (q_slot < 0) {
+      q_slot = p_slot;
+      sQ = sP;
+      qb = pb;
+    } else {  // Q <- P Q
+      const double qb_new = qb * pb;
+      const float sQn = sc(qb_new);
+      const int qn = freel.back();
+      freel.pop_back();
+      PhaseArgs pa{};
+      pa.a_slot = p_slot;
+      pa.b_slot = q_slot;
+      pa.c_slot = qn;
+      pa.alpha = sQn / (sP * sQ);
+      gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa);
+      freel.push_back(q_slot);
+      q_slot = qn;
+      sQ = sQn;
+      qb = qb_new;
+    }
+    if (k == K) break;
+    if (prm.restart[k - 1]) {
+      // X <- Q X, computed as X'^T = X^T Q; then X = transpose; G = X X^T
+      const float sXn = sc(sb_next);
+      const int xt_new = xt_slot == SLOT_XT0 ? SLOT_XT1 : SLOT_XT0;
+      {
+        PhaseArgs pa{};
+        pa.a_slot = xt_slot;
+        pa.b_slot = q_slot;
+        pa.c_slot = xt_new;
+        pa.a_rows_is_n = 1;
+        pa.alpha = x_is_x0 ? sXn / sQ : sXn / (sXT * sQ);
+        pa.alpha_pow = x_is_x0 ? 1 : 0;
+        gemm(t_xtq, bm_xtq, false, xterms, 1, EPI_RECT, pa);
+      }
+      Step tr;
+      tr.kind = ST_TRANSPOSE;
+      tr.table = t_tr;
+      tr.src_slot = xt_new;
+      tr.dst_slot = SLOT_X;
+      P.steps.push_back(tr);
+      const float sGn = sc(sb_next * sb_next);
+      {
+        PhaseArgs pa{};
+        pa.a_slot = pa.b_slot = SLOT_X;
+        pa.c_slot = g_slot;
+        pa.k_is_n = 1;
+        pa.alpha = sGn / (sXn * sXn);
+        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa);
+      }
+      sG = sGn;
+      xt_slot = xt_new;
+      xterms = P.fp64 ? 1 : 2;
+      sXT = sXn;
+      x_is_x0 = false;
+      freel.push_back(q_slot);
+      if (p_slot != q_slot) freel.push_back(p_slot);
+      q_slot = -1;
+    } else {
+      // G <- P (P G)
+      const float sT = sc(tb);
+      const int t_slot = freel.back();
+      freel.pop_back();
+      {
+        PhaseArgs pa{};
+        pa.a_slot = p_slot;
+        pa.b_slot = g_slot;
+        pa.c_slot = t_slot;
+        pa.alpha = sT / (sP * sG);
+        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa);
+      }
+      const float sGn = sc(sb_next * sb_next);
+      {
+        PhaseArgs pa{};
+        pa.a_slot = p_slot;
+        pa.b_slot = t_slot;
+        pa.c_slot = g_slot;
+        pa.alpha = sGn / (sP * sT);
+        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa);
+      }
+      sG = sGn;
+      freel.push_back(t_slot);
+      if (p_slot != q_slot) freel.push_back(p_slot);
+    }
+    sb = sb_next;
+  }
+  {  // out = Q X: wide matrices as Q * X, tall ones as X^T * Q
+    PhaseArgs pa{};
+    pa.alpha = x_is_x0 ? 1.0f / sQ : 1.0f / (sQ * sXT);
+    pa.alpha_pow = x_is_x0 ? 1 : 0;
+    pa.out_fp32 = (!step_mode && dtype == DION_FP32) ? 1 : 0;
+    PhaseArgs pw = pa;
+    pw.a_slot = q_slot;
+    pw.b_slot = xt_slot;
+    pw.b_rows_is_n = 1;
+    pw.out_rows_are_m = 1;
+    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, xterms, EPI_OUT, pw);
+    PhaseArgs pt = pa;
+    pt.a_slot = xt_slot;
+    pt.b_slot = q_slot;
+    pt.a_rows_is_n = 1;
+    pt.out_rows_are_m = 0;
+    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, xterms, 1, EPI_OUT, pt);
+  }
+  if (P.use_idx && !step_mode) {
+    Step cp;
+    cp.kind = ST_COPY;
+    P.steps.push_back(cp);
+  }
+  return DION_OK;
+}
+
+// ---------------------------------------------------- pinned upload stage
+struct Stage {
+  void* host[2] = {nullptr, nullptr};
+  size_t cap[2] = {0, 0};
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  int next = 0;
+};
+thread_local Stage g_stage;
+
+int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
+  Stage& S = g_stage;
+  const int i = S.next;
+  S.next ^= 1;
+  if (S.ev[i]) {
+    if (hipEventSynchronize(S.ev[i]) != hipSuccess) return fail(DION_E_HIP, "hipEventSynchronize failed");
+  } else if (hipEventCreateWithFlags(&S.ev[i], hipEventDisableTiming) != hipSuccess) {
+    return fail(DION_E_HIP, "hipEventCreate failed");
+  }
+  if (S.cap[i] < bytes) {
+    if (S.host[i]) hipHostFree(S.host[i]);
+    S.host[i] = nullptr;
+    const size_t cap = std::max(bytes, (size_t)1 << 16);
+    if (hipHostMalloc(&S.host[i], cap, hipHostMallocDefault) != hipSuccess)
+      return fail(DION_E_HIP, "hipHostMalloc of the upload stage failed");
+    S.cap[i] = cap;
+  }
+  std::memcpy(S.host[i], src, bytes);
+  if (hipMemcpyAsync(dst, S.host[i], bytes, hipMemcpyHostToDevice, s) != hipSuccess)
+    return fail(DION_E_HIP, "hipMemcpyAsync of the plan failed");
+  if (hipEventRecord(S.ev[i], s) != hipSuccess) return fail(DION_E_HIP, "hipEventRecord failed");
+  return DION_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int run(const Plan& P, const void* const* M, void* const* out, const void* const* grad, int batch, int dtype,
+        int grad_dtype, float beta, bool step_mode, int32_t* sel_idx, void* workspace, size_t ws_bytes,
+        hipStream_t stream) {
+  if (!workspace) return fail(DION_E_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255) != 0) return fail(DION_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < P.total)
+    return fail(DION_E_WORKSPACE, "workspace too small: need " + std::to_string(P.total) + " bytes");
+  char* ws = (char*)workspace;
+  // descriptors
+  std::vector<char> blob(P.upload_bytes, 0);
+  MatDesc* descs = (MatDesc*)blob.data();
+  int64_t row0 = 0, sel0 = 0;
+  for (int i = 0; i < batch; ++i) {
+    const MatPlan& mp = P.mats[i];
+    MatDesc& d = descs[i];
+    d.M = M[i];
+    d.out = out[i];
+    d.grad = grad ? grad[i] : nullptr;
+    for (int s = 0; s < N_SLOTS; ++s) d.buf[s] = mp.off[s] ? ws + mp.off[s] : nullptr;
+    d.row0 = row0;
+    d.sel0 = sel0;
+    d.R = mp.R;
+    d.C = mp.C;
+    d.k = mp.k;
+    d.m = mp.m;
+    d.n = mp.n;
+    d.m_pad = mp.m_pad;
+    d.n_pad = mp.n_pad;
+    d.tall = mp.tall;
+    row0 += mp.R;
+    sel0 += mp.k;
+  }
+  std::memcpy(blob.data() + P.off_ints, P.ints.data(), sizeof(int) * P.ints.size());
+  int rc = upload(blob.data(), blob.size(), ws, stream);
+  if (rc) return rc;
+
+  const MatDesc* d_descs = (const MatDesc*)(ws + P.off_descs);
+  MatScalars* d_scal = (MatScalars*)(ws + P.off_scalars);
+  double* d_keys = (double*)(ws + P.off_keys);
+  uint8_t* d_flags = (uint8_t*)(ws + P.off_flags);
+  int* d_idx = (int*)(ws + P.off_idx);
+  const int* d_ints = (const int*)(ws + P.off_ints);
+  const bool in_bf16 = step_mode ? false : dtype == DION_BF16;
+
+  for (const Step& st : P.steps) {
+    switch (st.kind) {
+      case ST_KEYS:
+        launch_rowkeys(in_bf16, d_descs, batch, P.total_rows, d_keys, stream);
+        break;
+      case ST_MOMENTUM:
+        launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, beta, d_keys, stream);
+        break;
+      case ST_SELECT:
+        launch_select(d_descs, batch, d_keys, d_flags, d_idx, d_scal, P.fp64, stream);
+        break;
+      case ST_PACK: {
+        const Table& t = P.tabs[st.table];
+        launch_pack(in_bf16, P.fp64, d_descs, d_ints + t.prefix_off, t.nmat, t.total, d_idx, d_scal, P.xterms0,
+                    P.use_idx, stream);
+        break;
+      }
+      case ST_TRANSPOSE: {
+        const Table& t = P.tabs[st.table];
+        launch_transpose(P.fp64, d_descs, d_ints + t.prefix_off, t.nmat, t.total, st.src_slot, st.dst_slot, stream);
+        break;
+      }
+      case ST_GEMM: {
+        const Table& t = P.tabs[st.table];
+        GemmLaunch L{d_descs, d_ints + t.mats_off, d_ints + t.prefix_off, t.nmat, t.total};
+        PhaseArgs pa = st.pa;
+        pa.scalars = d_scal;
+        pa.idx = P.use_idx ? d_idx : nullptr;
+        const bool ok = P.fp64 ? launch_gemm64(st.epi, st.sym, L, pa, stream)
+                               : launch_gemm16(st.bm, st.na, st.nb, st.epi, st.sym, L, pa, stream);
+        if (!ok) return fail(DION_E_UNSUPPORTED, "no GEMM kernel for this phase");
+        break;
+      }
+      case ST_COPY:
+        launch_copy_unselected(in_bf16, d_descs, batch, P.total_rows, d_flags, stream);
+        break;
+    }
+  }
+  if (sel_idx) {
+    if (hipMemcpyAsync(sel_idx, d_idx, sizeof(int) * P.total_sel, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(DION_E_HIP, "copy of selected indices failed");
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DION_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return DION_OK;
+}
+
+int check_ptrs(const void* const* M, void* const* out, const dion_shape* shapes, int batch, size_t esz_in,
+               size_t esz_out) {
+  if (!M || !out) return fail(DION_E_INVAL, "matrix pointer arrays are NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!M[i] || !out[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
+  // out must not overlap any input
+  for (int i = 0; i < batch; ++i) {
+    const size_t no = (size_t)shapes[i].rows * shapes[i].cols * esz_out;
+    for (int j = 0; j < batch; ++j) {
+      const size_t ni = (size_t)shapes[j].rows * shapes[j].cols * esz_in;
+      if (overlaps(out[i], no, M[j], ni)) return fail(DION_E_INVAL, "out must not overlap the inputs");
+    }
+  }
+  return DION_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dion_workspace_size(const dion_shape* shapes, int32_t batch, int32_t dtype, const dion_ns_params* p) {
+  Params prm;
+  if (parse_params(p, dtype, false, prm)) return 0;
+  Plan P;
+  if (build_plan(shapes, batch, dtype, prm, false, P)) return 0;
+  size_t need = P.total;
+  if (dtype == DION_FP32 && p->precision != DION_PREC_FP64) {  // may also serve dion_rowsubset_step
+    Params ps;
+    Plan Q;
+    if (parse_params(p, DION_FP32, true, ps) == DION_OK && build_plan(shapes, batch, DION_FP32, ps, true, Q) == DION_OK)
+      need = std::max(need, Q.total);
+  }
+  return need;
+}
+
+int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,
+                      int32_t dtype, const dion_ns_params* p, int32_t* sel_idx, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Params prm;
+  int rc = parse_params(p, dtype, false, prm);
+  if (rc) return rc;
+  Plan P;
+  rc = build_plan(shapes, batch, dtype, prm, false, P);
+  if (rc) return rc;
+  const size_t es = dtype == DION_BF16 ? 2 : 4;
+  rc = check_ptrs(M, out, shapes, batch, es, es);
+  if (rc) return rc;
+  return run(P, M, out, nullptr, batch, dtype, dtype, 0.f, false, sel_idx, workspace, workspace_bytes,
+             (hipStream_t)stream);
+}
+
+int dion_orth_batched_simple(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,
+                             int32_t dtype, const float* ns_coeffs, int32_t n_iter, int32_t restart_every,
+                             float safety, float row_frac, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  dion_ns_params p{};
+  p.ns_coeffs = ns_coeffs;
+  p.n_coeff_sets = 1;
+  p.n_iter = n_iter;
+  p.restart_every = restart_every;
+  p.restart_mask = 0;
+  p.safety = safety;
+  p.row_frac = row_frac;
+  p.precision = DION_PREC_AUTO;
+  return dion_orth_batched(M, out, shapes, batch, dtype, &p, nullptr, workspace, workspace_bytes, stream);
+}
+
+int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* out, const dion_shape* shapes,
+                        int32_t batch, int32_t grad_dtype, float beta, const dion_ns_params* p, int32_t* sel_idx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (grad_dtype != DION_BF16 && grad_dtype != DION_FP32) return fail(DION_E_INVAL, "unknown grad dtype");
+  if (!std::isfinite(beta)) return fail(DION_E_INVAL, "beta must be finite");
+  Params prm;
+  int rc = parse_params(p, DION_FP32, true, prm);
+  if (rc) return rc;
+  Plan P;
+  rc = build_plan(shapes, batch, DION_FP32, prm, true, P);
+  if (rc) return rc;
+  if (!E || !grad) return fail(DION_E_INVAL, "E or grad pointer array is NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!E[i] || !grad[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
+  rc = check_ptrs((const void* const*)E, out, shapes, batch, 4, 2);
+  if (rc) return rc;
+  rc = check_ptrs(grad, out, shapes, batch, grad_dtype == DION_BF16 ? 2 : 4, 2);
+  if (rc) return rc;
+  return run(P, (const void* const*)E, out, grad, batch, DION_FP32, grad_dtype, beta, true, sel_idx, workspace,
+             workspace_bytes, (hipStream_t)stream);
+}
+
+double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_params* p) {
+  Params prm;
+  if (!shapes || batch < 1 || parse_params(p, DION_BF16, false, prm)) return 0.0;
+  const int K = (int)prm.a.size();
+  std::vector<int> seg;
+  int L = 0;
+  for (int k = 1; k <= K; ++k) {
+    ++L;
+    if (k == K || prm.restart[k - 1]) { seg.push_back(L); L = 0; }
+  }
+  double total = 0.0;
+  for (int i = 0; i < batch; ++i) {
+    const int k = selected_count(shapes[i].rows, prm.row_frac);
+    const double m = std::min(k, shapes[i].cols), n = std::max(k, shapes[i].cols);
+    for (int l : seg) total += n * m * (m + 1) + 2.0 * m * m * n + (4.0 * l - 3.0) * m * m * (m + 1);
+  }
+  return total;
+}
+
+int32_t dion_selected_rows(int32_t rows, float row_frac) {
+  if (rows < 1 || !(row_frac > 0.f && row_frac <= 1.f)) return 0;
+  return selected_count(rows, row_frac);
+}
+
+const char* dion_strerror(int status) {
+  switch (status) {
+    case DION_OK: return "success";
+    case DION_E_INVAL: return "invalid argument";
+    case DION_E_UNSUPPORTED: return "unsupported combination";
+    case DION_E_WORKSPACE: return "workspace NULL, misaligned or too small";
+    case DION_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dion_last_error(void) { return g_last_error.c_str(); }
+
+int dion_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal structures shared by the host planner and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dion {
+
+// Every operand buffer in the workspace has both dimensions padded to a
+// multiple of PAD (the largest GEMM tile), and the padding holds zeros, so the
+// MFMA main loops never need bounds checks.
+constexpr int PAD = 256;
+
+inline __host__ __device__ int pad_up(int x) { return (x + PAD - 1) / PAD * PAD; }
+
+// Buffer slots of a matrix's workspace region.
+enum Slot : int {
+  SLOT_X = 0,   // [m_pad][n_pad] hi: Gram (SYRK) operand
+  SLOT_XT0 = 1, // [n_pad][m_pad] x terms: apply operand (ping)
+  SLOT_XT1 = 2, // [n_pad][m_pad] x terms: apply operand (pong)
+  SLOT_MM0 = 3, // four m_pad x m_pad buffers (G, P, T, Q roles rotate)
+  SLOT_MM1 = 4,
+  SLOT_MM2 = 5,
+  SLOT_MM3 = 6,
+  N_SLOTS = 7
+};
+
+// Per-matrix descriptor (device copy in the workspace).
+struct MatDesc {
+  const void* M;      // input (R x C), or the fp32 momentum buffer in step mode
+  void* out;          // output (R x C)
+  const void* grad;   // step mode: gradient (R x C)
+  void* buf[N_SLOTS]; // workspace buffers (fp16 or fp64 elements)
+  int64_t row0;       // first global row (into keys / flags)
+  int64_t sel0;       // first entry of this matrix in the idx array
+  int R, C;           // stored shape
+  int k;              // selected rows
+  int m, n;           // Gram side and long side (m <= n)
+  int m_pad, n_pad;   // padded
+  int tall;           // 1 if the selected block is tall (k > C): X = S^T
+  int pad_;
+};
+
+// Per-matrix scalars written by the device (selection / normalization).
+struct MatScalars {
+  double nu2;         // ||S||_F^2
+  double x0_alpha64;  // X0 = stored operand * x0_alpha (= 2^-e / nu, 0 if nu = 0)
+  float x0_alpha;     // the same in fp32
+  int e;              // stored operand = S * 2^e (0 on the FP64 path)
+};
+
+// Epilogue kinds of the GEMM kernels.
+enum Epi : int {
+  EPI_SYM = 0,   // symmetric output: write the upper tile and its mirror
+  EPI_POLY = 1,  // symmetric output P = a I + b G + c acc (G read from aux)
+  EPI_RECT = 2,  // rectangular internal output
+  EPI_OUT = 3    // final output rows -> out[rowmap[r]] (masked to valid)
+};
+
+// Arguments of one GEMM phase: C = alpha * A B^T over a list of tiles.
+struct PhaseArgs {
+  int a_slot, b_slot, c_slot, aux_slot;
+  int a_rows_is_n;   // rows of A: 1 -> n_pad, 0 -> m_pad
+  int b_rows_is_n;   // rows of B
+  int k_is_n;        // reduction length: 1 -> n_pad, 0 -> m_pad
+  int alpha_pow;     // alpha *= x0_alpha^alpha_pow (per matrix)
+  float alpha;       // scale applied to the accumulator
+  float out_scale;   // scale of the stored output (fp16 power of two)
+  float poly_a, poly_b, poly_c;  // EPI_POLY coefficients
+  float aux_inv_scale;           // EPI_POLY: G = stored aux * aux_inv_scale
+  int out_fp32;      // EPI_OUT: 1 -> fp32 output, 0 -> bf16
+  int out_rows_are_m;  // EPI_OUT: 1 -> product rows index the m side
+  const MatScalars* scalars;
+  const int* idx;      // selected rows (global), NULL when row_frac == 1
+};
+
+// One grouped launch: the matrices it covers and the prefix of their tile counts.
+struct GemmLaunch {
+  const MatDesc* descs;
+  const int* mats;
+  const int* prefix;
+  int nmat;
+  int total;
+};
+
+}  // namespace dion

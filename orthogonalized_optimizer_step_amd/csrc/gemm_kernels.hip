@@ -1,0 +1,370 @@
+// Grouped (megabatched) GEMM kernels of the Gram Newton-Schulz iteration.
+//
+// Every product of the iteration is C = alpha * A * B^T with both operands
+// stored row-major with the reduction dimension contiguous ("NT"):
+//   Gram        G = X X^T            (X: m x n)            symmetric output
+//   m x m chain G*G, P*Q, P*G, P*T   (symmetric, commuting) symmetric output
+//   apply       X'^T = X^T Q         (X^T: n x m, Q: m x m) rectangular
+//   final       out = Q X  or  X^T Q, scattered to the selected output rows
+// Symmetric outputs are computed on upper-triangle tiles only and written
+// twice (tile and mirror), the triangular scheduling and transpose epilogue
+// the Dion3 summary describes for its symmetric GEMM kernels (方法 / 核心模块,
+// CuteDSL bullet); the polynomial P = aI + bG + cG^2 is fused into the G*G
+// epilogue (the same bullet's fused GEMM + add).
+//
+// One launch covers every matrix of the batch: blocks map to (matrix, tile)
+// through a prefix table of tile counts, and block ids are remapped so that
+// each of the 8 XCDs (blocks are dealt to XCDs round-robin) walks a
+// contiguous run of tiles, keeping shared operand panels in its own L2.
+//
+// MFMA16 path: fp16 operands with power-of-two scales, v_mfma_f32_32x32x16_f16
+// with fp32 accumulation; an operand may carry two terms (hi + lo, the lo
+// term being the fp16 rounding of the residual), in which case the products
+// hi*hi + hi*lo + lo*hi are accumulated.  FP64 path: plain fp64 FMA tiles.
+#include "dion_internal.h"
+
+namespace dion {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------- helpers
+__device__ __forceinline__ int find_segment(const int* prefix, int n, int t) {
+  int lo = 0, hi = n;  // prefix[lo] <= t < prefix[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Blocks are dealt to the 8 XCDs round-robin; give XCD x the contiguous
+// logical range [x*per, (x+1)*per).  Grid = 8 * per; extra blocks exit.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int per = (total + 7) >> 3;
+  return (b & 7) * per + (b >> 3);
+}
+
+__device__ __forceinline__ void decode_tile(bool sym, int local, int arows, int brows, int bm,
+                                            int& ti, int& tj) {
+  if (sym) {
+    const int T = arows / bm;
+    int i = 0;
+    while (local >= T - i) { local -= T - i; ++i; }
+    ti = i;
+    tj = i + local;
+  } else {
+    const int tn = brows / bm;
+    ti = local / tn;
+    tj = local - ti * tn;
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Storage of internal matrices: fp16 hi/lo pairs (term stride apart) or fp64.
+template <typename ST> struct Store;
+template <> struct Store<_Float16> {
+  __device__ static void put(void* base, size_t term_stride, size_t off, float v) {
+    _Float16 h = (_Float16)v;
+    _Float16 l = (_Float16)(v - (float)h);
+    ((_Float16*)base)[off] = h;
+    ((_Float16*)base)[off + term_stride] = l;
+  }
+  __device__ static float get(const void* base, size_t term_stride, size_t off) {
+    const _Float16* p = (const _Float16*)base;
+    return (float)p[off] + (float)p[off + term_stride];
+  }
+};
+template <> struct Store<double> {
+  __device__ static void put(void* base, size_t, size_t off, double v) { ((double*)base)[off] = v; }
+  __device__ static double get(const void* base, size_t, size_t off) { return ((const double*)base)[off]; }
+};
+
+// Epilogue for one accumulator element at tile-local (r, c) of tile (ti, tj).
+template <int EPI, typename ST, typename AT>
+__device__ __forceinline__ void epilogue_elem(const MatDesc& d, const PhaseArgs& pa, int arows,
+                                              int brows, int ti, int tj, int bm, int r, int c,
+                                              AT acc, AT alpha) {
+  const int gi = ti * bm + r, gj = tj * bm + c;
+  if (EPI == EPI_SYM || EPI == EPI_POLY) {
+    const bool diag = (ti == tj);
+    if (diag && c < r) return;  // the diagonal tile writes its upper half (+ mirror)
+    const int ld = arows;       // square
+    const size_t ts = (size_t)ld * ld;
+    AT v;
+    if (EPI == EPI_POLY) {
+      if (gi >= d.m || gj >= d.m) {
+        v = 0;  // keep the zero padding (the identity term would fill it)
+      } else {
+        const AT g = (AT)Store<ST>::get(d.buf[pa.aux_slot], ts, (size_t)gi * ld + gj) * (AT)pa.aux_inv_scale;
+        v = (AT)pa.poly_b * g + (AT)pa.poly_c * (acc * alpha);
+        if (gi == gj) v += (AT)pa.poly_a;
+        v *= (AT)pa.out_scale;
+      }
+    } else {
+      v = acc * alpha;
+    }
+    Store<ST>::put(d.buf[pa.c_slot], ts, (size_t)gi * ld + gj, v);
+    if (gi != gj) Store<ST>::put(d.buf[pa.c_slot], ts, (size_t)gj * ld + gi, v);
+  } else if (EPI == EPI_RECT) {
+    const size_t ts = (size_t)arows * brows;
+    Store<ST>::put(d.buf[pa.c_slot], ts, (size_t)gi * brows + gj, acc * alpha);
+  } else {  // EPI_OUT
+    const int rows_valid = pa.out_rows_are_m ? d.m : d.n;
+    const int cols_valid = pa.out_rows_are_m ? d.n : d.m;
+    if (gi >= rows_valid || gj >= cols_valid) return;
+    const int orow = pa.idx ? pa.idx[d.sel0 + gi] : gi;
+    const size_t o = (size_t)orow * d.C + gj;
+    const float v = (float)(acc * alpha);
+    if (pa.out_fp32) ((float*)d.out)[o] = v;
+    else ((uint16_t*)d.out)[o] = f32_to_bf16_rne(v);
+  }
+}
+
+template <typename AT>
+__device__ __forceinline__ AT phase_alpha(const MatDesc& d, const PhaseArgs& pa, int mi) {
+  AT a = (AT)pa.alpha;
+  if (pa.alpha_pow > 0) {
+    const AT f = sizeof(AT) == 8 ? (AT)pa.scalars[mi].x0_alpha64 : (AT)pa.scalars[mi].x0_alpha;
+    a *= f;
+    if (pa.alpha_pow > 1) a *= f;
+  }
+  return a;
+}
+
+// ------------------------------------------------------- MFMA16 GEMM kernel
+// 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BM/2)
+// sub-tile made of 32 x 32 MFMA blocks.  BK = 32: each operand row of the
+// stage is 64 bytes = four 16-byte chunks, stored in LDS with the chunk index
+// XOR-swizzled by (row >> 2) & 3 so that both the 16-byte chunk stores and
+// the 16-byte fragment reads of 8 (or 16) lanes hit distinct banks.
+template <int BM, int NA, int NB, int EPI, bool SYM>
+__global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ descs,
+                                                   const int* __restrict__ mats,
+                                                   const int* __restrict__ prefix, int nmat,
+                                                   int total, PhaseArgs pa) {
+  constexpr int BK = 32;
+  constexpr int WT = BM / 2;           // wave tile
+  constexpr int F = WT / 32;           // MFMA blocks per wave dim
+  constexpr int CPT = BM * 4 / 256;    // 16-byte chunks per thread per operand term
+  constexpr int NT = NA + NB;
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][NT][BM * BK];
+
+  const int t = xcd_remap(blockIdx.x, total);
+  if (t >= total) return;
+  const int j = find_segment(prefix, nmat, t);
+  const int mi = mats[j];
+  const MatDesc& d = descs[mi];
+  const int arows = pa.a_rows_is_n ? d.n_pad : d.m_pad;
+  const int brows = pa.b_rows_is_n ? d.n_pad : d.m_pad;
+  const int K = pa.k_is_n ? d.n_pad : d.m_pad;
+  int ti, tj;
+  decode_tile(SYM, t - prefix[j], arows, brows, BM, ti, tj);
+
+  const _Float16* gA = (const _Float16*)d.buf[pa.a_slot] + (size_t)ti * BM * K;
+  const _Float16* gB = (const _Float16*)d.buf[pa.b_slot] + (size_t)tj * BM * K;
+  const size_t a_ts = (size_t)arows * K, b_ts = (size_t)brows * K;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // global -> register staging of one BK stage
+  half8 stage[NT][CPT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int ch = tid + 256 * q;
+      const int row = ch >> 2, c = ch & 3;
+      const size_t off = (size_t)row * K + k0 + c * 8;
+#pragma unroll
+      for (int s = 0; s < NA; ++s) stage[s][q] = *(const half8*)(gA + s * a_ts + off);
+#pragma unroll
+      for (int s = 0; s < NB; ++s) stage[NA + s][q] = *(const half8*)(gB + s * b_ts + off);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int ch = tid + 256 * q;
+      const int row = ch >> 2, c = ch & 3;
+      const int pos = row * BK + ((c ^ ((row >> 2) & 3)) << 3);
+#pragma unroll
+      for (int s = 0; s < NT; ++s) *(half8*)&lds[buf][s][pos] = stage[s][q];
+    }
+  };
+
+  floatx16 acc[F][F];
+#pragma unroll
+  for (int a = 0; a < F; ++a)
+#pragma unroll
+    for (int b = 0; b < F; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 fa[NA][F], fb[NB][F];
+      const int chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int ra = wm * WT + f * 32 + (lane & 31);
+        const int rb = wn * WT + f * 32 + (lane & 31);
+        const int pa_ = ra * BK + ((chunk ^ ((ra >> 2) & 3)) << 3);
+        const int pb_ = rb * BK + ((chunk ^ ((rb >> 2) & 3)) << 3);
+#pragma unroll
+        for (int s = 0; s < NA; ++s) fa[s][f] = *(const half8*)&lds[cur][s][pa_];
+#pragma unroll
+        for (int s = 0; s < NB; ++s) fb[s][f] = *(const half8*)&lds[cur][NA + s][pb_];
+      }
+#pragma unroll
+      for (int sa = 0; sa < NA; ++sa)
+#pragma unroll
+        for (int sb = 0; sb < NB; ++sb) {
+          if (sa + sb >= (NA > NB ? NA : NB)) continue;  // drop lo*lo
+#pragma unroll
+          for (int a = 0; a < F; ++a)
+#pragma unroll
+            for (int b = 0; b < F; ++b)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sa][a], fb[sb][b], acc[a][b], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: acc[a][b][e] holds C[row][col] with
+  //   row = a*32 + (e/4)*8 + (lane/32)*4 + e%4,  col = b*32 + lane%32
+  const float alpha = phase_alpha<float>(d, pa, mi);
+#pragma unroll
+  for (int a = 0; a < F; ++a)
+#pragma unroll
+    for (int b = 0; b < F; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = wm * WT + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int c = wn * WT + b * 32 + (lane & 31);
+        epilogue_elem<EPI, _Float16, float>(d, pa, arows, brows, ti, tj, BM, r, c, acc[a][b][e], alpha);
+      }
+}
+
+// --------------------------------------------------------- FP64 GEMM kernel
+// 64 x 64 tiles, 256 threads as 16 x 16, each thread a 4 x 4 block; BK = 16.
+template <int EPI, bool SYM>
+__global__ __launch_bounds__(256) void k_gemm64(const MatDesc* __restrict__ descs,
+                                                const int* __restrict__ mats,
+                                                const int* __restrict__ prefix, int nmat,
+                                                int total, PhaseArgs pa) {
+  constexpr int BM = 64, BK = 16;
+  __shared__ double sA[BK][BM + 1];
+  __shared__ double sB[BK][BM + 1];
+  const int t = xcd_remap(blockIdx.x, total);
+  if (t >= total) return;
+  const int j = find_segment(prefix, nmat, t);
+  const int mi = mats[j];
+  const MatDesc& d = descs[mi];
+  const int arows = pa.a_rows_is_n ? d.n_pad : d.m_pad;
+  const int brows = pa.b_rows_is_n ? d.n_pad : d.m_pad;
+  const int K = pa.k_is_n ? d.n_pad : d.m_pad;
+  int ti, tj;
+  decode_tile(SYM, t - prefix[j], arows, brows, BM, ti, tj);
+  const double* gA = (const double*)d.buf[pa.a_slot] + (size_t)ti * BM * K;
+  const double* gB = (const double*)d.buf[pa.b_slot] + (size_t)tj * BM * K;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    // 64 rows x 16 k per operand = 1024 values, 4 per thread
+    for (int q = 0; q < 4; ++q) {
+      const int v = threadIdx.x + 256 * q;
+      const int row = v >> 4, kk = v & 15;
+      sA[kk][row] = gA[(size_t)row * K + k0 + kk];
+      sB[kk][row] = gB[(size_t)row * K + k0 + kk];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = sA[kk][ty * 4 + i]; b[i] = sB[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = fma(a[i], b[jj], acc[i][jj]);
+    }
+    __syncthreads();
+  }
+  const double alpha = phase_alpha<double>(d, pa, mi);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      epilogue_elem<EPI, double, double>(d, pa, arows, brows, ti, tj, BM, ty * 4 + i, tx * 4 + jj,
+                                         acc[i][jj], alpha);
+}
+
+// ---------------------------------------------------------------- launchers
+#define DION_G16(BM_, NA_, NB_, EPI_, SYM_) \
+  hipLaunchKernelGGL((k_gemm16<BM_, NA_, NB_, EPI_, SYM_>), dim3(grid), dim3(256), 0, stream, \
+                     L.descs, L.mats, L.prefix, L.nmat, L.total, pa)
+
+// Returns false for an unsupported combination.
+bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& L,
+                   const PhaseArgs& pa, hipStream_t stream) {
+  if (L.total <= 0) return true;
+  const int grid = ((L.total + 7) / 8) * 8;
+  const int key = (na << 8) | (nb << 4) | epi;
+#define DION_CASES(BM_)                                                                  \
+  if (sym) {                                                                             \
+    switch (key) {                                                                       \
+      case (1 << 8) | (1 << 4) | EPI_SYM: DION_G16(BM_, 1, 1, EPI_SYM, true); return true; \
+      case (2 << 8) | (2 << 4) | EPI_SYM: DION_G16(BM_, 2, 2, EPI_SYM, true); return true; \
+      case (2 << 8) | (2 << 4) | EPI_POLY: DION_G16(BM_, 2, 2, EPI_POLY, true); return true; \
+      default: return false;                                                             \
+    }                                                                                    \
+  } else {                                                                               \
+    switch (key) {                                                                       \
+      case (1 << 8) | (1 << 4) | EPI_RECT: DION_G16(BM_, 1, 1, EPI_RECT, false); return true; \
+      case (2 << 8) | (1 << 4) | EPI_RECT: DION_G16(BM_, 2, 1, EPI_RECT, false); return true; \
+      case (1 << 8) | (1 << 4) | EPI_OUT: DION_G16(BM_, 1, 1, EPI_OUT, false); return true; \
+      case (2 << 8) | (1 << 4) | EPI_OUT: DION_G16(BM_, 2, 1, EPI_OUT, false); return true; \
+      case (1 << 8) | (2 << 4) | EPI_OUT: DION_G16(BM_, 1, 2, EPI_OUT, false); return true; \
+      default: return false;                                                             \
+    }                                                                                    \
+  }
+  if (bm == 256) { DION_CASES(256) }
+  else if (bm == 128) { DION_CASES(128) }
+  return false;
+#undef DION_CASES
+}
+#undef DION_G16
+
+bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream) {
+  if (L.total <= 0) return true;
+  const int grid = ((L.total + 7) / 8) * 8;
+#define DION_G64(EPI_, SYM_) \
+  hipLaunchKernelGGL((k_gemm64<EPI_, SYM_>), dim3(grid), dim3(256), 0, stream, L.descs, L.mats, \
+                     L.prefix, L.nmat, L.total, pa)
+  if (sym) {
+    if (epi == EPI_SYM) { DION_G64(EPI_SYM, true); return true; }
+    if (epi == EPI_POLY) { DION_G64(EPI_POLY, true); return true; }
+  } else {
+    if (epi == EPI_RECT) { DION_G64(EPI_RECT, false); return true; }
+    if (epi == EPI_OUT) { DION_G64(EPI_OUT, false); return true; }
+  }
+  return false;
+#undef DION_G64
+}
+
+}  // namespace dion

@@ -1,0 +1,430 @@
+// HBM-bound passes around the MFMA phases: row keys, the fp32 momentum /
+// error-feedback update, top-k row selection with the Frobenius norm,
+// gather + convert + transpose into the padded operand buffers, transposes,
+// and the copy of unselected rows.
+//
+// Row rule: the Dion3 abstract and the Dion3 summary (方法 / 核心模块, "Dion3
+// 更新规则" bullet) select a fraction of the momentum rows each step; the
+// pages name no criterion, so rows are ranked by squared L2 norm (fp64, from
+// the exact stored values), larger first, ties to the lower row index.
+// Momentum: the summary's flow (输入输出流程) updates the momentum first; the
+// fp32 buffer is updated by two separately rounded fp32 operations.
+#include "dion_internal.h"
+
+namespace dion {
+
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ double wave_sum(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// global row -> matrix (descs are in batch order with increasing row0)
+__device__ __forceinline__ int mat_of_row(const MatDesc* descs, int nmat, int64_t g) {
+  int lo = 0, hi = nmat;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (descs[mid].row0 <= g) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------ row keys
+// One wave per row: key = sum_c x^2 in fp64 (each square is exact in fp64).
+template <typename InT>
+__global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ descs, int nmat,
+                                                 int64_t total_rows, double* __restrict__ keys) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= total_rows) return;
+  const MatDesc& d = descs[mat_of_row(descs, nmat, g)];
+  const int64_t r = g - d.row0;
+  const InT* row = (const InT*)d.M + r * d.C;
+  double s = 0.0;
+  if (sizeof(InT) == 2) {
+    const uint16_t* p = (const uint16_t*)row;
+    if ((d.C & 7) == 0) {
+      for (int c = lane * 8; c < d.C; c += 512) {
+        uint4 v = *(const uint4*)(p + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const double lo = (double)__uint_as_float(w[q] << 16);
+          const double hi = (double)__uint_as_float(w[q] & 0xFFFF0000u);
+          s += lo * lo;
+          s += hi * hi;
+        }
+      }
+    } else {
+      for (int c = lane; c < d.C; c += 64) {
+        const double x = (double)bf16_to_f32(p[c]);
+        s += x * x;
+      }
+    }
+  } else {
+    const float* p = (const float*)row;
+    if ((d.C & 3) == 0) {
+      for (int c = lane * 4; c < d.C; c += 256) {
+        float4 v = *(const float4*)(p + c);
+        s += (double)v.x * v.x;
+        s += (double)v.y * v.y;
+        s += (double)v.z * v.z;
+        s += (double)v.w * v.w;
+      }
+    } else {
+      for (int c = lane; c < d.C; c += 64) {
+        const double x = (double)p[c];
+        s += x * x;
+      }
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) keys[g] = s;
+}
+
+// ---------------------------------------------- momentum / error feedback
+// E <- fl32(fl32(beta * E) + grad), out <- bf16(E), key <- sum E^2 (fp64).
+// __fmul_rn / __fadd_rn keep the two roundings separate (no contraction).
+template <typename GT>
+__global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict__ descs, int nmat,
+                                                       int64_t total_rows, float beta,
+                                                       double* __restrict__ keys) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= total_rows) return;
+  const MatDesc& d = descs[mat_of_row(descs, nmat, g)];
+  const int64_t r = g - d.row0;
+  float* E = (float*)d.M + r * d.C;
+  uint16_t* out = (uint16_t*)d.out + r * d.C;
+  double s = 0.0;
+  if ((d.C & 3) == 0) {
+    for (int c = lane * 4; c < d.C; c += 256) {
+      float4 e = *(float4*)(E + c);
+      float gv[4];
+      if (sizeof(GT) == 2) {
+        const uint2 b = *(const uint2*)((const uint16_t*)d.grad + r * d.C + c);
+        gv[0] = __uint_as_float(b.x << 16);
+        gv[1] = __uint_as_float(b.x & 0xFFFF0000u);
+        gv[2] = __uint_as_float(b.y << 16);
+        gv[3] = __uint_as_float(b.y & 0xFFFF0000u);
+      } else {
+        const float4 b = *(const float4*)((const float*)d.grad + r * d.C + c);
+        gv[0] = b.x; gv[1] = b.y; gv[2] = b.z; gv[3] = b.w;
+      }
+      float m[4] = {__fadd_rn(__fmul_rn(beta, e.x), gv[0]), __fadd_rn(__fmul_rn(beta, e.y), gv[1]),
+                    __fadd_rn(__fmul_rn(beta, e.z), gv[2]), __fadd_rn(__fmul_rn(beta, e.w), gv[3])};
+      *(float4*)(E + c) = make_float4(m[0], m[1], m[2], m[3]);
+      uint2 o;
+      o.x = (uint32_t)bf16_rne(m[0]) | ((uint32_t)bf16_rne(m[1]) << 16);
+      o.y = (uint32_t)bf16_rne(m[2]) | ((uint32_t)bf16_rne(m[3]) << 16);
+      *(uint2*)(out + c) = o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += (double)m[q] * (double)m[q];
+    }
+  } else {
+    for (int c = lane; c < d.C; c += 64) {
+      const float gv = sizeof(GT) == 2 ? bf16_to_f32(((const uint16_t*)d.grad)[r * d.C + c])
+                                       : ((const float*)d.grad)[r * d.C + c];
+      const float m = __fadd_rn(__fmul_rn(beta, E[c]), gv);
+      E[c] = m;
+      out[c] = bf16_rne(m);
+      s += (double)m * (double)m;
+    }
+  }
+  s = wave_sum(s);
+  if (lane == 0) keys[g] = s;
+}
+
+// ------------------------------------------------- selection + norm
+// One 1024-thread block per matrix.  Top-k by (key desc, row asc): an MSB
+// first radix select over the 64-bit key patterns (non-negative doubles order
+// like their bit patterns) finds the k-th largest key T and how many rows
+// equal to T are needed; ranks among equal keys and the ascending compaction
+// come from block scans in row order.  The squared Frobenius norm of the
+// selected rows is the sum of their keys, reduced in a fixed order.
+constexpr int SEL_THREADS = 1024;
+
+__device__ int block_excl_scan(int v, int* sh, int& total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < SEL_THREADS; o <<= 1) {
+    const int add = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  total = sh[SEL_THREADS - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void k_select(const MatDesc* __restrict__ descs,
+                                                        const double* __restrict__ keys_all,
+                                                        uint8_t* __restrict__ flags_all,
+                                                        int* __restrict__ idx_all,
+                                                        MatScalars* __restrict__ scalars,
+                                                        int fp64_path) {
+  __shared__ unsigned hist[256];
+  __shared__ int scan_sh[SEL_THREADS];
+  __shared__ double red[SEL_THREADS];
+  __shared__ int s_digit, s_need;
+  const MatDesc& d = descs[blockIdx.x];
+  const int R = d.R, k = d.k, tid = threadIdx.x;
+  const double* keys = keys_all + d.row0;
+  uint8_t* flags = flags_all + d.row0;
+  int* idx = idx_all + d.sel0;
+  const uint64_t* ukeys = (const uint64_t*)keys;
+
+  uint64_t T = 0;
+  int need = 0;  // rows with key == T still to take
+  if (k < R) {
+    uint64_t prefix = 0, mask = 0;
+    int kk = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
+      __syncthreads();
+      for (int r = tid; r < R; r += SEL_THREADS) {
+        const uint64_t u = ukeys[r];
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, dg = 0;
+        for (dg = 255; dg >= 0; --dg) {
+          if (cum + (int)hist[dg] >= kk) break;
+          cum += hist[dg];
+        }
+        s_digit = dg < 0 ? 0 : dg;
+        s_need = kk - cum;
+      }
+      __syncthreads();
+      prefix |= (uint64_t)s_digit << shift;
+      mask |= (uint64_t)0xFF << shift;
+      kk = s_need;
+      __syncthreads();
+    }
+    T = prefix;
+    need = kk;
+  }
+
+  // flags + ascending compaction, chunk by chunk in row order
+  int eq_base = 0, sel_base = 0;
+  for (int base = 0; base < R; base += SEL_THREADS) {
+    const int r = base + tid;
+    const bool valid = r < R;
+    int sel = 0;
+    if (k >= R) {
+      sel = valid;
+    } else {
+      const uint64_t u = valid ? ukeys[r] : 0;
+      const int is_eq = valid && u == T;
+      int tot;
+      const int rank = block_excl_scan(is_eq, scan_sh, tot);
+      sel = valid && (u > T || (is_eq && eq_base + rank < need));
+      eq_base += tot;
+    }
+    int tot2;
+    const int pos = block_excl_scan(sel, scan_sh, tot2);
+    if (valid) flags[r] = (uint8_t)sel;
+    if (sel && sel_base + pos < k) idx[sel_base + pos] = r;
+    sel_base += tot2;
+  }
+  __syncthreads();
+
+  // squared Frobenius norm of the selected rows, fixed-order reduction
+  double s = 0.0;
+  for (int r = tid; r < R; r += SEL_THREADS)
+    if (flags[r]) s += keys[r];
+  red[tid] = s;
+  __syncthreads();
+  for (int o = SEL_THREADS / 2; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double nu2 = red[0];
+    MatScalars sc;
+    sc.nu2 = nu2;
+    if (nu2 > 0.0) {
+      const double nu = sqrt(nu2);
+      int E2;
+      frexp(nu, &E2);  // nu <= 2^E2
+      const int e = fp64_path ? 0 : 14 - E2;  // |S * 2^e| <= nu 2^(14-E2) <= 2^14
+      sc.e = e;
+      sc.x0_alpha64 = ldexp(1.0, -e) / nu;
+    } else {
+      sc.e = 0;
+      sc.x0_alpha64 = 0.0;
+    }
+    sc.x0_alpha = (float)sc.x0_alpha64;
+    scalars[blockIdx.x] = sc;
+  }
+}
+
+// ------------------------------------------------------------- pack
+// S = M[selected rows] (k x C) into the padded operand buffers:
+//   SL [k_pad][C_pad] (S as is) and ST [C_pad][k_pad] (S transposed).
+// wide (k <= C): X = SL, X^T = ST;  tall: X = ST, X^T = SL.
+// The Gram operand X keeps one term; X^T keeps `xterms` terms (hi, lo).
+// MFMA16 values are S * 2^e rounded to fp16 (exact for bf16 input within
+// fp16's normal range); FP64 values are S exactly.  64 x 64 tiles via LDS.
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
+                                              const int* __restrict__ prefix, int nmat, int total,
+                                              const int* __restrict__ idx_all,
+                                              const MatScalars* __restrict__ scalars, int xterms,
+                                              int use_idx) {
+  __shared__ float tile[64][65];
+  const int t = blockIdx.x;
+  if (t >= total) return;
+  int lo = 0, hi = nmat;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid;
+  }
+  const MatDesc& d = descs[lo];
+  const int local = t - prefix[lo];
+  const int k_pad = d.tall ? d.n_pad : d.m_pad;
+  const int c_pad = d.tall ? d.m_pad : d.n_pad;
+  const int tc = c_pad / 64;
+  const int r0 = (local / tc) * 64, c0 = (local % tc) * 64;
+  const float scale = ldexpf(1.0f, scalars[lo].e);
+  const int* idx = idx_all + d.sel0;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    float v = 0.f;
+    if (r < d.k && c < d.C) {
+      const int src = use_idx ? idx[r] : r;
+      const InT* row = (const InT*)d.M + (int64_t)src * d.C;
+      if (sizeof(InT) == 2) v = bf16_to_f32(((const uint16_t*)row)[c]);
+      else v = ((const float*)row)[c];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  void* sl = d.tall ? d.buf[SLOT_XT0] : d.buf[SLOT_X];
+  void* st = d.tall ? d.buf[SLOT_X] : d.buf[SLOT_XT0];
+  const int sl_terms = d.tall ? xterms : 1;
+  const int st_terms = d.tall ? 1 : xterms;
+  const size_t ts = (size_t)k_pad * c_pad;
+  for (int i = ty; i < 64; i += 4) {
+    // SL row r0+i, column c0+tx
+    const float v = tile[i][tx];
+    const size_t o1 = (size_t)(r0 + i) * c_pad + c0 + tx;
+    // ST row c0+i, column r0+tx  (value S[r0+tx][c0+i])
+    const float w = tile[tx][i];
+    const size_t o2 = (size_t)(c0 + i) * k_pad + r0 + tx;
+    if (sizeof(OutT) == 8) {
+      ((double*)sl)[o1] = (double)v;
+      ((double*)st)[o2] = (double)w;
+    } else {
+      const float vs = v * scale, ws = w * scale;
+      const _Float16 vh = (_Float16)vs, wh = (_Float16)ws;
+      ((_Float16*)sl)[o1] = vh;
+      ((_Float16*)st)[o2] = wh;
+      if (sl_terms > 1) ((_Float16*)sl)[o1 + ts] = (_Float16)(vs - (float)vh);
+      if (st_terms > 1) ((_Float16*)st)[o2 + ts] = (_Float16)(ws - (float)wh);
+    }
+  }
+}
+
+// ---------------------------------------------------------- transpose
+// X^T (hi term) [n_pad][m_pad] -> X [m_pad][n_pad], fp16 or fp64.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const MatDesc* __restrict__ descs,
+                                                   const int* __restrict__ prefix, int nmat,
+                                                   int total, int src_slot, int dst_slot) {
+  __shared__ T tile[64][65];
+  const int t = blockIdx.x;
+  if (t >= total) return;
+  int lo = 0, hi = nmat;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid;
+  }
+  const MatDesc& d = descs[lo];
+  const int local = t - prefix[lo];
+  const int tm = d.m_pad / 64;
+  const int n0 = (local / tm) * 64, m0 = (local % tm) * 64;
+  const T* src = (const T*)d.buf[src_slot];
+  T* dst = (T*)d.buf[dst_slot];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) tile[i][tx] = src[(size_t)(n0 + i) * d.m_pad + m0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) dst[(size_t)(m0 + i) * d.n_pad + n0 + tx] = tile[tx][i];
+}
+
+// ------------------------------------------------- unselected row copy
+template <typename InT>
+__global__ __launch_bounds__(256) void k_copy_unselected(const MatDesc* __restrict__ descs, int nmat,
+                                                         int64_t total_rows,
+                                                         const uint8_t* __restrict__ flags) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= total_rows || flags[g]) return;
+  const MatDesc& d = descs[mat_of_row(descs, nmat, g)];
+  const int64_t r = g - d.row0;
+  const InT* src = (const InT*)d.M + r * d.C;
+  InT* dst = (InT*)d.out + r * d.C;
+  for (int c = lane; c < d.C; c += 64) dst[c] = src[c];
+}
+
+// ---------------------------------------------------------------- launchers
+static inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + 3) / 4); }
+
+void launch_rowkeys(bool bf16, const MatDesc* descs, int nmat, int64_t rows, double* keys,
+                    hipStream_t s) {
+  if (bf16) hipLaunchKernelGGL(k_rowkeys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
+  else hipLaunchKernelGGL(k_rowkeys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
+}
+
+void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
+                          double* keys, hipStream_t s) {
+  if (grad_bf16) hipLaunchKernelGGL(k_momentum_keys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys);
+  else hipLaunchKernelGGL(k_momentum_keys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys);
+}
+
+void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,
+                   MatScalars* scalars, bool fp64_path, hipStream_t s) {
+  hipLaunchKernelGGL(k_select, dim3(nmat), dim3(SEL_THREADS), 0, s, descs, keys, flags, idx, scalars,
+                     fp64_path ? 1 : 0);
+}
+
+void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat,
+                 int total, const int* idx, const MatScalars* scalars, int xterms, bool use_idx,
+                 hipStream_t s) {
+  if (total <= 0) return;
+  const int ui = use_idx ? 1 : 0;
+  if (fp64_path) {
+    if (in_bf16) hipLaunchKernelGGL((k_pack<uint16_t, double>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    else hipLaunchKernelGGL((k_pack<float, double>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+  } else {
+    if (in_bf16) hipLaunchKernelGGL((k_pack<uint16_t, _Float16>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    else hipLaunchKernelGGL((k_pack<float, _Float16>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+  }
+}
+
+void launch_transpose(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
+                      int src_slot, int dst_slot, hipStream_t s) {
+  if (total <= 0) return;
+  if (fp64_path) hipLaunchKernelGGL(k_transpose<double>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, src_slot, dst_slot);
+  else hipLaunchKernelGGL(k_transpose<_Float16>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, src_slot, dst_slot);
+}
+
+void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows,
+                            const uint8_t* flags, hipStream_t s) {
+  if (bf16) hipLaunchKernelGGL(k_copy_unselected<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags);
+  else hipLaunchKernelGGL(k_copy_unselected<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags);
+}
+
+}  // namespace dion

@@ -1,0 +1,116 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/dion.h, and its host-side functions (workspace sizing,
+FLOP count, selected-row count, argument validation) behave as documented.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import orthogonalized_optimizer_step_amd as dion
+from orthogonalized_optimizer_step_amd import _lib
+from oracle import dion_oracle as O
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "dion.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dion_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 9
+    cdll = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(cdll, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_version():
+    assert _lib.lib.dion_version() == 100
+
+
+@pytest.mark.parametrize("R,frac", [(4096, 0.125), (14336, 0.125), (28672, 0.25), (1000, 0.1), (7, 0.5),
+                                    (5, 1e-6), (5, 1.0), (8192, 0.25), (3, 0.34)])
+def test_selected_rows_matches_oracle(R, frac):
+    f32 = ctypes.c_float(frac).value
+    assert _lib.lib.dion_selected_rows(R, ctypes.c_float(frac)) == O.selected_count(R, f32)
+
+
+def test_useful_flops_formula():
+    # m=64, n=128, K=5, no restart: one segment of length 5
+    m, n = 64, 128
+    expect = n * m * (m + 1) + 2 * m * m * n + (4 * 5 - 3) * m * m * (m + 1)
+    assert dion.useful_flops([(64, 128)]) == expect
+    # restarts every 2 with K=5: segments 2, 2, 1
+    seg = lambda L: n * m * (m + 1) + 2 * m * m * n + (4 * L - 3) * m * m * (m + 1)
+    assert dion.useful_flops([(128, 64)], restart_every=2) == 2 * seg(2) + seg(1)
+    wl = WORKLOADS["llama3_8b"]
+    assert abs(dion.useful_flops(wl.shapes, restart_every=2) / 1e12 - 371.617) < 0.01
+
+
+def test_workspace_size_monotone_and_invalid():
+    small = dion.workspace_size([(64, 128)])
+    big = dion.workspace_size([(64, 128), (300, 200)])
+    assert 0 < small < big
+    assert dion.workspace_size([(64, 128)], "fp32") > 0
+    with pytest.raises(dion.DionError):
+        dion.workspace_size([(0, 5)])
+    with pytest.raises(dion.DionError):
+        dion.workspace_size([(5, 5)], row_frac=0.0)
+    with pytest.raises(dion.DionError):
+        dion.workspace_size([(5, 5)], n_iter=0)
+    with pytest.raises(dion.DionError):
+        dion.workspace_size([(5, 5)], coeffs=[(1, 2, 3), (1, 2, 3)], n_iter=3)
+
+
+def _params(**kw):
+    base = dict(coeffs=dion.QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0, row_frac=1.0,
+                precision="auto")
+    base.update(kw)
+    return dion._params(**base)
+
+
+def test_orth_validation_errors_before_launch():
+    """Invalid calls return an error code on the host; nothing is launched."""
+    lib = _lib.lib
+    shp = dion._shapes([(4, 4)])
+    fake = (ctypes.c_void_p * 1)(0x1000)
+    fake_out = (ctypes.c_void_p * 1)(0x2000)
+    p, keep = _params()
+    # NULL matrix pointer
+    null = (ctypes.c_void_p * 1)(None)
+    assert lib.dion_orth_batched(null, fake_out, shp, 1, 0, ctypes.byref(p), None, ctypes.c_void_p(0x10000),
+                                 1 << 30, None) == -1
+    # out overlapping M
+    assert lib.dion_orth_batched(fake, fake, shp, 1, 0, ctypes.byref(p), None, ctypes.c_void_p(0x10000),
+                                 1 << 30, None) == -1
+    # misaligned / small / NULL workspace
+    assert lib.dion_orth_batched(fake, fake_out, shp, 1, 0, ctypes.byref(p), None, ctypes.c_void_p(0x10001),
+                                 1 << 30, None) == -3
+    assert lib.dion_orth_batched(fake, fake_out, shp, 1, 0, ctypes.byref(p), None, ctypes.c_void_p(0x10000),
+                                 16, None) == -3
+    assert lib.dion_orth_batched(fake, fake_out, shp, 1, 0, ctypes.byref(p), None, None, 1 << 30, None) == -3
+    assert b"workspace" in lib.dion_last_error()
+    # bad params
+    for bad in (dict(safety=0.0), dict(row_frac=1.5), dict(n_iter=65), dict(precision=7)):
+        pb, keep2 = _params(**bad)
+        assert lib.dion_orth_batched(fake, fake_out, shp, 1, 0, ctypes.byref(pb), None,
+                                     ctypes.c_void_p(0x10000), 1 << 30, None) == -1
+    # bad dtype, bad batch
+    assert lib.dion_orth_batched(fake, fake_out, shp, 1, 7, ctypes.byref(p), None, ctypes.c_void_p(0x10000),
+                                 1 << 30, None) == -1
+    assert lib.dion_orth_batched(fake, fake_out, shp, 0, 0, ctypes.byref(p), None, ctypes.c_void_p(0x10000),
+                                 1 << 30, None) == -1
+    # the step refuses the FP64 path
+    pf, keep3 = _params(precision="fp64")
+    E = (ctypes.c_void_p * 1)(0x3000)
+    g = (ctypes.c_void_p * 1)(0x4000)
+    assert lib.dion_rowsubset_step(E, g, fake_out, shp, 1, 0, ctypes.c_float(0.9), ctypes.byref(pf), None,
+                                   ctypes.c_void_p(0x10000), 1 << 30, None) == -2
+    assert lib.dion_strerror(-2) == b"unsupported combination"

@@ -1,0 +1,185 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Gates: selected rows and the fp32 momentum buffer bit-exact; the update within
+a relative Frobenius error of 1e-4 on the FP64 path (fp32 data) and 2e-2 on
+the MFMA16 path (bf16 data), per matrix, against the oracle's fp64 result.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import dion_oracle as O  # noqa: E402
+from workloads import (WORKLOADS, fp32_64x128, gpt2_small_np, bf16_bits_to_f32, lowrank_np,  # noqa: E402
+                       round_bf16, LLAMA3_8B_LAYER)
+
+pytestmark = pytest.mark.gpu
+
+TOL_MFMA16 = 2e-2
+TOL_FP64 = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dion():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import orthogonalized_optimizer_step_amd as d
+    return d
+
+
+def to_dev_bf16(a32):
+    return torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).cuda().to(torch.bfloat16)
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def assert_selection(idx_gpu, M, frac):
+    """Bit-exact against the oracle's selection; an exchange is tolerated only
+    between rows whose fp64 keys agree to 4 ulps (several answers correct)."""
+    ref = O.select_rows(M, frac)
+    got = np.asarray(idx_gpu, dtype=np.int64)
+    assert got.shape == ref.shape
+    assert np.all(np.diff(got) > 0), "indices must be ascending"
+    if np.array_equal(got, ref):
+        return
+    keys = O.row_keys(M)
+    diff = np.setxor1d(got, ref)
+    kd = keys[diff]
+    assert np.max(kd) - np.min(kd) <= 4 * np.spacing(np.max(kd)), f"selection differs: {diff}"
+
+
+# ------------------------------------------------------------ fp64 path
+def test_fp32_64x128_fp64_path(dion):
+    M = fp32_64x128()
+    out = dion.orth_batched([torch.from_numpy(M).cuda()], n_iter=5)[0]
+    ref, _ = O.orthogonalize(M, n_iter=5)
+    err = O.rel_frobenius(to_np(out), ref)
+    print(f"fp32 64x128 FP64 path: rel err {err:.3e}")
+    assert err <= TOL_FP64
+    assert err < 1e-6  # fp64 internals, fp32 output rounding only
+
+
+SMALL_SHAPES = [(7, 33), (33, 7), (300, 200), (200, 520), (1, 5), (5, 1), (256, 256), (257, 511), (64, 64)]
+
+
+def small_batch(seed, dtype_bf16=True):
+    Ms = []
+    for i, (r, c) in enumerate(SMALL_SHAPES):
+        M = lowrank_np((seed, i), r, c, max(1, min(r, c) // 8), 0.1, log_scale=(-3.0, 0.0))
+        Ms.append(round_bf16(M) if dtype_bf16 else M)
+    return Ms
+
+
+@pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10, safety=1.01),
+                                   dict(n_iter=6, restart_every=2, safety=1.05)])
+def test_small_ragged_fp64_path(dion, sched):
+    Ms = small_batch(11)
+    outs = dion.orth_batched([torch.from_numpy(M).cuda() for M in Ms], precision="fp64",
+                             **{"n_iter": 5, **sched})
+    for M, o in zip(Ms, outs):
+        ref, _ = O.orthogonalize(M, **{"n_iter": 5, **sched})
+        err = O.rel_frobenius(to_np(o), ref)
+        assert err < 1e-6, (M.shape, err)
+
+
+# ---------------------------------------------------------- MFMA16 path
+@pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10, safety=1.01),
+                                   dict(n_iter=6, restart_every=2, safety=1.05), dict(restart_every=1)])
+def test_small_ragged_mfma16(dion, sched):
+    Ms = small_batch(12)
+    kw = {"n_iter": 5, **sched}
+    outs = dion.orth_batched([to_dev_bf16(M) for M in Ms], **kw)
+    errs = []
+    for M, o in zip(Ms, outs):
+        ref, _ = O.orthogonalize(M, **kw)
+        errs.append(O.rel_frobenius(to_np(o), ref))
+    print("MFMA16 small ragged", sched, " ".join(f"{e:.2e}" for e in errs))
+    assert max(errs) <= TOL_MFMA16
+
+
+def test_fp32_input_mfma16(dion):
+    """fp32 momentum on the MFMA16 path (two-term operands for X0)."""
+    Ms = small_batch(13, dtype_bf16=False)
+    outs = dion.orth_batched([torch.from_numpy(M).cuda() for M in Ms], precision="mfma16", restart_every=2)
+    for M, o in zip(Ms, outs):
+        ref, _ = O.orthogonalize(M, restart_every=2)
+        assert O.rel_frobenius(to_np(o), ref) <= TOL_MFMA16
+
+
+def test_gpt2_small_full(dion):
+    wl = WORKLOADS["gpt2_small"]
+    Ms = [bf16_bits_to_f32(b) for b in gpt2_small_np()]
+    outs = dion.orth_batched([to_dev_bf16(M) for M in Ms], **wl.ns_kwargs())
+    errs = []
+    for M, o in zip(Ms, outs):
+        ref, _ = O.orthogonalize(M, **wl.ns_kwargs())
+        errs.append(O.rel_frobenius(to_np(o), ref))
+    print(f"gpt2_small: max rel err {max(errs):.3e}, mean {np.mean(errs):.3e}")
+    assert max(errs) <= TOL_MFMA16
+
+
+def test_determinism(dion):
+    Ms = [to_dev_bf16(M) for M in small_batch(14)]
+    a = dion.orth_batched(Ms, restart_every=2, row_frac=0.5)
+    b = dion.orth_batched(Ms, restart_every=2, row_frac=0.5)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_zero_matrix(dion):
+    for prec, dt in (("mfma16", torch.bfloat16), ("fp64", torch.float32)):
+        Ms = [torch.zeros((12, 40), dtype=dt, device="cuda"), torch.zeros((40, 12), dtype=dt, device="cuda")]
+        outs, idx = dion.orth_batched(Ms, row_frac=0.25, precision=prec, return_indices=True)
+        for o in outs:
+            assert torch.count_nonzero(o) == 0
+        assert idx[0].tolist() == [0, 1, 2] and idx[1].tolist() == list(range(10))
+
+
+# ---------------------------------------------------------- row subset
+@pytest.mark.parametrize("frac", [0.25, 0.5, 0.125, 1.0 / 37])
+@pytest.mark.parametrize("prec", ["mfma16", "fp64"])
+def test_row_subset_ties(dion, frac, prec):
+    rng = np.random.default_rng(int(frac * 1000))
+    shapes = [(37, 16), (64, 20), (16, 300), (520, 40)]
+    Ms = []
+    for r, c in shapes:
+        M = rng.integers(-4, 5, size=(r, c)).astype(np.float32)
+        M[rng.integers(0, r, size=r // 4)] = 0.0
+        M[r // 2] = M[0]
+        M[r - 1] = M[1]
+        Ms.append(M)
+    dt = torch.bfloat16 if prec == "mfma16" else torch.float32
+    dev = [torch.from_numpy(M).cuda().to(dt) for M in Ms]
+    outs, idxs = dion.orth_batched(dev, restart_every=2, row_frac=frac, precision=prec, return_indices=True)
+    for M, o, ix in zip(Ms, outs, idxs):
+        ref_out, ref_idx = O.orthogonalize(M, restart_every=2, row_frac=frac)
+        assert np.array_equal(ix.cpu().numpy(), ref_idx)          # integer keys: exact
+        got = to_np(o)
+        rest = np.setdiff1d(np.arange(M.shape[0]), ref_idx)
+        assert np.array_equal(got[rest], M[rest].astype(np.float64))
+        tol = TOL_MFMA16 if prec == "mfma16" else 1e-6
+        assert O.rel_frobenius(got[ref_idx], ref_out[ref_idx]) <= tol
+
+
+def test_rowsubset_step_small(dion):
+    shapes = [(32, 20), (64, 48), (40, 200), (300, 64)]
+    beta = 0.95
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(3):
+        G = [round_bf16(lowrank_np((4, t, i, 0), r, c, 3, 0.05, log_scale=(-3.0, 0.0)))
+             for i, (r, c) in enumerate(shapes)]
+        outs, idxs = dion.rowsubset_step(E_dev, [to_dev_bf16(g) for g in G], beta, restart_every=2,
+                                         row_frac=0.25, return_indices=True)
+        newE, ref_outs, ref_idxs = O.rowsubset_step(E_host, G, beta, n_iter=5, restart_every=2, row_frac=0.25)
+        for i in range(len(shapes)):
+            assert np.array_equal(E_dev[i].cpu().numpy().view(np.uint32), newE[i].view(np.uint32))
+            assert_selection(idxs[i].cpu().numpy(), newE[i], 0.25)
+            got = to_np(outs[i])
+            ix = ref_idxs[i]
+            rest = np.setdiff1d(np.arange(shapes[i][0]), ix)
+            assert np.array_equal(got[rest], round_bf16(newE[i][rest]).astype(np.float64))
+            assert O.rel_frobenius(got[ix], ref_outs[i][ix]) <= TOL_MFMA16
+        E_host = newE
