@@ -1,0 +1,190 @@
+"""Benchmark: orthogonalized params/s and MFMA TFLOP/s on the Llama-3-8B layer set.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3_8b]
+
+A step is one megabatched orthogonalization call over all 224 momentum matrices
+of the 32-layer Llama-3-8B layer set (q,o 4096x4096; k,v 1024x4096; gate,up
+14336x4096; down 4096x14336), bf16, rank-64 + 0.05 noise with per-matrix scale
+10^U(-3,0), 5 Gram Newton-Schulz iterations with restarts every 2.  Inputs are
+synthetic and resident in HBM before the timed region.  Prints one JSON line.
+
+Beside the GPU figures: a roofline entry for the dominant kernel (algorithmic
+FLOPs per launch over its average launch time, measured with hipEvents on the
+launch stream by the library's profiling hook, against the dense fp16/bf16 MFMA
+peak), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA16_TFLOPS = 2516.6   # MI355X dense fp16 / bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "gpt2_small", "llama3_70b",
+                                                                "llama3_8b_rows"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--profile", action="store_true",
+                    help="only run warmup + steps (for rocprofv3), no baseline")
+    return ap.parse_args()
+
+
+def make_inputs(wl, torch):
+    import workloads as W
+    if wl.name in ("llama3_8b", "llama3_8b_rows"):
+        return W.llama3_8b_torch(step=1 if wl.name.endswith("rows") else None)
+    if wl.name == "gpt2_small":
+        import numpy as np
+        return [torch.from_numpy(W.bf16_bits_to_f32(b)).cuda().to(torch.bfloat16) for b in W.gpt2_small_np()]
+    if wl.name == "llama3_70b":
+        return W.llama3_70b_torch()
+    raise ValueError(wl.name)
+
+
+def cpu_baseline(wl, Ms, seconds, torch):
+    """Oracle (fp64 numpy) on a bounded sample: whole matrices of the workload
+    in batch order until about `seconds` of CPU work; params/s = sampled
+    params / wall time."""
+    import numpy as np
+    from oracle import dion_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    kw = wl.ns_kwargs()
+    # sample: layer 0's k and v (1024x4096), then q (4096x4096), then o, ... until the budget
+    order = [1, 2, 0, 3, 4, 5, 6] if len(Ms) >= 7 else list(range(len(Ms)))
+    done, params, t_total = [], 0, 0.0
+    for i in order:
+        M = Ms[i].float().cpu().numpy()
+        t0 = time.perf_counter()
+        O.orthogonalize(M, **kw)
+        t_total += time.perf_counter() - t0
+        params += M.shape[0] * M.shape[1]
+        done.append(f"{M.shape[0]}x{M.shape[1]}")
+        if t_total >= seconds:
+            break
+    return {"value": params / t_total, "unit": "params/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(done)} whole matrices of layer 0 ({', '.join(done)}; {params/1e6:.1f}M params), "
+                      f"full fp64 Gram-NS with the workload's hyper-parameters, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the path shards by whole "
+                                   "matrix across GPUs, see DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+    import orthogonalized_optimizer_step_amd as dion
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    Ms = make_inputs(wl, torch)
+    step_mode = wl.name.endswith("rows")
+    orth = dion.Orthogonalizer(wl.shapes, "bf16", wl.coeffs, wl.n_iter, wl.restart_every, wl.restart_mask,
+                               wl.safety, wl.row_frac, "auto", device=dev, step_mode=step_mode)
+    if step_mode:
+        Es = [torch.zeros(M.shape, dtype=torch.float32, device=dev) for M in Ms]
+        outs = [torch.empty_like(M) for M in Ms]
+        call = lambda: orth.step(Es, Ms, outs, wl.beta)  # noqa: E731
+    else:
+        outs = [torch.empty_like(M) for M in Ms]
+        call = lambda: orth(Ms, outs)  # noqa: E731
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    dion.profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    recs = dion.profile_records()
+    dion.profile_enable(False)
+    ms_per_step = ms_total / args.steps
+    if args.profile:
+        print(json.dumps({"ms_per_step": ms_per_step}))
+        return
+
+    params = wl.params
+    useful = orth.useful_flops()
+    # per-phase aggregation
+    phases = {}
+    for name, ms, u, r, b in recs:
+        ph = phases.setdefault(name, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0})
+        ph["ms"] += ms
+        ph["launches"] += 1
+        ph["useful"] += u
+        ph["mfma"] += r
+        ph["bytes"] += b
+    gemm_names = [n for n, p in phases.items() if p["mfma"] > 0]
+    dom = max(gemm_names, key=lambda n: phases[n]["ms"])
+    d = phases[dom]
+    avg_ms = d["ms"] / d["launches"]
+    achieved = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
+    raw_total = sum(p["mfma"] for p in phases.values()) / args.steps
+    phase_summary = {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
+                         "launches_per_step": p["launches"] // args.steps,
+                         **({"useful_tflops": round(p["useful"] / (p["ms"] * 1e-3) / 1e12, 1),
+                             "mfma_tflops": round(p["mfma"] / (p["ms"] * 1e-3) / 1e12, 1)} if p["mfma"] else
+                            {"gbs": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1)})}
+                     for n, p in sorted(phases.items(), key=lambda kv: -kv[1]["ms"])}
+    value = params * args.steps / (ms_total * 1e-3)
+    line = {
+        "metric": "orthogonalized params/sec and MFMA TFLOP/s (% peak), Llama-8B layer set",
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {len(wl.shapes)} matrices, {params/1e9:.3f} G params, "
+                               f"K={wl.n_iter}, restart_every={wl.restart_every}, restart_mask={wl.restart_mask}, "
+                               f"safety={wl.safety}, row_frac={wl.row_frac}",
+                   "matrices": len(wl.shapes), "params": params, "n_iter": wl.n_iter},
+        "useful_tflops": useful / (ms_per_step * 1e-3) / 1e12,
+        "useful_pct_peak": 100.0 * useful / (ms_per_step * 1e-3) / 1e12 / PEAK_MFMA16_TFLOPS,
+        "mfma_tflops": raw_total / (ms_per_step * 1e-3) / 1e12,
+        "host_wall_s": wall,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_MFMA16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA16_TFLOPS, "traffic": None,
+                     "launch_ms": avg_ms, "useful_flops_per_launch": d["useful"] / d["launches"]},
+        "phases": phase_summary,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, Ms, args.cpu_sample_seconds, torch)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

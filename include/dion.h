@@ -156,6 +156,21 @@ double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_
  * 1e-6 relative shrink described above, clamped to [1, rows]; 0 if invalid. */
 int32_t dion_selected_rows(int32_t rows, float row_frac);
 
+/* Profiling for benchmarks.  While enabled, every phase that a call of the
+ * calling thread enqueues is bracketed by two hipEvents recorded on the
+ * call's own stream, so the durations are those of the kernels on that
+ * stream.  dion_profile_enable clears the records and returns the previous
+ * state.  Record i carries the phase name ("rowkeys", "momentum", "select",
+ * "pack", "syrk", "gram_poly", "sym_product", "apply", "transpose", "final",
+ * "copy_rows"), its elapsed milliseconds (waits for its end event), its
+ * useful FLOPs (symmetric products counted once), the MFMA FLOPs it executes
+ * (split terms and full diagonal tiles included) and its algorithmic HBM
+ * bytes (streaming phases).  Names are static strings. */
+int dion_profile_enable(int enable);
+int dion_profile_count(void);
+int dion_profile_get(int index, const char** name, float* ms, double* useful_flops,
+                     double* mfma_flops, double* bytes);
+
 /* Static message for a status code. */
 const char* dion_strerror(int status);
 /* Message describing the last error on the calling thread ("" if none). */

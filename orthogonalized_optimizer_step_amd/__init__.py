@@ -12,7 +12,7 @@ import ctypes
 from ._lib import DION_BF16, DION_FP32, PREC, DionError, DionParams, DionShape, check, lib
 
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
-           "DionError", "QUINTIC"]
+           "DionError", "QUINTIC", "profile_enable", "profile_records"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
@@ -166,3 +166,21 @@ def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart
     if not return_indices:
         return outs
     return outs, list(torch.split(sel, orth.selected))
+
+
+def profile_enable(on=True) -> bool:
+    """Start (clearing old records) or stop per-phase event profiling on this thread."""
+    return bool(lib.dion_profile_enable(1 if on else 0))
+
+
+def profile_records():
+    """[(name, ms, useful_flops, mfma_flops, bytes)] of the phases enqueued while profiling."""
+    recs = []
+    name = ctypes.c_char_p()
+    ms = ctypes.c_float()
+    u, r, b = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    for i in range(lib.dion_profile_count()):
+        check(lib.dion_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(u), ctypes.byref(r),
+                                   ctypes.byref(b)))
+        recs.append((name.value.decode(), ms.value, u.value, r.value, b.value))
+    return recs

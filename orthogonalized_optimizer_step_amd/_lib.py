@@ -36,7 +36,8 @@ class DionParams(ctypes.Structure):
 EXPORTS = (
     "dion_workspace_size", "dion_orth_batched", "dion_orth_batched_simple",
     "dion_rowsubset_step", "dion_useful_flops", "dion_selected_rows", "dion_strerror",
-    "dion_last_error", "dion_version",
+    "dion_last_error", "dion_version", "dion_profile_enable", "dion_profile_count",
+    "dion_profile_get",
 )
 
 
@@ -72,6 +73,14 @@ def _load():
     lib.dion_strerror.restype = ctypes.c_char_p
     lib.dion_last_error.argtypes = []
     lib.dion_last_error.restype = ctypes.c_char_p
+    lib.dion_profile_enable.argtypes = [ctypes.c_int]
+    lib.dion_profile_enable.restype = ctypes.c_int
+    lib.dion_profile_count.argtypes = []
+    lib.dion_profile_count.restype = ctypes.c_int
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.dion_profile_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                     dp, dp, dp]
+    lib.dion_profile_get.restype = ctypes.c_int
     lib.dion_version.argtypes = []
     lib.dion_version.restype = ctypes.c_int
     return lib

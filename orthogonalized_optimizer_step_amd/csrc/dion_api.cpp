@@ -144,6 +144,9 @@ struct Step {
   int table = 0;  // index into Plan::tabs
   PhaseArgs pa{};
   int src_slot = 0, dst_slot = 0;
+  // accounting for profiles: name, useful FLOPs, executed MFMA FLOPs, algorithmic bytes
+  const char* name = "";
+  double useful = 0, raw = 0, bytes = 0;
 };
 
 struct Table {  // a (matrix list, prefix) pair inside the int blob
@@ -189,7 +192,8 @@ int add_table(Plan& P, const std::vector<int>& mats, const std::vector<int>& cou
   return (int)P.tabs.size() - 1;
 }
 
-int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm, bool step_mode, Plan& P) {
+int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm, bool step_mode, Plan& P,
+               int grad_es = 2) {
   if (!shapes) return fail(DION_E_INVAL, "shapes is NULL");
   if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
   P.fp64 = prm.fp64;
@@ -290,18 +294,47 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.total = off;
 
   // ---------------------------------------------------------- phase list
+  const double in_es = step_mode ? 4.0 : (dtype == DION_BF16 ? 2.0 : 4.0);
+  double elems = 0, sel_elems = 0, pad_elems = 0, unsel_elems = 0, rows = (double)P.total_rows;
+  for (const MatPlan& mp : P.mats) {
+    elems += (double)mp.R * mp.C;
+    sel_elems += (double)mp.k * mp.C;
+    pad_elems += (double)mp.m_pad * mp.n_pad;
+    unsel_elems += (double)(mp.R - mp.k) * mp.C;
+  }
   Step st;
   st.kind = step_mode ? ST_MOMENTUM : ST_KEYS;
+  st.name = step_mode ? "momentum" : "rowkeys";
+  st.bytes = step_mode ? elems * (4 + 4 + grad_es + 2) + rows * 8 : elems * in_es + rows * 8;
   P.steps.push_back(st);
+  st = Step();
   st.kind = ST_SELECT;
+  st.name = "select";
+  st.bytes = rows * 8 * (P.use_idx ? 10 : 1) + rows;
   P.steps.push_back(st);
   st = Step();
   st.kind = ST_PACK;
+  st.name = "pack";
   st.table = t_pack;
+  st.bytes = sel_elems * in_es + pad_elems * es * (1 + P.xterms0);
   P.steps.push_back(st);
 
-  auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, PhaseArgs pa) {
+  // per-matrix useful FLOPs of a product kind; executed MFMA FLOPs from the tile table
+  auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, PhaseArgs pa, const char* name) {
     Step g;
+    g.name = name;
+    const Table& tb = P.tabs[table];
+    const int nprod = P.fp64 ? 1 : ((na == 2 && nb == 2) ? 3 : ((na == 2 || nb == 2) ? 2 : 1));
+    for (int j = 0; j < tb.nmat; ++j) {
+      const MatPlan& mp = P.mats[P.ints[tb.mats_off + j]];
+      const double m = mp.m, n = mp.n;
+      const int tiles = P.ints[tb.prefix_off + j + 1] - P.ints[tb.prefix_off + j];
+      const double K = pa.k_is_n ? mp.n_pad : mp.m_pad;
+      g.raw += (double)tiles * bm * bm * K * 2.0 * nprod;
+      if (sym && pa.k_is_n) g.useful += n * m * (m + 1);          // Gram
+      else if (sym) g.useful += m * m * (m + 1);                 // m x m chain
+      else g.useful += 2.0 * m * m * n;                          // apply / final
+    }
     g.kind = ST_GEMM;
     g.table = table;
     g.bm = bm;
@@ -324,7 +357,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pa.k_is_n = 1;
     pa.alpha = sG;
     pa.alpha_pow = 2;
-    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa);
+    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk");
   }
   std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
   int q_slot = -1, xt_slot = SLOT_XT0, xterms = P.xterms0;
@@ -349,7 +382,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.poly_c = (float)c;
       pa.aux_inv_scale = 1.0f / sG;
       pa.out_scale = sP;
-      gemm(t_sym, bm_sym, true, 2, 2, EPI_POLY, pa);
+      gemm(t_sym, bm_sym, true, 2, 2, EPI_POLY, pa, "gram_poly");
     }
     if (q_slot < 0) {
       q_slot = p_slot;
@@ -365,7 +398,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.b_slot = q_slot;
       pa.c_slot = qn;
       pa.alpha = sQn / (sP * sQ);
-      gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa);
+      gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa, "sym_product");
       freel.push_back(q_slot);
       q_slot = qn;
       sQ = sQn;
@@ -384,13 +417,15 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.a_rows_is_n = 1;
         pa.alpha = x_is_x0 ? sXn / sQ : sXn / (sXT * sQ);
         pa.alpha_pow = x_is_x0 ? 1 : 0;
-        gemm(t_xtq, bm_xtq, false, xterms, 1, EPI_RECT, pa);
+        gemm(t_xtq, bm_xtq, false, xterms, 1, EPI_RECT, pa, "apply");
       }
       Step tr;
       tr.kind = ST_TRANSPOSE;
       tr.table = t_tr;
       tr.src_slot = xt_new;
       tr.dst_slot = SLOT_X;
+      tr.name = "transpose";
+      tr.bytes = 2.0 * pad_elems * es;
       P.steps.push_back(tr);
       const float sGn = sc(sb_next * sb_next);
       {
@@ -399,7 +434,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.c_slot = g_slot;
         pa.k_is_n = 1;
         pa.alpha = sGn / (sXn * sXn);
-        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa);
+        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk");
       }
       sG = sGn;
       xt_slot = xt_new;
@@ -420,7 +455,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = g_slot;
         pa.c_slot = t_slot;
         pa.alpha = sT / (sP * sG);
-        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa);
+        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa, "sym_product");
       }
       const float sGn = sc(sb_next * sb_next);
       {
@@ -429,7 +464,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = t_slot;
         pa.c_slot = g_slot;
         pa.alpha = sGn / (sP * sT);
-        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa);
+        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa, "sym_product");
       }
       sG = sGn;
       freel.push_back(t_slot);
@@ -447,17 +482,19 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pw.b_slot = xt_slot;
     pw.b_rows_is_n = 1;
     pw.out_rows_are_m = 1;
-    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, xterms, EPI_OUT, pw);
+    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, xterms, EPI_OUT, pw, "final");
     PhaseArgs pt = pa;
     pt.a_slot = xt_slot;
     pt.b_slot = q_slot;
     pt.a_rows_is_n = 1;
     pt.out_rows_are_m = 0;
-    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, xterms, 1, EPI_OUT, pt);
+    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, xterms, 1, EPI_OUT, pt, "final");
   }
   if (P.use_idx && !step_mode) {
     Step cp;
     cp.kind = ST_COPY;
+    cp.name = "copy_rows";
+    cp.bytes = 2.0 * unsel_elems * in_es + rows;
     P.steps.push_back(cp);
   }
   return DION_OK;
@@ -495,6 +532,39 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
   if (hipEventRecord(S.ev[i], s) != hipSuccess) return fail(DION_E_HIP, "hipEventRecord failed");
   return DION_OK;
 }
+
+// ------------------------------------------------------------ profiling
+// While enabled, each phase launch of the calling thread is bracketed by two
+// hipEvents recorded on the call's stream; records keep the phase's
+// accounting so callers can turn durations into rates.
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+  double useful, raw, bytes;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void clear() {
+    for (auto& r : recs) {
+      pool.push_back(r.a);
+      pool.push_back(r.b);
+    }
+    recs.clear();
+  }
+};
+thread_local Profiler g_prof;
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const char* pa = (const char*)a;
@@ -547,6 +617,13 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
   const bool in_bf16 = step_mode ? false : dtype == DION_BF16;
 
   for (const Step& st : P.steps) {
+    ProfRec rec{st.name, nullptr, nullptr, st.useful, st.raw, st.bytes};
+    if (g_prof.on) {
+      rec.a = g_prof.get();
+      rec.b = g_prof.get();
+      if (!rec.a || !rec.b || hipEventRecord(rec.a, stream) != hipSuccess)
+        return fail(DION_E_HIP, "profiling event failed");
+    }
     switch (st.kind) {
       case ST_KEYS:
         launch_rowkeys(in_bf16, d_descs, batch, P.total_rows, d_keys, stream);
@@ -582,6 +659,10 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
       case ST_COPY:
         launch_copy_unselected(in_bf16, d_descs, batch, P.total_rows, d_flags, stream);
         break;
+    }
+    if (g_prof.on) {
+      if (hipEventRecord(rec.b, stream) != hipSuccess) return fail(DION_E_HIP, "profiling event failed");
+      g_prof.recs.push_back(rec);
     }
   }
   if (sel_idx) {
@@ -671,7 +752,7 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
   int rc = parse_params(p, DION_FP32, true, prm);
   if (rc) return rc;
   Plan P;
-  rc = build_plan(shapes, batch, DION_FP32, prm, true, P);
+  rc = build_plan(shapes, batch, DION_FP32, prm, true, P, grad_dtype == DION_BF16 ? 2 : 4);
   if (rc) return rc;
   if (!E || !grad) return fail(DION_E_INVAL, "E or grad pointer array is NULL");
   for (int i = 0; i < batch; ++i)
@@ -706,6 +787,30 @@ double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_
 int32_t dion_selected_rows(int32_t rows, float row_frac) {
   if (rows < 1 || !(row_frac > 0.f && row_frac <= 1.f)) return 0;
   return selected_count(rows, row_frac);
+}
+
+int dion_profile_enable(int enable) {
+  const int prev = g_prof.on ? 1 : 0;
+  g_prof.clear();
+  g_prof.on = enable != 0;
+  return prev;
+}
+
+int dion_profile_count(void) { return (int)g_prof.recs.size(); }
+
+int dion_profile_get(int i, const char** name, float* ms, double* useful_flops, double* mfma_flops,
+                     double* bytes) {
+  if (i < 0 || i >= (int)g_prof.recs.size()) return fail(DION_E_INVAL, "profile record out of range");
+  const ProfRec& r = g_prof.recs[i];
+  if (hipEventSynchronize(r.b) != hipSuccess) return fail(DION_E_HIP, "hipEventSynchronize failed");
+  float t = 0.f;
+  if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return fail(DION_E_HIP, "hipEventElapsedTime failed");
+  if (name) *name = r.name;
+  if (ms) *ms = t;
+  if (useful_flops) *useful_flops = r.useful;
+  if (mfma_flops) *mfma_flops = r.raw;
+  if (bytes) *bytes = r.bytes;
+  return DION_OK;
 }
 
 const char* dion_strerror(int status) {

@@ -21,6 +21,8 @@
 // with fp32 accumulation; an operand may carry two terms (hi + lo, the lo
 // term being the fp16 rounding of the residual), in which case the products
 // hi*hi + hi*lo + lo*hi are accumulated.  FP64 path: plain fp64 FMA tiles.
+#include <utility>
+
 #include "dion_internal.h"
 
 namespace dion {
@@ -45,18 +47,40 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b & 7) * per + (b >> 3);
 }
 
+// Tile order within a matrix: bands of GROUP tile-rows, each band walked
+// column by column, so the ~32 tiles an XCD runs at once share a few operand
+// panels (K-slices of them stay in that XCD's L2).  Symmetric outputs use the
+// same banding restricted to the upper triangle (ti <= tj).
+constexpr int GROUP = 8;
+
 __device__ __forceinline__ void decode_tile(bool sym, int local, int arows, int brows, int bm,
                                             int& ti, int& tj) {
+  const int TM = arows / bm, TN = brows / bm;
   if (sym) {
-    const int T = arows / bm;
-    int i = 0;
-    while (local >= T - i) { local -= T - i; ++i; }
-    ti = i;
-    tj = i + local;
+    int r0 = 0;
+    while (r0 < TM) {
+      const int r1 = min(TM, r0 + GROUP);
+      int band = 0;  // tiles of rows [r0, r1) with tj >= ti
+      for (int i = r0; i < r1; ++i) band += TN - i;
+      if (local < band) {
+        for (int j = r0;; ++j) {
+          const int cnt = min(j + 1, r1) - r0;  // rows i in [r0, r1) with i <= j
+          if (local < cnt) { ti = r0 + local; tj = j; return; }
+          local -= cnt;
+        }
+      }
+      local -= band;
+      r0 = r1;
+    }
+    ti = tj = 0;  // unreachable for local < T(T+1)/2
   } else {
-    const int tn = brows / bm;
-    ti = local / tn;
-    tj = local - ti * tn;
+    const int band_rows = GROUP;
+    const int band = local / (band_rows * TN);
+    const int r0 = band * band_rows;
+    const int rows = min(band_rows, TM - r0);
+    const int l = local - band * band_rows * TN;
+    tj = l / rows;
+    ti = r0 + l % rows;
   }
 }
 
@@ -137,6 +161,217 @@ __device__ __forceinline__ AT phase_alpha(const MatDesc& d, const PhaseArgs& pa,
   return a;
 }
 
+// ------------------------------------------------- strip-staged epilogue
+// Each wave turns its (WT x WT) sub-tile into stores 32 rows ("a strip") at a
+// time: the strip's fp32 values go to LDS row-major, then leave as 16-byte
+// chunks of 8 consecutive columns; for symmetric outputs the strip is written
+// again transposed and leaves as 16-byte chunks of the mirror rows.  Masks are
+// needed only on diagonal tiles (upper half + mirror of the strict upper half)
+// and at the valid edge of the final output.
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+
+__host__ __device__ constexpr int epi_wave_bytes(int wt) {
+  // max(row-major strip 32 x (wt+8), transposed strip wt x (32+4)) floats
+  return (32 * (wt + 8) > wt * 36 ? 32 * (wt + 8) : wt * 36) * 4;
+}
+
+__device__ __forceinline__ void split8(const float* v, half8v& h, half8v& l) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const _Float16 x = (_Float16)v[i];
+    h[i] = x;
+    l[i] = (_Float16)(v[i] - (float)x);
+  }
+}
+
+// 8 consecutive columns [col0, col0+8) of row `row` of an fp16 hi/lo matrix
+// (ld columns, lo term `ts` elements after hi); elements with !mask skipped.
+__device__ __forceinline__ void store8_split(_Float16* base, size_t ts, int ld, int row, int col0,
+                                             const float* v, unsigned mask) {
+  half8v h, l;
+  split8(v, h, l);
+  const size_t off = (size_t)row * ld + col0;
+  if (mask == 0xFFu) {
+    *(half8v*)(base + off) = h;
+    *(half8v*)(base + off + ts) = l;
+  } else if (mask) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (mask >> i & 1u) {
+        base[off + i] = h[i];
+        base[off + ts + i] = l[i];
+      }
+  }
+}
+
+// One strip (compile-time index A) of the epilogue.
+template <int BM, int EPI, int F, int A>
+__device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs& pa, float alpha, int arows,
+                                               int brows, int ti, int tj, int wm, int wn, int lane,
+                                               const floatx16 (&acc)[F][F], float* st) {
+  constexpr int WT = F * 32;
+  constexpr int SROW = WT + 8;   // row-major strip stride (floats)
+  constexpr int TROW = 36;       // transposed strip stride (floats)
+  constexpr bool SYMO = (EPI == EPI_SYM || EPI == EPI_POLY);
+  constexpr int a = A;
+  const bool diag = SYMO && ti == tj;
+  const int row_base = ti * BM + wm * WT;  // global row of the sub-tile
+  const int col_base = tj * BM + wn * WT;  // global col of the sub-tile
+  _Float16* C = (_Float16*)d.buf[pa.c_slot];
+  const size_t cts = SYMO ? (size_t)arows * arows : (size_t)arows * brows;
+  const int cld = SYMO ? arows : brows;
+
+  {
+    // ---- values of strip a, in the accumulator layout
+    float v[F][16];
+    if (EPI == EPI_POLY) {
+      // G[gi][gj] for 4 consecutive rows = G[gj][gi..gi+3] (G is symmetric);
+      // every load of the strip is issued before any store of it.
+      const _Float16* G = (const _Float16*)d.buf[pa.aux_slot];
+      half4 gh[F][4], gl[F][4];
+#pragma unroll
+      for (int b = 0; b < F; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int gi = row_base + a * 32 + g * 8 + (lane >> 5) * 4;
+          const int gj = col_base + b * 32 + (lane & 31);
+          const size_t off = (size_t)gj * arows + gi;
+          gh[b][g] = *(const half4*)(G + off);
+          gl[b][g] = *(const half4*)(G + off + cts);
+        }
+#pragma unroll
+      for (int b = 0; b < F; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int gi = row_base + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          const int gj = col_base + b * 32 + (lane & 31);
+          const float g = ((float)gh[b][e >> 2][e & 3] + (float)gl[b][e >> 2][e & 3]) * pa.aux_inv_scale;
+          float x = pa.poly_b * g + pa.poly_c * (acc[a][b][e] * alpha);
+          if (gi == gj) x += pa.poly_a;
+          x *= pa.out_scale;
+          v[b][e] = (gi < d.m && gj < d.m) ? x : 0.f;  // keep the zero padding
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < F; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[b][e] = acc[a][b][e] * alpha;
+    }
+
+    // ---- row-major strip -> direct stores
+#pragma unroll
+    for (int b = 0; b < F; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        st[((e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)) * SROW + b * 32 + (lane & 31)] = v[b][e];
+    __syncthreads();
+    constexpr int CPR = WT / 8;  // chunks per strip row
+#pragma unroll
+    for (int q0 = 0; q0 < 32 * CPR; q0 += 64) {
+      const int q = q0 + lane;
+      const int rr = q / CPR, c0 = (q % CPR) * 8;
+      float w[8];
+      *(float4*)&w[0] = *(const float4*)&st[rr * SROW + c0];
+      *(float4*)&w[4] = *(const float4*)&st[rr * SROW + c0 + 4];
+      const int gi = row_base + a * 32 + rr, gj0 = col_base + c0;
+      if (EPI == EPI_OUT) {
+        const int rows_valid = pa.out_rows_are_m ? d.m : d.n;
+        const int cols_valid = pa.out_rows_are_m ? d.n : d.m;
+        if (gi < rows_valid && gj0 < cols_valid) {
+          const int orow = pa.idx ? pa.idx[d.sel0 + gi] : gi;
+          const size_t o = (size_t)orow * d.C + gj0;
+          const bool full = gj0 + 8 <= cols_valid;
+          if (pa.out_fp32) {
+            float* out = (float*)d.out + o;
+            if (full && ((uintptr_t)out & 15) == 0) {
+              *(float4*)out = *(float4*)&w[0];
+              *(float4*)(out + 4) = *(float4*)&w[4];
+            } else {
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                if (gj0 + i < cols_valid) out[i] = w[i];
+            }
+          } else {
+            uint16_t* out = (uint16_t*)d.out + o;
+            if (full && ((uintptr_t)out & 15) == 0) {
+              uint4 pk;
+              pk.x = (uint32_t)f32_to_bf16_rne(w[0]) | ((uint32_t)f32_to_bf16_rne(w[1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16_rne(w[2]) | ((uint32_t)f32_to_bf16_rne(w[3]) << 16);
+              pk.z = (uint32_t)f32_to_bf16_rne(w[4]) | ((uint32_t)f32_to_bf16_rne(w[5]) << 16);
+              pk.w = (uint32_t)f32_to_bf16_rne(w[6]) | ((uint32_t)f32_to_bf16_rne(w[7]) << 16);
+              *(uint4*)out = pk;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                if (gj0 + i < cols_valid) out[i] = f32_to_bf16_rne(w[i]);
+            }
+          }
+        }
+      } else {
+        unsigned mask = 0xFFu;
+        if (diag) {  // columns >= row only
+          mask = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mask |= (gj0 + i >= gi ? 1u : 0u) << i;
+        }
+        store8_split(C, cts, cld, gi, gj0, w, mask);
+      }
+    }
+    __syncthreads();
+
+    if (SYMO) {
+      // ---- transposed strip -> mirror stores C[gj][gi..gi+7]
+#pragma unroll
+      for (int b = 0; b < F; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cc = b * 32 + (lane & 31);
+          const int r0 = g * 8 + (lane >> 5) * 4;
+          *(float4*)&st[cc * TROW + r0] =
+              make_float4(v[b][g * 4 + 0], v[b][g * 4 + 1], v[b][g * 4 + 2], v[b][g * 4 + 3]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int q0 = 0; q0 < 4 * WT; q0 += 64) {
+        const int q = q0 + lane;
+        const int cc = q >> 2, r0 = (q & 3) * 8;
+        float w[8];
+        *(float4*)&w[0] = *(const float4*)&st[cc * TROW + r0];
+        *(float4*)&w[4] = *(const float4*)&st[cc * TROW + r0 + 4];
+        const int gj = col_base + cc, gi0 = row_base + a * 32 + r0;
+        unsigned mask = 0xFFu;
+        if (diag) {  // mirror of the strict upper half: gj > gi
+          mask = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) mask |= (gj > gi0 + i ? 1u : 0u) << i;
+        } else if (ti == tj) {
+          mask = 0;
+        }
+        store8_split(C, cts, cld, gj, gi0, w, mask);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int BM, int EPI, int F, int... As>
+__device__ __forceinline__ void epilogue_all(const MatDesc& d, const PhaseArgs& pa, float alpha, int arows,
+                                             int brows, int ti, int tj, int wm, int wn, int lane,
+                                             const floatx16 (&acc)[F][F], float* st,
+                                             std::integer_sequence<int, As...>) {
+  (epilogue_strip<BM, EPI, F, As>(d, pa, alpha, arows, brows, ti, tj, wm, wn, lane, acc, st), ...);
+}
+
+template <int BM, int EPI, int F>
+__device__ __forceinline__ void epilogue_strips(const MatDesc& d, const PhaseArgs& pa, int mi, int arows,
+                                                int brows, int ti, int tj, int wm, int wn, int lane,
+                                                const floatx16 (&acc)[F][F], float* st) {
+  const float alpha = phase_alpha<float>(d, pa, mi);
+  epilogue_all<BM, EPI, F>(d, pa, alpha, arows, brows, ti, tj, wm, wn, lane, acc, st,
+                           std::make_integer_sequence<int, F>{});
+}
+
 // ------------------------------------------------------- MFMA16 GEMM kernel
 // 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BM/2)
 // sub-tile made of 32 x 32 MFMA blocks.  BK = 32: each operand row of the
@@ -148,12 +383,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
                                                    const int* __restrict__ mats,
                                                    const int* __restrict__ prefix, int nmat,
                                                    int total, PhaseArgs pa) {
-  constexpr int BK = 32;
-  constexpr int WT = BM / 2;           // wave tile
-  constexpr int F = WT / 32;           // MFMA blocks per wave dim
-  constexpr int CPT = BM * 4 / 256;    // 16-byte chunks per thread per operand term
   constexpr int NT = NA + NB;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2][NT][BM * BK];
+  constexpr int BK = NT == 2 ? 64 : 32;  // two operand arrays fit two 64-deep stages
+  constexpr int CPR = BK / 8;            // 16-byte chunks per operand row of a stage
+  constexpr int RSH = CPR == 4 ? 2 : 1;  // rows sharing a 256-byte bank window: 16 / CPR
+  constexpr int WT = BM / 2;             // wave tile
+  constexpr int F = WT / 32;             // MFMA blocks per wave dim
+  constexpr int CPT = BM * CPR / 256;    // chunks per thread per operand term
+  constexpr int MAIN_BYTES = 2 * NT * BM * BK * 2;
+  constexpr int EPI_BYTES = 4 * epi_wave_bytes(WT);
+  constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  auto lds = reinterpret_cast<_Float16 (*)[NT][BM * BK]>(smem);
 
   const int t = xcd_remap(blockIdx.x, total);
   if (t >= total) return;
@@ -180,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int ch = tid + 256 * q;
-      const int row = ch >> 2, c = ch & 3;
+      const int row = ch / CPR, c = ch % CPR;
       const size_t off = (size_t)row * K + k0 + c * 8;
 #pragma unroll
       for (int s = 0; s < NA; ++s) stage[s][q] = *(const half8*)(gA + s * a_ts + off);
@@ -192,8 +433,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int ch = tid + 256 * q;
-      const int row = ch >> 2, c = ch & 3;
-      const int pos = row * BK + ((c ^ ((row >> 2) & 3)) << 3);
+      const int row = ch / CPR, c = ch % CPR;
+      const int pos = row * BK + ((c ^ ((row >> RSH) & (CPR - 1))) << 3);
 #pragma unroll
       for (int s = 0; s < NT; ++s) *(half8*)&lds[buf][s][pos] = stage[s][q];
     }
@@ -215,15 +456,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
     const int cur = kt & 1;
     if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       half8 fa[NA][F], fb[NB][F];
       const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
       for (int f = 0; f < F; ++f) {
         const int ra = wm * WT + f * 32 + (lane & 31);
         const int rb = wn * WT + f * 32 + (lane & 31);
-        const int pa_ = ra * BK + ((chunk ^ ((ra >> 2) & 3)) << 3);
-        const int pb_ = rb * BK + ((chunk ^ ((rb >> 2) & 3)) << 3);
+        const int pa_ = ra * BK + ((chunk ^ ((ra >> RSH) & (CPR - 1))) << 3);
+        const int pb_ = rb * BK + ((chunk ^ ((rb >> RSH) & (CPR - 1))) << 3);
 #pragma unroll
         for (int s = 0; s < NA; ++s) fa[s][f] = *(const half8*)&lds[cur][s][pa_];
 #pragma unroll
@@ -245,19 +486,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
     __syncthreads();
   }
 
-  // epilogue: acc[a][b][e] holds C[row][col] with
+  // epilogue: acc[a][b][e] holds C[row][col] of the wave's sub-tile with
   //   row = a*32 + (e/4)*8 + (lane/32)*4 + e%4,  col = b*32 + lane%32
-  const float alpha = phase_alpha<float>(d, pa, mi);
-#pragma unroll
-  for (int a = 0; a < F; ++a)
-#pragma unroll
-    for (int b = 0; b < F; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = wm * WT + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        const int c = wn * WT + b * 32 + (lane & 31);
-        epilogue_elem<EPI, _Float16, float>(d, pa, arows, brows, ti, tj, BM, r, c, acc[a][b][e], alpha);
-      }
+  __syncthreads();  // the main-loop stages are dead; reuse LDS for staging
+  epilogue_strips<BM, EPI, F>(d, pa, mi, arows, brows, ti, tj, wm, wn, lane, acc,
+                              (float*)smem + wave * (epi_wave_bytes(WT) / 4));
 }
 
 // --------------------------------------------------------- FP64 GEMM kernel
