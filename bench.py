@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true",
-                    help="only run warmup + steps (for rocprofv3), no baseline")
+                    help="only run warmup + steps (for rocprofv3), no baseline; also runs one plain 1 GiB "
+                         "device copy so byte counters can be calibrated against a known size")
     return ap.parse_args()
 
 
@@ -112,6 +113,12 @@ def main():
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    if args.profile:  # calibration copy: reads and writes exactly 1 GiB
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     dion.profile_enable(True)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -30,6 +30,20 @@ namespace dion {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// Pointers read from descriptors are generic; loads through them become flat
+// loads, which count against the LDS wait counter too and would make every
+// LDS fragment wait also wait for the in-flight HBM loads.  Casting to the
+// global address space gives global loads tracked by vmcnt only.
+#define DION_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const T DION_GLOBAL* to_global(const T* p) {
+  return (const T DION_GLOBAL*)p;
+}
+template <typename T>
+__device__ __forceinline__ T DION_GLOBAL* to_global_w(T* p) {
+  return (T DION_GLOBAL*)p;
+}
+
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ int find_segment(const int* prefix, int n, int t) {
   int lo = 0, hi = n;  // prefix[lo] <= t < prefix[hi]
@@ -192,15 +206,16 @@ __device__ __forceinline__ void store8_split(_Float16* base, size_t ts, int ld, 
   half8v h, l;
   split8(v, h, l);
   const size_t off = (size_t)row * ld + col0;
+  _Float16 DION_GLOBAL* g = to_global_w(base);
   if (mask == 0xFFu) {
-    *(half8v*)(base + off) = h;
-    *(half8v*)(base + off + ts) = l;
+    *(half8v DION_GLOBAL*)(g + off) = h;
+    *(half8v DION_GLOBAL*)(g + off + ts) = l;
   } else if (mask) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (mask >> i & 1u) {
-        base[off + i] = h[i];
-        base[off + ts + i] = l[i];
+        g[off + i] = h[i];
+        g[off + ts + i] = l[i];
       }
   }
 }
@@ -237,8 +252,8 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
           const int gi = row_base + a * 32 + g * 8 + (lane >> 5) * 4;
           const int gj = col_base + b * 32 + (lane & 31);
           const size_t off = (size_t)gj * arows + gi;
-          gh[b][g] = *(const half4*)(G + off);
-          gl[b][g] = *(const half4*)(G + off + cts);
+          gh[b][g] = *to_global((const half4*)(G + off));
+          gl[b][g] = *to_global((const half4*)(G + off + cts));
         }
 #pragma unroll
       for (int b = 0; b < F; ++b)
@@ -373,28 +388,51 @@ __device__ __forceinline__ void epilogue_strips(const MatDesc& d, const PhaseArg
 }
 
 // ------------------------------------------------------- MFMA16 GEMM kernel
+// Global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane l of the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16).  Issued
+// through asm so that the compiler does not turn every barrier into a wait for
+// all copies in flight; completion is tracked by the explicit vmcnt waits of
+// the pipeline below (extra, untracked vector-memory operations only make the
+// compiler's own vmcnt waits stronger, never weaker, as vmcnt drains in order).
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds_addr)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BM/2)
-// sub-tile made of 32 x 32 MFMA blocks.  BK = 32: each operand row of the
-// stage is 64 bytes = four 16-byte chunks, stored in LDS with the chunk index
-// XOR-swizzled by (row >> 2) & 3 so that both the 16-byte chunk stores and
-// the 16-byte fragment reads of 8 (or 16) lanes hit distinct banks.
+// sub-tile made of 32 x 32 MFMA blocks.  The K loop is an S-stage pipeline of
+// LDS buffers filled by direct global -> LDS copies, S - 1 stages ahead of the
+// MFMAs, with one barrier per stage.  A stage holds BK columns of every operand
+// term (BK = 16 when there are four operand arrays, 32 otherwise); each stage
+// row is BK * 2 bytes of 16-byte chunks whose order is XOR-swizzled by the row
+// (the copy picks the global chunk that belongs in each lane's fixed LDS slot)
+// so that the 16-byte fragment reads of 8 or 16 lanes hit distinct banks.
 template <int BM, int NA, int NB, int EPI, bool SYM>
 __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ descs,
                                                    const int* __restrict__ mats,
                                                    const int* __restrict__ prefix, int nmat,
                                                    int total, PhaseArgs pa) {
   constexpr int NT = NA + NB;
-  constexpr int BK = NT == 2 ? 64 : 32;  // two operand arrays fit two 64-deep stages
-  constexpr int CPR = BK / 8;            // 16-byte chunks per operand row of a stage
-  constexpr int RSH = CPR == 4 ? 2 : 1;  // rows sharing a 256-byte bank window: 16 / CPR
-  constexpr int WT = BM / 2;             // wave tile
-  constexpr int F = WT / 32;             // MFMA blocks per wave dim
-  constexpr int CPT = BM * CPR / 256;    // chunks per thread per operand term
-  constexpr int MAIN_BYTES = 2 * NT * BM * BK * 2;
+  constexpr int BK = 32;
+  constexpr int SLOTS = BK / 8;              // 16-byte chunks per stage row
+  constexpr int RPW = 128 / BK;              // stage rows per 256-byte bank window
+  constexpr int TERM_BYTES = BM * BK * 2;    // one operand term of one stage
+  constexpr int STAGE_BYTES = NT * TERM_BYTES;
+  constexpr int S = 4 * STAGE_BYTES <= 160 * 1024 ? 4 : (3 * STAGE_BYTES <= 160 * 1024 ? 3 : 2);
+  constexpr int IPW = TERM_BYTES / 4096;     // 1 KB copies per wave per term per stage
+  constexpr int WT = BM / 2;                 // wave tile
+  constexpr int F = WT / 32;                 // MFMA blocks per wave dim
+  constexpr int MAIN_BYTES = S * STAGE_BYTES;
   constexpr int EPI_BYTES = 4 * epi_wave_bytes(WT);
   constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  auto lds = reinterpret_cast<_Float16 (*)[NT][BM * BK]>(smem);
+  static_assert(IPW >= 1 && S >= 2, "tile too small for the copy layout");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int t = xcd_remap(blockIdx.x, total);
   if (t >= total) return;
@@ -414,29 +452,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
-  // global -> register staging of one BK stage
-  half8 stage[NT][CPT];
-  auto gload = [&](int k0) {
+  // copies of stage `st` (LDS buffer) holding K columns [k0, k0 + BK)
+  auto issue = [&](int st, int k0) {
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int ch = tid + 256 * q;
-      const int row = ch / CPR, c = ch % CPR;
-      const size_t off = (size_t)row * K + k0 + c * 8;
+    for (int i = 0; i < IPW; ++i) {
+      const int blk = i * 4 + wave;               // 1 KB block of the term region
+      const int o = blk * 1024 + lane * 16;       // this lane's LDS byte offset in it
+      const int row = o / (BK * 2);
+      const int slot = (o % (BK * 2)) / 16;
+      const int chunk = slot ^ ((row / RPW) & (SLOTS - 1));
+      const size_t goff = (size_t)row * K + k0 + chunk * 8;
+      const uint32_t lb = lds0 + st * STAGE_BYTES + blk * 1024;
 #pragma unroll
-      for (int s = 0; s < NA; ++s) stage[s][q] = *(const half8*)(gA + s * a_ts + off);
+      for (int u = 0; u < NA; ++u)
+        dma16(gA + u * a_ts + goff, __builtin_amdgcn_readfirstlane(lb + u * TERM_BYTES));
 #pragma unroll
-      for (int s = 0; s < NB; ++s) stage[NA + s][q] = *(const half8*)(gB + s * b_ts + off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-      const int ch = tid + 256 * q;
-      const int row = ch / CPR, c = ch % CPR;
-      const int pos = row * BK + ((c ^ ((row >> RSH) & (CPR - 1))) << 3);
-#pragma unroll
-      for (int s = 0; s < NT; ++s) *(half8*)&lds[buf][s][pos] = stage[s][q];
+      for (int u = 0; u < NB; ++u)
+        dma16(gB + u * b_ts + goff, __builtin_amdgcn_readfirstlane(lb + (NA + u) * TERM_BYTES));
     }
   };
 
@@ -448,43 +482,64 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  // fragments of one 16-deep half-stage: A rows and B rows of every term
+  half8 fa0[NA][F], fb0[NB][F], fa1[NA][F], fb1[NB][F];
+  auto read_frags = [&](const _Float16* sb, int kk, half8 (&fa)[NA][F], half8 (&fb)[NB][F]) {
+    const int chunk = kk * 2 + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      half8 fa[NA][F], fb[NB][F];
-      const int chunk = kk * 2 + (lane >> 5);
+    for (int f = 0; f < F; ++f) {
+      const int ra = wm * WT + f * 32 + (lane & 31);
+      const int rb = wn * WT + f * 32 + (lane & 31);
+      const int pa_ = ra * BK + ((chunk ^ ((ra / RPW) & (SLOTS - 1))) << 3);
+      const int pb_ = rb * BK + ((chunk ^ ((rb / RPW) & (SLOTS - 1))) << 3);
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const int ra = wm * WT + f * 32 + (lane & 31);
-        const int rb = wn * WT + f * 32 + (lane & 31);
-        const int pa_ = ra * BK + ((chunk ^ ((ra >> RSH) & (CPR - 1))) << 3);
-        const int pb_ = rb * BK + ((chunk ^ ((rb >> RSH) & (CPR - 1))) << 3);
+      for (int u = 0; u < NA; ++u) fa[u][f] = *(const half8*)(sb + u * (TERM_BYTES / 2) + pa_);
 #pragma unroll
-        for (int s = 0; s < NA; ++s) fa[s][f] = *(const half8*)&lds[cur][s][pa_];
-#pragma unroll
-        for (int s = 0; s < NB; ++s) fb[s][f] = *(const half8*)&lds[cur][NA + s][pb_];
-      }
-#pragma unroll
-      for (int sa = 0; sa < NA; ++sa)
-#pragma unroll
-        for (int sb = 0; sb < NB; ++sb) {
-          if (sa + sb >= (NA > NB ? NA : NB)) continue;  // drop lo*lo
-#pragma unroll
-          for (int a = 0; a < F; ++a)
-#pragma unroll
-            for (int b = 0; b < F; ++b)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sa][a], fb[sb][b], acc[a][b], 0, 0, 0);
-        }
+      for (int u = 0; u < NB; ++u) fb[u][f] = *(const half8*)(sb + (NA + u) * (TERM_BYTES / 2) + pb_);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  };
+  auto mfma_block = [&](const half8 (&fa)[NA][F], const half8 (&fb)[NB][F]) {
+#pragma unroll
+    for (int sa = 0; sa < NA; ++sa)
+#pragma unroll
+      for (int sb2 = 0; sb2 < NB; ++sb2) {
+        if (sa + sb2 >= (NA > NB ? NA : NB)) continue;  // drop lo*lo
+#pragma unroll
+        for (int a = 0; a < F; ++a)
+#pragma unroll
+          for (int b = 0; b < F; ++b)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sa][a], fb[sb2][b], acc[a][b], 0, 0, 0);
+      }
+  };
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) issue(st, st * BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most (stages issued after it) copies remain
+    const int pend = min(S - 2, nk - 1 - kt);
+    if (pend <= 0) wait_vmcnt<0>();
+    else if (pend == 1) wait_vmcnt<NT * IPW>();
+    else wait_vmcnt<2 * NT * IPW>();
+    __syncthreads();  // every lane's copies landed; stage kt-1 is no longer read
+    if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
+    const _Float16* sb = (const _Float16*)(smem + (kt % S) * STAGE_BYTES);
+    // Software pipeline over the two 16-deep halves of a stage, fragments in
+    // registers: read half 0 of stage kt, run the MFMAs of half 1 of stage
+    // kt-1 (already in registers, so they cover the read latency and the
+    // barrier), read half 1 of stage kt, run the MFMAs of half 0.  The
+    // scheduling fences keep this order.
+    read_frags(sb, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt > 0) mfma_block(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(sb, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (nk > 0) mfma_block(fa1, fb1);
 
   // epilogue: acc[a][b][e] holds C[row][col] of the wave's sub-tile with
   //   row = a*32 + (e/4)*8 + (lane/32)*4 + e%4,  col = b*32 + lane%32
