@@ -37,6 +37,8 @@ def parse():
                                                                 "llama3_8b_rows"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print a text summary of the rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--profile", action="store_true",
                     help="only run warmup + steps (for rocprofv3), no baseline; also runs one plain 1 GiB "
                          "device copy so byte counters can be calibrated against a known size")
@@ -84,8 +86,96 @@ def cpu_baseline(wl, Ms, seconds, torch):
                       f"full fp64 Gram-NS with the workload's hyper-parameters, {t_total:.1f} s"}
 
 
+KERNEL_SOURCES = ("orthogonalized_optimizer_step_amd/csrc/gemm_kernels.hip",
+                  "orthogonalized_optimizer_step_amd/csrc/stream_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama3_8b_hbm_traffic.txt")
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def short_kernel(name):
+    """Kernel name without its parameter list (template arguments kept)."""
+    depth, out = 0, []
+    for ch in name:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).replace("void ", "").strip('"')
+
+
+def summarize(d):
+    """Text summary of rocprofv3 --output-format csv results under d: the
+    kernel statistics, or per-kernel averages of collected counters.  HBM
+    byte counters (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) are scaled by
+    what the same counter reads for the plain 1 GiB calibration copy that
+    bench.py --profile runs, and emitted as TRAFFIC lines for bench.py."""
+    import collections
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    ctrs = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        rows = list(csv.DictReader(open(stats[0])))
+        print(f"{'kernel':64s} {'calls':>6s} {'total ms':>10s} {'avg us':>11s} {'%':>6s}")
+        for r in rows:
+            print(f"{short_kernel(r['Name'])[:64]:64s} {int(r['Calls']):6d} {float(r['TotalDurationNs'])/1e6:10.3f} "
+                  f"{float(r['AverageNs'])/1e3:11.1f} {float(r['Percentage']):6.2f}")
+    for f in ctrs:
+        rows = list(csv.DictReader(open(f)))
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in rows:
+            agg[short_kernel(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        calib = {}
+        for k, cs in agg.items():
+            if "copyBuffer" in k:
+                for c, v in cs.items():
+                    big = [x for x in v if x > (1 << 19)]   # the 1 GiB copy, counters in KiB
+                    if big:
+                        calib[c] = (1 << 20) / max(big)      # true KiB / counted KiB
+        print(f"\n{'kernel':64s} {'counter':12s} {'dispatches':>10s} {'avg GiB/dispatch':>17s} {'scaled':>8s}")
+        for k, cs in sorted(agg.items()):
+            for c, v in sorted(cs.items()):
+                avg = sum(v) / len(v) / (1 << 20)
+                sc = calib.get(c, 1.0)
+                print(f"{k[:64]:64s} {c:12s} {len(v):10d} {avg:17.3f} {avg * sc:8.3f}")
+                if c in ("FETCH_SIZE", "WRITE_SIZE") and "dion::" in k:
+                    print("TRAFFIC " + json.dumps({"kernel": k, "counter": c, "bytes_per_dispatch": avg * sc * (1 << 30),
+                                                   "scale": sc, "sources_sha256": sources_sha256()}))
+        if calib:
+            print("\ncalibration (true / counted, from the 1 GiB copy): " +
+                  ", ".join(f"{c} x{v:.3f}" for c, v in calib.items()))
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch (fetch + write) of `kernel` from the committed
+    counter summary, or None if absent or taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = sources_sha256()
+    got = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("TRAFFIC {"):
+            t = json.loads(line[8:])
+            if t["kernel"] == kernel and t["sources_sha256"] == sha:
+                got[t["counter"]] = t["bytes_per_dispatch"]
+    if "FETCH_SIZE" in got and "WRITE_SIZE" in got:
+        return got["FETCH_SIZE"] + got["WRITE_SIZE"]
+    return None
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the path shards by whole "
                                    "matrix across GPUs, see DESIGN.md)"}))
@@ -142,8 +232,10 @@ def main():
     useful = orth.useful_flops()
     # per-phase aggregation
     phases = {}
-    for name, ms, u, r, b in recs:
-        ph = phases.setdefault(name, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0})
+    for name, kern, ms, u, r, b in recs:
+        ph = phases.setdefault(name, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0,
+                                      "kernels": set()})
+        ph["kernels"].add(kern)
         ph["ms"] += ms
         ph["launches"] += 1
         ph["useful"] += u
@@ -154,6 +246,12 @@ def main():
     d = phases[dom]
     avg_ms = d["ms"] / d["launches"]
     achieved = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
+    dom_kernel = sorted(d["kernels"])[0] if len(d["kernels"]) == 1 else None
+    # algorithmic HBM bytes of one m x m product over the batch: two operands
+    # and one result, each an fp16 hi/lo pair (4 bytes per element)
+    m_sel = [min(orth.selected[i], c) for i, (r, c) in enumerate(wl.shapes)]
+    alg_bytes = 12.0 * sum(float(m) * m for m in m_sel) if dom in ("sym_product",) else None
+    traffic = traffic_for(dom_kernel) if dom_kernel else None
     raw_total = sum(p["mfma"] for p in phases.values()) / args.steps
     phase_summary = {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
                          "launches_per_step": p["launches"] // args.steps,
@@ -183,9 +281,12 @@ def main():
         "useful_pct_peak": 100.0 * useful / (ms_per_step * 1e-3) / 1e12 / PEAK_MFMA16_TFLOPS,
         "mfma_tflops": raw_total / (ms_per_step * 1e-3) / 1e12,
         "host_wall_s": wall,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_MFMA16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA16_TFLOPS, "traffic": None,
-                     "launch_ms": avg_ms, "useful_flops_per_launch": d["useful"] / d["launches"]},
+        "roofline": {"bound": "mfma", "kernel": dom_kernel or dom, "phase": dom, "achieved": achieved,
+                     "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA16_TFLOPS,
+                     "traffic": traffic, "launch_ms": avg_ms,
+                     "useful_flops_per_launch": d["useful"] / d["launches"],
+                     "mfma_tflops": d["mfma"] / d["launches"] / (avg_ms * 1e-3) / 1e12,
+                     "algorithmic_bytes_per_launch": alg_bytes},
         "phases": phase_summary,
     }
     if not args.no_cpu_baseline:

@@ -162,14 +162,16 @@ int32_t dion_selected_rows(int32_t rows, float row_frac);
  * stream.  dion_profile_enable clears the records and returns the previous
  * state.  Record i carries the phase name ("rowkeys", "momentum", "select",
  * "pack", "syrk", "gram_poly", "sym_product", "apply", "transpose", "final",
- * "copy_rows"), its elapsed milliseconds (waits for its end event), its
- * useful FLOPs (symmetric products counted once), the MFMA FLOPs it executes
- * (split terms and full diagonal tiles included) and its algorithmic HBM
- * bytes (streaming phases).  Names are static strings. */
+ * "copy_rows"), the kernel instance it launched (as profilers print it, e.g.
+ * "dion::k_gemm16<256, 2, 2, 0, true>"), its elapsed milliseconds (waits for
+ * its end event), its useful FLOPs (symmetric products counted once), the
+ * MFMA FLOPs it executes (split terms and full diagonal tiles included) and
+ * its algorithmic HBM bytes (streaming phases).  Strings stay valid until the
+ * thread exits.  Any output pointer may be NULL. */
 int dion_profile_enable(int enable);
 int dion_profile_count(void);
-int dion_profile_get(int index, const char** name, float* ms, double* useful_flops,
-                     double* mfma_flops, double* bytes);
+int dion_profile_get(int index, const char** name, const char** kernel, float* ms,
+                     double* useful_flops, double* mfma_flops, double* bytes);
 
 /* Static message for a status code. */
 const char* dion_strerror(int status);

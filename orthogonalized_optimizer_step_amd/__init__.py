@@ -174,13 +174,13 @@ def profile_enable(on=True) -> bool:
 
 
 def profile_records():
-    """[(name, ms, useful_flops, mfma_flops, bytes)] of the phases enqueued while profiling."""
+    """[(name, kernel, ms, useful_flops, mfma_flops, bytes)] of the phases enqueued while profiling."""
     recs = []
-    name = ctypes.c_char_p()
+    name, kern = ctypes.c_char_p(), ctypes.c_char_p()
     ms = ctypes.c_float()
     u, r, b = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
     for i in range(lib.dion_profile_count()):
-        check(lib.dion_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(u), ctypes.byref(r),
-                                   ctypes.byref(b)))
-        recs.append((name.value.decode(), ms.value, u.value, r.value, b.value))
+        check(lib.dion_profile_get(i, ctypes.byref(name), ctypes.byref(kern), ctypes.byref(ms), ctypes.byref(u),
+                                   ctypes.byref(r), ctypes.byref(b)))
+        recs.append((name.value.decode(), kern.value.decode(), ms.value, u.value, r.value, b.value))
     return recs

@@ -78,8 +78,8 @@ def _load():
     lib.dion_profile_count.argtypes = []
     lib.dion_profile_count.restype = ctypes.c_int
     dp = ctypes.POINTER(ctypes.c_double)
-    lib.dion_profile_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
-                                     dp, dp, dp]
+    lib.dion_profile_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_char_p),
+                                     ctypes.POINTER(ctypes.c_float), dp, dp, dp]
     lib.dion_profile_get.restype = ctypes.c_int
     lib.dion_version.argtypes = []
     lib.dion_version.restype = ctypes.c_int

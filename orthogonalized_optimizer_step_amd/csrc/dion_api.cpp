@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <functional>
 #include <string>
 #include <vector>
@@ -539,9 +540,35 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
 // accounting so callers can turn durations into rates.
 struct ProfRec {
   const char* name;
+  const char* kernel;
   hipEvent_t a, b;
   double useful, raw, bytes;
 };
+
+// Name of the kernel instance a step launches, as the profiler prints it.
+const char* kernel_name(const Plan& P, const Step& st) {
+  thread_local std::deque<std::pair<std::string, std::string>> cache;  // stable addresses
+  std::string key;
+  switch (st.kind) {
+    case ST_KEYS: return "dion::k_rowkeys";
+    case ST_MOMENTUM: return "dion::k_momentum_keys";
+    case ST_SELECT: return "dion::k_select";
+    case ST_PACK: return "dion::k_pack";
+    case ST_TRANSPOSE: return "dion::k_transpose";
+    case ST_COPY: return "dion::k_copy_unselected";
+    case ST_GEMM:
+      if (P.fp64)
+        key = "dion::k_gemm64<" + std::to_string(st.epi) + ", " + (st.sym ? "true" : "false") + ">";
+      else
+        key = "dion::k_gemm16<" + std::to_string(st.bm) + ", " + std::to_string(st.na) + ", " +
+              std::to_string(st.nb) + ", " + std::to_string(st.epi) + ", " + (st.sym ? "true" : "false") + ">";
+      break;
+  }
+  for (auto& kv : cache)
+    if (kv.first == key) return kv.second.c_str();
+  cache.emplace_back(key, key);
+  return cache.back().second.c_str();
+}
 struct Profiler {
   bool on = false;
   std::vector<ProfRec> recs;
@@ -617,7 +644,8 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
   const bool in_bf16 = step_mode ? false : dtype == DION_BF16;
 
   for (const Step& st : P.steps) {
-    ProfRec rec{st.name, nullptr, nullptr, st.useful, st.raw, st.bytes};
+    ProfRec rec{st.name, nullptr, nullptr, nullptr, st.useful, st.raw, st.bytes};
+    if (g_prof.on) rec.kernel = kernel_name(P, st);
     if (g_prof.on) {
       rec.a = g_prof.get();
       rec.b = g_prof.get();
@@ -798,14 +826,15 @@ int dion_profile_enable(int enable) {
 
 int dion_profile_count(void) { return (int)g_prof.recs.size(); }
 
-int dion_profile_get(int i, const char** name, float* ms, double* useful_flops, double* mfma_flops,
-                     double* bytes) {
+int dion_profile_get(int i, const char** name, const char** kernel, float* ms, double* useful_flops,
+                     double* mfma_flops, double* bytes) {
   if (i < 0 || i >= (int)g_prof.recs.size()) return fail(DION_E_INVAL, "profile record out of range");
   const ProfRec& r = g_prof.recs[i];
   if (hipEventSynchronize(r.b) != hipSuccess) return fail(DION_E_HIP, "hipEventSynchronize failed");
   float t = 0.f;
   if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return fail(DION_E_HIP, "hipEventElapsedTime failed");
   if (name) *name = r.name;
+  if (kernel) *kernel = r.kernel;
   if (ms) *ms = t;
   if (useful_flops) *useful_flops = r.useful;
   if (mfma_flops) *mfma_flops = r.raw;

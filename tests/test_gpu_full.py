@@ -138,3 +138,47 @@ def test_llama3_8b_rows_update_parity(llama8b_rows):
     print("llama3_8b_rows selected-row rel err:", {k: f"{v:.2e}" for k, v in res["err"].items()})
     assert len(res["err"]) == 14
     assert max(res["err"].values()) <= TOL
+
+
+@pytest.fixture(scope="module")
+def llama70b_one_each():
+    """One matrix of each Llama-3-70B shape at full size (8192x8192,
+    1024x8192, 28672x8192, 8192x28672), heavy-tailed spectrum k^-1/2 with
+    random orthogonal factors from seeded QR; K=6, restarts every 2, safety
+    1.05, top 1/4 of rows, one megabatched call."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import orthogonalized_optimizer_step_amd as dion
+    from workloads import LLAMA3_70B_SHAPES, heavytail_torch
+    wl = WORKLOADS["llama3_70b"]
+    Ms = []
+    for si, (r, c) in enumerate(LLAMA3_70B_SHAPES):
+        Ms.append(heavytail_torch((5, si, 0), r, c))
+        torch.cuda.synchronize()
+        print(f"llama3_70b: generated {r}x{c}", flush=True)
+    outs = [torch.empty_like(M) for M in Ms]
+    orth = dion.Orthogonalizer([tuple(M.shape) for M in Ms], "bf16", wl.coeffs, wl.n_iter, wl.restart_every,
+                               wl.restart_mask, wl.safety, wl.row_frac)
+    sel = torch.empty(orth.total_selected, dtype=torch.int32, device="cuda")
+    orth(Ms, outs, sel)
+    torch.cuda.synchronize()
+    print("llama3_70b: megabatch done", flush=True)
+    offs = np.concatenate([[0], np.cumsum(orth.selected)])
+    idx = [sel[offs[i]:offs[i + 1]].cpu().numpy() for i in range(len(Ms))]
+    yield wl, Ms, outs, idx
+    del Ms, outs, orth
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("i", [1, 0, 3, 2])
+def test_llama3_70b_rowsubset(llama70b_one_each, i):
+    wl, Ms, outs, idx = llama70b_one_each
+    M = Ms[i].float().cpu().numpy()
+    assert selection_ok(idx[i], M, wl.row_frac)
+    ref, ref_idx = O.orthogonalize(M, **wl.ns_kwargs())
+    got = to_np(outs[i])
+    rest = np.setdiff1d(np.arange(M.shape[0]), ref_idx)
+    assert np.array_equal(got[rest], M[rest].astype(np.float64))   # raw rows carried verbatim
+    err = O.rel_frobenius(got[ref_idx], ref[ref_idx])
+    print(f"llama3_70b matrix {i} {M.shape}: selected-row rel err {err:.3e}")
+    assert err <= TOL
