@@ -48,6 +48,12 @@ class DionError(RuntimeError):
 
 
 def _load():
+    # PyTorch bundles its own HIP runtime (libamdhip64, libhsa-runtime64) under
+    # a file name that the dynamic linker does not match against ours: loading
+    # libdion.so first would bring /opt/rocm's runtime and torch would then add
+    # a second one to the process (the second sees no device).  Importing torch
+    # first makes libdion.so bind to the runtime already loaded.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m orthogonalized_optimizer_step_amd.build`")

@@ -383,7 +383,14 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.poly_c = (float)c;
       pa.aux_inv_scale = 1.0f / sG;
       pa.out_scale = sP;
-      gemm(t_sym, bm_sym, true, 2, 2, EPI_POLY, pa, "gram_poly");
+      // At the first iteration of a segment G comes straight from the Gram
+      // product and G*G takes G's hi term only (one MFMA term instead of
+      // three; the bG term of the epilogue still reads both).  Later in a
+      // segment G has been through P G P updates and the error of a
+      // one-term G*G compounds, so those use both terms.  Chosen by
+      // emulation against the oracle on the workloads' data.
+      const int gg = q_slot < 0 ? 1 : 2;
+      gemm(t_sym, bm_sym, true, gg, gg, EPI_POLY, pa, "gram_poly");
     }
     if (q_slot < 0) {
       q_slot = p_slot;
@@ -418,16 +425,20 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.a_rows_is_n = 1;
         pa.alpha = x_is_x0 ? sXn / sQ : sXn / (sXT * sQ);
         pa.alpha_pow = x_is_x0 ? 1 : 0;
-        gemm(t_xtq, bm_xtq, false, xterms, 1, EPI_RECT, pa, "apply");
+        // MFMA16: the epilogue also writes X (hi) transposed; FP64: a transpose pass
+        pa.aux_slot = SLOT_X;
+        gemm(t_xtq, bm_xtq, false, xterms, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply");
       }
-      Step tr;
-      tr.kind = ST_TRANSPOSE;
-      tr.table = t_tr;
-      tr.src_slot = xt_new;
-      tr.dst_slot = SLOT_X;
-      tr.name = "transpose";
-      tr.bytes = 2.0 * pad_elems * es;
-      P.steps.push_back(tr);
+      if (P.fp64) {
+        Step tr;
+        tr.kind = ST_TRANSPOSE;
+        tr.table = t_tr;
+        tr.src_slot = xt_new;
+        tr.dst_slot = SLOT_X;
+        tr.name = "transpose";
+        tr.bytes = 2.0 * pad_elems * es;
+        P.steps.push_back(tr);
+      }
       const float sGn = sc(sb_next * sb_next);
       {
         PhaseArgs pa{};
@@ -510,27 +521,34 @@ struct Stage {
 };
 thread_local Stage g_stage;
 
+int hip_fail(const char* what, hipError_t e) {
+  return fail(DION_E_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")");
+}
+
 int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
   Stage& S = g_stage;
   const int i = S.next;
   S.next ^= 1;
+  hipError_t e;
   if (S.ev[i]) {
-    if (hipEventSynchronize(S.ev[i]) != hipSuccess) return fail(DION_E_HIP, "hipEventSynchronize failed");
-  } else if (hipEventCreateWithFlags(&S.ev[i], hipEventDisableTiming) != hipSuccess) {
-    return fail(DION_E_HIP, "hipEventCreate failed");
+    if ((e = hipEventSynchronize(S.ev[i])) != hipSuccess) return hip_fail("hipEventSynchronize", e);
+  } else if ((e = hipEventCreateWithFlags(&S.ev[i], hipEventDisableTiming)) != hipSuccess) {
+    S.ev[i] = nullptr;
+    return hip_fail("hipEventCreateWithFlags", e);
   }
   if (S.cap[i] < bytes) {
-    if (S.host[i]) hipHostFree(S.host[i]);
+    if (S.host[i]) (void)hipHostFree(S.host[i]);
     S.host[i] = nullptr;
+    S.cap[i] = 0;
     const size_t cap = std::max(bytes, (size_t)1 << 16);
-    if (hipHostMalloc(&S.host[i], cap, hipHostMallocDefault) != hipSuccess)
-      return fail(DION_E_HIP, "hipHostMalloc of the upload stage failed");
+    if ((e = hipHostMalloc(&S.host[i], cap, hipHostMallocDefault)) != hipSuccess)
+      return hip_fail("hipHostMalloc of the upload stage", e);
     S.cap[i] = cap;
   }
   std::memcpy(S.host[i], src, bytes);
-  if (hipMemcpyAsync(dst, S.host[i], bytes, hipMemcpyHostToDevice, s) != hipSuccess)
-    return fail(DION_E_HIP, "hipMemcpyAsync of the plan failed");
-  if (hipEventRecord(S.ev[i], s) != hipSuccess) return fail(DION_E_HIP, "hipEventRecord failed");
+  if ((e = hipMemcpyAsync(dst, S.host[i], bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return hip_fail("hipMemcpyAsync of the plan", e);
+  if ((e = hipEventRecord(S.ev[i], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
   return DION_OK;
 }
 

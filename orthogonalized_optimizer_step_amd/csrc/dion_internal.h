@@ -53,7 +53,8 @@ enum Epi : int {
   EPI_SYM = 0,   // symmetric output: write the upper tile and its mirror
   EPI_POLY = 1,  // symmetric output P = a I + b G + c acc (G read from aux)
   EPI_RECT = 2,  // rectangular internal output
-  EPI_OUT = 3    // final output rows -> out[rowmap[r]] (masked to valid)
+  EPI_OUT = 3,   // final output rows -> out[rowmap[r]] (masked to valid)
+  EPI_RECT_T = 4 // EPI_RECT, plus the transposed hi term into aux (the Gram operand)
 };
 
 // Arguments of one GEMM phase: C = alpha * A B^T over a list of tiles.

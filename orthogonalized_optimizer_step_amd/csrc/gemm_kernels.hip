@@ -220,6 +220,14 @@ __device__ __forceinline__ void store8_split(_Float16* base, size_t ts, int ld, 
   }
 }
 
+// 8 consecutive columns of row `row`, hi term only (fp16).
+__device__ __forceinline__ void store8_hi(_Float16* base, int ld, int row, int col0, const float* v) {
+  half8v h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
+  *(half8v DION_GLOBAL*)(to_global_w(base) + (size_t)row * ld + col0) = h;
+}
+
 // One strip (compile-time index A) of the epilogue.
 template <int BM, int EPI, int F, int A>
 __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs& pa, float alpha, int arows,
@@ -229,6 +237,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
   constexpr int SROW = WT + 8;   // row-major strip stride (floats)
   constexpr int TROW = 36;       // transposed strip stride (floats)
   constexpr bool SYMO = (EPI == EPI_SYM || EPI == EPI_POLY);
+  constexpr bool TRANS = SYMO || EPI == EPI_RECT_T;  // also writes the transposed strip
   constexpr int a = A;
   const bool diag = SYMO && ti == tj;
   const int row_base = ti * BM + wm * WT;  // global row of the sub-tile
@@ -323,7 +332,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
             }
           }
         }
-      } else {
+      } else {  // EPI_SYM, EPI_POLY, EPI_RECT, EPI_RECT_T
         unsigned mask = 0xFFu;
         if (diag) {  // columns >= row only
           mask = 0;
@@ -335,8 +344,10 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
     }
     __syncthreads();
 
-    if (SYMO) {
-      // ---- transposed strip -> mirror stores C[gj][gi..gi+7]
+    if (TRANS) {
+      // ---- transposed strip -> mirror stores C[gj][gi..gi+7] (symmetric
+      // outputs), or the hi term of the transposed result into aux
+      // (X <- (X^T)^T after a restart, ld = arows)
 #pragma unroll
       for (int b = 0; b < F; ++b)
 #pragma unroll
@@ -355,15 +366,17 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
         *(float4*)&w[0] = *(const float4*)&st[cc * TROW + r0];
         *(float4*)&w[4] = *(const float4*)&st[cc * TROW + r0 + 4];
         const int gj = col_base + cc, gi0 = row_base + a * 32 + r0;
-        unsigned mask = 0xFFu;
-        if (diag) {  // mirror of the strict upper half: gj > gi
-          mask = 0;
+        if (EPI == EPI_RECT_T) {
+          store8_hi((_Float16*)d.buf[pa.aux_slot], arows, gj, gi0, w);
+        } else {
+          unsigned mask = 0xFFu;
+          if (diag) {  // mirror of the strict upper half: gj > gi
+            mask = 0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) mask |= (gj > gi0 + i ? 1u : 0u) << i;
-        } else if (ti == tj) {
-          mask = 0;
+            for (int i = 0; i < 8; ++i) mask |= (gj > gi0 + i ? 1u : 0u) << i;
+          }
+          store8_split(C, cts, cld, gj, gi0, w, mask);
         }
-        store8_split(C, cts, cld, gj, gi0, w, mask);
       }
       __syncthreads();
     }
@@ -619,12 +632,15 @@ bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& 
       case (1 << 8) | (1 << 4) | EPI_SYM: DION_G16(BM_, 1, 1, EPI_SYM, true); return true; \
       case (2 << 8) | (2 << 4) | EPI_SYM: DION_G16(BM_, 2, 2, EPI_SYM, true); return true; \
       case (2 << 8) | (2 << 4) | EPI_POLY: DION_G16(BM_, 2, 2, EPI_POLY, true); return true; \
+      case (1 << 8) | (1 << 4) | EPI_POLY: DION_G16(BM_, 1, 1, EPI_POLY, true); return true; \
       default: return false;                                                             \
     }                                                                                    \
   } else {                                                                               \
     switch (key) {                                                                       \
       case (1 << 8) | (1 << 4) | EPI_RECT: DION_G16(BM_, 1, 1, EPI_RECT, false); return true; \
       case (2 << 8) | (1 << 4) | EPI_RECT: DION_G16(BM_, 2, 1, EPI_RECT, false); return true; \
+      case (1 << 8) | (1 << 4) | EPI_RECT_T: DION_G16(BM_, 1, 1, EPI_RECT_T, false); return true; \
+      case (2 << 8) | (1 << 4) | EPI_RECT_T: DION_G16(BM_, 2, 1, EPI_RECT_T, false); return true; \
       case (1 << 8) | (1 << 4) | EPI_OUT: DION_G16(BM_, 1, 1, EPI_OUT, false); return true; \
       case (2 << 8) | (1 << 4) | EPI_OUT: DION_G16(BM_, 2, 1, EPI_OUT, false); return true; \
       case (1 << 8) | (2 << 4) | EPI_OUT: DION_G16(BM_, 1, 2, EPI_OUT, false); return true; \

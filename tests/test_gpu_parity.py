@@ -95,7 +95,7 @@ def test_small_ragged_mfma16(dion, sched):
     for M, o in zip(Ms, outs):
         ref, _ = O.orthogonalize(M, **kw)
         errs.append(O.rel_frobenius(to_np(o), ref))
-    print("MFMA16 small ragged", sched, " ".join(f"{e:.2e}" for e in errs))
+    print("MFMA16 small ragged", sched, " ".join(f"{e:.2e}" for e in errs), flush=True)
     assert max(errs) <= TOL_MFMA16
 
 
