@@ -86,8 +86,11 @@ def cpu_baseline(wl, Ms, seconds, torch):
                       f"full fp64 Gram-NS with the workload's hyper-parameters, {t_total:.1f} s"}
 
 
+# the kernels and the plan that decides what each launch of them covers
 KERNEL_SOURCES = ("orthogonalized_optimizer_step_amd/csrc/gemm_kernels.hip",
-                  "orthogonalized_optimizer_step_amd/csrc/stream_kernels.hip")
+                  "orthogonalized_optimizer_step_amd/csrc/stream_kernels.hip",
+                  "orthogonalized_optimizer_step_amd/csrc/dion_api.cpp",
+                  "orthogonalized_optimizer_step_amd/csrc/dion_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama3_8b_hbm_traffic.txt")
 
 
@@ -177,8 +180,8 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1 (the path shards by whole "
-                                   "matrix across GPUs, see DESIGN.md)"}))
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 (across GPUs the path would shard by "
+                                   "whole matrix, with no collective inside the orthogonalization)"}))
         sys.exit(2)
     import torch
     import orthogonalized_optimizer_step_amd as dion
@@ -241,17 +244,25 @@ def main():
         ph["useful"] += u
         ph["mfma"] += r
         ph["bytes"] += b
-    gemm_names = [n for n, p in phases.items() if p["mfma"] > 0]
-    dom = max(gemm_names, key=lambda n: phases[n]["ms"])
-    d = phases[dom]
+    # the roofline entry is for the kernel instance with the most GPU time
+    kernels = {}
+    for name, kern, ms, u, r, b in recs:
+        k = kernels.setdefault(kern, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0,
+                                      "phases": set()})
+        k["phases"].add(name)
+        k["ms"] += ms
+        k["launches"] += 1
+        k["useful"] += u
+        k["mfma"] += r
+        k["bytes"] += b
+    dom_kernel = max((k for k, v in kernels.items() if v["mfma"] > 0), key=lambda k: kernels[k]["ms"])
+    d = kernels[dom_kernel]
     avg_ms = d["ms"] / d["launches"]
     achieved = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
-    dom_kernel = sorted(d["kernels"])[0] if len(d["kernels"]) == 1 else None
-    # algorithmic HBM bytes of one m x m product over the batch: two operands
-    # and one result, each an fp16 hi/lo pair (4 bytes per element)
-    m_sel = [min(orth.selected[i], c) for i, (r, c) in enumerate(wl.shapes)]
-    alg_bytes = 12.0 * sum(float(m) * m for m in m_sel) if dom in ("sym_product",) else None
-    traffic = traffic_for(dom_kernel) if dom_kernel else None
+    # algorithmic HBM bytes per launch, from the plan: each operand term read
+    # once and the result written once
+    alg_bytes = d["bytes"] / d["launches"]
+    traffic = traffic_for(dom_kernel)
     raw_total = sum(p["mfma"] for p in phases.values()) / args.steps
     phase_summary = {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
                          "launches_per_step": p["launches"] // args.steps,
@@ -281,7 +292,8 @@ def main():
         "useful_pct_peak": 100.0 * useful / (ms_per_step * 1e-3) / 1e12 / PEAK_MFMA16_TFLOPS,
         "mfma_tflops": raw_total / (ms_per_step * 1e-3) / 1e12,
         "host_wall_s": wall,
-        "roofline": {"bound": "mfma", "kernel": dom_kernel or dom, "phase": dom, "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": dom_kernel, "phase": "+".join(sorted(d["phases"])),
+                     "achieved": achieved,
                      "peak": PEAK_MFMA16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA16_TFLOPS,
                      "traffic": traffic, "launch_ms": avg_ms,
                      "useful_flops_per_launch": d["useful"] / d["launches"],

@@ -253,6 +253,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   };
   const int bm_sym = pick_bm([&](int bm) { return sym_counts(bm); });
   const int bm_xtq = pick_bm([&](int bm) { return rect_counts(all, bm, true); });
+  auto full_counts = [&](int bm) {
+    std::vector<int> c(batch);
+    for (int i = 0; i < batch; ++i) { int T = P.mats[i].m_pad / bm; c[i] = T * T; }
+    return c;
+  };
+  const int bm_full = pick_bm([&](int bm) { return full_counts(bm); });
   std::vector<int> wide, tall;
   for (int i = 0; i < batch; ++i) (P.mats[i].tall ? tall : wide).push_back(i);
   const int bm_fin = pick_bm([&](int bm) {
@@ -262,6 +268,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   });
   const int t_sym = add_table(P, all, sym_counts(bm_sym));
   const int t_xtq = add_table(P, all, rect_counts(all, bm_xtq, true));
+  const int t_full = add_table(P, all, full_counts(bm_full));
   const int t_wide = add_table(P, wide, rect_counts(wide, bm_fin, false));
   const int t_tall = add_table(P, tall, rect_counts(tall, bm_fin, true));
   std::vector<int> pack_c(batch), tr_c(batch);
@@ -332,9 +339,22 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       const int tiles = P.ints[tb.prefix_off + j + 1] - P.ints[tb.prefix_off + j];
       const double K = pa.k_is_n ? mp.n_pad : mp.m_pad;
       g.raw += (double)tiles * bm * bm * K * 2.0 * nprod;
+      // an m x m chain product counts as the symmetric half however it is run
+      const bool mxm = !pa.k_is_n && !pa.a_rows_is_n && !pa.b_rows_is_n && epi != EPI_OUT;
       if (sym && pa.k_is_n) g.useful += n * m * (m + 1);          // Gram
-      else if (sym) g.useful += m * m * (m + 1);                 // m x m chain
+      else if (mxm) g.useful += m * m * (m + 1);                 // m x m chain
       else g.useful += 2.0 * m * m * n;                          // apply / final
+      // algorithmic HBM bytes on the padded layout: every operand term read
+      // once, the result written once (both triangles of a symmetric one)
+      const double ar = pa.a_rows_is_n ? mp.n_pad : mp.m_pad, br = pa.b_rows_is_n ? mp.n_pad : mp.m_pad;
+      const double el = P.fp64 ? 8.0 : 2.0, to = P.fp64 ? 1.0 : 2.0;
+      g.bytes += el * K * (ar * (P.fp64 ? 1 : na) + br * (P.fp64 ? 1 : nb));
+      const double mm = (double)mp.m_pad * mp.m_pad;
+      if (epi == EPI_SYM) g.bytes += el * to * mm;
+      else if (epi == EPI_POLY) g.bytes += 2.0 * el * to * mm;      // reads G, writes P
+      else if (epi == EPI_RECT) g.bytes += el * to * ar * br;
+      else if (epi == EPI_RECT_T) g.bytes += el * (to + 1.0) * ar * br;
+      else g.bytes += (pa.out_fp32 ? 4.0 : 2.0) * m * n;
     }
     g.kind = ST_GEMM;
     g.table = table;
@@ -365,8 +385,38 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   float sQ = 1.f, sXT = 1.f;
   double qb = 1.0;
   bool x_is_x0 = true;
+  int ct = 2;         // operand terms of the m x m chain products in this segment
+  bool full = false;  // one-term chain: P G and P Q as full (unmirrored) products
   for (int k = 1; k <= K; ++k) {
     const double a = prm.a[k - 1], b = prm.b[k - 1], c = prm.c[k - 1];
+    if (q_slot < 0) {
+      // A segment runs from a (re)start to the next restart or the last
+      // iteration.  The fp16 rounding of a one-term operand enters G through
+      // every P G P update and is amplified by the polynomial's slope at the
+      // small singular values, so it compounds with the segment's length: a
+      // segment of one or two iterations (at most one G update) takes
+      // one-term chain products, longer segments two terms.  The restart
+      // apply keeps X in two terms in every case.
+      //
+      // With one-term operands the products P G and P Q are run in full
+      // rather than as an upper triangle plus its mirror.  In exact
+      // arithmetic both are symmetric (P, G and Q are polynomials in the same
+      // Gram matrix), but their rounding errors are not: in the eigenbasis
+      // the error of entry (i, j) of P G carries the weights of row i, and the
+      // mirror copies the entries whose row is a small singular direction
+      // (where P is near its slope a = 3.4445 and Q near a^2) into the
+      // transposed position.  The next product (P T^T, or Q X in the apply)
+      // then multiplies that copy by the large singular values, which about
+      // doubles the output error.  Gram-shaped products (X X^T, G G, P T^T
+      // with T = P G) have errors symmetric in (i, j) and stay mirrored.
+      // Emulation against the oracle: 2.9e-3 to 3.5e-3 of relative error for
+      // one-term chains with the full products, 6e-3 to 9e-3 with mirrored
+      // ones, 2.9e-3 for two-term operands.
+      int e = k;
+      while (e < K && !prm.restart[e - 1]) ++e;
+      ct = e - k + 1 <= 2 ? 1 : 2;
+      full = !P.fp64 && ct == 1;
+    }
     const double gb = sb * sb;
     const double pb = poly_max(a, b, c, gb, 0), tb = poly_max(a, b, c, gb, 1);
     const double sb_next = sv_max(a, b, c, sb);
@@ -386,10 +436,10 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       // At the first iteration of a segment G comes straight from the Gram
       // product and G*G takes G's hi term only (one MFMA term instead of
       // three; the bG term of the epilogue still reads both).  Later in a
-      // segment G has been through P G P updates and the error of a
+      // long segment G has been through P G P updates and the error of a
       // one-term G*G compounds, so those use both terms.  Chosen by
       // emulation against the oracle on the workloads' data.
-      const int gg = q_slot < 0 ? 1 : 2;
+      const int gg = q_slot < 0 ? 1 : ct;
       gemm(t_sym, bm_sym, true, gg, gg, EPI_POLY, pa, "gram_poly");
     }
     if (q_slot < 0) {
@@ -406,7 +456,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.b_slot = q_slot;
       pa.c_slot = qn;
       pa.alpha = sQn / (sP * sQ);
-      gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa, "sym_product");
+      if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product");
+      else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product");
       freel.push_back(q_slot);
       q_slot = qn;
       sQ = sQn;
@@ -457,7 +508,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       if (p_slot != q_slot) freel.push_back(p_slot);
       q_slot = -1;
     } else {
-      // G <- P (P G)
+      // G <- P T^T with T = P G, i.e. P G P (each product reads B by rows: C = A B^T)
       const float sT = sc(tb);
       const int t_slot = freel.back();
       freel.pop_back();
@@ -467,7 +518,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = g_slot;
         pa.c_slot = t_slot;
         pa.alpha = sT / (sP * sG);
-        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa, "sym_product");
+        if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product");
+        else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product");
       }
       const float sGn = sc(sb_next * sb_next);
       {
@@ -476,7 +528,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = t_slot;
         pa.c_slot = g_slot;
         pa.alpha = sGn / (sP * sT);
-        gemm(t_sym, bm_sym, true, 2, 2, EPI_SYM, pa, "sym_product");
+        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product");
       }
       sG = sGn;
       freel.push_back(t_slot);
@@ -485,6 +537,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     sb = sb_next;
   }
   {  // out = Q X: wide matrices as Q * X, tall ones as X^T * Q
+    // After a short last segment X enters in its hi term only: Q's gain there
+    // is at most about a^2 and nothing amplifies the fp16 rounding of X
+    // afterwards (emulation: +1e-4 of relative error; a three-iteration last
+    // segment, gain a^3, gives +1.3e-3 and keeps both terms).
+    const int fx = full ? 1 : xterms;
     PhaseArgs pa{};
     pa.alpha = x_is_x0 ? 1.0f / sQ : 1.0f / (sQ * sXT);
     pa.alpha_pow = x_is_x0 ? 1 : 0;
@@ -494,13 +551,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pw.b_slot = xt_slot;
     pw.b_rows_is_n = 1;
     pw.out_rows_are_m = 1;
-    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, xterms, EPI_OUT, pw, "final");
+    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, fx, EPI_OUT, pw, "final");
     PhaseArgs pt = pa;
     pt.a_slot = xt_slot;
     pt.b_slot = q_slot;
     pt.a_rows_is_n = 1;
     pt.out_rows_are_m = 0;
-    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, xterms, 1, EPI_OUT, pt, "final");
+    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, fx, 1, EPI_OUT, pt, "final");
   }
   if (P.use_idx && !step_mode) {
     Step cp;
