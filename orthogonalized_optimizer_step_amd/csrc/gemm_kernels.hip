@@ -3,7 +3,9 @@
 // Every product of the iteration is C = alpha * A * B^T with both operands
 // stored row-major with the reduction dimension contiguous ("NT"):
 //   Gram        G = X X^T            (X: m x n)            symmetric output
-//   m x m chain G*G, P*Q, P*G, P*T   (symmetric, commuting) symmetric output
+//   m x m chain G*G, P*T^T           (symmetric, commuting) symmetric output
+//               P*G, P*Q^T           symmetric output for two-term operands,
+//                                    full (rectangular) for one-term ones
 //   apply       X'^T = X^T Q         (X^T: n x m, Q: m x m) rectangular
 //   final       out = Q X  or  X^T Q, scattered to the selected output rows
 // Symmetric outputs are computed on upper-triangle tiles only and written
@@ -401,31 +403,49 @@ __device__ __forceinline__ void epilogue_strips(const MatDesc& d, const PhaseArg
 }
 
 // ------------------------------------------------------- MFMA16 GEMM kernel
-// Global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane l of the wave writes LDS bytes [lds + 16 l, lds + 16 l + 16).  Issued
-// through asm so that the compiler does not turn every barrier into a wait for
-// all copies in flight; completion is tracked by the explicit vmcnt waits of
-// the pipeline below (extra, untracked vector-memory operations only make the
-// compiler's own vmcnt waits stronger, never weaker, as vmcnt drains in order).
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// Global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4,
+// scalar base + 32-bit per-lane byte offset): lane l of the wave writes LDS
+// bytes [lds + 16 l, lds + 16 l + 16).  Issued through asm so that the
+// compiler does not turn every barrier into a wait for all copies in flight;
+// completion is tracked by the explicit vmcnt waits of the pipeline.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gsrc), "s"(lds_addr)
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" : : : "memory"); }
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// products of the term pairs kept: (0,0), then (0,1) and (1,0) for two-term operands
+template <int NA, int NB> struct Prods {
+  static constexpr int n = (NA == 2 && NB == 2) ? 3 : ((NA == 2 || NB == 2) ? 2 : 1);
+  static constexpr int sa(int p) { return (NA == 2 && NB == 2) ? (p == 2 ? 1 : 0) : (NA == 2 ? p : 0); }
+  static constexpr int sb(int p) { return (NA == 2 && NB == 2) ? (p == 1 ? 1 : 0) : (NB == 2 ? p : 0); }
+};
 
 // 256 threads = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BM/2)
 // sub-tile made of 32 x 32 MFMA blocks.  The K loop is an S-stage pipeline of
-// LDS buffers filled by direct global -> LDS copies, S - 1 stages ahead of the
-// MFMAs, with one barrier per stage.  A stage holds BK columns of every operand
-// term (BK = 16 when there are four operand arrays, 32 otherwise); each stage
-// row is BK * 2 bytes of 16-byte chunks whose order is XOR-swizzled by the row
-// (the copy picks the global chunk that belongs in each lane's fixed LDS slot)
-// so that the 16-byte fragment reads of 8 or 16 lanes hit distinct banks.
+// LDS buffers filled by direct global -> LDS copies S - 1 stages ahead, one
+// barrier per stage.  A stage holds BK = 32 columns of every operand term;
+// each stage row is 64 bytes of 16-byte chunks whose order is XOR-swizzled by
+// the row so that the 16-byte fragment reads of 8 or 16 lanes hit distinct
+// banks.  Within a stage the two 16-deep halves are software-pipelined
+// through two register sets, and every LDS fragment read and every copy is
+// issued right after an MFMA, so that the matrix pipe stays fed while they go
+// out: the MFMAs of half 1 of stage k-1 carry the reads of half 0 of stage k
+// and the copies of stage k+S-1; the MFMAs of half 0 of stage k carry the
+// reads of half 1 of stage k.
 template <int BM, int NA, int NB, int EPI, bool SYM>
 __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ descs,
                                                    const int* __restrict__ mats,
@@ -441,10 +461,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   constexpr int IPW = TERM_BYTES / 4096;     // 1 KB copies per wave per term per stage
   constexpr int WT = BM / 2;                 // wave tile
   constexpr int F = WT / 32;                 // MFMA blocks per wave dim
+  constexpr int NMF = Prods<NA, NB>::n * F * F;  // MFMAs per half-stage
+  constexpr int NRD = NT * F;                // fragment reads per half-stage
+  constexpr int NDMA = IPW * NT;             // copies per stage per wave
   constexpr int MAIN_BYTES = S * STAGE_BYTES;
   constexpr int EPI_BYTES = 4 * epi_wave_bytes(WT);
   constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   static_assert(IPW >= 1 && S >= 2, "tile too small for the copy layout");
+  static_assert(NRD + NDMA <= 2 * NMF, "memory operations outnumber MFMA slots");
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int t = xcd_remap(blockIdx.x, total);
@@ -458,33 +482,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   int ti, tj;
   decode_tile(SYM, t - prefix[j], arows, brows, BM, ti, tj);
 
-  const _Float16* gA = (const _Float16*)d.buf[pa.a_slot] + (size_t)ti * BM * K;
-  const _Float16* gB = (const _Float16*)d.buf[pa.b_slot] + (size_t)tj * BM * K;
-  const size_t a_ts = (size_t)arows * K, b_ts = (size_t)brows * K;
+  const char* gA = (const char*)((const _Float16*)d.buf[pa.a_slot] + (size_t)ti * BM * K);
+  const char* gB = (const char*)((const _Float16*)d.buf[pa.b_slot] + (size_t)tj * BM * K);
+  const size_t a_ts = (size_t)arows * K * 2, b_ts = (size_t)brows * K * 2;   // term strides, bytes
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
-  // copies of stage `st` (LDS buffer) holding K columns [k0, k0 + BK)
-  auto issue = [&](int st, int k0) {
+  // per-lane byte offsets of the copies (same pattern for A and B tiles)
+  uint32_t voff[IPW];
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int blk = i * 4 + wave;               // 1 KB block of the term region
-      const int o = blk * 1024 + lane * 16;       // this lane's LDS byte offset in it
-      const int row = o / (BK * 2);
-      const int slot = (o % (BK * 2)) / 16;
-      const int chunk = slot ^ ((row / RPW) & (SLOTS - 1));
-      const size_t goff = (size_t)row * K + k0 + chunk * 8;
-      const uint32_t lb = lds0 + st * STAGE_BYTES + blk * 1024;
-#pragma unroll
-      for (int u = 0; u < NA; ++u)
-        dma16(gA + u * a_ts + goff, __builtin_amdgcn_readfirstlane(lb + u * TERM_BYTES));
-#pragma unroll
-      for (int u = 0; u < NB; ++u)
-        dma16(gB + u * b_ts + goff, __builtin_amdgcn_readfirstlane(lb + (NA + u) * TERM_BYTES));
-    }
+  for (int i = 0; i < IPW; ++i) {
+    const int o = (i * 4 + wave) * 1024 + lane * 16;  // this lane's LDS byte offset in the term region
+    const int row = o / (BK * 2);
+    const int slot = (o % (BK * 2)) / 16;
+    const int chunk = slot ^ ((row / RPW) & (SLOTS - 1));
+    voff[i] = (uint32_t)((row * K + chunk * 8) * 2);
+  }
+  // q-th copy of the stage held in LDS buffer st, K columns from k0
+  auto dma = [&](int q, int st, int k0) {
+    const int i = q / NT, u = q % NT;
+    const char* base = u < NA ? gA + u * a_ts : gB + (u - NA) * b_ts;
+    dma16s(voff[i], sgpr_ptr(base + (size_t)k0 * 2),
+           (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + st * STAGE_BYTES + (i * 4 + wave) * 1024 + u * TERM_BYTES));
   };
 
   floatx16 acc[F][F];
@@ -495,68 +518,96 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  // fragments of one 16-deep half-stage: A rows and B rows of every term
-  half8 fa0[NA][F], fb0[NB][F], fa1[NA][F], fb1[NB][F];
-  auto read_frags = [&](const _Float16* sb, int kk, half8 (&fa)[NA][F], half8 (&fb)[NB][F]) {
+  // per-lane LDS element offsets of the fragments (f = 0; +32 rows per f)
+  const int rowa = wm * WT + (lane & 31), rowb = wn * WT + (lane & 31);
+  const int swa = (rowa / RPW) & (SLOTS - 1), swb = (rowb / RPW) & (SLOTS - 1);
+  int offa[2], offb[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
     const int chunk = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const int ra = wm * WT + f * 32 + (lane & 31);
-      const int rb = wn * WT + f * 32 + (lane & 31);
-      const int pa_ = ra * BK + ((chunk ^ ((ra / RPW) & (SLOTS - 1))) << 3);
-      const int pb_ = rb * BK + ((chunk ^ ((rb / RPW) & (SLOTS - 1))) << 3);
-#pragma unroll
-      for (int u = 0; u < NA; ++u) fa[u][f] = *(const half8*)(sb + u * (TERM_BYTES / 2) + pa_);
-#pragma unroll
-      for (int u = 0; u < NB; ++u) fb[u][f] = *(const half8*)(sb + (NA + u) * (TERM_BYTES / 2) + pb_);
+    offa[kk] = rowa * BK + ((chunk ^ swa) << 3);
+    offb[kk] = rowb * BK + ((chunk ^ swb) << 3);
+  }
+  half8 fa[2][NA][F], fb[2][NB][F];   // two register sets of one half-stage's fragments
+  // q-th fragment read of half kk of the stage at sb into register set r
+  auto rd = [&](int q, const _Float16* sb, int kk, int r) {
+    if (q < NA * F) {
+      const int u = q / F, f = q % F;
+      fa[r][u][f] = *(const half8*)(sb + u * (TERM_BYTES / 2) + offa[kk] + f * 32 * BK);
+    } else {
+      const int q2 = q - NA * F, u = q2 / F, f = q2 % F;
+      fb[r][u][f] = *(const half8*)(sb + (NA + u) * (TERM_BYTES / 2) + offb[kk] + f * 32 * BK);
     }
   };
-  auto mfma_block = [&](const half8 (&fa)[NA][F], const half8 (&fb)[NB][F]) {
-#pragma unroll
-    for (int sa = 0; sa < NA; ++sa)
-#pragma unroll
-      for (int sb2 = 0; sb2 < NB; ++sb2) {
-        if (sa + sb2 >= (NA > NB ? NA : NB)) continue;  // drop lo*lo
-#pragma unroll
-        for (int a = 0; a < F; ++a)
-#pragma unroll
-          for (int b = 0; b < F; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[sa][a], fb[sb2][b], acc[a][b], 0, 0, 0);
-      }
+  auto mf = [&](int q, int r) {
+    const int p = q / (F * F), a = (q / F) % F, b = q % F;
+    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[r][Prods<NA, NB>::sa(p)][a], fb[r][Prods<NA, NB>::sb(p)][b],
+                                                       acc[a][b], 0, 0, 0);
   };
 
-  const int nk = K / BK;
+  const int nk = K / BK;   // >= 8: every dimension is padded to a multiple of 256
+  const int klast = (nk - 1) * BK;
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
-    if (st < nk) issue(st, st * BK);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once at most (stages issued after it) copies remain
-    const int pend = min(S - 2, nk - 1 - kt);
-    if (pend <= 0) wait_vmcnt<0>();
-    else if (pend == 1) wait_vmcnt<NT * IPW>();
-    else wait_vmcnt<2 * NT * IPW>();
-    __syncthreads();  // every lane's copies landed; stage kt-1 is no longer read
-    if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
-    const _Float16* sb = (const _Float16*)(smem + (kt % S) * STAGE_BYTES);
-    // Software pipeline over the two 16-deep halves of a stage, fragments in
-    // registers: read half 0 of stage kt, run the MFMAs of half 1 of stage
-    // kt-1 (already in registers, so they cover the read latency and the
-    // barrier), read half 1 of stage kt, run the MFMAs of half 0.  The
-    // scheduling fences keep this order.
-    read_frags(sb, 0, fa0, fb0);
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) dma(q, st, st * BK);
+
+  // stage 0: wait, then read half 0 (set 0) and issue the copies of stage S-1
+  wait_vmcnt<(S - 2) * NDMA>();
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const _Float16* sb = (const _Float16*)smem;
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) rd(q, sb, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NDMA; ++q) dma(q, (S - 1) % S, min((S - 1) * BK, klast));
     __builtin_amdgcn_sched_barrier(0);
-    if (kt > 0) mfma_block(fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(sb, 1, fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
+    // MFMAs of half 0 (set 0) carry the reads of half 1 into set 1
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      mf(q, 0);
+      if (q < NRD) rd(q, sb, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (nk > 0) mfma_block(fa1, fb1);
+  for (int kt = 1; kt < nk; ++kt) {
+    wait_lgkm0();                     // this wave's reads of stage kt-1 are done
+    wait_vmcnt<(S - 2) * NDMA>();     // this wave's copies of stage kt have landed
+    lds_barrier();                    // ... and every wave's
+    __builtin_amdgcn_sched_barrier(0);
+    const _Float16* sb = (const _Float16*)(smem + (kt % S) * STAGE_BYTES);
+    const int st_next = (kt + S - 1) % S;
+    const int k_next = min((kt + S - 1) * BK, klast);   // past the end: a harmless re-copy
+    // MFMAs of half 1 of stage kt-1 (set 1) carry the reads of half 0 of
+    // stage kt (set 0), then the copies of stage kt+S-1
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      mf(q, 1);
+      if (q < NRD) rd(q, sb, 0, 0);
+      else if (q - NRD < NDMA) dma(q - NRD, st_next, k_next);
+      if (NRD + NDMA > NMF && q + NMF < NRD + NDMA) {   // more operations than MFMAs: two per slot
+        const int q2 = q + NMF;
+        if (q2 < NRD) rd(q2, sb, 0, 0);
+        else dma(q2 - NRD, st_next, k_next);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // MFMAs of half 0 of stage kt (set 0) carry the reads of half 1 (set 1)
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      mf(q, 0);
+      if (q < NRD) rd(q, sb, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NMF; ++q) mf(q, 1);
 
   // epilogue: acc[a][b][e] holds C[row][col] of the wave's sub-tile with
   //   row = a*32 + (e/4)*8 + (lane/32)*4 + e%4,  col = b*32 + lane%32
-  __syncthreads();  // the main-loop stages are dead; reuse LDS for staging
+  wait_vmcnt<0>();    // the re-copies past the end land before LDS is reused
+  __syncthreads();
   epilogue_strips<BM, EPI, F>(d, pa, mi, arows, brows, ti, tj, wm, wn, lane, acc,
                               (float*)smem + wave * (epi_wave_bytes(WT) / 4));
 }
