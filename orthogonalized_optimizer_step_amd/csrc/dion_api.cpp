@@ -32,8 +32,8 @@ void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* 
                    MatScalars* scalars, bool fp64_path, hipStream_t s);
 void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
                  const int* idx, const MatScalars* scalars, int xterms, bool use_idx, hipStream_t s);
-void launch_transpose(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
-                      int src_slot, int dst_slot, hipStream_t s);
+void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int total, int src_slot, int dst_slot,
+                      hipStream_t s);
 void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
                             hipStream_t s);
 }  // namespace dion
@@ -745,7 +745,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
       }
       case ST_TRANSPOSE: {
         const Table& t = P.tabs[st.table];
-        launch_transpose(P.fp64, d_descs, d_ints + t.prefix_off, t.nmat, t.total, st.src_slot, st.dst_slot, stream);
+        launch_transpose(d_descs, d_ints + t.prefix_off, t.nmat, t.total, st.src_slot, st.dst_slot, stream);
         break;
       }
       case ST_GEMM: {

@@ -12,6 +12,21 @@ constexpr int PAD = 256;
 
 inline __host__ __device__ int pad_up(int x) { return (x + PAD - 1) / PAD * PAD; }
 
+// Element offset of (r, c) in an fp16 workspace matrix with ld columns (MFMA16
+// path; ld a multiple of 32, rows a multiple of 256).  The matrix is stored
+// panel-blocked: blocks of 256 rows x 32 columns, each contiguous (8192
+// elements), ordered by row-block, then column-block.  Inside a block, row r
+// holds its 32 columns as four 8-element chunks, chunk j at position
+// j ^ ((r / 4) & 3).  One K-stage (32 columns) of a GEMM tile's operand is
+// then one contiguous run of whole cache lines, and a linear global -> LDS
+// copy of it lands in the XOR-swizzled layout the MFMA fragment reads want.
+// 8-column groups starting at a multiple of 8 stay contiguous.  FP64 path
+// buffers are plain row-major.
+inline __host__ __device__ size_t blk_off(int r, int c, int ld) {
+  return ((size_t)(r >> 8) * (size_t)(ld >> 5) + (size_t)(c >> 5)) * 8192u + (size_t)(r & 255) * 32u +
+         (size_t)(((((unsigned)c >> 3) & 3u) ^ (((unsigned)r >> 2) & 3u)) << 3) + (size_t)(c & 7);
+}
+
 // Buffer slots of a matrix's workspace region.
 enum Slot : int {
   SLOT_X = 0,   // [m_pad][n_pad] hi: Gram (SYRK) operand

@@ -201,13 +201,14 @@ __device__ __forceinline__ void split8(const float* v, half8v& h, half8v& l) {
   }
 }
 
-// 8 consecutive columns [col0, col0+8) of row `row` of an fp16 hi/lo matrix
-// (ld columns, lo term `ts` elements after hi); elements with !mask skipped.
+// 8 consecutive columns [col0, col0+8) of row `row` (col0 a multiple of 8) of
+// a panel-blocked fp16 hi/lo matrix (ld columns, lo term `ts` elements after
+// hi); elements with !mask skipped.
 __device__ __forceinline__ void store8_split(_Float16* base, size_t ts, int ld, int row, int col0,
                                              const float* v, unsigned mask) {
   half8v h, l;
   split8(v, h, l);
-  const size_t off = (size_t)row * ld + col0;
+  const size_t off = blk_off(row, col0, ld);
   _Float16 DION_GLOBAL* g = to_global_w(base);
   if (mask == 0xFFu) {
     *(half8v DION_GLOBAL*)(g + off) = h;
@@ -222,12 +223,12 @@ __device__ __forceinline__ void store8_split(_Float16* base, size_t ts, int ld, 
   }
 }
 
-// 8 consecutive columns of row `row`, hi term only (fp16).
+// 8 consecutive columns of row `row` of a panel-blocked matrix, hi term only.
 __device__ __forceinline__ void store8_hi(_Float16* base, int ld, int row, int col0, const float* v) {
   half8v h;
 #pragma unroll
   for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
-  *(half8v DION_GLOBAL*)(to_global_w(base) + (size_t)row * ld + col0) = h;
+  *(half8v DION_GLOBAL*)(to_global_w(base) + blk_off(row, col0, ld)) = h;
 }
 
 // One strip (compile-time index A) of the epilogue.
@@ -262,7 +263,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
         for (int g = 0; g < 4; ++g) {
           const int gi = row_base + a * 32 + g * 8 + (lane >> 5) * 4;
           const int gj = col_base + b * 32 + (lane & 31);
-          const size_t off = (size_t)gj * arows + gi;
+          const size_t off = blk_off(gj, gi, arows);   // 4 contiguous elements (gi % 4 == 0)
           gh[b][g] = *to_global((const half4*)(G + off));
           gl[b][g] = *to_global((const half4*)(G + off + cts));
         }
@@ -440,7 +441,9 @@ template <int NA, int NB> struct Prods {
 // barrier per stage.  A stage holds BK = 32 columns of every operand term;
 // each stage row is 64 bytes of 16-byte chunks whose order is XOR-swizzled by
 // the row so that the 16-byte fragment reads of 8 or 16 lanes hit distinct
-// banks.  Within a stage the two 16-deep halves are software-pipelined
+// banks.  The operands are stored panel-blocked with that swizzle applied
+// (blk_off), so one term of one stage is a single contiguous run of whole
+// cache lines that each lane copies 16 bytes of, linearly.  Within a stage the two 16-deep halves are software-pipelined
 // through two register sets, and every LDS fragment read and every copy is
 // issued right after an MFMA, so that the matrix pipe stays fed while they go
 // out: the MFMAs of half 1 of stage k-1 carry the reads of half 0 of stage k
@@ -482,8 +485,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   int ti, tj;
   decode_tile(SYM, t - prefix[j], arows, brows, BM, ti, tj);
 
-  const char* gA = (const char*)((const _Float16*)d.buf[pa.a_slot] + (size_t)ti * BM * K);
-  const char* gB = (const char*)((const _Float16*)d.buf[pa.b_slot] + (size_t)tj * BM * K);
+  // panel-blocked operands: the tile's rows start inside row-block (ti*BM)/256;
+  // stage kt is column-block kt, 16 KB further on per block (8 KB per tile
+  // when BM = 128, which covers half of the block's rows)
+  const char* gA = (const char*)((const _Float16*)d.buf[pa.a_slot] + blk_off(ti * BM, 0, K));
+  const char* gB = (const char*)((const _Float16*)d.buf[pa.b_slot] + blk_off(tj * BM, 0, K));
   const size_t a_ts = (size_t)arows * K * 2, b_ts = (size_t)brows * K * 2;   // term strides, bytes
 
   const int tid = threadIdx.x;
@@ -492,21 +498,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
-  // per-lane byte offsets of the copies (same pattern for A and B tiles)
+  // per-lane byte offsets of the copies: a stage of one term is a contiguous
+  // TERM_BYTES run of the blocked operand, copied linearly (same for A and B)
   uint32_t voff[IPW];
 #pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int o = (i * 4 + wave) * 1024 + lane * 16;  // this lane's LDS byte offset in the term region
-    const int row = o / (BK * 2);
-    const int slot = (o % (BK * 2)) / 16;
-    const int chunk = slot ^ ((row / RPW) & (SLOTS - 1));
-    voff[i] = (uint32_t)((row * K + chunk * 8) * 2);
-  }
+  for (int i = 0; i < IPW; ++i) voff[i] = (uint32_t)((i * 4 + wave) * 1024 + lane * 16);
   // q-th copy of the stage held in LDS buffer st, K columns from k0
   auto dma = [&](int q, int st, int k0) {
     const int i = q / NT, u = q % NT;
     const char* base = u < NA ? gA + u * a_ts : gB + (u - NA) * b_ts;
-    dma16s(voff[i], sgpr_ptr(base + (size_t)k0 * 2),
+    dma16s(voff[i], sgpr_ptr(base + (size_t)(k0 >> 5) * 16384),
            (uint32_t)__builtin_amdgcn_readfirstlane(lds0 + st * STAGE_BYTES + (i * 4 + wave) * 1024 + u * TERM_BYTES));
   };
 

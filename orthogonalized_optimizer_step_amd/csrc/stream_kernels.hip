@@ -320,14 +320,16 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
   for (int i = ty; i < 64; i += 4) {
     // SL row r0+i, column c0+tx
     const float v = tile[i][tx];
-    const size_t o1 = (size_t)(r0 + i) * c_pad + c0 + tx;
     // ST row c0+i, column r0+tx  (value S[r0+tx][c0+i])
     const float w = tile[tx][i];
-    const size_t o2 = (size_t)(c0 + i) * k_pad + r0 + tx;
-    if (sizeof(OutT) == 8) {
+    if (sizeof(OutT) == 8) {  // FP64 path: row-major
+      const size_t o1 = (size_t)(r0 + i) * c_pad + c0 + tx;
+      const size_t o2 = (size_t)(c0 + i) * k_pad + r0 + tx;
       ((double*)sl)[o1] = (double)v;
       ((double*)st)[o2] = (double)w;
-    } else {
+    } else {  // MFMA16 path: panel-blocked fp16
+      const size_t o1 = blk_off(r0 + i, c0 + tx, c_pad);
+      const size_t o2 = blk_off(c0 + i, r0 + tx, k_pad);
       const float vs = v * scale, ws = w * scale;
       const _Float16 vh = (_Float16)vs, wh = (_Float16)ws;
       ((_Float16*)sl)[o1] = vh;
@@ -339,7 +341,8 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
 }
 
 // ---------------------------------------------------------- transpose
-// X^T (hi term) [n_pad][m_pad] -> X [m_pad][n_pad], fp16 or fp64.
+// FP64 path: X^T [n_pad][m_pad] -> X [m_pad][n_pad], row-major (the MFMA16 path
+// writes X in the restart apply's epilogue).
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const MatDesc* __restrict__ descs,
                                                    const int* __restrict__ prefix, int nmat,
@@ -414,11 +417,10 @@ void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* 
   }
 }
 
-void launch_transpose(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
-                      int src_slot, int dst_slot, hipStream_t s) {
+void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int total, int src_slot, int dst_slot,
+                      hipStream_t s) {
   if (total <= 0) return;
-  if (fp64_path) hipLaunchKernelGGL(k_transpose<double>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, src_slot, dst_slot);
-  else hipLaunchKernelGGL(k_transpose<_Float16>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, src_slot, dst_slot);
+  hipLaunchKernelGGL(k_transpose<double>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, src_slot, dst_slot);
 }
 
 void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows,
