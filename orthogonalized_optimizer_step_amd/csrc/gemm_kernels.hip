@@ -443,12 +443,13 @@ template <int NA, int NB> struct Prods {
 // the row so that the 16-byte fragment reads of 8 or 16 lanes hit distinct
 // banks.  The operands are stored panel-blocked with that swizzle applied
 // (blk_off), so one term of one stage is a single contiguous run of whole
-// cache lines that each lane copies 16 bytes of, linearly.  Within a stage the two 16-deep halves are software-pipelined
-// through two register sets, and every LDS fragment read and every copy is
-// issued right after an MFMA, so that the matrix pipe stays fed while they go
-// out: the MFMAs of half 1 of stage k-1 carry the reads of half 0 of stage k
-// and the copies of stage k+S-1; the MFMAs of half 0 of stage k carry the
-// reads of half 1 of stage k.
+// cache lines that each lane copies 16 bytes of, linearly.  Within a stage the
+// two 16-deep halves are software-pipelined through two register sets, and
+// every LDS fragment read and every copy is issued right after an MFMA, so
+// that the matrix pipe stays fed while they go out: the MFMAs of half 1 of
+// stage k-1 carry the reads of half 0 of stage k, the MFMAs of half 0 of
+// stage k carry the reads of half 1, and the copies of stage k+S-1 ride in
+// between, one per two MFMAs over both halves.
 template <int BM, int NA, int NB, int EPI, bool SYM>
 __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ descs,
                                                    const int* __restrict__ mats,
@@ -471,7 +472,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   constexpr int EPI_BYTES = 4 * epi_wave_bytes(WT);
   constexpr int LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   static_assert(IPW >= 1 && S >= 2, "tile too small for the copy layout");
-  static_assert(NRD + NDMA <= 2 * NMF, "memory operations outnumber MFMA slots");
+  static_assert(NDMA % 2 == 0 && NDMA / 2 <= NMF / 2 && NRD <= NMF,
+                "every fragment read and copy needs an MFMA slot");
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int t = xcd_remap(blockIdx.x, total);
@@ -580,25 +582,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
     const _Float16* sb = (const _Float16*)(smem + (kt % S) * STAGE_BYTES);
     const int st_next = (kt + S - 1) % S;
     const int k_next = min((kt + S - 1) * BK, klast);   // past the end: a harmless re-copy
-    // MFMAs of half 1 of stage kt-1 (set 1) carry the reads of half 0 of
-    // stage kt (set 0), then the copies of stage kt+S-1
+    // Each half's MFMAs carry that half's fragment reads in even slots and
+    // half of the copies of stage kt+S-1 in odd slots, so copies leave at one
+    // per two MFMAs over the whole stage.  Copies of the second half may go
+    // out too: their buffer held stage kt-1, read and consumed by every wave
+    // before the barrier.
+    auto slot = [&](int q, int half, int r_set) {
+      if (q % 2 == 0 && q / 2 < NRD) rd(q / 2, sb, half, r_set);
+      if (q % 2 == 1) {
+        if (q / 2 < NDMA / 2) dma(half * (NDMA / 2) + q / 2, st_next, k_next);
+        if (NRD > NMF / 2 && q / 2 + NMF / 2 < NRD) rd(q / 2 + NMF / 2, sb, half, r_set);
+      }
+    };
+    // half 1 of stage kt-1 (set 1) carries the reads of half 0 of stage kt (set 0)
 #pragma unroll
     for (int q = 0; q < NMF; ++q) {
       mf(q, 1);
-      if (q < NRD) rd(q, sb, 0, 0);
-      else if (q - NRD < NDMA) dma(q - NRD, st_next, k_next);
-      if (NRD + NDMA > NMF && q + NMF < NRD + NDMA) {   // more operations than MFMAs: two per slot
-        const int q2 = q + NMF;
-        if (q2 < NRD) rd(q2, sb, 0, 0);
-        else dma(q2 - NRD, st_next, k_next);
-      }
+      slot(q, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // MFMAs of half 0 of stage kt (set 0) carry the reads of half 1 (set 1)
+    // half 0 of stage kt (set 0) carries the reads of half 1 of stage kt (set 1)
 #pragma unroll
     for (int q = 0; q < NMF; ++q) {
       mf(q, 0);
-      if (q < NRD) rd(q, sb, 1, 1);
+      slot(q, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
