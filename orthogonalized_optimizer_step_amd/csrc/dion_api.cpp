@@ -328,7 +328,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.steps.push_back(st);
 
   // per-matrix useful FLOPs of a product kind; executed MFMA FLOPs from the tile table
-  auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, PhaseArgs pa, const char* name) {
+  // out_lo: whether any later product or epilogue reads the lo term of this
+  // product's fp16 output (skipping it halves the output stores)
+  auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, PhaseArgs pa, const char* name,
+                  bool out_lo) {
+    pa.out_lo = out_lo ? 1 : 0;
     Step g;
     g.name = name;
     const Table& tb = P.tabs[table];
@@ -350,10 +354,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       const double el = P.fp64 ? 8.0 : 2.0, to = P.fp64 ? 1.0 : 2.0;
       g.bytes += el * K * (ar * (P.fp64 ? 1 : na) + br * (P.fp64 ? 1 : nb));
       const double mm = (double)mp.m_pad * mp.m_pad;
-      if (epi == EPI_SYM) g.bytes += el * to * mm;
-      else if (epi == EPI_POLY) g.bytes += 2.0 * el * to * mm;      // reads G, writes P
-      else if (epi == EPI_RECT) g.bytes += el * to * ar * br;
-      else if (epi == EPI_RECT_T) g.bytes += el * (to + 1.0) * ar * br;
+      const double tw = (P.fp64 || out_lo) ? to : 1.0;             // output terms written
+      if (epi == EPI_SYM) g.bytes += el * tw * mm;
+      else if (epi == EPI_POLY) g.bytes += el * (to + tw) * mm;     // reads G (both terms), writes P
+      else if (epi == EPI_RECT) g.bytes += el * tw * ar * br;
+      else if (epi == EPI_RECT_T) g.bytes += el * (tw + 1.0) * ar * br;
       else g.bytes += (pa.out_fp32 ? 4.0 : 2.0) * m * n;
     }
     g.kind = ST_GEMM;
@@ -378,7 +383,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pa.k_is_n = 1;
     pa.alpha = sG;
     pa.alpha_pow = 2;
-    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk");
+    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", true);
   }
   std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
   int q_slot = -1, xt_slot = SLOT_XT0, xterms = P.xterms0;
@@ -440,7 +445,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       // one-term G*G compounds, so those use both terms.  Chosen by
       // emulation against the oracle on the workloads' data.
       const int gg = q_slot < 0 ? 1 : ct;
-      gemm(t_sym, bm_sym, true, gg, gg, EPI_POLY, pa, "gram_poly");
+      gemm(t_sym, bm_sym, true, gg, gg, EPI_POLY, pa, "gram_poly", ct == 2);
     }
     if (q_slot < 0) {
       q_slot = p_slot;
@@ -456,8 +461,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.b_slot = q_slot;
       pa.c_slot = qn;
       pa.alpha = sQn / (sP * sQ);
-      if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product");
-      else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product");
+      if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product", false);
+      else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
       freel.push_back(q_slot);
       q_slot = qn;
       sQ = sQn;
@@ -478,7 +483,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.alpha_pow = x_is_x0 ? 1 : 0;
         // MFMA16: the epilogue also writes X (hi) transposed; FP64: a transpose pass
         pa.aux_slot = SLOT_X;
-        gemm(t_xtq, bm_xtq, false, xterms, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply");
+        // X^T is read in two terms by the next restart apply, or by the final
+        // apply, which takes its hi term only after a short last segment
+        int e2 = k + 1;
+        while (e2 < K && !prm.restart[e2 - 1]) ++e2;
+        const bool xt_lo = !(e2 == K && e2 - k <= 2);
+        gemm(t_xtq, bm_xtq, false, xterms, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply", xt_lo);
       }
       if (P.fp64) {
         Step tr;
@@ -497,7 +507,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.c_slot = g_slot;
         pa.k_is_n = 1;
         pa.alpha = sGn / (sXn * sXn);
-        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk");
+        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", true);
       }
       sG = sGn;
       xt_slot = xt_new;
@@ -518,8 +528,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = g_slot;
         pa.c_slot = t_slot;
         pa.alpha = sT / (sP * sG);
-        if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product");
-        else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product");
+        if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product", false);
+        else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
       }
       const float sGn = sc(sb_next * sb_next);
       {
@@ -528,7 +538,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = t_slot;
         pa.c_slot = g_slot;
         pa.alpha = sGn / (sP * sT);
-        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product");
+        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
       }
       sG = sGn;
       freel.push_back(t_slot);
@@ -551,13 +561,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pw.b_slot = xt_slot;
     pw.b_rows_is_n = 1;
     pw.out_rows_are_m = 1;
-    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, fx, EPI_OUT, pw, "final");
+    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, fx, EPI_OUT, pw, "final", false);
     PhaseArgs pt = pa;
     pt.a_slot = xt_slot;
     pt.b_slot = q_slot;
     pt.a_rows_is_n = 1;
     pt.out_rows_are_m = 0;
-    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, fx, 1, EPI_OUT, pt, "final");
+    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, fx, 1, EPI_OUT, pt, "final", false);
   }
   if (P.use_idx && !step_mode) {
     Step cp;

@@ -85,6 +85,7 @@ struct PhaseArgs {
   float aux_inv_scale;           // EPI_POLY: G = stored aux * aux_inv_scale
   int out_fp32;      // EPI_OUT: 1 -> fp32 output, 0 -> bf16
   int out_rows_are_m;  // EPI_OUT: 1 -> product rows index the m side
+  int out_lo;        // fp16 outputs: 1 -> store the lo term too, 0 -> hi only (no reader needs lo)
   const MatScalars* scalars;
   const int* idx;      // selected rows (global), NULL when row_frac == 1
 };

@@ -203,22 +203,22 @@ __device__ __forceinline__ void split8(const float* v, half8v& h, half8v& l) {
 
 // 8 consecutive columns [col0, col0+8) of row `row` (col0 a multiple of 8) of
 // a panel-blocked fp16 hi/lo matrix (ld columns, lo term `ts` elements after
-// hi); elements with !mask skipped.
+// hi; the lo term only if `lo`); elements with !mask skipped.
 __device__ __forceinline__ void store8_split(_Float16* base, size_t ts, int ld, int row, int col0,
-                                             const float* v, unsigned mask) {
+                                             const float* v, unsigned mask, bool lo) {
   half8v h, l;
   split8(v, h, l);
   const size_t off = blk_off(row, col0, ld);
   _Float16 DION_GLOBAL* g = to_global_w(base);
   if (mask == 0xFFu) {
     *(half8v DION_GLOBAL*)(g + off) = h;
-    *(half8v DION_GLOBAL*)(g + off + ts) = l;
+    if (lo) *(half8v DION_GLOBAL*)(g + off + ts) = l;
   } else if (mask) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (mask >> i & 1u) {
         g[off + i] = h[i];
-        g[off + ts + i] = l[i];
+        if (lo) g[off + ts + i] = l[i];
       }
   }
 }
@@ -230,6 +230,11 @@ __device__ __forceinline__ void store8_hi(_Float16* base, int ld, int row, int c
   for (int i = 0; i < 8; ++i) h[i] = (_Float16)v[i];
   *(half8v DION_GLOBAL*)(to_global_w(base) + blk_off(row, col0, ld)) = h;
 }
+
+// The epilogue's LDS staging area is private to each wave, and a wave's LDS
+// operations execute in issue order, so handing values between its lanes
+// through LDS needs only to keep the compiler from reordering the accesses.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("" : : : "memory"); }
 
 // One strip (compile-time index A) of the epilogue.
 template <int BM, int EPI, int F, int A>
@@ -292,7 +297,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         st[((e >> 2) * 8 + (lane >> 5) * 4 + (e & 3)) * SROW + b * 32 + (lane & 31)] = v[b][e];
-    __syncthreads();
+    wave_lds_sync();
     constexpr int CPR = WT / 8;  // chunks per strip row
 #pragma unroll
     for (int q0 = 0; q0 < 32 * CPR; q0 += 64) {
@@ -342,10 +347,10 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
 #pragma unroll
           for (int i = 0; i < 8; ++i) mask |= (gj0 + i >= gi ? 1u : 0u) << i;
         }
-        store8_split(C, cts, cld, gi, gj0, w, mask);
+        store8_split(C, cts, cld, gi, gj0, w, mask, pa.out_lo != 0);
       }
     }
-    __syncthreads();
+    wave_lds_sync();
 
     if (TRANS) {
       // ---- transposed strip -> mirror stores C[gj][gi..gi+7] (symmetric
@@ -360,7 +365,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
           *(float4*)&st[cc * TROW + r0] =
               make_float4(v[b][g * 4 + 0], v[b][g * 4 + 1], v[b][g * 4 + 2], v[b][g * 4 + 3]);
         }
-      __syncthreads();
+      wave_lds_sync();
 #pragma unroll
       for (int q0 = 0; q0 < 4 * WT; q0 += 64) {
         const int q = q0 + lane;
@@ -378,10 +383,10 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
 #pragma unroll
             for (int i = 0; i < 8; ++i) mask |= (gj > gi0 + i ? 1u : 0u) << i;
           }
-          store8_split(C, cts, cld, gj, gi0, w, mask);
+          store8_split(C, cts, cld, gj, gi0, w, mask, pa.out_lo != 0);
         }
       }
-      __syncthreads();
+      wave_lds_sync();
     }
   }
 }
