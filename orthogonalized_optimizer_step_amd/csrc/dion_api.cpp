@@ -638,7 +638,7 @@ const char* kernel_name(const Plan& P, const Step& st) {
     case ST_KEYS: return "dion::k_rowkeys";
     case ST_MOMENTUM: return "dion::k_momentum_keys";
     case ST_SELECT: return "dion::k_select";
-    case ST_PACK: return "dion::k_pack";
+    case ST_PACK: return P.fp64 ? "dion::k_pack" : "dion::k_pack16";
     case ST_TRANSPOSE: return "dion::k_transpose";
     case ST_COPY: return "dion::k_copy_unselected";
     case ST_GEMM:

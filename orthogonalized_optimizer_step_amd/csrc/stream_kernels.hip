@@ -275,8 +275,11 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const MatDesc* __restric
 // wide (k <= C): X = SL, X^T = ST;  tall: X = ST, X^T = SL.
 // The Gram operand X keeps one term; X^T keeps `xterms` terms (hi, lo).
 // MFMA16 values are S * 2^e rounded to fp16 (exact for bf16 input within
-// fp16's normal range); FP64 values are S exactly.  64 x 64 tiles via LDS.
-template <typename InT, typename OutT>
+// fp16's normal range), panel-blocked; FP64 values are S exactly, row-major.
+// 64 x 64 tiles via LDS.
+
+// FP64 path.
+template <typename InT>
 __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
                                               const int* __restrict__ prefix, int nmat, int total,
                                               const int* __restrict__ idx_all,
@@ -296,7 +299,6 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
   const int c_pad = d.tall ? d.m_pad : d.n_pad;
   const int tc = c_pad / 64;
   const int r0 = (local / tc) * 64, c0 = (local % tc) * 64;
-  const float scale = ldexpf(1.0f, scalars[lo].e);
   const int* idx = idx_all + d.sel0;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 
@@ -312,31 +314,104 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
     tile[i][tx] = v;
   }
   __syncthreads();
-  void* sl = d.tall ? d.buf[SLOT_XT0] : d.buf[SLOT_X];
-  void* st = d.tall ? d.buf[SLOT_X] : d.buf[SLOT_XT0];
-  const int sl_terms = d.tall ? xterms : 1;
-  const int st_terms = d.tall ? 1 : xterms;
-  const size_t ts = (size_t)k_pad * c_pad;
+  double* sl = (double*)(d.tall ? d.buf[SLOT_XT0] : d.buf[SLOT_X]);
+  double* st = (double*)(d.tall ? d.buf[SLOT_X] : d.buf[SLOT_XT0]);
   for (int i = ty; i < 64; i += 4) {
-    // SL row r0+i, column c0+tx
-    const float v = tile[i][tx];
-    // ST row c0+i, column r0+tx  (value S[r0+tx][c0+i])
-    const float w = tile[tx][i];
-    if (sizeof(OutT) == 8) {  // FP64 path: row-major
-      const size_t o1 = (size_t)(r0 + i) * c_pad + c0 + tx;
-      const size_t o2 = (size_t)(c0 + i) * k_pad + r0 + tx;
-      ((double*)sl)[o1] = (double)v;
-      ((double*)st)[o2] = (double)w;
-    } else {  // MFMA16 path: panel-blocked fp16
-      const size_t o1 = blk_off(r0 + i, c0 + tx, c_pad);
-      const size_t o2 = blk_off(c0 + i, r0 + tx, k_pad);
-      const float vs = v * scale, ws = w * scale;
-      const _Float16 vh = (_Float16)vs, wh = (_Float16)ws;
-      ((_Float16*)sl)[o1] = vh;
-      ((_Float16*)st)[o2] = wh;
-      if (sl_terms > 1) ((_Float16*)sl)[o1 + ts] = (_Float16)(vs - (float)vh);
-      if (st_terms > 1) ((_Float16*)st)[o2 + ts] = (_Float16)(ws - (float)wh);
+    sl[(size_t)(r0 + i) * c_pad + c0 + tx] = (double)tile[i][tx];   // SL row r0+i, column c0+tx
+    st[(size_t)(c0 + i) * k_pad + r0 + tx] = (double)tile[tx][i];   // ST row c0+i, column r0+tx
+  }
+}
+
+// MFMA16 path: 16-byte row loads (when rows are 16-byte aligned), SL stored
+// as 8-column chunks straight from registers, ST through a 64 x 65 fp32 LDS
+// tile read as 8-row column chunks (both LDS passes are bank-conflict-free).
+typedef _Float16 half8s __attribute__((ext_vector_type(8)));
+template <typename InT>
+__global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ descs,
+                                                const int* __restrict__ prefix, int nmat, int total,
+                                                const int* __restrict__ idx_all,
+                                                const MatScalars* __restrict__ scalars, int xterms,
+                                                int use_idx) {
+  __shared__ float tile[64][65];
+  const int t = blockIdx.x;
+  if (t >= total) return;
+  int lo = 0, hi = nmat;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid;
+  }
+  const MatDesc& d = descs[lo];
+  const int local = t - prefix[lo];
+  const int k_pad = d.tall ? d.n_pad : d.m_pad;
+  const int c_pad = d.tall ? d.m_pad : d.n_pad;
+  const int tc = c_pad / 64;
+  const int r0 = (local / tc) * 64, c0 = (local % tc) * 64;
+  const float scale = ldexpf(1.0f, scalars[lo].e);
+  const int* idx = idx_all + d.sel0;
+  _Float16* sl = (_Float16*)(d.tall ? d.buf[SLOT_XT0] : d.buf[SLOT_X]);
+  _Float16* st = (_Float16*)(d.tall ? d.buf[SLOT_X] : d.buf[SLOT_XT0]);
+  const bool sl_lo = d.tall && xterms > 1, st_lo = !d.tall && xterms > 1;
+  const size_t ts = (size_t)k_pad * c_pad;
+  const bool vec = (d.C & 7) == 0 && ((uintptr_t)d.M & 15) == 0;
+
+  auto split_store = [&](_Float16* base, size_t off, const float* v, bool with_lo) {
+    half8s h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h[i] = (_Float16)v[i];
+      l[i] = (_Float16)(v[i] - (float)h[i]);
     }
+    *(half8s*)(base + off) = h;
+    if (with_lo) *(half8s*)(base + off + ts) = l;
+  };
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = threadIdx.x + 256 * j;
+    const int row = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + row, c = c0 + cc;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    if (r < d.k && c < d.C) {
+      const int src = use_idx ? idx[r] : r;
+      const InT* p = (const InT*)d.M + (int64_t)src * d.C + c;
+      if (vec) {  // c + 8 <= C: C and c are multiples of 8
+        if (sizeof(InT) == 2) {
+          const uint4 u = *(const uint4*)p;
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w4[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+          }
+        } else {
+          const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
+          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+          v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (c + i < d.C)
+            v[i] = sizeof(InT) == 2 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] *= scale;
+      tile[row][cc + i] = v[i];
+    }
+    split_store(sl, blk_off(r, c, c_pad), v, sl_lo);      // SL row r, columns c..c+7
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = threadIdx.x + 256 * j;
+    const int col = q >> 3, rr = (q & 7) * 8;
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = tile[rr + i][col];
+    split_store(st, blk_off(c0 + col, r0 + rr, k_pad), w, st_lo);   // ST row c0+col, columns r0+rr..+7
   }
 }
 
@@ -409,11 +484,11 @@ void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* 
   if (total <= 0) return;
   const int ui = use_idx ? 1 : 0;
   if (fp64_path) {
-    if (in_bf16) hipLaunchKernelGGL((k_pack<uint16_t, double>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
-    else hipLaunchKernelGGL((k_pack<float, double>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    if (in_bf16) hipLaunchKernelGGL((k_pack<uint16_t>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    else hipLaunchKernelGGL((k_pack<float>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
   } else {
-    if (in_bf16) hipLaunchKernelGGL((k_pack<uint16_t, _Float16>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
-    else hipLaunchKernelGGL((k_pack<float, _Float16>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    if (in_bf16) hipLaunchKernelGGL((k_pack16<uint16_t>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    else hipLaunchKernelGGL((k_pack16<float>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
   }
 }
 
