@@ -237,7 +237,7 @@ __device__ __forceinline__ void store8_hi(_Float16* base, int ld, int row, int c
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("" : : : "memory"); }
 
 // One strip (compile-time index A) of the epilogue.
-template <int BM, int EPI, int F, int A>
+template <int BM, int EPI, int F, int A, bool DIAG>
 __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs& pa, float alpha, int arows,
                                                int brows, int ti, int tj, int wm, int wn, int lane,
                                                const floatx16 (&acc)[F][F], float* st) {
@@ -247,7 +247,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
   constexpr bool SYMO = (EPI == EPI_SYM || EPI == EPI_POLY);
   constexpr bool TRANS = SYMO || EPI == EPI_RECT_T;  // also writes the transposed strip
   constexpr int a = A;
-  const bool diag = SYMO && ti == tj;
+  constexpr bool diag = SYMO && DIAG;   // a diagonal tile: masked stores
   const int row_base = ti * BM + wm * WT;  // global row of the sub-tile
   const int col_base = tj * BM + wn * WT;  // global col of the sub-tile
   _Float16* C = (_Float16*)d.buf[pa.c_slot];
@@ -342,7 +342,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
         }
       } else {  // EPI_SYM, EPI_POLY, EPI_RECT, EPI_RECT_T
         unsigned mask = 0xFFu;
-        if (diag) {  // columns >= row only
+        if constexpr (diag) {  // columns >= row only
           mask = 0;
 #pragma unroll
           for (int i = 0; i < 8; ++i) mask |= (gj0 + i >= gi ? 1u : 0u) << i;
@@ -378,7 +378,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
           store8_hi((_Float16*)d.buf[pa.aux_slot], arows, gj, gi0, w);
         } else {
           unsigned mask = 0xFFu;
-          if (diag) {  // mirror of the strict upper half: gj > gi
+          if constexpr (diag) {  // mirror of the strict upper half: gj > gi
             mask = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) mask |= (gj > gi0 + i ? 1u : 0u) << i;
@@ -396,7 +396,12 @@ __device__ __forceinline__ void epilogue_all(const MatDesc& d, const PhaseArgs& 
                                              int brows, int ti, int tj, int wm, int wn, int lane,
                                              const floatx16 (&acc)[F][F], float* st,
                                              std::integer_sequence<int, As...>) {
-  (epilogue_strip<BM, EPI, F, As>(d, pa, alpha, arows, brows, ti, tj, wm, wn, lane, acc, st), ...);
+  // the tile's position is uniform over the block, so only diagonal tiles of
+  // symmetric outputs run the masked variant
+  if ((EPI == EPI_SYM || EPI == EPI_POLY) && ti == tj)
+    (epilogue_strip<BM, EPI, F, As, true>(d, pa, alpha, arows, brows, ti, tj, wm, wn, lane, acc, st), ...);
+  else
+    (epilogue_strip<BM, EPI, F, As, false>(d, pa, alpha, arows, brows, ti, tj, wm, wn, lane, acc, st), ...);
 }
 
 template <int BM, int EPI, int F>
