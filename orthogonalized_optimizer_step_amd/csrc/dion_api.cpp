@@ -438,14 +438,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.poly_c = (float)c;
       pa.aux_inv_scale = 1.0f / sG;
       pa.out_scale = sP;
-      // At the first iteration of a segment G comes straight from the Gram
-      // product and G*G takes G's hi term only (one MFMA term instead of
-      // three; the bG term of the epilogue still reads both).  Later in a
-      // long segment G has been through P G P updates and the error of a
-      // one-term G*G compounds, so those use both terms.  Chosen by
-      // emulation against the oracle on the workloads' data.
-      const int gg = q_slot < 0 ? 1 : ct;
-      gemm(t_sym, bm_sym, true, gg, gg, EPI_POLY, pa, "gram_poly", ct == 2);
+      // G*G takes the segment's operand terms (the bG term of the epilogue
+      // always reads both).  In a long segment a one-term G*G even at the
+      // segment's first iteration doubles the error of the segments that
+      // follow a restart (emulation: 1.5e-2 -> 7.4e-3 on 256 x 256 with a
+      // restart after iteration 2 of 5).
+      gemm(t_sym, bm_sym, true, ct, ct, EPI_POLY, pa, "gram_poly", ct == 2);
     }
     if (q_slot < 0) {
       q_slot = p_slot;
@@ -547,11 +545,15 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     sb = sb_next;
   }
   {  // out = Q X: wide matrices as Q * X, tall ones as X^T * Q
-    // After a short last segment X enters in its hi term only: Q's gain there
-    // is at most about a^2 and nothing amplifies the fp16 rounding of X
-    // afterwards (emulation: +1e-4 of relative error; a three-iteration last
-    // segment, gain a^3, gives +1.3e-3 and keeps both terms).
+    // After a short last segment both operands enter in their hi term: Q's
+    // gain there is at most about a^2 and nothing amplifies the rounding
+    // afterwards (emulation: +1e-4 of relative error).  After a long one Q
+    // carries the gain of every iteration of the segment and its one-term
+    // rounding dominates the output error, so Q takes both terms, and X too
+    // when it has two (emulation: 1.0e-2 -> 1.7e-3 without restarts, 7.4e-3 ->
+    // 2.7e-3 with a restart after iteration 2 of 5).
     const int fx = full ? 1 : xterms;
+    const int fq = (full || P.fp64) ? 1 : 2;
     PhaseArgs pa{};
     pa.alpha = x_is_x0 ? 1.0f / sQ : 1.0f / (sQ * sXT);
     pa.alpha_pow = x_is_x0 ? 1 : 0;
@@ -561,13 +563,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pw.b_slot = xt_slot;
     pw.b_rows_is_n = 1;
     pw.out_rows_are_m = 1;
-    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, 1, fx, EPI_OUT, pw, "final", false);
+    if (P.tabs[t_wide].nmat) gemm(t_wide, bm_fin, false, fq, fx, EPI_OUT, pw, "final", false);
     PhaseArgs pt = pa;
     pt.a_slot = xt_slot;
     pt.b_slot = q_slot;
     pt.a_rows_is_n = 1;
     pt.out_rows_are_m = 0;
-    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, fx, 1, EPI_OUT, pt, "final", false);
+    if (P.tabs[t_tall].nmat) gemm(t_tall, bm_fin, false, fx, fq, EPI_OUT, pt, "final", false);
   }
   if (P.use_idx && !step_mode) {
     Step cp;

@@ -713,6 +713,7 @@ bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& 
       case (1 << 8) | (1 << 4) | EPI_OUT: DION_G16(BM_, 1, 1, EPI_OUT, false); return true; \
       case (2 << 8) | (1 << 4) | EPI_OUT: DION_G16(BM_, 2, 1, EPI_OUT, false); return true; \
       case (1 << 8) | (2 << 4) | EPI_OUT: DION_G16(BM_, 1, 2, EPI_OUT, false); return true; \
+      case (2 << 8) | (2 << 4) | EPI_OUT: DION_G16(BM_, 2, 2, EPI_OUT, false); return true; \
       default: return false;                                                             \
     }                                                                                    \
   }
