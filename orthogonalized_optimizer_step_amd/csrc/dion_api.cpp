@@ -157,6 +157,7 @@ struct Table {  // a (matrix list, prefix) pair inside the int blob
 
 struct MatPlan {
   int R, C, k, m, n, m_pad, n_pad, tall;
+  bool acc;  // restarts after the first start from X0 with the accumulated factor
   size_t off[N_SLOTS];
 };
 
@@ -202,8 +203,9 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;  // bf16 values are exact in one fp16 term
   P.use_idx = prm.row_frac < 1.0;
   const int K = (int)prm.a.size();
-  bool any_restart = false;
-  for (int r : prm.restart) any_restart |= (r != 0);
+  int n_restarts = 0;
+  for (int r : prm.restart) n_restarts += (r != 0);
+  const bool any_restart = n_restarts > 0;
   const size_t es = P.fp64 ? 8 : 2;
   const size_t mm_terms = P.fp64 ? 1 : 2;
   const size_t xt_terms = P.fp64 ? 1 : 2;
@@ -222,6 +224,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     mp.n = std::max(mp.k, C);
     mp.m_pad = pad_up(mp.m);
     mp.n_pad = pad_up(mp.n);
+    // From the second restart on, X_r = Q_r X_{r-1} can be formed as
+    // (Q_r ... Q_1) X0: X0 is exact in one fp16 term (bf16 input), so the
+    // apply takes one term instead of the iterate's two, at the price of one
+    // m x m product.  That pays where the apply's long side dominates.
+    mp.acc = !P.fp64 && P.xterms0 == 1 && n_restarts >= 2 && 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m;
     P.total_rows += R;
     P.total_sel += mp.k;
   }
@@ -259,8 +266,10 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     return c;
   };
   const int bm_full = pick_bm([&](int bm) { return full_counts(bm); });
-  std::vector<int> wide, tall;
+  std::vector<int> wide, tall, accs, naccs;
   for (int i = 0; i < batch; ++i) (P.mats[i].tall ? tall : wide).push_back(i);
+  for (int i = 0; i < batch; ++i) (P.mats[i].acc ? accs : naccs).push_back(i);
+  const bool any_acc = !accs.empty();
   const int bm_fin = pick_bm([&](int bm) {
     auto a = rect_counts(wide, bm, false), b = rect_counts(tall, bm, true);
     a.insert(a.end(), b.begin(), b.end());
@@ -271,6 +280,15 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   const int t_full = add_table(P, all, full_counts(bm_full));
   const int t_wide = add_table(P, wide, rect_counts(wide, bm_fin, false));
   const int t_tall = add_table(P, tall, rect_counts(tall, bm_fin, true));
+  // restarts after the first: matrices that restart from X0 and the others
+  auto sub_full = [&](const std::vector<int>& ms, int bm) {
+    std::vector<int> c;
+    for (int i : ms) { int T = P.mats[i].m_pad / bm; c.push_back(T * T); }
+    return c;
+  };
+  const int t_xtq_acc = add_table(P, accs, rect_counts(accs, bm_xtq, true));
+  const int t_xtq_nacc = add_table(P, naccs, rect_counts(naccs, bm_xtq, true));
+  const int t_full_acc = add_table(P, accs, sub_full(accs, bm_full));
   std::vector<int> pack_c(batch), tr_c(batch);
   for (int i = 0; i < batch; ++i) {
     const MatPlan& mp = P.mats[i];
@@ -296,8 +314,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     for (int s = 0; s < N_SLOTS; ++s) mp.off[s] = 0;
     mp.off[SLOT_X] = off;   off = align256(off + mn * es);
     mp.off[SLOT_XT0] = off; off = align256(off + mn * es * xt_terms);
-    if (any_restart) { mp.off[SLOT_XT1] = off; off = align256(off + mn * es * xt_terms); }
-    for (int s = SLOT_MM0; s <= SLOT_MM3; ++s) { mp.off[s] = off; off = align256(off + mm * es * mm_terms); }
+    if (any_restart) {
+      mp.off[SLOT_XT1] = off; off = align256(off + mn * es * xt_terms);
+      mp.off[SLOT_XTE] = mp.acc ? mp.off[SLOT_XT1] : mp.off[SLOT_XT0];
+    }
+    const int last_mm = any_acc ? SLOT_MM4 : SLOT_MM3;
+    for (int s = SLOT_MM0; s <= last_mm; ++s) { mp.off[s] = off; off = align256(off + mm * es * mm_terms); }
   }
   P.total = off;
 
@@ -331,7 +353,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   // out_lo: whether any later product or epilogue reads the lo term of this
   // product's fp16 output (skipping it halves the output stores)
   auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, PhaseArgs pa, const char* name,
-                  bool out_lo) {
+                  bool out_lo, bool counts_useful = true) {
     pa.out_lo = out_lo ? 1 : 0;
     Step g;
     g.name = name;
@@ -345,7 +367,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       g.raw += (double)tiles * bm * bm * K * 2.0 * nprod;
       // an m x m chain product counts as the symmetric half however it is run
       const bool mxm = !pa.k_is_n && !pa.a_rows_is_n && !pa.b_rows_is_n && epi != EPI_OUT;
-      if (sym && pa.k_is_n) g.useful += n * m * (m + 1);          // Gram
+      if (!counts_useful) {}                                     // extra work of the execution
+      else if (sym && pa.k_is_n) g.useful += n * m * (m + 1);   // Gram
       else if (mxm) g.useful += m * m * (m + 1);                 // m x m chain
       else g.useful += 2.0 * m * m * n;                          // apply / final
       // algorithmic HBM bytes on the padded layout: every operand term read
@@ -386,9 +409,14 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", true);
   }
   std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
+  if (any_acc) freel.insert(freel.begin(), SLOT_MM4);
   int q_slot = -1, xt_slot = SLOT_XT0, xterms = P.xterms0;
   float sQ = 1.f, sXT = 1.f;
   double qb = 1.0;
+  int n_rest = 0;         // restarts taken so far
+  int qa_slot = -1;       // accumulated factor Q_r ... Q_1 (matrices restarting from X0)
+  float sQA = 1.f;
+  double qab = 1.0;
   bool x_is_x0 = true;
   int ct = 2;         // operand terms of the m x m chain products in this segment
   bool full = false;  // one-term chain: P G and P Q as full (unmirrored) products
@@ -469,24 +497,56 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     if (k == K) break;
     if (prm.restart[k - 1]) {
       // X <- Q X, computed as X'^T = X^T Q; then X = transpose; G = X X^T
+      ++n_rest;
       const float sXn = sc(sb_next);
-      const int xt_new = xt_slot == SLOT_XT0 ? SLOT_XT1 : SLOT_XT0;
-      {
+      // odd-numbered restarts write XT1, even-numbered ones XTE (XT0's buffer,
+      // or XT1's for matrices restarting from X0, whose X0^T stays in XT0)
+      const int xt_new = (n_rest & 1) ? SLOT_XT1 : SLOT_XTE;
+      // X^T is read in two terms by the next restart apply, or by the final
+      // apply, which takes its hi term only after a short last segment.
+      // Matrices restarting from X0 read it only in the final apply.
+      int e2 = k + 1;
+      while (e2 < K && !prm.restart[e2 - 1]) ++e2;
+      const bool xt_lo = !(e2 == K && e2 - k <= 2);
+      const bool xt_lo_acc = xt_lo && e2 == K;
+      auto apply = [&](int table, int a_slot, int na, int b_slot, float alpha, int alpha_pow, bool lo) {
         PhaseArgs pa{};
-        pa.a_slot = xt_slot;
-        pa.b_slot = q_slot;
+        pa.a_slot = a_slot;
+        pa.b_slot = b_slot;
         pa.c_slot = xt_new;
         pa.a_rows_is_n = 1;
-        pa.alpha = x_is_x0 ? sXn / sQ : sXn / (sXT * sQ);
-        pa.alpha_pow = x_is_x0 ? 1 : 0;
+        pa.alpha = alpha;
+        pa.alpha_pow = alpha_pow;
         // MFMA16: the epilogue also writes X (hi) transposed; FP64: a transpose pass
         pa.aux_slot = SLOT_X;
-        // X^T is read in two terms by the next restart apply, or by the final
-        // apply, which takes its hi term only after a short last segment
-        int e2 = k + 1;
-        while (e2 < K && !prm.restart[e2 - 1]) ++e2;
-        const bool xt_lo = !(e2 == K && e2 - k <= 2);
-        gemm(t_xtq, bm_xtq, false, xterms, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply", xt_lo);
+        gemm(table, bm_xtq, false, na, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply", lo);
+      };
+      const float al = x_is_x0 ? sXn / sQ : sXn / (sXT * sQ);
+      const int alp = x_is_x0 ? 1 : 0;
+      if (!any_acc) {
+        apply(t_xtq, xt_slot, xterms, q_slot, al, alp, xt_lo);
+      } else if (n_rest == 1) {  // the same product, split by who reads the lo term
+        apply(t_xtq_acc, xt_slot, xterms, q_slot, al, alp, xt_lo_acc);
+        if (P.tabs[t_xtq_nacc].nmat) apply(t_xtq_nacc, xt_slot, xterms, q_slot, al, alp, xt_lo);
+      } else {
+        // matrices restarting from X0: QA <- Q QA^T (a full one-term product,
+        // outside the useful count), then X'^T = X0^T QA
+        const double qab_new = qab * qb;
+        const float sQAn = sc(qab_new);
+        const int qa_new = freel.back();
+        freel.pop_back();
+        PhaseArgs pq{};
+        pq.a_slot = q_slot;
+        pq.b_slot = qa_slot;
+        pq.c_slot = qa_new;
+        pq.alpha = sQAn / (sQ * sQA);
+        gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
+        freel.push_back(qa_slot);
+        qa_slot = qa_new;
+        sQA = sQAn;
+        qab = qab_new;
+        apply(t_xtq_acc, SLOT_XT0, 1, qa_slot, sXn / sQA, 1, xt_lo_acc);
+        if (P.tabs[t_xtq_nacc].nmat) apply(t_xtq_nacc, xt_slot, xterms, q_slot, al, alp, xt_lo);
       }
       if (P.fp64) {
         Step tr;
@@ -512,7 +572,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       xterms = P.fp64 ? 1 : 2;
       sXT = sXn;
       x_is_x0 = false;
-      freel.push_back(q_slot);
+      if (n_rest == 1 && any_acc) {  // Q_1 starts the accumulated factor
+        qa_slot = q_slot;
+        sQA = sQ;
+        qab = qb;
+      } else {
+        freel.push_back(q_slot);
+      }
       if (p_slot != q_slot) freel.push_back(p_slot);
       q_slot = -1;
     } else {

@@ -30,13 +30,16 @@ inline __host__ __device__ size_t blk_off(int r, int c, int ld) {
 // Buffer slots of a matrix's workspace region.
 enum Slot : int {
   SLOT_X = 0,   // [m_pad][n_pad] hi: Gram (SYRK) operand
-  SLOT_XT0 = 1, // [n_pad][m_pad] x terms: apply operand (ping)
-  SLOT_XT1 = 2, // [n_pad][m_pad] x terms: apply operand (pong)
-  SLOT_MM0 = 3, // four m_pad x m_pad buffers (G, P, T, Q roles rotate)
-  SLOT_MM1 = 4,
-  SLOT_MM2 = 5,
-  SLOT_MM3 = 6,
-  N_SLOTS = 7
+  SLOT_XT0 = 1, // [n_pad][m_pad] x terms: apply operand (X0^T from the pack)
+  SLOT_XT1 = 2, // [n_pad][m_pad] x terms: iterate of odd-numbered restarts
+  SLOT_XTE = 3, // iterate of even-numbered restarts: XT0's buffer, or XT1's for
+                // matrices that restart from X0 (their X0^T must survive)
+  SLOT_MM0 = 4, // m_pad x m_pad buffers (G, P, T, Q roles rotate; a fifth one
+  SLOT_MM1 = 5, // holds the accumulated factor when some matrix restarts from X0)
+  SLOT_MM2 = 6,
+  SLOT_MM3 = 7,
+  SLOT_MM4 = 8,
+  N_SLOTS = 9
 };
 
 // Per-matrix descriptor (device copy in the workspace).
