@@ -289,6 +289,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   const int t_xtq_acc = add_table(P, accs, rect_counts(accs, bm_xtq, true));
   const int t_xtq_nacc = add_table(P, naccs, rect_counts(naccs, bm_xtq, true));
   const int t_full_acc = add_table(P, accs, sub_full(accs, bm_full));
+  const int t_full_nacc = add_table(P, naccs, sub_full(naccs, bm_full));
   std::vector<int> pack_c(batch), tr_c(batch);
   for (int i = 0; i < batch; ++i) {
     const MatPlan& mp = P.mats[i];
@@ -318,7 +319,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       mp.off[SLOT_XT1] = off; off = align256(off + mn * es * xt_terms);
       mp.off[SLOT_XTE] = mp.acc ? mp.off[SLOT_XT1] : mp.off[SLOT_XT0];
     }
-    const int last_mm = any_acc ? SLOT_MM4 : SLOT_MM3;
+    const int last_mm = any_acc ? SLOT_MM5 : SLOT_MM3;
     for (int s = SLOT_MM0; s <= last_mm; ++s) { mp.off[s] = off; off = align256(off + mm * es * mm_terms); }
   }
   P.total = off;
@@ -409,17 +410,19 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", true);
   }
   std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
-  if (any_acc) freel.insert(freel.begin(), SLOT_MM4);
+  if (any_acc) freel.insert(freel.begin(), {SLOT_MM5, SLOT_MM4});
   int q_slot = -1, xt_slot = SLOT_XT0, xterms = P.xterms0;
   float sQ = 1.f, sXT = 1.f;
   double qb = 1.0;
   int n_rest = 0;         // restarts taken so far
-  int qa_slot = -1;       // accumulated factor Q_r ... Q_1 (matrices restarting from X0)
+  int qa_slot = -1;       // accumulated factor S = Q_r ... Q_1 (matrices restarting from X0)
+  int qat_slot = -1;      // S^T (hi term), or qa_slot when S is exactly symmetric
+  int pending_qat = -1;   // Q_1^T written by the product that forms Q_1
   float sQA = 1.f;
   double qab = 1.0;
   bool x_is_x0 = true;
   int ct = 2;         // operand terms of the m x m chain products in this segment
-  bool full = false;  // one-term chain: P G and P Q as full (unmirrored) products
+  bool short_seg = false;  // one-term chain: Q <- P Q as a full (unmirrored) product
   for (int k = 1; k <= K; ++k) {
     const double a = prm.a[k - 1], b = prm.b[k - 1], c = prm.c[k - 1];
     if (q_slot < 0) {
@@ -431,24 +434,23 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       // one-term chain products, longer segments two terms.  The restart
       // apply keeps X in two terms in every case.
       //
-      // With one-term operands the products P G and P Q are run in full
-      // rather than as an upper triangle plus its mirror.  In exact
-      // arithmetic both are symmetric (P, G and Q are polynomials in the same
-      // Gram matrix), but their rounding errors are not: in the eigenbasis
-      // the error of entry (i, j) of P G carries the weights of row i, and the
-      // mirror copies the entries whose row is a small singular direction
-      // (where P is near its slope a = 3.4445 and Q near a^2) into the
-      // transposed position.  The next product (P T^T, or Q X in the apply)
-      // then multiplies that copy by the large singular values, which about
-      // doubles the output error.  Gram-shaped products (X X^T, G G, P T^T
-      // with T = P G) have errors symmetric in (i, j) and stay mirrored.
-      // Emulation against the oracle: 2.9e-3 to 3.5e-3 of relative error for
-      // one-term chains with the full products, 6e-3 to 9e-3 with mirrored
-      // ones, 2.9e-3 for two-term operands.
+      // With one-term operands the product Q <- P Q is run in full rather
+      // than as an upper triangle plus its mirror.  In exact arithmetic it is
+      // symmetric (P and Q are polynomials in the same Gram matrix), but its
+      // rounding error is not: in the eigenbasis the error of entry (i, j)
+      // carries the weights of row i, and the mirror copies the entries whose
+      // row is a small singular direction (where P is near its slope
+      // a = 3.4445) into the transposed position, which the apply Q X then
+      // multiplies by the large singular values.  T = P G is mirrored: its
+      // error is only half as harmful, since the next product P T^T is
+      // Gram-shaped.  Emulation against the oracle (Llama-shaped 1024 x 4096,
+      // restarts every 2): relative error 5.6e-3 with both products full,
+      // 6.3e-3 with T mirrored, 9.1e-3 with both mirrored; on the row-subset
+      // blocks 3.7e-3, 5.9e-3 and 1.2e-2.
       int e = k;
       while (e < K && !prm.restart[e - 1]) ++e;
       ct = e - k + 1 <= 2 ? 1 : 2;
-      full = !P.fp64 && ct == 1;
+      short_seg = !P.fp64 && ct == 1;
     }
     const double gb = sb * sb;
     const double pb = poly_max(a, b, c, gb, 0), tb = poly_max(a, b, c, gb, 1);
@@ -487,8 +489,21 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.b_slot = q_slot;
       pa.c_slot = qn;
       pa.alpha = sQn / (sP * sQ);
-      if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product", false);
-      else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
+      if (short_seg && any_acc && k < K && prm.restart[k - 1] && n_rest == 0) {
+        // this Q starts the accumulated factor of the matrices restarting
+        // from X0; their next accumulation multiplies by it from the right,
+        // which reads its rows as columns: keep Q^T (hi) as well
+        pending_qat = freel.back();
+        freel.pop_back();
+        PhaseArgs pt = pa;
+        pt.aux_slot = pending_qat;
+        gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT_T, pt, "full_product", false);
+        if (P.tabs[t_full_nacc].nmat) gemm(t_full_nacc, bm_full, false, 1, 1, EPI_RECT, pa, "full_product", false);
+      } else if (short_seg) {
+        gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product", false);
+      } else {
+        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
+      }
       freel.push_back(q_slot);
       q_slot = qn;
       sQ = sQn;
@@ -529,20 +544,30 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         apply(t_xtq_acc, xt_slot, xterms, q_slot, al, alp, xt_lo_acc);
         if (P.tabs[t_xtq_nacc].nmat) apply(t_xtq_nacc, xt_slot, xterms, q_slot, al, alp, xt_lo);
       } else {
-        // matrices restarting from X0: QA <- Q QA^T (a full one-term product,
-        // outside the useful count), then X'^T = X0^T QA
+        // matrices restarting from X0: S <- Q S (a full one-term product in
+        // this order, outside the useful count; it reads S^T by rows and
+        // writes S^T too when a later restart needs it), then X'^T = X0^T S^T
         const double qab_new = qab * qb;
         const float sQAn = sc(qab_new);
+        const bool more = n_rest < n_restarts;
         const int qa_new = freel.back();
         freel.pop_back();
+        int qat_new = qa_new;
+        if (more) {
+          qat_new = freel.back();
+          freel.pop_back();
+        }
         PhaseArgs pq{};
         pq.a_slot = q_slot;
-        pq.b_slot = qa_slot;
+        pq.b_slot = qat_slot;
         pq.c_slot = qa_new;
+        pq.aux_slot = qat_new;
         pq.alpha = sQAn / (sQ * sQA);
-        gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
+        gemm(t_full_acc, bm_full, false, 1, 1, more ? EPI_RECT_T : EPI_RECT, pq, "acc_product", false, false);
         freel.push_back(qa_slot);
+        if (qat_slot != qa_slot) freel.push_back(qat_slot);
         qa_slot = qa_new;
+        qat_slot = qat_new;
         sQA = sQAn;
         qab = qab_new;
         apply(t_xtq_acc, SLOT_XT0, 1, qa_slot, sXn / sQA, 1, xt_lo_acc);
@@ -574,6 +599,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       x_is_x0 = false;
       if (n_rest == 1 && any_acc) {  // Q_1 starts the accumulated factor
         qa_slot = q_slot;
+        qat_slot = pending_qat >= 0 ? pending_qat : q_slot;  // else Q_1 is exactly symmetric
         sQA = sQ;
         qab = qb;
       } else {
@@ -592,8 +618,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = g_slot;
         pa.c_slot = t_slot;
         pa.alpha = sT / (sP * sG);
-        if (full) gemm(t_full, bm_full, false, 1, 1, EPI_RECT, pa, "full_product", false);
-        else gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
+        // the lo term of T is read only by a two-term P T^T
+        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", ct == 2);
       }
       const float sGn = sc(sb_next * sb_next);
       {
@@ -618,8 +644,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     // rounding dominates the output error, so Q takes both terms, and X too
     // when it has two (emulation: 1.0e-2 -> 1.7e-3 without restarts, 7.4e-3 ->
     // 2.7e-3 with a restart after iteration 2 of 5).
-    const int fx = full ? 1 : xterms;
-    const int fq = (full || P.fp64) ? 1 : 2;
+    const int fx = short_seg ? 1 : xterms;
+    const int fq = (short_seg || P.fp64) ? 1 : 2;
     PhaseArgs pa{};
     pa.alpha = x_is_x0 ? 1.0f / sQ : 1.0f / (sQ * sXT);
     pa.alpha_pow = x_is_x0 ? 1 : 0;

@@ -34,12 +34,13 @@ enum Slot : int {
   SLOT_XT1 = 2, // [n_pad][m_pad] x terms: iterate of odd-numbered restarts
   SLOT_XTE = 3, // iterate of even-numbered restarts: XT0's buffer, or XT1's for
                 // matrices that restart from X0 (their X0^T must survive)
-  SLOT_MM0 = 4, // m_pad x m_pad buffers (G, P, T, Q roles rotate; a fifth one
-  SLOT_MM1 = 5, // holds the accumulated factor when some matrix restarts from X0)
-  SLOT_MM2 = 6,
+  SLOT_MM0 = 4, // m_pad x m_pad buffers: G, P, T, Q roles rotate over four;
+  SLOT_MM1 = 5, // two more hold the accumulated factor and its transpose when
+  SLOT_MM2 = 6, // some matrix restarts from X0
   SLOT_MM3 = 7,
   SLOT_MM4 = 8,
-  N_SLOTS = 9
+  SLOT_MM5 = 9,
+  N_SLOTS = 10
 };
 
 // Per-matrix descriptor (device copy in the workspace).

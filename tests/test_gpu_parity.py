@@ -86,7 +86,8 @@ def test_small_ragged_fp64_path(dion, sched):
 
 # ---------------------------------------------------------- MFMA16 path
 @pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10, safety=1.01),
-                                   dict(n_iter=6, restart_every=2, safety=1.05), dict(restart_every=1)])
+                                   dict(n_iter=6, restart_every=2, safety=1.05), dict(restart_every=1),
+                                   dict(n_iter=6, restart_every=1)])
 def test_small_ragged_mfma16(dion, sched):
     Ms = small_batch(12)
     kw = {"n_iter": 5, **sched}
