@@ -146,6 +146,74 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
                         const dion_ns_params* p, int32_t* sel_idx, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Phase entry points: one step of the path on its own, with the same kernels,
+ * operand layout and precision as inside dion_orth_batched, for kernel-level
+ * checks.  Conventions as above; each takes its own workspace of
+ * dion_phase_workspace_size(phase, ...) bytes.  "Gram side" means the
+ * orientation of the iteration: a wide matrix (R <= C) is X itself, a tall
+ * one is processed as X^T, and m = min(R, C).
+ * precision: DION_PREC_MFMA16 (fp16 MFMA, fp32 accumulation), DION_PREC_FP64,
+ * or DION_PREC_AUTO (FP64 for DION_FP32 inputs, MFMA16 otherwise).
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  DION_PHASE_ROWKEYS_TOPK = 1,
+  DION_PHASE_SYRK = 2,
+  DION_PHASE_SYMPOLY = 3,
+  DION_PHASE_APPLY = 4
+} dion_phase;
+
+/* Workspace bytes of one phase entry point (0 on invalid arguments).  For
+ * DION_PHASE_SYMPOLY pass shapes {m_i, m_i} (dtype is ignored); row_frac is
+ * used by DION_PHASE_ROWKEYS_TOPK only. */
+size_t dion_phase_workspace_size(int32_t phase, const dion_shape* shapes, int32_t batch, int32_t dtype,
+                                 int32_t precision, float row_frac);
+
+/* Row keys and top-k selection (the row rule of the Dion3 abstract and of the
+ * Dion3 summary, 核心模块, "Dion3 更新规则" bullet), as step 1 above:
+ *   keys     optional device fp64 buffer of sum_i R_i entries: the squared L2
+ *            norm of every row, matrices in batch order
+ *   sel_idx  optional device int32 buffer of sum_i k_i entries: the selected
+ *            rows of each matrix, ascending (larger key first, ties to the
+ *            lower row index, k = dion_selected_rows(R, row_frac)) */
+int dion_rowkeys_topk_batched(const void* const* M, const dion_shape* shapes, int32_t batch, int32_t dtype,
+                              float row_frac, double* keys, int32_t* sel_idx, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Gram matrix on the Gram side (Dion3 summary, 核心模块, "Gram Newton-Schulz"
+ * and CuteDSL bullets: the symmetric product computed on the upper triangle
+ * and mirrored):
+ *   X[i]  device R x C of dtype, read only
+ *   G[i]  device m x m fp32, row-major: X X^T (wide) or X^T X (tall)
+ * MFMA16 runs on one fp16 term of X / ||X||_F (exact for bf16 input, an fp16
+ * rounding of fp32 input), fp32 accumulation, result kept in two fp16 terms
+ * and scaled back by ||X||_F^2. */
+int dion_syrk_batched(const void* const* X, float* const* G, const dion_shape* shapes, int32_t batch,
+                      int32_t dtype, int32_t precision, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gram polynomial of one iteration (the same bullet; the polynomial is fused
+ * into the epilogue of G * G):
+ *   G[i]    device m_i x m_i fp32, symmetric, spectral norm <= 1 (the Gram
+ *           matrix of a Frobenius-normalized iterate); only G^T is read, so
+ *           the result is exact for the transpose of a nonsymmetric input
+ *   P[i]    device m_i x m_i fp32: a I + b G + c G^2
+ *   coeffs  host (a, b, c); NULL = the fixed quintic
+ * MFMA16 takes G in two fp16 terms; a spectral norm above 1 may overflow its
+ * fixed fp16 scale (output unspecified). */
+int dion_sympoly_batched(const float* const* G, float* const* P, const int32_t* m, int32_t batch,
+                         const float* coeffs, int32_t precision, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Apply of an m x m factor on the Gram side (the final apply of the path):
+ *   Q[i]  device m x m fp32 (m = min(R, C)), read only
+ *   X[i]  device R x C of dtype, read only
+ *   Y[i]  device R x C of dtype: Q X when R <= C, X Q when R > C (rounded to
+ *         nearest even for bf16)
+ * MFMA16 takes Q in two fp16 terms and X in one (bf16) or two (fp32). */
+int dion_apply_batched(const float* const* Q, const void* const* X, void* const* Y, const dion_shape* shapes,
+                       int32_t batch, int32_t dtype, int32_t precision, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Useful floating-point operations of one dion_orth_batched call on this
  * batch, in the executed formulation, symmetric products counted once:
  * per matrix and restart segment of length L,

@@ -6,8 +6,11 @@ product package.
 """
 from .dion_oracle import (  # noqa: F401
     DEFAULT_COEFFS,
+    apply_factor,
     coefficient_schedule,
+    gram,
     gram_newton_schulz,
+    gram_polynomial,
     momentum_update,
     orthogonalize,
     orthogonalize_batch,

@@ -142,6 +142,39 @@ def select_rows(M, row_frac: float) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# The single steps of one iteration, on the Gram side (reading R3)
+# --------------------------------------------------------------------------
+def gram(S) -> np.ndarray:
+    """Gram matrix on the Gram side: X X^T with X = S (wide) or S^T (tall, R3).
+
+    Pages: Dion3 summary, 核心模块, "Gram Newton-Schulz" bullet (the iteration
+    runs on the Gram matrix) and CuteDSL bullet (symmetric products).
+    """
+    X = np.asarray(S, dtype=np.float64)
+    if X.shape[0] > X.shape[1]:
+        X = X.T
+    return X @ X.T
+
+
+def gram_polynomial(G, a: float, b: float, c: float) -> np.ndarray:
+    """P = a I + b G + c G^2: the iteration's polynomial in the Gram matrix.
+
+    One Newton-Schulz step X <- a X + b A X + c A^2 X (A = X X^T) is X <- P X
+    with this P.  Pages: Dion3 summary, 核心模块, "Gram Newton-Schulz" bullet
+    and CuteDSL bullet (the polynomial fused into the product as GEMM + add).
+    """
+    G = np.asarray(G, dtype=np.float64)
+    return a * np.eye(G.shape[0]) + b * G + c * (G @ G)
+
+
+def apply_factor(Q, S) -> np.ndarray:
+    """The factor applied on the Gram side: Q S for a wide block, S Q for a tall one."""
+    Q = np.asarray(Q, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    return S @ Q if S.shape[0] > S.shape[1] else Q @ S
+
+
+# --------------------------------------------------------------------------
 # Gram Newton-Schulz (readings R2-R5)
 # --------------------------------------------------------------------------
 def gram_newton_schulz(X, coeff_list, restarts) -> np.ndarray:
@@ -164,7 +197,7 @@ def gram_newton_schulz(X, coeff_list, restarts) -> np.ndarray:
     restart_set = set(restarts)
     for k in range(1, K + 1):
         a, b, c = coeff_list[k - 1]
-        P = a * eye + b * G + c * (G @ G)
+        P = gram_polynomial(G, a, b, c)
         Q = P @ Q
         if k == K:
             break

@@ -9,10 +9,11 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import DION_BF16, DION_FP32, PREC, DionError, DionParams, DionShape, check, lib
+from ._lib import DION_BF16, DION_FP32, PHASE, PREC, DionError, DionParams, DionShape, check, lib
 
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
-           "DionError", "QUINTIC", "profile_enable", "profile_records"]
+           "DionError", "QUINTIC", "profile_enable", "profile_records", "rowkeys_topk", "syrk", "sympoly",
+           "apply"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
@@ -166,6 +167,85 @@ def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart
     if not return_indices:
         return outs
     return outs, list(torch.split(sel, orth.selected))
+
+
+# ------------------------------------------------------------ phase entry points
+def _phase_ws(phase, shapes, dtype_code, precision, row_frac, device):
+    n = lib.dion_phase_workspace_size(PHASE[phase], _shapes(shapes), len(shapes), dtype_code,
+                                      PREC[precision] if isinstance(precision, str) else int(precision),
+                                      ctypes.c_float(float(row_frac)))
+    if n == 0:
+        raise DionError(-1, lib.dion_last_error().decode())
+    return _workspace(n, device, None)
+
+
+def _gram_side(shape):
+    return min(int(shape[0]), int(shape[1]))
+
+
+def rowkeys_topk(Ms, row_frac=1.0, stream=None):
+    """Squared L2 norm of every row (fp64) and the selected rows of each matrix
+    (int32, ascending).  Returns (list of key vectors, list of index vectors)."""
+    import torch
+    _check_tensors(Ms, Ms[0].dtype)
+    shapes = [tuple(M.shape) for M in Ms]
+    code = _dtype_code(Ms[0].dtype)
+    keep, ws, wl = _phase_ws("rowkeys_topk", shapes, code, "mfma16", row_frac, Ms[0].device)
+    ks = [int(lib.dion_selected_rows(r, ctypes.c_float(float(row_frac)))) for r, _ in shapes]
+    keys = torch.empty(sum(r for r, _ in shapes), dtype=torch.float64, device=Ms[0].device)
+    idx = torch.empty(sum(ks), dtype=torch.int32, device=Ms[0].device)
+    check(lib.dion_rowkeys_topk_batched(_ptrs(Ms), _shapes(shapes), len(Ms), code, ctypes.c_float(float(row_frac)),
+                                        ctypes.c_void_p(keys.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
+                                        ctypes.c_void_p(ws), wl, _stream(stream)))
+    return list(torch.split(keys, [r for r, _ in shapes])), list(torch.split(idx, ks))
+
+
+def syrk(Xs, precision="auto", stream=None):
+    """Gram matrix on the Gram side of each matrix (X X^T if wide, X^T X if tall), fp32."""
+    import torch
+    _check_tensors(Xs, Xs[0].dtype)
+    shapes = [tuple(X.shape) for X in Xs]
+    code = _dtype_code(Xs[0].dtype)
+    keep, ws, wl = _phase_ws("syrk", shapes, code, precision, 1.0, Xs[0].device)
+    Gs = [torch.empty((_gram_side(s), _gram_side(s)), dtype=torch.float32, device=Xs[0].device) for s in shapes]
+    check(lib.dion_syrk_batched(_ptrs(Xs), _ptrs(Gs), _shapes(shapes), len(Xs), code,
+                                PREC[precision] if isinstance(precision, str) else int(precision),
+                                ctypes.c_void_p(ws), wl, _stream(stream)))
+    return Gs
+
+
+def sympoly(Gs, coeffs=QUINTIC, precision="auto", stream=None):
+    """a I + b G + c G^2 for symmetric fp32 G with spectral norm <= 1."""
+    import torch
+    _check_tensors(Gs, torch.float32)
+    ms = [int(G.shape[0]) for G in Gs]
+    if any(G.shape[0] != G.shape[1] for G in Gs):
+        raise DionError(-1, "G must be square")
+    keep, ws, wl = _phase_ws("sympoly", [(m, m) for m in ms], DION_FP32, precision, 1.0, Gs[0].device)
+    Ps = [torch.empty_like(G) for G in Gs]
+    co = (ctypes.c_float * 3)(*[float(x) for x in coeffs])
+    check(lib.dion_sympoly_batched(_ptrs(Gs), _ptrs(Ps), (ctypes.c_int32 * len(ms))(*ms), len(Gs), co,
+                                   PREC[precision] if isinstance(precision, str) else int(precision),
+                                   ctypes.c_void_p(ws), wl, _stream(stream)))
+    return Ps
+
+
+def apply(Qs, Xs, precision="auto", stream=None):
+    """Q X (wide X) or X Q (tall X) with Q the fp32 m x m factor on the Gram side."""
+    import torch
+    _check_tensors(Xs, Xs[0].dtype)
+    _check_tensors(Qs, torch.float32)
+    shapes = [tuple(X.shape) for X in Xs]
+    for Q, s in zip(Qs, shapes):
+        if tuple(Q.shape) != (_gram_side(s), _gram_side(s)):
+            raise DionError(-1, f"Q must be {_gram_side(s)} x {_gram_side(s)} for X of shape {s}")
+    code = _dtype_code(Xs[0].dtype)
+    keep, ws, wl = _phase_ws("apply", shapes, code, precision, 1.0, Xs[0].device)
+    Ys = [torch.empty_like(X) for X in Xs]
+    check(lib.dion_apply_batched(_ptrs(Qs), _ptrs(Xs), _ptrs(Ys), _shapes(shapes), len(Xs), code,
+                                 PREC[precision] if isinstance(precision, str) else int(precision),
+                                 ctypes.c_void_p(ws), wl, _stream(stream)))
+    return Ys
 
 
 def profile_enable(on=True) -> bool:

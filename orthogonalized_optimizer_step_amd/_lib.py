@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdion.so")
 
 DION_BF16, DION_FP32 = 0, 1
+PHASE = {"rowkeys_topk": 1, "syrk": 2, "sympoly": 3, "apply": 4}
 PREC = {"auto": 0, "mfma16": 1, "fp64": 2}
 
 
@@ -37,7 +38,8 @@ EXPORTS = (
     "dion_workspace_size", "dion_orth_batched", "dion_orth_batched_simple",
     "dion_rowsubset_step", "dion_useful_flops", "dion_selected_rows", "dion_strerror",
     "dion_last_error", "dion_version", "dion_profile_enable", "dion_profile_count",
-    "dion_profile_get",
+    "dion_profile_get", "dion_phase_workspace_size", "dion_rowkeys_topk_batched", "dion_syrk_batched",
+    "dion_sympoly_batched", "dion_apply_batched",
 )
 
 
@@ -89,6 +91,17 @@ def _load():
     lib.dion_profile_get.restype = ctypes.c_int
     lib.dion_version.argtypes = []
     lib.dion_version.restype = ctypes.c_int
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.dion_phase_workspace_size.argtypes = [i32, shp, i32, i32, i32, ctypes.c_float]
+    lib.dion_phase_workspace_size.restype = sz
+    lib.dion_rowkeys_topk_batched.argtypes = [pp, shp, i32, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.dion_rowkeys_topk_batched.restype = ctypes.c_int
+    lib.dion_syrk_batched.argtypes = [pp, pp, shp, i32, i32, i32, vp, sz, vp]
+    lib.dion_syrk_batched.restype = ctypes.c_int
+    lib.dion_sympoly_batched.argtypes = [pp, pp, ctypes.POINTER(i32), i32, fp, i32, vp, sz, vp]
+    lib.dion_sympoly_batched.restype = ctypes.c_int
+    lib.dion_apply_batched.argtypes = [pp, pp, pp, shp, i32, i32, i32, vp, sz, vp]
+    lib.dion_apply_batched.restype = ctypes.c_int
     return lib
 
 

@@ -36,6 +36,9 @@ void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int tot
                       hipStream_t s);
 void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
                             hipStream_t s);
+void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total, int slot,
+                   const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
+void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
 }  // namespace dion
 
 using namespace dion;
@@ -136,7 +139,7 @@ float pow2_scale(double bound) {  // largest 2^j with bound * 2^j <= 2^15
 }
 
 // ------------------------------------------------------------ the plan
-enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY };
+enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY, ST_UNPACK, ST_COMBINE };
 
 struct Step {
   StepKind kind;
@@ -145,6 +148,9 @@ struct Step {
   int table = 0;  // index into Plan::tabs
   PhaseArgs pa{};
   int src_slot = 0, dst_slot = 0;
+  int dset = 0;          // phase entry points: 0 = the matrices, 1 = the apply's Q operands
+  float scale = 1.f;     // ST_UNPACK: value scale (times nu^2 when use_nu2)
+  bool use_nu2 = false;
   // accounting for profiles: name, useful FLOPs, executed MFMA FLOPs, algorithmic bytes
   const char* name = "";
   double useful = 0, raw = 0, bytes = 0;
@@ -168,6 +174,12 @@ struct Plan {
   bool use_idx = false;
   std::vector<MatPlan> mats;
   int64_t total_rows = 0, total_sel = 0;
+  // phase entry points: a second descriptor set (the apply's Q operands, one
+  // per matrix, rows counted after the matrices' rows), host-written scalars
+  int nq = 0;
+  int64_t x_rows = 0, x_sel = 0;
+  bool host_scalars = false;
+  std::vector<MatScalars> hscal;
   size_t off_descs = 0, off_scalars = 0, off_keys = 0, off_flags = 0, off_idx = 0, off_ints = 0,
          off_data = 0, total = 0, upload_bytes = 0;
   std::vector<int> ints;
@@ -232,6 +244,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     P.total_rows += R;
     P.total_sel += mp.k;
   }
+  P.x_rows = P.total_rows;
+  P.x_sel = P.total_sel;
   size_t off = 0;
   P.off_descs = off;
   off = align256(off + sizeof(MatDesc) * batch);
@@ -673,6 +687,211 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   return DION_OK;
 }
 
+// ------------------------------------------------- phase entry points
+// One phase of the path on its own, for kernel-level checks: the same
+// kernels, descriptors and workspace layout as the full plan, with an unpack
+// of the m x m result to fp32 where the phase's output is internal.
+enum PhaseKind { PH_KEYS = 1, PH_SYRK = 2, PH_POLY = 3, PH_APPLY = 4 };
+
+bool phase_fp64(int precision, int dtype) {
+  return precision == DION_PREC_FP64 || (precision == DION_PREC_AUTO && dtype == DION_FP32);
+}
+
+int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int precision, double row_frac,
+                     const float* coeffs, Plan& P) {
+  if (!shapes) return fail(DION_E_INVAL, "shapes is NULL");
+  if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
+  if (dtype != DION_BF16 && dtype != DION_FP32) return fail(DION_E_INVAL, "unknown dtype");
+  if (precision < DION_PREC_AUTO || precision > DION_PREC_FP64) return fail(DION_E_INVAL, "unknown precision");
+  if (!(row_frac > 0.0 && row_frac <= 1.0)) return fail(DION_E_INVAL, "row_frac must be in (0, 1]");
+  P.fp64 = phase_fp64(precision, dtype);
+  P.bf16_in = dtype == DION_BF16;
+  P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;
+  P.use_idx = row_frac < 1.0;
+  P.mats.resize(batch);
+  for (int i = 0; i < batch; ++i) {
+    const int R = shapes[i].rows, C = shapes[i].cols;
+    if (R < 1 || C < 1) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + ": rows and cols must be >= 1");
+    if ((int64_t)R * C > ((int64_t)1 << 40)) return fail(DION_E_INVAL, "matrix too large");
+    if (ph == PH_POLY && R != C) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " must be square");
+    MatPlan& mp = P.mats[i];
+    mp.R = R;
+    mp.C = C;
+    mp.k = selected_count(R, row_frac);
+    mp.tall = mp.k > C;
+    mp.m = std::min(mp.k, C);
+    mp.n = std::max(mp.k, C);
+    mp.m_pad = pad_up(mp.m);
+    mp.n_pad = pad_up(mp.n);
+    mp.acc = false;
+    for (int s2 = 0; s2 < N_SLOTS; ++s2) mp.off[s2] = 0;
+    P.total_rows += R;
+    P.total_sel += mp.k;
+  }
+  P.x_rows = P.total_rows;
+  P.x_sel = P.total_sel;
+  if (ph == PH_APPLY) {
+    P.nq = batch;
+    for (const MatPlan& mp : P.mats) {
+      P.total_rows += mp.m;
+      P.total_sel += mp.m;
+    }
+  }
+  const int ndesc = batch + P.nq;
+  const size_t es = P.fp64 ? 8 : 2;
+  const size_t terms = P.fp64 ? 1 : 2;
+
+  std::vector<int> all(batch), wide, tall;
+  for (int i = 0; i < batch; ++i) {
+    all[i] = i;
+    (P.mats[i].tall ? tall : wide).push_back(i);
+  }
+  auto counts = [&](const std::vector<int>& ms, std::function<int(const MatPlan&)> f) {
+    std::vector<int> c;
+    for (int i : ms) c.push_back(f(P.mats[i]));
+    return c;
+  };
+  auto total_of = [](const std::vector<int>& c) { long long t = 0; for (int x : c) t += x; return t; };
+  auto pick = [&](std::function<std::vector<int>(int)> cnt) {
+    if (P.fp64) return 64;
+    return total_of(cnt(256)) >= 512 ? 256 : 128;
+  };
+  const int t_pack = add_table(P, all, counts(all, [](const MatPlan& mp) { return (mp.m_pad / 64) * (mp.n_pad / 64); }));
+  const int t_mm64 = add_table(P, all, counts(all, [](const MatPlan& mp) { return (mp.m_pad / 64) * (mp.m_pad / 64); }));
+  const int bm_sym = pick([&](int bm) {
+    return counts(all, [bm](const MatPlan& mp) { const int T = mp.m_pad / bm; return T * (T + 1) / 2; });
+  });
+  const int t_sym = add_table(P, all, counts(all, [bm_sym](const MatPlan& mp) {
+    const int T = mp.m_pad / bm_sym; return T * (T + 1) / 2; }));
+  auto rect = [&](const std::vector<int>& ms, int bm) {
+    return counts(ms, [bm](const MatPlan& mp) { return (mp.m_pad / bm) * (mp.n_pad / bm); });
+  };
+  const int bm_fin = pick([&](int bm) {
+    auto a = rect(wide, bm), b = rect(tall, bm);
+    a.insert(a.end(), b.begin(), b.end());
+    return a;
+  });
+  const int t_wide = add_table(P, wide, rect(wide, bm_fin));
+  const int t_tall = add_table(P, tall, rect(tall, bm_fin));
+
+  size_t off = 0;
+  P.off_descs = off;
+  off = align256(off + sizeof(MatDesc) * ndesc);
+  P.off_ints = off;
+  off = align256(off + sizeof(int) * P.ints.size());
+  if (ph == PH_POLY) {  // the operand scale is known on the host: ||G||_2 <= 1
+    P.host_scalars = true;
+    P.off_scalars = off;
+    off = align256(off + sizeof(MatScalars) * ndesc);
+    P.hscal.resize(ndesc);
+    for (MatScalars& sc : P.hscal) {
+      sc.nu2 = 1.0;
+      sc.e = P.fp64 ? 0 : 14;  // |G_ij| <= 1 -> |G_ij * 2^14| <= 2^14
+      sc.x0_alpha64 = std::ldexp(1.0, -sc.e);
+      sc.x0_alpha = (float)sc.x0_alpha64;
+    }
+  }
+  P.upload_bytes = off;
+  if (ph != PH_POLY) {
+    P.off_scalars = off;
+    off = align256(off + sizeof(MatScalars) * ndesc);
+  }
+  P.off_keys = off;  off = align256(off + sizeof(double) * P.total_rows);
+  P.off_flags = off; off = align256(off + P.total_rows);
+  P.off_idx = off;   off = align256(off + sizeof(int) * P.total_sel);
+  P.off_data = off;
+  if (ph != PH_KEYS) {
+    for (MatPlan& mp : P.mats) {
+      const size_t mn = (size_t)mp.m_pad * mp.n_pad, mm = (size_t)mp.m_pad * mp.m_pad;
+      mp.off[SLOT_X] = off;   off = align256(off + mn * es);
+      mp.off[SLOT_XT0] = off; off = align256(off + mn * es * terms);
+      mp.off[SLOT_MM0] = off; off = align256(off + mm * es * terms);
+      if (ph == PH_APPLY) { mp.off[SLOT_MM1] = off; off = align256(off + mm * es * terms); }
+    }
+  }
+  P.total = off;
+
+  auto step = [&](StepKind kind, const char* name, int dset = 0, int table = 0) {
+    Step st;
+    st.kind = kind;
+    st.name = name;
+    st.dset = dset;
+    st.table = table;
+    P.steps.push_back(st);
+    return &P.steps.back();
+  };
+  auto gemm = [&](int table, int bm, bool sym, int na, int nb, int epi, const PhaseArgs& pa, const char* name) {
+    Step* g = step(ST_GEMM, name, 0, table);
+    g->bm = bm;
+    g->sym = sym;
+    g->na = P.fp64 ? 1 : na;
+    g->nb = P.fp64 ? 1 : nb;
+    g->epi = epi;
+    g->pa = pa;
+    g->pa.out_lo = 1;
+  };
+  const float sG = P.fp64 ? 1.f : pow2_scale(1.0);
+  if (ph == PH_KEYS || ph == PH_SYRK || ph == PH_APPLY) {
+    step(ST_KEYS, "rowkeys");
+    step(ST_SELECT, "select");
+  }
+  if (ph == PH_APPLY) {
+    step(ST_KEYS, "rowkeys", 1);
+    step(ST_SELECT, "select", 1);
+    step(ST_COMBINE, "combine");
+    step(ST_PACK, "pack", 1, t_mm64);
+  }
+  if (ph != PH_KEYS) step(ST_PACK, "pack", 0, t_pack);
+  if (ph == PH_SYRK) {  // G = X X^T / nu^2 (one fp16 term of X), unpacked times nu^2
+    PhaseArgs pa{};
+    pa.a_slot = pa.b_slot = SLOT_X;
+    pa.c_slot = SLOT_MM0;
+    pa.k_is_n = 1;
+    pa.alpha = sG;
+    pa.alpha_pow = 2;
+    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk");
+    Step* u = step(ST_UNPACK, "unpack", 0, t_mm64);
+    u->src_slot = SLOT_MM0;
+    u->scale = 1.f / sG;
+    u->use_nu2 = true;
+  } else if (ph == PH_POLY) {  // P = a I + b G + c G^2 from G^T in XT0 (two terms)
+    const double a = coeffs[0], b = coeffs[1], c = coeffs[2];
+    const float sP = P.fp64 ? 1.f : pow2_scale(std::fabs(a) + std::fabs(b) + std::fabs(c));
+    const float sX = (float)P.hscal[0].x0_alpha64;
+    PhaseArgs pa{};
+    pa.a_slot = pa.b_slot = pa.aux_slot = SLOT_XT0;
+    pa.c_slot = SLOT_MM0;
+    pa.alpha = sX * sX;
+    pa.poly_a = (float)a;
+    pa.poly_b = (float)b;
+    pa.poly_c = (float)c;
+    pa.aux_inv_scale = sX;
+    pa.out_scale = sP;
+    gemm(t_sym, bm_sym, true, 2, 2, EPI_POLY, pa, "gram_poly");
+    Step* u = step(ST_UNPACK, "unpack", 0, t_mm64);
+    u->src_slot = SLOT_MM0;
+    u->scale = 1.f / sP;
+  } else if (ph == PH_APPLY) {  // Y = Q X (wide) or X Q (tall), scale 2^-(e_X + e_Q)
+    PhaseArgs pa{};
+    pa.alpha = 1.f;
+    pa.alpha_pow = 1;
+    pa.out_fp32 = dtype == DION_FP32 ? 1 : 0;
+    PhaseArgs pw = pa;
+    pw.a_slot = SLOT_MM0;
+    pw.b_slot = SLOT_XT0;
+    pw.b_rows_is_n = 1;
+    pw.out_rows_are_m = 1;
+    if (!wide.empty()) gemm(t_wide, bm_fin, false, 2, P.xterms0, EPI_OUT, pw, "final");
+    PhaseArgs pt = pa;
+    pt.a_slot = SLOT_XT0;
+    pt.b_slot = SLOT_MM0;
+    pt.a_rows_is_n = 1;
+    pt.out_rows_are_m = 0;
+    if (!tall.empty()) gemm(t_tall, bm_fin, false, P.xterms0, 2, EPI_OUT, pt, "final");
+  }
+  return DION_OK;
+}
+
 // ---------------------------------------------------- pinned upload stage
 struct Stage {
   void* host[2] = {nullptr, nullptr};
@@ -735,6 +954,8 @@ const char* kernel_name(const Plan& P, const Step& st) {
     case ST_PACK: return P.fp64 ? "dion::k_pack" : "dion::k_pack16";
     case ST_TRANSPOSE: return "dion::k_transpose";
     case ST_COPY: return "dion::k_copy_unselected";
+    case ST_UNPACK: return "dion::k_unpack";
+    case ST_COMBINE: return "dion::k_scale_combine";
     case ST_GEMM:
       if (P.fp64)
         key = "dion::k_gemm64<" + std::to_string(st.epi) + ", " + (st.sym ? "true" : "false") + ">";
@@ -780,7 +1001,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int run(const Plan& P, const void* const* M, void* const* out, const void* const* grad, int batch, int dtype,
         int grad_dtype, float beta, bool step_mode, int32_t* sel_idx, void* workspace, size_t ws_bytes,
-        hipStream_t stream) {
+        hipStream_t stream, const void* const* Qs = nullptr, double* keys_out = nullptr) {
   if (!workspace) return fail(DION_E_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255) != 0) return fail(DION_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < P.total)
@@ -794,7 +1015,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     const MatPlan& mp = P.mats[i];
     MatDesc& d = descs[i];
     d.M = M[i];
-    d.out = out[i];
+    d.out = out ? out[i] : nullptr;
     d.grad = grad ? grad[i] : nullptr;
     for (int s = 0; s < N_SLOTS; ++s) d.buf[s] = mp.off[s] ? ws + mp.off[s] : nullptr;
     d.row0 = row0;
@@ -810,7 +1031,26 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     row0 += mp.R;
     sel0 += mp.k;
   }
+  // the apply's Q operands (m x m fp32): packed as they are into MM0 (two
+  // terms) for wide matrices, transposed for tall ones, through the pack's
+  // tall / wide roles; their rows, keys and indices are counted from 0
+  row0 = sel0 = 0;
+  for (int i = 0; i < P.nq; ++i) {
+    const MatPlan& mp = P.mats[i];
+    MatDesc& d = descs[batch + i];
+    d.M = Qs[i];
+    d.buf[SLOT_XT0] = ws + mp.off[SLOT_MM0];
+    d.buf[SLOT_X] = ws + mp.off[SLOT_MM1];
+    d.row0 = row0;
+    d.sel0 = sel0;
+    d.R = d.C = d.k = d.m = d.n = mp.m;
+    d.m_pad = d.n_pad = mp.m_pad;
+    d.tall = mp.tall ? 0 : 1;
+    row0 += mp.m;
+    sel0 += mp.m;
+  }
   std::memcpy(blob.data() + P.off_ints, P.ints.data(), sizeof(int) * P.ints.size());
+  if (P.host_scalars) std::memcpy(blob.data() + P.off_scalars, P.hscal.data(), sizeof(MatScalars) * P.hscal.size());
   int rc = upload(blob.data(), blob.size(), ws, stream);
   if (rc) return rc;
 
@@ -831,20 +1071,30 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
       if (!rec.a || !rec.b || hipEventRecord(rec.a, stream) != hipSuccess)
         return fail(DION_E_HIP, "profiling event failed");
     }
+    // descriptor set of the step: the matrices, or the apply's Q operands
+    const bool qset = st.dset == 1;
+    const MatDesc* sd = qset ? d_descs + batch : d_descs;
+    MatScalars* ss = qset ? d_scal + batch : d_scal;
+    const int sn = qset ? P.nq : batch;
+    const int64_t srows = qset ? P.total_rows - P.x_rows : P.x_rows;
+    double* skeys = qset ? d_keys + P.x_rows : d_keys;
+    uint8_t* sflags = qset ? d_flags + P.x_rows : d_flags;
+    int* sidx = qset ? d_idx + P.x_sel : d_idx;
+    const bool s_bf16 = qset ? false : in_bf16;
     switch (st.kind) {
       case ST_KEYS:
-        launch_rowkeys(in_bf16, d_descs, batch, P.total_rows, d_keys, stream);
+        launch_rowkeys(s_bf16, sd, sn, srows, skeys, stream);
         break;
       case ST_MOMENTUM:
         launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, beta, d_keys, stream);
         break;
       case ST_SELECT:
-        launch_select(d_descs, batch, d_keys, d_flags, d_idx, d_scal, P.fp64, stream);
+        launch_select(sd, sn, skeys, sflags, sidx, ss, P.fp64, stream);
         break;
       case ST_PACK: {
         const Table& t = P.tabs[st.table];
-        launch_pack(in_bf16, P.fp64, d_descs, d_ints + t.prefix_off, t.nmat, t.total, d_idx, d_scal, P.xterms0,
-                    P.use_idx, stream);
+        launch_pack(s_bf16, P.fp64, sd, d_ints + t.prefix_off, t.nmat, t.total, sidx, ss,
+                    qset ? 2 : P.xterms0, P.use_idx && !qset, stream);
         break;
       }
       case ST_TRANSPOSE: {
@@ -866,6 +1116,15 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
       case ST_COPY:
         launch_copy_unselected(in_bf16, d_descs, batch, P.total_rows, d_flags, stream);
         break;
+      case ST_UNPACK: {
+        const Table& t = P.tabs[st.table];
+        launch_unpack(P.fp64, d_descs, d_ints + t.prefix_off, t.nmat, t.total, st.src_slot, d_scal, st.scale,
+                      st.use_nu2, stream);
+        break;
+      }
+      case ST_COMBINE:
+        launch_scale_combine(d_scal, batch, stream);
+        break;
     }
     if (g_prof.on) {
       if (hipEventRecord(rec.b, stream) != hipSuccess) return fail(DION_E_HIP, "profiling event failed");
@@ -873,8 +1132,12 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     }
   }
   if (sel_idx) {
-    if (hipMemcpyAsync(sel_idx, d_idx, sizeof(int) * P.total_sel, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    if (hipMemcpyAsync(sel_idx, d_idx, sizeof(int) * P.x_sel, hipMemcpyDeviceToDevice, stream) != hipSuccess)
       return fail(DION_E_HIP, "copy of selected indices failed");
+  }
+  if (keys_out) {
+    if (hipMemcpyAsync(keys_out, d_keys, sizeof(double) * P.x_rows, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(DION_E_HIP, "copy of row keys failed");
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DION_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -970,6 +1233,96 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
   if (rc) return rc;
   return run(P, (const void* const*)E, out, grad, batch, DION_FP32, grad_dtype, beta, true, sel_idx, workspace,
              workspace_bytes, (hipStream_t)stream);
+}
+
+size_t dion_phase_workspace_size(int32_t phase, const dion_shape* shapes, int32_t batch, int32_t dtype,
+                                 int32_t precision, float row_frac) {
+  if (phase < PH_KEYS || phase > PH_APPLY) return 0;
+  static const float kOne[3] = {1.f, 0.f, 0.f};
+  Plan P;
+  const int dt = phase == PH_POLY ? DION_FP32 : dtype;
+  if (build_phase_plan(phase, shapes, batch, dt, precision, phase == PH_KEYS ? row_frac : 1.0, kOne, P)) return 0;
+  return P.total;
+}
+
+int dion_rowkeys_topk_batched(const void* const* M, const dion_shape* shapes, int32_t batch, int32_t dtype,
+                              float row_frac, double* keys, int32_t* sel_idx, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Plan P;
+  int rc = build_phase_plan(PH_KEYS, shapes, batch, dtype, DION_PREC_MFMA16, row_frac, nullptr, P);
+  if (rc) return rc;
+  if (!M) return fail(DION_E_INVAL, "matrix pointer array is NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!M[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
+  return run(P, M, nullptr, nullptr, batch, dtype, dtype, 0.f, false, sel_idx, workspace, workspace_bytes,
+             (hipStream_t)stream, nullptr, keys);
+}
+
+int dion_syrk_batched(const void* const* X, float* const* G, const dion_shape* shapes, int32_t batch,
+                      int32_t dtype, int32_t precision, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Plan P;
+  int rc = build_phase_plan(PH_SYRK, shapes, batch, dtype, precision, 1.0, nullptr, P);
+  if (rc) return rc;
+  if (!X || !G) return fail(DION_E_INVAL, "pointer arrays are NULL");
+  std::vector<dion_shape> gs(batch);
+  for (int i = 0; i < batch; ++i) {
+    if (!X[i] || !G[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
+    gs[i] = {P.mats[i].m, P.mats[i].m};
+  }
+  const size_t es = dtype == DION_BF16 ? 2 : 4;
+  for (int i = 0; i < batch; ++i)
+    for (int j = 0; j < batch; ++j)
+      if (overlaps(G[i], (size_t)gs[i].rows * gs[i].cols * 4, X[j], (size_t)shapes[j].rows * shapes[j].cols * es))
+        return fail(DION_E_INVAL, "G must not overlap the inputs");
+  return run(P, X, (void* const*)G, nullptr, batch, dtype, dtype, 0.f, false, nullptr, workspace, workspace_bytes,
+             (hipStream_t)stream);
+}
+
+int dion_sympoly_batched(const float* const* G, float* const* Pout, const int32_t* m, int32_t batch,
+                         const float* coeffs, int32_t precision, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_last_error.clear();
+  if (!m) return fail(DION_E_INVAL, "m is NULL");
+  if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
+  const float* co = coeffs ? coeffs : kQuintic;
+  if (!std::isfinite(co[0]) || !std::isfinite(co[1]) || !std::isfinite(co[2]))
+    return fail(DION_E_INVAL, "coefficients must be finite");
+  std::vector<dion_shape> shapes(batch);
+  for (int i = 0; i < batch; ++i) shapes[i] = {m[i], m[i]};
+  Plan P;
+  int rc = build_phase_plan(PH_POLY, shapes.data(), batch, DION_FP32, precision, 1.0, co, P);
+  if (rc) return rc;
+  if (!G || !Pout) return fail(DION_E_INVAL, "pointer arrays are NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!G[i] || !Pout[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
+  rc = check_ptrs((const void* const*)G, (void* const*)Pout, shapes.data(), batch, 4, 4);
+  if (rc) return rc;
+  return run(P, (const void* const*)G, (void* const*)Pout, nullptr, batch, DION_FP32, DION_FP32, 0.f, false,
+             nullptr, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int dion_apply_batched(const float* const* Q, const void* const* X, void* const* Y, const dion_shape* shapes,
+                       int32_t batch, int32_t dtype, int32_t precision, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  g_last_error.clear();
+  Plan P;
+  int rc = build_phase_plan(PH_APPLY, shapes, batch, dtype, precision, 1.0, nullptr, P);
+  if (rc) return rc;
+  if (!Q || !X || !Y) return fail(DION_E_INVAL, "pointer arrays are NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!Q[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL Q pointer");
+  const size_t es = dtype == DION_BF16 ? 2 : 4;
+  rc = check_ptrs(X, Y, shapes, batch, es, es);
+  if (rc) return rc;
+  for (int i = 0; i < batch; ++i)
+    for (int j = 0; j < batch; ++j)
+      if (overlaps(Y[i], (size_t)shapes[i].rows * shapes[i].cols * es, Q[j],
+                   (size_t)P.mats[j].m * P.mats[j].m * 4))
+        return fail(DION_E_INVAL, "Y must not overlap the inputs");
+  return run(P, X, Y, nullptr, batch, dtype, dtype, 0.f, false, nullptr, workspace, workspace_bytes,
+             (hipStream_t)stream, (const void* const*)Q);
 }
 
 double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_params* p) {

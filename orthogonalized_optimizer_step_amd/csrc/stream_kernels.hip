@@ -457,6 +457,56 @@ __global__ __launch_bounds__(256) void k_copy_unselected(const MatDesc* __restri
   for (int c = lane; c < d.C; c += 64) dst[c] = src[c];
 }
 
+// ------------------------------------------------------------ unpack
+// Phase entry points: an m x m workspace matrix (slot `slot`; MFMA16: fp16
+// hi + lo, panel-blocked; FP64: row-major doubles) -> out (m x m fp32,
+// row-major), each value times `scale` (and times the matrix's nu^2 when
+// use_nu2).  64 x 64 tiles of the padded matrix; padding is not written.
+template <typename ST>
+__global__ __launch_bounds__(256) void k_unpack(const MatDesc* __restrict__ descs,
+                                                const int* __restrict__ prefix, int nmat, int total,
+                                                int slot, const MatScalars* __restrict__ scalars,
+                                                float scale, int use_nu2) {
+  const int t = blockIdx.x;
+  if (t >= total) return;
+  int lo = 0, hi = nmat;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= t) lo = mid; else hi = mid;
+  }
+  const MatDesc& d = descs[lo];
+  const int local = t - prefix[lo];
+  const int tm = d.m_pad / 64;
+  const int r0 = (local / tm) * 64, c0 = (local % tm) * 64;
+  const double sc = (double)scale * (use_nu2 ? scalars[lo].nu2 : 1.0);
+  float* out = (float*)d.out;
+  const size_t ts = (size_t)d.m_pad * d.m_pad;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = r0 + (i >> 6), c = c0 + (i & 63);
+    if (r >= d.m || c >= d.m) continue;
+    double v;
+    if (sizeof(ST) == 8) {
+      v = ((const double*)d.buf[slot])[(size_t)r * d.m_pad + c];
+    } else {
+      const _Float16* b = (const _Float16*)d.buf[slot];
+      const size_t o = blk_off(r, c, d.m_pad);
+      v = (double)(float)b[o] + (double)(float)b[o + ts];
+    }
+    out[(size_t)r * d.m + c] = (float)(v * sc);
+  }
+}
+
+// Phase entry point for the apply: descs [0, nmat) are the X operands and
+// [nmat, 2 nmat) the Q operands, each packed as stored * 2^e; the product's
+// scale 2^-(e_X + e_Q) goes to the X scalars' x0_alpha.
+__global__ void k_scale_combine(MatScalars* __restrict__ scalars, int nmat) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nmat) return;
+  const int e = scalars[i].e + scalars[nmat + i].e;
+  scalars[i].x0_alpha64 = ldexp(1.0, -e);
+  scalars[i].x0_alpha = (float)scalars[i].x0_alpha64;
+}
+
 // ---------------------------------------------------------------- launchers
 static inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + 3) / 4); }
 
@@ -502,6 +552,17 @@ void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t r
                             const uint8_t* flags, hipStream_t s) {
   if (bf16) hipLaunchKernelGGL(k_copy_unselected<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags);
   else hipLaunchKernelGGL(k_copy_unselected<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags);
+}
+
+void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total, int slot,
+                   const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s) {
+  if (total <= 0) return;
+  if (fp64_path) hipLaunchKernelGGL(k_unpack<double>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, slot, scalars, scale, use_nu2 ? 1 : 0);
+  else hipLaunchKernelGGL(k_unpack<_Float16>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, slot, scalars, scale, use_nu2 ? 1 : 0);
+}
+
+void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s) {
+  hipLaunchKernelGGL(k_scale_combine, dim3((nmat + 255) / 256), dim3(256), 0, s, scalars, nmat);
 }
 
 }  // namespace dion

@@ -114,3 +114,23 @@ def test_orth_validation_errors_before_launch():
     assert lib.dion_rowsubset_step(E, g, fake_out, shp, 1, 0, ctypes.c_float(0.9), ctypes.byref(pf), None,
                                    ctypes.c_void_p(0x10000), 1 << 30, None) == -2
     assert lib.dion_strerror(-2) == b"unsupported combination"
+
+
+def test_phase_workspace_sizes_and_validation():
+    """Host-side checks of the phase entry points: sizes, and argument errors
+    returned before any launch (NULL pointers, non-square polynomial input)."""
+    L = _lib.lib
+    shp = dion._shapes([(300, 200), (64, 640)])
+    for ph in (1, 2, 4):
+        assert L.dion_phase_workspace_size(ph, shp, 2, _lib.DION_BF16, 1, ctypes.c_float(0.5)) > 0
+    assert L.dion_phase_workspace_size(3, shp, 2, _lib.DION_FP32, 1, ctypes.c_float(1.0)) == 0  # not square
+    assert L.dion_phase_workspace_size(3, dion._shapes([(64, 64)]), 1, _lib.DION_FP32, 2, ctypes.c_float(1.0)) > 0
+    assert L.dion_phase_workspace_size(9, shp, 2, _lib.DION_BF16, 1, ctypes.c_float(1.0)) == 0   # no such phase
+    assert L.dion_phase_workspace_size(2, shp, 2, 7, 1, ctypes.c_float(1.0)) == 0                  # bad dtype
+    null2 = (ctypes.c_void_p * 2)(None, None)
+    assert L.dion_syrk_batched(null2, null2, shp, 2, _lib.DION_BF16, 1, None, 0, None) == -1
+    assert L.dion_apply_batched(null2, null2, null2, shp, 2, _lib.DION_BF16, 1, None, 0, None) == -1
+    assert L.dion_rowkeys_topk_batched(null2, shp, 2, _lib.DION_BF16, ctypes.c_float(0.0), None, None, None, 0,
+                                       None) == -1                                              # row_frac 0
+    ms = (ctypes.c_int32 * 1)(0)
+    assert L.dion_sympoly_batched(null2, null2, ms, 1, None, 1, None, 0, None) == -1             # m = 0

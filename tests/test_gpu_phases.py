@@ -1,0 +1,211 @@
+"""Parity of the phase entry points (one step of the path on its own, through
+the C ABI) with the oracle's single steps: row keys and top-k, the Gram
+matrix, the Gram polynomial and the apply on the Gram side.
+
+Gates, derived from the arithmetic of each path:
+  keys     relative 1e-12 per row (fp64 sums of exact squares, other order);
+           selected rows bit-exact (exchanges only between keys within 4 ulps)
+  MFMA16   bf16 operands are exact in fp16 and products accumulate in fp32:
+           relative Frobenius 2e-5 on fp32 outputs; fp32 operands of the Gram
+           product take one fp16 term (2^-11 relative each): 2e-3; two-term
+           operands (Q, G, fp32 X of the apply): 2e-5
+  bf16 out round to nearest even: at most 2^-8 relative per element, so
+           relative Frobenius 2^-8 + 2e-5
+  FP64     only the final fp32 rounding: 1e-7
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import dion_oracle as O  # noqa: E402
+from workloads import lowrank_np, round_bf16  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+TOL_ACC = 2e-5
+TOL_GRAM_FP32_ONE_TERM = 2e-3
+TOL_BF16_OUT = 2.0 ** -8 + 2e-5
+TOL_FP64 = 1e-7
+
+SHAPES = [(7, 33), (33, 7), (300, 200), (200, 520), (1, 5), (5, 1), (257, 511), (64, 64)]
+
+
+@pytest.fixture(scope="module")
+def dion():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import orthogonalized_optimizer_step_amd as d
+    return d
+
+
+def dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(dt)
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def batch(seed, shapes, bf16=True):
+    out = []
+    for i, (r, c) in enumerate(shapes):
+        M = lowrank_np((seed, i), r, c, max(1, min(r, c) // 8), 0.1, log_scale=(-3.0, 0.0))
+        out.append(round_bf16(M) if bf16 else M.astype(np.float32))
+    return out
+
+
+def sym_unit_gram(seed, m):
+    """Symmetric PSD fp32 matrix with spectral norm <= 1: the Gram matrix of a
+    Frobenius-normalized random block, symmetrized before rounding."""
+    S = lowrank_np((seed, m), m, m + 37, max(1, m // 4), 0.2)
+    S = S / np.linalg.norm(S.astype(np.float64))
+    G = O.gram(S)
+    return ((G + G.T) / 2).astype(np.float32)
+
+
+def assert_selection(idx_gpu, M, frac):
+    ref = O.select_rows(M, frac)
+    got = np.asarray(idx_gpu, dtype=np.int64)
+    assert got.shape == ref.shape and np.all(np.diff(got) > 0)
+    if np.array_equal(got, ref):
+        return
+    keys = O.row_keys(M)
+    kd = keys[np.setxor1d(got, ref)]
+    assert np.max(kd) - np.min(kd) <= 4 * np.spacing(np.max(kd))
+
+
+# ------------------------------------------------------------ rowkeys + top-k
+@pytest.mark.parametrize("frac", [1.0, 0.5, 0.125, 1.0 / 37])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_rowkeys_topk_random(dion, frac, bf16):
+    Ms = batch(21, SHAPES, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    keys, idx = dion.rowkeys_topk([dev(M, dt) for M in Ms], row_frac=frac)
+    for M, k, ix in zip(Ms, keys, idx):
+        ref = O.row_keys(M)
+        got = k.cpu().numpy()
+        assert np.all(np.abs(got - ref) <= 1e-12 * ref + 1e-300), M.shape
+        assert_selection(ix.cpu().numpy(), M, frac)
+
+
+def test_rowkeys_topk_ties_and_zero_rows(dion):
+    """Integer entries: keys are exact integers on both sides, so the
+    selection (ties to the lower row index) must match bit for bit."""
+    rng = np.random.default_rng(5)
+    Ms = []
+    for r, c in [(37, 16), (64, 20), (16, 300), (520, 40)]:
+        M = rng.integers(-4, 5, size=(r, c)).astype(np.float32)
+        M[rng.integers(0, r, size=r // 4)] = 0.0
+        M[r // 2] = M[0]
+        M[r - 1] = M[1]
+        Ms.append(M)
+    for frac in (0.25, 0.5, 1.0 / 37):
+        keys, idx = dion.rowkeys_topk([dev(M, torch.bfloat16) for M in Ms], row_frac=frac)
+        for M, k, ix in zip(Ms, keys, idx):
+            assert np.array_equal(k.cpu().numpy(), O.row_keys(M))
+            assert np.array_equal(ix.cpu().numpy(), O.select_rows(M, frac))
+
+
+def test_rowkeys_topk_full_size(dion):
+    """Llama-3-8B q and gate shapes at 1/8 of the rows, as the row-subset step selects."""
+    Ms = [round_bf16(lowrank_np((3, 0, 0), 4096, 4096, 64, 0.05, log_scale=(-3, 0))),
+          round_bf16(lowrank_np((3, 0, 4), 14336, 4096, 64, 0.05, log_scale=(-3, 0)))]
+    keys, idx = dion.rowkeys_topk([dev(M, torch.bfloat16) for M in Ms], row_frac=0.125)
+    for M, k, ix in zip(Ms, keys, idx):
+        ref = O.row_keys(M)
+        assert np.all(np.abs(k.cpu().numpy() - ref) <= 1e-12 * ref)
+        assert_selection(ix.cpu().numpy(), M, 0.125)
+
+
+# ------------------------------------------------------------------- Gram
+@pytest.mark.parametrize("prec,bf16,tol", [("mfma16", True, TOL_ACC), ("mfma16", False, TOL_GRAM_FP32_ONE_TERM),
+                                           ("fp64", False, TOL_FP64), ("fp64", True, TOL_FP64)])
+def test_syrk_ragged(dion, prec, bf16, tol):
+    Ms = batch(22, SHAPES, bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    Gs = dion.syrk([dev(M, dt) for M in Ms], precision=prec)
+    errs = [O.rel_frobenius(to_np(G), O.gram(M)) for M, G in zip(Ms, Gs)]
+    print(f"syrk {prec} {'bf16' if bf16 else 'fp32'}:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= tol
+
+
+def test_syrk_zero_matrix(dion):
+    Gs = dion.syrk([torch.zeros((12, 40), dtype=torch.bfloat16, device="cuda")], precision="mfma16")
+    assert torch.count_nonzero(Gs[0]) == 0 and tuple(Gs[0].shape) == (12, 12)
+
+
+def test_syrk_full_size(dion):
+    """Three 4096 x 4096 and one 14336 x 4096 (tall: X^T X) bf16 matrices:
+    544 upper-triangle tiles, so the 256 x 256 tile kernel the benchmark runs."""
+    shapes = [(4096, 4096)] * 3 + [(14336, 4096)]
+    Ms = [round_bf16(lowrank_np((3, 0, j), r, c, 64, 0.05, log_scale=(-3, 0))) for j, (r, c) in enumerate(shapes)]
+    Gs = dion.syrk([dev(M, torch.bfloat16) for M in Ms], precision="mfma16")
+    errs = [O.rel_frobenius(to_np(G), O.gram(M)) for M, G in zip(Ms, Gs)]
+    print("syrk full size:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= TOL_ACC
+
+
+# -------------------------------------------------------- Gram polynomial
+@pytest.mark.parametrize("prec,tol", [("mfma16", TOL_ACC), ("fp64", TOL_FP64)])
+@pytest.mark.parametrize("coeffs", [QUINTIC, (1.5, -0.5, 0.0), (3.4445 / 1.05, -4.7750 / 1.05 ** 3,
+                                                                 2.0315 / 1.05 ** 5)])
+def test_sympoly(dion, prec, tol, coeffs):
+    Gs = [sym_unit_gram(23, m) for m in (1, 7, 64, 257, 300)]
+    Ps = dion.sympoly([torch.from_numpy(G).cuda() for G in Gs], coeffs=coeffs, precision=prec)
+    errs = [O.rel_frobenius(to_np(P), O.gram_polynomial(G, *coeffs)) for G, P in zip(Gs, Ps)]
+    print(f"sympoly {prec} {coeffs}:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= tol
+
+
+def test_sympoly_full_size(dion):
+    """Four 4096 x 4096 Gram matrices (544 upper tiles: the 256-tile kernel)."""
+    Gs = [sym_unit_gram(24 + i, 4096) for i in range(4)]
+    Ps = dion.sympoly([torch.from_numpy(G).cuda() for G in Gs], precision="mfma16")
+    errs = [O.rel_frobenius(to_np(P), O.gram_polynomial(G, *QUINTIC)) for G, P in zip(Gs, Ps)]
+    print("sympoly full size:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= TOL_ACC
+
+
+# ------------------------------------------------------------------ apply
+def general_factor(seed, m):
+    """A nonsymmetric fp32 m x m factor: a transposed operand changes the result."""
+    rng = np.random.default_rng([seed, m])
+    return (rng.standard_normal((m, m)) / np.sqrt(m) + np.eye(m)).astype(np.float32)
+
+
+@pytest.mark.parametrize("prec,bf16,tol", [("mfma16", True, TOL_BF16_OUT), ("mfma16", False, TOL_ACC),
+                                           ("fp64", False, TOL_FP64)])
+def test_apply_ragged(dion, prec, bf16, tol):
+    Xs = batch(25, SHAPES, bf16)
+    Qs = [general_factor(25, min(X.shape)) for X in Xs]
+    dt = torch.bfloat16 if bf16 else torch.float32
+    Ys = dion.apply([torch.from_numpy(Q).cuda() for Q in Qs], [dev(X, dt) for X in Xs], precision=prec)
+    errs = [O.rel_frobenius(to_np(Y), O.apply_factor(Q, X)) for Q, X, Y in zip(Qs, Xs, Ys)]
+    print(f"apply {prec} {'bf16' if bf16 else 'fp32'}:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= tol
+    if bf16:  # elementwise: within 2^-8 of each exact value, plus the accumulation
+        for Q, X, Y in zip(Qs, Xs, Ys):
+            ref = O.apply_factor(Q, X)
+            assert np.all(np.abs(to_np(Y) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
+def test_apply_zero_operand(dion):
+    X = torch.zeros((12, 40), dtype=torch.bfloat16, device="cuda")
+    Q = torch.from_numpy(general_factor(1, 12)).cuda()
+    Y = dion.apply([Q], [X], precision="mfma16")[0]
+    assert torch.count_nonzero(Y) == 0
+
+
+def test_apply_full_size(dion):
+    """The down (4096 x 14336, Q X) and gate (14336 x 4096, X Q) shapes with
+    4096 x 4096 factors: 896 tiles each, the 256-tile kernel."""
+    Xs = [round_bf16(lowrank_np((3, 0, 6), 4096, 14336, 64, 0.05, log_scale=(-3, 0))),
+          round_bf16(lowrank_np((3, 0, 4), 14336, 4096, 64, 0.05, log_scale=(-3, 0)))]
+    Qs = [general_factor(26, 4096), general_factor(27, 4096)]
+    Ys = dion.apply([torch.from_numpy(Q).cuda() for Q in Qs], [dev(X, torch.bfloat16) for X in Xs],
+                    precision="mfma16")
+    errs = [O.rel_frobenius(to_np(Y), O.apply_factor(Q, X)) for Q, X, Y in zip(Qs, Xs, Ys)]
+    print("apply full size:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= TOL_BF16_OUT

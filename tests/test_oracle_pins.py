@@ -319,3 +319,44 @@ def test_hyperparameter_expansion():
     with pytest.raises(ValueError):
         O.coefficient_schedule([QUINTIC, QUINTIC], 3)
     assert math.isclose(O.rel_frobenius(np.ones(3), np.ones(3) * 2), 0.5)
+
+
+# ------------------------------------- the single steps of one iteration
+@pytest.mark.parametrize("shape", [(7, 33), (33, 7), (40, 40), (1, 9), (9, 1)])
+def test_gram_spectrum_is_squared_singular_values(shape):
+    """gram(S) is symmetric PSD on the smaller side, with eigenvalues sigma_i^2
+    (LAPACK SVD of S) and eigenvectors the left (wide) / right (tall) singular vectors."""
+    S = RNG.standard_normal(shape)
+    G = O.gram(S)
+    m = min(shape)
+    assert G.shape == (m, m)
+    U, s, Vt = np.linalg.svd(S, full_matrices=False)
+    W = U if shape[0] <= shape[1] else Vt.T
+    assert np.allclose(G, (W * s ** 2) @ W.T, atol=1e-12 * max(1.0, s[0] ** 2))
+    assert np.allclose(np.sort(np.linalg.eigvalsh(G)), np.sort(s ** 2), atol=1e-12 * s[0] ** 2)
+
+
+def test_gram_polynomial_spectral_form():
+    """For G = V diag(lam) V^T (V orthogonal from a seeded QR), a I + b G + c G^2
+    = V diag(a + b lam + c lam^2) V^T."""
+    m = 24
+    V, _ = np.linalg.qr(RNG.standard_normal((m, m)))
+    lam = RNG.uniform(-1.0, 1.0, m)
+    G = (V * lam) @ V.T
+    a, b, c = QUINTIC
+    P = O.gram_polynomial(G, a, b, c)
+    assert np.allclose(P, (V * (a + b * lam + c * lam ** 2)) @ V.T, atol=1e-12)
+    # the identity term sits on the diagonal only
+    assert np.allclose(O.gram_polynomial(np.zeros((3, 3)), 2.0, 5.0, 7.0), 2.0 * np.eye(3))
+
+
+@pytest.mark.parametrize("shape", [(12, 30), (30, 12)])
+def test_one_step_composition_is_one_ns_iteration(shape):
+    """apply_factor(gram_polynomial(gram(X)), X) on a normalized X is one
+    Newton-Schulz iteration: the SVD closed form with K = 1."""
+    S = RNG.standard_normal(shape)
+    X = S / np.linalg.norm(S)
+    a, b, c = QUINTIC
+    Y = O.apply_factor(O.gram_polynomial(O.gram(X), a, b, c), X)
+    assert np.allclose(Y, svd_closed_form(S, QUINTIC, 1), atol=1e-13)
+    assert np.array_equal(O.apply_factor(np.eye(min(shape)), X), X)
