@@ -414,6 +414,14 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   double sb = 1.0;  // bound on the singular values of the current iterate
   int g_slot = SLOT_MM0;
   float sG = sc(sb * sb);
+  // operand terms of the m x m chain in the segment that starts after
+  // iteration k0 (a restart, or k0 = 0): one for segments of at most two
+  // iterations, two for longer ones (see the policy below)
+  auto seg_terms = [&](int k0) {
+    int e = k0 + 1;
+    while (e < K && !prm.restart[e - 1]) ++e;
+    return (P.fp64 || e - k0 > 2) ? 2 : 1;
+  };
   {
     PhaseArgs pa{};
     pa.a_slot = pa.b_slot = SLOT_X;
@@ -421,7 +429,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pa.k_is_n = 1;
     pa.alpha = sG;
     pa.alpha_pow = 2;
-    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", true);
+    // G's lo term is read only by a segment that runs two-term
+    gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", seg_terms(0) == 2);
   }
   std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
   if (any_acc) freel.insert(freel.begin(), {SLOT_MM5, SLOT_MM4});
@@ -481,12 +490,16 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.poly_b = (float)b;
       pa.poly_c = (float)c;
       pa.aux_inv_scale = 1.0f / sG;
+      pa.aux_lo = ct == 2 ? 1 : 0;
       pa.out_scale = sP;
-      // G*G takes the segment's operand terms (the bG term of the epilogue
-      // always reads both).  In a long segment a one-term G*G even at the
-      // segment's first iteration doubles the error of the segments that
-      // follow a restart (emulation: 1.5e-2 -> 7.4e-3 on 256 x 256 with a
-      // restart after iteration 2 of 5).
+      // G*G takes the segment's operand terms, and so does the bG term of
+      // the epilogue.  In a one-term segment bG then reads the same rounding
+      // of G as the product, so P is a polynomial of one matrix: emulated
+      // error 6.0e-3 against 6.3e-3 with a two-term bG (Llama-shaped
+      // 1024 x 4096), and G's lo term is never stored.  In a long segment a
+      // one-term G*G even at the segment's first iteration doubles the error
+      // of the segments that follow a restart (emulation: 1.5e-2 -> 7.4e-3 on
+      // 256 x 256 with a restart after iteration 2 of 5).
       gemm(t_sym, bm_sym, true, ct, ct, EPI_POLY, pa, "gram_poly", ct == 2);
     }
     if (q_slot < 0) {
@@ -604,7 +617,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.c_slot = g_slot;
         pa.k_is_n = 1;
         pa.alpha = sGn / (sXn * sXn);
-        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", true);
+        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", seg_terms(k) == 2);
       }
       sG = sGn;
       xt_slot = xt_new;
@@ -642,7 +655,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.b_slot = t_slot;
         pa.c_slot = g_slot;
         pa.alpha = sGn / (sP * sT);
-        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", true);
+        gemm(t_sym, bm_sym, true, ct, ct, EPI_SYM, pa, "sym_product", ct == 2);
       }
       sG = sGn;
       freel.push_back(t_slot);
@@ -866,6 +879,7 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
     pa.poly_b = (float)b;
     pa.poly_c = (float)c;
     pa.aux_inv_scale = sX;
+    pa.aux_lo = 1;
     pa.out_scale = sP;
     gemm(t_sym, bm_sym, true, 2, 2, EPI_POLY, pa, "gram_poly");
     Step* u = step(ST_UNPACK, "unpack", 0, t_mm64);

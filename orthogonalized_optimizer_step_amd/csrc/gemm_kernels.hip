@@ -180,16 +180,18 @@ __device__ __forceinline__ AT phase_alpha(const MatDesc& d, const PhaseArgs& pa,
 // ------------------------------------------------- strip-staged epilogue
 // Each wave turns its (WT x WT) sub-tile into stores 32 rows ("a strip") at a
 // time: the strip's fp32 values go to LDS row-major, then leave as 16-byte
-// chunks of 8 consecutive columns; for symmetric outputs the strip is written
-// again transposed and leaves as 16-byte chunks of the mirror rows.  Masks are
-// needed only on diagonal tiles (upper half + mirror of the strict upper half)
-// and at the valid edge of the final output.
+// chunks of 8 consecutive columns.  The transposed copy (the mirror of a
+// symmetric output, or X from X^T after a restart) needs no staging: in the
+// accumulator layout a lane holds 4 consecutive rows of one column, which are
+// 4 consecutive columns of a transposed row, so it leaves as 8-byte stores
+// straight from registers.  A diagonal tile of a symmetric output is written
+// whole by the direct stores (both of its triangles are computed) and has no
+// mirror, so no store is masked except at the valid edge of the final output.
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 
 __host__ __device__ constexpr int epi_wave_bytes(int wt) {
-  // max(row-major strip 32 x (wt+8), transposed strip wt x (32+4)) floats
-  return (32 * (wt + 8) > wt * 36 ? 32 * (wt + 8) : wt * 36) * 4;
+  return 32 * (wt + 8) * 4;   // row-major strip 32 x (wt + 8) floats
 }
 
 __device__ __forceinline__ void split8(const float* v, half8v& h, half8v& l) {
@@ -243,11 +245,10 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
                                                const floatx16 (&acc)[F][F], float* st) {
   constexpr int WT = F * 32;
   constexpr int SROW = WT + 8;   // row-major strip stride (floats)
-  constexpr int TROW = 36;       // transposed strip stride (floats)
   constexpr bool SYMO = (EPI == EPI_SYM || EPI == EPI_POLY);
-  constexpr bool TRANS = SYMO || EPI == EPI_RECT_T;  // also writes the transposed strip
   constexpr int a = A;
-  constexpr bool diag = SYMO && DIAG;   // a diagonal tile: masked stores
+  // the transposed copy: mirror of an off-diagonal symmetric tile, or X (hi)
+  constexpr bool TRANS = (SYMO && !DIAG) || EPI == EPI_RECT_T;
   const int row_base = ti * BM + wm * WT;  // global row of the sub-tile
   const int col_base = tj * BM + wn * WT;  // global col of the sub-tile
   _Float16* C = (_Float16*)d.buf[pa.c_slot];
@@ -259,8 +260,10 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
     float v[F][16];
     if (EPI == EPI_POLY) {
       // G[gi][gj] for 4 consecutive rows = G[gj][gi..gi+3] (G is symmetric);
-      // every load of the strip is issued before any store of it.
+      // every load of the strip is issued before any store of it.  The lo
+      // term is read only when the product runs on two-term operands.
       const _Float16* G = (const _Float16*)d.buf[pa.aux_slot];
+      const bool with_lo = pa.aux_lo != 0;
       half4 gh[F][4], gl[F][4];
 #pragma unroll
       for (int b = 0; b < F; ++b)
@@ -270,7 +273,7 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
           const int gj = col_base + b * 32 + (lane & 31);
           const size_t off = blk_off(gj, gi, arows);   // 4 contiguous elements (gi % 4 == 0)
           gh[b][g] = *to_global((const half4*)(G + off));
-          gl[b][g] = *to_global((const half4*)(G + off + cts));
+          gl[b][g] = with_lo ? *to_global((const half4*)(G + off + cts)) : half4{0, 0, 0, 0};
         }
 #pragma unroll
       for (int b = 0; b < F; ++b)
@@ -341,52 +344,36 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
           }
         }
       } else {  // EPI_SYM, EPI_POLY, EPI_RECT, EPI_RECT_T
-        unsigned mask = 0xFFu;
-        if constexpr (diag) {  // columns >= row only
-          mask = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) mask |= (gj0 + i >= gi ? 1u : 0u) << i;
-        }
-        store8_split(C, cts, cld, gi, gj0, w, mask, pa.out_lo != 0);
+        store8_split(C, cts, cld, gi, gj0, w, 0xFFu, pa.out_lo != 0);
       }
     }
     wave_lds_sync();
 
     if (TRANS) {
-      // ---- transposed strip -> mirror stores C[gj][gi..gi+7] (symmetric
-      // outputs), or the hi term of the transposed result into aux
-      // (X <- (X^T)^T after a restart, ld = arows)
+      // ---- transposed copy from registers: lane holds rows gi0..gi0+3 of
+      // column gj, i.e. columns gi0..gi0+3 of transposed row gj (the mirror
+      // C[gj][gi], or the hi term of X = (X^T)^T into aux, ld = arows)
+      _Float16* T = EPI == EPI_RECT_T ? (_Float16*)d.buf[pa.aux_slot] : C;
+      const int tld = EPI == EPI_RECT_T ? arows : cld;
+      const bool tlo = EPI != EPI_RECT_T && pa.out_lo != 0;
+      _Float16 DION_GLOBAL* g = to_global_w(T);
 #pragma unroll
       for (int b = 0; b < F; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int cc = b * 32 + (lane & 31);
-          const int r0 = g * 8 + (lane >> 5) * 4;
-          *(float4*)&st[cc * TROW + r0] =
-              make_float4(v[b][g * 4 + 0], v[b][g * 4 + 1], v[b][g * 4 + 2], v[b][g * 4 + 3]);
-        }
-      wave_lds_sync();
+        for (int q = 0; q < 4; ++q) {
+          const int gj = col_base + b * 32 + (lane & 31);
+          const int gi0 = row_base + a * 32 + q * 8 + (lane >> 5) * 4;
+          half4 h, l;
 #pragma unroll
-      for (int q0 = 0; q0 < 4 * WT; q0 += 64) {
-        const int q = q0 + lane;
-        const int cc = q >> 2, r0 = (q & 3) * 8;
-        float w[8];
-        *(float4*)&w[0] = *(const float4*)&st[cc * TROW + r0];
-        *(float4*)&w[4] = *(const float4*)&st[cc * TROW + r0 + 4];
-        const int gj = col_base + cc, gi0 = row_base + a * 32 + r0;
-        if (EPI == EPI_RECT_T) {
-          store8_hi((_Float16*)d.buf[pa.aux_slot], arows, gj, gi0, w);
-        } else {
-          unsigned mask = 0xFFu;
-          if constexpr (diag) {  // mirror of the strict upper half: gj > gi
-            mask = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) mask |= (gj > gi0 + i ? 1u : 0u) << i;
+          for (int i = 0; i < 4; ++i) {
+            const float x = v[b][q * 4 + i];
+            h[i] = (_Float16)x;
+            l[i] = (_Float16)(x - (float)h[i]);
           }
-          store8_split(C, cts, cld, gj, gi0, w, mask, pa.out_lo != 0);
+          const size_t off = blk_off(gj, gi0, tld);   // 4 contiguous elements (gi0 % 4 == 0)
+          *(half4 DION_GLOBAL*)(g + off) = h;
+          if (tlo) *(half4 DION_GLOBAL*)(g + off + cts) = l;
         }
-      }
-      wave_lds_sync();
     }
   }
 }
@@ -396,8 +383,8 @@ __device__ __forceinline__ void epilogue_all(const MatDesc& d, const PhaseArgs& 
                                              int brows, int ti, int tj, int wm, int wn, int lane,
                                              const floatx16 (&acc)[F][F], float* st,
                                              std::integer_sequence<int, As...>) {
-  // the tile's position is uniform over the block, so only diagonal tiles of
-  // symmetric outputs run the masked variant
+  // the tile's position is uniform over the block: diagonal tiles of
+  // symmetric outputs take the variant without the mirror
   if ((EPI == EPI_SYM || EPI == EPI_POLY) && ti == tj)
     (epilogue_strip<BM, EPI, F, As, true>(d, pa, alpha, arows, brows, ti, tj, wm, wn, lane, acc, st), ...);
   else
