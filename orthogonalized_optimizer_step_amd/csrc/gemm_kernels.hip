@@ -183,12 +183,14 @@ __device__ __forceinline__ AT phase_alpha(const MatDesc& d, const PhaseArgs& pa,
 // chunks of 8 consecutive columns.  The transposed copy (the mirror of a
 // symmetric output, or X from X^T after a restart) needs no staging: in the
 // accumulator layout a lane holds 4 consecutive rows of one column, which are
-// 4 consecutive columns of a transposed row, so it leaves as 8-byte stores
-// straight from registers.  A diagonal tile of a symmetric output is written
+// 4 consecutive columns of a transposed row, so it leaves straight from
+// registers (8-byte stores, or 16-byte ones after an exchange between lanes l
+// and l + 32).  A diagonal tile of a symmetric output is written
 // whole by the direct stores (both of its triangles are computed) and has no
 // mirror, so no store is masked except at the valid edge of the final output.
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __host__ __device__ constexpr int epi_wave_bytes(int wt) {
   return 32 * (wt + 8) * 4;   // row-major strip 32 x (wt + 8) floats
@@ -350,30 +352,68 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
     wave_lds_sync();
 
     if (TRANS) {
-      // ---- transposed copy from registers: lane holds rows gi0..gi0+3 of
-      // column gj, i.e. columns gi0..gi0+3 of transposed row gj (the mirror
-      // C[gj][gi], or the hi term of X = (X^T)^T into aux, ld = arows)
+      // ---- transposed copy from registers.  Lane (c, h) = (lane % 32, lane / 32)
+      // holds rows gi0 + 8q + 4h + (0..3) of column gj, i.e. columns
+      // 8q + 4h + (0..3) of transposed row gj.  Targets: the mirror C[gj][gi]
+      // of a symmetric tile, or the hi term of X = (X^T)^T into aux (ld =
+      // arows).  The mirror leaves as 8-byte stores.  For X, lanes c and c + 32
+      // first swap halves so that each lane holds whole 8-column chunks (q even
+      // in lane h = 0, q odd in lane h = 1), and a pair of chunks leaves as one
+      // instruction writing 32 contiguous bytes per row (chunk pairs stay
+      // adjacent under the panel swizzle); measured on one box, the exchange
+      // gains 2% on the restart apply and loses 2% on the mirrored products.
       _Float16* T = EPI == EPI_RECT_T ? (_Float16*)d.buf[pa.aux_slot] : C;
       const int tld = EPI == EPI_RECT_T ? arows : cld;
       const bool tlo = EPI != EPI_RECT_T && pa.out_lo != 0;
       _Float16 DION_GLOBAL* g = to_global_w(T);
+      if constexpr (EPI == EPI_RECT_T) {
+        const int h = lane >> 5;
 #pragma unroll
-      for (int b = 0; b < F; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int b = 0; b < F; ++b) {
           const int gj = col_base + b * 32 + (lane & 31);
-          const int gi0 = row_base + a * 32 + q * 8 + (lane >> 5) * 4;
-          half4 h, l;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = v[b][q * 4 + i];
-            h[i] = (_Float16)x;
-            l[i] = (_Float16)(x - (float)h[i]);
+          for (int qp = 0; qp < 4; qp += 2) {
+            uint32_t hw[2][2];   // own values of chunks qp and qp + 1, as fp16 pairs
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                const _Float16 h0 = (_Float16)v[b][(qp + u) * 4 + 2 * i];
+                const _Float16 h1 = (_Float16)v[b][(qp + u) * 4 + 2 * i + 1];
+                hw[u][i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+              }
+            // lane h = 0 keeps chunk qp and sends its half of chunk qp + 1;
+            // lane h = 1 keeps chunk qp + 1 and sends its half of chunk qp
+            uint32_t rh[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) rh[i] = (uint32_t)__shfl_xor((int)hw[1 - h][i], 32, 64);
+            // h = 0 owns the low half of its chunk, h = 1 the high half
+            const u32x4 ch = h == 0 ? u32x4{hw[0][0], hw[0][1], rh[0], rh[1]}
+                                    : u32x4{rh[0], rh[1], hw[1][0], hw[1][1]};
+            const int gi0 = row_base + a * 32 + (qp + h) * 8;   // chunk start (a multiple of 8)
+            *(u32x4 DION_GLOBAL*)(g + blk_off(gj, gi0, tld)) = ch;
           }
-          const size_t off = blk_off(gj, gi0, tld);   // 4 contiguous elements (gi0 % 4 == 0)
-          *(half4 DION_GLOBAL*)(g + off) = h;
-          if (tlo) *(half4 DION_GLOBAL*)(g + off + cts) = l;
         }
+      } else {
+#pragma unroll
+        for (int b = 0; b < F; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int gj = col_base + b * 32 + (lane & 31);
+            const int gi0 = row_base + a * 32 + q * 8 + (lane >> 5) * 4;
+            half4 hh, ll;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = v[b][q * 4 + i];
+              hh[i] = (_Float16)x;
+              ll[i] = (_Float16)(x - (float)hh[i]);
+            }
+            const size_t off = blk_off(gj, gi0, tld);   // 4 contiguous elements (gi0 % 4 == 0)
+            *(half4 DION_GLOBAL*)(g + off) = hh;
+            if (tlo) *(half4 DION_GLOBAL*)(g + off + cts) = ll;
+          }
+      }
     }
   }
 }
