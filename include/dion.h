@@ -146,6 +146,25 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
                         const dion_ns_params* p, int32_t* sel_idx, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* The same step followed by the weight update, fused: the flow of the Dion3
+ * summary (输入输出流程: update the momentum, select rows, Gram Newton-Schulz,
+ * update the weights), with the optimizer's last step in the final apply:
+ *   E, grad, shapes, grad_dtype, beta, p, sel_idx  as dion_rowsubset_step
+ *   W[i]          device R x C of w_dtype (bf16 or fp32), updated in place:
+ *                 W <- fl32(fl32(W * (1 - weight_decay)) - fl32(alpha[i] * U)),
+ *                 rounded to nearest even for bf16, where U is the step's
+ *                 update: the orthogonalized selected rows (fp32, before any
+ *                 rounding) and the new momentum E in the other rows
+ *   alpha         host array of `batch` floats: the learning rate times the
+ *                 matrix's shape scale (chosen by the caller)
+ *   weight_decay  decoupled weight decay factor (0 = none)
+ * No separate output is written.  Workspace: dion_workspace_size(shapes,
+ * batch, DION_FP32, p). */
+int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* const* W,
+                               const dion_shape* shapes, int32_t batch, int32_t grad_dtype, int32_t w_dtype,
+                               float beta, const float* alpha, float weight_decay, const dion_ns_params* p,
+                               int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Phase entry points: one step of the path on its own, with the same kernels,
  * operand layout and precision as inside dion_orth_batched, for kernel-level

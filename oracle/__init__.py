@@ -17,7 +17,10 @@ from .dion_oracle import (  # noqa: F401
     rel_frobenius,
     restart_points,
     row_keys,
+    round_to_bf16,
     rowsubset_step,
+    rowsubset_step_update,
     select_rows,
     selected_count,
+    weight_update_f32,
 )

@@ -43,6 +43,10 @@ formula, selection criterion or worked example.  The readings taken here are:
       M_t = fl32(fl32(beta * E_{t-1}) + G_t) (two correctly rounded fp32
       operations, heavy-ball form) and E_t = M_t; unselected rows of the
       output carry M_t unchanged.
+  R11 Weight update (the step's last stage, 输入输出流程): W <- W (1 - wd) -
+      alpha U with U the step's output and alpha the learning rate times a
+      per-matrix shape scale chosen by the caller; in fp32 arithmetic with one
+      rounding per operation, then round-to-nearest-even for bf16 weights.
 
 Parity pins (in tests/): SVD closed form U f^K(Sigma) V^T, textbook polar
 factor via the cubic Newton-Schulz map, the NS band invariant, equivalence with
@@ -262,6 +266,55 @@ def momentum_update(E, G, beta: float) -> np.ndarray:
     b = np.float32(beta)
     t = np.multiply(b, E32, dtype=np.float32)
     return np.add(t, G32, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------
+# Weight update (reading R11)
+# --------------------------------------------------------------------------
+def round_to_bf16(x) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16, ties to even (as float32)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return (u & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+
+
+def weight_update_f32(W, U, alpha: float, weight_decay: float = 0.0, bf16: bool = False) -> np.ndarray:
+    """W <- fl32(fl32(W * keep) - fl32(alpha * U)), keep = fl32(1 - weight_decay),
+    then rounded to bfloat16 when the weight is stored in bf16 (R11).
+
+    Each numpy float32 operation is one IEEE rounding.  The rounding of the
+    stored weight decides its bits, so this is computed in the precision the
+    weight is stored and updated in (fp32).
+    Pages: Dion3 summary, 输入输出流程 (the weight update ends the step).
+    """
+    W32 = np.asarray(W, dtype=np.float32)
+    U32 = np.asarray(U, dtype=np.float32)
+    keep = np.subtract(np.float32(1.0), np.float32(weight_decay), dtype=np.float32)
+    a = np.multiply(W32, keep, dtype=np.float32)
+    b = np.multiply(np.float32(alpha), U32, dtype=np.float32)
+    out = np.subtract(a, b, dtype=np.float32)
+    return round_to_bf16(out) if bf16 else out
+
+
+def rowsubset_step_update(Es, grads, Ws, beta: float, alphas, weight_decay: float = 0.0, bf16: bool = False,
+                          **kw):
+    """One row-subset step followed by the weight update (R8, R11).
+
+    Returns (new E list, new W list (fp64), idx list).  Selected rows take the
+    exact update: W * (1 - weight_decay) - alpha * O in fp64; the other rows
+    take the raw momentum through ``weight_update_f32`` (their update is an
+    exact fp32 value, so their stored result is fixed bit for bit).
+    """
+    newE, outs, idxs = rowsubset_step(Es, grads, beta, **kw)
+    newW = []
+    for W, Mt, out, idx, alpha in zip(Ws, newE, outs, idxs, alphas):
+        W64 = np.asarray(W, dtype=np.float64)
+        keep = float(np.subtract(np.float32(1.0), np.float32(weight_decay), dtype=np.float32))
+        res = W64 * keep - float(np.float32(alpha)) * out
+        rest = np.setdiff1d(np.arange(W64.shape[0]), idx)
+        res[rest] = weight_update_f32(np.asarray(W)[rest], Mt[rest], alpha, weight_decay, bf16)
+        newW.append(res)
+    return newE, newW, idxs
 
 
 def rowsubset_step(Es, grads, beta: float, **kw):

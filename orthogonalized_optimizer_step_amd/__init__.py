@@ -13,7 +13,7 @@ from ._lib import DION_BF16, DION_FP32, PHASE, PREC, DionError, DionParams, Dion
 
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
            "DionError", "QUINTIC", "profile_enable", "profile_records", "rowkeys_topk", "syrk", "sympoly",
-           "apply"]
+           "apply", "rowsubset_step_update", "Dion3"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
@@ -118,6 +118,18 @@ class Orthogonalizer:
                                    ctypes.c_void_p(self._ws), self._ws_len, _stream(stream))
         check(rc)
         return outs
+
+    def step_update(self, Es, grads, Ws, beta, alphas, weight_decay=0.0, sel_idx=None, stream=None):
+        """Row-subset step with the fused weight update W <- W (1 - wd) - alpha_i U."""
+        gcode = _dtype_code(grads[0].dtype)
+        wcode = _dtype_code(Ws[0].dtype)
+        al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
+        rc = lib.dion_rowsubset_step_update(_ptrs(Es), _ptrs(grads), _ptrs(Ws), self._shp, len(self.shapes), gcode,
+                                            wcode, float(beta), al, float(weight_decay), ctypes.byref(self._p),
+                                            ctypes.c_void_p(sel_idx.data_ptr() if sel_idx is not None else None),
+                                            ctypes.c_void_p(self._ws), self._ws_len, _stream(stream))
+        check(rc)
+        return Ws
 
     def step(self, Es, grads, outs, beta, sel_idx=None, stream=None):
         code = _dtype_code(grads[0].dtype)
@@ -248,6 +260,23 @@ def apply(Qs, Xs, precision="auto", stream=None):
     return Ys
 
 
+def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=QUINTIC, n_iter=5,
+                          restart_every=0, restart_mask=0, safety=1.0, row_frac=0.125, return_indices=False,
+                          stream=None):
+    """One row-subset step fused with the weight update; E and W are updated in place."""
+    import torch
+    _check_tensors(Es, torch.float32)
+    _check_tensors(grads, grads[0].dtype)
+    _check_tensors(Ws, Ws[0].dtype)
+    orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
+                          safety, row_frac, "mfma16", device=Es[0].device, step_mode=True)
+    sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
+    orth.step_update(Es, grads, Ws, beta, alphas, weight_decay, sel, stream)
+    if not return_indices:
+        return Ws
+    return Ws, list(torch.split(sel, orth.selected))
+
+
 def profile_enable(on=True) -> bool:
     """Start (clearing old records) or stop per-phase event profiling on this thread."""
     return bool(lib.dion_profile_enable(1 if on else 0))
@@ -264,3 +293,6 @@ def profile_records():
                                    ctypes.byref(r), ctypes.byref(b)))
         recs.append((name.value.decode(), kern.value.decode(), ms.value, u.value, r.value, b.value))
     return recs
+
+
+from .optim import Dion3  # noqa: E402

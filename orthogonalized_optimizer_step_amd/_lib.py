@@ -39,7 +39,7 @@ EXPORTS = (
     "dion_rowsubset_step", "dion_useful_flops", "dion_selected_rows", "dion_strerror",
     "dion_last_error", "dion_version", "dion_profile_enable", "dion_profile_count",
     "dion_profile_get", "dion_phase_workspace_size", "dion_rowkeys_topk_batched", "dion_syrk_batched",
-    "dion_sympoly_batched", "dion_apply_batched",
+    "dion_sympoly_batched", "dion_apply_batched", "dion_rowsubset_step_update",
 )
 
 
@@ -102,6 +102,9 @@ def _load():
     lib.dion_sympoly_batched.restype = ctypes.c_int
     lib.dion_apply_batched.argtypes = [pp, pp, pp, shp, i32, i32, i32, vp, sz, vp]
     lib.dion_apply_batched.restype = ctypes.c_int
+    lib.dion_rowsubset_step_update.argtypes = [pp, pp, pp, shp, i32, i32, i32, ctypes.c_float, fp, ctypes.c_float,
+                                               prm, vp, vp, sz, vp]
+    lib.dion_rowsubset_step_update.restype = ctypes.c_int
     return lib
 
 

@@ -27,7 +27,9 @@ bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& 
 bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream);
 void launch_rowkeys(bool bf16, const MatDesc* descs, int nmat, int64_t rows, double* keys, hipStream_t s);
 void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
-                          double* keys, hipStream_t s);
+                          double* keys, bool write_out, hipStream_t s);
+void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
+                              float keep, hipStream_t s);
 void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,
                    MatScalars* scalars, bool fp64_path, hipStream_t s);
 void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
@@ -139,7 +141,8 @@ float pow2_scale(double bound) {  // largest 2^j with bound * 2^j <= 2^15
 }
 
 // ------------------------------------------------------------ the plan
-enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY, ST_UNPACK, ST_COMBINE };
+enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY, ST_UNPACK, ST_COMBINE,
+                ST_UPDATE };
 
 struct Step {
   StepKind kind;
@@ -180,6 +183,9 @@ struct Plan {
   int64_t x_rows = 0, x_sel = 0;
   bool host_scalars = false;
   std::vector<MatScalars> hscal;
+  // fused weight update (row-subset step): out is the weight W
+  bool update = false, w_bf16 = true;
+  float keep = 1.f;
   size_t off_descs = 0, off_scalars = 0, off_keys = 0, off_flags = 0, off_idx = 0, off_ints = 0,
          off_data = 0, total = 0, upload_bytes = 0;
   std::vector<int> ints;
@@ -970,6 +976,7 @@ const char* kernel_name(const Plan& P, const Step& st) {
     case ST_COPY: return "dion::k_copy_unselected";
     case ST_UNPACK: return "dion::k_unpack";
     case ST_COMBINE: return "dion::k_scale_combine";
+    case ST_UPDATE: return P.w_bf16 ? "dion::k_update_unselected<unsigned short>" : "dion::k_update_unselected<float>";
     case ST_GEMM:
       if (P.fp64)
         key = "dion::k_gemm64<" + std::to_string(st.epi) + ", " + (st.sym ? "true" : "false") + ">";
@@ -1015,7 +1022,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int run(const Plan& P, const void* const* M, void* const* out, const void* const* grad, int batch, int dtype,
         int grad_dtype, float beta, bool step_mode, int32_t* sel_idx, void* workspace, size_t ws_bytes,
-        hipStream_t stream, const void* const* Qs = nullptr, double* keys_out = nullptr) {
+        hipStream_t stream, const void* const* Qs = nullptr, double* keys_out = nullptr,
+        const float* upd_alpha = nullptr) {
   if (!workspace) return fail(DION_E_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255) != 0) return fail(DION_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < P.total)
@@ -1042,6 +1050,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     d.m_pad = mp.m_pad;
     d.n_pad = mp.n_pad;
     d.tall = mp.tall;
+    d.upd_alpha = upd_alpha ? upd_alpha[i] : 0.f;
     row0 += mp.R;
     sel0 += mp.k;
   }
@@ -1100,7 +1109,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         launch_rowkeys(s_bf16, sd, sn, srows, skeys, stream);
         break;
       case ST_MOMENTUM:
-        launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, beta, d_keys, stream);
+        launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, beta, d_keys, !P.update, stream);
         break;
       case ST_SELECT:
         launch_select(sd, sn, skeys, sflags, sidx, ss, P.fp64, stream);
@@ -1138,6 +1147,9 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
       }
       case ST_COMBINE:
         launch_scale_combine(d_scal, batch, stream);
+        break;
+      case ST_UPDATE:
+        launch_update_unselected(P.w_bf16, d_descs, batch, P.total_rows, d_flags, P.keep, stream);
         break;
     }
     if (g_prof.on) {
@@ -1337,6 +1349,53 @@ int dion_apply_batched(const float* const* Q, const void* const* X, void* const*
         return fail(DION_E_INVAL, "Y must not overlap the inputs");
   return run(P, X, Y, nullptr, batch, dtype, dtype, 0.f, false, nullptr, workspace, workspace_bytes,
              (hipStream_t)stream, (const void* const*)Q);
+}
+
+int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* const* W,
+                               const dion_shape* shapes, int32_t batch, int32_t grad_dtype, int32_t w_dtype,
+                               float beta, const float* alpha, float weight_decay, const dion_ns_params* p,
+                               int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (grad_dtype != DION_BF16 && grad_dtype != DION_FP32) return fail(DION_E_INVAL, "unknown grad dtype");
+  if (w_dtype != DION_BF16 && w_dtype != DION_FP32) return fail(DION_E_INVAL, "unknown weight dtype");
+  if (!std::isfinite(beta)) return fail(DION_E_INVAL, "beta must be finite");
+  if (!std::isfinite(weight_decay)) return fail(DION_E_INVAL, "weight_decay must be finite");
+  if (!alpha) return fail(DION_E_INVAL, "alpha is NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!std::isfinite(alpha[i])) return fail(DION_E_INVAL, "alpha must be finite");
+  Params prm;
+  int rc = parse_params(p, DION_FP32, true, prm);
+  if (rc) return rc;
+  Plan P;
+  rc = build_plan(shapes, batch, DION_FP32, prm, true, P, grad_dtype == DION_BF16 ? 2 : 4);
+  if (rc) return rc;
+  if (!E || !grad || !W) return fail(DION_E_INVAL, "E, grad or W pointer array is NULL");
+  for (int i = 0; i < batch; ++i)
+    if (!E[i] || !grad[i] || !W[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
+  const size_t wes = w_dtype == DION_BF16 ? 2 : 4;
+  rc = check_ptrs((const void* const*)E, W, shapes, batch, 4, wes);
+  if (rc) return rc;
+  rc = check_ptrs(grad, W, shapes, batch, grad_dtype == DION_BF16 ? 2 : 4, wes);
+  if (rc) return rc;
+  // the final apply updates W in its epilogue; rows left out by the selection
+  // are updated with the raw momentum by a pass of their own
+  P.update = true;
+  P.w_bf16 = w_dtype == DION_BF16;
+  P.keep = 1.0f - weight_decay;
+  for (Step& st : P.steps)
+    if (st.kind == ST_GEMM && st.epi == EPI_OUT) {
+      st.pa.out_update = 1;
+      st.pa.upd_keep = P.keep;
+      st.pa.out_fp32 = w_dtype == DION_FP32 ? 1 : 0;
+    }
+  if (P.use_idx) {
+    Step u;
+    u.kind = ST_UPDATE;
+    u.name = "update_rows";
+    P.steps.push_back(u);
+  }
+  return run(P, (const void* const*)E, W, grad, batch, DION_FP32, grad_dtype, beta, true, sel_idx, workspace,
+             workspace_bytes, (hipStream_t)stream, nullptr, nullptr, alpha);
 }
 
 double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_params* p) {

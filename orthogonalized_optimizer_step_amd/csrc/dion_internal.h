@@ -56,7 +56,7 @@ struct MatDesc {
   int m, n;           // Gram side and long side (m <= n)
   int m_pad, n_pad;   // padded
   int tall;           // 1 if the selected block is tall (k > C): X = S^T
-  int pad_;
+  float upd_alpha;    // weight-update mode: W <- W * keep - upd_alpha * update
 };
 
 // Per-matrix scalars written by the device (selection / normalization).
@@ -91,6 +91,8 @@ struct PhaseArgs {
   int out_fp32;      // EPI_OUT: 1 -> fp32 output, 0 -> bf16
   int out_rows_are_m;  // EPI_OUT: 1 -> product rows index the m side
   int out_lo;        // fp16 outputs: 1 -> store the lo term too, 0 -> hi only (no reader needs lo)
+  int out_update;    // EPI_OUT: 1 -> out is the weight W, updated as W <- W * upd_keep - upd_alpha * value
+  float upd_keep;    // EPI_OUT weight update: 1 - decoupled weight decay
   const MatScalars* scalars;
   const int* idx;      // selected rows (global), NULL when row_frac == 1
 };

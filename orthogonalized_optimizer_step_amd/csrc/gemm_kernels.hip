@@ -319,6 +319,21 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
           const int orow = pa.idx ? pa.idx[d.sel0 + gi] : gi;
           const size_t o = (size_t)orow * d.C + gj0;
           const bool full = gj0 + 8 <= cols_valid;
+          if (pa.out_update) {
+            // the weight update: W <- fl32(fl32(W * keep) - fl32(alpha * u)),
+            // rounded to W's dtype below (u = this fp32 output)
+            float cur[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const bool ok = gj0 + i < cols_valid;
+              cur[i] = !ok ? 0.f
+                           : (pa.out_fp32 ? ((const float*)d.out)[o + i]
+                                          : __uint_as_float((uint32_t)((const uint16_t*)d.out)[o + i] << 16));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              w[i] = __fsub_rn(__fmul_rn(cur[i], pa.upd_keep), __fmul_rn(d.upd_alpha, w[i]));
+          }
           if (pa.out_fp32) {
             float* out = (float*)d.out + o;
             if (full && ((uintptr_t)out & 15) == 0) {

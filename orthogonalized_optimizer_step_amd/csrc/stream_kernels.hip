@@ -89,12 +89,13 @@ __global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ des
 }
 
 // ---------------------------------------------- momentum / error feedback
-// E <- fl32(fl32(beta * E) + grad), out <- bf16(E), key <- sum E^2 (fp64).
-// __fmul_rn / __fadd_rn keep the two roundings separate (no contraction).
+// E <- fl32(fl32(beta * E) + grad), out <- bf16(E) (unless out is the weight
+// of the fused update), key <- sum E^2 (fp64).  __fmul_rn / __fadd_rn keep the
+// two roundings separate (no contraction).
 template <typename GT>
 __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict__ descs, int nmat,
                                                        int64_t total_rows, float beta,
-                                                       double* __restrict__ keys) {
+                                                       double* __restrict__ keys, int write_out) {
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (g >= total_rows) return;
@@ -120,10 +121,12 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
       float m[4] = {__fadd_rn(__fmul_rn(beta, e.x), gv[0]), __fadd_rn(__fmul_rn(beta, e.y), gv[1]),
                     __fadd_rn(__fmul_rn(beta, e.z), gv[2]), __fadd_rn(__fmul_rn(beta, e.w), gv[3])};
       *(float4*)(E + c) = make_float4(m[0], m[1], m[2], m[3]);
-      uint2 o;
-      o.x = (uint32_t)bf16_rne(m[0]) | ((uint32_t)bf16_rne(m[1]) << 16);
-      o.y = (uint32_t)bf16_rne(m[2]) | ((uint32_t)bf16_rne(m[3]) << 16);
-      *(uint2*)(out + c) = o;
+      if (write_out) {
+        uint2 o;
+        o.x = (uint32_t)bf16_rne(m[0]) | ((uint32_t)bf16_rne(m[1]) << 16);
+        o.y = (uint32_t)bf16_rne(m[2]) | ((uint32_t)bf16_rne(m[3]) << 16);
+        *(uint2*)(out + c) = o;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) s += (double)m[q] * (double)m[q];
     }
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
                                        : ((const float*)d.grad)[r * d.C + c];
       const float m = __fadd_rn(__fmul_rn(beta, E[c]), gv);
       E[c] = m;
-      out[c] = bf16_rne(m);
+      if (write_out) out[c] = bf16_rne(m);
       s += (double)m * (double)m;
     }
   }
@@ -457,6 +460,31 @@ __global__ __launch_bounds__(256) void k_copy_unselected(const MatDesc* __restri
   for (int c = lane; c < d.C; c += 64) dst[c] = src[c];
 }
 
+// ------------------------------------------- weight update, unselected rows
+// Fused weight update of a row-subset step: the rows the selection left out
+// carry the raw momentum E (fp32, already updated), so
+// W <- fl32(fl32(W * keep) - fl32(alpha * E)), rounded to W's dtype.  One wave
+// per row; selected rows are left to the final apply's epilogue.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_update_unselected(const MatDesc* __restrict__ descs, int nmat,
+                                                           int64_t total_rows, const uint8_t* __restrict__ flags,
+                                                           float keep) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= total_rows || flags[g]) return;
+  const MatDesc& d = descs[mat_of_row(descs, nmat, g)];
+  const int64_t r = g - d.row0;
+  const float* E = (const float*)d.M + r * d.C;
+  WT* W = (WT*)d.out + r * d.C;
+  const float al = d.upd_alpha;
+  for (int c = lane; c < d.C; c += 64) {
+    const float w = sizeof(WT) == 2 ? bf16_to_f32(((const uint16_t*)W)[c]) : ((const float*)W)[c];
+    const float v = __fsub_rn(__fmul_rn(w, keep), __fmul_rn(al, E[c]));
+    if (sizeof(WT) == 2) ((uint16_t*)W)[c] = bf16_rne(v);
+    else ((float*)W)[c] = v;
+  }
+}
+
 // ------------------------------------------------------------ unpack
 // Phase entry points: an m x m workspace matrix (slot `slot`; MFMA16: fp16
 // hi + lo, panel-blocked; FP64: row-major doubles) -> out (m x m fp32,
@@ -517,9 +545,16 @@ void launch_rowkeys(bool bf16, const MatDesc* descs, int nmat, int64_t rows, dou
 }
 
 void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
-                          double* keys, hipStream_t s) {
-  if (grad_bf16) hipLaunchKernelGGL(k_momentum_keys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys);
-  else hipLaunchKernelGGL(k_momentum_keys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys);
+                          double* keys, bool write_out, hipStream_t s) {
+  const int wo = write_out ? 1 : 0;
+  if (grad_bf16) hipLaunchKernelGGL(k_momentum_keys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, wo);
+  else hipLaunchKernelGGL(k_momentum_keys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, wo);
+}
+
+void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
+                              float keep, hipStream_t s) {
+  if (w_bf16) hipLaunchKernelGGL(k_update_unselected<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags, keep);
+  else hipLaunchKernelGGL(k_update_unselected<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags, keep);
 }
 
 void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,

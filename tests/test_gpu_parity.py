@@ -184,3 +184,74 @@ def test_rowsubset_step_small(dion):
             assert np.array_equal(got[rest], round_bf16(newE[i][rest]).astype(np.float64))
             assert O.rel_frobenius(got[ix], ref_outs[i][ix]) <= TOL_MFMA16
         E_host = newE
+
+
+# -------------------------------------------------- fused weight update
+@pytest.mark.parametrize("wbf16", [False, True])
+def test_rowsubset_step_update(dion, wbf16):
+    """Momentum + selection + Gram-NS + weight update in one call, three steps.
+
+    E and the rows left out by the selection are fixed bit for bit (their
+    update is the exact fp32 momentum).  Selected rows: fp32 weights gate the
+    update W_new - W keep against -alpha O at 2e-2; bf16 weights add their
+    rounding, 2^-9 relative per element."""
+    shapes = [(32, 20), (64, 48), (40, 200), (300, 64)]
+    beta, wd = 0.95, 0.01
+    alphas = [0.02 * float(np.sqrt(max(1.0, r / c))) for r, c in shapes]
+    keep = float(np.float32(1.0) - np.float32(wd))
+    rng = np.random.default_rng(7)
+    W_host = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    if wbf16:
+        W_host = [O.round_to_bf16(w) for w in W_host]
+    wdt = torch.bfloat16 if wbf16 else torch.float32
+    W_dev = [torch.from_numpy(w).cuda().to(wdt) for w in W_host]
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(3):
+        G = [round_bf16(lowrank_np((4, t, i, 1), r, c, 3, 0.05, log_scale=(-3.0, 0.0)))
+             for i, (r, c) in enumerate(shapes)]
+        _, idxs = dion.rowsubset_step_update(E_dev, [to_dev_bf16(g) for g in G], W_dev, beta, alphas, wd,
+                                             restart_every=2, row_frac=0.25, return_indices=True)
+        newE, newW, ref_idxs = O.rowsubset_step_update(E_host, G, W_host, beta, alphas, wd, bf16=wbf16, n_iter=5,
+                                                       restart_every=2, row_frac=0.25)
+        for i in range(len(shapes)):
+            assert np.array_equal(E_dev[i].cpu().numpy().view(np.uint32), newE[i].view(np.uint32))
+            assert_selection(idxs[i].cpu().numpy(), newE[i], 0.25)
+            got = to_np(W_dev[i])
+            ix = ref_idxs[i]
+            rest = np.setdiff1d(np.arange(shapes[i][0]), ix)
+            assert np.array_equal(got[rest], newW[i][rest])
+            base = W_host[i][ix].astype(np.float64) * keep
+            d_ref = newW[i][ix] - base
+            if wbf16:
+                err = np.linalg.norm(got[ix] - newW[i][ix])
+                assert err <= 2.0 ** -9 * 1.01 * np.linalg.norm(newW[i][ix]) + TOL_MFMA16 * np.linalg.norm(d_ref)
+            else:
+                assert O.rel_frobenius(got[ix] - base, d_ref) <= TOL_MFMA16
+        E_host = newE
+        W_host = [to_np(w).astype(np.float32) for w in W_dev]   # selected rows follow the GPU's own values
+
+
+def test_dion3_optimizer_step(dion):
+    """The optimizer class: one step on two fp32 weights equals the fused call
+    with alpha = lr * sqrt(max(1, rows / cols)) and decay lr * weight_decay."""
+    torch.manual_seed(0)
+    shapes = [(96, 64), (64, 160)]
+    params = [torch.nn.Parameter(torch.randn(s, device="cuda") * 0.02) for s in shapes]
+    W0 = [p.detach().cpu().numpy().copy() for p in params]
+    G = [round_bf16(lowrank_np((8, i), r, c, 4, 0.05)) for i, (r, c) in enumerate(shapes)]
+    for p, g in zip(params, G):
+        p.grad = torch.from_numpy(g).cuda()
+    opt = dion.Dion3(params, lr=0.02, momentum=0.95, row_frac=0.5, weight_decay=0.1, restart_every=2)
+    opt.step()
+    alphas = [0.02 * float(np.sqrt(max(1.0, r / c))) for r, c in shapes]
+    newE, newW, idxs = O.rowsubset_step_update([np.zeros(s, np.float32) for s in shapes], G, W0, 0.95, alphas,
+                                               0.02 * 0.1, n_iter=5, restart_every=2, row_frac=0.5)
+    keep = float(np.float32(1.0) - np.float32(0.02 * 0.1))
+    for p, E, W, ix, w0 in zip(params, newE, newW, idxs, W0):
+        assert np.array_equal(opt.state[p]["momentum_buffer"].cpu().numpy(), E)
+        got = p.detach().cpu().numpy().astype(np.float64)
+        rest = np.setdiff1d(np.arange(W.shape[0]), ix)
+        assert np.array_equal(got[rest], W[rest])
+        base = w0[ix].astype(np.float64) * keep
+        assert O.rel_frobenius(got[ix] - base, W[ix] - base) <= TOL_MFMA16

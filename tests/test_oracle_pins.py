@@ -360,3 +360,55 @@ def test_one_step_composition_is_one_ns_iteration(shape):
     Y = O.apply_factor(O.gram_polynomial(O.gram(X), a, b, c), X)
     assert np.allclose(Y, svd_closed_form(S, QUINTIC, 1), atol=1e-13)
     assert np.array_equal(O.apply_factor(np.eye(min(shape)), X), X)
+
+
+# ------------------------------------------------------ weight update (R11)
+def f32_bits_to_bf16_rne(x: float) -> float:
+    """Scalar round-to-nearest-even of an fp32 value to bfloat16, by its bits."""
+    u = struct.unpack("<I", struct.pack("<f", x))[0]
+    lower = u & 0xFFFF
+    up = u >> 16
+    if lower > 0x8000 or (lower == 0x8000 and (up & 1)):
+        up += 1
+    return struct.unpack("<f", struct.pack("<I", (up & 0xFFFF) << 16))[0]
+
+
+def test_bf16_rounding_ties_to_even():
+    vals = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -(1.0 + 2.0 ** -8),
+                     3.0, 0.0], dtype=np.float32)
+    got = O.round_to_bf16(vals)
+    assert got.tolist() == [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -1.0, 3.0, 0.0]
+    x = RNG.standard_normal(2000).astype(np.float32) * 10.0 ** RNG.uniform(-5, 3, 2000).astype(np.float32)
+    assert np.array_equal(O.round_to_bf16(x), np.array([f32_bits_to_bf16_rne(float(v)) for v in x], np.float32))
+
+
+@pytest.mark.parametrize("wd,bf16", [(0.0, False), (0.01, False), (0.01, True)])
+def test_weight_update_scalar_emulation(wd, bf16):
+    """fl32(fl32(W keep) - fl32(alpha U)) reproduced with struct-rounded fp64 scalars."""
+    W = (RNG.standard_normal(500) * 0.02).astype(np.float32)
+    U = (RNG.standard_normal(500) * 0.05).astype(np.float32)
+    alpha = 0.02 * 1.7
+    got = O.weight_update_f32(W, U, alpha, wd, bf16)
+    keep = f32(1.0 - f32(wd))
+    a32 = f32(alpha)
+    for i in range(500):
+        v = f32(f32(float(W[i]) * keep) - f32(a32 * float(U[i])))
+        if bf16:
+            v = f32_bits_to_bf16_rne(v)
+        assert got[i] == v
+
+
+def test_rowsubset_step_update_structure():
+    """Selected rows: W keep - alpha * orthogonalize(M_t); the others: the raw momentum update."""
+    Es = [np.zeros((12, 20), np.float32)]
+    G = [round_bf16(RNG.standard_normal((12, 20))).astype(np.float32)]
+    Ws = [(RNG.standard_normal((12, 20)) * 0.02).astype(np.float32)]
+    newE, newW, idxs = O.rowsubset_step_update(Es, G, Ws, 0.95, [0.03], 0.01, row_frac=0.25, n_iter=5,
+                                               restart_every=2)
+    out, idx = O.orthogonalize(newE[0], n_iter=5, restart_every=2, row_frac=0.25)
+    assert np.array_equal(idx, idxs[0])
+    keep = float(np.float32(1.0) - np.float32(0.01))
+    assert np.allclose(newW[0][idx], Ws[0][idx].astype(np.float64) * keep - float(np.float32(0.03)) * out[idx],
+                       atol=1e-15)
+    rest = np.setdiff1d(np.arange(12), idx)
+    assert np.array_equal(newW[0][rest], O.weight_update_f32(Ws[0][rest], newE[0][rest], 0.03, 0.01))
