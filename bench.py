@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "gpt2_small", "llama3_70b",
                                                                 "llama3_8b_rows"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--update", action="store_true",
+                    help="row-subset workload only: fuse the weight update into the step (bf16 weights, "
+                         "lr 0.02 times sqrt(max(1, rows/cols)), weight decay 0.1)")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
     ap.add_argument("--summarize", metavar="DIR",
                     help="print a text summary of the rocprofv3 CSV output under DIR and exit")
@@ -194,7 +197,17 @@ def main():
     step_mode = wl.name.endswith("rows")
     orth = dion.Orthogonalizer(wl.shapes, "bf16", wl.coeffs, wl.n_iter, wl.restart_every, wl.restart_mask,
                                wl.safety, wl.row_frac, "auto", device=dev, step_mode=step_mode)
-    if step_mode:
+    if args.update and not step_mode:
+        print(json.dumps({"error": "--update needs the row-subset workload (llama3_8b_rows)"}))
+        sys.exit(2)
+    if step_mode and args.update:
+        Es = [torch.zeros(M.shape, dtype=torch.float32, device=dev) for M in Ms]
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        Ws = [(torch.randn(M.shape, generator=g, device=dev) * 0.02).to(torch.bfloat16) for M in Ms]
+        alphas = [0.02 * max(1.0, r / c) ** 0.5 for r, c in wl.shapes]
+        call = lambda: orth.step_update(Es, Ms, Ws, wl.beta, alphas, 0.02 * 0.1)  # noqa: E731
+    elif step_mode:
         Es = [torch.zeros(M.shape, dtype=torch.float32, device=dev) for M in Ms]
         outs = [torch.empty_like(M) for M in Ms]
         call = lambda: orth.step(Es, Ms, outs, wl.beta)  # noqa: E731
@@ -284,7 +297,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: {len(wl.shapes)} matrices, {params/1e9:.3f} G params, "
+        "config": {"workload": f"{wl.name}{' + fused weight update' if args.update else ''}: "
+                               f"{len(wl.shapes)} matrices, {params/1e9:.3f} G params, "
                                f"K={wl.n_iter}, restart_every={wl.restart_every}, restart_mask={wl.restart_mask}, "
                                f"safety={wl.safety}, row_frac={wl.row_frac}",
                    "matrices": len(wl.shapes), "params": params, "n_iter": wl.n_iter},

@@ -323,12 +323,30 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
             // the weight update: W <- fl32(fl32(W * keep) - fl32(alpha * u)),
             // rounded to W's dtype below (u = this fp32 output)
             float cur[8];
+            if (pa.out_fp32) {
+              const float* wp = (const float*)d.out + o;
+              if (full && ((uintptr_t)wp & 15) == 0) {
+                *(float4*)&cur[0] = *(const float4*)wp;
+                *(float4*)&cur[4] = *(const float4*)(wp + 4);
+              } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const bool ok = gj0 + i < cols_valid;
-              cur[i] = !ok ? 0.f
-                           : (pa.out_fp32 ? ((const float*)d.out)[o + i]
-                                          : __uint_as_float((uint32_t)((const uint16_t*)d.out)[o + i] << 16));
+                for (int i = 0; i < 8; ++i) cur[i] = gj0 + i < cols_valid ? wp[i] : 0.f;
+              }
+            } else {
+              const uint16_t* wp = (const uint16_t*)d.out + o;
+              if (full && ((uintptr_t)wp & 15) == 0) {
+                const uint4 b = *(const uint4*)wp;
+                const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  cur[2 * i] = __uint_as_float(bw[i] << 16);
+                  cur[2 * i + 1] = __uint_as_float(bw[i] & 0xFFFF0000u);
+                }
+              } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                  cur[i] = gj0 + i < cols_valid ? __uint_as_float((uint32_t)wp[i] << 16) : 0.f;
+              }
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)

@@ -477,11 +477,39 @@ __global__ __launch_bounds__(256) void k_update_unselected(const MatDesc* __rest
   const float* E = (const float*)d.M + r * d.C;
   WT* W = (WT*)d.out + r * d.C;
   const float al = d.upd_alpha;
-  for (int c = lane; c < d.C; c += 64) {
-    const float w = sizeof(WT) == 2 ? bf16_to_f32(((const uint16_t*)W)[c]) : ((const float*)W)[c];
-    const float v = __fsub_rn(__fmul_rn(w, keep), __fmul_rn(al, E[c]));
-    if (sizeof(WT) == 2) ((uint16_t*)W)[c] = bf16_rne(v);
-    else ((float*)W)[c] = v;
+  if ((d.C & 3) == 0) {   // 4 consecutive elements per lane (rows start 16-byte aligned)
+    for (int c = lane * 4; c < d.C; c += 256) {
+      const float4 e = *(const float4*)(E + c);
+      const float ev[4] = {e.x, e.y, e.z, e.w};
+      float wv[4];
+      if (sizeof(WT) == 2) {
+        const uint2 b = *(const uint2*)((const uint16_t*)W + c);
+        wv[0] = __uint_as_float(b.x << 16);
+        wv[1] = __uint_as_float(b.x & 0xFFFF0000u);
+        wv[2] = __uint_as_float(b.y << 16);
+        wv[3] = __uint_as_float(b.y & 0xFFFF0000u);
+      } else {
+        const float4 b = *(const float4*)((const float*)W + c);
+        wv[0] = b.x; wv[1] = b.y; wv[2] = b.z; wv[3] = b.w;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[q] = __fsub_rn(__fmul_rn(wv[q], keep), __fmul_rn(al, ev[q]));
+      if (sizeof(WT) == 2) {
+        uint2 o;
+        o.x = (uint32_t)bf16_rne(wv[0]) | ((uint32_t)bf16_rne(wv[1]) << 16);
+        o.y = (uint32_t)bf16_rne(wv[2]) | ((uint32_t)bf16_rne(wv[3]) << 16);
+        *(uint2*)((uint16_t*)W + c) = o;
+      } else {
+        *(float4*)((float*)W + c) = make_float4(wv[0], wv[1], wv[2], wv[3]);
+      }
+    }
+  } else {
+    for (int c = lane; c < d.C; c += 64) {
+      const float w = sizeof(WT) == 2 ? bf16_to_f32(((const uint16_t*)W)[c]) : ((const float*)W)[c];
+      const float v = __fsub_rn(__fmul_rn(w, keep), __fmul_rn(al, E[c]));
+      if (sizeof(WT) == 2) ((uint16_t*)W)[c] = bf16_rne(v);
+      else ((float*)W)[c] = v;
+    }
   }
 }
 
