@@ -65,8 +65,11 @@ typedef enum {
   DION_E_HIP = -4           /* a HIP runtime call or kernel launch failed */
 } dion_status;
 
-/* Storage dtype of the momentum / gradient / output matrices. */
-typedef enum { DION_BF16 = 0, DION_FP32 = 1 } dion_dtype;
+/* Storage dtype of the momentum / gradient / output matrices.  DION_FP16 is
+ * accepted by dion_orth_batched and the phase entry points (inputs and
+ * outputs in fp16, processed like bf16: the values are exact in one fp16
+ * term); the row-subset step takes bf16 or fp32 gradients. */
+typedef enum { DION_BF16 = 0, DION_FP32 = 1, DION_FP16 = 2 } dion_dtype;
 
 /* Arithmetic of the iteration.
  *   DION_PREC_MFMA16: fp16 MFMA with fp32 accumulation; operands carry
@@ -76,7 +79,7 @@ typedef enum { DION_BF16 = 0, DION_FP32 = 1 } dion_dtype;
  *     momentum (gate 2e-2).
  *   DION_PREC_FP64: fp64 arithmetic throughout (error ~1e-12; gate 1e-4).
  *   DION_PREC_AUTO: FP64 for DION_FP32 inputs of dion_orth_batched, MFMA16
- *     otherwise. */
+ *     otherwise (bf16 and fp16). */
 typedef enum { DION_PREC_AUTO = 0, DION_PREC_MFMA16 = 1, DION_PREC_FP64 = 2 } dion_precision;
 
 typedef struct {

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 
-from ._lib import DION_BF16, DION_FP32, PHASE, PREC, DionError, DionParams, DionShape, check, lib
+from ._lib import DION_BF16, DION_FP16, DION_FP32, PHASE, PREC, DionError, DionParams, DionShape, check, lib
 
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
            "DionError", "QUINTIC", "profile_enable", "profile_records", "rowkeys_topk", "syrk", "sympoly",
@@ -41,6 +41,8 @@ def _dtype_code(dt):
         return DION_BF16
     if dt == torch.float32:
         return DION_FP32
+    if dt == torch.float16:
+        return DION_FP16
     raise DionError(-1, f"unsupported dtype {dt}")
 
 
@@ -59,7 +61,7 @@ def _check_tensors(ts, dtype=None):
 def workspace_size(shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
                    safety=1.0, row_frac=1.0, precision="auto") -> int:
     p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision)
-    code = DION_BF16 if dtype in ("bf16", DION_BF16) else DION_FP32
+    code = {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
     n = lib.dion_workspace_size(_shapes(shapes), len(shapes), code, ctypes.byref(p))
     if n == 0:
         raise DionError(-1, lib.dion_last_error().decode())
@@ -100,7 +102,7 @@ class Orthogonalizer:
         self.step_mode = step_mode
         self._p, self._keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision)
         self._shp = _shapes(self.shapes)
-        code = DION_FP32 if (step_mode or dtype == "fp32") else DION_BF16
+        code = DION_FP32 if step_mode else {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
         self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
         if self.ws_bytes == 0:
             raise DionError(-1, lib.dion_last_error().decode())
@@ -150,7 +152,7 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
     """
     import torch
     _check_tensors(Ms, Ms[0].dtype)
-    dt = "bf16" if Ms[0].dtype == torch.bfloat16 else "fp32"
+    dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(Ms[0].dtype, "fp32")
     orth = Orthogonalizer([tuple(M.shape) for M in Ms], dt, coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, precision, device=Ms[0].device)
     if outs is None:

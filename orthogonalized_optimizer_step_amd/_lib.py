@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdion.so")
 
-DION_BF16, DION_FP32 = 0, 1
+DION_BF16, DION_FP32, DION_FP16 = 0, 1, 2
 PHASE = {"rowkeys_topk": 1, "syrk": 2, "sympoly": 3, "apply": 4}
 PREC = {"auto": 0, "mfma16": 1, "fp64": 2}
 

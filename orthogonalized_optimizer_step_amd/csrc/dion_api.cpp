@@ -25,14 +25,14 @@ namespace dion {
 bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa,
                    hipStream_t stream);
 bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream);
-void launch_rowkeys(bool bf16, const MatDesc* descs, int nmat, int64_t rows, double* keys, hipStream_t s);
+void launch_rowkeys(int fmt, const MatDesc* descs, int nmat, int64_t rows, double* keys, hipStream_t s);
 void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
                           double* keys, bool write_out, hipStream_t s);
 void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
                               float keep, hipStream_t s);
 void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,
                    MatScalars* scalars, bool fp64_path, hipStream_t s);
-void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
+void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
                  const int* idx, const MatScalars* scalars, int xterms, bool use_idx, hipStream_t s);
 void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int total, int src_slot, int dst_slot,
                       hipStream_t s);
@@ -65,9 +65,12 @@ struct Params {
   bool fp64;
 };
 
+bool valid_dtype(int dtype) { return dtype == DION_BF16 || dtype == DION_FP32 || dtype == DION_FP16; }
+size_t dtype_bytes(int dtype) { return dtype == DION_FP32 ? 4 : 2; }
+
 int parse_params(const dion_ns_params* p, int dtype, bool step_mode, Params& out) {
   if (!p) return fail(DION_E_INVAL, "params is NULL");
-  if (dtype != DION_BF16 && dtype != DION_FP32) return fail(DION_E_INVAL, "unknown dtype");
+  if (!valid_dtype(dtype)) return fail(DION_E_INVAL, "unknown dtype");
   if (p->n_iter < 1 || p->n_iter > kMaxIter) return fail(DION_E_INVAL, "n_iter must be in [1, 64]");
   const int K = p->n_iter;
   const float* co = p->ns_coeffs ? p->ns_coeffs : kQuintic;
@@ -172,7 +175,8 @@ struct MatPlan {
 
 struct Plan {
   bool fp64 = false;
-  bool bf16_in = true;
+  bool bf16_in = true;   // 16-bit inputs (bf16 or fp16): exact in one fp16 term
+  int fmt = 0;           // input storage: 0 bf16, 1 fp32, 2 fp16
   int xterms0 = 1;
   bool use_idx = false;
   std::vector<MatPlan> mats;
@@ -217,8 +221,9 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   if (!shapes) return fail(DION_E_INVAL, "shapes is NULL");
   if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
   P.fp64 = prm.fp64;
-  P.bf16_in = !step_mode && dtype == DION_BF16;
-  P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;  // bf16 values are exact in one fp16 term
+  P.fmt = step_mode ? 1 : (dtype == DION_FP32 ? 1 : (dtype == DION_FP16 ? 2 : 0));
+  P.bf16_in = P.fmt != 1;
+  P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;  // bf16 and fp16 values are exact in one fp16 term
   P.use_idx = prm.row_frac < 1.0;
   const int K = (int)prm.a.size();
   int n_restarts = 0;
@@ -345,7 +350,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.total = off;
 
   // ---------------------------------------------------------- phase list
-  const double in_es = step_mode ? 4.0 : (dtype == DION_BF16 ? 2.0 : 4.0);
+  const double in_es = step_mode ? 4.0 : (double)dtype_bytes(dtype);
   double elems = 0, sel_elems = 0, pad_elems = 0, unsel_elems = 0, rows = (double)P.total_rows;
   for (const MatPlan& mp : P.mats) {
     elems += (double)mp.R * mp.C;
@@ -683,6 +688,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     pa.alpha = x_is_x0 ? 1.0f / sQ : 1.0f / (sQ * sXT);
     pa.alpha_pow = x_is_x0 ? 1 : 0;
     pa.out_fp32 = (!step_mode && dtype == DION_FP32) ? 1 : 0;
+    pa.out_f16 = (!step_mode && dtype == DION_FP16) ? 1 : 0;
     PhaseArgs pw = pa;
     pw.a_slot = q_slot;
     pw.b_slot = xt_slot;
@@ -720,11 +726,12 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
                      const float* coeffs, Plan& P) {
   if (!shapes) return fail(DION_E_INVAL, "shapes is NULL");
   if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
-  if (dtype != DION_BF16 && dtype != DION_FP32) return fail(DION_E_INVAL, "unknown dtype");
+  if (!valid_dtype(dtype)) return fail(DION_E_INVAL, "unknown dtype");
   if (precision < DION_PREC_AUTO || precision > DION_PREC_FP64) return fail(DION_E_INVAL, "unknown precision");
   if (!(row_frac > 0.0 && row_frac <= 1.0)) return fail(DION_E_INVAL, "row_frac must be in (0, 1]");
   P.fp64 = phase_fp64(precision, dtype);
-  P.bf16_in = dtype == DION_BF16;
+  P.fmt = dtype == DION_FP32 ? 1 : (dtype == DION_FP16 ? 2 : 0);
+  P.bf16_in = P.fmt != 1;
   P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;
   P.use_idx = row_frac < 1.0;
   P.mats.resize(batch);
@@ -896,6 +903,7 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
     pa.alpha = 1.f;
     pa.alpha_pow = 1;
     pa.out_fp32 = dtype == DION_FP32 ? 1 : 0;
+    pa.out_f16 = dtype == DION_FP16 ? 1 : 0;
     PhaseArgs pw = pa;
     pw.a_slot = SLOT_MM0;
     pw.b_slot = SLOT_XT0;
@@ -1083,7 +1091,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
   uint8_t* d_flags = (uint8_t*)(ws + P.off_flags);
   int* d_idx = (int*)(ws + P.off_idx);
   const int* d_ints = (const int*)(ws + P.off_ints);
-  const bool in_bf16 = step_mode ? false : dtype == DION_BF16;
+  const int fmt = P.fmt;
 
   for (const Step& st : P.steps) {
     ProfRec rec{st.name, nullptr, nullptr, nullptr, st.useful, st.raw, st.bytes};
@@ -1103,10 +1111,10 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     double* skeys = qset ? d_keys + P.x_rows : d_keys;
     uint8_t* sflags = qset ? d_flags + P.x_rows : d_flags;
     int* sidx = qset ? d_idx + P.x_sel : d_idx;
-    const bool s_bf16 = qset ? false : in_bf16;
+    const int s_fmt = qset ? 1 : fmt;   // the apply's Q operands are fp32
     switch (st.kind) {
       case ST_KEYS:
-        launch_rowkeys(s_bf16, sd, sn, srows, skeys, stream);
+        launch_rowkeys(s_fmt, sd, sn, srows, skeys, stream);
         break;
       case ST_MOMENTUM:
         launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, beta, d_keys, !P.update, stream);
@@ -1116,7 +1124,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         break;
       case ST_PACK: {
         const Table& t = P.tabs[st.table];
-        launch_pack(s_bf16, P.fp64, sd, d_ints + t.prefix_off, t.nmat, t.total, sidx, ss,
+        launch_pack(s_fmt, P.fp64, sd, d_ints + t.prefix_off, t.nmat, t.total, sidx, ss,
                     qset ? 2 : P.xterms0, P.use_idx && !qset, stream);
         break;
       }
@@ -1137,7 +1145,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         break;
       }
       case ST_COPY:
-        launch_copy_unselected(in_bf16, d_descs, batch, P.total_rows, d_flags, stream);
+        launch_copy_unselected(fmt != 1, d_descs, batch, P.total_rows, d_flags, stream);
         break;
       case ST_UNPACK: {
         const Table& t = P.tabs[st.table];
@@ -1215,7 +1223,7 @@ int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* 
   Plan P;
   rc = build_plan(shapes, batch, dtype, prm, false, P);
   if (rc) return rc;
-  const size_t es = dtype == DION_BF16 ? 2 : 4;
+  const size_t es = dtype_bytes(dtype);
   rc = check_ptrs(M, out, shapes, batch, es, es);
   if (rc) return rc;
   return run(P, M, out, nullptr, batch, dtype, dtype, 0.f, false, sel_idx, workspace, workspace_bytes,
@@ -1297,7 +1305,7 @@ int dion_syrk_batched(const void* const* X, float* const* G, const dion_shape* s
     if (!X[i] || !G[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL pointer");
     gs[i] = {P.mats[i].m, P.mats[i].m};
   }
-  const size_t es = dtype == DION_BF16 ? 2 : 4;
+  const size_t es = dtype_bytes(dtype);
   for (int i = 0; i < batch; ++i)
     for (int j = 0; j < batch; ++j)
       if (overlaps(G[i], (size_t)gs[i].rows * gs[i].cols * 4, X[j], (size_t)shapes[j].rows * shapes[j].cols * es))
@@ -1339,7 +1347,7 @@ int dion_apply_batched(const float* const* Q, const void* const* X, void* const*
   if (!Q || !X || !Y) return fail(DION_E_INVAL, "pointer arrays are NULL");
   for (int i = 0; i < batch; ++i)
     if (!Q[i]) return fail(DION_E_INVAL, "matrix " + std::to_string(i) + " has a NULL Q pointer");
-  const size_t es = dtype == DION_BF16 ? 2 : 4;
+  const size_t es = dtype_bytes(dtype);
   rc = check_ptrs(X, Y, shapes, batch, es, es);
   if (rc) return rc;
   for (int i = 0; i < batch; ++i)

@@ -88,7 +88,8 @@ struct PhaseArgs {
   float poly_a, poly_b, poly_c;  // EPI_POLY coefficients
   float aux_inv_scale;           // EPI_POLY: G = stored aux * aux_inv_scale
   int aux_lo;                    // EPI_POLY (MFMA16): 1 -> G = hi + lo, 0 -> hi only
-  int out_fp32;      // EPI_OUT: 1 -> fp32 output, 0 -> bf16
+  int out_fp32;      // EPI_OUT: 1 -> fp32 output, 0 -> 16-bit (bf16, or fp16 when out_f16)
+  int out_f16;       // EPI_OUT: 16-bit output in fp16 rather than bf16
   int out_rows_are_m;  // EPI_OUT: 1 -> product rows index the m side
   int out_lo;        // fp16 outputs: 1 -> store the lo term too, 0 -> hi only (no reader needs lo)
   int out_update;    // EPI_OUT: 1 -> out is the weight W, updated as W <- W * upd_keep - upd_alpha * value

@@ -162,6 +162,7 @@ __device__ __forceinline__ void epilogue_elem(const MatDesc& d, const PhaseArgs&
     const size_t o = (size_t)orow * d.C + gj;
     const float v = (float)(acc * alpha);
     if (pa.out_fp32) ((float*)d.out)[o] = v;
+    else if (pa.out_f16) ((_Float16*)d.out)[o] = (_Float16)v;
     else ((uint16_t*)d.out)[o] = f32_to_bf16_rne(v);
   }
 }
@@ -361,6 +362,18 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
 #pragma unroll
               for (int i = 0; i < 8; ++i)
                 if (gj0 + i < cols_valid) out[i] = w[i];
+            }
+          } else if (pa.out_f16) {
+            _Float16* out = (_Float16*)d.out + o;
+            if (full && ((uintptr_t)out & 15) == 0) {
+              half8v pk;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) pk[i] = (_Float16)w[i];
+              *(half8v*)out = pk;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                if (gj0 + i < cols_valid) out[i] = (_Float16)w[i];
             }
           } else {
             uint16_t* out = (uint16_t*)d.out + o;

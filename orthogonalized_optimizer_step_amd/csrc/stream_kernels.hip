@@ -20,6 +20,14 @@ __device__ __forceinline__ uint16_t bf16_rne(float v) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// 16-bit input element -> fp32: InT = uint16_t holds bf16 bits, _Float16 holds fp16.
+template <typename InT> __device__ __forceinline__ float in16_to_f32(uint32_t b);
+template <> __device__ __forceinline__ float in16_to_f32<uint16_t>(uint32_t b) { return bf16_to_f32((uint16_t)b); }
+template <> __device__ __forceinline__ float in16_to_f32<_Float16>(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+template <> __device__ __forceinline__ float in16_to_f32<float>(uint32_t b) { return __uint_as_float(b); }  // unused
+
 __device__ __forceinline__ double wave_sum(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -55,15 +63,15 @@ __global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ des
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const double lo = (double)__uint_as_float(w[q] << 16);
-          const double hi = (double)__uint_as_float(w[q] & 0xFFFF0000u);
+          const double lo = (double)in16_to_f32<InT>(w[q] & 0xFFFFu);
+          const double hi = (double)in16_to_f32<InT>(w[q] >> 16);
           s += lo * lo;
           s += hi * hi;
         }
       }
     } else {
       for (int c = lane; c < d.C; c += 64) {
-        const double x = (double)bf16_to_f32(p[c]);
+        const double x = (double)in16_to_f32<InT>(p[c]);
         s += x * x;
       }
     }
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
     if (r < d.k && c < d.C) {
       const int src = use_idx ? idx[r] : r;
       const InT* row = (const InT*)d.M + (int64_t)src * d.C;
-      if (sizeof(InT) == 2) v = bf16_to_f32(((const uint16_t*)row)[c]);
+      if (sizeof(InT) == 2) v = in16_to_f32<InT>(((const uint16_t*)row)[c]);
       else v = ((const float*)row)[c];
     }
     tile[i][tx] = v;
@@ -384,8 +392,8 @@ __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ desc
           const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w4[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+            v[2 * i] = in16_to_f32<InT>(w4[i] & 0xFFFFu);
+            v[2 * i + 1] = in16_to_f32<InT>(w4[i] >> 16);
           }
         } else {
           const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ desc
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (c + i < d.C)
-            v[i] = sizeof(InT) == 2 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+            v[i] = sizeof(InT) == 2 ? in16_to_f32<InT>(((const uint16_t*)p)[i]) : ((const float*)p)[i];
       }
     }
 #pragma unroll
@@ -566,9 +574,11 @@ __global__ void k_scale_combine(MatScalars* __restrict__ scalars, int nmat) {
 // ---------------------------------------------------------------- launchers
 static inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + 3) / 4); }
 
-void launch_rowkeys(bool bf16, const MatDesc* descs, int nmat, int64_t rows, double* keys,
+// fmt: the storage format of the inputs, 0 = bf16, 1 = fp32, 2 = fp16
+void launch_rowkeys(int fmt, const MatDesc* descs, int nmat, int64_t rows, double* keys,
                     hipStream_t s) {
-  if (bf16) hipLaunchKernelGGL(k_rowkeys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
+  if (fmt == 0) hipLaunchKernelGGL(k_rowkeys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
+  else if (fmt == 2) hipLaunchKernelGGL(k_rowkeys<_Float16>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
   else hipLaunchKernelGGL(k_rowkeys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
 }
 
@@ -591,18 +601,22 @@ void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* 
                      fp64_path ? 1 : 0);
 }
 
-void launch_pack(bool in_bf16, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat,
+void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat,
                  int total, const int* idx, const MatScalars* scalars, int xterms, bool use_idx,
                  hipStream_t s) {
   if (total <= 0) return;
   const int ui = use_idx ? 1 : 0;
+#define DION_PACK(K_, T_) hipLaunchKernelGGL((K_<T_>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui)
   if (fp64_path) {
-    if (in_bf16) hipLaunchKernelGGL((k_pack<uint16_t>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
-    else hipLaunchKernelGGL((k_pack<float>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    if (fmt == 0) DION_PACK(k_pack, uint16_t);
+    else if (fmt == 2) DION_PACK(k_pack, _Float16);
+    else DION_PACK(k_pack, float);
   } else {
-    if (in_bf16) hipLaunchKernelGGL((k_pack16<uint16_t>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
-    else hipLaunchKernelGGL((k_pack16<float>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui);
+    if (fmt == 0) DION_PACK(k_pack16, uint16_t);
+    else if (fmt == 2) DION_PACK(k_pack16, _Float16);
+    else DION_PACK(k_pack16, float);
   }
+#undef DION_PACK
 }
 
 void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int total, int src_slot, int dst_slot,

@@ -255,3 +255,41 @@ def test_dion3_optimizer_step(dion):
         assert np.array_equal(got[rest], W[rest])
         base = w0[ix].astype(np.float64) * keep
         assert O.rel_frobenius(got[ix] - base, W[ix] - base) <= TOL_MFMA16
+
+
+# ------------------------------------------------------------ fp16 I/O
+def f16_batch(seed):
+    return [lowrank_np((seed, i), r, c, max(1, min(r, c) // 8), 0.1, log_scale=(-3.0, 0.0)).astype(np.float16)
+            .astype(np.float32) for i, (r, c) in enumerate(SMALL_SHAPES)]
+
+
+@pytest.mark.parametrize("prec,tol", [("mfma16", TOL_MFMA16), ("fp64", 2.0 ** -10)])
+def test_small_ragged_fp16_io(dion, prec, tol):
+    """fp16 momentum in, fp16 update out.  MFMA16: the bf16-path gate (fp16
+    values are exact in one fp16 term); FP64: only the fp16 output rounding,
+    at most 2^-11 relative per element."""
+    Ms = f16_batch(31)
+    kw = {"n_iter": 5, "restart_every": 2}
+    outs, idx = dion.orth_batched([torch.from_numpy(M).cuda().to(torch.float16) for M in Ms], precision=prec,
+                                  row_frac=0.5, return_indices=True, **kw)
+    errs = []
+    for M, o, ix in zip(Ms, outs, idx):
+        assert o.dtype == torch.float16
+        ref, ref_idx = O.orthogonalize(M, row_frac=0.5, **kw)
+        assert np.array_equal(ix.cpu().numpy(), ref_idx)
+        got = to_np(o)
+        rest = np.setdiff1d(np.arange(M.shape[0]), ref_idx)
+        assert np.array_equal(got[rest], M[rest].astype(np.float64))
+        errs.append(O.rel_frobenius(got[ref_idx], ref[ref_idx]))
+    print(f"fp16 I/O {prec}:", " ".join(f"{e:.1e}" for e in errs), flush=True)
+    assert max(errs) <= tol
+
+
+def test_fp16_full_size(dion):
+    """A Llama-3-8B down-projection-shaped fp16 matrix (4096 x 14336), restarts every 2."""
+    M = lowrank_np((3, 0, 6), 4096, 14336, 64, 0.05, log_scale=(-3, 0)).astype(np.float16).astype(np.float32)
+    out = dion.orth_batched([torch.from_numpy(M).cuda().to(torch.float16)], n_iter=5, restart_every=2)[0]
+    ref, _ = O.orthogonalize(M, n_iter=5, restart_every=2)
+    err = O.rel_frobenius(to_np(out), ref)
+    print(f"fp16 4096x14336: rel err {err:.3e}", flush=True)
+    assert err <= TOL_MFMA16

@@ -209,3 +209,21 @@ def test_apply_full_size(dion):
     errs = [O.rel_frobenius(to_np(Y), O.apply_factor(Q, X)) for Q, X, Y in zip(Qs, Xs, Ys)]
     print("apply full size:", " ".join(f"{e:.1e}" for e in errs), flush=True)
     assert max(errs) <= TOL_BF16_OUT
+
+
+def test_phases_fp16(dion):
+    """The phase entry points on fp16 inputs (exact in one fp16 term)."""
+    Ms = [M.astype(np.float16).astype(np.float32) for M in batch(27, SHAPES, bf16=False)]
+    dev16 = [torch.from_numpy(M).cuda().to(torch.float16) for M in Ms]
+    keys, idx = dion.rowkeys_topk(dev16, row_frac=0.25)
+    for M, k, ix in zip(Ms, keys, idx):
+        ref = O.row_keys(M)
+        assert np.all(np.abs(k.cpu().numpy() - ref) <= 1e-12 * ref + 1e-300)
+        assert_selection(ix.cpu().numpy(), M, 0.25)
+    Gs = dion.syrk(dev16, precision="mfma16")
+    assert max(O.rel_frobenius(to_np(G), O.gram(M)) for M, G in zip(Ms, Gs)) <= TOL_ACC
+    Qs = [general_factor(28, min(M.shape)) for M in Ms]
+    Ys = dion.apply([torch.from_numpy(Q).cuda() for Q in Qs], dev16, precision="mfma16")
+    errs = [O.rel_frobenius(to_np(Y), O.apply_factor(Q, M)) for Q, M, Y in zip(Qs, Ms, Ys)]
+    assert all(Y.dtype == torch.float16 for Y in Ys)
+    assert max(errs) <= 2.0 ** -11 + TOL_ACC   # fp16 output rounding plus the accumulation
