@@ -47,6 +47,12 @@ formula, selection criterion or worked example.  The readings taken here are:
       alpha U with U the step's output and alpha the learning rate times a
       per-matrix shape scale chosen by the caller; in fp32 arithmetic with one
       rounding per operation, then round-to-nearest-even for bf16 weights.
+  R12 Restart threshold tau (局限 names it as a hyperparameter; the same
+      passage ties restarts to spurious negative eigenvalues of the
+      intermediate matrices): in the smallest singular directions P is close
+      to a_k I, so one iteration scales an error of the Gram matrix there by
+      a_k^2.  A restart is taken after the iteration at which the product of
+      these factors since the last restart first reaches tau.
 
 Parity pins (in tests/): SVD closed form U f^K(Sigma) V^T, textbook polar
 factor via the cubic Newton-Schulz map, the NS band invariant, equivalence with
@@ -88,16 +94,32 @@ def coefficient_schedule(coeffs, n_iter: int, safety: float = 1.0):
     return [(float(a) / s, float(b) / s ** 3, float(c) / s ** 5) for a, b, c in arr]
 
 
-def restart_points(n_iter: int, restart_every: int = 0, restart_mask: int = 0):
-    """Iterations k (1-based) after which the Gram matrix is re-formed (R5).
+def restart_points(n_iter: int, restart_every: int = 0, restart_mask: int = 0,
+                   restart_threshold: float = 0.0, coeff_list=None):
+    """Iterations k (1-based) after which the Gram matrix is re-formed (R5, R12).
 
     A nonzero ``restart_mask`` wins: bit (k-1) set means restart after k.
-    Otherwise every ``restart_every``-th iteration restarts.  No restart is
-    ever taken after the last iteration.
-    Pages: Dion3 summary, 核心模块 (restart strategy) and 局限 (restart threshold).
+    Otherwise a positive ``restart_threshold`` tau applies R12: the growth
+    factor a_k^2 of every iteration since the last restart (``coeff_list``
+    holds the safety-folded triples) is multiplied up, and the iteration at
+    which the product first reaches tau restarts.  Otherwise every
+    ``restart_every``-th iteration restarts.  No restart is ever taken after
+    the last iteration.
+    Pages: Dion3 summary, 核心模块 (restart strategy) and 局限 (restart
+    threshold; spurious negative eigenvalues of the intermediate matrices).
     """
     if restart_mask:
         pts = {k for k in range(1, n_iter + 1) if (restart_mask >> (k - 1)) & 1}
+    elif restart_threshold and restart_threshold > 0:
+        if coeff_list is None or len(coeff_list) != n_iter:
+            raise ValueError("the restart threshold needs the per-iteration coefficients")
+        pts, growth = set(), 1.0
+        for k in range(1, n_iter + 1):
+            a = coeff_list[k - 1][0]
+            growth *= a * a
+            if growth >= restart_threshold:
+                pts.add(k)
+                growth = 1.0
     elif restart_every and restart_every > 0:
         pts = set(range(restart_every, n_iter + 1, restart_every))
     else:
@@ -215,7 +237,8 @@ def gram_newton_schulz(X, coeff_list, restarts) -> np.ndarray:
 
 
 def orthogonalize(M, coeffs=DEFAULT_COEFFS, n_iter: int = 5, restart_every: int = 0,
-                  restart_mask: int = 0, safety: float = 1.0, row_frac: float = 1.0):
+                  restart_mask: int = 0, safety: float = 1.0, row_frac: float = 1.0,
+                  restart_threshold: float = 0.0):
     """One matrix of the hot path.  Returns (out fp64 R x C, idx int64[k]).
 
     out[idx] is the orthogonalized selected block; the other rows are the
@@ -228,7 +251,7 @@ def orthogonalize(M, coeffs=DEFAULT_COEFFS, n_iter: int = 5, restart_every: int 
     idx = select_rows(M64, row_frac)
     S = M64[idx, :]
     coeff_list = coefficient_schedule(coeffs, n_iter, safety)
-    restarts = restart_points(n_iter, restart_every, restart_mask)
+    restarts = restart_points(n_iter, restart_every, restart_mask, restart_threshold, coeff_list)
 
     tall = S.shape[0] > C                       # R3
     X = S.T if tall else S

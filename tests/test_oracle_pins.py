@@ -321,6 +321,69 @@ def test_hyperparameter_expansion():
     assert math.isclose(O.rel_frobenius(np.ones(3), np.ones(3) * 2), 0.5)
 
 
+@pytest.mark.parametrize("tau,safety,n_iter", [(100.0, 1.0, 5), (100.0, 1.0, 9), (1000.0, 1.0, 7), (5.0, 1.0, 4),
+                                                 (1e4, 1.0, 5), (116.0, 1.0, 6), (116.0, 1.05, 6), (1e30, 1.0, 5)])
+def test_restart_threshold_closed_form(tau, safety, n_iter):
+    """Reading R12 with one fixed triple: the growth per iteration is the constant
+    (a/s)^2, so segments have the length L = ceil(ln tau / ln (a/s)^2) and the
+    restarts fall on the multiples of L below K (taus chosen away from ties)."""
+    g = (QUINTIC[0] / safety) ** 2
+    L = max(1, math.ceil(math.log(tau) / math.log(g)))
+    expect = [k for k in range(L, n_iter, L)]
+    sched = O.coefficient_schedule(QUINTIC, n_iter, safety)
+    assert O.restart_points(n_iter, restart_threshold=tau, coeff_list=sched) == expect
+
+
+def test_restart_threshold_safety_lengthens_segments():
+    """tau = 116 lies between the two-iteration growths (3.4445/1.05)^4 = 115.8 and
+    3.4445^4 = 140.8: segments of 2 at s = 1, of 3 at s = 1.05."""
+    assert (3.4445 / 1.05) ** 4 < 116 < 3.4445 ** 4
+    assert O.restart_points(6, restart_threshold=116, coeff_list=O.coefficient_schedule(QUINTIC, 6, 1.0)) == [2, 4]
+    assert O.restart_points(6, restart_threshold=116, coeff_list=O.coefficient_schedule(QUINTIC, 6, 1.05)) == [3]
+
+
+def test_restart_threshold_schedule_by_hand():
+    """Per-iteration slopes a = 2, 2, 4, 1.5, 3 give growths 4, 4, 16, 2.25, 9; with
+    tau = 15 the products since the last restart are 4, 16 (restart), 16 (restart),
+    2.25, then the last iteration, which never restarts."""
+    sched = [(2.0, 0.0, 0.0), (2.0, 0.0, 0.0), (4.0, 0.0, 0.0), (1.5, 0.0, 0.0), (3.0, 0.0, 0.0)]
+    assert O.restart_points(5, restart_threshold=15.0, coeff_list=sched) == [2, 3]
+    # a mask still wins over the threshold; a threshold wins over restart_every
+    assert O.restart_points(5, restart_mask=0b1, restart_threshold=15.0, coeff_list=sched) == [1]
+    assert O.restart_points(5, restart_every=1, restart_threshold=15.0, coeff_list=sched) == [2, 3]
+    with pytest.raises(ValueError):
+        O.restart_points(5, restart_threshold=15.0)
+
+
+def test_restart_threshold_growth_factor_is_a_squared():
+    """The premise of R12, checked on the oracle's own polynomial step: an error of
+    size eps in a null direction of G comes out of one Gram update P G P multiplied
+    by a^2 (to first order), with P = a I + b G + c G^2."""
+    a, b, c = QUINTIC
+    lam = np.array([0.0, 0.3, 0.9, 1.2])
+    G = np.diag(lam)
+    eps = 1e-9
+    dG = np.zeros_like(G)
+    dG[0, 0] = eps
+
+    def step(H):
+        P = O.gram_polynomial(H, a, b, c)
+        return P @ H @ P
+
+    grown = (step(G + dG) - step(G))[0, 0]
+    assert abs(grown / eps - a * a) < 1e-6 * a * a
+
+
+def test_restart_threshold_keeps_exact_output():
+    """Restarts change only rounding: with threshold-chosen restarts the fp64 output
+    still equals the SVD closed form."""
+    M = RNG.standard_normal((24, 40))
+    ref = svd_closed_form(M, QUINTIC, 6)
+    for tau in (5.0, 100.0, 1e3):
+        out, _ = O.orthogonalize(M, n_iter=6, restart_threshold=tau)
+        assert np.abs(out - ref).max() < 1e-12
+
+
 # ------------------------------------- the single steps of one iteration
 @pytest.mark.parametrize("shape", [(7, 33), (33, 7), (40, 40), (1, 9), (9, 1)])
 def test_gram_spectrum_is_squared_singular_values(shape):
