@@ -94,10 +94,21 @@ typedef struct {
  *   n_iter        K >= 1 (at most 64)
  *   restart_every restart after every restart_every-th iteration (0 = none)
  *   restart_mask  if nonzero, bit (k-1) set = restart after iteration k;
- *                 overrides restart_every.  Never applied after iteration K.
+ *                 overrides restart_threshold and restart_every.  Never
+ *                 applied after iteration K.
  *   safety        s > 0
  *   row_frac      in (0, 1]
- *   precision     a dion_precision value */
+ *   precision     a dion_precision value
+ *   restart_threshold  tau >= 0 (0 = off); with no mask it overrides
+ *                 restart_every: a restart follows the iteration at which the
+ *                 product of (a_k / s)^2 since the last restart first reaches
+ *                 tau.  (a_k/s)^2 is the factor by which one iteration scales
+ *                 an error of the Gram matrix in its smallest singular
+ *                 directions, where the spurious negative eigenvalues that
+ *                 restarts remove appear (Dion3 summary, 局限: restart
+ *                 threshold).  With the fixed quintic, tau = 100 restarts
+ *                 every 2 iterations.  Evaluated on the host from the
+ *                 coefficients: no device synchronization. */
 typedef struct {
   const float* ns_coeffs;
   int32_t n_coeff_sets;
@@ -107,7 +118,14 @@ typedef struct {
   float safety;
   float row_frac;
   int32_t precision;
+  float restart_threshold;
 } dion_ns_params;
+
+/* The iterations after which this parameter set restarts (host only, no
+ * device work): writes up to `cap` 1-based iteration indices, ascending, to
+ * `after` (may be NULL when cap = 0) and returns how many there are, or a
+ * negative dion error code for invalid parameters. */
+int dion_restart_points(const dion_ns_params* p, int32_t* after, int32_t cap);
 
 /* Bytes of device workspace needed by dion_orth_batched for this batch
  * (pure function of its arguments; 0 on invalid arguments).  For

@@ -13,18 +13,18 @@ from ._lib import DION_BF16, DION_FP16, DION_FP32, PHASE, PREC, DionError, DionP
 
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
            "DionError", "QUINTIC", "profile_enable", "profile_records", "rowkeys_topk", "syrk", "sympoly",
-           "apply", "rowsubset_step_update", "Dion3"]
+           "apply", "rowsubset_step_update", "Dion3", "restart_points"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
 
-def _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision):
+def _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold=0.0):
     flat = [float(x) for trip in ([coeffs] if len(coeffs) == 3 and not hasattr(coeffs[0], "__len__")
                                   else coeffs) for x in trip]
     arr = (ctypes.c_float * len(flat))(*flat)
     p = DionParams(ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), len(flat) // 3, int(n_iter),
                    int(restart_every), int(restart_mask), float(safety), float(row_frac),
-                   PREC[precision] if isinstance(precision, str) else int(precision))
+                   PREC[precision] if isinstance(precision, str) else int(precision), float(restart_threshold))
     return p, arr
 
 
@@ -59,8 +59,8 @@ def _check_tensors(ts, dtype=None):
 
 
 def workspace_size(shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                   safety=1.0, row_frac=1.0, precision="auto") -> int:
-    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision)
+                   safety=1.0, row_frac=1.0, precision="auto", restart_threshold=0.0) -> int:
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold)
     code = {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
     n = lib.dion_workspace_size(_shapes(shapes), len(shapes), code, ctypes.byref(p))
     if n == 0:
@@ -69,9 +69,19 @@ def workspace_size(shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every
 
 
 def useful_flops(shapes, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
-                 row_frac=1.0) -> float:
-    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, "auto")
+                 row_frac=1.0, restart_threshold=0.0) -> float:
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, "auto", restart_threshold)
     return float(lib.dion_useful_flops(_shapes(shapes), len(shapes), ctypes.byref(p)))
+
+
+def restart_points(coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
+                   restart_threshold=0.0) -> list:
+    """The iterations (1-based) after which these hyper-parameters restart, as the library plans them."""
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, 1.0, "auto", restart_threshold)
+    buf = (ctypes.c_int32 * 64)()
+    n = lib.dion_restart_points(ctypes.byref(p), buf, 64)
+    check(n if n < 0 else 0)
+    return [int(buf[i]) for i in range(n)]
 
 
 def _workspace(nbytes, device, workspace):
@@ -95,12 +105,13 @@ class Orthogonalizer:
     its own workspace, so repeated calls only marshal pointers."""
 
     def __init__(self, shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                 safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False):
+                 safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False, restart_threshold=0.0):
         import torch
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.dtype = dtype
         self.step_mode = step_mode
-        self._p, self._keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision)
+        self._p, self._keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision,
+                                      restart_threshold)
         self._shp = _shapes(self.shapes)
         code = DION_FP32 if step_mode else {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
         self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
@@ -144,7 +155,7 @@ class Orthogonalizer:
 
 
 def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
-                 row_frac=1.0, precision="auto", return_indices=False, stream=None):
+                 row_frac=1.0, precision="auto", return_indices=False, stream=None, restart_threshold=0.0):
     """Orthogonalize a list of 2-D bf16 or fp32 CUDA tensors in one megabatched call.
 
     Returns the list of outputs (same shapes and dtype), and with
@@ -154,7 +165,7 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
     _check_tensors(Ms, Ms[0].dtype)
     dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(Ms[0].dtype, "fp32")
     orth = Orthogonalizer([tuple(M.shape) for M in Ms], dt, coeffs, n_iter, restart_every, restart_mask,
-                          safety, row_frac, precision, device=Ms[0].device)
+                          safety, row_frac, precision, device=Ms[0].device, restart_threshold=restart_threshold)
     if outs is None:
         outs = [torch.empty_like(M) for M in Ms]
     _check_tensors(outs, Ms[0].dtype)
@@ -166,13 +177,14 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
 
 
 def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                   safety=1.0, row_frac=0.125, return_indices=False, stream=None):
+                   safety=1.0, row_frac=0.125, return_indices=False, stream=None, restart_threshold=0.0):
     """One row-subset step: E <- fl32(fl32(beta E) + grad) in place; returns bf16 outputs."""
     import torch
     _check_tensors(Es, torch.float32)
     _check_tensors(grads, grads[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
-                          safety, row_frac, "mfma16", device=Es[0].device, step_mode=True)
+                          safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
+                          restart_threshold=restart_threshold)
     if outs is None:
         outs = [torch.empty(E.shape, dtype=torch.bfloat16, device=E.device) for E in Es]
     _check_tensors(outs, torch.bfloat16)
@@ -264,14 +276,15 @@ def apply(Qs, Xs, precision="auto", stream=None):
 
 def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=QUINTIC, n_iter=5,
                           restart_every=0, restart_mask=0, safety=1.0, row_frac=0.125, return_indices=False,
-                          stream=None):
+                          stream=None, restart_threshold=0.0):
     """One row-subset step fused with the weight update; E and W are updated in place."""
     import torch
     _check_tensors(Es, torch.float32)
     _check_tensors(grads, grads[0].dtype)
     _check_tensors(Ws, Ws[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
-                          safety, row_frac, "mfma16", device=Es[0].device, step_mode=True)
+                          safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
+                          restart_threshold=restart_threshold)
     sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
     orth.step_update(Es, grads, Ws, beta, alphas, weight_decay, sel, stream)
     if not return_indices:

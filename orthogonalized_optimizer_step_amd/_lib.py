@@ -30,6 +30,7 @@ class DionParams(ctypes.Structure):
         ("safety", ctypes.c_float),
         ("row_frac", ctypes.c_float),
         ("precision", ctypes.c_int32),
+        ("restart_threshold", ctypes.c_float),
     ]
 
 
@@ -39,7 +40,7 @@ EXPORTS = (
     "dion_rowsubset_step", "dion_useful_flops", "dion_selected_rows", "dion_strerror",
     "dion_last_error", "dion_version", "dion_profile_enable", "dion_profile_count",
     "dion_profile_get", "dion_phase_workspace_size", "dion_rowkeys_topk_batched", "dion_syrk_batched",
-    "dion_sympoly_batched", "dion_apply_batched", "dion_rowsubset_step_update",
+    "dion_sympoly_batched", "dion_apply_batched", "dion_rowsubset_step_update", "dion_restart_points",
 )
 
 
@@ -77,6 +78,8 @@ def _load():
     lib.dion_useful_flops.restype = ctypes.c_double
     lib.dion_selected_rows.argtypes = [i32, ctypes.c_float]
     lib.dion_selected_rows.restype = i32
+    lib.dion_restart_points.argtypes = [prm, ctypes.POINTER(i32), i32]
+    lib.dion_restart_points.restype = ctypes.c_int
     lib.dion_strerror.argtypes = [ctypes.c_int]
     lib.dion_strerror.restype = ctypes.c_char_p
     lib.dion_last_error.argtypes = []

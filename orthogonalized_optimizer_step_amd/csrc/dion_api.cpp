@@ -95,8 +95,21 @@ int parse_params(const dion_ns_params* p, int dtype, bool step_mode, Params& out
     out.b[k] = (double)t[1] / (s * s * s);
     out.c[k] = (double)t[2] / (s * s * s * s * s);
   }
+  if (!std::isfinite(p->restart_threshold) || p->restart_threshold < 0.f)
+    return fail(DION_E_INVAL, "restart_threshold must be finite and >= 0");
+  const bool by_threshold = !p->restart_mask && p->restart_threshold > 0.f;
+  double growth = 1.0;  // product of a_k^2 since the last restart
   for (int k = 1; k < K; ++k) {  // never after the last iteration
-    bool r = p->restart_mask ? ((p->restart_mask >> (k - 1)) & 1u) : (p->restart_every > 0 && k % p->restart_every == 0);
+    bool r;
+    if (p->restart_mask) {
+      r = k <= 32 && ((p->restart_mask >> (k - 1)) & 1u);
+    } else if (by_threshold) {
+      growth *= out.a[k - 1] * out.a[k - 1];
+      r = growth >= (double)p->restart_threshold;
+      if (r) growth = 1.0;
+    } else {
+      r = p->restart_every > 0 && k % p->restart_every == 0;
+    }
     out.restart[k - 1] = r ? 1 : 0;
   }
   out.row_frac = p->row_frac;
@@ -1428,6 +1441,20 @@ double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_
 int32_t dion_selected_rows(int32_t rows, float row_frac) {
   if (rows < 1 || !(row_frac > 0.f && row_frac <= 1.f)) return 0;
   return selected_count(rows, row_frac);
+}
+
+int dion_restart_points(const dion_ns_params* p, int32_t* after, int32_t cap) {
+  Params P;
+  const int rc = parse_params(p, DION_BF16, false, P);
+  if (rc != DION_OK) return rc;
+  if (cap < 0 || (cap > 0 && !after)) return fail(DION_E_INVAL, "after must hold cap entries");
+  int n = 0;
+  for (size_t k = 0; k < P.restart.size(); ++k)
+    if (P.restart[k]) {
+      if (n < cap) after[n] = (int32_t)(k + 1);
+      ++n;
+    }
+  return n;
 }
 
 int dion_profile_enable(int enable) {

@@ -34,8 +34,10 @@ class Dion3(torch.optim.Optimizer):
       row_frac      fraction of each momentum matrix's rows orthogonalized per
                     step (largest L2 norms); the other rows apply the raw momentum
       weight_decay  decoupled: W <- W (1 - lr * weight_decay) - lr * scale * update
-      ns_coeffs, n_iter, restart_every, safety
-                    the Gram Newton-Schulz schedule
+      ns_coeffs, n_iter, restart_every, safety, restart_threshold
+                    the Gram Newton-Schulz schedule (a positive restart_threshold
+                    replaces restart_every: restart once the product of a_k^2
+                    since the last restart reaches it)
       shape_scale   callable(shape) -> float, or None for 1 (default:
                     sqrt(max(1, rows / cols)))
 
@@ -45,12 +47,12 @@ class Dion3(torch.optim.Optimizer):
     """
 
     def __init__(self, params, lr=0.02, momentum=0.95, row_frac=0.125, weight_decay=0.0, ns_coeffs=QUINTIC,
-                 n_iter=5, restart_every=2, safety=1.0, shape_scale=rows_over_cols_scale):
+                 n_iter=5, restart_every=2, safety=1.0, shape_scale=rows_over_cols_scale, restart_threshold=0.0):
         if lr < 0 or not 0 < row_frac <= 1 or weight_decay < 0:
             raise ValueError("invalid lr, row_frac or weight_decay")
         defaults = dict(lr=lr, momentum=momentum, row_frac=row_frac, weight_decay=weight_decay,
                         ns_coeffs=tuple(ns_coeffs), n_iter=n_iter, restart_every=restart_every, safety=safety,
-                        shape_scale=shape_scale)
+                        shape_scale=shape_scale, restart_threshold=restart_threshold)
         super().__init__(params, defaults)
         for g in self.param_groups:
             for p in g["params"]:
@@ -60,11 +62,13 @@ class Dion3(torch.optim.Optimizer):
 
     def _orthogonalizer(self, shapes, g):
         from . import Orthogonalizer
-        key = (tuple(shapes), g["ns_coeffs"], g["n_iter"], g["restart_every"], g["safety"], g["row_frac"])
+        key = (tuple(shapes), g["ns_coeffs"], g["n_iter"], g["restart_every"], g["safety"], g["row_frac"],
+               g["restart_threshold"])
         orth = self._orth.get(key)
         if orth is None:
             orth = Orthogonalizer(shapes, "fp32", g["ns_coeffs"], g["n_iter"], g["restart_every"], 0, g["safety"],
-                                  g["row_frac"], "mfma16", device="cuda", step_mode=True)
+                                  g["row_frac"], "mfma16", device="cuda", step_mode=True,
+                                  restart_threshold=g["restart_threshold"])
             self._orth[key] = orth
         return orth
 

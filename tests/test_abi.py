@@ -134,3 +134,38 @@ def test_phase_workspace_sizes_and_validation():
                                        None) == -1                                              # row_frac 0
     ms = (ctypes.c_int32 * 1)(0)
     assert L.dion_sympoly_batched(null2, null2, ms, 1, None, 1, None, 0, None) == -1             # m = 0
+
+
+@pytest.mark.parametrize("n_iter", [1, 2, 5, 6, 9, 40])
+@pytest.mark.parametrize("tau", [5.0, 100.0, 116.0, 1000.0, 1e4, 1e30])
+@pytest.mark.parametrize("safety", [1.0, 1.05])
+def test_restart_threshold_matches_oracle(n_iter, tau, safety):
+    """The planner's restart points for a threshold equal the oracle's (reading R12)."""
+    got = dion.restart_points(n_iter=n_iter, safety=safety, restart_threshold=tau)
+    want = O.restart_points(n_iter, restart_threshold=tau,
+                            coeff_list=O.coefficient_schedule(dion.QUINTIC, n_iter, safety))
+    assert got == want
+
+
+def test_restart_points_schedules_and_precedence():
+    sched = [(2.0, -1.0, 0.5), (2.0, -1.0, 0.5), (4.0, -1.0, 0.5), (1.5, -1.0, 0.5), (3.0, -1.0, 0.5)]
+    want = O.restart_points(5, restart_threshold=15.0, coeff_list=O.coefficient_schedule(sched, 5))
+    assert want == [2, 3]
+    assert dion.restart_points(coeffs=sched, n_iter=5, restart_threshold=15.0) == want
+    assert dion.restart_points(coeffs=sched, n_iter=5, restart_every=1, restart_threshold=15.0) == want
+    assert dion.restart_points(coeffs=sched, n_iter=5, restart_mask=0b1, restart_threshold=15.0) == [1]
+    assert dion.restart_points(n_iter=6, restart_every=2) == O.restart_points(6, restart_every=2)
+    assert dion.restart_points(n_iter=5, restart_mask=0b10) == [2]
+    assert dion.restart_points(n_iter=40, restart_mask=1 << 31) == [32]
+    assert dion.restart_points(n_iter=5) == []
+
+
+def test_restart_threshold_flops_and_validation():
+    shapes = [(4096, 4096), (1024, 4096), (4096, 14336)]
+    assert dion.useful_flops(shapes, restart_threshold=100.0) == dion.useful_flops(shapes, restart_every=2)
+    assert dion.useful_flops(shapes, restart_threshold=1000.0) == dion.useful_flops(shapes, restart_mask=0b100)
+    for bad in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(dion.DionError):
+            dion.restart_points(n_iter=5, restart_threshold=bad)
+        with pytest.raises(dion.DionError):
+            dion.workspace_size(shapes, restart_threshold=bad)

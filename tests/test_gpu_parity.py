@@ -73,7 +73,8 @@ def small_batch(seed, dtype_bf16=True):
 
 
 @pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10, safety=1.01),
-                                   dict(n_iter=6, restart_every=2, safety=1.05)])
+                                   dict(n_iter=6, restart_every=2, safety=1.05),
+                                   dict(n_iter=6, restart_threshold=116.0, safety=1.05)])
 def test_small_ragged_fp64_path(dion, sched):
     Ms = small_batch(11)
     outs = dion.orth_batched([torch.from_numpy(M).cuda() for M in Ms], precision="fp64",
@@ -87,7 +88,9 @@ def test_small_ragged_fp64_path(dion, sched):
 # ---------------------------------------------------------- MFMA16 path
 @pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10, safety=1.01),
                                    dict(n_iter=6, restart_every=2, safety=1.05), dict(restart_every=1),
-                                   dict(n_iter=6, restart_every=1)])
+                                   dict(n_iter=6, restart_every=1), dict(restart_threshold=1000.0),
+                                   dict(n_iter=6, restart_threshold=116.0, safety=1.05),
+                                   dict(n_iter=6, restart_threshold=5.0)])
 def test_small_ragged_mfma16(dion, sched):
     Ms = small_batch(12)
     kw = {"n_iter": 5, **sched}
@@ -98,6 +101,17 @@ def test_small_ragged_mfma16(dion, sched):
         errs.append(O.rel_frobenius(to_np(o), ref))
     print("MFMA16 small ragged", sched, " ".join(f"{e:.2e}" for e in errs), flush=True)
     assert max(errs) <= TOL_MFMA16
+
+
+def test_restart_threshold_same_plan_as_mask(dion):
+    """A threshold only chooses the restart points: tau = 100 with the fixed quintic
+    plans restarts {2, 4}, so the output is bit-identical to restart_every = 2."""
+    Ms = small_batch(14)
+    dev = [to_dev_bf16(M) for M in Ms]
+    a = dion.orth_batched(dev, restart_threshold=100.0)
+    b = dion.orth_batched(dev, restart_every=2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 def test_fp32_input_mfma16(dion):
