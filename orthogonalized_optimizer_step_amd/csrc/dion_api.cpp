@@ -168,6 +168,8 @@ struct Step {
   PhaseArgs pa{};
   int src_slot = 0, dst_slot = 0;
   int dset = 0;          // phase entry points: 0 = the matrices, 1 = the apply's Q operands
+  int ranges = -1;       // ST_GEMM: index of its 9 tile-range starts in Plan::range_ints
+  int grid = 0;          // ST_GEMM: blocks launched
   float scale = 1.f;     // ST_UNPACK: value scale (times nu^2 when use_nu2)
   bool use_nu2 = false;
   // accounting for profiles: name, useful FLOPs, executed MFMA FLOPs, algorithmic bytes
@@ -205,12 +207,23 @@ struct Plan {
   float keep = 1.f;
   size_t off_descs = 0, off_scalars = 0, off_keys = 0, off_flags = 0, off_idx = 0, off_ints = 0,
          off_data = 0, total = 0, upload_bytes = 0;
+  // per GEMM launch, the 9 starts of its 8 per-XCD tile ranges (uploaded
+  // with the header; room for max_ranges launches is reserved at layout time)
+  size_t off_ranges = 0;
+  int max_ranges = 0;
+  std::vector<int> range_ints;
   std::vector<int> ints;
   std::vector<Table> tabs;
   std::vector<Step> steps;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Splits a GEMM launch's tiles into 8 contiguous ranges, one per XCD, of
+// equal work: a tile costs its reduction depth K plus a fixed 512 for its
+// prologue and epilogue.  Batches grouped by shape (all the long-K matrices
+// last, say) would otherwise leave most of the work to one XCD.
+void balance_ranges(Plan& P, int table, const PhaseArgs& pa, Step& g);
 
 int add_table(Plan& P, const std::vector<int>& mats, const std::vector<int>& counts) {
   Table t;
@@ -227,6 +240,39 @@ int add_table(Plan& P, const std::vector<int>& mats, const std::vector<int>& cou
   t.total = acc;
   P.tabs.push_back(t);
   return (int)P.tabs.size() - 1;
+}
+
+void balance_ranges(Plan& P, int table, const PhaseArgs& pa, Step& g) {
+  const Table& tb = P.tabs[table];
+  const int* mats = P.ints.data() + tb.mats_off;
+  const int* prefix = P.ints.data() + tb.prefix_off;
+  std::vector<double> cost(tb.nmat);
+  double total = 0.0;
+  for (int j = 0; j < tb.nmat; ++j) {
+    const MatPlan& mp = P.mats[mats[j]];
+    cost[j] = (double)(pa.k_is_n ? mp.n_pad : mp.m_pad) + 512.0;
+    total += cost[j] * (prefix[j + 1] - prefix[j]);
+  }
+  int r[9];
+  r[0] = 0;
+  r[8] = tb.total;
+  double cum = 0.0;  // work of the matrices before j
+  int j = 0;
+  for (int x = 1; x < 8; ++x) {
+    const double target = total * x / 8.0;
+    while (j < tb.nmat && cum + cost[j] * (prefix[j + 1] - prefix[j]) < target) {
+      cum += cost[j] * (prefix[j + 1] - prefix[j]);
+      ++j;
+    }
+    int t = tb.total;
+    if (j < tb.nmat) t = prefix[j] + (int)std::ceil((target - cum) / cost[j]);
+    r[x] = std::min(std::max(t, r[x - 1]), tb.total);
+  }
+  int widest = 0;
+  for (int x = 0; x < 8; ++x) widest = std::max(widest, r[x + 1] - r[x]);
+  g.ranges = (int)(P.range_ints.size() / 9);
+  g.grid = 8 * widest;
+  P.range_ints.insert(P.range_ints.end(), r, r + 9);
 }
 
 int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm, bool step_mode, Plan& P,
@@ -336,9 +382,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   }
   const int t_pack = add_table(P, all, pack_c);
   const int t_tr = add_table(P, all, tr_c);
-  // uploaded part: descriptors, then tables; then device-written scratch
+  // uploaded part: descriptors, tables, tile ranges; then device-written scratch
   P.off_ints = off;
   off = align256(off + sizeof(int) * P.ints.size());
+  P.max_ranges = 16 + 8 * K;   // more than the GEMM launches of any plan below
+  P.off_ranges = off;
+  off = align256(off + sizeof(int) * 9 * P.max_ranges);
   P.upload_bytes = off;
   P.off_scalars = off; off = align256(off + sizeof(MatScalars) * batch);
   P.off_keys = off;    off = align256(off + sizeof(double) * P.total_rows);
@@ -425,6 +474,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     }
     g.kind = ST_GEMM;
     g.table = table;
+    balance_ranges(P, table, pa, g);
     g.bm = bm;
     g.sym = sym;
     g.na = P.fp64 ? 1 : na;
@@ -722,6 +772,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     cp.bytes = 2.0 * unsel_elems * in_es + rows;
     P.steps.push_back(cp);
   }
+  if ((int)P.range_ints.size() > 9 * P.max_ranges)
+    return fail(DION_E_UNSUPPORTED, "internal: more GEMM launches than reserved tile ranges");
   return DION_OK;
 }
 
@@ -818,6 +870,9 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
   off = align256(off + sizeof(MatDesc) * ndesc);
   P.off_ints = off;
   off = align256(off + sizeof(int) * P.ints.size());
+  P.max_ranges = 16;
+  P.off_ranges = off;
+  off = align256(off + sizeof(int) * 9 * P.max_ranges);
   if (ph == PH_POLY) {  // the operand scale is known on the host: ||G||_2 <= 1
     P.host_scalars = true;
     P.off_scalars = off;
@@ -868,6 +923,7 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
     g->epi = epi;
     g->pa = pa;
     g->pa.out_lo = 1;
+    balance_ranges(P, table, pa, *g);
   };
   const float sG = P.fp64 ? 1.f : pow2_scale(1.0);
   if (ph == PH_KEYS || ph == PH_SYRK || ph == PH_APPLY) {
@@ -930,6 +986,8 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
     pt.out_rows_are_m = 0;
     if (!tall.empty()) gemm(t_tall, bm_fin, false, P.xterms0, 2, EPI_OUT, pt, "final");
   }
+  if ((int)P.range_ints.size() > 9 * P.max_ranges)
+    return fail(DION_E_UNSUPPORTED, "internal: more GEMM launches than reserved tile ranges");
   return DION_OK;
 }
 
@@ -1094,6 +1152,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     sel0 += mp.m;
   }
   std::memcpy(blob.data() + P.off_ints, P.ints.data(), sizeof(int) * P.ints.size());
+  std::memcpy(blob.data() + P.off_ranges, P.range_ints.data(), sizeof(int) * P.range_ints.size());
   if (P.host_scalars) std::memcpy(blob.data() + P.off_scalars, P.hscal.data(), sizeof(MatScalars) * P.hscal.size());
   int rc = upload(blob.data(), blob.size(), ws, stream);
   if (rc) return rc;
@@ -1148,7 +1207,8 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
       }
       case ST_GEMM: {
         const Table& t = P.tabs[st.table];
-        GemmLaunch L{d_descs, d_ints + t.mats_off, d_ints + t.prefix_off, t.nmat, t.total};
+        GemmLaunch L{d_descs, d_ints + t.mats_off, d_ints + t.prefix_off, t.nmat, t.total,
+                     (const int*)(ws + P.off_ranges) + 9 * st.ranges, st.grid};
         PhaseArgs pa = st.pa;
         pa.scalars = d_scal;
         pa.idx = P.use_idx ? d_idx : nullptr;

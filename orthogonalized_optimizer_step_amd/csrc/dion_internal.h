@@ -104,7 +104,9 @@ struct GemmLaunch {
   const int* mats;
   const int* prefix;
   int nmat;
-  int total;
+  int total;           // tiles
+  const int* ranges;   // 9 ints: XCD x runs tiles [ranges[x], ranges[x+1])
+  int grid;            // 8 * the largest range
 };
 
 }  // namespace dion

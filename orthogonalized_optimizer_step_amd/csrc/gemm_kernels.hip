@@ -56,11 +56,15 @@ __device__ __forceinline__ int find_segment(const int* prefix, int n, int t) {
   return lo;
 }
 
-// Blocks are dealt to the 8 XCDs round-robin; give XCD x the contiguous
-// logical range [x*per, (x+1)*per).  Grid = 8 * per; extra blocks exit.
-__device__ __forceinline__ int xcd_remap(int b, int total) {
-  const int per = (total + 7) >> 3;
-  return (b & 7) * per + (b >> 3);
+// Blocks are dealt to the 8 XCDs round-robin; block b runs tile
+// ranges[x] + b / 8 of the contiguous range [ranges[x], ranges[x+1]) of XCD
+// x = b % 8, so the tiles an XCD runs at once share operand panels in its
+// L2.  The host sizes the ranges to equal work (tiles weighted by their
+// reduction depth), and launches 8 * (largest range) blocks; the rest exit.
+__device__ __forceinline__ int range_tile(const int* __restrict__ ranges, int b) {
+  const int x = b & 7;
+  const int t = ranges[x] + (b >> 3);
+  return t < ranges[x + 1] ? t : -1;
 }
 
 // Tile order within a matrix: bands of GROUP tile-rows, each band walked
@@ -537,7 +541,7 @@ template <int BM, int NA, int NB, int EPI, bool SYM>
 __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ descs,
                                                    const int* __restrict__ mats,
                                                    const int* __restrict__ prefix, int nmat,
-                                                   int total, PhaseArgs pa) {
+                                                   const int* __restrict__ ranges, PhaseArgs pa) {
   constexpr int NT = NA + NB;
   constexpr int BK = 32;
   constexpr int SLOTS = BK / 8;              // 16-byte chunks per stage row
@@ -559,8 +563,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
                 "every fragment read and copy needs an MFMA slot");
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
-  const int t = xcd_remap(blockIdx.x, total);
-  if (t >= total) return;
+  const int t = range_tile(ranges, blockIdx.x);
+  if (t < 0) return;
   const int j = find_segment(prefix, nmat, t);
   const int mi = mats[j];
   const MatDesc& d = descs[mi];
@@ -709,12 +713,12 @@ template <int EPI, bool SYM>
 __global__ __launch_bounds__(256) void k_gemm64(const MatDesc* __restrict__ descs,
                                                 const int* __restrict__ mats,
                                                 const int* __restrict__ prefix, int nmat,
-                                                int total, PhaseArgs pa) {
+                                                const int* __restrict__ ranges, PhaseArgs pa) {
   constexpr int BM = 64, BK = 16;
   __shared__ double sA[BK][BM + 1];
   __shared__ double sB[BK][BM + 1];
-  const int t = xcd_remap(blockIdx.x, total);
-  if (t >= total) return;
+  const int t = range_tile(ranges, blockIdx.x);
+  if (t < 0) return;
   const int j = find_segment(prefix, nmat, t);
   const int mi = mats[j];
   const MatDesc& d = descs[mi];
@@ -760,13 +764,13 @@ __global__ __launch_bounds__(256) void k_gemm64(const MatDesc* __restrict__ desc
 // ---------------------------------------------------------------- launchers
 #define DION_G16(BM_, NA_, NB_, EPI_, SYM_) \
   hipLaunchKernelGGL((k_gemm16<BM_, NA_, NB_, EPI_, SYM_>), dim3(grid), dim3(256), 0, stream, \
-                     L.descs, L.mats, L.prefix, L.nmat, L.total, pa)
+                     L.descs, L.mats, L.prefix, L.nmat, L.ranges, pa)
 
 // Returns false for an unsupported combination.
 bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& L,
                    const PhaseArgs& pa, hipStream_t stream) {
   if (L.total <= 0) return true;
-  const int grid = ((L.total + 7) / 8) * 8;
+  const int grid = L.grid;
   const int key = (na << 8) | (nb << 4) | epi;
 #define DION_CASES(BM_)                                                                  \
   if (sym) {                                                                             \
@@ -799,10 +803,10 @@ bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& 
 
 bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream) {
   if (L.total <= 0) return true;
-  const int grid = ((L.total + 7) / 8) * 8;
+  const int grid = L.grid;
 #define DION_G64(EPI_, SYM_) \
   hipLaunchKernelGGL((k_gemm64<EPI_, SYM_>), dim3(grid), dim3(256), 0, stream, L.descs, L.mats, \
-                     L.prefix, L.nmat, L.total, pa)
+                     L.prefix, L.nmat, L.ranges, pa)
   if (sym) {
     if (epi == EPI_SYM) { DION_G64(EPI_SYM, true); return true; }
     if (epi == EPI_POLY) { DION_G64(EPI_POLY, true); return true; }

@@ -465,7 +465,22 @@ __global__ __launch_bounds__(256) void k_copy_unselected(const MatDesc* __restri
   const int64_t r = g - d.row0;
   const InT* src = (const InT*)d.M + r * d.C;
   InT* dst = (InT*)d.out + r * d.C;
-  for (int c = lane; c < d.C; c += 64) dst[c] = src[c];
+  const size_t bytes = (size_t)d.C * sizeof(InT);
+  if (((bytes | (uintptr_t)src | (uintptr_t)dst) & 15) == 0) {
+    // 16 bytes per lane, two chunks in flight per lane
+    const uint4* s4 = (const uint4*)src;
+    uint4* d4 = (uint4*)dst;
+    const int n = (int)(bytes >> 4);
+    int c = lane;
+    for (; c + 64 < n; c += 128) {
+      const uint4 x0 = s4[c], x1 = s4[c + 64];
+      d4[c] = x0;
+      d4[c + 64] = x1;
+    }
+    if (c < n) d4[c] = s4[c];
+  } else {
+    for (int c = lane; c < d.C; c += 64) dst[c] = src[c];
+  }
 }
 
 // ------------------------------------------- weight update, unselected rows
