@@ -307,3 +307,25 @@ def test_fp16_full_size(dion):
     err = O.rel_frobenius(to_np(out), ref)
     print(f"fp16 4096x14336: rel err {err:.3e}", flush=True)
     assert err <= TOL_MFMA16
+
+
+@pytest.mark.parametrize("prec", ["mfma16", "fp64"])
+def test_batch_order_independence(dion, prec):
+    """A tile's arithmetic does not depend on which XCD or CU runs it, so permuting
+    the batch (which moves the work-balanced per-XCD tile ranges) leaves every
+    matrix's output bit-identical.  Shapes mix reduction depths from 512 to 8192;
+    on the MFMA16 path four 4096 x 4096 matrices push the symmetric phases onto
+    256-row tiles."""
+    rng = np.random.default_rng(77)
+    if prec == "mfma16":
+        shapes = [(4096, 4096)] * 4 + [(1024, 8192)] * 3 + [(8192, 1024), (300, 500), (512, 512), (2048, 600)]
+        Ms = [to_dev_bf16(rng.standard_normal(s).astype(np.float32)) for s in shapes]
+    else:
+        shapes = [(96, 700), (64, 64), (500, 130), (40, 1200), (256, 256), (130, 333)]
+        Ms = [torch.from_numpy(rng.standard_normal(s).astype(np.float32)).cuda() for s in shapes]
+    kw = dict(n_iter=5, restart_every=2, precision=prec)
+    base = dion.orth_batched(Ms, **kw)
+    for perm in (list(range(len(Ms)))[::-1], list(rng.permutation(len(Ms)))):
+        outs = dion.orth_batched([Ms[i] for i in perm], **kw)
+        for o, i in zip(outs, perm):
+            assert torch.equal(o, base[i]), (prec, shapes[i], perm)
