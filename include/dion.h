@@ -186,6 +186,43 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
                                float beta, const float* alpha, float weight_decay, const dion_ns_params* p,
                                int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Low-rank update: Dion and Orth-Dion (Orth-Dion explainer, technical
+ * summary: Problem Statement, Methodology "The Geometric Insight" and
+ * "Orth-Dion", Error Feedback Analysis).  One step per matrix, with
+ * r = min(rank, R, C):
+ *   B = fl32(M + G)            the residual buffer takes the gradient
+ *   P = orth(B Q)              one power-iteration step from the previous Q
+ *   W = B^T P
+ *   M <- B - beta P W^T        error feedback (beta = 1 removes the captured part)
+ *   Q <- orth(W)  (DION_LOWRANK_QR, Orth-Dion)  or  W / column norms
+ *                              (DION_LOWRANK_COLNORM, Dion)
+ *   out = P Q^T                unscaled (the caller applies lr and shape factors)
+ * orth(F) is the reduced QR factor with a positive triangular diagonal,
+ * computed as CholeskyQR twice (Gram in fp32, Cholesky factor and its inverse
+ * in fp64).  Inputs for which B Q or W has rank below r are outside the
+ * method's contract (the factor is not unique): the output is finite but
+ * unspecified.
+ *   M[i]      device R x C fp32 buffer, updated in place
+ *   grad[i]   device R x C of grad_dtype (bf16, fp32 or fp16), read only
+ *   Q[i]      device C x r fp32 right factor: read as the previous one,
+ *             overwritten with the new one; must not overlap M[i]
+ *   out[i]    device R x C of out_dtype; must not overlap M[i]
+ *   rank      1 .. 512 (DION_E_UNSUPPORTED above)
+ * The rank-r products run as batched rocBLAS GEMMs (one group per distinct
+ * (R, C, r)), on the caller's stream with a 32 MiB slice of the workspace as
+ * rocBLAS's workspace; the rocBLAS handle (one per thread and device, made at
+ * the first call) holds rocBLAS's own state.  All other memory is the
+ * caller's workspace.  Asynchronous on `stream`. */
+typedef enum { DION_LOWRANK_QR = 0, DION_LOWRANK_COLNORM = 1 } dion_lowrank_mode;
+
+/* Bytes of workspace for dion_lowrank_step (0 on invalid arguments). */
+size_t dion_lowrank_workspace_size(const dion_shape* shapes, int32_t batch, int32_t rank, int32_t out_dtype);
+
+int dion_lowrank_step(float* const* M, const void* const* grad, float* const* Q, void* const* out,
+                      const dion_shape* shapes, int32_t batch, int32_t grad_dtype, int32_t out_dtype,
+                      int32_t rank, float beta, int32_t mode, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* ------------------------------------------------------------------------
  * Phase entry points: one step of the path on its own, with the same kernels,
  * operand layout and precision as inside dion_orth_batched, for kernel-level

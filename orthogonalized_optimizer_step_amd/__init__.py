@@ -13,7 +13,8 @@ from ._lib import DION_BF16, DION_FP16, DION_FP32, PHASE, PREC, DionError, DionP
 
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
            "DionError", "QUINTIC", "profile_enable", "profile_records", "rowkeys_topk", "syrk", "sympoly",
-           "apply", "rowsubset_step_update", "Dion3", "restart_points"]
+           "apply", "rowsubset_step_update", "Dion3", "restart_points", "lowrank_step",
+           "lowrank_workspace_size"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
@@ -290,6 +291,51 @@ def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=
     if not return_indices:
         return Ws
     return Ws, list(torch.split(sel, orth.selected))
+
+
+LOWRANK_MODE = {"qr": 0, "colnorm": 1}
+
+
+def lowrank_workspace_size(shapes, rank, out_dtype="bf16") -> int:
+    code = {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(out_dtype, out_dtype)
+    n = lib.dion_lowrank_workspace_size(_shapes(shapes), len(shapes), int(rank), code)
+    if n == 0:
+        raise DionError(-1, lib.dion_last_error().decode())
+    return int(n)
+
+
+def lowrank_step(Ms, grads, Qs, beta, mode="qr", outs=None, out_dtype=None, workspace=None, stream=None):
+    """One Dion ("colnorm") or Orth-Dion ("qr") low-rank step over a batch.
+
+    Ms: fp32 R x C buffers (updated in place); grads: R x C gradients (bf16,
+    fp32 or fp16); Qs: fp32 C x r right factors, r = min(rank, R, C) with one
+    rank for the batch (read, then overwritten with the new factors).
+    Returns the R x C updates P Q^T (bf16 unless out_dtype or outs say
+    otherwise).
+    """
+    import torch
+    _check_tensors(Ms, torch.float32)
+    _check_tensors(grads, grads[0].dtype)
+    _check_tensors(Qs, torch.float32)
+    shapes = [tuple(M.shape) for M in Ms]
+    rank = max(int(Q.shape[1]) for Q in Qs)
+    for (R, C), Q in zip(shapes, Qs):
+        if tuple(Q.shape) != (C, min(rank, R, C)):
+            raise DionError(-1, f"Q must be {C} x {min(rank, R, C)} for a {R} x {C} matrix at rank {rank}")
+    if outs is None:
+        dt = out_dtype if out_dtype is not None else torch.bfloat16
+        outs = [torch.empty(s, dtype=dt, device=Ms[0].device) for s in shapes]
+    _check_tensors(outs, outs[0].dtype)
+    ocode = _dtype_code(outs[0].dtype)
+    nbytes = lib.dion_lowrank_workspace_size(_shapes(shapes), len(shapes), rank, ocode)
+    if nbytes == 0:
+        raise DionError(-1, lib.dion_last_error().decode())
+    keep, ws, wl = _workspace(nbytes, Ms[0].device, workspace)
+    check(lib.dion_lowrank_step(_ptrs(Ms), _ptrs(grads), _ptrs(Qs), _ptrs(outs), _shapes(shapes), len(Ms),
+                                _dtype_code(grads[0].dtype), ocode, rank, float(beta),
+                                LOWRANK_MODE[mode] if isinstance(mode, str) else int(mode),
+                                ctypes.c_void_p(ws), wl, _stream(stream)))
+    return outs
 
 
 def profile_enable(on=True) -> bool:

@@ -41,6 +41,7 @@ EXPORTS = (
     "dion_last_error", "dion_version", "dion_profile_enable", "dion_profile_count",
     "dion_profile_get", "dion_phase_workspace_size", "dion_rowkeys_topk_batched", "dion_syrk_batched",
     "dion_sympoly_batched", "dion_apply_batched", "dion_rowsubset_step_update", "dion_restart_points",
+    "dion_lowrank_workspace_size", "dion_lowrank_step",
 )
 
 
@@ -80,6 +81,10 @@ def _load():
     lib.dion_selected_rows.restype = i32
     lib.dion_restart_points.argtypes = [prm, ctypes.POINTER(i32), i32]
     lib.dion_restart_points.restype = ctypes.c_int
+    lib.dion_lowrank_workspace_size.argtypes = [shp, i32, i32, i32]
+    lib.dion_lowrank_workspace_size.restype = sz
+    lib.dion_lowrank_step.argtypes = [pp, pp, pp, pp, shp, i32, i32, i32, i32, ctypes.c_float, i32, vp, sz, vp]
+    lib.dion_lowrank_step.restype = ctypes.c_int
     lib.dion_strerror.argtypes = [ctypes.c_int]
     lib.dion_strerror.restype = ctypes.c_char_p
     lib.dion_last_error.argtypes = []

@@ -22,6 +22,7 @@ ARCH = "gfx950"
 SOURCES = [
     ("gemm_kernels.hip", []),
     ("stream_kernels.hip", ["-ffp-contract=off"]),
+    ("lowrank_kernels.hip", ["-ffp-contract=off"]),
     ("dion_api.cpp", []),
 ]
 
@@ -55,7 +56,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -7,6 +7,7 @@
 // then per iteration P = aI + bG + cG^2, Q <- P Q, and either G <- P G P or,
 // at a restart, X <- Q X, G <- X X^T, Q <- I; finally out = Q X.
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <cmath>
@@ -14,11 +15,14 @@
 #include <cstring>
 #include <deque>
 #include <functional>
+#include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/dion.h"
 #include "dion_internal.h"
+#include "lowrank_internal.h"
 
 namespace dion {
 // launchers (gemm_kernels.hip, stream_kernels.hip)
@@ -1267,6 +1271,218 @@ int check_ptrs(const void* const* M, void* const* out, const dion_shape* shapes,
   return DION_OK;
 }
 
+
+// ------------------------------------------- low-rank (Dion / Orth-Dion) step
+// Orth-Dion explainer, technical summary: one power-iteration step from the
+// previous right factor, the residual (error-feedback) buffer, and the right
+// factor normalized by columns (Dion) or by QR (Orth-Dion).  Per matrix,
+// with r = min(rank, R, C):
+//   B = fl32(M + G)                        k_lr_accumulate (M in place)
+//   P = orth(B Q)                          GEMM, then CholeskyQR2
+//   W = B^T P                              GEMM
+//   M = B - beta P W^T                     GEMM (beta = -beta, accumulate)
+//   Q = orth(W) or colnorm(W)              CholeskyQR2, or k_lr_colnorm
+//   out = P Q^T                            GEMM (fp32, cast to bf16/fp16)
+// orth is CholeskyQR run twice: S = F^T F (GEMM), L = chol(S) and L^-1 in
+// fp64 (k_lr_cholinv), F <- F L^-T (GEMM); the triangular factor has a
+// positive diagonal, the QR convention of the oracle.  The rank-r products
+// are plain GEMMs and run in rocBLAS, batched over the matrices of one shape.
+constexpr int kMaxRank = 512;
+constexpr size_t kBlasWorkspace = (size_t)32 << 20;
+enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_N };
+
+struct LrGroup {
+  int R, C, r;
+  std::vector<int> mats;
+  size_t ptr_off;   // LP_N arrays of mats.size() device pointers
+};
+
+struct LrPlan {
+  std::vector<int> R, C, r;
+  std::vector<LrGroup> groups;
+  std::vector<int64_t> blk0;
+  int64_t blocks = 0;
+  bool out_fp32 = false;
+  size_t off_descs = 0, off_ptrs = 0, off_blas = 0, upload_bytes = 0, total = 0;
+  std::vector<size_t> off[LP_N];   // per matrix: X, Y, W, W2, S, L, A64 (in LP_D's place: D)
+  std::vector<size_t> off_a64;
+};
+
+int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, LrPlan& P) {
+  if (!shapes || batch < 1) return fail(DION_E_INVAL, "shapes must be non-NULL and batch >= 1");
+  if (rank < 1) return fail(DION_E_INVAL, "rank must be >= 1");
+  if (rank > kMaxRank) return fail(DION_E_UNSUPPORTED, "rank above 512 is not supported");
+  if (!valid_dtype(out_dtype)) return fail(DION_E_INVAL, "unknown output dtype");
+  P.out_fp32 = out_dtype == DION_FP32;
+  std::map<std::tuple<int, int, int>, int> gi;
+  P.R.resize(batch); P.C.resize(batch); P.r.resize(batch); P.blk0.resize(batch);
+  for (int i = 0; i < batch; ++i) {
+    const int R = shapes[i].rows, C = shapes[i].cols;
+    if (R < 1 || C < 1) return fail(DION_E_INVAL, "rows and cols must be >= 1");
+    const int r = std::min(rank, std::min(R, C));
+    P.R[i] = R; P.C[i] = C; P.r[i] = r;
+    auto key = std::make_tuple(R, C, r);
+    auto it = gi.find(key);
+    if (it == gi.end()) {
+      gi[key] = (int)P.groups.size();
+      P.groups.push_back(LrGroup{R, C, r, {i}, 0});
+    } else {
+      P.groups[it->second].mats.push_back(i);
+    }
+    P.blk0[i] = P.blocks;
+    P.blocks += ((int64_t)R * C + LR_BLOCK_ELEMS - 1) / LR_BLOCK_ELEMS;
+  }
+  size_t off = 0;
+  P.off_descs = off; off = align256(off + sizeof(LrDesc) * batch);
+  P.off_ptrs = off;
+  for (LrGroup& g : P.groups) { g.ptr_off = off; off += sizeof(float*) * LP_N * g.mats.size(); }
+  off = align256(off);
+  P.upload_bytes = off;
+  P.off_blas = off; off = align256(off + kBlasWorkspace);
+  for (int k = 0; k < LP_N; ++k) P.off[k].assign(batch, 0);
+  P.off_a64.assign(batch, 0);
+  for (int i = 0; i < batch; ++i) {
+    const size_t R = P.R[i], C = P.C[i], r = P.r[i];
+    P.off[LP_X][i] = off;  off = align256(off + 4 * R * r);
+    P.off[LP_Y][i] = off;  off = align256(off + 4 * R * r);
+    P.off[LP_W][i] = off;  off = align256(off + 4 * C * r);
+    P.off[LP_W2][i] = off; off = align256(off + 4 * C * r);
+    P.off[LP_S][i] = off;  off = align256(off + 4 * r * r);
+    P.off[LP_L][i] = off;  off = align256(off + 4 * r * r);
+    P.off_a64[i] = off;    off = align256(off + 8 * r * r);
+    if (!P.out_fp32) { P.off[LP_D][i] = off; off = align256(off + 4 * R * C); }
+  }
+  P.total = off;
+  return DION_OK;
+}
+
+// one rocBLAS handle per thread and device, created on first use
+int blas_handle(hipStream_t stream, void* wsp, rocblas_handle& h) {
+  thread_local std::vector<std::pair<int, rocblas_handle>> handles;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  h = nullptr;
+  for (auto& p : handles)
+    if (p.first == dev) h = p.second;
+  if (!h) {
+    if (rocblas_create_handle(&h) != rocblas_status_success) return fail(DION_E_HIP, "rocblas_create_handle failed");
+    handles.emplace_back(dev, h);
+  }
+  if (rocblas_set_stream(h, stream) != rocblas_status_success) return fail(DION_E_HIP, "rocblas_set_stream failed");
+  if (rocblas_set_workspace(h, wsp, kBlasWorkspace) != rocblas_status_success)
+    return fail(DION_E_HIP, "rocblas_set_workspace failed");
+  return DION_OK;
+}
+
+// Row-major C (m x n) = alpha op(A) op(B) + beta C over a batch of pointer
+// triples (device arrays), as the column-major product C^T = op(B)^T op(A)^T.
+// A is m x k (k x m when ta); B is k x n (n x k when tb).
+int gemm_rm(rocblas_handle h, bool ta, bool tb, int m, int n, int k, float alpha, float* const* A,
+            float* const* B, float beta, float* const* Cm, int count) {
+  const int lda = ta ? m : k, ldb = tb ? k : n;
+  const rocblas_status st = rocblas_sgemm_batched(
+      h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+      ta ? rocblas_operation_transpose : rocblas_operation_none, n, m, k, &alpha, (const float* const*)B, ldb,
+      (const float* const*)A, lda, &beta, Cm, n, count);
+  if (st != rocblas_status_success)
+    return fail(DION_E_HIP, "rocblas_sgemm_batched failed: " + std::string(rocblas_status_to_string(st)));
+  return DION_OK;
+}
+
+int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const* Q, void* const* out,
+           int batch, int grad_dtype, int out_dtype, float beta, int mode, void* workspace, size_t ws_bytes,
+           hipStream_t stream) {
+  if (!workspace) return fail(DION_E_WORKSPACE, "workspace is NULL");
+  if (((uintptr_t)workspace & 255) != 0) return fail(DION_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < P.total) return fail(DION_E_WORKSPACE, "workspace too small: need " + std::to_string(P.total) + " bytes");
+  char* ws = (char*)workspace;
+  std::vector<char> blob(P.upload_bytes, 0);
+  LrDesc* descs = (LrDesc*)(blob.data() + P.off_descs);
+  for (int i = 0; i < batch; ++i) {
+    LrDesc& d = descs[i];
+    d.M = M[i];
+    d.G = G[i];
+    d.Q = Q[i];
+    d.out = out[i];
+    d.X = (float*)(ws + P.off[LP_X][i]);
+    d.Y = (float*)(ws + P.off[LP_Y][i]);
+    d.W = (float*)(ws + P.off[LP_W][i]);
+    d.W2 = (float*)(ws + P.off[LP_W2][i]);
+    d.S = (float*)(ws + P.off[LP_S][i]);
+    d.Linv = (float*)(ws + P.off[LP_L][i]);
+    d.A64 = (double*)(ws + P.off_a64[i]);
+    d.D = P.out_fp32 ? (float*)out[i] : (float*)(ws + P.off[LP_D][i]);
+    d.elems = (int64_t)P.R[i] * P.C[i];
+    d.blk0 = P.blk0[i];
+    d.R = P.R[i];
+    d.C = P.C[i];
+    d.r = P.r[i];
+  }
+  for (const LrGroup& g : P.groups) {
+    float** arr = (float**)(blob.data() + g.ptr_off);
+    const size_t n = g.mats.size();
+    for (size_t t = 0; t < n; ++t) {
+      const LrDesc& d = descs[g.mats[t]];
+      float* const v[LP_N] = {d.M, d.Q, d.X, d.Y, d.W, d.W2, d.S, d.Linv, d.D};
+      for (int k = 0; k < LP_N; ++k) arr[k * n + t] = v[k];
+    }
+  }
+  int rc = upload(blob.data(), P.upload_bytes, ws, stream);
+  if (rc != DION_OK) return rc;
+  rocblas_handle h;
+  if ((rc = blas_handle(stream, ws + P.off_blas, h)) != DION_OK) return rc;
+  const LrDesc* d_descs = (const LrDesc*)(ws + P.off_descs);
+  auto arrays = [&](const LrGroup& g, int k) { return (float* const*)(ws + g.ptr_off) + k * g.mats.size(); };
+  const int nmat = batch;
+
+  launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, stream);
+  for (const LrGroup& g : P.groups)   // X = B Q
+    if ((rc = gemm_rm(h, false, false, g.R, g.r, g.C, 1.f, arrays(g, LP_M), arrays(g, LP_Q), 0.f,
+                      arrays(g, LP_X), (int)g.mats.size())) != DION_OK) return rc;
+  // CholeskyQR2 of F (rows x r) through tmp into dst
+  auto cholqr2 = [&](int F, int tmp, int dst, bool rows_are_R) -> int {
+    int src = F;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int to = pass == 0 ? tmp : dst;
+      for (const LrGroup& g : P.groups) {
+        const int rows = rows_are_R ? g.R : g.C;
+        int e = gemm_rm(h, true, false, g.r, g.r, rows, 1.f, arrays(g, src), arrays(g, src), 0.f,
+                        arrays(g, LP_S), (int)g.mats.size());
+        if (e != DION_OK) return e;
+      }
+      launch_lr_cholinv(d_descs, nmat, stream);
+      for (const LrGroup& g : P.groups) {
+        const int rows = rows_are_R ? g.R : g.C;
+        int e = gemm_rm(h, false, true, rows, g.r, g.r, 1.f, arrays(g, src), arrays(g, LP_L), 0.f,
+                        arrays(g, to), (int)g.mats.size());
+        if (e != DION_OK) return e;
+      }
+      src = to;
+    }
+    return DION_OK;
+  };
+  if ((rc = cholqr2(LP_X, LP_Y, LP_X, true)) != DION_OK) return rc;   // P
+  for (const LrGroup& g : P.groups)   // W = B^T P
+    if ((rc = gemm_rm(h, true, false, g.C, g.r, g.R, 1.f, arrays(g, LP_M), arrays(g, LP_X), 0.f,
+                      arrays(g, LP_W), (int)g.mats.size())) != DION_OK) return rc;
+  for (const LrGroup& g : P.groups)   // M = B - beta P W^T
+    if ((rc = gemm_rm(h, false, true, g.R, g.C, g.r, -beta, arrays(g, LP_X), arrays(g, LP_W), 1.f,
+                      arrays(g, LP_M), (int)g.mats.size())) != DION_OK) return rc;
+  if (mode == DION_LOWRANK_QR) {
+    if ((rc = cholqr2(LP_W, LP_W2, LP_Q, false)) != DION_OK) return rc;
+  } else {
+    launch_lr_colnorm(d_descs, nmat, stream);
+  }
+  for (const LrGroup& g : P.groups)   // D = P Q^T
+    if ((rc = gemm_rm(h, false, true, g.R, g.C, g.r, 1.f, arrays(g, LP_X), arrays(g, LP_Q), 0.f,
+                      arrays(g, LP_D), (int)g.mats.size())) != DION_OK) return rc;
+  if (!P.out_fp32) launch_lr_cast(d_descs, nmat, P.blocks, out_dtype, stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail("kernel launch", e);
+  return DION_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1554,6 +1770,33 @@ const char* dion_strerror(int status) {
 }
 
 const char* dion_last_error(void) { return g_last_error.c_str(); }
+
+size_t dion_lowrank_workspace_size(const dion_shape* shapes, int32_t batch, int32_t rank, int32_t out_dtype) {
+  LrPlan P;
+  if (build_lr_plan(shapes, batch, rank, out_dtype, P) != DION_OK) return 0;
+  return P.total;
+}
+
+int dion_lowrank_step(float* const* M, const void* const* grad, float* const* Q, void* const* out,
+                      const dion_shape* shapes, int32_t batch, int32_t grad_dtype, int32_t out_dtype, int32_t rank,
+                      float beta, int32_t mode, void* workspace, size_t workspace_bytes, void* stream) {
+  LrPlan P;
+  int rc = build_lr_plan(shapes, batch, rank, out_dtype, P);
+  if (rc != DION_OK) return rc;
+  if (!M || !grad || !Q || !out) return fail(DION_E_INVAL, "M, grad, Q and out must be non-NULL");
+  if (!valid_dtype(grad_dtype)) return fail(DION_E_INVAL, "unknown gradient dtype");
+  if (mode != DION_LOWRANK_QR && mode != DION_LOWRANK_COLNORM) return fail(DION_E_INVAL, "unknown mode");
+  if (!std::isfinite(beta)) return fail(DION_E_INVAL, "beta must be finite");
+  const size_t oes = dtype_bytes(out_dtype);
+  for (int i = 0; i < batch; ++i) {
+    if (!M[i] || !grad[i] || !Q[i] || !out[i]) return fail(DION_E_INVAL, "NULL matrix pointer");
+    const size_t n = (size_t)P.R[i] * P.C[i];
+    if (overlaps(out[i], n * oes, M[i], n * 4)) return fail(DION_E_INVAL, "out must not overlap M");
+    if (overlaps(Q[i], (size_t)P.C[i] * P.r[i] * 4, M[i], n * 4)) return fail(DION_E_INVAL, "Q must not overlap M");
+  }
+  return run_lr(P, M, grad, Q, out, batch, grad_dtype, out_dtype, beta, mode, workspace, workspace_bytes,
+                (hipStream_t)stream);
+}
 
 int dion_version(void) { return 100; }
 

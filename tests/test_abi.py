@@ -169,3 +169,31 @@ def test_restart_threshold_flops_and_validation():
             dion.restart_points(n_iter=5, restart_threshold=bad)
         with pytest.raises(dion.DionError):
             dion.workspace_size(shapes, restart_threshold=bad)
+
+
+def test_lowrank_validation_errors_before_launch():
+    """The low-rank entry point rejects bad arguments on the host (fake device pointers, no device work)."""
+    shp = (_lib.DionShape * 2)()
+    shp[0].rows, shp[0].cols, shp[1].rows, shp[1].cols = 64, 32, 32, 64
+    def ptrs(*v):
+        return (ctypes.c_void_p * 2)(*v)
+    M, G, Q, O = ptrs(0x10000, 0x20000), ptrs(0x30000, 0x40000), ptrs(0x50000, 0x60000), ptrs(0x70000, 0x80000)
+    need = dion.lowrank_workspace_size([(64, 32), (32, 64)], 8)
+    assert need > 0 and dion.lowrank_workspace_size([(64, 32), (32, 64)], 8, "fp32") < need
+
+    def call(M=M, G=G, Q=Q, O=O, rank=8, beta=1.0, mode=0, gdt=0, odt=0, ws=0x100000, nbytes=need, batch=2):
+        return _lib.lib.dion_lowrank_step(M, G, Q, O, shp, batch, gdt, odt, rank, beta, mode,
+                                          ctypes.c_void_p(ws), nbytes, None)
+    assert call(rank=0) == -1
+    assert call(rank=513) == -2
+    assert call(mode=2) == -1
+    assert call(gdt=7) == -1
+    assert call(odt=7) == -1
+    assert call(beta=float("nan")) == -1
+    assert call(batch=0) == -1
+    assert call(O=ptrs(0x10000, 0x80000)) == -1          # out overlaps M
+    assert call(Q=ptrs(0x10000 + 64, 0x60000)) == -1     # Q overlaps M
+    assert call(M=ptrs(0, 0x20000)) == -1                # NULL matrix
+    assert call(nbytes=need - 1) == -3                   # workspace too small
+    assert call(ws=0x100001) == -3                       # misaligned
+    assert call(ws=0) == -3
