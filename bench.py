@@ -26,6 +26,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA16_TFLOPS = 2516.6   # MI355X dense fp16 / bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_MFMA32_TFLOPS = 157.3    # MI355X dense fp32 matrix
+LOWRANK_RANK, LOWRANK_BETA = 256, 0.1
 
 
 def parse():
@@ -34,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b", choices=["llama3_8b", "gpt2_small", "llama3_70b",
-                                                                "llama3_8b_rows"])
+                                                                "llama3_8b_rows", "llama3_8b_lowrank"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--update", action="store_true",
                     help="row-subset workload only: fuse the weight update into the step (bf16 weights, "
@@ -177,6 +179,116 @@ def traffic_for(kernel):
     return None
 
 
+def cpu_baseline_lowrank(grads, Qs, seconds):
+    """The low-rank oracle on whole matrices of layer 0 (k, v, q, ...) until
+    about `seconds` of CPU work; params/s = sampled params / wall time."""
+    import numpy as np
+    from oracle import orthdion_oracle as L
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    done, params, t_total = [], 0, 0.0
+    for i in [1, 2, 0, 3, 4, 5, 6]:
+        G = grads[i].float().cpu().numpy()
+        M = np.zeros_like(G)
+        Q = Qs[i].cpu().numpy()
+        t0 = time.perf_counter()
+        L.lowrank_step(M, G, Q, LOWRANK_BETA, "qr")
+        t_total += time.perf_counter() - t0
+        params += G.shape[0] * G.shape[1]
+        done.append(f"{G.shape[0]}x{G.shape[1]}")
+        if t_total >= seconds:
+            break
+    return {"value": params / t_total, "unit": "params/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(done)} whole matrices of layer 0 ({', '.join(done)}; {params/1e6:.1f}M params), "
+                      f"one fp64 Orth-Dion step at rank {LOWRANK_RANK}, {t_total:.1f} s"}
+
+
+def bench_lowrank(args, torch, dion):
+    """One Orth-Dion step (rank 256, beta 0.1) over the Llama-3-8B layer set:
+    bf16 gradients of one step, fp32 buffers from zero, seeded Gaussian right
+    factors, bf16 updates."""
+    import workloads as W
+    dev = torch.device("cuda:0")
+    grads = W.llama3_8b_torch(step=1)
+    shapes = [tuple(g.shape) for g in grads]
+    Ms = [torch.zeros(s, dtype=torch.float32, device=dev) for s in shapes]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(21)
+    Qs = [torch.randn(c, min(LOWRANK_RANK, r, c), generator=gen, device=dev) for r, c in shapes]
+    Q0 = [Q.clone() for Q in Qs] if not args.no_cpu_baseline else None
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+    ws = torch.empty(dion.lowrank_workspace_size(shapes, LOWRANK_RANK) + 256, dtype=torch.uint8, device=dev)
+    call = lambda: dion.lowrank_step(Ms, grads, Qs, LOWRANK_BETA, mode="qr", outs=outs, workspace=ws)  # noqa: E731
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    dion.profile_enable(True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    recs = dion.profile_records()
+    dion.profile_enable(False)
+    ms_per_step = ms_total / args.steps
+    if args.profile:
+        print(json.dumps({"ms_per_step": ms_per_step}))
+        return
+    phases, kernels = {}, {}
+    for name, kern, ms, u, r, b in recs:
+        for key, tab in ((name, phases), (kern, kernels)):
+            e = tab.setdefault(key, {"ms": 0.0, "launches": 0, "useful": 0.0, "bytes": 0.0})
+            e["ms"] += ms
+            e["launches"] += 1
+            e["useful"] += u
+            e["bytes"] += b
+    dom = max((k for k, v in kernels.items() if v["useful"] > 0), key=lambda k: kernels[k]["ms"])
+    d = kernels[dom]
+    avg_ms = d["ms"] / d["launches"]
+    achieved = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
+    useful = sum(v["useful"] for v in phases.values()) / args.steps
+    params = sum(r * c for r, c in shapes)
+    line = {
+        "metric": f"low-rank Orth-Dion updated params/sec (rank {LOWRANK_RANK}), Llama-8B layer set",
+        "value": params * args.steps / (ms_total * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"llama3_8b_lowrank: {len(shapes)} matrices, {params/1e9:.3f} G params, "
+                               f"Orth-Dion (QR), rank {LOWRANK_RANK}, beta {LOWRANK_BETA}, bf16 gradients and update",
+                   "matrices": len(shapes), "params": params, "rank": LOWRANK_RANK},
+        "useful_tflops": useful / (ms_per_step * 1e-3) / 1e12,
+        "host_wall_s": wall,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_MFMA32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA32_TFLOPS, "traffic": None,
+                     "launch_ms": avg_ms, "useful_flops_per_launch": d["useful"] / d["launches"],
+                     "algorithmic_bytes_per_launch": d["bytes"] / d["launches"]},
+        "phases": {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
+                       "launches_per_step": p["launches"] // args.steps,
+                       **({"tflops": round(p["useful"] / (p["ms"] * 1e-3) / 1e12, 1)} if p["useful"] else
+                          {"gbs": round(p["bytes"] / (p["ms"] * 1e-3) / 1e9, 1)})}
+                   for n, p in sorted(phases.items(), key=lambda kv: -kv[1]["ms"])},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_lowrank(grads, Q0, args.cpu_sample_seconds)
+    print(json.dumps(line))
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -190,6 +302,10 @@ def main():
     import orthogonalized_optimizer_step_amd as dion
     from workloads import WORKLOADS
 
+    if args.workload == "llama3_8b_lowrank":
+        torch.cuda.init()
+        bench_lowrank(args, torch, dion)
+        return
     wl = WORKLOADS[args.workload]
     torch.cuda.init()
     dev = torch.device("cuda:0")

@@ -1436,10 +1436,47 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   auto arrays = [&](const LrGroup& g, int k) { return (float* const*)(ws + g.ptr_off) + k * g.mats.size(); };
   const int nmat = batch;
 
-  launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, stream);
+  // each launch (or batched rocBLAS call) as one profiling record, with its
+  // useful FLOPs (2 m n k per product) and algorithmic bytes
+  auto phase = [&](const char* name, const char* kernel, double useful, double bytes,
+                   const std::function<int()>& fn) -> int {
+    ProfRec rec{name, kernel, nullptr, nullptr, useful, useful, bytes};
+    if (g_prof.on) {
+      rec.a = g_prof.get();
+      rec.b = g_prof.get();
+      if (!rec.a || !rec.b || hipEventRecord(rec.a, stream) != hipSuccess)
+        return fail(DION_E_HIP, "profiling event failed");
+    }
+    const int e = fn();
+    if (e != DION_OK) return e;
+    if (g_prof.on) {
+      if (hipEventRecord(rec.b, stream) != hipSuccess) return fail(DION_E_HIP, "profiling event failed");
+      g_prof.recs.push_back(rec);
+    }
+    return DION_OK;
+  };
+  const char* kSgemm = "rocblas_sgemm_batched";
+  bool any_small = false, any_large = false;
+  for (int i = 0; i < batch; ++i) (P.r[i] <= LR_REG_RMAX ? any_small : any_large) = true;
+  double elems = 0.0;
+  for (int i = 0; i < batch; ++i) elems += (double)P.R[i] * P.C[i];
+  // product of one group: row-major C (m x n) = op(A) op(B) with inner dimension k
+  auto gprod = [&](const char* name, const LrGroup& g, bool ta, bool tb, int m, int n, int k, float alpha,
+                   int A, int B, float beta_, int Cm, double bytes_each) -> int {
+    const double cnt = (double)g.mats.size();
+    return phase(name, kSgemm, 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
+      return gemm_rm(h, ta, tb, m, n, k, alpha, arrays(g, A), arrays(g, B), beta_, arrays(g, Cm), (int)g.mats.size());
+    });
+  };
+
+  const double gsz = (double)dtype_bytes(grad_dtype);
+  if ((rc = phase("lr_accumulate", "dion::k_lr_accumulate", 0.0, elems * (8.0 + gsz), [&]() {
+         launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, stream);
+         return DION_OK;
+       })) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // X = B Q
-    if ((rc = gemm_rm(h, false, false, g.R, g.r, g.C, 1.f, arrays(g, LP_M), arrays(g, LP_Q), 0.f,
-                      arrays(g, LP_X), (int)g.mats.size())) != DION_OK) return rc;
+    if ((rc = gprod("lr_power", g, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, 0.f, LP_X,
+                    4.0 * ((double)g.R * g.C + (double)g.C * g.r + (double)g.R * g.r))) != DION_OK) return rc;
   // CholeskyQR2 of F (rows x r) through tmp into dst
   auto cholqr2 = [&](int F, int tmp, int dst, bool rows_are_R) -> int {
     int src = F;
@@ -1447,15 +1484,21 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
       const int to = pass == 0 ? tmp : dst;
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
-        int e = gemm_rm(h, true, false, g.r, g.r, rows, 1.f, arrays(g, src), arrays(g, src), 0.f,
-                        arrays(g, LP_S), (int)g.mats.size());
+        const int e = gprod("lr_orth", g, true, false, g.r, g.r, rows, 1.f, src, src, 0.f, LP_S,
+                            4.0 * ((double)rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
-      launch_lr_cholinv(d_descs, nmat, stream);
+      double rr = 0.0;
+      for (int i = 0; i < batch; ++i) rr += (double)P.r[i] * P.r[i];
+      int e = phase("lr_cholinv", "dion::k_lr_cholinv", 0.0, rr * 8.0, [&]() {
+        launch_lr_cholinv(d_descs, nmat, any_small, any_large, stream);
+        return DION_OK;
+      });
+      if (e != DION_OK) return e;
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
-        int e = gemm_rm(h, false, true, rows, g.r, g.r, 1.f, arrays(g, src), arrays(g, LP_L), 0.f,
-                        arrays(g, to), (int)g.mats.size());
+        e = gprod("lr_orth", g, false, true, rows, g.r, g.r, 1.f, src, LP_L, 0.f, to,
+                  4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
       src = to;
@@ -1464,20 +1507,29 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   };
   if ((rc = cholqr2(LP_X, LP_Y, LP_X, true)) != DION_OK) return rc;   // P
   for (const LrGroup& g : P.groups)   // W = B^T P
-    if ((rc = gemm_rm(h, true, false, g.C, g.r, g.R, 1.f, arrays(g, LP_M), arrays(g, LP_X), 0.f,
-                      arrays(g, LP_W), (int)g.mats.size())) != DION_OK) return rc;
+    if ((rc = gprod("lr_right", g, true, false, g.C, g.r, g.R, 1.f, LP_M, LP_X, 0.f, LP_W,
+                    4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // M = B - beta P W^T
-    if ((rc = gemm_rm(h, false, true, g.R, g.C, g.r, -beta, arrays(g, LP_X), arrays(g, LP_W), 1.f,
-                      arrays(g, LP_M), (int)g.mats.size())) != DION_OK) return rc;
+    if ((rc = gprod("lr_feedback", g, false, true, g.R, g.C, g.r, -beta, LP_X, LP_W, 1.f, LP_M,
+                    4.0 * (2.0 * g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   if (mode == DION_LOWRANK_QR) {
     if ((rc = cholqr2(LP_W, LP_W2, LP_Q, false)) != DION_OK) return rc;
   } else {
-    launch_lr_colnorm(d_descs, nmat, stream);
+    double cr = 0.0;
+    for (int i = 0; i < batch; ++i) cr += (double)P.C[i] * P.r[i];
+    if ((rc = phase("lr_colnorm", "dion::k_lr_colnorm", 0.0, cr * 8.0, [&]() {
+           launch_lr_colnorm(d_descs, nmat, stream);
+           return DION_OK;
+         })) != DION_OK) return rc;
   }
   for (const LrGroup& g : P.groups)   // D = P Q^T
-    if ((rc = gemm_rm(h, false, true, g.R, g.C, g.r, 1.f, arrays(g, LP_X), arrays(g, LP_Q), 0.f,
-                      arrays(g, LP_D), (int)g.mats.size())) != DION_OK) return rc;
-  if (!P.out_fp32) launch_lr_cast(d_descs, nmat, P.blocks, out_dtype, stream);
+    if ((rc = gprod("lr_update", g, false, true, g.R, g.C, g.r, 1.f, LP_X, LP_Q, 0.f, LP_D,
+                    4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
+  if (!P.out_fp32)
+    if ((rc = phase("lr_cast", "dion::k_lr_cast", 0.0, elems * (4.0 + dtype_bytes(out_dtype)), [&]() {
+           launch_lr_cast(d_descs, nmat, P.blocks, out_dtype, stream);
+           return DION_OK;
+         })) != DION_OK) return rc;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);
   return DION_OK;

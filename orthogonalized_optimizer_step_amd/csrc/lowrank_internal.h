@@ -29,10 +29,12 @@ struct LrDesc {
 
 // element-wise launches: 256 threads x 8 elements per block
 constexpr int LR_BLOCK_ELEMS = 2048;
+// ranks up to this factor their Gram matrix in registers (k_lr_cholinv_reg)
+constexpr int LR_REG_RMAX = 256;
 
 void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, hipStream_t s);
 void launch_lr_cast(const LrDesc* d, int nmat, int64_t blocks, int out_fmt, hipStream_t s);
-void launch_lr_cholinv(const LrDesc* d, int nmat, hipStream_t s);
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, hipStream_t s);
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
 
 }  // namespace dion

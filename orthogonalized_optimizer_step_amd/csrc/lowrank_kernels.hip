@@ -74,9 +74,16 @@ __global__ __launch_bounds__(256) void k_lr_cast(const LrDesc* __restrict__ desc
   const float* D = d.D + e0;
   uint16_t* o = (uint16_t*)d.out + e0;
   const int n = e0 + 8 <= d.elems ? 8 : (int)(d.elems - e0);
+  float v[8];
+  if (n == 8 && ((uintptr_t)D & 15) == 0) {
+    *(float4*)&v[0] = *(const float4*)D;
+    *(float4*)&v[4] = *(const float4*)(D + 4);
+  } else {
+    for (int i = 0; i < n; ++i) v[i] = D[i];
+  }
   uint16_t h[8];
   for (int i = 0; i < n; ++i)
-    h[i] = fmt == 0 ? lr_bf16_rne(D[i]) : __builtin_bit_cast(uint16_t, (_Float16)D[i]);
+    h[i] = fmt == 0 ? lr_bf16_rne(v[i]) : __builtin_bit_cast(uint16_t, (_Float16)v[i]);
   if (n == 8 && ((uintptr_t)o & 15) == 0) {
     uint4 pk;
     pk.x = h[0] | ((uint32_t)h[1] << 16);
@@ -103,6 +110,7 @@ __global__ __launch_bounds__(256) void k_lr_cast(const LrDesc* __restrict__ desc
 __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs) {
   const LrDesc& d = descs[blockIdx.x];
   const int r = d.r;
+  if (r <= LR_REG_RMAX) return;   // k_lr_cholinv_reg
   const int tid = threadIdx.x;
   double* A = d.A64;
   __shared__ double rowj[512];
@@ -163,6 +171,103 @@ __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ d
   }
 }
 
+// The same factorization for r <= 256 with the lower triangle held in
+// registers: 1024 threads as a 32 x 32 grid, thread (ty, tx) owning the
+// entries (ty + 32 a, tx + 32 b), a >= b, of the 8 x 8 block-cyclic layout (36
+// fp64 registers; an entry's row and column follow from its slot, so nothing
+// else is stored).  Both steps are right-looking eliminations with the pivot
+// column (and, for the inverse, the finished row) broadcast through LDS:
+//   Cholesky, step k: L[k][k] = sqrt(A[k][k]); L[i][k] = A[i][k] / L[k][k];
+//     A[i][c] -= L[i][k] L[c][k] for k < c <= i;
+//   inverse of L X = I, step k: row k of X divided by L[k][k], then
+//     X[i][c] -= L[i][k] X[k][c] for i > k, c <= k.
+// L leaves the registers for the fp64 scratch (column-major, so that a
+// column is one contiguous read) before the inverse reuses them.
+constexpr int LR_REG_THREADS = 1024;
+constexpr int LR_GRID = 32;
+constexpr int LR_NB = LR_REG_RMAX / LR_GRID;
+constexpr int LR_SLOTS = LR_NB * (LR_NB + 1) / 2;
+static_assert(LR_GRID * LR_GRID == LR_REG_THREADS, "thread grid");
+
+__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs) {
+  const LrDesc& d = descs[blockIdx.x];
+  const int r = d.r;
+  if (r > LR_REG_RMAX) return;    // k_lr_cholinv
+  const int tid = threadIdx.x;
+  const int ty = tid / LR_GRID, tx = tid % LR_GRID;
+  __shared__ double col[LR_REG_RMAX];
+  __shared__ double rowx[LR_REG_RMAX];
+  __shared__ double diag[LR_REG_RMAX];
+  __shared__ double red[LR_REG_THREADS / 64];
+  __shared__ double s_piv;
+  double v[LR_SLOTS];
+  // slot of (a, b), a >= b: a (a + 1) / 2 + b
+#define LR_FOR_SLOTS(BODY)                                            \
+  _Pragma("unroll") for (int a = 0; a < LR_NB; ++a)                   \
+  _Pragma("unroll") for (int b = 0; b <= a; ++b) {                    \
+    const int sl = a * (a + 1) / 2 + b;                               \
+    const int i = ty + LR_GRID * a, c = tx + LR_GRID * b;             \
+    const bool own = i < r && (a > b || ty >= tx);                    \
+    (void)sl; (void)own;                                              \
+    BODY                                                              \
+  }
+  double mx = 0.0;
+  LR_FOR_SLOTS({
+    v[sl] = own ? (double)d.S[(size_t)i * r + c] : 0.0;
+    if (own && i == c) mx = fmax(mx, v[sl]);
+  })
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  double big = 0.0;
+  for (int w = 0; w < LR_REG_THREADS / 64; ++w) big = fmax(big, red[w]);
+  const double tiny = 1e-14 * big;
+
+  for (int k = 0; k < r; ++k) {
+    LR_FOR_SLOTS({ if (own && i == k && c == k) s_piv = v[sl]; })
+    __syncthreads();
+    const double piv = s_piv;
+    const double dk = piv > tiny ? sqrt(piv) : 0.0;
+    const double inv = dk > 0.0 ? 1.0 / dk : 0.0;
+    LR_FOR_SLOTS({
+      if (own && c == k) {
+        const double x = i == k ? dk : v[sl] * inv;
+        v[sl] = x;
+        col[i] = x;
+      }
+    })
+    if (tid == 0) diag[k] = dk;
+    __syncthreads();
+    LR_FOR_SLOTS({ if (own && c > k) v[sl] -= col[i] * col[c]; })
+  }
+  // L (column-major) to the scratch; X = I in the registers
+  double* Lc = d.A64;
+  LR_FOR_SLOTS({
+    if (own) Lc[(size_t)c * r + i] = v[sl];
+    v[sl] = (own && i == c) ? 1.0 : 0.0;
+  })
+  __syncthreads();
+  for (int k = 0; k < r; ++k) {
+    for (int i = k + 1 + tid; i < r; i += LR_REG_THREADS) col[i] = Lc[(size_t)k * r + i];
+    const double dinv = diag[k] > 0.0 ? 1.0 / diag[k] : 0.0;
+    LR_FOR_SLOTS({
+      if (own && i == k) {
+        v[sl] *= dinv;
+        rowx[c] = v[sl];
+      }
+    })
+    __syncthreads();
+    LR_FOR_SLOTS({ if (own && i > k && c <= k) v[sl] -= col[i] * rowx[c]; })
+    __syncthreads();
+  }
+  for (int e = tid; e < r * r; e += LR_REG_THREADS) {
+    const int i = e / r, c = e - (e / r) * r;
+    if (c > i) d.Linv[e] = 0.f;
+  }
+  LR_FOR_SLOTS({ if (own) d.Linv[(size_t)i * r + c] = (float)v[sl]; })
+#undef LR_FOR_SLOTS
+}
+
 // One block per matrix: Q[:, j] = W[:, j] / ||W[:, j]|| (fp64 norm), zero
 // columns stay zero (Dion's column normalization).
 __global__ __launch_bounds__(256) void k_lr_colnorm(const LrDesc* __restrict__ descs) {
@@ -185,8 +290,9 @@ void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fm
 void launch_lr_cast(const LrDesc* d, int nmat, int64_t blocks, int out_fmt, hipStream_t s) {
   if (blocks > 0) hipLaunchKernelGGL(k_lr_cast, dim3((unsigned)blocks), dim3(256), 0, s, d, nmat, out_fmt);
 }
-void launch_lr_cholinv(const LrDesc* d, int nmat, hipStream_t s) {
-  if (nmat > 0) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d);
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, hipStream_t s) {
+  if (nmat > 0 && any_small) hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d);
+  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d);
 }
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s) {
   if (nmat > 0) hipLaunchKernelGGL(k_lr_colnorm, dim3(nmat), dim3(256), 0, s, d);

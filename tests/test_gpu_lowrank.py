@@ -164,3 +164,17 @@ def test_lowrank_zero_input_is_finite(dion):
     torch.cuda.synchronize()
     for o, M in zip(outs, dM):
         assert torch.isfinite(o).all() and torch.isfinite(M).all()
+
+
+@pytest.mark.parametrize("mode", ["qr", "colnorm"])
+def test_lowrank_rank_above_256(dion, mode):
+    """Ranks 257..512 factor the Gram matrix with the general (scratch-memory) kernel."""
+    shapes = [(700, 400), (400, 700), (520, 520)]
+    Ms, Gs, Qs = make(shapes, 300, 18)
+    dM, dQ, outs = run(dion, Ms, Gs, Qs, 1.0, mode)
+    for i, s in enumerate(shapes):
+        G = Gs[i].float().numpy()
+        M_ref, Q_ref, _, D_ref = L.lowrank_step(Ms[i], G, Qs[i], 1.0, mode)
+        e = (buf_err(as64(dM[i]), M_ref, Ms[i], G), rel_frobenius(as64(dQ[i]), Q_ref),
+             rel_frobenius(as64(outs[i]), D_ref))
+        assert max(e) <= TOL, (s, e)
