@@ -23,6 +23,7 @@ SOURCES = [
     ("gemm_kernels.hip", []),
     ("stream_kernels.hip", ["-ffp-contract=off"]),
     ("lowrank_kernels.hip", ["-ffp-contract=off"]),
+    ("tiny_kernels.hip", []),
     ("dion_api.cpp", []),
 ]
 

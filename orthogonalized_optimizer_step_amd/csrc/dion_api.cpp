@@ -45,6 +45,10 @@ void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t r
 void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total, int slot,
                    const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
+void launch_tiny_gns(const MatDesc* descs, int nmat, const MatScalars* scalars, const int* idx, const double* coef,
+                     int K, unsigned long long restarts, int fmt, hipStream_t s);
+// matrices with Gram side m <= 64 and long side n <= 1024 run in one launch
+constexpr int kTinyM = 64, kTinyN = 1024;
 }  // namespace dion
 
 using namespace dion;
@@ -162,7 +166,7 @@ float pow2_scale(double bound) {  // largest 2^j with bound * 2^j <= 2^15
 
 // ------------------------------------------------------------ the plan
 enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY, ST_UNPACK, ST_COMBINE,
-                ST_UPDATE };
+                ST_UPDATE, ST_TINY };
 
 struct Step {
   StepKind kind;
@@ -206,6 +210,12 @@ struct Plan {
   int64_t x_rows = 0, x_sel = 0;
   bool host_scalars = false;
   std::vector<MatScalars> hscal;
+  // every matrix small: the whole iteration in one launch (k_tiny_gns), with
+  // the per-iteration coefficients (fp64, as int pairs) at ints[coef_off]
+  bool tiny = false;
+  size_t coef_off = 0;
+  unsigned long long restarts = 0;
+  int K = 0;
   // fused weight update (row-subset step): out is the weight W
   bool update = false, w_bf16 = true;
   float keep = 1.f;
@@ -386,6 +396,22 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   }
   const int t_pack = add_table(P, all, pack_c);
   const int t_tr = add_table(P, all, tr_c);
+  P.K = K;
+  P.tiny = !step_mode && K <= 64;
+  for (const MatPlan& mp : P.mats) P.tiny = P.tiny && mp.m <= kTinyM && mp.n <= kTinyN;
+  if (P.tiny) {
+    if (P.ints.size() & 1) P.ints.push_back(0);   // 8-byte alignment of the fp64 table
+    P.coef_off = P.ints.size();
+    for (int k = 0; k < K; ++k)
+      for (double v : {prm.a[k], prm.b[k], prm.c[k]}) {
+        int w[2];
+        std::memcpy(w, &v, sizeof v);
+        P.ints.push_back(w[0]);
+        P.ints.push_back(w[1]);
+      }
+    for (int k = 1; k < K; ++k)
+      if (prm.restart[k - 1]) P.restarts |= 1ull << (k - 1);
+  }
   // uploaded part: descriptors, tables, tile ranges; then device-written scratch
   P.off_ints = off;
   off = align256(off + sizeof(int) * P.ints.size());
@@ -434,6 +460,33 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   st.name = "select";
   st.bytes = rows * 8 * (P.use_idx ? 10 : 1) + rows;
   P.steps.push_back(st);
+  if (P.tiny) {
+    // useful FLOPs per segment of length L: n m (m + 1) + 2 m^2 n + (4L - 3) m^2 (m + 1)
+    st = Step();
+    st.kind = ST_TINY;
+    st.name = "tiny";
+    for (const MatPlan& mp : P.mats) {
+      const double m = mp.m, n = mp.n;
+      int k0 = 0;
+      for (int k = 1; k <= K; ++k)
+        if (k == K || prm.restart[k - 1]) {
+          const double L = k - k0;
+          st.useful += n * m * (m + 1) + 2.0 * m * m * n + (4.0 * L - 3.0) * m * m * (m + 1);
+          k0 = k;
+        }
+      st.bytes += 2.0 * mp.k * mp.C * in_es;
+    }
+    st.raw = st.useful;
+    P.steps.push_back(st);
+    if (P.use_idx) {
+      Step cp;
+      cp.kind = ST_COPY;
+      cp.name = "copy_rows";
+      cp.bytes = 2.0 * unsel_elems * in_es + rows;
+      P.steps.push_back(cp);
+    }
+    return DION_OK;
+  }
   st = Step();
   st.kind = ST_PACK;
   st.name = "pack";
@@ -1057,6 +1110,7 @@ const char* kernel_name(const Plan& P, const Step& st) {
     case ST_PACK: return P.fp64 ? "dion::k_pack" : "dion::k_pack16";
     case ST_TRANSPOSE: return "dion::k_transpose";
     case ST_COPY: return "dion::k_copy_unselected";
+    case ST_TINY: return "dion::k_tiny_gns";
     case ST_UNPACK: return "dion::k_unpack";
     case ST_COMBINE: return "dion::k_scale_combine";
     case ST_UPDATE: return P.w_bf16 ? "dion::k_update_unselected<unsigned short>" : "dion::k_update_unselected<float>";
@@ -1221,6 +1275,10 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         if (!ok) return fail(DION_E_UNSUPPORTED, "no GEMM kernel for this phase");
         break;
       }
+      case ST_TINY:
+        launch_tiny_gns(d_descs, batch, d_scal, P.use_idx ? d_idx : nullptr, (const double*)(d_ints + P.coef_off),
+                        P.K, P.restarts, fmt, stream);
+        break;
       case ST_COPY:
         launch_copy_unselected(fmt != 1, d_descs, batch, P.total_rows, d_flags, stream);
         break;

@@ -329,3 +329,45 @@ def test_batch_order_independence(dion, prec):
         outs = dion.orth_batched([Ms[i] for i in perm], **kw)
         for o, i in zip(outs, perm):
             assert torch.equal(o, base[i]), (prec, shapes[i], perm)
+
+
+TINY_SHAPES = [(64, 128), (128, 64), (1, 5), (5, 1), (40, 40), (64, 1024), (1024, 64), (3, 700), (63, 65)]
+TINY_TOL = {"fp32": 1e-6, "bf16": 2.0 ** -8, "fp16": 2.0 ** -10}
+
+
+@pytest.mark.parametrize("sched", [dict(), dict(restart_every=2), dict(restart_mask=0b10, safety=1.01),
+                                   dict(n_iter=6, restart_every=1), dict(restart_threshold=100.0)])
+@pytest.mark.parametrize("dt", ["fp32", "bf16", "fp16"])
+def test_tiny_batch_one_launch(dion, sched, dt):
+    """Every matrix with Gram side <= 64 and long side <= 1024: keys, selection and one fp64
+    launch for the whole iteration; the output carries only its own rounding."""
+    rng = np.random.default_rng(31)
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[dt]
+    dev = [torch.from_numpy(rng.standard_normal(s).astype(np.float32)).to(tdt).cuda() for s in TINY_SHAPES]
+    kw = {"n_iter": 5, **sched}
+    dion.profile_enable(True)
+    outs = dion.orth_batched(dev, **kw)
+    names = [r[0] for r in dion.profile_records()]
+    dion.profile_enable(False)
+    assert "tiny" in names and "syrk" not in names, names
+    for M, o, s in zip(dev, outs, TINY_SHAPES):
+        ref, _ = O.orthogonalize(M.float().cpu().numpy(), **kw)
+        err = O.rel_frobenius(to_np(o), ref)
+        assert err <= TINY_TOL[dt], (s, dt, err)
+
+
+@pytest.mark.parametrize("frac", [0.125, 0.25, 1.0 / 3])
+def test_tiny_row_subset(dion, frac):
+    """Row subsets on the one-launch path: indices as the oracle's, unselected rows copied exactly."""
+    rng = np.random.default_rng(32)
+    shapes = [(512, 64), (256, 300), (96, 8), (40, 1000)]
+    Ms = [round_bf16(rng.standard_normal(s).astype(np.float32)) for s in shapes]
+    outs, idxs = dion.orth_batched([to_dev_bf16(M) for M in Ms], row_frac=frac, restart_every=2,
+                                   return_indices=True)
+    for M, o, ix, s in zip(Ms, outs, idxs, shapes):
+        assert_selection(ix.cpu().numpy(), M, frac)
+        ref, idx = O.orthogonalize(M, row_frac=frac, restart_every=2)
+        on = to_np(o)
+        unsel = np.setdiff1d(np.arange(s[0]), idx)
+        assert np.array_equal(on[unsel], M[unsel].astype(np.float64)), s
+        assert O.rel_frobenius(on[idx], ref[idx]) <= 2.0 ** -8, s
