@@ -47,6 +47,11 @@ formula, selection criterion or worked example.  The readings taken here are:
       alpha U with U the step's output and alpha the learning rate times a
       per-matrix shape scale chosen by the caller; in fp32 arithmetic with one
       rounding per operation, then round-to-nearest-even for bf16 weights.
+  R14 Error feedback, "carry" alternative (ef="carry"): Dion's recurrence
+      with only the selected rows captured.  The buffer takes the gradient,
+      B = fl32(E + G); the update is the orthogonalized selected rows and
+      zero elsewhere; the buffer keeps fl32(beta * B) on the selected rows and
+      B unchanged on the others (carried undecayed).  The default remains R8.
   R12 Restart threshold tau (局限 names it as a hyperparameter; the same
       passage ties restarts to spurious negative eigenvalues of the
       intermediate matrices): in the smallest singular directions P is close
@@ -328,6 +333,7 @@ def rowsubset_step_update(Es, grads, Ws, beta: float, alphas, weight_decay: floa
     take the raw momentum through ``weight_update_f32`` (their update is an
     exact fp32 value, so their stored result is fixed bit for bit).
     """
+    ef = kw.get("ef", "raw")
     newE, outs, idxs = rowsubset_step(Es, grads, beta, **kw)
     newW = []
     for W, Mt, out, idx, alpha in zip(Ws, newE, outs, idxs, alphas):
@@ -335,22 +341,38 @@ def rowsubset_step_update(Es, grads, Ws, beta: float, alphas, weight_decay: floa
         keep = float(np.subtract(np.float32(1.0), np.float32(weight_decay), dtype=np.float32))
         res = W64 * keep - float(np.float32(alpha)) * out
         rest = np.setdiff1d(np.arange(W64.shape[0]), idx)
-        res[rest] = weight_update_f32(np.asarray(W)[rest], Mt[rest], alpha, weight_decay, bf16)
+        # unselected rows: the raw momentum (R8), or a zero update under "carry" (R14)
+        U = Mt[rest] if ef == "raw" else np.zeros_like(Mt[rest])
+        res[rest] = weight_update_f32(np.asarray(W)[rest], U, alpha, weight_decay, bf16)
         newW.append(res)
     return newE, newW, idxs
 
 
-def rowsubset_step(Es, grads, beta: float, **kw):
+def rowsubset_step(Es, grads, beta: float, ef: str = "raw", **kw):
     """One step of the row-subset rule over a batch.
 
-    Returns (new E list (fp32), out list (fp64), idx list).  E_t = M_t, and
-    the output is orthogonalize(M_t) with unselected rows = M_t (R8).
+    Returns (new E list (fp32), out list (fp64), idx list).
+    ef="raw" (R8): E_t = M_t = fl32(fl32(beta E) + G), and the output is
+    orthogonalize(M_t) with unselected rows = M_t.
+    ef="carry" (R14): B = fl32(E + G); the output is orthogonalize(B) with
+    unselected rows zero; E_t = fl32(beta B) on the selected rows, B elsewhere.
     """
+    if ef not in ("raw", "carry"):
+        raise ValueError("ef must be 'raw' or 'carry'")
     newE, outs, idxs = [], [], []
     for E, G in zip(Es, grads):
-        Mt = momentum_update(E, G, beta)
-        out, idx = orthogonalize(Mt, **kw)
-        newE.append(Mt)
+        if ef == "raw":
+            Mt = momentum_update(E, G, beta)
+            out, idx = orthogonalize(Mt, **kw)
+            newE.append(Mt)
+        else:
+            B = np.add(np.asarray(E, dtype=np.float32), np.asarray(G, dtype=np.float32), dtype=np.float32)
+            out, idx = orthogonalize(B, **kw)
+            rest = np.setdiff1d(np.arange(B.shape[0]), idx)
+            out[rest] = 0.0
+            Et = B.copy()
+            Et[idx] = np.multiply(np.float32(beta), B[idx], dtype=np.float32)
+            newE.append(Et)
         outs.append(out)
         idxs.append(idx)
     return newE, outs, idxs

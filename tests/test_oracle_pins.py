@@ -475,3 +475,57 @@ def test_rowsubset_step_update_structure():
                        atol=1e-15)
     rest = np.setdiff1d(np.arange(12), idx)
     assert np.array_equal(newW[0][rest], O.weight_update_f32(Ws[0][rest], newE[0][rest], 0.03, 0.01))
+
+
+def _carry_inputs(shape=(48, 20), steps=3, seed=5):
+    rng = np.random.default_rng(seed)
+    return [round_bf16(rng.standard_normal(shape).astype(np.float32)) for _ in range(steps)]
+
+
+def test_carry_equals_raw_at_full_rows():
+    """rho = 1: both readings run the same momentum sequence.  Carry's buffer is
+    fl32(beta M_t) where raw keeps M_t, and the next step forms fl32(fl32(beta M_t) + G)
+    either way, so the outputs agree bit for bit over several steps."""
+    Gs = _carry_inputs()
+    Er = [np.zeros(Gs[0].shape, np.float32)]
+    Ec = [np.zeros(Gs[0].shape, np.float32)]
+    for G in Gs:
+        Er, outr, _ = O.rowsubset_step(Er, [G], 0.95, row_frac=1.0, n_iter=5)
+        Ec, outc, _ = O.rowsubset_step(Ec, [G], 0.95, ef="carry", row_frac=1.0, n_iter=5)
+        assert np.array_equal(outr[0], outc[0])
+        assert np.array_equal(Ec[0], np.multiply(np.float32(0.95), Er[0], dtype=np.float32))
+
+
+def test_carry_with_beta_one_differs_only_in_unselected_output_rows():
+    """beta = 1: fl32(1 E) = E, so both buffers are fl32(E + G) and the selected
+    output rows agree; the unselected rows are the momentum (raw) or zero (carry)."""
+    Gs = _carry_inputs()
+    Er = [np.zeros(Gs[0].shape, np.float32)]
+    Ec = [np.zeros(Gs[0].shape, np.float32)]
+    for G in Gs:
+        Er, outr, idr = O.rowsubset_step(Er, [G], 1.0, row_frac=0.25, n_iter=5)
+        Ec, outc, idc = O.rowsubset_step(Ec, [G], 1.0, ef="carry", row_frac=0.25, n_iter=5)
+        assert np.array_equal(Er[0], Ec[0]) and np.array_equal(idr[0], idc[0])
+        rest = np.setdiff1d(np.arange(G.shape[0]), idr[0])
+        assert np.array_equal(outr[0][idr[0]], outc[0][idc[0]])
+        assert np.all(outc[0][rest] == 0.0) and np.array_equal(outr[0][rest], Er[0][rest].astype(np.float64))
+
+
+def test_carry_keeps_unselected_rows_undecayed():
+    """Carry: unselected buffer rows are B = fl32(E + G) exactly (scalar IEEE
+    emulation), selected rows fl32(beta B); the update's unselected rows are zero."""
+    rng = np.random.default_rng(6)
+    E = rng.standard_normal((30, 12)).astype(np.float32)
+    G = round_bf16(rng.standard_normal((30, 12)).astype(np.float32))
+    (Et,), (out,), (idx,) = O.rowsubset_step([E], [G], 0.9, ef="carry", row_frac=0.2, n_iter=3)
+    def f32(x):
+        return struct.unpack("f", struct.pack("f", x))[0]
+    B = np.array([[f32(float(a) + float(b)) for a, b in zip(r1, r2)] for r1, r2 in zip(E, G)], np.float32)
+    rest = np.setdiff1d(np.arange(30), idx)
+    assert np.array_equal(Et[rest].view(np.uint32), B[rest].view(np.uint32))
+    decayed = np.array([[f32(f32(0.9) * float(v)) for v in row] for row in B[idx]], np.float32)
+    assert np.array_equal(Et[idx].view(np.uint32), decayed.view(np.uint32))
+    assert np.all(out[rest] == 0.0)
+    assert np.array_equal(idx, O.select_rows(B, 0.2))
+    with pytest.raises(ValueError):
+        O.rowsubset_step([E], [G], 0.9, ef="dion")
