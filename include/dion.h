@@ -99,6 +99,12 @@ typedef struct {
  *   safety        s > 0
  *   row_frac      in (0, 1]
  *   precision     a dion_precision value
+ *   ef_carry      row-subset steps only: 0 = the buffer keeps the momentum and
+ *                 unselected rows apply it raw (the pages' "raw momentum
+ *                 update"); 1 = the carry form of error feedback: the buffer
+ *                 takes the gradient undecayed, B = fl32(E + G), only the
+ *                 selected (captured) rows decay to fl32(beta * B), and
+ *                 unselected rows contribute a zero update.  Ignored elsewhere.
  *   restart_threshold  tau >= 0 (0 = off); with no mask it overrides
  *                 restart_every: a restart follows the iteration at which the
  *                 product of (a_k / s)^2 since the last restart first reaches
@@ -119,6 +125,7 @@ typedef struct {
   float row_frac;
   int32_t precision;
   float restart_threshold;
+  int32_t ef_carry;
 } dion_ns_params;
 
 /* The iterations after which this parameter set restarts (host only, no

@@ -19,13 +19,18 @@ __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
 
-def _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold=0.0):
+EF = {"raw": 0, "carry": 1}
+
+
+def _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold=0.0,
+            ef="raw"):
     flat = [float(x) for trip in ([coeffs] if len(coeffs) == 3 and not hasattr(coeffs[0], "__len__")
                                   else coeffs) for x in trip]
     arr = (ctypes.c_float * len(flat))(*flat)
     p = DionParams(ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), len(flat) // 3, int(n_iter),
                    int(restart_every), int(restart_mask), float(safety), float(row_frac),
-                   PREC[precision] if isinstance(precision, str) else int(precision), float(restart_threshold))
+                   PREC[precision] if isinstance(precision, str) else int(precision), float(restart_threshold),
+                   EF[ef] if isinstance(ef, str) else int(ef))
     return p, arr
 
 
@@ -106,13 +111,14 @@ class Orthogonalizer:
     its own workspace, so repeated calls only marshal pointers."""
 
     def __init__(self, shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                 safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False, restart_threshold=0.0):
+                 safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False, restart_threshold=0.0,
+                 ef="raw"):
         import torch
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.dtype = dtype
         self.step_mode = step_mode
         self._p, self._keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision,
-                                      restart_threshold)
+                                      restart_threshold, ef)
         self._shp = _shapes(self.shapes)
         code = DION_FP32 if step_mode else {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
         self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
@@ -178,14 +184,19 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
 
 
 def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                   safety=1.0, row_frac=0.125, return_indices=False, stream=None, restart_threshold=0.0):
-    """One row-subset step: E <- fl32(fl32(beta E) + grad) in place; returns bf16 outputs."""
+                   safety=1.0, row_frac=0.125, return_indices=False, stream=None, restart_threshold=0.0, ef="raw"):
+    """One row-subset step; returns bf16 outputs.
+
+    ef="raw": E <- fl32(fl32(beta E) + grad) in place, unselected output rows are E.
+    ef="carry": E <- fl32(E + grad), then the selected rows of E decay to fl32(beta E)
+    and the unselected output rows are zero (the carry form of error feedback).
+    """
     import torch
     _check_tensors(Es, torch.float32)
     _check_tensors(grads, grads[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
-                          restart_threshold=restart_threshold)
+                          restart_threshold=restart_threshold, ef=ef)
     if outs is None:
         outs = [torch.empty(E.shape, dtype=torch.bfloat16, device=E.device) for E in Es]
     _check_tensors(outs, torch.bfloat16)
@@ -277,7 +288,7 @@ def apply(Qs, Xs, precision="auto", stream=None):
 
 def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=QUINTIC, n_iter=5,
                           restart_every=0, restart_mask=0, safety=1.0, row_frac=0.125, return_indices=False,
-                          stream=None, restart_threshold=0.0):
+                          stream=None, restart_threshold=0.0, ef="raw"):
     """One row-subset step fused with the weight update; E and W are updated in place."""
     import torch
     _check_tensors(Es, torch.float32)
@@ -285,7 +296,7 @@ def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=
     _check_tensors(Ws, Ws[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
-                          restart_threshold=restart_threshold)
+                          restart_threshold=restart_threshold, ef=ef)
     sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
     orth.step_update(Es, grads, Ws, beta, alphas, weight_decay, sel, stream)
     if not return_indices:

@@ -31,6 +31,7 @@ class DionParams(ctypes.Structure):
         ("row_frac", ctypes.c_float),
         ("precision", ctypes.c_int32),
         ("restart_threshold", ctypes.c_float),
+        ("ef_carry", ctypes.c_int32),
     ]
 
 

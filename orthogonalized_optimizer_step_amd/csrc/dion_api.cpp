@@ -31,9 +31,11 @@ bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& 
 bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream);
 void launch_rowkeys(int fmt, const MatDesc* descs, int nmat, int64_t rows, double* keys, hipStream_t s);
 void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
-                          double* keys, bool write_out, hipStream_t s);
+                          double* keys, int write_out, hipStream_t s);
 void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
-                              float keep, hipStream_t s);
+                              float keep, bool raw, hipStream_t s);
+void launch_decay_selected(const MatDesc* descs, int nmat, int64_t total_sel, const int* idx, float beta,
+                           hipStream_t s);
 void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,
                    MatScalars* scalars, bool fp64_path, hipStream_t s);
 void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
@@ -71,6 +73,7 @@ struct Params {
   std::vector<int> restart;     // restart[k-1] = 1: restart after iteration k
   double row_frac;
   bool fp64;
+  bool carry;   // row-subset step: the carry form of error feedback
 };
 
 bool valid_dtype(int dtype) { return dtype == DION_BF16 || dtype == DION_FP32 || dtype == DION_FP16; }
@@ -120,6 +123,8 @@ int parse_params(const dion_ns_params* p, int dtype, bool step_mode, Params& out
     }
     out.restart[k - 1] = r ? 1 : 0;
   }
+  if (p->ef_carry != 0 && p->ef_carry != 1) return fail(DION_E_INVAL, "ef_carry must be 0 or 1");
+  out.carry = p->ef_carry == 1;
   out.row_frac = p->row_frac;
   out.fp64 = p->precision == DION_PREC_FP64 || (p->precision == DION_PREC_AUTO && dtype == DION_FP32 && !step_mode);
   return DION_OK;
@@ -166,7 +171,7 @@ float pow2_scale(double bound) {  // largest 2^j with bound * 2^j <= 2^15
 
 // ------------------------------------------------------------ the plan
 enum StepKind { ST_KEYS, ST_MOMENTUM, ST_SELECT, ST_PACK, ST_GEMM, ST_TRANSPOSE, ST_COPY, ST_UNPACK, ST_COMBINE,
-                ST_UPDATE, ST_TINY };
+                ST_UPDATE, ST_TINY, ST_DECAY };
 
 struct Step {
   StepKind kind;
@@ -216,6 +221,8 @@ struct Plan {
   size_t coef_off = 0;
   unsigned long long restarts = 0;
   int K = 0;
+  // row-subset step with the carry form of error feedback
+  bool carry = false;
   // fused weight update (row-subset step): out is the weight W
   bool update = false, w_bf16 = true;
   float keep = 1.f;
@@ -493,6 +500,14 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   st.table = t_pack;
   st.bytes = sel_elems * in_es + pad_elems * es * (1 + P.xterms0);
   P.steps.push_back(st);
+  P.carry = step_mode && prm.carry;
+  if (P.carry) {   // the captured rows of the buffer decay once packed
+    st = Step();
+    st.kind = ST_DECAY;
+    st.name = "decay_rows";
+    st.bytes = 8.0 * sel_elems;
+    P.steps.push_back(st);
+  }
 
   // per-matrix useful FLOPs of a product kind; executed MFMA FLOPs from the tile table
   // out_lo: whether any later product or epilogue reads the lo term of this
@@ -1111,6 +1126,7 @@ const char* kernel_name(const Plan& P, const Step& st) {
     case ST_TRANSPOSE: return "dion::k_transpose";
     case ST_COPY: return "dion::k_copy_unselected";
     case ST_TINY: return "dion::k_tiny_gns";
+    case ST_DECAY: return "dion::k_decay_selected";
     case ST_UNPACK: return "dion::k_unpack";
     case ST_COMBINE: return "dion::k_scale_combine";
     case ST_UPDATE: return P.w_bf16 ? "dion::k_update_unselected<unsigned short>" : "dion::k_update_unselected<float>";
@@ -1247,7 +1263,8 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         launch_rowkeys(s_fmt, sd, sn, srows, skeys, stream);
         break;
       case ST_MOMENTUM:
-        launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, beta, d_keys, !P.update, stream);
+        launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, P.carry ? 1.0f : beta, d_keys,
+                             P.update ? 0 : (P.carry ? 2 : 1), stream);
         break;
       case ST_SELECT:
         launch_select(sd, sn, skeys, sflags, sidx, ss, P.fp64, stream);
@@ -1275,6 +1292,9 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         if (!ok) return fail(DION_E_UNSUPPORTED, "no GEMM kernel for this phase");
         break;
       }
+      case ST_DECAY:
+        launch_decay_selected(d_descs, batch, P.total_sel, P.use_idx ? d_idx : nullptr, beta, stream);
+        break;
       case ST_TINY:
         launch_tiny_gns(d_descs, batch, d_scal, P.use_idx ? d_idx : nullptr, (const double*)(d_ints + P.coef_off),
                         P.K, P.restarts, fmt, stream);
@@ -1292,7 +1312,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         launch_scale_combine(d_scal, batch, stream);
         break;
       case ST_UPDATE:
-        launch_update_unselected(P.w_bf16, d_descs, batch, P.total_rows, d_flags, P.keep, stream);
+        launch_update_unselected(P.w_bf16, d_descs, batch, P.total_rows, d_flags, P.keep, !P.carry, stream);
         break;
     }
     if (g_prof.on) {

@@ -97,9 +97,11 @@ __global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ des
 }
 
 // ---------------------------------------------- momentum / error feedback
-// E <- fl32(fl32(beta * E) + grad), out <- bf16(E) (unless out is the weight
-// of the fused update), key <- sum E^2 (fp64).  __fmul_rn / __fadd_rn keep the
-// two roundings separate (no contraction).
+// E <- fl32(fl32(beta * E) + grad), key <- sum E^2 (fp64), and out <- bf16(E)
+// (write_out 1), out <- 0 (write_out 2: the carry form of error feedback,
+// where unselected rows contribute no update) or nothing (write_out 0: out is
+// the weight of the fused update).  __fmul_rn / __fadd_rn keep the two
+// roundings separate (no contraction); beta = 1 gives fl32(E + grad).
 template <typename GT>
 __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict__ descs, int nmat,
                                                        int64_t total_rows, float beta,
@@ -129,11 +131,13 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
       float m[4] = {__fadd_rn(__fmul_rn(beta, e.x), gv[0]), __fadd_rn(__fmul_rn(beta, e.y), gv[1]),
                     __fadd_rn(__fmul_rn(beta, e.z), gv[2]), __fadd_rn(__fmul_rn(beta, e.w), gv[3])};
       *(float4*)(E + c) = make_float4(m[0], m[1], m[2], m[3]);
-      if (write_out) {
+      if (write_out == 1) {
         uint2 o;
         o.x = (uint32_t)bf16_rne(m[0]) | ((uint32_t)bf16_rne(m[1]) << 16);
         o.y = (uint32_t)bf16_rne(m[2]) | ((uint32_t)bf16_rne(m[3]) << 16);
         *(uint2*)(out + c) = o;
+      } else if (write_out == 2) {
+        *(uint2*)(out + c) = make_uint2(0u, 0u);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) s += (double)m[q] * (double)m[q];
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
                                        : ((const float*)d.grad)[r * d.C + c];
       const float m = __fadd_rn(__fmul_rn(beta, E[c]), gv);
       E[c] = m;
-      if (write_out) out[c] = bf16_rne(m);
+      if (write_out) out[c] = write_out == 1 ? bf16_rne(m) : (uint16_t)0;
       s += (double)m * (double)m;
     }
   }
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(256) void k_copy_unselected(const MatDesc* __restri
 template <typename WT>
 __global__ __launch_bounds__(256) void k_update_unselected(const MatDesc* __restrict__ descs, int nmat,
                                                            int64_t total_rows, const uint8_t* __restrict__ flags,
-                                                           float keep) {
+                                                           float keep, int raw) {
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (g >= total_rows || flags[g]) return;
@@ -516,7 +520,8 @@ __global__ __launch_bounds__(256) void k_update_unselected(const MatDesc* __rest
         wv[0] = b.x; wv[1] = b.y; wv[2] = b.z; wv[3] = b.w;
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wv[q] = __fsub_rn(__fmul_rn(wv[q], keep), __fmul_rn(al, ev[q]));
+      for (int q = 0; q < 4; ++q)
+        wv[q] = raw ? __fsub_rn(__fmul_rn(wv[q], keep), __fmul_rn(al, ev[q])) : __fmul_rn(wv[q], keep);
       if (sizeof(WT) == 2) {
         uint2 o;
         o.x = (uint32_t)bf16_rne(wv[0]) | ((uint32_t)bf16_rne(wv[1]) << 16);
@@ -529,10 +534,39 @@ __global__ __launch_bounds__(256) void k_update_unselected(const MatDesc* __rest
   } else {
     for (int c = lane; c < d.C; c += 64) {
       const float w = sizeof(WT) == 2 ? bf16_to_f32(((const uint16_t*)W)[c]) : ((const float*)W)[c];
-      const float v = __fsub_rn(__fmul_rn(w, keep), __fmul_rn(al, E[c]));
+      const float v = raw ? __fsub_rn(__fmul_rn(w, keep), __fmul_rn(al, E[c])) : __fmul_rn(w, keep);
       if (sizeof(WT) == 2) ((uint16_t*)W)[c] = bf16_rne(v);
       else ((float*)W)[c] = v;
     }
+  }
+}
+
+// ---------------------------------------- carry: decay of captured rows
+// Error feedback in the carry form: after the selected rows of the buffer
+// have been packed for orthogonalization, they keep fl32(beta * B); the other
+// rows are carried as they are.  One wave per selected row (idx NULL: every
+// row is selected).
+__global__ __launch_bounds__(256) void k_decay_selected(const MatDesc* __restrict__ descs, int nmat,
+                                                        int64_t total_sel, const int* __restrict__ idx,
+                                                        float beta) {
+  const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (s >= total_sel) return;
+  int lo = 0, hi = nmat;   // descs[lo].sel0 <= s < descs[hi].sel0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (descs[mid].sel0 <= s) lo = mid; else hi = mid;
+  }
+  const MatDesc& d = descs[lo];
+  float* E = (float*)d.M + (idx ? (int64_t)idx[s] : s - d.sel0) * d.C;   // rho = 1: every row
+  if ((d.C & 3) == 0) {
+    for (int c = lane * 4; c < d.C; c += 256) {
+      float4 e = *(float4*)(E + c);
+      e.x = __fmul_rn(beta, e.x); e.y = __fmul_rn(beta, e.y); e.z = __fmul_rn(beta, e.z); e.w = __fmul_rn(beta, e.w);
+      *(float4*)(E + c) = e;
+    }
+  } else {
+    for (int c = lane; c < d.C; c += 64) E[c] = __fmul_rn(beta, E[c]);
   }
 }
 
@@ -598,16 +632,23 @@ void launch_rowkeys(int fmt, const MatDesc* descs, int nmat, int64_t rows, doubl
 }
 
 void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
-                          double* keys, bool write_out, hipStream_t s) {
-  const int wo = write_out ? 1 : 0;
+                          double* keys, int write_out, hipStream_t s) {
+  const int wo = write_out;
   if (grad_bf16) hipLaunchKernelGGL(k_momentum_keys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, wo);
   else hipLaunchKernelGGL(k_momentum_keys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, wo);
 }
 
 void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
-                              float keep, hipStream_t s) {
-  if (w_bf16) hipLaunchKernelGGL(k_update_unselected<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags, keep);
-  else hipLaunchKernelGGL(k_update_unselected<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags, keep);
+                              float keep, bool raw, hipStream_t s) {
+  const int rw = raw ? 1 : 0;
+  if (w_bf16) hipLaunchKernelGGL(k_update_unselected<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags, keep, rw);
+  else hipLaunchKernelGGL(k_update_unselected<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, flags, keep, rw);
+}
+
+void launch_decay_selected(const MatDesc* descs, int nmat, int64_t total_sel, const int* idx, float beta,
+                           hipStream_t s) {
+  if (total_sel > 0)
+    hipLaunchKernelGGL(k_decay_selected, dim3(row_blocks(total_sel)), dim3(256), 0, s, descs, nmat, total_sel, idx, beta);
 }
 
 void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,

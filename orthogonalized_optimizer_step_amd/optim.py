@@ -38,6 +38,9 @@ class Dion3(torch.optim.Optimizer):
                     the Gram Newton-Schulz schedule (a positive restart_threshold
                     replaces restart_every: restart once the product of a_k^2
                     since the last restart reaches it)
+      ef            "raw" (the buffer keeps the momentum; unselected rows step with it)
+                    or "carry" (unselected rows are carried in the buffer undecayed
+                    and do not step; only the selected rows decay by momentum)
       shape_scale   callable(shape) -> float, or None for 1 (default:
                     sqrt(max(1, rows / cols)))
 
@@ -47,12 +50,13 @@ class Dion3(torch.optim.Optimizer):
     """
 
     def __init__(self, params, lr=0.02, momentum=0.95, row_frac=0.125, weight_decay=0.0, ns_coeffs=QUINTIC,
-                 n_iter=5, restart_every=2, safety=1.0, shape_scale=rows_over_cols_scale, restart_threshold=0.0):
+                 n_iter=5, restart_every=2, safety=1.0, shape_scale=rows_over_cols_scale, restart_threshold=0.0,
+                 ef="raw"):
         if lr < 0 or not 0 < row_frac <= 1 or weight_decay < 0:
             raise ValueError("invalid lr, row_frac or weight_decay")
         defaults = dict(lr=lr, momentum=momentum, row_frac=row_frac, weight_decay=weight_decay,
                         ns_coeffs=tuple(ns_coeffs), n_iter=n_iter, restart_every=restart_every, safety=safety,
-                        shape_scale=shape_scale, restart_threshold=restart_threshold)
+                        shape_scale=shape_scale, restart_threshold=restart_threshold, ef=ef)
         super().__init__(params, defaults)
         for g in self.param_groups:
             for p in g["params"]:
@@ -63,12 +67,12 @@ class Dion3(torch.optim.Optimizer):
     def _orthogonalizer(self, shapes, g):
         from . import Orthogonalizer
         key = (tuple(shapes), g["ns_coeffs"], g["n_iter"], g["restart_every"], g["safety"], g["row_frac"],
-               g["restart_threshold"])
+               g["restart_threshold"], g["ef"])
         orth = self._orth.get(key)
         if orth is None:
             orth = Orthogonalizer(shapes, "fp32", g["ns_coeffs"], g["n_iter"], g["restart_every"], 0, g["safety"],
                                   g["row_frac"], "mfma16", device="cuda", step_mode=True,
-                                  restart_threshold=g["restart_threshold"])
+                                  restart_threshold=g["restart_threshold"], ef=g["ef"])
             self._orth[key] = orth
         return orth
 

@@ -197,3 +197,14 @@ def test_lowrank_validation_errors_before_launch():
     assert call(nbytes=need - 1) == -3                   # workspace too small
     assert call(ws=0x100001) == -3                       # misaligned
     assert call(ws=0) == -3
+
+
+def test_ef_carry_validation():
+    """ef_carry is 0 or 1; anything else is rejected when the parameters are parsed."""
+    shp = [(64, 32)]
+    assert dion.workspace_size(shp, "fp32", row_frac=0.25) > 0
+    p, keep = dion._params(dion.QUINTIC, 5, 2, 0, 1.0, 0.25, "mfma16", 0.0, "carry")
+    assert p.ef_carry == 1
+    p.ef_carry = 2
+    assert _lib.lib.dion_workspace_size(dion._shapes(shp), 1, _lib.DION_FP32, ctypes.byref(p)) == 0
+    assert "ef_carry" in _lib.lib.dion_last_error().decode()

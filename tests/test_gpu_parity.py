@@ -371,3 +371,73 @@ def test_tiny_row_subset(dion, frac):
         unsel = np.setdiff1d(np.arange(s[0]), idx)
         assert np.array_equal(on[unsel], M[unsel].astype(np.float64)), s
         assert O.rel_frobenius(on[idx], ref[idx]) <= 2.0 ** -8, s
+
+
+# ---------------------------------------- carry form of error feedback
+def test_rowsubset_carry_steps(dion):
+    """ef="carry", three steps: the buffer bit-exact (unselected rows carried
+    undecayed, selected rows fl32(beta B)), indices as the oracle's on
+    B = fl32(E + G), unselected output rows exactly zero."""
+    shapes = [(32, 20), (64, 48), (40, 200), (300, 64)]
+    beta = 0.95
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(3):
+        G = [round_bf16(lowrank_np((4, t, i, 2), r, c, 3, 0.05, log_scale=(-3.0, 0.0)))
+             for i, (r, c) in enumerate(shapes)]
+        outs, idxs = dion.rowsubset_step(E_dev, [to_dev_bf16(g) for g in G], beta, restart_every=2,
+                                         row_frac=0.25, return_indices=True, ef="carry")
+        newE, ref_outs, ref_idxs = O.rowsubset_step(E_host, G, beta, ef="carry", n_iter=5, restart_every=2,
+                                                    row_frac=0.25)
+        for i in range(len(shapes)):
+            B = np.add(E_host[i], G[i], dtype=np.float32)
+            assert np.array_equal(E_dev[i].cpu().numpy().view(np.uint32), newE[i].view(np.uint32))
+            assert_selection(idxs[i].cpu().numpy(), B, 0.25)
+            got = to_np(outs[i])
+            ix = ref_idxs[i]
+            rest = np.setdiff1d(np.arange(shapes[i][0]), ix)
+            assert np.all(got[rest] == 0.0)
+            assert O.rel_frobenius(got[ix], ref_outs[i][ix]) <= TOL_MFMA16
+        E_host = newE
+
+
+def test_rowsubset_carry_update(dion):
+    """ef="carry" with the fused weight update: unselected weight rows take only the
+    decay, fl32(W keep) rounded to bf16, bit for bit; the buffer bit-exact."""
+    shapes = [(32, 20), (64, 48), (300, 64)]
+    beta, wd = 0.9, 0.01
+    alphas = [0.02 * float(np.sqrt(max(1.0, r / c))) for r, c in shapes]
+    rng = np.random.default_rng(8)
+    W_host = [O.round_to_bf16((rng.standard_normal(s) * 0.02).astype(np.float32)) for s in shapes]
+    W_dev = [torch.from_numpy(w).cuda().to(torch.bfloat16) for w in W_host]
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(2):
+        G = [round_bf16(lowrank_np((4, t, i, 3), r, c, 3, 0.05)) for i, (r, c) in enumerate(shapes)]
+        dion.rowsubset_step_update(E_dev, [to_dev_bf16(g) for g in G], W_dev, beta, alphas, wd,
+                                   restart_every=2, row_frac=0.25, ef="carry")
+        newE, newW, ref_idxs = O.rowsubset_step_update(E_host, G, W_host, beta, alphas, wd, bf16=True, n_iter=5,
+                                                       restart_every=2, row_frac=0.25, ef="carry")
+        for i in range(len(shapes)):
+            assert np.array_equal(E_dev[i].cpu().numpy().view(np.uint32), newE[i].view(np.uint32))
+            rest = np.setdiff1d(np.arange(shapes[i][0]), ref_idxs[i])
+            assert np.array_equal(to_np(W_dev[i])[rest], newW[i][rest])
+        E_host = newE
+        W_host = [to_np(w).astype(np.float32) for w in W_dev]
+
+
+def test_rowsubset_carry_equals_raw_at_full_rows(dion):
+    """row_frac = 1: carry and raw run the same momentum sequence, so their outputs are
+    bit-identical over several steps, and carry's buffer is fl32(beta * raw's)."""
+    shapes = [(64, 48), (40, 200)]
+    beta = 0.95
+    Er = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    Ec = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(3):
+        G = [to_dev_bf16(round_bf16(lowrank_np((4, t, i, 4), r, c, 3, 0.05))) for i, (r, c) in enumerate(shapes)]
+        o_r = dion.rowsubset_step(Er, G, beta, restart_every=2, row_frac=1.0)
+        o_c = dion.rowsubset_step(Ec, G, beta, restart_every=2, row_frac=1.0, ef="carry")
+        for i in range(len(shapes)):
+            assert torch.equal(o_r[i], o_c[i])
+            want = np.multiply(np.float32(beta), Er[i].cpu().numpy(), dtype=np.float32)
+            assert np.array_equal(Ec[i].cpu().numpy().view(np.uint32), want.view(np.uint32))
