@@ -578,8 +578,20 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     // G's lo term is read only by a segment that runs two-term
     gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", seg_terms(0) == 2);
   }
+  // the m x m slots not holding G; an exhausted list fails the plan below
+  // rather than handing out a slot twice
   std::vector<int> freel = {SLOT_MM3, SLOT_MM2, SLOT_MM1};
   if (any_acc) freel.insert(freel.begin(), {SLOT_MM5, SLOT_MM4});
+  bool out_of_slots = false;
+  auto take = [&]() {
+    if (freel.empty()) {
+      out_of_slots = true;
+      return (int)SLOT_MM1;
+    }
+    const int v = freel.back();
+    freel.pop_back();
+    return v;
+  };
   int q_slot = -1, xt_slot = SLOT_XT0, xterms = P.xterms0;
   float sQ = 1.f, sXT = 1.f;
   double qb = 1.0;
@@ -625,8 +637,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     const double pb = poly_max(a, b, c, gb, 0), tb = poly_max(a, b, c, gb, 1);
     const double sb_next = sv_max(a, b, c, sb);
     const float sP = sc(pb);
-    const int p_slot = freel.back();
-    freel.pop_back();
+    const int p_slot = take();
     {  // P = a I + b G + c G^2, fused into the G*G epilogue
       PhaseArgs pa{};
       pa.a_slot = pa.b_slot = pa.aux_slot = g_slot;
@@ -655,8 +666,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     } else {  // Q <- P Q
       const double qb_new = qb * pb;
       const float sQn = sc(qb_new);
-      const int qn = freel.back();
-      freel.pop_back();
+      const int qn = take();
       PhaseArgs pa{};
       pa.a_slot = p_slot;
       pa.b_slot = q_slot;
@@ -666,8 +676,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         // this Q starts the accumulated factor of the matrices restarting
         // from X0; their next accumulation multiplies by it from the right,
         // which reads its rows as columns: keep Q^T (hi) as well
-        pending_qat = freel.back();
-        freel.pop_back();
+        pending_qat = take();
         PhaseArgs pt = pa;
         pt.aux_slot = pending_qat;
         gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT_T, pt, "full_product", false);
@@ -684,7 +693,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     }
     if (k == K) break;
     if (prm.restart[k - 1]) {
-      // X <- Q X, computed as X'^T = X^T Q; then X = transpose; G = X X^T
+      // X <- Q X, computed as X'^T = X^T Q; then X = transpose; G = X X^T.
+      // P is dead here (the apply and the accumulation read Q and X): its slot
+      // goes back first, so that the accumulation's two new slots fit beside
+      // G, Q, S and S^T in the six m x m slots
+      if (p_slot != q_slot) freel.push_back(p_slot);
       ++n_rest;
       const float sXn = sc(sb_next);
       // odd-numbered restarts write XT1, even-numbered ones XTE (XT0's buffer,
@@ -723,12 +736,10 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         const double qab_new = qab * qb;
         const float sQAn = sc(qab_new);
         const bool more = n_rest < n_restarts;
-        const int qa_new = freel.back();
-        freel.pop_back();
+        const int qa_new = take();
         int qat_new = qa_new;
         if (more) {
-          qat_new = freel.back();
-          freel.pop_back();
+          qat_new = take();
         }
         PhaseArgs pq{};
         pq.a_slot = q_slot;
@@ -778,13 +789,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       } else {
         freel.push_back(q_slot);
       }
-      if (p_slot != q_slot) freel.push_back(p_slot);
       q_slot = -1;
     } else {
       // G <- P T^T with T = P G, i.e. P G P (each product reads B by rows: C = A B^T)
       const float sT = sc(tb);
-      const int t_slot = freel.back();
-      freel.pop_back();
+      const int t_slot = take();
       {
         PhaseArgs pa{};
         pa.a_slot = p_slot;
@@ -809,6 +818,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     }
     sb = sb_next;
   }
+  if (out_of_slots) return fail(DION_E_UNSUPPORTED, "internal: the schedule needs more m x m buffers");
   {  // out = Q X: wide matrices as Q * X, tall ones as X^T * Q
     // After a short last segment both operands enter in their hi term: Q's
     // gain there is at most about a^2 and nothing amplifies the rounding

@@ -441,3 +441,19 @@ def test_rowsubset_carry_equals_raw_at_full_rows(dion):
             assert torch.equal(o_r[i], o_c[i])
             want = np.multiply(np.float32(beta), Er[i].cpu().numpy(), dtype=np.float32)
             assert np.array_equal(Ec[i].cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("sched", [dict(n_iter=12, restart_every=2), dict(n_iter=9, restart_every=2),
+                                   dict(n_iter=8, restart_mask=0b1010101)])
+def test_many_restarts_with_accumulated_factor(dion, sched):
+    """Three to five restarts of two-iteration segments with matrices that restart from X0
+    through the accumulated factor (n >= 1.5 m): the schedule whose third restart once needed
+    a seventh m x m buffer.  Row subsets, bf16, against the oracle."""
+    rng = np.random.default_rng(41)
+    shapes = [(92, 43), (280, 85), (196, 298), (83, 114), (200, 640), (640, 200), (128, 128)]
+    Ms = [round_bf16(rng.standard_normal(s).astype(np.float32)) for s in shapes]
+    kw = dict(row_frac=0.5, **sched)
+    outs = dion.orth_batched([to_dev_bf16(M) for M in Ms], **kw)
+    for M, o, s in zip(Ms, outs, shapes):
+        ref, idx = O.orthogonalize(M, **kw)
+        assert O.rel_frobenius(to_np(o)[idx], ref[idx]) <= TOL_MFMA16, (s, sched)

@@ -1,0 +1,31 @@
+"""The library's host code (planner, workspace layout, argument checks) under
+AddressSanitizer and UndefinedBehaviorSanitizer, on the CPU: builds
+tests/host_check/host_check.cpp with dion_api.cpp (sanitizers on the host
+compilation only, kernel launchers stubbed) and runs it."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "orthogonalized_optimizer_step_amd", "csrc")
+
+
+def test_host_code_under_asan_ubsan(tmp_path):
+    hipcc = "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else shutil.which("hipcc")
+    if not hipcc:
+        pytest.skip("hipcc not available")
+    exe = str(tmp_path / "host_check")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
+           os.path.join(CSRC, "dion_api.cpp"), os.path.join(ROOT, "tests", "host_check", "host_check.cpp"),
+           "-lrocblas", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
+    assert "host check:" in r.stdout
