@@ -457,3 +457,29 @@ def test_many_restarts_with_accumulated_factor(dion, sched):
     for M, o, s in zip(Ms, outs, shapes):
         ref, idx = O.orthogonalize(M, **kw)
         assert O.rel_frobenius(to_np(o)[idx], ref[idx]) <= TOL_MFMA16, (s, sched)
+
+
+@pytest.mark.parametrize("ef", ["raw", "carry"])
+def test_rowsubset_resume_from_host_copy(dion, ef):
+    """The caller's fp32 buffer is the only state across steps: ten consecutive steps equal
+    five steps, a round trip of the buffer through host memory into fresh device tensors,
+    and five more steps, bit for bit (buffer, indices and outputs)."""
+    shapes = [(64, 48), (40, 200), (300, 64)]
+    grads = [[to_dev_bf16(round_bf16(lowrank_np((4, t, i, 5), r, c, 3, 0.05))) for i, (r, c) in enumerate(shapes)]
+             for t in range(10)]
+    kw = dict(restart_every=2, row_frac=0.25, return_indices=True, ef=ef)
+    E1 = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    run1 = [dion.rowsubset_step(E1, grads[t], 0.95, **kw) for t in range(10)]
+    E2 = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    run2 = [dion.rowsubset_step(E2, grads[t], 0.95, **kw) for t in range(5)]
+    host = [e.cpu().numpy().copy() for e in E2]
+    del E2
+    E3 = [torch.from_numpy(h).cuda() for h in host]
+    run2 += [dion.rowsubset_step(E3, grads[t], 0.95, **kw) for t in range(5, 10)]
+    for a, b in zip(E1, E3):
+        assert torch.equal(a, b)
+    for (oa, ia), (ob, ib) in zip(run1, run2):
+        for x, y in zip(oa, ob):
+            assert torch.equal(x, y)
+        for x, y in zip(ia, ib):
+            assert torch.equal(x, y)
