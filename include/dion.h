@@ -114,7 +114,18 @@ typedef struct {
  *                 restarts remove appear (Dion3 summary, 局限: restart
  *                 threshold).  With the fixed quintic, tau = 100 restarts
  *                 every 2 iterations.  Evaluated on the host from the
- *                 coefficients: no device synchronization. */
+ *                 coefficients: no device synchronization.
+ *   keep_schedule MFMA16 path only.  0 (default): a run of more than two
+ *                 iterations between restarts is cut by an extra restart after
+ *                 every second iteration of the run.  A restart gives the same
+ *                 result in exact arithmetic; the short runs take one-term
+ *                 fp16 operands in the m x m chain (with the fixed quintic and
+ *                 bf16 Llama-shaped inputs, relative error about 5e-3).
+ *                 1: run the schedule as given; runs longer than two
+ *                 iterations take two-term operands (about 1e-3 without
+ *                 restarts, at about three times the MFMA work of those
+ *                 runs).  dion_restart_points and the useful-FLOP count
+ *                 follow the schedule as given either way. */
 typedef struct {
   const float* ns_coeffs;
   int32_t n_coeff_sets;
@@ -126,6 +137,7 @@ typedef struct {
   int32_t precision;
   float restart_threshold;
   int32_t ef_carry;
+  int32_t keep_schedule;
 } dion_ns_params;
 
 /* The iterations after which this parameter set restarts (host only, no

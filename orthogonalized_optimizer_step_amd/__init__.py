@@ -23,14 +23,14 @@ EF = {"raw": 0, "carry": 1}
 
 
 def _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold=0.0,
-            ef="raw"):
+            ef="raw", keep_schedule=False):
     flat = [float(x) for trip in ([coeffs] if len(coeffs) == 3 and not hasattr(coeffs[0], "__len__")
                                   else coeffs) for x in trip]
     arr = (ctypes.c_float * len(flat))(*flat)
     p = DionParams(ctypes.cast(arr, ctypes.POINTER(ctypes.c_float)), len(flat) // 3, int(n_iter),
                    int(restart_every), int(restart_mask), float(safety), float(row_frac),
                    PREC[precision] if isinstance(precision, str) else int(precision), float(restart_threshold),
-                   EF[ef] if isinstance(ef, str) else int(ef))
+                   EF[ef] if isinstance(ef, str) else int(ef), int(bool(keep_schedule)))
     return p, arr
 
 
@@ -65,8 +65,9 @@ def _check_tensors(ts, dtype=None):
 
 
 def workspace_size(shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                   safety=1.0, row_frac=1.0, precision="auto", restart_threshold=0.0) -> int:
-    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold)
+                   safety=1.0, row_frac=1.0, precision="auto", restart_threshold=0.0, keep_schedule=False) -> int:
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold,
+                      keep_schedule=keep_schedule)
     code = {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
     n = lib.dion_workspace_size(_shapes(shapes), len(shapes), code, ctypes.byref(p))
     if n == 0:
@@ -112,13 +113,13 @@ class Orthogonalizer:
 
     def __init__(self, shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
                  safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False, restart_threshold=0.0,
-                 ef="raw"):
+                 ef="raw", keep_schedule=False):
         import torch
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.dtype = dtype
         self.step_mode = step_mode
         self._p, self._keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision,
-                                      restart_threshold, ef)
+                                      restart_threshold, ef, keep_schedule)
         self._shp = _shapes(self.shapes)
         code = DION_FP32 if step_mode else {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
         self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
@@ -162,7 +163,8 @@ class Orthogonalizer:
 
 
 def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
-                 row_frac=1.0, precision="auto", return_indices=False, stream=None, restart_threshold=0.0):
+                 row_frac=1.0, precision="auto", return_indices=False, stream=None, restart_threshold=0.0,
+                 keep_schedule=False):
     """Orthogonalize a list of 2-D bf16 or fp32 CUDA tensors in one megabatched call.
 
     Returns the list of outputs (same shapes and dtype), and with
@@ -172,7 +174,8 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
     _check_tensors(Ms, Ms[0].dtype)
     dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(Ms[0].dtype, "fp32")
     orth = Orthogonalizer([tuple(M.shape) for M in Ms], dt, coeffs, n_iter, restart_every, restart_mask,
-                          safety, row_frac, precision, device=Ms[0].device, restart_threshold=restart_threshold)
+                          safety, row_frac, precision, device=Ms[0].device, restart_threshold=restart_threshold,
+                          keep_schedule=keep_schedule)
     if outs is None:
         outs = [torch.empty_like(M) for M in Ms]
     _check_tensors(outs, Ms[0].dtype)

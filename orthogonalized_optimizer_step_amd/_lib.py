@@ -32,6 +32,7 @@ class DionParams(ctypes.Structure):
         ("precision", ctypes.c_int32),
         ("restart_threshold", ctypes.c_float),
         ("ef_carry", ctypes.c_int32),
+        ("keep_schedule", ctypes.c_int32),
     ]
 
 

@@ -74,6 +74,7 @@ struct Params {
   double row_frac;
   bool fp64;
   bool carry;   // row-subset step: the carry form of error feedback
+  bool keep_schedule;  // MFMA16: run long segments as given (two-term chain)
 };
 
 bool valid_dtype(int dtype) { return dtype == DION_BF16 || dtype == DION_FP32 || dtype == DION_FP16; }
@@ -125,6 +126,8 @@ int parse_params(const dion_ns_params* p, int dtype, bool step_mode, Params& out
   }
   if (p->ef_carry != 0 && p->ef_carry != 1) return fail(DION_E_INVAL, "ef_carry must be 0 or 1");
   out.carry = p->ef_carry == 1;
+  if (p->keep_schedule != 0 && p->keep_schedule != 1) return fail(DION_E_INVAL, "keep_schedule must be 0 or 1");
+  out.keep_schedule = p->keep_schedule == 1;
   out.row_frac = p->row_frac;
   out.fp64 = p->precision == DION_PREC_FP64 || (p->precision == DION_PREC_AUTO && dtype == DION_FP32 && !step_mode);
   return DION_OK;
@@ -306,8 +309,26 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;  // bf16 and fp16 values are exact in one fp16 term
   P.use_idx = prm.row_frac < 1.0;
   const int K = (int)prm.a.size();
+  // The restarts the GEMM schedule runs: the caller's and, on the MFMA16 path
+  // unless keep_schedule is set, one more after every second iteration of a
+  // longer run between restarts.  A restart re-forms G from the current
+  // iterate, so the result is the same in exact arithmetic; only the rounding
+  // changes.  Runs of at most two iterations take one-term fp16 operands in
+  // their m x m chain, whose rounding does not get to compound; a longer run
+  // needs two terms, about three times the MFMA work of its chain and of the
+  // final apply, where a restart costs one apply and one Gram.  Useful FLOPs
+  // are counted on the caller's schedule: the added restarts' products are
+  // extra work.
+  std::vector<int> xr = prm.restart;
+  if (!P.fp64 && !prm.keep_schedule) {
+    int k0 = 0;  // the current run started after iteration k0
+    for (int k = 1; k < K; ++k) {
+      if (!xr[k - 1] && k - k0 == 2) xr[k - 1] = 2;   // 2 = added here
+      if (xr[k - 1]) k0 = k;
+    }
+  }
   int n_restarts = 0;
-  for (int r : prm.restart) n_restarts += (r != 0);
+  for (int r : xr) n_restarts += (r != 0);
   const bool any_restart = n_restarts > 0;
   const size_t es = P.fp64 ? 8 : 2;
   const size_t mm_terms = P.fp64 ? 1 : 2;
@@ -565,7 +586,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   // iterations, two for longer ones (see the policy below)
   auto seg_terms = [&](int k0) {
     int e = k0 + 1;
-    while (e < K && !prm.restart[e - 1]) ++e;
+    while (e < K && !xr[e - 1]) ++e;
     return (P.fp64 || e - k0 > 2) ? 2 : 1;
   };
   {
@@ -629,7 +650,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       // 6.3e-3 with T mirrored, 9.1e-3 with both mirrored; on the row-subset
       // blocks 3.7e-3, 5.9e-3 and 1.2e-2.
       int e = k;
-      while (e < K && !prm.restart[e - 1]) ++e;
+      while (e < K && !xr[e - 1]) ++e;
       ct = e - k + 1 <= 2 ? 1 : 2;
       short_seg = !P.fp64 && ct == 1;
     }
@@ -672,7 +693,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.b_slot = q_slot;
       pa.c_slot = qn;
       pa.alpha = sQn / (sP * sQ);
-      if (short_seg && any_acc && k < K && prm.restart[k - 1] && n_rest == 0) {
+      if (short_seg && any_acc && k < K && xr[k - 1] && n_rest == 0) {
         // this Q starts the accumulated factor of the matrices restarting
         // from X0; their next accumulation multiplies by it from the right,
         // which reads its rows as columns: keep Q^T (hi) as well
@@ -692,13 +713,14 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       qb = qb_new;
     }
     if (k == K) break;
-    if (prm.restart[k - 1]) {
+    if (xr[k - 1]) {
       // X <- Q X, computed as X'^T = X^T Q; then X = transpose; G = X X^T.
       // P is dead here (the apply and the accumulation read Q and X): its slot
       // goes back first, so that the accumulation's two new slots fit beside
       // G, Q, S and S^T in the six m x m slots
       if (p_slot != q_slot) freel.push_back(p_slot);
       ++n_rest;
+      const bool added = xr[k - 1] == 2;   // a restart of the schedule policy: extra work
       const float sXn = sc(sb_next);
       // odd-numbered restarts write XT1, even-numbered ones XTE (XT0's buffer,
       // or XT1's for matrices restarting from X0, whose X0^T stays in XT0)
@@ -707,7 +729,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       // apply, which takes its hi term only after a short last segment.
       // Matrices restarting from X0 read it only in the final apply.
       int e2 = k + 1;
-      while (e2 < K && !prm.restart[e2 - 1]) ++e2;
+      while (e2 < K && !xr[e2 - 1]) ++e2;
       const bool xt_lo = !(e2 == K && e2 - k <= 2);
       const bool xt_lo_acc = xt_lo && e2 == K;
       auto apply = [&](int table, int a_slot, int na, int b_slot, float alpha, int alpha_pow, bool lo) {
@@ -720,7 +742,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.alpha_pow = alpha_pow;
         // MFMA16: the epilogue also writes X (hi) transposed; FP64: a transpose pass
         pa.aux_slot = SLOT_X;
-        gemm(table, bm_xtq, false, na, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply", lo);
+        gemm(table, bm_xtq, false, na, 1, P.fp64 ? EPI_RECT : EPI_RECT_T, pa, "apply", lo, !added);
       };
       const float al = x_is_x0 ? sXn / sQ : sXn / (sXT * sQ);
       const int alp = x_is_x0 ? 1 : 0;
@@ -774,7 +796,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pa.c_slot = g_slot;
         pa.k_is_n = 1;
         pa.alpha = sGn / (sXn * sXn);
-        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", seg_terms(k) == 2);
+        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "syrk", seg_terms(k) == 2, !added);
       }
       sG = sGn;
       xt_slot = xt_new;

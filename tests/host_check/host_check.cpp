@@ -81,6 +81,7 @@ int main() {
     p.row_frac = (const float[]){1.0f, 0.5f, 0.25f, 0.125f, 1.0f / 37}[pick(0, 4)];
     p.precision = pick(0, 2);
     p.ef_carry = pick(0, 1);
+    p.keep_schedule = pick(0, 1);
     for (int dt : {DION_BF16, DION_FP32, DION_FP16}) {
       const size_t n = dion_workspace_size(sh.data(), batch, dt, &p);
       if (n) ++planned;
@@ -114,6 +115,9 @@ int main() {
   p.restart_threshold = NAN;
   bad += dion_workspace_size(s2, 2, DION_BF16, &p) != 0;
   p.restart_threshold = 0.0f;
+  p.keep_schedule = 2;
+  bad += dion_workspace_size(s2, 2, DION_BF16, &p) != 0;
+  p.keep_schedule = 0;
   bad += dion_rowsubset_step(nullptr, nullptr, nullptr, s2, 2, DION_BF16, 0.9f, &p, nullptr, nullptr, 0, nullptr) == 0;
   bad += dion_lowrank_step(nullptr, nullptr, nullptr, nullptr, s2, 2, DION_BF16, DION_BF16, 8, 1.0f, 0, nullptr, 0,
                            nullptr) == 0;

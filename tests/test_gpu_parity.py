@@ -103,6 +103,41 @@ def test_small_ragged_mfma16(dion, sched):
     assert max(errs) <= TOL_MFMA16
 
 
+@pytest.mark.parametrize("sched", [dict(), dict(restart_mask=0b10, safety=1.01), dict(n_iter=6, restart_mask=0b1),
+                                   dict(n_iter=7, restart_threshold=1e5)])
+def test_long_runs_cut_or_kept(dion, sched):
+    """Schedules with runs of more than two iterations between restarts: cut by extra
+    restarts (the default) or run as given with two-term operands (keep_schedule).  Both
+    against the oracle of the schedule as given, since a restart does not change the exact
+    result; the kept plan forms one Gram per run of the schedule, the cut one more."""
+    Ms = small_batch(15)
+    kw = {"n_iter": 5, **sched}
+    dev = [to_dev_bf16(M) for M in Ms]
+    refs = [O.orthogonalize(M, **kw)[0] for M in Ms]
+    grams, worst = {}, {}
+    for keep in (False, True):
+        dion.profile_enable(True)
+        outs = dion.orth_batched(dev, keep_schedule=keep, **kw)
+        names = [r[0] for r in dion.profile_records()]
+        dion.profile_enable(False)
+        errs = [O.rel_frobenius(to_np(o), ref) for o, ref in zip(outs, refs)]
+        grams[keep], worst[keep] = names.count("syrk"), max(errs)
+        assert max(errs) <= TOL_MFMA16, (sched, keep, errs)
+    runs = len(dion.restart_points(**{k: v for k, v in kw.items() if k != "row_frac"})) + 1
+    assert grams[True] == runs and grams[False] > runs, (grams, runs)
+    print("long runs", sched, f"cut {worst[False]:.2e} kept {worst[True]:.2e}", flush=True)
+
+
+def test_keep_schedule_no_effect_on_short_runs(dion):
+    """Runs of at most two iterations are never cut: the same plan, bit-identical outputs."""
+    dev = [to_dev_bf16(M) for M in small_batch(16)]
+    for kw in (dict(restart_every=2), dict(n_iter=6, restart_every=2, safety=1.05), dict(n_iter=2)):
+        a = dion.orth_batched(dev, **kw)
+        b = dion.orth_batched(dev, keep_schedule=True, **kw)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), kw
+
+
 def test_restart_threshold_same_plan_as_mask(dion):
     """A threshold only chooses the restart points: tau = 100 with the fixed quintic
     plans restarts {2, 4}, so the output is bit-identical to restart_every = 2."""
