@@ -8,10 +8,12 @@ of the 32-layer Llama-3-8B layer set (q,o 4096x4096; k,v 1024x4096; gate,up
 10^U(-3,0), 5 Gram Newton-Schulz iterations with restarts every 2.  Inputs are
 synthetic and resident in HBM before the timed region.  Prints one JSON line.
 
-Beside the GPU figures: a roofline entry for the dominant kernel (algorithmic
-FLOPs per launch over its average launch time, measured with hipEvents on the
-launch stream by the library's profiling hook, against the dense fp16/bf16 MFMA
-peak), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Beside the GPU figures: a roofline entry for the dominant kernel (the one with
+the most GPU time: algorithmic FLOPs per launch over its average launch time,
+measured with hipEvents on the launch stream by the library's profiling hook,
+against the dense fp16/bf16 MFMA peak; for a streaming pass, algorithmic bytes
+against HBM), and the fp64 CPU oracle timed on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -100,7 +102,9 @@ KERNEL_SOURCES = ("orthogonalized_optimizer_step_amd/csrc/gemm_kernels.hip",
                   "orthogonalized_optimizer_step_amd/csrc/stream_kernels.hip",
                   "orthogonalized_optimizer_step_amd/csrc/dion_api.cpp",
                   "orthogonalized_optimizer_step_amd/csrc/dion_internal.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama3_8b_hbm_traffic.txt")
+# counter summaries per workload (the TRAFFIC lines of a file hold only for the workload it was taken on)
+TRAFFIC_FILES = {"llama3_8b": os.path.join(ROOT, "profiles", "llama3_8b_hbm_traffic.txt"),
+                 "llama3_8b_rows": os.path.join(ROOT, "profiles", "llama3_8b_rows_hbm_traffic.txt")}
 
 
 def sources_sha256():
@@ -149,7 +153,9 @@ def summarize(d):
         for k, cs in agg.items():
             if "copyBuffer" in k:
                 for c, v in cs.items():
-                    big = [x for x in v if x > (1 << 19)]   # the 1 GiB copy, counters in KiB
+                    # the 1 GiB copy (counters in KiB; FETCH_SIZE reads about half of it),
+                    # far above the per-call uploads of a few KiB
+                    big = [x for x in v if x > (1 << 18)]
                     if big:
                         calib[c] = (1 << 20) / max(big)      # true KiB / counted KiB
         print(f"\n{'kernel':64s} {'counter':12s} {'dispatches':>10s} {'avg GiB/dispatch':>17s} {'scaled':>8s}")
@@ -166,14 +172,16 @@ def summarize(d):
                   ", ".join(f"{c} x{v:.3f}" for c, v in calib.items()))
 
 
-def traffic_for(kernel):
+def traffic_for(kernel, workload):
     """HBM bytes per launch (fetch + write) of `kernel` from the committed
-    counter summary, or None if absent or taken on different kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    counter summary of `workload`, or None if absent or taken on different
+    kernel sources."""
+    path = TRAFFIC_FILES.get(workload)
+    if path is None or not os.path.exists(path):
         return None
     sha = sources_sha256()
     got = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if line.startswith("TRAFFIC {"):
             t = json.loads(line[8:])
             if t["kernel"] == kernel and t["sources_sha256"] == sha:
@@ -377,7 +385,8 @@ def main():
         ph["useful"] += u
         ph["mfma"] += r
         ph["bytes"] += b
-    # the roofline entry is for the kernel instance with the most GPU time
+    # the roofline entry is for the kernel instance with the most GPU time:
+    # an MFMA kernel against the matrix peak, a streaming pass against HBM
     kernels = {}
     for name, kern, ms, u, r, b in recs:
         k = kernels.setdefault(kern, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0,
@@ -388,14 +397,16 @@ def main():
         k["useful"] += u
         k["mfma"] += r
         k["bytes"] += b
-    dom_kernel = max((k for k, v in kernels.items() if v["mfma"] > 0), key=lambda k: kernels[k]["ms"])
+    dom_kernel = max(kernels, key=lambda k: kernels[k]["ms"])
     d = kernels[dom_kernel]
     avg_ms = d["ms"] / d["launches"]
-    achieved = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
+    compute = d["mfma"] > 0
+    achieved = ((d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12 if compute else
+                (d["bytes"] / d["launches"]) / (avg_ms * 1e-3) / 1e9)
     # algorithmic HBM bytes per launch, from the plan: each operand term read
     # once and the result written once
     alg_bytes = d["bytes"] / d["launches"]
-    traffic = traffic_for(dom_kernel)
+    traffic = None if args.update else traffic_for(dom_kernel, wl.name)
     raw_total = sum(p["mfma"] for p in phases.values()) / args.steps
     phase_summary = {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
                          "launches_per_step": p["launches"] // args.steps,
@@ -428,13 +439,16 @@ def main():
         "useful_pct_peak": 100.0 * useful / (ms_per_step * 1e-3) / 1e12 / peak,
         "mfma_tflops": raw_total / (ms_per_step * 1e-3) / 1e12,
         "host_wall_s": wall,
-        "roofline": {"bound": "alu" if fp64 else "mfma", "kernel": dom_kernel,
-                     "phase": "+".join(sorted(d["phases"])), "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic, "launch_ms": avg_ms,
-                     "useful_flops_per_launch": d["useful"] / d["launches"],
-                     "mfma_tflops": d["mfma"] / d["launches"] / (avg_ms * 1e-3) / 1e12,
-                     "algorithmic_bytes_per_launch": alg_bytes},
+        "roofline": ({"bound": "alu" if fp64 else "mfma", "kernel": dom_kernel,
+                      "phase": "+".join(sorted(d["phases"])), "achieved": achieved,
+                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                      "traffic": traffic, "launch_ms": avg_ms,
+                      "useful_flops_per_launch": d["useful"] / d["launches"],
+                      "mfma_tflops": d["mfma"] / d["launches"] / (avg_ms * 1e-3) / 1e12,
+                      "algorithmic_bytes_per_launch": alg_bytes} if compute else
+                     {"bound": "hbm", "kernel": dom_kernel, "phase": "+".join(sorted(d["phases"])),
+                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                      "traffic": traffic, "launch_ms": avg_ms, "algorithmic_bytes_per_launch": alg_bytes}),
         "phases": phase_summary,
     }
     if not args.no_cpu_baseline:
