@@ -1146,22 +1146,27 @@ struct ProfRec {
   double useful, raw, bytes;
 };
 
-// Name of the kernel instance a step launches, as the profiler prints it.
-const char* kernel_name(const Plan& P, const Step& st) {
-  thread_local std::deque<std::pair<std::string, std::string>> cache;  // stable addresses
+// Name of the kernel instance a step launches, as the profiler prints it
+// (template arguments included); s_fmt is the element format the step reads
+// (0 bf16, 1 fp32, 2 fp16), grad_bf16 the row-subset step's gradient type.
+const char* kernel_name(const Plan& P, const Step& st, int s_fmt, bool grad_bf16) {
+  thread_local std::deque<std::string> cache;  // stable addresses
+  const char* in_t = s_fmt == 1 ? "float" : (s_fmt == 2 ? "_Float16" : "unsigned short");
   std::string key;
   switch (st.kind) {
-    case ST_KEYS: return "dion::k_rowkeys";
-    case ST_MOMENTUM: return "dion::k_momentum_keys";
-    case ST_SELECT: return "dion::k_select";
-    case ST_PACK: return P.fp64 ? "dion::k_pack" : "dion::k_pack16";
-    case ST_TRANSPOSE: return "dion::k_transpose";
-    case ST_COPY: return "dion::k_copy_unselected";
-    case ST_TINY: return "dion::k_tiny_gns";
-    case ST_DECAY: return "dion::k_decay_selected";
-    case ST_UNPACK: return "dion::k_unpack";
-    case ST_COMBINE: return "dion::k_scale_combine";
-    case ST_UPDATE: return P.w_bf16 ? "dion::k_update_unselected<unsigned short>" : "dion::k_update_unselected<float>";
+    case ST_KEYS: key = std::string("dion::k_rowkeys<") + in_t + ">"; break;
+    case ST_MOMENTUM: key = grad_bf16 ? "dion::k_momentum_keys<unsigned short>" : "dion::k_momentum_keys<float>"; break;
+    case ST_SELECT: key = "dion::k_select"; break;
+    case ST_PACK: key = std::string(P.fp64 ? "dion::k_pack<" : "dion::k_pack16<") + in_t + ">"; break;
+    case ST_TRANSPOSE: key = "dion::k_transpose<double>"; break;
+    case ST_COPY: key = s_fmt != 1 ? "dion::k_copy_unselected<unsigned short>" : "dion::k_copy_unselected<float>"; break;
+    case ST_TINY: key = "dion::k_tiny_gns"; break;
+    case ST_DECAY: key = "dion::k_decay_selected"; break;
+    case ST_UNPACK: key = P.fp64 ? "dion::k_unpack<double>" : "dion::k_unpack<_Float16>"; break;
+    case ST_COMBINE: key = "dion::k_scale_combine"; break;
+    case ST_UPDATE:
+      key = P.w_bf16 ? "dion::k_update_unselected<unsigned short>" : "dion::k_update_unselected<float>";
+      break;
     case ST_GEMM:
       if (P.fp64)
         key = "dion::k_gemm64<" + std::to_string(st.epi) + ", " + (st.sym ? "true" : "false") + ">";
@@ -1170,10 +1175,10 @@ const char* kernel_name(const Plan& P, const Step& st) {
               std::to_string(st.nb) + ", " + std::to_string(st.epi) + ", " + (st.sym ? "true" : "false") + ">";
       break;
   }
-  for (auto& kv : cache)
-    if (kv.first == key) return kv.second.c_str();
-  cache.emplace_back(key, key);
-  return cache.back().second.c_str();
+  for (const std::string& k : cache)
+    if (k == key) return k.c_str();
+  cache.push_back(key);
+  return cache.back().c_str();
 }
 struct Profiler {
   bool on = false;
@@ -1273,7 +1278,6 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
 
   for (const Step& st : P.steps) {
     ProfRec rec{st.name, nullptr, nullptr, nullptr, st.useful, st.raw, st.bytes};
-    if (g_prof.on) rec.kernel = kernel_name(P, st);
     if (g_prof.on) {
       rec.a = g_prof.get();
       rec.b = g_prof.get();
@@ -1290,6 +1294,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     uint8_t* sflags = qset ? d_flags + P.x_rows : d_flags;
     int* sidx = qset ? d_idx + P.x_sel : d_idx;
     const int s_fmt = qset ? 1 : fmt;   // the apply's Q operands are fp32
+    if (g_prof.on) rec.kernel = kernel_name(P, st, s_fmt, grad_dtype == DION_BF16);
     switch (st.kind) {
       case ST_KEYS:
         launch_rowkeys(s_fmt, sd, sn, srows, skeys, stream);
