@@ -110,7 +110,8 @@ KERNEL_SOURCES = ("orthogonalized_optimizer_step_amd/csrc/gemm_kernels.hip",
                   "orthogonalized_optimizer_step_amd/csrc/dion_internal.h")
 # counter summaries per workload (the TRAFFIC lines of a file hold only for the workload it was taken on)
 TRAFFIC_FILES = {"llama3_8b": os.path.join(ROOT, "profiles", "llama3_8b_hbm_traffic.txt"),
-                 "llama3_8b_rows": os.path.join(ROOT, "profiles", "llama3_8b_rows_hbm_traffic.txt")}
+                 "llama3_8b_rows": os.path.join(ROOT, "profiles", "llama3_8b_rows_hbm_traffic.txt"),
+                 "llama3_8b_rows+update": os.path.join(ROOT, "profiles", "llama3_8b_rows_update_hbm_traffic.txt")}
 
 
 def sources_sha256():
@@ -412,7 +413,7 @@ def main():
     # algorithmic HBM bytes per launch, from the plan: each operand term read
     # once and the result written once
     alg_bytes = d["bytes"] / d["launches"]
-    traffic = None if args.update else traffic_for(dom_kernel, wl.name)
+    traffic = traffic_for(dom_kernel, wl.name + ("+update" if args.update else ""))
     raw_total = sum(p["mfma"] for p in phases.values()) / args.steps
     phase_summary = {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
                          "launches_per_step": p["launches"] // args.steps,

@@ -1846,16 +1846,31 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
   P.update = true;
   P.w_bf16 = w_dtype == DION_BF16;
   P.keep = 1.0f - weight_decay;
-  for (Step& st : P.steps)
+  // algorithmic bytes: the momentum pass writes no update rows here, and the
+  // final apply reads and writes the selected rows of W instead of writing out
+  double elems = 0.0, unsel = 0.0;
+  for (const MatPlan& mp : P.mats) {
+    elems += (double)mp.R * mp.C;
+    unsel += (double)(mp.R - mp.k) * mp.C;
+  }
+  for (Step& st : P.steps) {
+    if (st.kind == ST_MOMENTUM) st.bytes -= 2.0 * elems;
     if (st.kind == ST_GEMM && st.epi == EPI_OUT) {
       st.pa.out_update = 1;
       st.pa.upd_keep = P.keep;
       st.pa.out_fp32 = w_dtype == DION_FP32 ? 1 : 0;
+      const Table& tb = P.tabs[st.table];
+      for (int j = 0; j < tb.nmat; ++j) {
+        const MatPlan& mp = P.mats[P.ints[tb.mats_off + j]];
+        st.bytes += (2.0 * wes - 2.0) * (double)mp.m * mp.n;
+      }
     }
+  }
   if (P.use_idx) {
     Step u;
     u.kind = ST_UPDATE;
     u.name = "update_rows";
+    u.bytes = unsel * (4.0 + 2.0 * wes) + (double)P.total_rows;   // E read, W read and written; row flags
     P.steps.push_back(u);
   }
   return run(P, (const void* const*)E, W, grad, batch, DION_FP32, grad_dtype, beta, true, sel_idx, workspace,
