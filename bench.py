@@ -145,12 +145,22 @@ def summarize(d):
     import glob
     stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     ctrs = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if stats:
+        # per-dispatch durations in launch order, for the average after the first
+        # dispatch (the warmup call's, when the kernel runs once per call)
+        per = collections.defaultdict(list)
+        for f in traces:
+            for r in sorted(csv.DictReader(open(f)), key=lambda r: int(r["Start_Timestamp"])):
+                per[short_kernel(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
         rows = list(csv.DictReader(open(stats[0])))
-        print(f"{'kernel':64s} {'calls':>6s} {'total ms':>10s} {'avg us':>11s} {'%':>6s}")
+        print(f"{'kernel':64s} {'calls':>6s} {'total ms':>10s} {'avg us':>11s} {'%':>6s} {'avg us after 1st':>17s}")
         for r in rows:
-            print(f"{short_kernel(r['Name'])[:64]:64s} {int(r['Calls']):6d} {float(r['TotalDurationNs'])/1e6:10.3f} "
-                  f"{float(r['AverageNs'])/1e3:11.1f} {float(r['Percentage']):6.2f}")
+            k = short_kernel(r["Name"])
+            ds = per.get(k, [])
+            rest = f"{sum(ds[1:]) / len(ds[1:]) / 1e3:17.1f}" if len(ds) > 1 else f"{'-':>17s}"
+            print(f"{k[:64]:64s} {int(r['Calls']):6d} {float(r['TotalDurationNs'])/1e6:10.3f} "
+                  f"{float(r['AverageNs'])/1e3:11.1f} {float(r['Percentage']):6.2f} {rest}")
     for f in ctrs:
         rows = list(csv.DictReader(open(f)))
         agg = collections.defaultdict(lambda: collections.defaultdict(list))

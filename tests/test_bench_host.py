@@ -68,3 +68,22 @@ def test_gpus_above_one_is_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU only" in capsys.readouterr().out
+
+
+def test_summarize_kernel_stats_with_warm_average(tmp_path, capsys):
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "x_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": "void dion::k_select(int)", "Calls": 3, "TotalDurationNs": 6000, "AverageNs": 2000,
+                    "Percentage": 100.0})
+    with open(d / "x_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for start, end in ((500, 1500), (0, 3000), (4000, 5000)):   # out of order: the first launch is the slow one
+            w.writerow({"Kernel_Name": "void dion::k_select(int)", "Start_Timestamp": start, "End_Timestamp": end})
+    bench.summarize(str(d))
+    line = [l for l in capsys.readouterr().out.splitlines() if l.startswith("dion::k_select")][0]
+    assert line.split()[-1] == "1.0"   # (1000 + 1000) / 2 ns after the first launch, in us
+    assert line.split()[3] == "2.0"
