@@ -187,7 +187,8 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
 
 
 def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                   safety=1.0, row_frac=0.125, return_indices=False, stream=None, restart_threshold=0.0, ef="raw"):
+                   safety=1.0, row_frac=0.125, return_indices=False, stream=None, restart_threshold=0.0, ef="raw",
+                   keep_schedule=False):
     """One row-subset step; returns bf16 outputs.
 
     ef="raw": E <- fl32(fl32(beta E) + grad) in place, unselected output rows are E.
@@ -199,7 +200,7 @@ def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart
     _check_tensors(grads, grads[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
-                          restart_threshold=restart_threshold, ef=ef)
+                          restart_threshold=restart_threshold, ef=ef, keep_schedule=keep_schedule)
     if outs is None:
         outs = [torch.empty(E.shape, dtype=torch.bfloat16, device=E.device) for E in Es]
     _check_tensors(outs, torch.bfloat16)

@@ -235,6 +235,26 @@ def test_rowsubset_step_small(dion):
         E_host = newE
 
 
+@pytest.mark.parametrize("keep", [False, True])
+def test_long_runs_fp32_operands(dion, keep):
+    """fp32 inputs on the MFMA16 path (two-term X0) and the row-subset step's fp32 buffer,
+    with no restarts in K = 5: the cut plan restarts from the two-term iterate; both plans
+    against the oracle of the schedule as given."""
+    Ms = small_batch(17, dtype_bf16=False)
+    outs = dion.orth_batched([torch.from_numpy(M).cuda() for M in Ms], precision="mfma16", keep_schedule=keep)
+    for M, o in zip(Ms, outs):
+        assert O.rel_frobenius(to_np(o), O.orthogonalize(M)[0]) <= TOL_MFMA16, (M.shape, keep)
+    shapes = [(64, 48), (40, 200), (300, 64), (257, 511)]
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(2):
+        G = [round_bf16(lowrank_np((4, t, i, 6), r, c, 3, 0.05)) for i, (r, c) in enumerate(shapes)]
+        outs = dion.rowsubset_step(E_dev, [to_dev_bf16(g) for g in G], 0.95, row_frac=0.25, keep_schedule=keep)
+        E_host, ref_outs, ref_idxs = O.rowsubset_step(E_host, G, 0.95, n_iter=5, row_frac=0.25)
+        for i, ix in enumerate(ref_idxs):
+            assert O.rel_frobenius(to_np(outs[i])[ix], ref_outs[i][ix]) <= TOL_MFMA16, (shapes[i], t, keep)
+
+
 # -------------------------------------------------- fused weight update
 @pytest.mark.parametrize("wbf16", [False, True])
 def test_rowsubset_step_update(dion, wbf16):
