@@ -348,11 +348,16 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     mp.n = std::max(mp.k, C);
     mp.m_pad = pad_up(mp.m);
     mp.n_pad = pad_up(mp.n);
-    // From the second restart on, X_r = Q_r X_{r-1} can be formed as
-    // (Q_r ... Q_1) X0: X0 is exact in one fp16 term (bf16 input), so the
-    // apply takes one term instead of the iterate's two, at the price of one
-    // m x m product.  That pays where the apply's long side dominates.
-    mp.acc = !P.fp64 && P.xterms0 == 1 && n_restarts >= 2 && 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m;
+    // At the second restart, X_2 = Q_2 X_1 can be formed as (Q_2 Q_1) X0:
+    // X0 is exact in one fp16 term (bf16 input), so the apply takes one term
+    // instead of the iterate's two, at the price of one m x m product.  That
+    // pays where the apply's long side dominates.  Only in schedules of
+    // exactly two restarts: the accumulated factor is rounded to one term at
+    // every accumulation and carries the gain of every iteration since X0, so
+    // with more restarts its rounding compounds (emulation, K = 7 or 8 with
+    // restarts every 2 or every iteration: 1.0-2.4e-2 against 1.8-7.8e-3
+    // restarting from the two-term iterate).
+    mp.acc = !P.fp64 && P.xterms0 == 1 && n_restarts == 2 && 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m;
     P.total_rows += R;
     P.total_sel += mp.k;
   }

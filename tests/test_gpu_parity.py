@@ -500,10 +500,11 @@ def test_rowsubset_carry_equals_raw_at_full_rows(dion):
 
 @pytest.mark.parametrize("sched", [dict(n_iter=12, restart_every=2), dict(n_iter=9, restart_every=2),
                                    dict(n_iter=8, restart_mask=0b1010101)])
-def test_many_restarts_with_accumulated_factor(dion, sched):
-    """Three to five restarts of two-iteration segments with matrices that restart from X0
-    through the accumulated factor (n >= 1.5 m): the schedule whose third restart once needed
-    a seventh m x m buffer.  Row subsets, bf16, against the oracle."""
+def test_many_restarts(dion, sched):
+    """Three to five restarts of two-iteration segments, wide and tall matrices among them
+    (n >= 1.5 m): with more than two restarts every matrix restarts from the two-term iterate,
+    since the accumulated restart factor's rounding would compound.  Row subsets, bf16,
+    against the oracle."""
     rng = np.random.default_rng(41)
     shapes = [(92, 43), (280, 85), (196, 298), (83, 114), (200, 640), (640, 200), (128, 128)]
     Ms = [round_bf16(rng.standard_normal(s).astype(np.float32)) for s in shapes]
