@@ -217,8 +217,11 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
  *                              (DION_LOWRANK_COLNORM, Dion)
  *   out = P Q^T                unscaled (the caller applies lr and shape factors)
  * orth(F) is the reduced QR factor with a positive triangular diagonal,
- * computed as CholeskyQR twice (Gram in fp32, Cholesky factor and its inverse
- * in fp64).  Inputs for which B Q or W has rank below r are outside the
+ * computed as shifted CholeskyQR3 (Gram in fp32, Cholesky factor and its
+ * inverse in fp64; the first of three passes factors the Gram matrix plus
+ * 1e-3 times its largest diagonal entry), which keeps the factor
+ * orthonormal to working precision for F of condition number up to about
+ * 1e7, where plain CholeskyQR2 in fp32 needs about 4e3 at most.  Inputs for which B Q or W has rank below r are outside the
  * method's contract (the factor is not unique): the output is finite but
  * unspecified.
  *   M[i]      device R x C fp32 buffer, updated in place

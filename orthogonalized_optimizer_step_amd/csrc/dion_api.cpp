@@ -1398,15 +1398,16 @@ int check_ptrs(const void* const* M, void* const* out, const dion_shape* shapes,
 // factor normalized by columns (Dion) or by QR (Orth-Dion).  Per matrix,
 // with r = min(rank, R, C):
 //   B = fl32(M + G)                        k_lr_accumulate (M in place)
-//   P = orth(B Q)                          GEMM, then CholeskyQR2
+//   P = orth(B Q)                          GEMM, then shifted CholeskyQR3
 //   W = B^T P                              GEMM
 //   M = B - beta P W^T                     GEMM (beta = -beta, accumulate)
-//   Q = orth(W) or colnorm(W)              CholeskyQR2, or k_lr_colnorm
+//   Q = orth(W) or colnorm(W)              shifted CholeskyQR3, or k_lr_colnorm
 //   out = P Q^T                            GEMM (fp32, cast to bf16/fp16)
-// orth is CholeskyQR run twice: S = F^T F (GEMM), L = chol(S) and L^-1 in
-// fp64 (k_lr_cholinv), F <- F L^-T (GEMM); the triangular factor has a
-// positive diagonal, the QR convention of the oracle.  The rank-r products
-// are plain GEMMs and run in rocBLAS, batched over the matrices of one shape.
+// orth is CholeskyQR run three times, the first on a shifted Gram matrix:
+// S = F^T F (GEMM), L = chol(S (+ shift)) and L^-1 in fp64 (k_lr_cholinv),
+// F <- F L^-T (GEMM); the triangular factor has a positive diagonal, the QR
+// convention of the oracle.  The rank-r products are plain GEMMs and run in
+// rocBLAS, batched over the matrices of one shape.
 constexpr int kMaxRank = 512;
 constexpr size_t kBlasWorkspace = (size_t)32 << 20;
 enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_N };
@@ -1594,38 +1595,44 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
          launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, stream);
          return DION_OK;
        })) != DION_OK) return rc;
-  for (const LrGroup& g : P.groups)   // X = B Q
-    if ((rc = gprod("lr_power", g, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, 0.f, LP_X,
+  for (const LrGroup& g : P.groups)   // Y = B Q
+    if ((rc = gprod("lr_power", g, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, 0.f, LP_Y,
                     4.0 * ((double)g.R * g.C + (double)g.C * g.r + (double)g.R * g.r))) != DION_OK) return rc;
-  // CholeskyQR2 of F (rows x r) through tmp into dst
-  auto cholqr2 = [&](int F, int tmp, int dst, bool rows_are_R) -> int {
-    int src = F;
-    for (int pass = 0; pass < 2; ++pass) {
-      const int to = pass == 0 ? tmp : dst;
+  // shifted CholeskyQR3 of F (rows x r): F -> dst -> tmp -> dst (tmp may be F).
+  // The first pass factors S + 1e-3 max_i S_ii I: an ill-conditioned F (its
+  // fp32 Gram matrix losing the small directions to rounding) then still
+  // gives a factor of condition at most about 30, which two plain passes
+  // (CholeskyQR2) make orthonormal to working precision; a well-conditioned F
+  // is unaffected (shifted CholeskyQR, Fukaya, Kannan, Nakatsukasa, Yamamoto
+  // and Yanagisawa, SIAM J. Sci. Comput. 2020, with a practical shift in
+  // place of their worst-case one)
+  constexpr float kShift = 1e-3f;
+  auto cholqr3 = [&](int F, int tmp, int dst, bool rows_are_R) -> int {
+    const int from[3] = {F, dst, tmp}, to[3] = {dst, tmp, dst};
+    for (int pass = 0; pass < 3; ++pass) {
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
-        const int e = gprod("lr_orth", g, true, false, g.r, g.r, rows, 1.f, src, src, 0.f, LP_S,
+        const int e = gprod("lr_orth", g, true, false, g.r, g.r, rows, 1.f, from[pass], from[pass], 0.f, LP_S,
                             4.0 * ((double)rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
       double rr = 0.0;
       for (int i = 0; i < batch; ++i) rr += (double)P.r[i] * P.r[i];
       int e = phase("lr_cholinv", "dion::k_lr_cholinv", 0.0, rr * 8.0, [&]() {
-        launch_lr_cholinv(d_descs, nmat, any_small, any_large, stream);
+        launch_lr_cholinv(d_descs, nmat, any_small, any_large, pass == 0 ? kShift : 0.f, stream);
         return DION_OK;
       });
       if (e != DION_OK) return e;
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
-        e = gprod("lr_orth", g, false, true, rows, g.r, g.r, 1.f, src, LP_L, 0.f, to,
+        e = gprod("lr_orth", g, false, true, rows, g.r, g.r, 1.f, from[pass], LP_L, 0.f, to[pass],
                   4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
-      src = to;
     }
     return DION_OK;
   };
-  if ((rc = cholqr2(LP_X, LP_Y, LP_X, true)) != DION_OK) return rc;   // P
+  if ((rc = cholqr3(LP_Y, LP_Y, LP_X, true)) != DION_OK) return rc;   // P = orth(Y), in X
   for (const LrGroup& g : P.groups)   // W = B^T P
     if ((rc = gprod("lr_right", g, true, false, g.C, g.r, g.R, 1.f, LP_M, LP_X, 0.f, LP_W,
                     4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
@@ -1633,7 +1640,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     if ((rc = gprod("lr_feedback", g, false, true, g.R, g.C, g.r, -beta, LP_X, LP_W, 1.f, LP_M,
                     4.0 * (2.0 * g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   if (mode == DION_LOWRANK_QR) {
-    if ((rc = cholqr2(LP_W, LP_W2, LP_Q, false)) != DION_OK) return rc;
+    if ((rc = cholqr3(LP_W, LP_W2, LP_Q, false)) != DION_OK) return rc;
   } else {
     double cr = 0.0;
     for (int i = 0; i < batch; ++i) cr += (double)P.C[i] * P.r[i];

@@ -13,8 +13,8 @@ struct LrDesc {
   const void* G;     // R x C gradient
   float* Q;          // C x r right factor (in: previous, out: new)
   void* out;         // R x C update
-  float* X;          // R x r  P (and its first CholeskyQR pass input)
-  float* Y;          // R x r  CholeskyQR intermediate
+  float* X;          // R x r  P = orth(B Q)
+  float* Y;          // R x r  B Q, then a CholeskyQR intermediate
   float* W;          // C x r  right factor before normalization
   float* W2;         // C x r  CholeskyQR intermediate of W
   float* S;          // r x r  Gram of the factor being orthogonalized
@@ -34,7 +34,9 @@ constexpr int LR_REG_RMAX = 256;
 
 void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, hipStream_t s);
 void launch_lr_cast(const LrDesc* d, int nmat, int64_t blocks, int out_fmt, hipStream_t s);
-void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, hipStream_t s);
+// shift > 0: factor S + shift * (largest diagonal entry of S) * I (the first,
+// shifted pass of shifted CholeskyQR3)
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, hipStream_t s);
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
 
 }  // namespace dion

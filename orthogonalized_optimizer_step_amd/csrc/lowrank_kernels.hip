@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void k_lr_cast(const LrDesc* __restrict__ desc
 // contract): its column of L^-1 and of the result is zero, which keeps every
 // value finite.  The inverse is column-wise forward substitution, one column
 // per thread, X = L^-1 kept transposed in the upper triangle of the scratch.
-__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs) {
+__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, float shift) {
   const LrDesc& d = descs[blockIdx.x];
   const int r = d.r;
   if (r <= LR_REG_RMAX) return;   // k_lr_cholinv_reg
@@ -131,6 +131,10 @@ __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ d
     __syncthreads();
   }
   const double tiny = 1e-14 * red[0];
+  // shifted pass: S + shift * max_i S_ii * I (every thread has read red[0]
+  // before the first barrier of the loop below, which orders these writes)
+  if (shift > 0.f)
+    for (int i = tid; i < r; i += 256) A[(size_t)i * r + i] += (double)shift * red[0];
 
   for (int j = 0; j < r; ++j) {
     for (int k = tid; k < j; k += 256) rowj[k] = A[(size_t)j * r + k];
@@ -189,7 +193,7 @@ constexpr int LR_NB = LR_REG_RMAX / LR_GRID;
 constexpr int LR_SLOTS = LR_NB * (LR_NB + 1) / 2;
 static_assert(LR_GRID * LR_GRID == LR_REG_THREADS, "thread grid");
 
-__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs) {
+__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, float shift) {
   const LrDesc& d = descs[blockIdx.x];
   const int r = d.r;
   if (r > LR_REG_RMAX) return;    // k_lr_cholinv
@@ -222,6 +226,7 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
   double big = 0.0;
   for (int w = 0; w < LR_REG_THREADS / 64; ++w) big = fmax(big, red[w]);
   const double tiny = 1e-14 * big;
+  if (shift > 0.f) LR_FOR_SLOTS({ if (own && i == c) v[sl] += (double)shift * big; })
 
   for (int k = 0; k < r; ++k) {
     LR_FOR_SLOTS({ if (own && i == k && c == k) s_piv = v[sl]; })
@@ -290,9 +295,9 @@ void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fm
 void launch_lr_cast(const LrDesc* d, int nmat, int64_t blocks, int out_fmt, hipStream_t s) {
   if (blocks > 0) hipLaunchKernelGGL(k_lr_cast, dim3((unsigned)blocks), dim3(256), 0, s, d, nmat, out_fmt);
 }
-void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, hipStream_t s) {
-  if (nmat > 0 && any_small) hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d);
-  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d);
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, hipStream_t s) {
+  if (nmat > 0 && any_small) hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, shift);
+  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, shift);
 }
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s) {
   if (nmat > 0) hipLaunchKernelGGL(k_lr_colnorm, dim3(nmat), dim3(256), 0, s, d);

@@ -43,7 +43,7 @@ void launch_tiny_gns(const MatDesc*, int, const MatScalars*, const int*, const d
 }
 void launch_lr_accumulate(const LrDesc*, int, int64_t, int, hipStream_t) { std::abort(); }
 void launch_lr_cast(const LrDesc*, int, int64_t, int, hipStream_t) { std::abort(); }
-void launch_lr_cholinv(const LrDesc*, int, bool, bool, hipStream_t) { std::abort(); }
+void launch_lr_cholinv(const LrDesc*, int, bool, bool, float, hipStream_t) { std::abort(); }
 void launch_lr_colnorm(const LrDesc*, int, hipStream_t) { std::abort(); }
 }  // namespace dion
 

@@ -1,4 +1,4 @@
-"""A randomized sweep of the batched call against the fp64 oracle.
+"""A randomized sweep of the batched call and the row-subset step against the fp64 oracle.
 
 Shapes, schedule (restart period, mask or threshold), safety factor, row
 fraction, element type, precision and keep_schedule are drawn from a fixed
@@ -14,12 +14,13 @@ import pytest
 torch = pytest.importorskip("torch")
 
 from oracle import dion_oracle as O  # noqa: E402
-from workloads import lowrank_np  # noqa: E402
+from workloads import lowrank_np, round_bf16  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
 DIMS = [1, 3, 17, 64, 65, 128, 200, 255, 256, 257, 384, 511, 600]
-N_CASES = 40
+N_CASES = 300
+N_STEP_CASES = 100
 
 
 @pytest.fixture(scope="module")
@@ -83,3 +84,91 @@ def test_random_config(dion, case):
         err = O.rel_frobenius(got[got_idx], ref[got_idx]) if np.array_equal(got_idx, ref_idx) else \
             O.rel_frobenius(got[ref_idx], ref[ref_idx])
         assert err <= tol, (s, dt, prec, keep, kw, err)
+
+
+def near_tie(got_idx, ref_idx, M):
+    """The selections agree, or differ only by rows whose fp64 keys agree to 4 ulps."""
+    if np.array_equal(got_idx, ref_idx):
+        return True
+    keys = O.row_keys(M)
+    diff = np.setxor1d(got_idx, ref_idx)
+    assert np.max(keys[diff]) - np.min(keys[diff]) <= 4 * np.spacing(np.max(keys[diff])), diff
+    return False
+
+
+@pytest.mark.parametrize("case", range(N_STEP_CASES))
+def test_random_rowsubset_steps(dion, case):
+    """Two consecutive row-subset steps: the fp32 buffer bit-exact (both error-feedback
+    forms), indices as the oracle's, unselected rows exact, selected rows within 2e-2."""
+    rng = np.random.default_rng([8, case])
+    shapes = [(int(rng.choice(DIMS)), int(rng.choice(DIMS))) for _ in range(int(rng.integers(1, 5)))]
+    _, kw, _, _, keep = draw(case + 1000)
+    kw["row_frac"] = float(rng.choice([1.0, 0.5, 0.25, 1.0 / 3, 0.125]))
+    if keep and longest_run(dion, kw) > 5:
+        keep = False
+    ef = str(rng.choice(["raw", "carry"]))
+    gdt = str(rng.choice(["bf16", "fp32"]))
+    beta = float(rng.choice([0.9, 0.95]))
+    print(f"step case {case}: {shapes} grad {gdt} ef={ef} beta={beta} keep={keep} {kw}", flush=True)
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    for t in range(2):
+        G = []
+        for j, (r, c) in enumerate(shapes):
+            g = lowrank_np((8, case, t, j), r, c, max(1, min(r, c) // 8), 0.05, log_scale=(-3.0, 0.0))
+            G.append(round_bf16(g) if gdt == "bf16" else g.astype(np.float32))
+        G_dev = [torch.from_numpy(np.ascontiguousarray(g)).cuda().to(torch.bfloat16 if gdt == "bf16" else torch.float32)
+                 for g in G]
+        outs, idxs = dion.rowsubset_step(E_dev, G_dev, beta, return_indices=True, ef=ef, keep_schedule=keep, **kw)
+        newE, ref_outs, ref_idxs = O.rowsubset_step(E_host, G, beta, ef=ef, **kw)
+        for i, s in enumerate(shapes):
+            B = np.add(np.multiply(np.float32(beta), E_host[i], dtype=np.float32) if ef == "raw" else E_host[i], G[i],
+                       dtype=np.float32)
+            got_idx = idxs[i].cpu().numpy().astype(np.int64)
+            same = near_tie(got_idx, ref_idxs[i], B)
+            E_got = E_dev[i].cpu().numpy()
+            if same:
+                assert np.array_equal(E_got.view(np.uint32), newE[i].view(np.uint32)), (s, t, "buffer")
+            got = outs[i].float().cpu().numpy().astype(np.float64)
+            rest = np.setdiff1d(np.arange(s[0]), got_idx)
+            want_rest = round_bf16(B[rest]).astype(np.float64) if ef == "raw" else np.zeros((len(rest), s[1]))
+            assert np.array_equal(got[rest], want_rest), (s, t, "unselected rows")
+            err = O.rel_frobenius(got[ref_idxs[i]], ref_outs[i][ref_idxs[i]])
+            assert err <= 2e-2, (s, t, gdt, ef, keep, kw, err)
+            E_host[i] = E_got   # continue from the device's buffer (identical unless a near-tie exchanged rows)
+
+
+N_LOWRANK_CASES = 40
+
+
+@pytest.mark.parametrize("case", range(N_LOWRANK_CASES))
+def test_random_lowrank_step(dion, case):
+    """The low-rank Dion / Orth-Dion step on random shapes, ranks, beta, modes and
+    gradient types: buffer (relative to ||B||), right factor and fp32 update within 1e-4."""
+    from oracle import orthdion_oracle as L
+    rng = np.random.default_rng([9, case])
+    shapes = [(int(rng.choice(DIMS[1:])), int(rng.choice(DIMS[1:]))) for _ in range(int(rng.integers(1, 5)))]
+    rank = int(rng.choice([1, 4, 16, 33, 64, 128]))
+    beta = float(rng.choice([0.0, 0.1, 0.5, 1.0]))
+    mode = str(rng.choice(["qr", "colnorm"]))
+    gdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[str(rng.choice(["bf16", "fp16", "fp32"]))]
+    print(f"lowrank case {case}: {shapes} rank {rank} beta {beta} {mode} {gdt}", flush=True)
+    Ms, Gs, Qs = [], [], []
+    for R, C in shapes:
+        r = min(rank, R, C)
+        A = rng.standard_normal((R, 8)) @ rng.standard_normal((8, C)) + 0.3 * rng.standard_normal((R, C))
+        Ms.append(A.astype(np.float32))
+        Gs.append(torch.from_numpy((0.5 * rng.standard_normal((R, C))).astype(np.float32)).to(gdt))
+        Qs.append(rng.standard_normal((C, r)).astype(np.float32))
+    dM = [torch.from_numpy(M.copy()).cuda() for M in Ms]
+    dQ = [torch.from_numpy(Q.copy()).cuda() for Q in Qs]
+    outs = dion.lowrank_step(dM, [g.cuda() for g in Gs], dQ, beta, mode=mode, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for i, s in enumerate(shapes):
+        G = Gs[i].float().numpy()
+        M_ref, Q_ref, _, D_ref = L.lowrank_step(Ms[i], G, Qs[i], beta, mode)
+        B = L.accumulate(Ms[i], G).astype(np.float64)
+        eb = float(np.linalg.norm(dM[i].cpu().numpy().astype(np.float64) - M_ref) / max(np.linalg.norm(B), 1e-300))
+        eq = O.rel_frobenius(dQ[i].cpu().numpy().astype(np.float64), Q_ref)
+        ed = O.rel_frobenius(outs[i].cpu().numpy().astype(np.float64), D_ref)
+        assert max(eb, eq, ed) <= 1e-4, (s, rank, beta, mode, gdt, eb, eq, ed)

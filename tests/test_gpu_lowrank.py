@@ -3,7 +3,7 @@ fp64 oracle.
 
 Gates: the accumulated buffer B = fl32(M + G) bit-exact (checked with beta = 0,
 where the buffer is B); the new right factor and an fp32 update within 1e-4
-relative Frobenius error of the oracle (fp32 GEMMs and CholeskyQR2 with an
+relative Frobenius error of the oracle (fp32 GEMMs and shifted CholeskyQR3 with an
 fp64 Cholesky factor); the new buffer B - beta P W^T within 1e-4 of ||B||, the
 scale of its operands (at full rank and beta = 1 it is zero up to rounding, so
 an error relative to itself says nothing); a bf16 update within its rounding
