@@ -292,7 +292,7 @@ def apply(Qs, Xs, precision="auto", stream=None):
 
 def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=QUINTIC, n_iter=5,
                           restart_every=0, restart_mask=0, safety=1.0, row_frac=0.125, return_indices=False,
-                          stream=None, restart_threshold=0.0, ef="raw"):
+                          stream=None, restart_threshold=0.0, ef="raw", keep_schedule=False):
     """One row-subset step fused with the weight update; E and W are updated in place."""
     import torch
     _check_tensors(Es, torch.float32)
@@ -300,7 +300,7 @@ def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=
     _check_tensors(Ws, Ws[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
-                          restart_threshold=restart_threshold, ef=ef)
+                          restart_threshold=restart_threshold, ef=ef, keep_schedule=keep_schedule)
     sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
     orth.step_update(Es, grads, Ws, beta, alphas, weight_decay, sel, stream)
     if not return_indices:

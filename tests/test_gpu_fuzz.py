@@ -172,3 +172,57 @@ def test_random_lowrank_step(dion, case):
         eq = O.rel_frobenius(dQ[i].cpu().numpy().astype(np.float64), Q_ref)
         ed = O.rel_frobenius(outs[i].cpu().numpy().astype(np.float64), D_ref)
         assert max(eb, eq, ed) <= 1e-4, (s, rank, beta, mode, gdt, eb, eq, ed)
+
+
+N_UPDATE_CASES = 40
+
+
+@pytest.mark.parametrize("case", range(N_UPDATE_CASES))
+def test_random_fused_update(dion, case):
+    """The row-subset step with the fused weight update on random draws: buffer, indices
+    and the unselected weight rows bit-exact (both error-feedback forms, bf16 or fp32
+    weights); selected rows within 2e-2 of the oracle's update (plus bf16 rounding)."""
+    rng = np.random.default_rng([10, case])
+    shapes = [(int(rng.choice(DIMS)), int(rng.choice(DIMS))) for _ in range(int(rng.integers(1, 5)))]
+    _, kw, _, _, keep_s = draw(case + 2000)
+    kw["row_frac"] = float(rng.choice([1.0, 0.5, 0.25, 1.0 / 3, 0.125]))
+    if keep_s and longest_run(dion, kw) > 5:
+        keep_s = False
+    ef = str(rng.choice(["raw", "carry"]))
+    wbf16 = bool(rng.integers(0, 2))
+    beta, wd = float(rng.choice([0.9, 0.95])), float(rng.choice([0.0, 0.01, 0.1]))
+    alphas = [float(rng.choice([0.01, 0.02])) * float(np.sqrt(max(1.0, r / c))) for r, c in shapes]
+    print(f"update case {case}: {shapes} wbf16={wbf16} ef={ef} wd={wd} keep={keep_s} {kw}", flush=True)
+    W_host = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    if wbf16:
+        W_host = [O.round_to_bf16(w) for w in W_host]
+    W_dev = [torch.from_numpy(w).cuda().to(torch.bfloat16 if wbf16 else torch.float32) for w in W_host]
+    E_host = [np.zeros(s, np.float32) for s in shapes]
+    E_dev = [torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes]
+    keep = float(np.float32(1.0) - np.float32(wd))
+    for t in range(2):
+        G = [round_bf16(lowrank_np((10, case, t, j), r, c, max(1, min(r, c) // 8), 0.05, log_scale=(-3.0, 0.0)))
+             for j, (r, c) in enumerate(shapes)]
+        G_dev = [torch.from_numpy(np.ascontiguousarray(g)).cuda().to(torch.bfloat16) for g in G]
+        _, idxs = dion.rowsubset_step_update(E_dev, G_dev, W_dev, beta, alphas, wd, return_indices=True, ef=ef,
+                                             keep_schedule=keep_s, **kw)
+        newE, newW, ref_idxs = O.rowsubset_step_update(E_host, G, W_host, beta, alphas, wd, bf16=wbf16, ef=ef, **kw)
+        for i, s in enumerate(shapes):
+            B = np.add(np.multiply(np.float32(beta), E_host[i], dtype=np.float32) if ef == "raw" else E_host[i], G[i],
+                       dtype=np.float32)
+            got_idx = idxs[i].cpu().numpy().astype(np.int64)
+            if near_tie(got_idx, ref_idxs[i], B):
+                assert np.array_equal(E_dev[i].cpu().numpy().view(np.uint32), newE[i].view(np.uint32)), (s, t)
+                got = W_dev[i].float().cpu().numpy().astype(np.float64)
+                ix = ref_idxs[i]
+                rest = np.setdiff1d(np.arange(s[0]), ix)
+                assert np.array_equal(got[rest], newW[i][rest]), (s, t, "unselected weight rows")
+                base = W_host[i][ix].astype(np.float64) * keep
+                d_ref = newW[i][ix] - base
+                if wbf16:
+                    err = np.linalg.norm(got[ix] - newW[i][ix])
+                    assert err <= 2.0 ** -9 * 1.01 * np.linalg.norm(newW[i][ix]) + 2e-2 * np.linalg.norm(d_ref), (s, t)
+                else:
+                    assert O.rel_frobenius(got[ix] - base, d_ref) <= 2e-2, (s, t)
+        E_host = [e.cpu().numpy() for e in E_dev]
+        W_host = [w.float().cpu().numpy() for w in W_dev]
