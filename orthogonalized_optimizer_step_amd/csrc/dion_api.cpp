@@ -622,8 +622,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   float sQ = 1.f, sXT = 1.f;
   double qb = 1.0;
   int n_rest = 0;         // restarts taken so far
-  int qa_slot = -1;       // accumulated factor S = Q_r ... Q_1 (matrices restarting from X0)
-  int qat_slot = -1;      // S^T (hi term), or qa_slot when S is exactly symmetric
+  int qa_slot = -1;       // accumulated factor: Q_1, then S = Q_2 Q_1 (matrices restarting from X0)
+  int qat_slot = -1;      // Q_1^T (hi term), or qa_slot when Q_1 is exactly symmetric
   int pending_qat = -1;   // Q_1^T written by the product that forms Q_1
   float sQA = 1.f;
   double qab = 1.0;
@@ -700,8 +700,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.alpha = sQn / (sP * sQ);
       if (short_seg && any_acc && k < K && xr[k - 1] && n_rest == 0) {
         // this Q starts the accumulated factor of the matrices restarting
-        // from X0; their next accumulation multiplies by it from the right,
-        // which reads its rows as columns: keep Q^T (hi) as well
+        // from X0; the accumulation at the second restart multiplies by it
+        // from the right, which reads its rows as columns: keep Q^T (hi) as well
         pending_qat = take();
         PhaseArgs pt = pa;
         pt.aux_slot = pending_qat;
@@ -757,28 +757,21 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         apply(t_xtq_acc, xt_slot, xterms, q_slot, al, alp, xt_lo_acc);
         if (P.tabs[t_xtq_nacc].nmat) apply(t_xtq_nacc, xt_slot, xterms, q_slot, al, alp, xt_lo);
       } else {
-        // matrices restarting from X0: S <- Q S (a full one-term product in
-        // this order, outside the useful count; it reads S^T by rows and
-        // writes S^T too when a later restart needs it), then X'^T = X0^T S^T
+        // the second (and last) restart of the matrices restarting from X0:
+        // S = Q_2 Q_1 (a full one-term product in this order, outside the
+        // useful count; it reads Q_1^T by rows), then X'^T = X0^T S^T
         const double qab_new = qab * qb;
         const float sQAn = sc(qab_new);
-        const bool more = n_rest < n_restarts;
         const int qa_new = take();
-        int qat_new = qa_new;
-        if (more) {
-          qat_new = take();
-        }
         PhaseArgs pq{};
         pq.a_slot = q_slot;
         pq.b_slot = qat_slot;
         pq.c_slot = qa_new;
-        pq.aux_slot = qat_new;
         pq.alpha = sQAn / (sQ * sQA);
-        gemm(t_full_acc, bm_full, false, 1, 1, more ? EPI_RECT_T : EPI_RECT, pq, "acc_product", false, false);
+        gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
         freel.push_back(qa_slot);
         if (qat_slot != qa_slot) freel.push_back(qat_slot);
-        qa_slot = qa_new;
-        qat_slot = qat_new;
+        qa_slot = qat_slot = qa_new;
         sQA = sQAn;
         qab = qab_new;
         apply(t_xtq_acc, SLOT_XT0, 1, qa_slot, sXn / sQA, 1, xt_lo_acc);
