@@ -47,8 +47,8 @@ void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t r
 void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total, int slot,
                    const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
-void launch_tiny_gns(const MatDesc* descs, int nmat, const MatScalars* scalars, const int* idx, const double* coef,
-                     int K, unsigned long long restarts, int fmt, hipStream_t s);
+void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
+                     const double* coef, int K, unsigned long long restarts, int fmt, hipStream_t s);
 // matrices with Gram side m <= 64 and long side n <= 1024 run in one launch
 constexpr int kTinyM = 64, kTinyN = 1024;
 }  // namespace dion
@@ -220,7 +220,9 @@ struct Plan {
   std::vector<MatScalars> hscal;
   // every matrix small: the whole iteration in one launch (k_tiny_gns), with
   // the per-iteration coefficients (fp64, as int pairs) at ints[coef_off]
-  bool tiny = false;
+  bool tiny = false;      // every matrix takes k_tiny_gns: the plan is that one launch
+  int ntiny = 0;          // matrices taking k_tiny_gns; their ids at ints[tiny_ids_off]
+  size_t tiny_ids_off = 0;
   size_t coef_off = 0;
   unsigned long long restarts = 0;
   int K = 0;
@@ -367,12 +369,23 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.off_descs = off;
   off = align256(off + sizeof(MatDesc) * batch);
 
-  // tables
-  std::vector<int> all(batch);
-  for (int i = 0; i < batch; ++i) all[i] = i;
+  // Matrices small enough for the one-workgroup fp64 kernel (k_tiny_gns)
+  // take it: all of them, and the plan is that one launch, or some, and they
+  // take it beside the GEMM phases of the others (the "mf" list below).  On
+  // the MFMA path they would occupy 256-row tiles for a few rows, and a Gram
+  // side of a few rows cannot average out the fp16 rounding of its small
+  // singular direction (errors near 2e-2 for two rows).
+  std::vector<int> mf, tiny_ids;
+  for (int i = 0; i < batch; ++i) {
+    const MatPlan& mp = P.mats[i];
+    (!step_mode && K <= 64 && mp.m <= kTinyM && mp.n <= kTinyN ? tiny_ids : mf).push_back(i);
+  }
+  P.tiny = mf.empty();
+
+  // tables of the GEMM phases, over mf
   auto sym_counts = [&](int bm) {
-    std::vector<int> c(batch);
-    for (int i = 0; i < batch; ++i) { int T = P.mats[i].m_pad / bm; c[i] = T * (T + 1) / 2; }
+    std::vector<int> c;
+    for (int i : mf) { int T = P.mats[i].m_pad / bm; c.push_back(T * (T + 1) / 2); }
     return c;
   };
   auto rect_counts = [&](const std::vector<int>& ms, int bm, bool rows_n) {
@@ -390,25 +403,25 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     return total_of(counts(256)) >= 512 ? 256 : 128;
   };
   const int bm_sym = pick_bm([&](int bm) { return sym_counts(bm); });
-  const int bm_xtq = pick_bm([&](int bm) { return rect_counts(all, bm, true); });
+  const int bm_xtq = pick_bm([&](int bm) { return rect_counts(mf, bm, true); });
   auto full_counts = [&](int bm) {
-    std::vector<int> c(batch);
-    for (int i = 0; i < batch; ++i) { int T = P.mats[i].m_pad / bm; c[i] = T * T; }
+    std::vector<int> c;
+    for (int i : mf) { int T = P.mats[i].m_pad / bm; c.push_back(T * T); }
     return c;
   };
   const int bm_full = pick_bm([&](int bm) { return full_counts(bm); });
   std::vector<int> wide, tall, accs, naccs;
-  for (int i = 0; i < batch; ++i) (P.mats[i].tall ? tall : wide).push_back(i);
-  for (int i = 0; i < batch; ++i) (P.mats[i].acc ? accs : naccs).push_back(i);
+  for (int i : mf) (P.mats[i].tall ? tall : wide).push_back(i);
+  for (int i : mf) (P.mats[i].acc ? accs : naccs).push_back(i);
   const bool any_acc = !accs.empty();
   const int bm_fin = pick_bm([&](int bm) {
     auto a = rect_counts(wide, bm, false), b = rect_counts(tall, bm, true);
     a.insert(a.end(), b.begin(), b.end());
     return a;
   });
-  const int t_sym = add_table(P, all, sym_counts(bm_sym));
-  const int t_xtq = add_table(P, all, rect_counts(all, bm_xtq, true));
-  const int t_full = add_table(P, all, full_counts(bm_full));
+  const int t_sym = add_table(P, mf, sym_counts(bm_sym));
+  const int t_xtq = add_table(P, mf, rect_counts(mf, bm_xtq, true));
+  const int t_full = add_table(P, mf, full_counts(bm_full));
   const int t_wide = add_table(P, wide, rect_counts(wide, bm_fin, false));
   const int t_tall = add_table(P, tall, rect_counts(tall, bm_fin, true));
   // restarts after the first: matrices that restart from X0 and the others
@@ -421,18 +434,22 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   const int t_xtq_nacc = add_table(P, naccs, rect_counts(naccs, bm_xtq, true));
   const int t_full_acc = add_table(P, accs, sub_full(accs, bm_full));
   const int t_full_nacc = add_table(P, naccs, sub_full(naccs, bm_full));
-  std::vector<int> pack_c(batch), tr_c(batch);
+  // pack and transpose tables over every matrix: those kernels take the
+  // table's matrices as batch indices 0 .. n-1.  The small matrices' share is
+  // wasted but harmless: it runs after k_tiny_gns has finished with their
+  // buffers, and nothing reads it
+  std::vector<int> all(batch), pack_c(batch);
   for (int i = 0; i < batch; ++i) {
-    const MatPlan& mp = P.mats[i];
-    pack_c[i] = (mp.m_pad / 64) * (mp.n_pad / 64);  // k_pad * C_pad = m_pad * n_pad either way
-    tr_c[i] = pack_c[i];
+    all[i] = i;
+    pack_c[i] = (P.mats[i].m_pad / 64) * (P.mats[i].n_pad / 64);  // k_pad C_pad = m_pad n_pad either way
   }
   const int t_pack = add_table(P, all, pack_c);
-  const int t_tr = add_table(P, all, tr_c);
+  const int t_tr = add_table(P, all, pack_c);
   P.K = K;
-  P.tiny = !step_mode && K <= 64;
-  for (const MatPlan& mp : P.mats) P.tiny = P.tiny && mp.m <= kTinyM && mp.n <= kTinyN;
-  if (P.tiny) {
+  if (!tiny_ids.empty()) {
+    P.ntiny = (int)tiny_ids.size();
+    P.tiny_ids_off = P.ints.size();
+    P.ints.insert(P.ints.end(), tiny_ids.begin(), tiny_ids.end());
     if (P.ints.size() & 1) P.ints.push_back(0);   // 8-byte alignment of the fp64 table
     P.coef_off = P.ints.size();
     for (int k = 0; k < K; ++k)
@@ -493,12 +510,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   st.name = "select";
   st.bytes = rows * 8 * (P.use_idx ? 10 : 1) + rows;
   P.steps.push_back(st);
-  if (P.tiny) {
+  if (P.ntiny) {
     // useful FLOPs per segment of length L: n m (m + 1) + 2 m^2 n + (4L - 3) m^2 (m + 1)
     st = Step();
     st.kind = ST_TINY;
     st.name = "tiny";
-    for (const MatPlan& mp : P.mats) {
+    for (int i : tiny_ids) {
+      const MatPlan& mp = P.mats[i];
       const double m = mp.m, n = mp.n;
       int k0 = 0;
       for (int k = 1; k <= K; ++k)
@@ -511,6 +529,8 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     }
     st.raw = st.useful;
     P.steps.push_back(st);
+  }
+  if (P.tiny) {
     if (P.use_idx) {
       Step cp;
       cp.kind = ST_COPY;
@@ -1331,8 +1351,8 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         launch_decay_selected(d_descs, batch, P.total_sel, P.use_idx ? d_idx : nullptr, beta, stream);
         break;
       case ST_TINY:
-        launch_tiny_gns(d_descs, batch, d_scal, P.use_idx ? d_idx : nullptr, (const double*)(d_ints + P.coef_off),
-                        P.K, P.restarts, fmt, stream);
+        launch_tiny_gns(d_descs, d_ints + P.tiny_ids_off, P.ntiny, d_scal, P.use_idx ? d_idx : nullptr,
+                        (const double*)(d_ints + P.coef_off), P.K, P.restarts, fmt, stream);
         break;
       case ST_COPY:
         launch_copy_unselected(fmt != 1, d_descs, batch, P.total_rows, d_flags, stream);

@@ -3,9 +3,10 @@
 // P = aI + bG + cG^2, Q <- P Q, and G <- P G P or, at a restart, X <- Q X,
 // G <- X X^T, Q <- I; out = Q X).
 //
-// When every matrix's Gram side m is at most 64 (and its long side at most
-// 1024), the GEMM phases would be some twenty launches of one or three tiles
-// each, so the call is bound by launch latency.  Here one workgroup per matrix
+// For matrices whose Gram side m is at most 64 (and long side at most 1024)
+// the GEMM phases would be some twenty launches of a tile or three each, so a
+// call of only such matrices is bound by launch latency, and beside larger
+// ones they would take 256-row tiles for a few rows.  Here one workgroup per matrix
 // runs the whole iteration in fp64: the m x m matrices G, P, Q and a temporary
 // live in LDS (four 64 x 64 fp64 buffers, 128 KB, plus a 16 KB staging chunk
 // for the Gram), the iterate X (m x n, fp64) in two workspace buffers that
@@ -51,17 +52,20 @@ __device__ __forceinline__ int tiny_free(int x, int y, int z) {
 
 }  // namespace
 
-// coef: K triples (a, b, c) in fp64 with the safety factor folded in;
+// ids: the batch indices of the matrices this launch covers, one workgroup
+// each; coef: K triples (a, b, c) in fp64 with the safety factor folded in;
 // restarts: bit k-1 set = restart after iteration k.
 __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __restrict__ descs,
+                                                           const int* __restrict__ ids,
                                                            const MatScalars* __restrict__ scalars,
                                                            const int* __restrict__ idx,
                                                            const double* __restrict__ coef, int K,
                                                            unsigned long long restarts, int fmt) {
-  const MatDesc& d = descs[blockIdx.x];
+  const int mi = ids[blockIdx.x];
+  const MatDesc& d = descs[mi];
   const int m = d.m, n = d.n;
   const int tid = threadIdx.x;
-  const double nu2 = scalars[blockIdx.x].nu2;        // ||S||_F^2 from the selection
+  const double nu2 = scalars[mi].nu2;                // ||S||_F^2 from the selection
   const double s = nu2 > 0.0 ? 1.0 / sqrt(nu2) : 0.0;
   __shared__ double buf[4][TINY_M * TINY_M];          // row-major, ld TINY_M
   double* X = (double*)d.buf[SLOT_X];                 // m x n, ld n
@@ -191,10 +195,11 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
   });
 }
 
-void launch_tiny_gns(const MatDesc* descs, int nmat, const MatScalars* scalars, const int* idx, const double* coef,
-                     int K, unsigned long long restarts, int fmt, hipStream_t s) {
-  if (nmat > 0)
-    hipLaunchKernelGGL(k_tiny_gns, dim3(nmat), dim3(TINY_THREADS), 0, s, descs, scalars, idx, coef, K, restarts, fmt);
+void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
+                     const double* coef, int K, unsigned long long restarts, int fmt, hipStream_t s) {
+  if (ntiny > 0)
+    hipLaunchKernelGGL(k_tiny_gns, dim3(ntiny), dim3(TINY_THREADS), 0, s, descs, ids, scalars, idx, coef, K, restarts,
+                       fmt);
 }
 
 }  // namespace dion

@@ -37,7 +37,7 @@ void launch_unpack(bool, const MatDesc*, const int*, int, int, int, const MatSca
   std::abort();
 }
 void launch_scale_combine(MatScalars*, int, hipStream_t) { std::abort(); }
-void launch_tiny_gns(const MatDesc*, int, const MatScalars*, const int*, const double*, int, unsigned long long, int,
+void launch_tiny_gns(const MatDesc*, const int*, int, const MatScalars*, const int*, const double*, int, unsigned long long, int,
                      hipStream_t) {
   std::abort();
 }

@@ -226,3 +226,27 @@ def test_random_fused_update(dion, case):
                     assert O.rel_frobenius(got[ix] - base, d_ref) <= 2e-2, (s, t)
         E_host = [e.cpu().numpy() for e in E_dev]
         W_host = [w.float().cpu().numpy() for w in W_dev]
+
+
+def test_large_megabatch(dion):
+    """One call over 400 matrices of mixed shapes (1 ... 600 per side): the megabatch's
+    tile tables, matrix lookup and per-XCD tile ranges at a size where every phase spans
+    hundreds of matrices; every output against the oracle."""
+    rng = np.random.default_rng(11)
+    shapes = [(int(rng.choice(DIMS)), int(rng.choice(DIMS))) for _ in range(400)]
+    kw = dict(n_iter=5, restart_every=2, row_frac=0.5)
+    Ms = [lowrank_np((11, j), r, c, max(1, min(r, c) // 8), 0.1, log_scale=(-3.0, 0.0)) for j, (r, c) in enumerate(shapes)]
+    dev = [torch.from_numpy(M).to(torch.bfloat16).cuda() for M in Ms]
+    outs, idxs = dion.orth_batched(dev, return_indices=True, **kw)
+    worst = 0.0
+    for M_dev, o, idx, s in zip(dev, outs, idxs, shapes):
+        M = M_dev.float().cpu().numpy()
+        ref, ref_idx = O.orthogonalize(M, **kw)
+        got_idx = idx.cpu().numpy().astype(np.int64)
+        if near_tie(got_idx, ref_idx, M):
+            got = o.float().cpu().numpy().astype(np.float64)
+            rest = np.setdiff1d(np.arange(s[0]), got_idx)
+            assert np.array_equal(got[rest], M[rest].astype(np.float64)), s
+            worst = max(worst, O.rel_frobenius(got[got_idx], ref[got_idx]))
+    print(f"400 matrices: worst {worst:.2e}", flush=True)
+    assert worst <= 2e-2
