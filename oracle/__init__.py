@@ -17,6 +17,7 @@ from .dion_oracle import (  # noqa: F401
     rel_frobenius,
     restart_points,
     row_keys,
+    row_keys_fsum,
     round_to_bf16,
     rowsubset_step,
     rowsubset_step_update,

@@ -34,8 +34,10 @@ formula, selection criterion or worked example.  The readings taken here are:
       f_s(x) = f(x / s), i.e. (a, b, c) -> (a/s, b/s^3, c/s^5).
   R5  A restart after iteration k (never after the last) re-forms the Gram
       matrix from the current iterate X_k = Q X and resets Q to I.
-  R6  Rows are ranked by squared L2 norm (fp64, from the exact stored values),
-      larger first, ties to the lower row index; k = ceil(row_frac * R),
+  R6  Rows are ranked by squared L2 norm: the exact sum of the squares of the
+      stored values rounded once to the nearest double (ties to even), so the
+      ranking does not depend on a summation order; larger first, ties (equal
+      doubles) to the lower row index; k = ceil(row_frac * R),
       clamped to [1, R]; selected rows are processed in ascending order.
   R7  No output scaling (learning rate and shape factors belong to the
       weight update).
@@ -142,9 +144,37 @@ def restart_points(n_iter: int, restart_every: int = 0, restart_mask: int = 0,
 # Row selection (reading R6)
 # --------------------------------------------------------------------------
 def row_keys(M) -> np.ndarray:
-    """Squared L2 norm of every row, in fp64, from the exact stored values."""
+    """Squared L2 norm of every row (R6): the exact sum of the squares of the
+    stored values, rounded once to the nearest double (ties to even).
+
+    A correctly rounded sum does not depend on the order of summation, so the
+    selection it decides is the same for every implementation that rounds the
+    exact sum once.  For float32 values (the stored bf16, fp16 and fp32
+    inputs) it is computed with integer arithmetic in the oracle's C part
+    (exact_keys.c); other doubles go through ``row_keys_fsum``, the same
+    definition through Python's correctly rounded ``math.fsum``.  The two are
+    pinned equal.
+    """
+    A = np.asarray(M)
+    with np.errstate(over="ignore", invalid="ignore"):
+        A32 = np.ascontiguousarray(A, dtype=np.float32)
+    if A.dtype == np.float32 or np.array_equal(A32.astype(A.dtype), A):
+        from . import native
+        return native.row_sumsq_f32(A32)
+    return row_keys_fsum(A)
+
+
+def row_keys_fsum(M) -> np.ndarray:
+    """``row_keys`` from its definition: math.fsum (correctly rounded) of the
+    exact squares.  Each value x is split as x = h + l with h and l of at most
+    26 significant bits (Veltkamp's split), so that x^2 = h^2 + 2hl + l^2 with
+    every term exact in fp64.  Slow; for pins and fp64 data."""
     A = np.asarray(M, dtype=np.float64)
-    return np.einsum("ij,ij->i", A, A)
+    c = A * 134217729.0            # 2^27 + 1
+    h = c - (c - A)
+    lo = A - h
+    terms = np.stack([h * h, 2.0 * h * lo, lo * lo], axis=-1).reshape(A.shape[0], -1)
+    return np.array([math.fsum(row) for row in terms.tolist()], dtype=np.float64)
 
 
 def selected_count(n_rows: int, row_frac: float) -> int:
@@ -293,7 +323,8 @@ def momentum_update(E, G, beta: float) -> np.ndarray:
     fp32).  numpy float32 ufuncs are correctly rounded IEEE operations with no
     contraction, so each line is one rounding.
     Pages: Dion3 summary, 输入输出流程 (momentum update comes first) and
-    核心模块 ("配合误差反馈与有限精度处理": error feedback, finite precision).
+    核心模块 ("Dion3 更新规则" bullet: the row rule comes with error feedback
+    and handling of finite precision).
     """
     E32 = np.asarray(E, dtype=np.float32)
     G32 = np.asarray(G, dtype=np.float32)

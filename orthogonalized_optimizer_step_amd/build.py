@@ -45,17 +45,22 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    objs = []
-    for src, extra in SOURCES:
+    objs, procs = [], []
+    for src, extra in SOURCES:   # the units compile concurrently
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmd = [cc] + BASE_FLAGS + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
+    failed = []
+    for src, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            failed.append(f"hipcc failed on {src}:\n{out}\n{err}")
+    if failed:
+        raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -29,8 +29,9 @@ namespace dion {
 bool launch_gemm16(int bm, int na, int nb, int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa,
                    hipStream_t stream);
 bool launch_gemm64(int epi, bool sym, const GemmLaunch& L, const PhaseArgs& pa, hipStream_t stream);
-void launch_rowkeys(int fmt, const MatDesc* descs, int nmat, int64_t rows, double* keys, hipStream_t s);
-void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
+void launch_rowkeys(int fmt, bool exact, const MatDesc* descs, int nmat, int64_t rows, double* keys,
+                    hipStream_t s);
+void launch_momentum_keys(bool grad_bf16, bool exact, const MatDesc* descs, int nmat, int64_t rows, float beta,
                           double* keys, int write_out, hipStream_t s);
 void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
                               float keep, bool raw, hipStream_t s);
@@ -38,19 +39,22 @@ void launch_decay_selected(const MatDesc* descs, int nmat, int64_t total_sel, co
                            hipStream_t s);
 void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* flags, int* idx,
                    MatScalars* scalars, bool fp64_path, hipStream_t s);
-void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total,
-                 const int* idx, const MatScalars* scalars, int xterms, bool use_idx, hipStream_t s);
-void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int total, int src_slot, int dst_slot,
-                      hipStream_t s);
+void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* mats, const int* prefix, int nmat,
+                 int total, const int* idx, const MatScalars* scalars, int xterms, bool use_idx, hipStream_t s);
+void launch_transpose(const MatDesc* descs, const int* mats, const int* prefix, int nmat, int total, int src_slot,
+                      int dst_slot, hipStream_t s);
 void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
                             hipStream_t s);
 void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total, int slot,
                    const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
 void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
-                     const double* coef, int K, unsigned long long restarts, int fmt, hipStream_t s);
-// matrices with Gram side m <= 64 and long side n <= 1024 run in one launch
-constexpr int kTinyM = 64, kTinyN = 1024;
+                     const double* coef, int K, unsigned long long restarts, int in_fmt, int out_fmt, int update,
+                     float keep, hipStream_t s);
+// matrices with Gram side m <= 64 and long side n <= 1024, or m <= 16 and any
+// long side up to 2^24, run in one fp64 launch
+constexpr int kTinyM = 64, kTinyN = 1024, kTinyMLong = 16, kTinyNMax = 1 << 24;
+inline bool tiny_shape(int m, int n) { return m <= kTinyM && n <= kTinyNMax && (n <= kTinyN || m <= kTinyMLong); }
 }  // namespace dion
 
 using namespace dion;
@@ -66,6 +70,14 @@ int fail(int code, const std::string& msg) {
 
 const float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
 constexpr int kMaxIter = 64;
+// The MFMA16 path's error grows with the iterations: each one scales the
+// rounding in the small singular directions by its slope a_k (safety folded
+// in).  Its 2e-2 gate is established up to twelve iterations whose slopes
+// multiply to at most the fixed quintic's 3.4445^12 and, for schedules kept as
+// given, runs of at most five iterations between restarts; calls that would put
+// a matrix on that path beyond this are refused (the FP64 path takes them).
+constexpr int kMfmaMaxIter = 12, kMfmaMaxKeptRun = 5;
+const double kMfmaMaxGain = std::pow(3.4445, 12);
 
 // ------------------------------------------------------------ parameters
 struct Params {
@@ -201,6 +213,7 @@ struct Table {  // a (matrix list, prefix) pair inside the int blob
 struct MatPlan {
   int R, C, k, m, n, m_pad, n_pad, tall;
   bool acc;  // restarts after the first start from X0 with the accumulated factor
+  bool tiny = false;  // runs in the one-workgroup fp64 kernel
   size_t off[N_SLOTS];
 };
 
@@ -210,6 +223,9 @@ struct Plan {
   int fmt = 0;           // input storage: 0 bf16, 1 fp32, 2 fp16
   int xterms0 = 1;
   bool use_idx = false;
+  // row keys rounded exactly (they decide a selection, or are an output);
+  // otherwise they only give ||M||_F^2 and the plain fp64 sum serves
+  bool exact_keys = false;
   std::vector<MatPlan> mats;
   int64_t total_rows = 0, total_sel = 0;
   // phase entry points: a second descriptor set (the apply's Q operands, one
@@ -310,6 +326,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   P.bf16_in = P.fmt != 1;
   P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;  // bf16 and fp16 values are exact in one fp16 term
   P.use_idx = prm.row_frac < 1.0;
+  P.exact_keys = P.use_idx;
   const int K = (int)prm.a.size();
   // The restarts the GEMM schedule runs: the caller's and, on the MFMA16 path
   // unless keep_schedule is set, one more after every second iteration of a
@@ -377,10 +394,29 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   // singular direction (errors near 2e-2 for two rows).
   std::vector<int> mf, tiny_ids;
   for (int i = 0; i < batch; ++i) {
-    const MatPlan& mp = P.mats[i];
-    (!step_mode && K <= 64 && mp.m <= kTinyM && mp.n <= kTinyN ? tiny_ids : mf).push_back(i);
+    MatPlan& mp = P.mats[i];
+    mp.tiny = tiny_shape(mp.m, mp.n);
+    (mp.tiny ? tiny_ids : mf).push_back(i);
   }
   P.tiny = mf.empty();
+  if (!P.fp64 && !mf.empty()) {
+    double gain = 1.0;
+    for (int k = 0; k < K; ++k) gain *= std::max(1.0, std::fabs(prm.a[k]));
+    int run = 0, longest = 0;
+    for (int k = 1; k <= K; ++k) {
+      ++run;
+      if (k == K || prm.restart[k - 1]) {
+        longest = std::max(longest, run);
+        run = 0;
+      }
+    }
+    if (K > kMfmaMaxIter || gain > kMfmaMaxGain * (1.0 + 1e-9))
+      return fail(DION_E_UNSUPPORTED, "the MFMA16 path holds its error bound up to 12 iterations with slopes a_k "
+                                      "multiplying to at most 3.4445^12; use DION_PREC_FP64");
+    if (prm.keep_schedule && longest > kMfmaMaxKeptRun)
+      return fail(DION_E_UNSUPPORTED, "keep_schedule: runs of more than 5 iterations between restarts are outside "
+                                      "the MFMA16 path's error bound");
+  }
 
   // tables of the GEMM phases, over mf
   auto sym_counts = [&](int bm) {
@@ -434,17 +470,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   const int t_xtq_nacc = add_table(P, naccs, rect_counts(naccs, bm_xtq, true));
   const int t_full_acc = add_table(P, accs, sub_full(accs, bm_full));
   const int t_full_nacc = add_table(P, naccs, sub_full(naccs, bm_full));
-  // pack and transpose tables over every matrix: those kernels take the
-  // table's matrices as batch indices 0 .. n-1.  The small matrices' share is
-  // wasted but harmless: it runs after k_tiny_gns has finished with their
-  // buffers, and nothing reads it
-  std::vector<int> all(batch), pack_c(batch);
-  for (int i = 0; i < batch; ++i) {
-    all[i] = i;
-    pack_c[i] = (P.mats[i].m_pad / 64) * (P.mats[i].n_pad / 64);  // k_pad C_pad = m_pad n_pad either way
-  }
-  const int t_pack = add_table(P, all, pack_c);
-  const int t_tr = add_table(P, all, pack_c);
+  // pack and transpose tables over the MFMA matrices (the kernels look the
+  // matrices up through the table's list)
+  std::vector<int> pack_c;
+  for (int i : mf) pack_c.push_back((P.mats[i].m_pad / 64) * (P.mats[i].n_pad / 64));  // k_pad C_pad = m_pad n_pad
+  const int t_pack = add_table(P, mf, pack_c);
+  const int t_tr = add_table(P, mf, pack_c);
   P.K = K;
   if (!tiny_ids.empty()) {
     P.ntiny = (int)tiny_ids.size();
@@ -480,6 +511,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     MatPlan& mp = P.mats[i];
     const size_t mn = (size_t)mp.m_pad * mp.n_pad, mm = (size_t)mp.m_pad * mp.m_pad;
     for (int s = 0; s < N_SLOTS; ++s) mp.off[s] = 0;
+    if (mp.tiny) {   // k_tiny_gns: the iterate and its restart copy, m x n fp64 each
+      const size_t x = (size_t)mp.m * mp.n * 8;
+      mp.off[SLOT_X] = off;   off = align256(off + x);
+      mp.off[SLOT_XT0] = off; off = align256(off + x);
+      continue;
+    }
     mp.off[SLOT_X] = off;   off = align256(off + mn * es);
     mp.off[SLOT_XT0] = off; off = align256(off + mn * es * xt_terms);
     if (any_restart) {
@@ -497,7 +534,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   for (const MatPlan& mp : P.mats) {
     elems += (double)mp.R * mp.C;
     sel_elems += (double)mp.k * mp.C;
-    pad_elems += (double)mp.m_pad * mp.n_pad;
+    if (!mp.tiny) pad_elems += (double)mp.m_pad * mp.n_pad;
     unsel_elems += (double)(mp.R - mp.k) * mp.C;
   }
   Step st;
@@ -530,8 +567,17 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     st.raw = st.useful;
     P.steps.push_back(st);
   }
+  P.carry = step_mode && prm.carry;
+  auto decay = [&]() {   // carry: the captured rows of the buffer decay once read
+    Step dc;
+    dc.kind = ST_DECAY;
+    dc.name = "decay_rows";
+    dc.bytes = 8.0 * sel_elems;
+    P.steps.push_back(dc);
+  };
   if (P.tiny) {
-    if (P.use_idx) {
+    if (P.carry) decay();
+    if (P.use_idx && !step_mode) {
       Step cp;
       cp.kind = ST_COPY;
       cp.name = "copy_rows";
@@ -546,14 +592,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   st.table = t_pack;
   st.bytes = sel_elems * in_es + pad_elems * es * (1 + P.xterms0);
   P.steps.push_back(st);
-  P.carry = step_mode && prm.carry;
-  if (P.carry) {   // the captured rows of the buffer decay once packed
-    st = Step();
-    st.kind = ST_DECAY;
-    st.name = "decay_rows";
-    st.bytes = 8.0 * sel_elems;
-    P.steps.push_back(st);
-  }
+  if (P.carry) decay();
 
   // per-matrix useful FLOPs of a product kind; executed MFMA FLOPs from the tile table
   // out_lo: whether any later product or epilogue reads the lo term of this
@@ -921,6 +960,7 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
   P.bf16_in = P.fmt != 1;
   P.xterms0 = (P.fp64 || P.bf16_in) ? 1 : 2;
   P.use_idx = row_frac < 1.0;
+  P.exact_keys = ph == PH_KEYS || P.use_idx;
   P.mats.resize(batch);
   for (int i = 0; i < batch; ++i) {
     const int R = shapes[i].rows, C = shapes[i].cols;
@@ -1172,8 +1212,11 @@ const char* kernel_name(const Plan& P, const Step& st, int s_fmt, bool grad_bf16
   const char* in_t = s_fmt == 1 ? "float" : (s_fmt == 2 ? "_Float16" : "unsigned short");
   std::string key;
   switch (st.kind) {
-    case ST_KEYS: key = std::string("dion::k_rowkeys<") + in_t + ">"; break;
-    case ST_MOMENTUM: key = grad_bf16 ? "dion::k_momentum_keys<unsigned short>" : "dion::k_momentum_keys<float>"; break;
+    case ST_KEYS: key = std::string("dion::k_rowkeys<") + in_t + (P.exact_keys ? ", true>" : ", false>"); break;
+    case ST_MOMENTUM:
+      key = std::string(grad_bf16 ? "dion::k_momentum_keys<unsigned short" : "dion::k_momentum_keys<float") +
+            (P.exact_keys ? ", true>" : ", false>");
+      break;
     case ST_SELECT: key = "dion::k_select"; break;
     case ST_PACK: key = std::string(P.fp64 ? "dion::k_pack<" : "dion::k_pack16<") + in_t + ">"; break;
     case ST_TRANSPOSE: key = "dion::k_transpose<double>"; break;
@@ -1315,10 +1358,11 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
     if (g_prof.on) rec.kernel = kernel_name(P, st, s_fmt, grad_dtype == DION_BF16);
     switch (st.kind) {
       case ST_KEYS:
-        launch_rowkeys(s_fmt, sd, sn, srows, skeys, stream);
+        launch_rowkeys(s_fmt, P.exact_keys && !qset, sd, sn, srows, skeys, stream);
         break;
       case ST_MOMENTUM:
-        launch_momentum_keys(grad_dtype == DION_BF16, d_descs, batch, P.total_rows, P.carry ? 1.0f : beta, d_keys,
+        launch_momentum_keys(grad_dtype == DION_BF16, P.exact_keys, d_descs, batch, P.total_rows, P.carry ? 1.0f : beta,
+                             d_keys,
                              P.update ? 0 : (P.carry ? 2 : 1), stream);
         break;
       case ST_SELECT:
@@ -1326,13 +1370,14 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         break;
       case ST_PACK: {
         const Table& t = P.tabs[st.table];
-        launch_pack(s_fmt, P.fp64, sd, d_ints + t.prefix_off, t.nmat, t.total, sidx, ss,
+        launch_pack(s_fmt, P.fp64, sd, d_ints + t.mats_off, d_ints + t.prefix_off, t.nmat, t.total, sidx, ss,
                     qset ? 2 : P.xterms0, P.use_idx && !qset, stream);
         break;
       }
       case ST_TRANSPOSE: {
         const Table& t = P.tabs[st.table];
-        launch_transpose(d_descs, d_ints + t.prefix_off, t.nmat, t.total, st.src_slot, st.dst_slot, stream);
+        launch_transpose(d_descs, d_ints + t.mats_off, d_ints + t.prefix_off, t.nmat, t.total, st.src_slot,
+                         st.dst_slot, stream);
         break;
       }
       case ST_GEMM: {
@@ -1351,8 +1396,11 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
         launch_decay_selected(d_descs, batch, P.total_sel, P.use_idx ? d_idx : nullptr, beta, stream);
         break;
       case ST_TINY:
+        // the row-subset step reads the fp32 buffer and writes a bf16 update, or
+        // updates the weight in its own dtype
         launch_tiny_gns(d_descs, d_ints + P.tiny_ids_off, P.ntiny, d_scal, P.use_idx ? d_idx : nullptr,
-                        (const double*)(d_ints + P.coef_off), P.K, P.restarts, fmt, stream);
+                        (const double*)(d_ints + P.coef_off), P.K, P.restarts, fmt,
+                        step_mode ? (P.update && !P.w_bf16 ? 1 : 0) : fmt, P.update ? 1 : 0, P.keep, stream);
         break;
       case ST_COPY:
         launch_copy_unselected(fmt != 1, d_descs, batch, P.total_rows, d_flags, stream);

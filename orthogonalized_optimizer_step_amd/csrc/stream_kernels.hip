@@ -44,8 +44,197 @@ __device__ __forceinline__ int mat_of_row(const MatDesc* descs, int nmat, int64_
 }
 
 // ------------------------------------------------------------ row keys
-// One wave per row: key = sum_c x^2 in fp64 (each square is exact in fp64).
-template <typename InT>
+// A row's key is the exact sum of the squares of its stored values, rounded
+// once to the nearest double (ties to even).  A correctly rounded sum does not
+// depend on the order of summation, so the rows it selects are the ones any
+// implementation that rounds the exact sum once selects.  The square of a
+// float32 value (bf16 and fp16 values included) is exact in fp64.
+//
+// Fast path: each lane keeps its running sum as an unevaluated pair hi + lo,
+// updated by two error-free additions (Knuth's TwoSum), and raises a flag when
+// the second addition rounds; the wave combines the lanes' pairs the same
+// way.  Without the flag hi + lo is the exact sum and one IEEE addition
+// fl(hi + lo) rounds it correctly.  The flag needs the squares of a row to
+// spread over more than about 106 bits (a value near 2^-45 times the row's
+// largest).  Then the wave reads the row again and adds the squares into an
+// exact 640-bit fixed-point integer per lane, whose unit 2^-298 is the
+// weight of the smallest square; the lanes' integers are summed and the total
+// is rounded once.  Rows with an Inf or NaN get a NaN key.
+//
+// At row_frac = 1 no row is chosen by its key: the keys only give ||M||_F^2,
+// and the plain fp64 sum (EXACT = false) serves.
+
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = __dadd_rn(a, b);
+  const double bb = __dsub_rn(s, a);
+  e = __dadd_rn(__dsub_rn(a, __dsub_rn(s, bb)), __dsub_rn(b, bb));
+}
+
+struct SqAcc {
+  double hi = 0.0, lo = 0.0;
+  unsigned bad = 0u;
+  __device__ __forceinline__ void add(float x) {
+    const double q = __dmul_rn((double)x, (double)x);   // exact: 48 significant bits at most
+    double s, e, t, f;
+    two_sum(hi, q, s, e);
+    two_sum(lo, e, t, f);
+    hi = s;
+    lo = t;
+    bad |= f != 0.0 ? 1u : 0u;
+  }
+  // afterwards every lane holds the wave's pair and flag (both partners of an
+  // exchange form the same sums: TwoSum's result does not depend on the order)
+  __device__ __forceinline__ void wave() {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double h2 = __shfl_xor(hi, o, 64), l2 = __shfl_xor(lo, o, 64);
+      const unsigned b2 = __shfl_xor(bad, o, 64);
+      double s, e, t, f1, u, f2;
+      two_sum(hi, h2, s, e);
+      two_sum(lo, l2, t, f1);
+      two_sum(t, e, u, f2);
+      hi = s;
+      lo = u;
+      bad |= b2 | (f1 != 0.0 ? 1u : 0u) | (f2 != 0.0 ? 1u : 0u);
+    }
+  }
+};
+
+constexpr int SQ_WORDS = 20;   // 640 bits: squares reach 2^256, 2^31 of them fit
+
+// The exact fallback.  Each lane adds its squares into its own 640-bit
+// integer in LDS (lane-private words, so the word index may differ between
+// lanes).  The wave then sums the integers column by column (lane j < 20 adds
+// word j of all 64 lanes) and propagates the carries, leaving word j of the
+// total in lane j; the rounding reads the words it needs with shuffles and
+// ballots, so no lane ever holds the whole integer.
+struct SqExact {
+  uint32_t* base;              // the wave's 64 x SQ_WORDS words in LDS
+  int lane;
+  unsigned special = 0u;       // an Inf or NaN was seen
+  uint32_t word = 0u;          // after wave(): word `lane` of the total (lanes < SQ_WORDS)
+  __device__ __forceinline__ SqExact(uint32_t* wave_words, int lane_) : base(wave_words), lane(lane_) {
+    uint32_t* a = base + lane * SQ_WORDS;
+    for (int j = 0; j < SQ_WORDS; ++j) a[j] = 0u;
+  }
+  // x = m 2^(E - 150) (E >= 1) or f 2^-149 (E = 0), so x^2 = m^2 2^(pos - 298)
+  // with m^2 < 2^48 and pos = 2E - 2 (0 for E = 0): pos <= 508, so the three
+  // words from pos / 32 stay below word 18
+  __device__ __forceinline__ void add(float x) {
+    uint32_t* a = base + lane * SQ_WORDS;
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t E = (u >> 23) & 0xFFu, f = u & 0x7FFFFFu;
+    special |= E == 0xFFu ? 1u : 0u;
+    const uint64_t m = E ? (uint64_t)(f | 0x800000u) : (uint64_t)f;
+    const int pos = E ? 2 * (int)E - 2 : 0;
+    const uint64_t v = m * m;
+    const int wi = pos >> 5, sh = pos & 31;
+    const uint64_t lo = v << sh;
+    uint64_t t = (uint64_t)a[wi] + (uint32_t)lo;
+    a[wi] = (uint32_t)t;
+    t = (uint64_t)a[wi + 1] + (uint32_t)(lo >> 32) + (t >> 32);
+    a[wi + 1] = (uint32_t)t;
+    t = (uint64_t)a[wi + 2] + (sh ? (uint32_t)(v >> (64 - sh)) : 0u) + (t >> 32);
+    a[wi + 2] = (uint32_t)t;
+    uint32_t carry = (uint32_t)(t >> 32);
+    for (int j = wi + 3; carry && j < SQ_WORDS; ++j) {
+      t = (uint64_t)a[j] + carry;
+      a[j] = (uint32_t)t;
+      carry = (uint32_t)(t >> 32);
+    }
+  }
+  __device__ __forceinline__ void wave() {
+    // every lane's words are written before any lane reads another's
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint64_t col = 0;   // at most 64 (2^32 - 1) < 2^38
+    if (lane < SQ_WORDS)
+      for (int l = 0; l < 64; ++l) col += base[l * SQ_WORDS + lane];
+    uint64_t carry = 0;
+    for (int j = 0; j < SQ_WORDS; ++j) {
+      const uint64_t t = __shfl(col, j, 64) + carry;
+      if (lane == j) word = (uint32_t)t;
+      carry = t >> 32;
+    }
+    special = __any(special) ? 1u : 0u;
+  }
+  __device__ __forceinline__ uint32_t word_at(int j) const {   // j wave-uniform, >= 0
+    const uint32_t v = __shfl(word, j < SQ_WORDS ? j : 0, 64);
+    return j < SQ_WORDS ? v : 0u;
+  }
+  // bits [lo, lo + 64) of the total, lo >= 0 and wave-uniform
+  __device__ __forceinline__ uint64_t bits(int lo) const {
+    const int wi = lo >> 5, sh = lo & 31;
+    const uint64_t pq = ((uint64_t)word_at(wi + 1) << 32) | word_at(wi);
+    return sh ? (pq >> sh) | ((uint64_t)word_at(wi + 2) << (64 - sh)) : pq;
+  }
+  // the total times 2^-298, rounded to the nearest double, ties to even
+  __device__ __forceinline__ double rounded() const {
+    if (special) return __longlong_as_double(0x7FF8000000000000ll);
+    const unsigned long long nz = __ballot(lane < SQ_WORDS && word != 0u);
+    if (!nz) return 0.0;
+    const int tw = 63 - __clzll((long long)nz);                // highest nonzero word
+    const int top = 32 * tw + 31 - __clz((int)word_at(tw));    // highest set bit
+    if (top <= 52) return ldexp((double)bits(0), -298);       // 53 bits at most: exact
+    int ex = top - 52;                                         // weight of the last kept bit
+    uint64_t mant = bits(ex) & ((1ull << 53) - 1ull);
+    const int g = ex - 1;                                      // guard bit
+    const unsigned guard = (unsigned)(bits(g) & 1ull);
+    // sticky: any bit below the guard bit, from the words each lane holds
+    const int b0 = 32 * lane;
+    const uint32_t mask = b0 + 32 <= g ? 0xFFFFFFFFu : (b0 >= g ? 0u : ((1u << (g - b0)) - 1u));
+    const bool sticky = __ballot(lane < SQ_WORDS && (word & mask) != 0u) != 0ull;
+    if (guard && (sticky || (mant & 1ull))) ++mant;
+    if (mant >> 53) {   // rounded up into the next binade
+      mant >>= 1;
+      ++ex;
+    }
+    return ldexp((double)mant, ex - 298);
+  }
+};
+// LDS words of the fallback: one 640-bit integer per lane of a 256-thread block (20 KB)
+constexpr int SQ_LDS_WORDS = 256 * SQ_WORDS;
+
+// Calls f(x) on the elements of row r that this lane owns: 8 consecutive
+// 16-bit or 4 consecutive fp32 values per lane and step when the row allows
+// 16-byte loads, else one element per lane and step.
+template <typename InT, typename F>
+__device__ __forceinline__ void row_elems(const MatDesc& d, int64_t r, int lane, F&& f) {
+  const InT* row = (const InT*)d.M + r * d.C;
+  if (sizeof(InT) == 2) {
+    const uint16_t* p = (const uint16_t*)row;
+    if ((d.C & 7) == 0 && ((uintptr_t)d.M & 15) == 0) {
+      for (int c = lane * 8; c < d.C; c += 512) {
+        const uint4 v = *(const uint4*)(p + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f(in16_to_f32<InT>(w[q] & 0xFFFFu));
+          f(in16_to_f32<InT>(w[q] >> 16));
+        }
+      }
+    } else {
+      for (int c = lane; c < d.C; c += 64) f(in16_to_f32<InT>(p[c]));
+    }
+  } else {
+    const float* p = (const float*)row;
+    if ((d.C & 3) == 0 && ((uintptr_t)d.M & 15) == 0) {
+      for (int c = lane * 4; c < d.C; c += 256) {
+        const float4 v = *(const float4*)(p + c);
+        f(v.x);
+        f(v.y);
+        f(v.z);
+        f(v.w);
+      }
+    } else {
+      for (int c = lane; c < d.C; c += 64) f(p[c]);
+    }
+  }
+}
+
+// One wave per row.
+template <typename InT, bool EXACT>
 __global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ descs, int nmat,
                                                  int64_t total_rows, double* __restrict__ keys) {
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -53,56 +242,45 @@ __global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ des
   if (g >= total_rows) return;
   const MatDesc& d = descs[mat_of_row(descs, nmat, g)];
   const int64_t r = g - d.row0;
-  const InT* row = (const InT*)d.M + r * d.C;
-  double s = 0.0;
-  if (sizeof(InT) == 2) {
-    const uint16_t* p = (const uint16_t*)row;
-    if ((d.C & 7) == 0) {
-      for (int c = lane * 8; c < d.C; c += 512) {
-        uint4 v = *(const uint4*)(p + c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const double lo = (double)in16_to_f32<InT>(w[q] & 0xFFFFu);
-          const double hi = (double)in16_to_f32<InT>(w[q] >> 16);
-          s += lo * lo;
-          s += hi * hi;
-        }
-      }
-    } else {
-      for (int c = lane; c < d.C; c += 64) {
-        const double x = (double)in16_to_f32<InT>(p[c]);
-        s += x * x;
-      }
-    }
+  double key;
+  if (!EXACT) {
+    double s = 0.0;
+    row_elems<InT>(d, r, lane, [&](float x) { s += (double)x * (double)x; });
+    key = wave_sum(s);
   } else {
-    const float* p = (const float*)row;
-    if ((d.C & 3) == 0) {
-      for (int c = lane * 4; c < d.C; c += 256) {
-        float4 v = *(const float4*)(p + c);
-        s += (double)v.x * v.x;
-        s += (double)v.y * v.y;
-        s += (double)v.z * v.z;
-        s += (double)v.w * v.w;
-      }
-    } else {
+    SqAcc A;
+    row_elems<InT>(d, r, lane, [&](float x) { A.add(x); });
+    A.wave();
+    if (!A.bad) {
+      key = __dadd_rn(A.hi, A.lo);
+    } else {   // wave-uniform: every lane holds the combined flag
+      __shared__ uint32_t sq_lds[SQ_LDS_WORDS];
+      SqExact X(sq_lds + (threadIdx.x & ~63u) * SQ_WORDS, lane);
+      const InT* row = (const InT*)d.M + r * d.C;
+#pragma unroll 1
       for (int c = lane; c < d.C; c += 64) {
-        const double x = (double)p[c];
-        s += x * x;
+        float x;
+        if (sizeof(InT) == 2) x = in16_to_f32<InT>(((const uint16_t*)row)[c]);
+        else x = ((const float*)row)[c];
+        X.add(x);
       }
+      X.wave();
+      key = X.rounded();
     }
   }
-  s = wave_sum(s);
-  if (lane == 0) keys[g] = s;
+  if (lane == 0) keys[g] = key;
 }
 
 // ---------------------------------------------- momentum / error feedback
-// E <- fl32(fl32(beta * E) + grad), key <- sum E^2 (fp64), and out <- bf16(E)
-// (write_out 1), out <- 0 (write_out 2: the carry form of error feedback,
-// where unselected rows contribute no update) or nothing (write_out 0: out is
-// the weight of the fused update).  __fmul_rn / __fadd_rn keep the two
-// roundings separate (no contraction); beta = 1 gives fl32(E + grad).
-template <typename GT>
+// E <- fl32(fl32(beta * E) + grad), key <- the key of the new row of E (as
+// above), and out <- bf16(E) (write_out 1), out <- 0 (write_out 2: the carry
+// form of error feedback, where unselected rows contribute no update) or
+// nothing (write_out 0: out is the weight of the fused update).  __fmul_rn /
+// __fadd_rn keep the two roundings separate (no contraction); beta = 1 gives
+// fl32(E + grad).  The exact fallback reads the new E back with the same
+// lane-to-element map as the pass that wrote it, so each lane reads its own
+// stores.
+template <typename GT, bool EXACT>
 __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict__ descs, int nmat,
                                                        int64_t total_rows, float beta,
                                                        double* __restrict__ keys, int write_out) {
@@ -114,7 +292,13 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
   float* E = (float*)d.M + r * d.C;
   uint16_t* out = (uint16_t*)d.out + r * d.C;
   double s = 0.0;
-  if ((d.C & 3) == 0) {
+  SqAcc A;
+  auto key_of = [&](float m) {
+    if (EXACT) A.add(m);
+    else s += (double)m * (double)m;
+  };
+  const bool vec = (d.C & 3) == 0;
+  if (vec) {
     for (int c = lane * 4; c < d.C; c += 256) {
       float4 e = *(float4*)(E + c);
       float gv[4];
@@ -140,7 +324,7 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
         *(uint2*)(out + c) = make_uint2(0u, 0u);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s += (double)m[q] * (double)m[q];
+      for (int q = 0; q < 4; ++q) key_of(m[q]);
     }
   } else {
     for (int c = lane; c < d.C; c += 64) {
@@ -149,11 +333,33 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
       const float m = __fadd_rn(__fmul_rn(beta, E[c]), gv);
       E[c] = m;
       if (write_out) out[c] = write_out == 1 ? bf16_rne(m) : (uint16_t)0;
-      s += (double)m * (double)m;
+      key_of(m);
     }
   }
-  s = wave_sum(s);
-  if (lane == 0) keys[g] = s;
+  double key;
+  if (!EXACT) {
+    key = wave_sum(s);
+  } else {
+    A.wave();
+    if (!A.bad) {
+      key = __dadd_rn(A.hi, A.lo);
+    } else {
+      __shared__ uint32_t sq_lds[SQ_LDS_WORDS];
+      SqExact X(sq_lds + (threadIdx.x & ~63u) * SQ_WORDS, lane);
+      if (vec) {
+#pragma unroll 1
+        for (int c = lane * 4; c < d.C; c += 256)
+#pragma unroll 1
+          for (int q = 0; q < 4; ++q) X.add(E[c + q]);
+      } else {
+#pragma unroll 1
+        for (int c = lane; c < d.C; c += 64) X.add(E[c]);
+      }
+      X.wave();
+      key = X.rounded();
+    }
+  }
+  if (lane == 0) keys[g] = key;
 }
 
 // ------------------------------------------------- selection + norm
@@ -295,7 +501,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(const MatDesc* __restric
 
 // FP64 path.
 template <typename InT>
-__global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
+__global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs, const int* __restrict__ mats,
                                               const int* __restrict__ prefix, int nmat, int total,
                                               const int* __restrict__ idx_all,
                                               const MatScalars* __restrict__ scalars, int xterms,
@@ -308,7 +514,7 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
     int mid = (lo + hi) >> 1;
     if (prefix[mid] <= t) lo = mid; else hi = mid;
   }
-  const MatDesc& d = descs[lo];
+  const MatDesc& d = descs[mats[lo]];
   const int local = t - prefix[lo];
   const int k_pad = d.tall ? d.n_pad : d.m_pad;
   const int c_pad = d.tall ? d.m_pad : d.n_pad;
@@ -342,7 +548,7 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
 // tile read as 8-row column chunks (both LDS passes are bank-conflict-free).
 typedef _Float16 half8s __attribute__((ext_vector_type(8)));
 template <typename InT>
-__global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ descs,
+__global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ descs, const int* __restrict__ mats,
                                                 const int* __restrict__ prefix, int nmat, int total,
                                                 const int* __restrict__ idx_all,
                                                 const MatScalars* __restrict__ scalars, int xterms,
@@ -355,13 +561,14 @@ __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ desc
     int mid = (lo + hi) >> 1;
     if (prefix[mid] <= t) lo = mid; else hi = mid;
   }
-  const MatDesc& d = descs[lo];
+  const int mi = mats[lo];
+  const MatDesc& d = descs[mi];
   const int local = t - prefix[lo];
   const int k_pad = d.tall ? d.n_pad : d.m_pad;
   const int c_pad = d.tall ? d.m_pad : d.n_pad;
   const int tc = c_pad / 64;
   const int r0 = (local / tc) * 64, c0 = (local % tc) * 64;
-  const float scale = ldexpf(1.0f, scalars[lo].e);
+  const float scale = ldexpf(1.0f, scalars[mi].e);
   const int* idx = idx_all + d.sel0;
   _Float16* sl = (_Float16*)(d.tall ? d.buf[SLOT_XT0] : d.buf[SLOT_X]);
   _Float16* st = (_Float16*)(d.tall ? d.buf[SLOT_X] : d.buf[SLOT_XT0]);
@@ -434,7 +641,7 @@ __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ desc
 // FP64 path: X^T [n_pad][m_pad] -> X [m_pad][n_pad], row-major (the MFMA16 path
 // writes X in the restart apply's epilogue).
 template <typename T>
-__global__ __launch_bounds__(256) void k_transpose(const MatDesc* __restrict__ descs,
+__global__ __launch_bounds__(256) void k_transpose(const MatDesc* __restrict__ descs, const int* __restrict__ mats,
                                                    const int* __restrict__ prefix, int nmat,
                                                    int total, int src_slot, int dst_slot) {
   __shared__ T tile[64][65];
@@ -445,7 +652,7 @@ __global__ __launch_bounds__(256) void k_transpose(const MatDesc* __restrict__ d
     int mid = (lo + hi) >> 1;
     if (prefix[mid] <= t) lo = mid; else hi = mid;
   }
-  const MatDesc& d = descs[lo];
+  const MatDesc& d = descs[mats[lo]];
   const int local = t - prefix[lo];
   const int tm = d.m_pad / 64;
   const int n0 = (local / tm) * 64, m0 = (local % tm) * 64;
@@ -624,18 +831,32 @@ __global__ void k_scale_combine(MatScalars* __restrict__ scalars, int nmat) {
 static inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + 3) / 4); }
 
 // fmt: the storage format of the inputs, 0 = bf16, 1 = fp32, 2 = fp16
-void launch_rowkeys(int fmt, const MatDesc* descs, int nmat, int64_t rows, double* keys,
+void launch_rowkeys(int fmt, bool exact, const MatDesc* descs, int nmat, int64_t rows, double* keys,
                     hipStream_t s) {
-  if (fmt == 0) hipLaunchKernelGGL(k_rowkeys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
-  else if (fmt == 2) hipLaunchKernelGGL(k_rowkeys<_Float16>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
-  else hipLaunchKernelGGL(k_rowkeys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys);
+#define DION_KEYS(T_, X_) hipLaunchKernelGGL((k_rowkeys<T_, X_>), dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, keys)
+  if (exact) {
+    if (fmt == 0) DION_KEYS(uint16_t, true);
+    else if (fmt == 2) DION_KEYS(_Float16, true);
+    else DION_KEYS(float, true);
+  } else {
+    if (fmt == 0) DION_KEYS(uint16_t, false);
+    else if (fmt == 2) DION_KEYS(_Float16, false);
+    else DION_KEYS(float, false);
+  }
+#undef DION_KEYS
 }
 
-void launch_momentum_keys(bool grad_bf16, const MatDesc* descs, int nmat, int64_t rows, float beta,
+void launch_momentum_keys(bool grad_bf16, bool exact, const MatDesc* descs, int nmat, int64_t rows, float beta,
                           double* keys, int write_out, hipStream_t s) {
-  const int wo = write_out;
-  if (grad_bf16) hipLaunchKernelGGL(k_momentum_keys<uint16_t>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, wo);
-  else hipLaunchKernelGGL(k_momentum_keys<float>, dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, wo);
+#define DION_MOM(T_, X_) hipLaunchKernelGGL((k_momentum_keys<T_, X_>), dim3(row_blocks(rows)), dim3(256), 0, s, descs, nmat, rows, beta, keys, write_out)
+  if (exact) {
+    if (grad_bf16) DION_MOM(uint16_t, true);
+    else DION_MOM(float, true);
+  } else {
+    if (grad_bf16) DION_MOM(uint16_t, false);
+    else DION_MOM(float, false);
+  }
+#undef DION_MOM
 }
 
 void launch_update_unselected(bool w_bf16, const MatDesc* descs, int nmat, int64_t rows, const uint8_t* flags,
@@ -657,12 +878,12 @@ void launch_select(const MatDesc* descs, int nmat, const double* keys, uint8_t* 
                      fp64_path ? 1 : 0);
 }
 
-void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* prefix, int nmat,
+void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* mats, const int* prefix, int nmat,
                  int total, const int* idx, const MatScalars* scalars, int xterms, bool use_idx,
                  hipStream_t s) {
   if (total <= 0) return;
   const int ui = use_idx ? 1 : 0;
-#define DION_PACK(K_, T_) hipLaunchKernelGGL((K_<T_>), dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, idx, scalars, xterms, ui)
+#define DION_PACK(K_, T_) hipLaunchKernelGGL((K_<T_>), dim3(total), dim3(256), 0, s, descs, mats, prefix, nmat, total, idx, scalars, xterms, ui)
   if (fp64_path) {
     if (fmt == 0) DION_PACK(k_pack, uint16_t);
     else if (fmt == 2) DION_PACK(k_pack, _Float16);
@@ -675,10 +896,11 @@ void launch_pack(int fmt, bool fp64_path, const MatDesc* descs, const int* prefi
 #undef DION_PACK
 }
 
-void launch_transpose(const MatDesc* descs, const int* prefix, int nmat, int total, int src_slot, int dst_slot,
-                      hipStream_t s) {
+void launch_transpose(const MatDesc* descs, const int* mats, const int* prefix, int nmat, int total, int src_slot,
+                      int dst_slot, hipStream_t s) {
   if (total <= 0) return;
-  hipLaunchKernelGGL(k_transpose<double>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, src_slot, dst_slot);
+  hipLaunchKernelGGL(k_transpose<double>, dim3(total), dim3(256), 0, s, descs, mats, prefix, nmat, total, src_slot,
+                     dst_slot);
 }
 
 void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t rows,

@@ -3,10 +3,12 @@
 // P = aI + bG + cG^2, Q <- P Q, and G <- P G P or, at a restart, X <- Q X,
 // G <- X X^T, Q <- I; out = Q X).
 //
-// For matrices whose Gram side m is at most 64 (and long side at most 1024)
-// the GEMM phases would be some twenty launches of a tile or three each, so a
-// call of only such matrices is bound by launch latency, and beside larger
-// ones they would take 256-row tiles for a few rows.  Here one workgroup per matrix
+// For matrices whose Gram side m is at most 64 (and long side at most 1024,
+// or any long side when m is at most 16) the GEMM phases would be some twenty
+// launches of a tile or three each, so a call of only such matrices is bound
+// by launch latency, and beside larger ones they would take 256-row tiles for
+// a few rows, whose fp16 rounding a Gram side of a few rows cannot average
+// out.  Here one workgroup per matrix
 // runs the whole iteration in fp64: the m x m matrices G, P, Q and a temporary
 // live in LDS (four 64 x 64 fp64 buffers, 128 KB, plus a 16 KB staging chunk
 // for the Gram), the iterate X (m x n, fp64) in two workspace buffers that
@@ -18,7 +20,6 @@
 namespace dion {
 
 constexpr int TINY_M = 64;
-constexpr int TINY_N = 1024;
 constexpr int TINY_THREADS = 1024;
 
 namespace {
@@ -30,8 +31,16 @@ __device__ __forceinline__ double tiny_in(const void* p, size_t e, int fmt) {
   return (double)(float)__builtin_bit_cast(_Float16, u);
 }
 
-__device__ __forceinline__ void tiny_out(void* p, size_t e, double v, int fmt) {
-  const float f = (float)v;
+// the result's element (rounded to fp32 first), or with `update` the weight
+// update of the row-subset step: W <- fl32(fl32(W * keep) - fl32(alpha * u)),
+// u = the fp32 result, then rounded to W's dtype
+__device__ __forceinline__ void tiny_out(void* p, size_t e, double v, int fmt, int update, float keep,
+                                         float alpha) {
+  float f = (float)v;
+  if (update) {
+    const float cur = fmt == 1 ? ((const float*)p)[e] : __uint_as_float((uint32_t)((const uint16_t*)p)[e] << 16);
+    f = __fsub_rn(__fmul_rn(cur, keep), __fmul_rn(alpha, f));
+  }
   if (fmt == 1) {
     ((float*)p)[e] = f;
   } else if (fmt == 0) {
@@ -54,13 +63,17 @@ __device__ __forceinline__ int tiny_free(int x, int y, int z) {
 
 // ids: the batch indices of the matrices this launch covers, one workgroup
 // each; coef: K triples (a, b, c) in fp64 with the safety factor folded in;
-// restarts: bit k-1 set = restart after iteration k.
+// restarts: bit k-1 set = restart after iteration k; in_fmt, out_fmt: element
+// formats of M and out (0 bf16, 1 fp32, 2 fp16); update: out is the weight W
+// of the row-subset step's fused update (bf16 or fp32), with the decay factor
+// keep and the matrix's alpha.
 __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __restrict__ descs,
                                                            const int* __restrict__ ids,
                                                            const MatScalars* __restrict__ scalars,
                                                            const int* __restrict__ idx,
                                                            const double* __restrict__ coef, int K,
-                                                           unsigned long long restarts, int fmt) {
+                                                           unsigned long long restarts, int in_fmt,
+                                                           int out_fmt, int update, float keep) {
   const int mi = ids[blockIdx.x];
   const MatDesc& d = descs[mi];
   const int m = d.m, n = d.n;
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
   for (int e = tid; e < m * n; e += TINY_THREADS) {
     const int i = e / n, l = e - (e / n) * n;
     const int sr = d.tall ? l : i, sc = d.tall ? i : l;
-    X[e] = tiny_in(d.M, (size_t)src_row(sr) * d.C + sc, fmt) * s;
+    X[e] = tiny_in(d.M, (size_t)src_row(sr) * d.C + sc, in_fmt) * s;
   }
   __syncthreads();
 
@@ -191,15 +204,16 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
   // out[rows of S] = (Q X), transposed back when the block is tall
   apply(q < 0 ? nullptr : buf[q], [&](int i, int l, double v) {
     const int sr = d.tall ? l : i, sc = d.tall ? i : l;
-    tiny_out(d.out, (size_t)src_row(sr) * d.C + sc, v, fmt);
+    tiny_out(d.out, (size_t)src_row(sr) * d.C + sc, v, out_fmt, update, keep, d.upd_alpha);
   });
 }
 
 void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
-                     const double* coef, int K, unsigned long long restarts, int fmt, hipStream_t s) {
+                     const double* coef, int K, unsigned long long restarts, int in_fmt, int out_fmt, int update,
+                     float keep, hipStream_t s) {
   if (ntiny > 0)
     hipLaunchKernelGGL(k_tiny_gns, dim3(ntiny), dim3(TINY_THREADS), 0, s, descs, ids, scalars, idx, coef, K, restarts,
-                       fmt);
+                       in_fmt, out_fmt, update, keep);
 }
 
 }  // namespace dion

@@ -18,8 +18,8 @@ namespace dion {
 // never reached: every call below fails validation or only plans
 bool launch_gemm16(int, int, int, int, bool, const GemmLaunch&, const PhaseArgs&, hipStream_t) { std::abort(); }
 bool launch_gemm64(int, bool, const GemmLaunch&, const PhaseArgs&, hipStream_t) { std::abort(); }
-void launch_rowkeys(int, const MatDesc*, int, int64_t, double*, hipStream_t) { std::abort(); }
-void launch_momentum_keys(bool, const MatDesc*, int, int64_t, float, double*, int, hipStream_t) { std::abort(); }
+void launch_rowkeys(int, bool, const MatDesc*, int, int64_t, double*, hipStream_t) { std::abort(); }
+void launch_momentum_keys(bool, bool, const MatDesc*, int, int64_t, float, double*, int, hipStream_t) { std::abort(); }
 void launch_update_unselected(bool, const MatDesc*, int, int64_t, const uint8_t*, float, bool, hipStream_t) {
   std::abort();
 }
@@ -27,18 +27,18 @@ void launch_decay_selected(const MatDesc*, int, int64_t, const int*, float, hipS
 void launch_select(const MatDesc*, int, const double*, uint8_t*, int*, MatScalars*, bool, hipStream_t) {
   std::abort();
 }
-void launch_pack(int, bool, const MatDesc*, const int*, int, int, const int*, const MatScalars*, int, bool,
+void launch_pack(int, bool, const MatDesc*, const int*, const int*, int, int, const int*, const MatScalars*, int, bool,
                  hipStream_t) {
   std::abort();
 }
-void launch_transpose(const MatDesc*, const int*, int, int, int, int, hipStream_t) { std::abort(); }
+void launch_transpose(const MatDesc*, const int*, const int*, int, int, int, int, hipStream_t) { std::abort(); }
 void launch_copy_unselected(bool, const MatDesc*, int, int64_t, const uint8_t*, hipStream_t) { std::abort(); }
 void launch_unpack(bool, const MatDesc*, const int*, int, int, int, const MatScalars*, float, bool, hipStream_t) {
   std::abort();
 }
 void launch_scale_combine(MatScalars*, int, hipStream_t) { std::abort(); }
 void launch_tiny_gns(const MatDesc*, const int*, int, const MatScalars*, const int*, const double*, int, unsigned long long, int,
-                     hipStream_t) {
+                     int, int, float, hipStream_t) {
   std::abort();
 }
 void launch_lr_accumulate(const LrDesc*, int, int64_t, int, hipStream_t) { std::abort(); }

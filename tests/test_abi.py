@@ -234,3 +234,49 @@ def test_keep_schedule_validation_and_plan():
         assert dion.workspace_size(shp, "bf16", **sched) == dion.workspace_size(shp, "bf16", keep_schedule=True,
                                                                                  **sched), sched
     assert dion.restart_points(n_iter=5) == []
+
+
+def _orth_rc(shapes, dtype=_lib.DION_BF16, **kw):
+    """dion_orth_batched's status for these hyper-parameters with placeholder
+    pointers: the plan is checked before any pointer is used."""
+    p, keep = dion._params(kw.pop("coeffs", dion.QUINTIC), kw.pop("n_iter", 5), kw.pop("restart_every", 0),
+                           kw.pop("restart_mask", 0), kw.pop("safety", 1.0), 1.0, kw.pop("precision", "auto"),
+                           keep_schedule=kw.pop("keep_schedule", False))
+    assert not kw
+    n = len(shapes)
+    fake = (ctypes.c_void_p * n)(*[0x10000 * (i + 1) for i in range(n)])
+    out = (ctypes.c_void_p * n)(*[0x90000000 + 0x10000 * i for i in range(n)])
+    return _lib.lib.dion_orth_batched(fake, out, dion._shapes(shapes), n, dtype, ctypes.byref(p), None, None, 0,
+                                      None)
+
+
+def test_mfma16_iteration_range_guard():
+    """The MFMA16 path refuses schedules beyond the range its 2e-2 error bound is
+    established for (more than 12 iterations, slopes multiplying to more than
+    3.4445^12, or kept runs of more than 5 iterations between restarts), with
+    DION_E_UNSUPPORTED before any launch; the FP64 path and matrices that take
+    the one-launch fp64 kernel (Gram side <= 64 and long side <= 1024, or Gram
+    side <= 16) accept them."""
+    big = [(256, 512)]
+    tiny = [(64, 1024), (16, 20000), (30000, 9)]
+    ws = -3   # DION_E_WORKSPACE: the plan was accepted, the (absent) workspace was not
+    assert _orth_rc(big, n_iter=12, restart_every=2) == ws
+    for kw in (dict(n_iter=13, restart_every=2), dict(n_iter=20), dict(coeffs=(5.0, -6.0, 2.0), n_iter=10),
+               dict(n_iter=6, keep_schedule=True), dict(n_iter=8, restart_mask=0b1, keep_schedule=True)):
+        assert _orth_rc(big, **kw) == -2, kw
+        assert _orth_rc(big, precision="fp64", **kw) == ws, kw
+        assert _orth_rc(tiny, **kw) == ws, kw
+        with pytest.raises(dion.DionError):
+            dion.workspace_size(big, "bf16", **kw)
+    # slopes below the quintic's pass; the safety factor divides the slopes
+    assert _orth_rc(big, coeffs=(1.5, -0.5, 0.0), n_iter=12) == ws
+    assert _orth_rc(big, coeffs=(3.6, -4.8, 2.0), n_iter=12, safety=1.05) == ws
+    assert _orth_rc(big, coeffs=(3.6, -4.8, 2.0), n_iter=12) == -2
+    assert _orth_rc(big, n_iter=5, keep_schedule=True) == ws
+    # the row-subset step (MFMA16 only) refuses the same schedules
+    p, keep = dion._params(dion.QUINTIC, 13, 2, 0, 1.0, 0.125, "mfma16")
+    fake = (ctypes.c_void_p * 1)(0x10000)
+    rc = _lib.lib.dion_rowsubset_step(fake, (ctypes.c_void_p * 1)(0x20000), (ctypes.c_void_p * 1)(0x90000000),
+                                      dion._shapes([(2048, 512)]), 1, _lib.DION_BF16, 0.9, ctypes.byref(p), None, None, 0,
+                                      None)
+    assert rc == -2

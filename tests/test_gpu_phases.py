@@ -3,8 +3,8 @@ the C ABI) with the oracle's single steps: row keys and top-k, the Gram
 matrix, the Gram polynomial and the apply on the Gram side.
 
 Gates, derived from the arithmetic of each path:
-  keys     relative 1e-12 per row (fp64 sums of exact squares, other order);
-           selected rows bit-exact (exchanges only between keys within 4 ulps)
+  keys     bit-exact: both sides round the exact sum of squares once;
+           selected rows bit-exact
   MFMA16   bf16 operands are exact in fp16 and products accumulate in fp32:
            relative Frobenius 2e-5 on fp32 outputs; fp32 operands of the Gram
            product take one fp16 term (2^-11 relative each): 2e-3; two-term
@@ -68,12 +68,7 @@ def sym_unit_gram(seed, m):
 def assert_selection(idx_gpu, M, frac):
     ref = O.select_rows(M, frac)
     got = np.asarray(idx_gpu, dtype=np.int64)
-    assert got.shape == ref.shape and np.all(np.diff(got) > 0)
-    if np.array_equal(got, ref):
-        return
-    keys = O.row_keys(M)
-    kd = keys[np.setxor1d(got, ref)]
-    assert np.max(kd) - np.min(kd) <= 4 * np.spacing(np.max(kd))
+    assert np.array_equal(got, ref), np.setxor1d(got, ref)
 
 
 # ------------------------------------------------------------ rowkeys + top-k
@@ -86,7 +81,7 @@ def test_rowkeys_topk_random(dion, frac, bf16):
     for M, k, ix in zip(Ms, keys, idx):
         ref = O.row_keys(M)
         got = k.cpu().numpy()
-        assert np.all(np.abs(got - ref) <= 1e-12 * ref + 1e-300), M.shape
+        assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), M.shape   # rounded once from the exact sum
         assert_selection(ix.cpu().numpy(), M, frac)
 
 
@@ -115,8 +110,79 @@ def test_rowkeys_topk_full_size(dion):
     keys, idx = dion.rowkeys_topk([dev(M, torch.bfloat16) for M in Ms], row_frac=0.125)
     for M, k, ix in zip(Ms, keys, idx):
         ref = O.row_keys(M)
-        assert np.all(np.abs(k.cpu().numpy() - ref) <= 1e-12 * ref)
+        assert np.array_equal(k.cpu().numpy().view(np.uint64), ref.view(np.uint64))
         assert_selection(ix.cpu().numpy(), M, 0.125)
+
+
+T27 = 2.0 ** -27   # T27^2 = 2^-54: two such squares add exactly half an ulp of 1.0
+
+
+def adversarial_matrix(dtype, cols, seed):
+    """Rows of random values mixed with rows whose exact sum of squares sits on
+    a rounding midpoint of the doubles, a hair above one (only an exact sum
+    tells), or spreads over hundreds of bits, placed at varied columns so that
+    different lanes hold them; all values exact in `dtype`."""
+    rng = np.random.default_rng(seed)
+    if dtype == "fp16":   # fp16 squares span 2^-48 .. 2^32: ties against 2^30
+        big, t, tiny, far = 32768.0, 2.0 ** -12, 2.0 ** -24, 2.0 ** -24
+    else:                 # bf16 and fp32 share the exponent range
+        big, t, tiny, far = 1.0, T27, 2.0 ** -100, 2.0 ** (-133 if dtype == "bf16" else -149)
+    rows = []
+    for j in range(24):
+        r = np.zeros(cols, np.float32)
+        c = rng.choice(cols, size=4, replace=False)
+        kind = j % 6
+        if kind == 0:
+            r[:] = rng.standard_normal(cols)
+        elif kind == 1:                          # a tie: ties to even
+            r[c[:3]] = [big, t, t]
+        elif kind == 2:                          # just above the tie
+            r[c] = [big, t, t, tiny]
+        elif kind == 3:                          # squares spread far apart
+            r[c] = [big * 1.5, far, tiny, -t]
+        elif kind == 4:                          # random values plus one far below them
+            r[:] = rng.standard_normal(cols)
+            r[c[0]] = far
+        else:                                    # equal to a tie row's key: ties to the lower row
+            r[c[0]] = big
+        rows.append(r)
+    A = np.stack(rows)
+    if dtype == "bf16":
+        A = round_bf16(A)
+    elif dtype == "fp16":
+        A = A.astype(np.float16).astype(np.float32)
+    return A
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("cols", [640, 333, 64, 5])
+def test_rowkeys_exact_rounding(dion, dtype, cols):
+    """Keys bit-equal to the exact sum of squares rounded once, on rows built to
+    defeat any fixed summation order (ties, a hair above a tie, squares hundreds
+    of bits apart): the first exercise the exact-pair fast path, the others the
+    exact integer fallback; 640 and 64 columns take 16-byte loads, 333 and 5 do not."""
+    A = adversarial_matrix(dtype, cols, seed=cols)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
+    for frac in (1.0 / 8, 0.5):
+        keys, idx = dion.rowkeys_topk([dev(A, tdt)], row_frac=frac)
+        ref = O.row_keys(A)
+        got = keys[0].cpu().numpy()
+        assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), np.flatnonzero(got != ref)
+        assert_selection(idx[0].cpu().numpy(), A, frac)
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "fp32"])
+def test_momentum_keys_exact_rounding(dion, gdt):
+    """The momentum pass's keys decide the row-subset step's selection: with
+    beta = 0 the new buffer is the gradient itself, built from adversarial rows;
+    the selection must match the oracle's exactly and the buffer bit for bit."""
+    A = adversarial_matrix("bf16" if gdt == "bf16" else "fp32", 640, seed=9)
+    E = torch.zeros(A.shape, dtype=torch.float32, device="cuda")
+    G = dev(A, torch.bfloat16 if gdt == "bf16" else torch.float32)
+    for frac in (1.0 / 8, 1.0 / 3):
+        outs, idx = dion.rowsubset_step([E], [G], 0.0, row_frac=frac, return_indices=True)
+        assert np.array_equal(E.cpu().numpy().view(np.uint32), A.view(np.uint32))
+        assert_selection(idx[0].cpu().numpy(), A, frac)
 
 
 # ------------------------------------------------------------------- Gram

@@ -243,6 +243,98 @@ def test_selection_brute_force_with_ties(R, C, frac):
     assert list(O.select_rows(M, frac)) == brute_force_select(M, k)
 
 
+# ------------------------------------ P7: row keys, rounded once from the exact sum
+def exact_key(row) -> float:
+    """The exact sum of the squares as a Fraction, rounded once by float():
+    CPython's int / int true division is correctly rounded, ties to even."""
+    s = sum((Fraction(float(v)) ** 2 for v in row), Fraction(0))
+    return float(s)
+
+
+T27 = 2.0 ** -27   # T27^2 = 2^-54: two of them add exactly half an ulp of 1.0
+ADVERSARIAL_ROWS = [
+    ([1.0, T27, T27], "tie"),                              # 1 + 2^-53: ties to even -> 1
+    ([1.0, T27, T27, 2.0 ** -100], "above"),               # a hair above the tie -> 1 + 2^-52
+    ([1.0, 3 * 2.0 ** -26, T27, T27], "tie"),              # 1 + 2^-49 + 2^-52 + 2^-53: odd below -> up
+    ([T27, 1.0, T27], "tie"),                              # the same tie in another order
+    ([2.0 ** -149, 2.0 ** -149, 2.0 ** -140], "small"),    # subnormal squares (2^-298)
+    ([1.5 * 2.0 ** 127, 2.0 ** -100, 2.0 ** -149, -(2.0 ** 126)], "spread"),   # squares over 550 bits
+    ([0.0, -0.0, 0.0], "zero"),
+    ([-1.0, -T27, -T27], "tie"),                           # signs do not matter
+]
+
+
+def _is_midpoint(row):
+    s = sum((Fraction(float(v)) ** 2 for v in row), Fraction(0))
+    r = float(s)
+    if Fraction(r) == s:
+        return False
+    lo, hi = (r, math.nextafter(r, math.inf)) if Fraction(r) < s else (math.nextafter(r, 0.0), r)
+    return 2 * s == Fraction(lo) + Fraction(hi)
+
+
+def test_row_keys_adversarial_exact():
+    """Rows on a rounding midpoint of the doubles (ties to even), a hair off one,
+    with subnormal squares and with squares spread over 550 bits: the keys equal
+    the exact sum rounded once (Fraction) and the fsum definition."""
+    width = max(len(r) for r, _ in ADVERSARIAL_ROWS)
+    M = np.zeros((len(ADVERSARIAL_ROWS), width), np.float32)
+    for i, (r, kind) in enumerate(ADVERSARIAL_ROWS):
+        M[i, :len(r)] = np.float32(r)
+        assert np.array_equal(M[i, :len(r)].astype(np.float64), np.asarray(r)), "inputs must be float32 values"
+        assert _is_midpoint(r) == (kind == "tie"), (i, kind)
+    got = O.row_keys(M)
+    want = np.array([exact_key(row) for row in M])
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+    assert np.array_equal(got.view(np.uint64), O.row_keys_fsum(M).view(np.uint64))
+    assert got[0] == 1.0 and got[1] == 1.0 + 2.0 ** -52 and got[2] == 1.0 + 2.0 ** -49 + 2.0 ** -51
+    # the plain fp64 sum in row order rounds the first tie away from the exact answer's neighbour
+    assert float(np.sum(np.float64(M[2]) ** 2)) != got[2] or float(np.sum(np.float64(M[1]) ** 2)) != got[1]
+
+
+@pytest.mark.parametrize("kind", ["normal", "bf16", "fp16", "wide", "sparse", "fp64"])
+def test_row_keys_equal_fsum_and_fractions(kind):
+    """On random float32 data of several kinds, bit-equal to math.fsum of the exact
+    squares, and (on a subset) to the Fraction sum rounded once; permuting the
+    columns changes no key (the definition has no summation order)."""
+    rng = np.random.default_rng({"normal": 1, "bf16": 2, "fp16": 3, "wide": 4, "sparse": 5, "fp64": 6}[kind])
+    A = rng.standard_normal((200, 333)).astype(np.float32)
+    if kind == "fp64":   # doubles that are not float32 values: the Veltkamp-split fsum branch
+        A = rng.standard_normal((200, 333)) * 10.0 ** rng.uniform(-100, 100, (200, 333))
+    if kind == "bf16":
+        A = round_bf16(A * 10.0 ** rng.uniform(-3, 3, (200, 1)))
+    elif kind == "fp16":
+        A = (A * 10.0 ** rng.uniform(-6, 4, A.shape)).astype(np.float16).astype(np.float32)
+    elif kind == "wide":
+        A = (A * 10.0 ** rng.uniform(-45, 38, A.shape)).astype(np.float32)
+    elif kind == "sparse":
+        A[rng.random(A.shape) < 0.9] = 0.0
+        A[:5] = 0.0
+    got = O.row_keys(A)
+    assert np.array_equal(got.view(np.uint64), O.row_keys_fsum(A).view(np.uint64))
+    for i in range(0, 200, 40):
+        assert got[i] == exact_key(A[i])
+    perm = rng.permutation(A.shape[1])
+    assert np.array_equal(O.row_keys(A[:, perm]).view(np.uint64), got.view(np.uint64))
+    if kind == "normal":   # einsum's summation order differs from the rounded exact sum on most rows
+        assert np.count_nonzero(np.einsum("ij,ij->i", A.astype(np.float64), A.astype(np.float64)) != got) > 20
+
+
+def test_selection_follows_rounded_exact_keys():
+    """Rows whose exact sums differ below the doubles' spacing rank by their rounded
+    keys, and equal keys rank by row index (brute force on Fraction keys)."""
+    rows = [[1.0, T27, T27], [1.0], [1.0, T27, T27, 2.0 ** -100], [0.5, 0.5, 0.5, 0.5], [1.0, 2.0 ** -120]]
+    M = np.zeros((len(rows), 4), np.float32)
+    for i, r in enumerate(rows):
+        M[i, :len(r)] = r
+    keys = [exact_key(r) for r in M]
+    for k in range(1, len(rows) + 1):
+        order = sorted(range(len(rows)), key=lambda j: (-keys[j], j))
+        assert list(O.select_rows(M, k / len(rows))) == sorted(order[:k])
+    assert list(O.select_rows(M, 0.2)) == [2]         # the one key above 1.0
+    assert list(O.select_rows(M, 0.4)) == [0, 2]      # then the first of four keys equal to 1.0
+
+
 def test_selected_count():
     assert O.selected_count(4096, 0.125) == 512
     assert O.selected_count(14336, 0.125) == 1792
@@ -461,20 +553,92 @@ def test_weight_update_scalar_emulation(wd, bf16):
         assert got[i] == v
 
 
-def test_rowsubset_step_update_structure():
-    """Selected rows: W keep - alpha * orthogonalize(M_t); the others: the raw momentum update."""
-    Es = [np.zeros((12, 20), np.float32)]
-    G = [round_bf16(RNG.standard_normal((12, 20))).astype(np.float32)]
-    Ws = [(RNG.standard_normal((12, 20)) * 0.02).astype(np.float32)]
-    newE, newW, idxs = O.rowsubset_step_update(Es, G, Ws, 0.95, [0.03], 0.01, row_frac=0.25, n_iter=5,
-                                               restart_every=2)
-    out, idx = O.orthogonalize(newE[0], n_iter=5, restart_every=2, row_frac=0.25)
-    assert np.array_equal(idx, idxs[0])
-    keep = float(np.float32(1.0) - np.float32(0.01))
-    assert np.allclose(newW[0][idx], Ws[0][idx].astype(np.float64) * keep - float(np.float32(0.03)) * out[idx],
-                       atol=1e-15)
-    rest = np.setdiff1d(np.arange(12), idx)
-    assert np.array_equal(newW[0][rest], O.weight_update_f32(Ws[0][rest], newE[0][rest], 0.03, 0.01))
+def _svd_orth_rows(Mt, idx, **ns):
+    """The selected block's exact output from the SVD closed form."""
+    return svd_closed_form(np.asarray(Mt, np.float64)[idx], ns.get("coeffs", QUINTIC), ns["n_iter"],
+                           ns.get("safety", 1.0))
+
+
+def _scalar_update(W, U, alpha, wd, bf16=False):
+    """fl32(fl32(W keep) - fl32(alpha U)) with struct-rounded fp64 scalars."""
+    keep = f32(1.0 - f32(wd))
+    a32 = f32(alpha)
+    out = np.array([[f32(f32(float(w) * keep) - f32(a32 * float(u))) for w, u in zip(rw, ru)]
+                    for rw, ru in zip(np.asarray(W), np.asarray(U))], np.float32)
+    return O.round_to_bf16(out) if bf16 else out
+
+
+def _brute_idx(M, frac):
+    keys = [exact_key(r) for r in np.asarray(M)]
+    k = O.selected_count(len(keys), frac)
+    return sorted(sorted(range(len(keys)), key=lambda j: (-keys[j], j))[:k])
+
+
+@pytest.mark.parametrize("ef", ["raw", "carry"])
+def test_rowsubset_step_update_alpha_zero_keeps_decayed_weights(ef):
+    """alpha = 0: every row becomes W (1 - wd); the selected rows exactly (fp64),
+    the others as the fp32 update fl32(W keep) (scalar emulation)."""
+    rng = np.random.default_rng(21)
+    E = [rng.standard_normal((16, 24)).astype(np.float32)]
+    G = [round_bf16(rng.standard_normal((16, 24)).astype(np.float32))]
+    W = [(rng.standard_normal((16, 24)) * 0.02).astype(np.float32)]
+    _, newW, idxs = O.rowsubset_step_update(E, G, W, 0.9, [0.0], 0.01, ef=ef, row_frac=0.25, n_iter=5)
+    keep = f32(1.0 - f32(0.01))
+    idx, rest = idxs[0], np.setdiff1d(np.arange(16), idxs[0])
+    exact = np.array([[float(Fraction(float(w)) * Fraction(keep)) for w in row] for row in W[0][idx]])
+    assert np.array_equal(newW[0][idx], exact)
+    assert np.array_equal(newW[0][rest], _scalar_update(W[0][rest], np.zeros((len(rest), 24)), 0.0, 0.01))
+
+
+@pytest.mark.parametrize("ef,shape,frac", [("raw", (24, 10), 0.25), ("raw", (12, 30), 0.5),
+                                           ("carry", (24, 10), 0.25), ("carry", (12, 30), 1 / 3)])
+def test_rowsubset_step_update_from_zero_weights(ef, shape, frac):
+    """W = 0, no decay: the selected rows are -alpha times the SVD closed form of the
+    selected block of the buffer the step orthogonalizes, the rows chosen by brute
+    force on exact keys; the others are -fl32(alpha M_t) (raw) or zero (carry).
+    The buffer the step orthogonalizes is fl32(fl32(beta E) + G) (raw) or
+    fl32(E + G) (carry), each rebuilt by scalar emulation."""
+    rng = np.random.default_rng(hash((ef, shape)) % 2 ** 32)
+    E = rng.standard_normal(shape).astype(np.float32)
+    G = round_bf16(rng.standard_normal(shape).astype(np.float32))
+    W0 = np.zeros(shape, np.float32)
+    beta, alpha = 0.9, 0.05
+    ns = dict(n_iter=5, restart_every=2)
+    _, newW, idxs = O.rowsubset_step_update([E], [G], [W0], beta, [alpha], 0.0, ef=ef, row_frac=frac, **ns)
+    if ef == "raw":
+        B = np.array([[f32(f32(f32(beta) * float(e)) + float(g)) for e, g in zip(re_, rg)] for re_, rg in zip(E, G)],
+                     np.float32)
+    else:
+        B = np.array([[f32(float(e) + float(g)) for e, g in zip(re_, rg)] for re_, rg in zip(E, G)], np.float32)
+    idx = _brute_idx(B, frac)
+    assert list(idxs[0]) == idx
+    rest = np.setdiff1d(np.arange(shape[0]), idx)
+    want = -f32(alpha) * _svd_orth_rows(B, idx, **ns)
+    assert O.rel_frobenius(newW[0][idx], want) < 1e-11
+    if ef == "raw":
+        assert np.array_equal(newW[0][rest], _scalar_update(W0[rest], B[rest], alpha, 0.0))
+        assert np.all(newW[0][rest] == -np.array([[f32(f32(alpha) * float(b)) for b in r] for r in B[rest]]))
+    else:
+        assert np.all(newW[0][rest] == 0.0)
+
+
+def test_rowsubset_step_update_carry_routes_zero_update():
+    """Carry with weights and decay: unselected rows take the zero update,
+    fl32(W keep) bit for bit; selected rows W keep - alpha O (closed form)."""
+    rng = np.random.default_rng(33)
+    E = rng.standard_normal((20, 9)).astype(np.float32)
+    G = round_bf16(rng.standard_normal((20, 9)).astype(np.float32))
+    W = (rng.standard_normal((20, 9)) * 0.05).astype(np.float32)
+    ns = dict(n_iter=4, restart_every=2)
+    _, newW, idxs = O.rowsubset_step_update([E], [G], [W], 0.95, [0.02], 0.1, ef="carry", row_frac=0.3, **ns)
+    B = np.array([[f32(float(e) + float(g)) for e, g in zip(re_, rg)] for re_, rg in zip(E, G)], np.float32)
+    idx = _brute_idx(B, 0.3)
+    assert list(idxs[0]) == idx
+    rest = np.setdiff1d(np.arange(20), idx)
+    keep = f32(1.0 - f32(0.1))
+    assert np.array_equal(newW[0][rest], np.array([[f32(float(w) * keep) for w in r] for r in W[rest]], np.float32))
+    want = W[idx].astype(np.float64) * keep - f32(0.02) * _svd_orth_rows(B, idx, **ns)
+    assert O.rel_frobenius(newW[0][idx], want) < 1e-11
 
 
 def _carry_inputs(shape=(48, 20), steps=3, seed=5):
