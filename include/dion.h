@@ -39,7 +39,9 @@
  *     device buffer is owned by the caller.  The library allocates no device
  *     memory and keeps no device state between calls: all scratch lives in
  *     the caller's `workspace` (device memory, at least
- *     dion_workspace_size() bytes, 256-byte aligned).
+ *     dion_workspace_size() bytes, 256-byte aligned).  The one exception is
+ *     dion_orth_batched_noalloc, whose scratch is a fixed array that each
+ *     device holds for the life of the process.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work on it and return without synchronizing; host arrays are only read
  *     during the call.  Two calls must not share a workspace concurrently.
@@ -164,6 +166,22 @@ size_t dion_workspace_size(const dion_shape* shapes, int32_t batch, int32_t dtyp
 int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* shapes,
                       int32_t batch, int32_t dtype, const dion_ns_params* p,
                       int32_t* sel_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as dion_orth_batched, with its scratch in a fixed array inside the
+ * library instead of a caller's workspace.  It calls no allocating routine:
+ * the plan header reaches the device as kernel arguments.
+ *   Limit: the batch's dion_workspace_size() must not exceed
+ *   DION_NOALLOC_SCRATCH_BYTES (256 MiB), else DION_E_WORKSPACE before any
+ *   launch.  Each device the library runs on holds one such array until the
+ *   process ends, shared by every call on that device: calls that overlap in
+ *   time on one device (other streams, other threads) race on it and must be
+ *   serialized by the caller.  Nothing in it needs to start at zero.
+ *   Arguments as dion_orth_batched. */
+#define DION_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int dion_orth_batched_noalloc(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,
+                              int32_t dtype, const dion_ns_params* p, int32_t* sel_idx, void* stream);
 
 /* Same operation with a flat parameter list: one coefficient triple (NULL =
  * the fixed quintic), restarts every restart_every iterations, AUTO precision. */

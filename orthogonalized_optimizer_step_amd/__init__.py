@@ -14,7 +14,7 @@ from ._lib import DION_BF16, DION_FP16, DION_FP32, PHASE, PREC, DionError, DionP
 __all__ = ["orth_batched", "rowsubset_step", "workspace_size", "useful_flops", "Orthogonalizer",
            "DionError", "QUINTIC", "profile_enable", "profile_records", "rowkeys_topk", "syrk", "sympoly",
            "apply", "rowsubset_step_update", "Dion3", "restart_points", "lowrank_step",
-           "lowrank_workspace_size"]
+           "lowrank_workspace_size", "orth_batched_noalloc", "NOALLOC_SCRATCH_BYTES"]
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 
@@ -184,6 +184,28 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
     if not return_indices:
         return outs
     return outs, list(torch.split(sel, orth.selected))
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # DION_NOALLOC_SCRATCH_BYTES
+
+
+def orth_batched_noalloc(Ms, outs, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
+                         row_frac=1.0, precision="auto", sel_idx=None, stream=None, restart_threshold=0.0,
+                         keep_schedule=False):
+    """dion_orth_batched_noalloc: orth_batched with the library's fixed scratch
+    array (no workspace, no device allocation in the call).  ``outs`` (and
+    ``sel_idx``, int32 of the total selected rows) are the caller's."""
+    _check_tensors(Ms, Ms[0].dtype)
+    _check_tensors(outs, Ms[0].dtype)
+    shapes = [tuple(M.shape) for M in Ms]
+    if [tuple(o.shape) for o in outs] != shapes:
+        raise DionError(-1, "outs must match the inputs' shapes")
+    p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold,
+                      keep_schedule=keep_schedule)
+    check(lib.dion_orth_batched_noalloc(_ptrs(Ms), _ptrs(outs), _shapes(shapes), len(Ms), _dtype_code(Ms[0].dtype),
+                                        ctypes.byref(p), ctypes.c_void_p(sel_idx.data_ptr() if sel_idx is not None
+                                                                         else None), _stream(stream)))
+    return outs
 
 
 def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,

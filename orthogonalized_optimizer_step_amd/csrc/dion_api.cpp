@@ -16,6 +16,7 @@
 #include <deque>
 #include <functional>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -48,6 +49,7 @@ void launch_copy_unselected(bool bf16, const MatDesc* descs, int nmat, int64_t r
 void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int nmat, int total, int slot,
                    const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
+void launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
 void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
                      const double* coef, int K, unsigned long long restarts, int in_fmt, int out_fmt, int update,
                      float keep, hipStream_t s);
@@ -1271,10 +1273,12 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return pa < pb + nb && pb < pa + na;
 }
 
+// by_value: upload the plan header as kernel arguments (no pinned staging
+// buffer), for the allocation-free entry point
 int run(const Plan& P, const void* const* M, void* const* out, const void* const* grad, int batch, int dtype,
         int grad_dtype, float beta, bool step_mode, int32_t* sel_idx, void* workspace, size_t ws_bytes,
         hipStream_t stream, const void* const* Qs = nullptr, double* keys_out = nullptr,
-        const float* upd_alpha = nullptr) {
+        const float* upd_alpha = nullptr, bool by_value = false) {
   if (!workspace) return fail(DION_E_WORKSPACE, "workspace is NULL");
   if (((uintptr_t)workspace & 255) != 0) return fail(DION_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (ws_bytes < P.total)
@@ -1326,8 +1330,12 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
   std::memcpy(blob.data() + P.off_ints, P.ints.data(), sizeof(int) * P.ints.size());
   std::memcpy(blob.data() + P.off_ranges, P.range_ints.data(), sizeof(int) * P.range_ints.size());
   if (P.host_scalars) std::memcpy(blob.data() + P.off_scalars, P.hscal.data(), sizeof(MatScalars) * P.hscal.size());
-  int rc = upload(blob.data(), blob.size(), ws, stream);
-  if (rc) return rc;
+  if (by_value) {
+    launch_upload(ws, blob.data(), blob.size(), stream);
+  } else {
+    const int rc = upload(blob.data(), blob.size(), ws, stream);
+    if (rc) return rc;
+  }
 
   const MatDesc* d_descs = (const MatDesc*)(ws + P.off_descs);
   MatScalars* d_scal = (MatScalars*)(ws + P.off_scalars);
@@ -1723,6 +1731,36 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   return DION_OK;
 }
 
+// ------------------------------------------------ allocation-free scratch
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): dion_orth_batched_noalloc runs the plan of
+// dion_orth_batched in this fixed array instead of a caller's workspace.  Each
+// device that the library runs on holds its own copy until the process ends.
+// In host code `scratch` only names the array; its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[DION_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(DION_E_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress of the scratch array", e);
+    if (!ptr || ((uintptr_t)ptr & 255) != 0) return fail(DION_E_HIP, "scratch array address is not 256-byte aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DION_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1757,6 +1795,30 @@ int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* 
   if (rc) return rc;
   return run(P, M, out, nullptr, batch, dtype, dtype, 0.f, false, sel_idx, workspace, workspace_bytes,
              (hipStream_t)stream);
+}
+
+int dion_orth_batched_noalloc(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,
+                              int32_t dtype, const dion_ns_params* p, int32_t* sel_idx, void* stream) {
+  g_last_error.clear();
+  Params prm;
+  int rc = parse_params(p, dtype, false, prm);
+  if (rc) return rc;
+  Plan P;
+  rc = build_plan(shapes, batch, dtype, prm, false, P);
+  if (rc) return rc;
+  if (P.total > (size_t)DION_NOALLOC_SCRATCH_BYTES)
+    return fail(DION_E_WORKSPACE, "this batch needs " + std::to_string(P.total) +
+                                      " bytes of scratch; dion_orth_batched_noalloc holds " +
+                                      std::to_string((size_t)DION_NOALLOC_SCRATCH_BYTES) +
+                                      " (use dion_orth_batched with a workspace)");
+  const size_t es = dtype_bytes(dtype);
+  rc = check_ptrs(M, out, shapes, batch, es, es);
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return run(P, M, out, nullptr, batch, dtype, dtype, 0.f, false, sel_idx, ws, (size_t)DION_NOALLOC_SCRATCH_BYTES,
+             (hipStream_t)stream, nullptr, nullptr, nullptr, true);
 }
 
 int dion_orth_batched_simple(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,

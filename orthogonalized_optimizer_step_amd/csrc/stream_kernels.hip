@@ -9,6 +9,8 @@
 // the exact stored values), larger first, ties to the lower row index.
 // Momentum: the summary's flow (输入输出流程) updates the momentum first; the
 // fp32 buffer is updated by two separately rounded fp32 operations.
+#include <cstring>
+
 #include "dion_internal.h"
 
 namespace dion {
@@ -827,6 +829,20 @@ __global__ void k_scale_combine(MatScalars* __restrict__ scalars, int nmat) {
   scalars[i].x0_alpha = (float)scalars[i].x0_alpha64;
 }
 
+// ------------------------------------------------- plan upload by value
+// The allocation-free entry point has no pinned staging buffer: the plan
+// header travels to the device as kernel arguments, 2 KB per launch, and a
+// copy kernel stores it.  The arguments are copied at launch, so the host
+// blob may be reused at once.
+constexpr int UPLOAD_WORDS = 512;
+struct UploadChunk {
+  uint32_t w[UPLOAD_WORDS];
+};
+
+__global__ __launch_bounds__(256) void k_upload(uint32_t* __restrict__ dst, UploadChunk c, int nwords) {
+  for (int i = threadIdx.x; i < nwords; i += 256) dst[i] = c.w[i];
+}
+
 // ---------------------------------------------------------------- launchers
 static inline unsigned row_blocks(int64_t rows) { return (unsigned)((rows + 3) / 4); }
 
@@ -914,6 +930,17 @@ void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int 
   if (total <= 0) return;
   if (fp64_path) hipLaunchKernelGGL(k_unpack<double>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, slot, scalars, scale, use_nu2 ? 1 : 0);
   else hipLaunchKernelGGL(k_unpack<_Float16>, dim3(total), dim3(256), 0, s, descs, prefix, nmat, total, slot, scalars, scale, use_nu2 ? 1 : 0);
+}
+
+// bytes: a multiple of 4; src: host memory, read before this returns
+void launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  for (size_t w0 = 0; w0 < words; w0 += UPLOAD_WORDS) {
+    UploadChunk c;
+    const int n = (int)(words - w0 < (size_t)UPLOAD_WORDS ? words - w0 : (size_t)UPLOAD_WORDS);
+    memcpy(c.w, (const uint32_t*)src + w0, 4 * (size_t)n);
+    hipLaunchKernelGGL(k_upload, dim3(1), dim3(256), 0, s, (uint32_t*)dst + w0, c, n);
+  }
 }
 
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s) {
