@@ -46,6 +46,8 @@ def parse():
                     help="row-subset workload only: fuse the weight update into the step (bf16 weights, "
                          "lr 0.02 times sqrt(max(1, rows/cols)), weight decay 0.1)")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--workspace-gib", type=float, default=None,
+                    help="cap the workspace at this many GiB: the batch runs in waves of matrices that fit it")
     ap.add_argument("--summarize", metavar="DIR",
                     help="print a text summary of the rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--profile", action="store_true",
@@ -96,7 +98,15 @@ def cpu_baseline(wl, Ms, seconds, torch):
         done.append(f"{M.shape[0]}x{M.shape[1]}")
         if t_total >= seconds:
             break
-    return {"value": params / t_total, "unit": "params/s", "cores": int(cores), "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": params / t_total, "unit": "params/s", "cores": int(cores), "nproc": int(nproc),
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{len(done)} whole matrices of layer 0 ({', '.join(done)}; {params/1e6:.1f}M params), "
                       + ("one full row-subset step each (fp32 momentum, selection, fp64 Gram-NS of the selected "
                          "rows)" if step_mode else "full fp64 Gram-NS") +
@@ -230,7 +240,15 @@ def cpu_baseline_lowrank(grads, Qs, seconds):
         done.append(f"{G.shape[0]}x{G.shape[1]}")
         if t_total >= seconds:
             break
-    return {"value": params / t_total, "unit": "params/s", "cores": int(cores), "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": params / t_total, "unit": "params/s", "cores": int(cores), "nproc": int(nproc),
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{len(done)} whole matrices of layer 0 ({', '.join(done)}; {params/1e6:.1f}M params), "
                       f"one fp64 Orth-Dion step at rank {LOWRANK_RANK}, {t_total:.1f} s"}
 
@@ -340,8 +358,10 @@ def main():
     dev = torch.device("cuda:0")
     Ms = make_inputs(wl, torch)
     step_mode = wl.name.endswith("rows")
+    budget = int(args.workspace_gib * (1 << 30)) if args.workspace_gib else None
     orth = dion.Orthogonalizer(wl.shapes, wl.dtype, wl.coeffs, wl.n_iter, wl.restart_every, wl.restart_mask,
-                               wl.safety, wl.row_frac, "auto", device=dev, step_mode=step_mode)
+                               wl.safety, wl.row_frac, "auto", device=dev, step_mode=step_mode,
+                               workspace_budget=budget)
     if args.update and not step_mode:
         print(json.dumps({"error": "--update needs the row-subset workload (llama3_8b_rows)"}))
         sys.exit(2)
@@ -451,7 +471,8 @@ def main():
                                f"{len(wl.shapes)} matrices, {params/1e9:.3f} G params, "
                                f"K={wl.n_iter}, restart_every={wl.restart_every}, restart_mask={wl.restart_mask}, "
                                f"safety={wl.safety}, row_frac={wl.row_frac}",
-                   "matrices": len(wl.shapes), "params": params, "n_iter": wl.n_iter},
+                   "matrices": len(wl.shapes), "params": params, "n_iter": wl.n_iter,
+                   **({"workspace_bytes": orth.ws_bytes} if budget else {})},
         "useful_tflops": useful / (ms_per_step * 1e-3) / 1e12,
         "useful_pct_peak": 100.0 * useful / (ms_per_step * 1e-3) / 1e12 / peak,
         "mfma_tflops": raw_total / (ms_per_step * 1e-3) / 1e12,

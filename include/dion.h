@@ -19,9 +19,11 @@
  *
  * Per matrix M (R x C, row-major, densely packed), with k = ceil(row_frac*R)
  * (clamped to [1, R]; x = row_frac*R is shrunk by a relative 1e-6 first):
- *   1. rows are ranked by squared L2 norm (fp64 from the stored values),
- *      larger first, ties to the lower row index; the top k are selected and
- *      kept in ascending row order (all rows when row_frac = 1);
+ *   1. rows are ranked by squared L2 norm: the exact sum of the squares of
+ *      the stored values, rounded once to the nearest double (ties to even),
+ *      which no summation order changes; larger first, equal keys to the
+ *      lower row index; the top k are selected and kept in ascending row
+ *      order (all rows when row_frac = 1);
  *   2. S = M[selected]; if S is tall (k > C) it is transposed so that the
  *      Gram matrix is formed on the smaller side m = min(k, C);
  *   3. X = S / ||S||_F (a zero S gives zero output rows);
@@ -41,10 +43,14 @@
  *     the caller's `workspace` (device memory, at least
  *     dion_workspace_size() bytes, 256-byte aligned).  The one exception is
  *     dion_orth_batched_noalloc, whose scratch is a fixed array that each
- *     device holds for the life of the process.
+ *     device holds for the life of the process (and dion_lowrank_step's
+ *     rocBLAS handle, see there).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
- *     work on it and return without synchronizing; host arrays are only read
- *     during the call.  Two calls must not share a workspace concurrently.
+ *     work on it and return without waiting for the device: the plan header
+ *     goes up through a ring of pinned host buffers, each refilled only once
+ *     its copy has completed, or as kernel arguments while all of them are in
+ *     flight.  Host arrays are only read during the call.  Two calls must not
+ *     share a workspace concurrently.
  *   - Errors are detected on the host before any launch and returned as a
  *     negative dion_status; dion_last_error() gives a message for the calling
  *     thread.  NaN/Inf inputs are not checked: the output is unspecified.
@@ -80,7 +86,13 @@ typedef enum { DION_BF16 = 0, DION_FP32 = 1, DION_FP16 = 2 } dion_dtype;
  *     error against the exact result: a few 1e-3 on low-rank-plus-noise
  *     momentum at 5 to 8 iterations (gate 2e-2); it grows with n_iter, as
  *     each iteration amplifies the rounding in the small singular directions
- *     (about 1.4e-2 at 12 and 2e-2 at 16 iterations on small blocks).
+ *     (about 1.4e-2 at 12 and 2e-2 at 16 iterations on small blocks).  A
+ *     call that would run a matrix on this path with more than 12 iterations,
+ *     with slopes a_k / s multiplying to more than 3.4445^12, or with
+ *     keep_schedule and a run of more than 5 iterations between restarts is
+ *     refused (DION_E_UNSUPPORTED); DION_PREC_FP64 takes it.  Matrices with a
+ *     Gram side of at most 64 and a long side of at most 1024, or a Gram side
+ *     of at most 16, run in fp64 in one launch on every precision setting.
  *   DION_PREC_FP64: fp64 arithmetic throughout (error ~1e-12; gate 1e-4).
  *   DION_PREC_AUTO: FP64 for DION_FP32 inputs of dion_orth_batched, MFMA16
  *     otherwise (bf16 and fp16). */
@@ -95,7 +107,7 @@ typedef struct {
  *   ns_coeffs     host array of n_coeff_sets * 3 floats (a, b, c); NULL means
  *                 the fixed quintic (3.4445, -4.7750, 2.0315)
  *   n_coeff_sets  1 (same triple every iteration) or n_iter
- *   n_iter        K >= 1 (at most 64)
+ *   n_iter        K >= 1 (at most 64; see DION_PREC_MFMA16 for that path's range)
  *   restart_every restart after every restart_every-th iteration (0 = none)
  *   restart_mask  if nonzero, bit (k-1) set = restart after iteration k;
  *                 overrides restart_threshold and restart_every.  Never
@@ -156,7 +168,22 @@ int dion_restart_points(const dion_ns_params* p, int32_t* after, int32_t cap);
 size_t dion_workspace_size(const dion_shape* shapes, int32_t batch, int32_t dtype,
                            const dion_ns_params* p);
 
+/* Workspace for running the batch within at most `cap` bytes (the megabatch
+ * of the Dion3 abstract, sized to fit beside the model's own memory): the
+ * full size when it fits, else the largest of the waves the call will run
+ * (see dion_orth_batched); 0 if one matrix alone needs more than `cap`, or on
+ * invalid arguments.  Like dion_workspace_size it also covers the row-subset
+ * step for dtype = DION_FP32. */
+size_t dion_workspace_size_capped(const dion_shape* shapes, int32_t batch, int32_t dtype,
+                                  const dion_ns_params* p, size_t cap);
+
 /* Orthogonalize a batch of momentum matrices in one megabatched pass.
+ * Workspace: dion_workspace_size() bytes run the batch as one wave (one
+ * grouped launch per phase over every matrix).  A smaller workspace runs it as
+ * consecutive waves of matrices, each wave's plan fitting workspace_bytes, one
+ * after another on the stream, with the same kernels and tile sizes: the
+ * results are bit-identical.  DION_E_WORKSPACE if one matrix alone does not
+ * fit (dion_workspace_size_capped gives the size a cap leads to).
  *   M[i]     device, R_i x C_i of `dtype`, read only
  *   out[i]   device, R_i x C_i of `dtype`, must not overlap any M[j]
  *   sel_idx  optional device int32 buffer of sum_i k_i entries: receives each
@@ -200,7 +227,8 @@ int dion_orth_batched_simple(const void* const* M, void* const* out, const dion_
  *   out[i]   device bf16 R x C: the orthogonalized selected rows of the new E,
  *            the raw new E (rounded to bf16) in the other rows
  *   p        as above; p->precision must be AUTO or MFMA16
- * Workspace: dion_workspace_size(shapes, batch, DION_FP32, p). */
+ * Workspace: dion_workspace_size(shapes, batch, DION_FP32, p), or less for
+ * waves as in dion_orth_batched. */
 int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* out,
                         const dion_shape* shapes, int32_t batch, int32_t grad_dtype, float beta,
                         const dion_ns_params* p, int32_t* sel_idx, void* workspace,
@@ -219,7 +247,7 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
  *                 matrix's shape scale (chosen by the caller)
  *   weight_decay  decoupled weight decay factor (0 = none)
  * No separate output is written.  Workspace: dion_workspace_size(shapes,
- * batch, DION_FP32, p). */
+ * batch, DION_FP32, p), or less for waves as in dion_orth_batched. */
 int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* const* W,
                                const dion_shape* shapes, int32_t batch, int32_t grad_dtype, int32_t w_dtype,
                                float beta, const float* alpha, float weight_decay, const dion_ns_params* p,

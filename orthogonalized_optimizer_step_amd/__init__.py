@@ -56,20 +56,36 @@ def _ptrs(tensors):
     return (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
 
 
-def _check_tensors(ts, dtype=None):
+def _check_tensors(ts, dtype=None, shapes=None, what="matrices", device=True):
+    """Refuse, before any C call, a list that does not match the batch the
+    call was planned for: its length and each shape (when ``shapes`` is
+    given), the dtype, and (with ``device``) 2-D contiguous device tensors."""
+    ts = list(ts)
+    if shapes is not None:
+        if len(ts) != len(shapes):
+            raise DionError(-1, f"{what}: {len(ts)} tensors for a batch of {len(shapes)}")
+        for i, (t, sh) in enumerate(zip(ts, shapes)):
+            if tuple(t.shape) != tuple(sh):
+                raise DionError(-1, f"{what}[{i}]: shape {tuple(t.shape)}, planned {tuple(sh)}")
     for t in ts:
-        if t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
-            raise DionError(-1, "matrices must be 2-D, contiguous, on the GPU")
         if dtype is not None and t.dtype != dtype:
-            raise DionError(-1, f"expected {dtype}, got {t.dtype}")
+            raise DionError(-1, f"{what}: expected {dtype}, got {t.dtype}")
+        if device and (t.dim() != 2 or not t.is_cuda or not t.is_contiguous()):
+            raise DionError(-1, f"{what} must be 2-D, contiguous, on the GPU")
 
 
 def workspace_size(shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
-                   safety=1.0, row_frac=1.0, precision="auto", restart_threshold=0.0, keep_schedule=False) -> int:
+                   safety=1.0, row_frac=1.0, precision="auto", restart_threshold=0.0, keep_schedule=False,
+                   budget=None) -> int:
+    """Workspace bytes of a call; with ``budget``, of the call run in waves that
+    fit it (dion_workspace_size_capped)."""
     p, keep = _params(coeffs, n_iter, restart_every, restart_mask, safety, row_frac, precision, restart_threshold,
                       keep_schedule=keep_schedule)
     code = {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
-    n = lib.dion_workspace_size(_shapes(shapes), len(shapes), code, ctypes.byref(p))
+    if budget is None:
+        n = lib.dion_workspace_size(_shapes(shapes), len(shapes), code, ctypes.byref(p))
+    else:
+        n = lib.dion_workspace_size_capped(_shapes(shapes), len(shapes), code, ctypes.byref(p), int(budget))
     if n == 0:
         raise DionError(-1, lib.dion_last_error().decode())
     return int(n)
@@ -91,10 +107,17 @@ def restart_points(coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, sa
     return [int(buf[i]) for i in range(n)]
 
 
-def _workspace(nbytes, device, workspace):
+def _workspace(nbytes, device, workspace, stream=None):
+    """The caller's workspace, or a new one.  A new one is allocated in the
+    stream the call runs on, so that the caching allocator does not hand its
+    memory to other work before that stream has finished with it."""
     import torch
     if workspace is None:
-        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        if stream is not None and str(device) != "cpu":
+            with torch.cuda.stream(stream):
+                workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        else:
+            workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-workspace.data_ptr()) % 256
     if workspace.numel() - off < nbytes:
         raise DionError(-3, f"workspace too small: need {nbytes} bytes")
@@ -107,13 +130,38 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream, *tensors):
+    """Tensors this binding allocated and a call on a stream other than the
+    current one writes: tell the caching allocator that stream uses them."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is None:
+            continue
+        for x in (t if isinstance(t, (list, tuple)) else [t]):
+            x.record_stream(stream)
+
+
+def _dtype_of(dtype):
+    import torch
+    return {"bf16": torch.bfloat16, "fp32": torch.float32, "fp16": torch.float16, DION_BF16: torch.bfloat16,
+            DION_FP32: torch.float32, DION_FP16: torch.float16}.get(dtype, dtype)
+
+
+def _sel_check(sel_idx, n):
+    if sel_idx is not None:
+        import torch
+        if sel_idx.dtype != torch.int32 or sel_idx.numel() < n or not sel_idx.is_cuda or not sel_idx.is_contiguous():
+            raise DionError(-1, f"sel_idx must be a contiguous int32 GPU tensor of at least {n} entries")
+
+
 class Orthogonalizer:
     """A reusable megabatch: fixed shapes, dtype and hyper-parameters, with
     its own workspace, so repeated calls only marshal pointers."""
 
     def __init__(self, shapes, dtype="bf16", coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0,
                  safety=1.0, row_frac=1.0, precision="auto", device="cuda", step_mode=False, restart_threshold=0.0,
-                 ef="raw", keep_schedule=False):
+                 ef="raw", keep_schedule=False, stream=None, workspace_budget=None):
         import torch
         self.shapes = [tuple(int(x) for x in s) for s in shapes]
         self.dtype = dtype
@@ -122,10 +170,14 @@ class Orthogonalizer:
                                       restart_threshold, ef, keep_schedule)
         self._shp = _shapes(self.shapes)
         code = DION_FP32 if step_mode else {"bf16": DION_BF16, "fp32": DION_FP32, "fp16": DION_FP16}.get(dtype, dtype)
-        self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
+        if workspace_budget is None:
+            self.ws_bytes = lib.dion_workspace_size(self._shp, len(self.shapes), code, ctypes.byref(self._p))
+        else:   # waves of matrices that fit the budget
+            self.ws_bytes = lib.dion_workspace_size_capped(self._shp, len(self.shapes), code, ctypes.byref(self._p),
+                                                           int(workspace_budget))
         if self.ws_bytes == 0:
             raise DionError(-1, lib.dion_last_error().decode())
-        self._ws_tensor, self._ws, self._ws_len = _workspace(self.ws_bytes, device, None)
+        self._ws_tensor, self._ws, self._ws_len = _workspace(self.ws_bytes, device, None, stream)
         self.selected = [int(lib.dion_selected_rows(r, ctypes.c_float(float(row_frac)))) for r, _ in self.shapes]
         self.total_selected = sum(self.selected)
 
@@ -133,6 +185,14 @@ class Orthogonalizer:
         return float(lib.dion_useful_flops(self._shp, len(self.shapes), ctypes.byref(self._p)))
 
     def __call__(self, Ms, outs, sel_idx=None, stream=None):
+        if self.step_mode:
+            raise DionError(-1, "this batch was planned for the row-subset step: use step() or step_update()")
+        dt = _dtype_of(self.dtype)
+        for ts, what in ((Ms, "Ms"), (outs, "outs")):
+            _check_tensors(ts, dt, self.shapes, what, device=False)
+        for ts, what in ((Ms, "Ms"), (outs, "outs")):
+            _check_tensors(ts, dt, self.shapes, what)
+        _sel_check(sel_idx, self.total_selected)
         code = _dtype_code(Ms[0].dtype)
         rc = lib.dion_orth_batched(_ptrs(Ms), _ptrs(outs), self._shp, len(self.shapes), code, ctypes.byref(self._p),
                                    ctypes.c_void_p(sel_idx.data_ptr() if sel_idx is not None else None),
@@ -142,6 +202,17 @@ class Orthogonalizer:
 
     def step_update(self, Es, grads, Ws, beta, alphas, weight_decay=0.0, sel_idx=None, stream=None):
         """Row-subset step with the fused weight update W <- W (1 - wd) - alpha_i U."""
+        import torch
+        if not self.step_mode:
+            raise DionError(-1, "this batch was not planned for the row-subset step")
+        if len(alphas) != len(self.shapes):
+            raise DionError(-1, f"{len(alphas)} alphas for a batch of {len(self.shapes)}")
+        lists = ((Es, torch.float32, "Es"), (grads, grads[0].dtype if len(grads) else None, "grads"),
+                 (Ws, Ws[0].dtype if len(Ws) else None, "Ws"))
+        for dev in (False, True):
+            for ts, dt, what in lists:
+                _check_tensors(ts, dt, self.shapes, what, device=dev)
+        _sel_check(sel_idx, self.total_selected)
         gcode = _dtype_code(grads[0].dtype)
         wcode = _dtype_code(Ws[0].dtype)
         al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
@@ -153,6 +224,15 @@ class Orthogonalizer:
         return Ws
 
     def step(self, Es, grads, outs, beta, sel_idx=None, stream=None):
+        import torch
+        if not self.step_mode:
+            raise DionError(-1, "this batch was not planned for the row-subset step")
+        lists = ((Es, torch.float32, "Es"), (grads, grads[0].dtype if len(grads) else None, "grads"),
+                 (outs, torch.bfloat16, "outs"))
+        for dev in (False, True):
+            for ts, dt, what in lists:
+                _check_tensors(ts, dt, self.shapes, what, device=dev)
+        _sel_check(sel_idx, self.total_selected)
         code = _dtype_code(grads[0].dtype)
         rc = lib.dion_rowsubset_step(_ptrs(Es), _ptrs(grads), _ptrs(outs), self._shp, len(self.shapes), code,
                                      float(beta), ctypes.byref(self._p),
@@ -164,7 +244,7 @@ class Orthogonalizer:
 
 def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, restart_mask=0, safety=1.0,
                  row_frac=1.0, precision="auto", return_indices=False, stream=None, restart_threshold=0.0,
-                 keep_schedule=False):
+                 keep_schedule=False, workspace_budget=None):
     """Orthogonalize a list of 2-D bf16 or fp32 CUDA tensors in one megabatched call.
 
     Returns the list of outputs (same shapes and dtype), and with
@@ -175,12 +255,14 @@ def orth_batched(Ms, outs=None, coeffs=QUINTIC, n_iter=5, restart_every=0, resta
     dt = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(Ms[0].dtype, "fp32")
     orth = Orthogonalizer([tuple(M.shape) for M in Ms], dt, coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, precision, device=Ms[0].device, restart_threshold=restart_threshold,
-                          keep_schedule=keep_schedule)
-    if outs is None:
+                          keep_schedule=keep_schedule, stream=stream, workspace_budget=workspace_budget)
+    new_outs = outs is None
+    if new_outs:
         outs = [torch.empty_like(M) for M in Ms]
     _check_tensors(outs, Ms[0].dtype)
     sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Ms[0].device) if return_indices else None
     orth(Ms, outs, sel, stream)
+    _on_stream(stream, outs if new_outs else None, sel)
     if not return_indices:
         return outs
     return outs, list(torch.split(sel, orth.selected))
@@ -222,25 +304,27 @@ def rowsubset_step(Es, grads, beta, outs=None, coeffs=QUINTIC, n_iter=5, restart
     _check_tensors(grads, grads[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
-                          restart_threshold=restart_threshold, ef=ef, keep_schedule=keep_schedule)
-    if outs is None:
+                          restart_threshold=restart_threshold, ef=ef, keep_schedule=keep_schedule, stream=stream)
+    new_outs = outs is None
+    if new_outs:
         outs = [torch.empty(E.shape, dtype=torch.bfloat16, device=E.device) for E in Es]
     _check_tensors(outs, torch.bfloat16)
     sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
     orth.step(Es, grads, outs, beta, sel, stream)
+    _on_stream(stream, outs if new_outs else None, sel)
     if not return_indices:
         return outs
     return outs, list(torch.split(sel, orth.selected))
 
 
 # ------------------------------------------------------------ phase entry points
-def _phase_ws(phase, shapes, dtype_code, precision, row_frac, device):
+def _phase_ws(phase, shapes, dtype_code, precision, row_frac, device, stream=None):
     n = lib.dion_phase_workspace_size(PHASE[phase], _shapes(shapes), len(shapes), dtype_code,
                                       PREC[precision] if isinstance(precision, str) else int(precision),
                                       ctypes.c_float(float(row_frac)))
     if n == 0:
         raise DionError(-1, lib.dion_last_error().decode())
-    return _workspace(n, device, None)
+    return _workspace(n, device, None, stream)
 
 
 def _gram_side(shape):
@@ -254,13 +338,14 @@ def rowkeys_topk(Ms, row_frac=1.0, stream=None):
     _check_tensors(Ms, Ms[0].dtype)
     shapes = [tuple(M.shape) for M in Ms]
     code = _dtype_code(Ms[0].dtype)
-    keep, ws, wl = _phase_ws("rowkeys_topk", shapes, code, "mfma16", row_frac, Ms[0].device)
+    keep, ws, wl = _phase_ws("rowkeys_topk", shapes, code, "mfma16", row_frac, Ms[0].device, stream)
     ks = [int(lib.dion_selected_rows(r, ctypes.c_float(float(row_frac)))) for r, _ in shapes]
     keys = torch.empty(sum(r for r, _ in shapes), dtype=torch.float64, device=Ms[0].device)
     idx = torch.empty(sum(ks), dtype=torch.int32, device=Ms[0].device)
     check(lib.dion_rowkeys_topk_batched(_ptrs(Ms), _shapes(shapes), len(Ms), code, ctypes.c_float(float(row_frac)),
                                         ctypes.c_void_p(keys.data_ptr()), ctypes.c_void_p(idx.data_ptr()),
                                         ctypes.c_void_p(ws), wl, _stream(stream)))
+    _on_stream(stream, keys, idx)
     return list(torch.split(keys, [r for r, _ in shapes])), list(torch.split(idx, ks))
 
 
@@ -270,11 +355,12 @@ def syrk(Xs, precision="auto", stream=None):
     _check_tensors(Xs, Xs[0].dtype)
     shapes = [tuple(X.shape) for X in Xs]
     code = _dtype_code(Xs[0].dtype)
-    keep, ws, wl = _phase_ws("syrk", shapes, code, precision, 1.0, Xs[0].device)
+    keep, ws, wl = _phase_ws("syrk", shapes, code, precision, 1.0, Xs[0].device, stream)
     Gs = [torch.empty((_gram_side(s), _gram_side(s)), dtype=torch.float32, device=Xs[0].device) for s in shapes]
     check(lib.dion_syrk_batched(_ptrs(Xs), _ptrs(Gs), _shapes(shapes), len(Xs), code,
                                 PREC[precision] if isinstance(precision, str) else int(precision),
                                 ctypes.c_void_p(ws), wl, _stream(stream)))
+    _on_stream(stream, Gs)
     return Gs
 
 
@@ -285,12 +371,13 @@ def sympoly(Gs, coeffs=QUINTIC, precision="auto", stream=None):
     ms = [int(G.shape[0]) for G in Gs]
     if any(G.shape[0] != G.shape[1] for G in Gs):
         raise DionError(-1, "G must be square")
-    keep, ws, wl = _phase_ws("sympoly", [(m, m) for m in ms], DION_FP32, precision, 1.0, Gs[0].device)
+    keep, ws, wl = _phase_ws("sympoly", [(m, m) for m in ms], DION_FP32, precision, 1.0, Gs[0].device, stream)
     Ps = [torch.empty_like(G) for G in Gs]
     co = (ctypes.c_float * 3)(*[float(x) for x in coeffs])
     check(lib.dion_sympoly_batched(_ptrs(Gs), _ptrs(Ps), (ctypes.c_int32 * len(ms))(*ms), len(Gs), co,
                                    PREC[precision] if isinstance(precision, str) else int(precision),
                                    ctypes.c_void_p(ws), wl, _stream(stream)))
+    _on_stream(stream, Ps)
     return Ps
 
 
@@ -304,11 +391,12 @@ def apply(Qs, Xs, precision="auto", stream=None):
         if tuple(Q.shape) != (_gram_side(s), _gram_side(s)):
             raise DionError(-1, f"Q must be {_gram_side(s)} x {_gram_side(s)} for X of shape {s}")
     code = _dtype_code(Xs[0].dtype)
-    keep, ws, wl = _phase_ws("apply", shapes, code, precision, 1.0, Xs[0].device)
+    keep, ws, wl = _phase_ws("apply", shapes, code, precision, 1.0, Xs[0].device, stream)
     Ys = [torch.empty_like(X) for X in Xs]
     check(lib.dion_apply_batched(_ptrs(Qs), _ptrs(Xs), _ptrs(Ys), _shapes(shapes), len(Xs), code,
                                  PREC[precision] if isinstance(precision, str) else int(precision),
                                  ctypes.c_void_p(ws), wl, _stream(stream)))
+    _on_stream(stream, Ys)
     return Ys
 
 
@@ -322,9 +410,10 @@ def rowsubset_step_update(Es, grads, Ws, beta, alphas, weight_decay=0.0, coeffs=
     _check_tensors(Ws, Ws[0].dtype)
     orth = Orthogonalizer([tuple(E.shape) for E in Es], "fp32", coeffs, n_iter, restart_every, restart_mask,
                           safety, row_frac, "mfma16", device=Es[0].device, step_mode=True,
-                          restart_threshold=restart_threshold, ef=ef, keep_schedule=keep_schedule)
+                          restart_threshold=restart_threshold, ef=ef, keep_schedule=keep_schedule, stream=stream)
     sel = torch.empty(orth.total_selected, dtype=torch.int32, device=Es[0].device) if return_indices else None
     orth.step_update(Es, grads, Ws, beta, alphas, weight_decay, sel, stream)
+    _on_stream(stream, sel)
     if not return_indices:
         return Ws
     return Ws, list(torch.split(sel, orth.selected))
@@ -359,7 +448,8 @@ def lowrank_step(Ms, grads, Qs, beta, mode="qr", outs=None, out_dtype=None, work
     for (R, C), Q in zip(shapes, Qs):
         if tuple(Q.shape) != (C, min(rank, R, C)):
             raise DionError(-1, f"Q must be {C} x {min(rank, R, C)} for a {R} x {C} matrix at rank {rank}")
-    if outs is None:
+    new_outs = outs is None
+    if new_outs:
         dt = out_dtype if out_dtype is not None else torch.bfloat16
         outs = [torch.empty(s, dtype=dt, device=Ms[0].device) for s in shapes]
     _check_tensors(outs, outs[0].dtype)
@@ -367,11 +457,12 @@ def lowrank_step(Ms, grads, Qs, beta, mode="qr", outs=None, out_dtype=None, work
     nbytes = lib.dion_lowrank_workspace_size(_shapes(shapes), len(shapes), rank, ocode)
     if nbytes == 0:
         raise DionError(-1, lib.dion_last_error().decode())
-    keep, ws, wl = _workspace(nbytes, Ms[0].device, workspace)
+    keep, ws, wl = _workspace(nbytes, Ms[0].device, workspace, stream)
     check(lib.dion_lowrank_step(_ptrs(Ms), _ptrs(grads), _ptrs(Qs), _ptrs(outs), _shapes(shapes), len(Ms),
                                 _dtype_code(grads[0].dtype), ocode, rank, float(beta),
                                 LOWRANK_MODE[mode] if isinstance(mode, str) else int(mode),
                                 ctypes.c_void_p(ws), wl, _stream(stream)))
+    _on_stream(stream, outs if new_outs else None)
     return outs
 
 

@@ -43,7 +43,7 @@ EXPORTS = (
     "dion_last_error", "dion_version", "dion_profile_enable", "dion_profile_count",
     "dion_profile_get", "dion_phase_workspace_size", "dion_rowkeys_topk_batched", "dion_syrk_batched",
     "dion_sympoly_batched", "dion_apply_batched", "dion_rowsubset_step_update", "dion_restart_points",
-    "dion_lowrank_workspace_size", "dion_lowrank_step", "dion_orth_batched_noalloc",
+    "dion_lowrank_workspace_size", "dion_lowrank_step", "dion_orth_batched_noalloc", "dion_workspace_size_capped",
 )
 
 
@@ -72,6 +72,8 @@ def _load():
     lib.dion_workspace_size.restype = sz
     lib.dion_orth_batched.argtypes = [pp, pp, shp, i32, i32, prm, vp, vp, sz, vp]
     lib.dion_orth_batched.restype = ctypes.c_int
+    lib.dion_workspace_size_capped.argtypes = [shp, i32, i32, prm, sz]
+    lib.dion_workspace_size_capped.restype = sz
     lib.dion_orth_batched_noalloc.argtypes = [pp, pp, shp, i32, i32, prm, vp, vp]
     lib.dion_orth_batched_noalloc.restype = ctypes.c_int
     lib.dion_orth_batched_simple.argtypes = [pp, pp, shp, i32, i32, ctypes.POINTER(ctypes.c_float), i32, i32,

@@ -217,6 +217,7 @@ struct MatPlan {
   bool acc;  // restarts after the first start from X0 with the accumulated factor
   bool tiny = false;  // runs in the one-workgroup fp64 kernel
   size_t off[N_SLOTS];
+  size_t bytes = 0;   // its buffers in the workspace
 };
 
 struct Plan {
@@ -256,6 +257,7 @@ struct Plan {
   size_t off_ranges = 0;
   int max_ranges = 0;
   std::vector<int> range_ints;
+  int bm[4] = {0, 0, 0, 0};   // tile sizes of the symmetric, restart-apply, full and final products
   std::vector<int> ints;
   std::vector<Table> tabs;
   std::vector<Step> steps;
@@ -319,8 +321,10 @@ void balance_ranges(Plan& P, int table, const PhaseArgs& pa, Step& g) {
   P.range_ints.insert(P.range_ints.end(), r, r + 9);
 }
 
+// bm_force: the four tile sizes to use (a wave of a larger call takes the
+// whole call's, so that its results are bit-identical), or NULL to choose
 int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm, bool step_mode, Plan& P,
-               int grad_es = 2) {
+               int grad_es = 2, const int* bm_force = nullptr) {
   if (!shapes) return fail(DION_E_INVAL, "shapes is NULL");
   if (batch < 1) return fail(DION_E_INVAL, "batch must be >= 1");
   P.fp64 = prm.fp64;
@@ -440,23 +444,27 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     if (P.fp64) return 64;
     return total_of(counts(256)) >= 512 ? 256 : 128;
   };
-  const int bm_sym = pick_bm([&](int bm) { return sym_counts(bm); });
-  const int bm_xtq = pick_bm([&](int bm) { return rect_counts(mf, bm, true); });
+  const int bm_sym = bm_force ? bm_force[0] : pick_bm([&](int bm) { return sym_counts(bm); });
+  const int bm_xtq = bm_force ? bm_force[1] : pick_bm([&](int bm) { return rect_counts(mf, bm, true); });
   auto full_counts = [&](int bm) {
     std::vector<int> c;
     for (int i : mf) { int T = P.mats[i].m_pad / bm; c.push_back(T * T); }
     return c;
   };
-  const int bm_full = pick_bm([&](int bm) { return full_counts(bm); });
+  const int bm_full = bm_force ? bm_force[2] : pick_bm([&](int bm) { return full_counts(bm); });
   std::vector<int> wide, tall, accs, naccs;
   for (int i : mf) (P.mats[i].tall ? tall : wide).push_back(i);
   for (int i : mf) (P.mats[i].acc ? accs : naccs).push_back(i);
   const bool any_acc = !accs.empty();
-  const int bm_fin = pick_bm([&](int bm) {
+  const int bm_fin = bm_force ? bm_force[3] : pick_bm([&](int bm) {
     auto a = rect_counts(wide, bm, false), b = rect_counts(tall, bm, true);
     a.insert(a.end(), b.begin(), b.end());
     return a;
   });
+  P.bm[0] = bm_sym;
+  P.bm[1] = bm_xtq;
+  P.bm[2] = bm_full;
+  P.bm[3] = bm_fin;
   const int t_sym = add_table(P, mf, sym_counts(bm_sym));
   const int t_xtq = add_table(P, mf, rect_counts(mf, bm_xtq, true));
   const int t_full = add_table(P, mf, full_counts(bm_full));
@@ -512,11 +520,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   for (int i = 0; i < batch; ++i) {
     MatPlan& mp = P.mats[i];
     const size_t mn = (size_t)mp.m_pad * mp.n_pad, mm = (size_t)mp.m_pad * mp.m_pad;
+    const size_t first = off;
     for (int s = 0; s < N_SLOTS; ++s) mp.off[s] = 0;
     if (mp.tiny) {   // k_tiny_gns: the iterate and its restart copy, m x n fp64 each
       const size_t x = (size_t)mp.m * mp.n * 8;
       mp.off[SLOT_X] = off;   off = align256(off + x);
       mp.off[SLOT_XT0] = off; off = align256(off + x);
+      mp.bytes = off - first;
       continue;
     }
     mp.off[SLOT_X] = off;   off = align256(off + mn * es);
@@ -527,6 +537,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     }
     const int last_mm = any_acc ? SLOT_MM5 : SLOT_MM3;
     for (int s = SLOT_MM0; s <= last_mm; ++s) { mp.off[s] = off; off = align256(off + mm * es * mm_terms); }
+    mp.bytes = off - first;
   }
   P.total = off;
 
@@ -1156,11 +1167,19 @@ int build_phase_plan(int ph, const dion_shape* shapes, int batch, int dtype, int
 }
 
 // ---------------------------------------------------- pinned upload stage
+// The plan header goes to the device from a pinned host buffer with one
+// asynchronous copy.  A buffer may be refilled once the stream has passed its
+// copy (its event has completed); the host never waits for that.  The ring
+// grows to kStageSlots buffers when the host runs ahead of the device, and
+// beyond that the header travels as kernel arguments (launch_upload), which
+// needs no buffer at all.
+constexpr int kStageSlots = 8;
 struct Stage {
-  void* host[2] = {nullptr, nullptr};
-  size_t cap[2] = {0, 0};
-  hipEvent_t ev[2] = {nullptr, nullptr};
-  int next = 0;
+  void* host[kStageSlots] = {};
+  size_t cap[kStageSlots] = {};
+  hipEvent_t ev[kStageSlots] = {};
+  int n = 0;      // slots in use
+  int next = 0;   // where the search for a free slot starts
 };
 thread_local Stage g_stage;
 
@@ -1170,28 +1189,40 @@ int hip_fail(const char* what, hipError_t e) {
 
 int upload(const void* src, size_t bytes, void* dst, hipStream_t s) {
   Stage& S = g_stage;
-  const int i = S.next;
-  S.next ^= 1;
   hipError_t e;
-  if (S.ev[i]) {
-    if ((e = hipEventSynchronize(S.ev[i])) != hipSuccess) return hip_fail("hipEventSynchronize", e);
-  } else if ((e = hipEventCreateWithFlags(&S.ev[i], hipEventDisableTiming)) != hipSuccess) {
-    S.ev[i] = nullptr;
-    return hip_fail("hipEventCreateWithFlags", e);
+  int slot = -1;
+  for (int j = 0; j < S.n && slot < 0; ++j) {   // a slot whose last copy has completed
+    const int i = (S.next + j) % S.n;
+    e = hipEventQuery(S.ev[i]);
+    if (e == hipSuccess) slot = i;
+    else if (e != hipErrorNotReady) return hip_fail("hipEventQuery", e);
   }
-  if (S.cap[i] < bytes) {
-    if (S.host[i]) (void)hipHostFree(S.host[i]);
-    S.host[i] = nullptr;
-    S.cap[i] = 0;
+  if (slot < 0 && S.n < kStageSlots) {          // none free: one more slot
+    slot = S.n;
+    if ((e = hipEventCreateWithFlags(&S.ev[slot], hipEventDisableTiming)) != hipSuccess) {
+      S.ev[slot] = nullptr;
+      return hip_fail("hipEventCreateWithFlags", e);
+    }
+    ++S.n;
+  }
+  if (slot < 0) {                               // the host is kStageSlots calls ahead
+    launch_upload(dst, src, bytes, s);
+    return DION_OK;
+  }
+  S.next = (slot + 1) % S.n;
+  if (S.cap[slot] < bytes) {
+    if (S.host[slot]) (void)hipHostFree(S.host[slot]);
+    S.host[slot] = nullptr;
+    S.cap[slot] = 0;
     const size_t cap = std::max(bytes, (size_t)1 << 16);
-    if ((e = hipHostMalloc(&S.host[i], cap, hipHostMallocDefault)) != hipSuccess)
+    if ((e = hipHostMalloc(&S.host[slot], cap, hipHostMallocDefault)) != hipSuccess)
       return hip_fail("hipHostMalloc of the upload stage", e);
-    S.cap[i] = cap;
+    S.cap[slot] = cap;
   }
-  std::memcpy(S.host[i], src, bytes);
-  if ((e = hipMemcpyAsync(dst, S.host[i], bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
+  std::memcpy(S.host[slot], src, bytes);
+  if ((e = hipMemcpyAsync(dst, S.host[slot], bytes, hipMemcpyHostToDevice, s)) != hipSuccess)
     return hip_fail("hipMemcpyAsync of the plan", e);
-  if ((e = hipEventRecord(S.ev[i], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
+  if ((e = hipEventRecord(S.ev[slot], s)) != hipSuccess) return hip_fail("hipEventRecord", e);
   return DION_OK;
 }
 
@@ -1460,6 +1491,100 @@ int check_ptrs(const void* const* M, void* const* out, const dion_shape* shapes,
   return DION_OK;
 }
 
+
+// ------------------------------------------------------------------ waves
+// A call whose workspace is smaller than its whole plan runs as waves:
+// consecutive matrices whose own plan fits the workspace, one after another on
+// the call's stream (each wave is a full plan: its own selection, Gram
+// Newton-Schulz and write-out, all independent per matrix).  Waves take the
+// whole call's tile sizes, so the results are bit-identical to one wave.  The
+// whole plan bounds each wave's: a wave's header is at most the whole header,
+// and each matrix's buffers at most what the whole plan gives it.
+struct Wave {
+  int i0 = 0, n = 0;   // matrices [i0, i0 + n)
+  int64_t sel0 = 0;    // first selected-row entry of the wave
+  Plan plan;
+};
+
+int plan_waves(const dion_shape* shapes, int batch, int dtype, const Params& prm, bool step_mode, int grad_es,
+               size_t budget, std::vector<Wave>& waves, size_t& need) {
+  waves.clear();
+  waves.emplace_back();
+  Plan& full = waves.back().plan;
+  int rc = build_plan(shapes, batch, dtype, prm, step_mode, full, grad_es);
+  if (rc) return rc;
+  waves.back().n = batch;
+  need = full.total;
+  if (full.total <= budget) return DION_OK;
+  const size_t header = full.off_data;
+  std::vector<size_t> bytes(batch);
+  std::vector<int> ks(batch);
+  for (int i = 0; i < batch; ++i) {
+    bytes[i] = full.mats[i].bytes;
+    ks[i] = full.mats[i].k;
+  }
+  int bm[4];
+  std::memcpy(bm, full.bm, sizeof bm);
+  waves.clear();
+  need = 0;
+  int64_t sel = 0;
+  for (int i = 0; i < batch;) {
+    size_t acc = header;
+    int j = i;
+    while (j < batch && acc + bytes[j] <= budget) acc += bytes[j++];
+    if (j == i)
+      return fail(DION_E_WORKSPACE, "workspace too small: matrix " + std::to_string(i) + " alone needs " +
+                                        std::to_string(header + bytes[i]) + " bytes");
+    waves.emplace_back();
+    Wave& w = waves.back();
+    w.i0 = i;
+    w.n = j - i;
+    w.sel0 = sel;
+    rc = build_plan(shapes + i, j - i, dtype, prm, step_mode, w.plan, grad_es, bm);
+    if (rc) return rc;
+    if (w.plan.total > budget) return fail(DION_E_WORKSPACE, "internal: a wave exceeds its bound");
+    need = std::max(need, w.plan.total);
+    for (int t = i; t < j; ++t) sel += ks[t];
+    i = j;
+  }
+  return DION_OK;
+}
+
+// The row-subset step's fused weight update on a plan: the final apply's
+// epilogue updates the selected rows of W, a pass of its own the others.
+void make_update(Plan& P, int w_dtype, float weight_decay) {
+  P.update = true;
+  P.w_bf16 = w_dtype == DION_BF16;
+  P.keep = 1.0f - weight_decay;
+  const double wes = w_dtype == DION_BF16 ? 2.0 : 4.0;
+  // algorithmic bytes: the momentum pass writes no update rows here, and the
+  // final apply reads and writes the selected rows of W instead of writing out
+  double elems = 0.0, unsel = 0.0;
+  for (const MatPlan& mp : P.mats) {
+    elems += (double)mp.R * mp.C;
+    unsel += (double)(mp.R - mp.k) * mp.C;
+  }
+  for (Step& st : P.steps) {
+    if (st.kind == ST_MOMENTUM) st.bytes -= 2.0 * elems;
+    if (st.kind == ST_GEMM && st.epi == EPI_OUT) {
+      st.pa.out_update = 1;
+      st.pa.upd_keep = P.keep;
+      st.pa.out_fp32 = w_dtype == DION_FP32 ? 1 : 0;
+      const Table& tb = P.tabs[st.table];
+      for (int j = 0; j < tb.nmat; ++j) {
+        const MatPlan& mp = P.mats[P.ints[tb.mats_off + j]];
+        st.bytes += (2.0 * wes - 2.0) * (double)mp.m * mp.n;
+      }
+    }
+  }
+  if (P.use_idx) {
+    Step u;
+    u.kind = ST_UPDATE;
+    u.name = "update_rows";
+    u.bytes = unsel * (4.0 + 2.0 * wes) + (double)P.total_rows;   // E read, W read and written; row flags
+    P.steps.push_back(u);
+  }
+}
 
 // ------------------------------------------- low-rank (Dion / Orth-Dion) step
 // Orth-Dion explainer, technical summary: one power-iteration step from the
@@ -1780,6 +1905,23 @@ size_t dion_workspace_size(const dion_shape* shapes, int32_t batch, int32_t dtyp
   return need;
 }
 
+size_t dion_workspace_size_capped(const dion_shape* shapes, int32_t batch, int32_t dtype, const dion_ns_params* p,
+                                  size_t cap) {
+  Params prm;
+  if (parse_params(p, dtype, false, prm)) return 0;
+  std::vector<Wave> waves;
+  size_t need = 0;
+  if (plan_waves(shapes, batch, dtype, prm, false, 2, cap, waves, need)) return 0;
+  if (dtype == DION_FP32 && p->precision != DION_PREC_FP64) {  // may also serve dion_rowsubset_step
+    Params ps;
+    size_t need2 = 0;
+    if (parse_params(p, DION_FP32, true, ps) == DION_OK &&
+        plan_waves(shapes, batch, DION_FP32, ps, true, 4, cap, waves, need2) == DION_OK)
+      need = std::max(need, need2);
+  }
+  return need;
+}
+
 int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,
                       int32_t dtype, const dion_ns_params* p, int32_t* sel_idx, void* workspace,
                       size_t workspace_bytes, void* stream) {
@@ -1787,14 +1929,19 @@ int dion_orth_batched(const void* const* M, void* const* out, const dion_shape* 
   Params prm;
   int rc = parse_params(p, dtype, false, prm);
   if (rc) return rc;
-  Plan P;
-  rc = build_plan(shapes, batch, dtype, prm, false, P);
+  std::vector<Wave> waves;
+  size_t need = 0;
+  rc = plan_waves(shapes, batch, dtype, prm, false, 2, workspace ? workspace_bytes : (size_t)-1, waves, need);
   if (rc) return rc;
   const size_t es = dtype_bytes(dtype);
   rc = check_ptrs(M, out, shapes, batch, es, es);
   if (rc) return rc;
-  return run(P, M, out, nullptr, batch, dtype, dtype, 0.f, false, sel_idx, workspace, workspace_bytes,
-             (hipStream_t)stream);
+  for (const Wave& w : waves) {
+    rc = run(w.plan, M + w.i0, out + w.i0, nullptr, w.n, dtype, dtype, 0.f, false, sel_idx ? sel_idx + w.sel0 : nullptr,
+             workspace, workspace_bytes, (hipStream_t)stream);
+    if (rc) return rc;
+  }
+  return DION_OK;
 }
 
 int dion_orth_batched_noalloc(const void* const* M, void* const* out, const dion_shape* shapes, int32_t batch,
@@ -1846,8 +1993,10 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
   Params prm;
   int rc = parse_params(p, DION_FP32, true, prm);
   if (rc) return rc;
-  Plan P;
-  rc = build_plan(shapes, batch, DION_FP32, prm, true, P, grad_dtype == DION_BF16 ? 2 : 4);
+  std::vector<Wave> waves;
+  size_t need = 0;
+  rc = plan_waves(shapes, batch, DION_FP32, prm, true, grad_dtype == DION_BF16 ? 2 : 4,
+                  workspace ? workspace_bytes : (size_t)-1, waves, need);
   if (rc) return rc;
   if (!E || !grad) return fail(DION_E_INVAL, "E or grad pointer array is NULL");
   for (int i = 0; i < batch; ++i)
@@ -1856,8 +2005,12 @@ int dion_rowsubset_step(float* const* E, const void* const* grad, void* const* o
   if (rc) return rc;
   rc = check_ptrs(grad, out, shapes, batch, grad_dtype == DION_BF16 ? 2 : 4, 2);
   if (rc) return rc;
-  return run(P, (const void* const*)E, out, grad, batch, DION_FP32, grad_dtype, beta, true, sel_idx, workspace,
-             workspace_bytes, (hipStream_t)stream);
+  for (const Wave& w : waves) {
+    rc = run(w.plan, (const void* const*)(E + w.i0), out + w.i0, grad + w.i0, w.n, DION_FP32, grad_dtype, beta, true,
+             sel_idx ? sel_idx + w.sel0 : nullptr, workspace, workspace_bytes, (hipStream_t)stream);
+    if (rc) return rc;
+  }
+  return DION_OK;
 }
 
 size_t dion_phase_workspace_size(int32_t phase, const dion_shape* shapes, int32_t batch, int32_t dtype,
@@ -1965,8 +2118,10 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
   Params prm;
   int rc = parse_params(p, DION_FP32, true, prm);
   if (rc) return rc;
-  Plan P;
-  rc = build_plan(shapes, batch, DION_FP32, prm, true, P, grad_dtype == DION_BF16 ? 2 : 4);
+  std::vector<Wave> waves;
+  size_t need = 0;
+  rc = plan_waves(shapes, batch, DION_FP32, prm, true, grad_dtype == DION_BF16 ? 2 : 4,
+                  workspace ? workspace_bytes : (size_t)-1, waves, need);
   if (rc) return rc;
   if (!E || !grad || !W) return fail(DION_E_INVAL, "E, grad or W pointer array is NULL");
   for (int i = 0; i < batch; ++i)
@@ -1978,38 +2133,14 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
   if (rc) return rc;
   // the final apply updates W in its epilogue; rows left out by the selection
   // are updated with the raw momentum by a pass of their own
-  P.update = true;
-  P.w_bf16 = w_dtype == DION_BF16;
-  P.keep = 1.0f - weight_decay;
-  // algorithmic bytes: the momentum pass writes no update rows here, and the
-  // final apply reads and writes the selected rows of W instead of writing out
-  double elems = 0.0, unsel = 0.0;
-  for (const MatPlan& mp : P.mats) {
-    elems += (double)mp.R * mp.C;
-    unsel += (double)(mp.R - mp.k) * mp.C;
+  for (Wave& w : waves) {
+    make_update(w.plan, w_dtype, weight_decay);
+    rc = run(w.plan, (const void* const*)(E + w.i0), W + w.i0, grad + w.i0, w.n, DION_FP32, grad_dtype, beta, true,
+             sel_idx ? sel_idx + w.sel0 : nullptr, workspace, workspace_bytes, (hipStream_t)stream, nullptr, nullptr,
+             alpha + w.i0);
+    if (rc) return rc;
   }
-  for (Step& st : P.steps) {
-    if (st.kind == ST_MOMENTUM) st.bytes -= 2.0 * elems;
-    if (st.kind == ST_GEMM && st.epi == EPI_OUT) {
-      st.pa.out_update = 1;
-      st.pa.upd_keep = P.keep;
-      st.pa.out_fp32 = w_dtype == DION_FP32 ? 1 : 0;
-      const Table& tb = P.tabs[st.table];
-      for (int j = 0; j < tb.nmat; ++j) {
-        const MatPlan& mp = P.mats[P.ints[tb.mats_off + j]];
-        st.bytes += (2.0 * wes - 2.0) * (double)mp.m * mp.n;
-      }
-    }
-  }
-  if (P.use_idx) {
-    Step u;
-    u.kind = ST_UPDATE;
-    u.name = "update_rows";
-    u.bytes = unsel * (4.0 + 2.0 * wes) + (double)P.total_rows;   // E read, W read and written; row flags
-    P.steps.push_back(u);
-  }
-  return run(P, (const void* const*)E, W, grad, batch, DION_FP32, grad_dtype, beta, true, sel_idx, workspace,
-             workspace_bytes, (hipStream_t)stream, nullptr, nullptr, alpha);
+  return DION_OK;
 }
 
 double dion_useful_flops(const dion_shape* shapes, int32_t batch, const dion_ns_params* p) {

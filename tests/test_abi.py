@@ -280,3 +280,58 @@ def test_mfma16_iteration_range_guard():
                                       dion._shapes([(2048, 512)]), 1, _lib.DION_BF16, 0.9, ctypes.byref(p), None, None, 0,
                                       None)
     assert rc == -2
+
+
+def test_binding_refuses_mismatched_batches():
+    """The binding checks tensor lists against the planned batch before any C
+    call: count, shapes, dtype, the entry point the batch was planned for and
+    the index buffer (the C library would otherwise read past the pointer
+    arrays or the tensors)."""
+    import torch
+    shapes = [(4, 6), (8, 3)]
+    orth = dion.Orthogonalizer(shapes, "bf16", device="cpu")
+    ok = [torch.zeros(s, dtype=torch.bfloat16) for s in shapes]
+    for Ms, outs, msg in [
+        (ok[:1], ok, "1 tensors for a batch of 2"),
+        (ok, ok + ok[:1], "3 tensors for a batch of 2"),
+        ([ok[0], torch.zeros((3, 8), dtype=torch.bfloat16)], ok, "planned (8, 3)"),
+        ([torch.zeros(s) for s in shapes], ok, "expected torch.bfloat16"),
+        (ok, ok, "on the GPU"),                    # right shapes, but host tensors
+    ]:
+        with pytest.raises(dion.DionError, match=msg.replace("(", r"\(").replace(")", r"\)")):
+            orth(Ms, outs)
+    with pytest.raises(dion.DionError, match="row-subset step"):
+        orth.step(ok, ok, ok, 0.9)
+    step = dion.Orthogonalizer(shapes, "fp32", precision="mfma16", device="cpu", step_mode=True, row_frac=0.5)
+    E = [torch.zeros(s) for s in shapes]
+    with pytest.raises(dion.DionError, match="planned for the row-subset step"):
+        step(E, E)
+    with pytest.raises(dion.DionError, match="2 tensors for a batch of 2|planned"):
+        step.step(E, [torch.zeros((4, 6), dtype=torch.bfloat16)] * 2, ok, 0.9)
+    with pytest.raises(dion.DionError, match="alphas"):
+        step.step_update(E, ok, ok, 0.9, [0.1])
+
+
+def test_workspace_cap_sizes():
+    """dion_workspace_size_capped: the full size when it fits the cap, otherwise
+    the largest wave's plan (at most the cap, at least one matrix's); 0 when one
+    matrix alone exceeds the cap (the bound counts the whole call's header, so a
+    cap of exactly one matrix's own plan is not enough)."""
+    wl = WORKLOADS["llama3_8b"]
+    full = dion.workspace_size(wl.shapes, "bf16", restart_every=2)
+    assert dion.workspace_size(wl.shapes, "bf16", restart_every=2, budget=full) == full
+    one = dion.workspace_size([wl.shapes[4]], "bf16", restart_every=2)   # a 14336 x 4096 matrix alone
+    prev = 0
+    for cap in (one + (64 << 20), 2 * one, 8 << 30, 32 << 30, full - 1):
+        need = dion.workspace_size(wl.shapes, "bf16", restart_every=2, budget=cap)
+        assert one <= need <= cap and need >= prev
+        prev = need
+    with pytest.raises(dion.DionError):
+        dion.workspace_size(wl.shapes, "bf16", restart_every=2, budget=one - 1)
+    # a workspace below one matrix's need is still refused by the call itself
+    p, keep = dion._params(dion.QUINTIC, 5, 2, 0, 1.0, 1.0, "auto")
+    fake = (ctypes.c_void_p * 1)(0x10000)
+    out = (ctypes.c_void_p * 1)(0x90000000)
+    rc = _lib.lib.dion_orth_batched(fake, out, dion._shapes([(4096, 4096)]), 1, _lib.DION_BF16, ctypes.byref(p), None,
+                                    ctypes.c_void_p(1 << 20), 1 << 20, None)
+    assert rc == -3 and b"alone needs" in _lib.lib.dion_last_error()

@@ -635,3 +635,75 @@ def test_rowsubset_step_update_small_blocks(dion, wbf16, ef):
                 assert O.rel_frobenius(got[ix] - base, d_ref) <= TOL_MFMA16, (s, t)
         E_host = newE
         W_host = [to_np(w).astype(np.float32) for w in W_dev]
+
+
+def test_calls_never_block_the_host(dion):
+    """Eight calls enqueued back to back return while the device is still on
+    the first ones: the plan upload never waits on the host (a ring of pinned
+    buffers, then kernel-argument uploads once the host is eight calls ahead)."""
+    import time
+    shapes = [(4096, 4096)] * 4
+    Ms = [torch.from_numpy(round_bf16(lowrank_np((41, j), r, c, 64, 0.05))).cuda().to(torch.bfloat16)
+          for j, (r, c) in enumerate(shapes)]
+    outs = [torch.empty_like(M) for M in Ms]
+    orth = dion.Orthogonalizer(shapes, "bf16", restart_every=2)
+    for _ in range(10):            # warm up, and let the ring grow
+        orth(Ms, outs)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    for n_calls in (8, 12):        # 12: beyond the ring, kernel-argument uploads
+        t0 = time.perf_counter()
+        for _ in range(n_calls):
+            orth(Ms, outs)
+        t_host = time.perf_counter() - t0
+        pending = not torch.cuda.current_stream().query()
+        torch.cuda.synchronize()
+        t_all = time.perf_counter() - t0
+        print(f"{n_calls} calls: enqueued in {1e3 * t_host:.1f} ms, done after {1e3 * t_all:.1f} ms", flush=True)
+        assert pending and t_host < 0.25 * t_all
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r)
+
+
+# ------------------------------------------------------ workspace in waves
+def test_waves_bit_identical(dion):
+    """A workspace smaller than the whole plan runs the batch in waves of
+    consecutive matrices: outputs, indices, buffers and weights are bit-identical
+    to one wave, for the batched call and both row-subset entry points."""
+    from workloads import LLAMA3_8B_LAYER
+    shapes = [(r // 4, c // 4) for _ in range(2) for _, r, c in LLAMA3_8B_LAYER] + [(5, 700), (3000, 40)]
+    Ms = [torch.from_numpy(round_bf16(lowrank_np((42, j), r, c, 16, 0.05, log_scale=(-3.0, 0.0)))).cuda()
+          .to(torch.bfloat16) for j, (r, c) in enumerate(shapes)]
+    full = dion.workspace_size(shapes, "bf16", restart_every=2, row_frac=0.5)
+    for budget in (full // 3, full // 6):
+        need = dion.workspace_size(shapes, "bf16", restart_every=2, row_frac=0.5, budget=budget)
+        assert need <= budget < full
+        a, ia = dion.orth_batched(Ms, restart_every=2, row_frac=0.5, return_indices=True)
+        b, ib = dion.orth_batched(Ms, restart_every=2, row_frac=0.5, return_indices=True, workspace_budget=budget)
+        for x, y, u, v in zip(a, b, ia, ib):
+            assert torch.equal(u, v) and torch.equal(x.view(torch.int16), y.view(torch.int16))
+        print(f"orth waves at {budget / full:.2f} of the full workspace: bit-identical", flush=True)
+    # the row-subset step and its fused update, two steps each
+    Es = [[torch.zeros(s, dtype=torch.float32, device="cuda") for s in shapes] for _ in range(2)]
+    Ws = [[torch.full(s, 0.01, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(2)]
+    alphas = [0.02] * len(shapes)
+    full_s = dion.workspace_size(shapes, "fp32", restart_every=2, row_frac=0.125, precision="mfma16")
+    orths = [dion.Orthogonalizer(shapes, "fp32", restart_every=2, row_frac=0.125, precision="mfma16",
+                                 step_mode=True, workspace_budget=b) for b in (None, full_s // 4)]
+    assert orths[1].ws_bytes < full_s
+    for t in range(2):
+        G = [torch.from_numpy(round_bf16(lowrank_np((43, t, j), r, c, 8, 0.05))).cuda().to(torch.bfloat16)
+             for j, (r, c) in enumerate(shapes)]
+        outs = [[torch.empty(s, dtype=torch.bfloat16, device="cuda") for s in shapes] for _ in range(2)]
+        sels = [torch.empty(orths[0].total_selected, dtype=torch.int32, device="cuda") for _ in range(2)]
+        for k in range(2):
+            orths[k].step(Es[k], G, outs[k], 0.95, sels[k])
+        assert torch.equal(sels[0], sels[1])
+        for x, y, e, f in zip(outs[0], outs[1], Es[0], Es[1]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)) and torch.equal(e, f)
+        for k in range(2):
+            orths[k].step_update(Es[k], G, Ws[k], 0.95, alphas, 0.01, sels[k])
+        assert torch.equal(sels[0], sels[1])
+        for x, y in zip(Ws[0], Ws[1]):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    print("row-subset waves: bit-identical", flush=True)
