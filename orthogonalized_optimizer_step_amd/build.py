@@ -23,6 +23,7 @@ SOURCES = [
     ("gemm_kernels.hip", []),
     ("stream_kernels.hip", ["-ffp-contract=off"]),
     ("lowrank_kernels.hip", ["-ffp-contract=off"]),
+    ("lowrank_gemm.hip", []),
     ("tiny_kernels.hip", []),
     ("dion_api.cpp", []),
 ]
@@ -62,7 +63,7 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lrocblas"]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -7,7 +7,6 @@
 // then per iteration P = aI + bG + cG^2, Q <- P Q, and either G <- P G P or,
 // at a restart, X <- Q X, G <- X X^T, Q <- I; finally out = Q X.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <cmath>
@@ -50,6 +49,8 @@ void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int 
                    const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
 void launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
+void launch_lr_gemm(bool ta, bool tb, int m, int n, int k, float alpha, const float* const* A, const float* const* B,
+                    float beta, float* const* C, int count, hipStream_t s);
 void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
                      const double* coef, int K, unsigned long long restarts, int in_fmt, int out_fmt, int update,
                      float keep, hipStream_t s);
@@ -1600,10 +1601,9 @@ void make_update(Plan& P, int w_dtype, float weight_decay) {
 // orth is CholeskyQR run three times, the first on a shifted Gram matrix:
 // S = F^T F (GEMM), L = chol(S (+ shift)) and L^-1 in fp64 (k_lr_cholinv),
 // F <- F L^-T (GEMM); the triangular factor has a positive diagonal, the QR
-// convention of the oracle.  The rank-r products are plain GEMMs and run in
-// rocBLAS, batched over the matrices of one shape.
+// convention of the oracle.  The rank-r products run in k_lr_gemm
+// (lowrank_gemm.hip), batched over the matrices of one shape.
 constexpr int kMaxRank = 512;
-constexpr size_t kBlasWorkspace = (size_t)32 << 20;
 enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_N };
 
 struct LrGroup {
@@ -1618,7 +1618,7 @@ struct LrPlan {
   std::vector<int64_t> blk0;
   int64_t blocks = 0;
   bool out_fp32 = false;
-  size_t off_descs = 0, off_ptrs = 0, off_blas = 0, upload_bytes = 0, total = 0;
+  size_t off_descs = 0, off_ptrs = 0, upload_bytes = 0, total = 0;
   std::vector<size_t> off[LP_N];   // per matrix: X, Y, W, W2, S, L, A64 (in LP_D's place: D)
   std::vector<size_t> off_a64;
 };
@@ -1653,7 +1653,6 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
   for (LrGroup& g : P.groups) { g.ptr_off = off; off += sizeof(float*) * LP_N * g.mats.size(); }
   off = align256(off);
   P.upload_bytes = off;
-  P.off_blas = off; off = align256(off + kBlasWorkspace);
   for (int k = 0; k < LP_N; ++k) P.off[k].assign(batch, 0);
   P.off_a64.assign(batch, 0);
   for (int i = 0; i < batch; ++i) {
@@ -1668,40 +1667,6 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
     if (!P.out_fp32) { P.off[LP_D][i] = off; off = align256(off + 4 * R * C); }
   }
   P.total = off;
-  return DION_OK;
-}
-
-// one rocBLAS handle per thread and device, created on first use
-int blas_handle(hipStream_t stream, void* wsp, rocblas_handle& h) {
-  thread_local std::vector<std::pair<int, rocblas_handle>> handles;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
-  h = nullptr;
-  for (auto& p : handles)
-    if (p.first == dev) h = p.second;
-  if (!h) {
-    if (rocblas_create_handle(&h) != rocblas_status_success) return fail(DION_E_HIP, "rocblas_create_handle failed");
-    handles.emplace_back(dev, h);
-  }
-  if (rocblas_set_stream(h, stream) != rocblas_status_success) return fail(DION_E_HIP, "rocblas_set_stream failed");
-  if (rocblas_set_workspace(h, wsp, kBlasWorkspace) != rocblas_status_success)
-    return fail(DION_E_HIP, "rocblas_set_workspace failed");
-  return DION_OK;
-}
-
-// Row-major C (m x n) = alpha op(A) op(B) + beta C over a batch of pointer
-// triples (device arrays), as the column-major product C^T = op(B)^T op(A)^T.
-// A is m x k (k x m when ta); B is k x n (n x k when tb).
-int gemm_rm(rocblas_handle h, bool ta, bool tb, int m, int n, int k, float alpha, float* const* A,
-            float* const* B, float beta, float* const* Cm, int count) {
-  const int lda = ta ? m : k, ldb = tb ? k : n;
-  const rocblas_status st = rocblas_sgemm_batched(
-      h, tb ? rocblas_operation_transpose : rocblas_operation_none,
-      ta ? rocblas_operation_transpose : rocblas_operation_none, n, m, k, &alpha, (const float* const*)B, ldb,
-      (const float* const*)A, lda, &beta, Cm, n, count);
-  if (st != rocblas_status_success)
-    return fail(DION_E_HIP, "rocblas_sgemm_batched failed: " + std::string(rocblas_status_to_string(st)));
   return DION_OK;
 }
 
@@ -1745,8 +1710,6 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   }
   int rc = upload(blob.data(), P.upload_bytes, ws, stream);
   if (rc != DION_OK) return rc;
-  rocblas_handle h;
-  if ((rc = blas_handle(stream, ws + P.off_blas, h)) != DION_OK) return rc;
   const LrDesc* d_descs = (const LrDesc*)(ws + P.off_descs);
   auto arrays = [&](const LrGroup& g, int k) { return (float* const*)(ws + g.ptr_off) + k * g.mats.size(); };
   const int nmat = batch;
@@ -1770,7 +1733,11 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     }
     return DION_OK;
   };
-  const char* kSgemm = "rocblas_sgemm_batched";
+  // kernel instance names as profilers print them
+  auto gemm_name = [](bool ta, bool tb) {
+    return !ta ? (tb ? "dion::k_lr_gemm<true, true>" : "dion::k_lr_gemm<true, false>")
+               : (tb ? "dion::k_lr_gemm<false, true>" : "dion::k_lr_gemm<false, false>");
+  };
   bool any_small = false, any_large = false;
   for (int i = 0; i < batch; ++i) (P.r[i] <= LR_REG_RMAX ? any_small : any_large) = true;
   double elems = 0.0;
@@ -1779,8 +1746,10 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   auto gprod = [&](const char* name, const LrGroup& g, bool ta, bool tb, int m, int n, int k, float alpha,
                    int A, int B, float beta_, int Cm, double bytes_each) -> int {
     const double cnt = (double)g.mats.size();
-    return phase(name, kSgemm, 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
-      return gemm_rm(h, ta, tb, m, n, k, alpha, arrays(g, A), arrays(g, B), beta_, arrays(g, Cm), (int)g.mats.size());
+    return phase(name, gemm_name(ta, tb), 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
+      launch_lr_gemm(ta, tb, m, n, k, alpha, (const float* const*)arrays(g, A), (const float* const*)arrays(g, B), beta_,
+                     arrays(g, Cm), (int)g.mats.size(), stream);
+      return DION_OK;
     });
   };
 

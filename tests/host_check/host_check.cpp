@@ -46,6 +46,10 @@ void launch_lr_accumulate(const LrDesc*, int, int64_t, int, hipStream_t) { std::
 void launch_lr_cast(const LrDesc*, int, int64_t, int, hipStream_t) { std::abort(); }
 void launch_lr_cholinv(const LrDesc*, int, bool, bool, float, hipStream_t) { std::abort(); }
 void launch_lr_colnorm(const LrDesc*, int, hipStream_t) { std::abort(); }
+void launch_lr_gemm(bool, bool, int, int, int, float, const float* const*, const float* const*, float, float* const*, int,
+                    hipStream_t) {
+  std::abort();
+}
 }  // namespace dion
 
 static unsigned long long rng_state = 88172645463325252ull;

@@ -22,7 +22,7 @@ def test_host_code_under_asan_ubsan(tmp_path):
            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
            os.path.join(CSRC, "dion_api.cpp"), os.path.join(ROOT, "tests", "host_check", "host_check.cpp"),
-           "-lrocblas", "-o", exe]
+           "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-3000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
