@@ -703,6 +703,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   bool x_is_x0 = true;
   int ct = 2;         // operand terms of the m x m chain products in this segment
   bool short_seg = false;  // one-term chain: Q <- P Q as a full (unmirrored) product
+  // ... or mirrored, when the schedule's slopes multiply to at most six
+  // iterations of the fixed quintic's (every configured workload): the
+  // mirrored triangle's rounding is amplified by fewer iterations afterwards
+  double gain_all = 1.0;
+  for (int k = 0; k < K; ++k) gain_all *= std::max(1.0, std::fabs(prm.a[k]));
+  const bool mirror_q = !P.fp64 && gain_all <= std::pow(3.4445, 6) * (1.0 + 1e-9);
   for (int k = 1; k <= K; ++k) {
     const double a = prm.a[k - 1], b = prm.b[k - 1], c = prm.c[k - 1];
     if (q_slot < 0) {
@@ -714,19 +720,24 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       // one-term chain products, longer segments two terms.  The restart
       // apply keeps X in two terms in every case.
       //
-      // With one-term operands the product Q <- P Q is run in full rather
-      // than as an upper triangle plus its mirror.  In exact arithmetic it is
-      // symmetric (P and Q are polynomials in the same Gram matrix), but its
+      // With one-term operands the product Q <- P Q is symmetric in exact
+      // arithmetic (P and Q are polynomials in the same Gram matrix), but its
       // rounding error is not: in the eigenbasis the error of entry (i, j)
-      // carries the weights of row i, and the mirror copies the entries whose
+      // carries the weights of row i, and a mirror copies the entries whose
       // row is a small singular direction (where P is near its slope
       // a = 3.4445) into the transposed position, which the apply Q X then
-      // multiplies by the large singular values.  T = P G is mirrored: its
+      // multiplies by the large singular values, and every later iteration
+      // by its slope.  So it is mirrored (half the work) only when the slopes
+      // of the whole schedule multiply to at most six iterations of the fixed
+      // quintic's, and run in full otherwise.  T = P G is always mirrored: its
       // error is only half as harmful, since the next product P T^T is
       // Gram-shaped.  Emulation against the oracle (Llama-shaped 1024 x 4096,
       // restarts every 2): relative error 5.6e-3 with both products full,
       // 6.3e-3 with T mirrored, 9.1e-3 with both mirrored; on the row-subset
-      // blocks 3.7e-3, 5.9e-3 and 1.2e-2.
+      // blocks 3.7e-3, 5.9e-3 and 1.2e-2.  Measured on the GPU with both
+      // mirrored: 7.1-7.2e-3 on the Llama-3-8B samples (5.5-5.9e-3 with Q
+      // full), 5.2-6.2e-3 on the row-subset blocks (gate 2e-2), for 4.5% less
+      // time on that batch.
       int e = k;
       while (e < K && !xr[e - 1]) ++e;
       ct = e - k + 1 <= 2 ? 1 : 2;
@@ -771,7 +782,9 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       pa.b_slot = q_slot;
       pa.c_slot = qn;
       pa.alpha = sQn / (sP * sQ);
-      if (short_seg && any_acc && k < K && xr[k - 1] && n_rest == 0) {
+      if (short_seg && mirror_q) {   // symmetric in exact arithmetic: the upper triangle and its mirror
+        gemm(t_sym, bm_sym, true, 1, 1, EPI_SYM, pa, "sym_product", false);
+      } else if (short_seg && any_acc && k < K && xr[k - 1] && n_rest == 0) {
         // this Q starts the accumulated factor of the matrices restarting
         // from X0; the accumulation at the second restart multiplies by it
         // from the right, which reads its rows as columns: keep Q^T (hi) as well
