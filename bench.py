@@ -197,6 +197,46 @@ def summarize(d):
         if calib:
             print("\ncalibration (true / counted, from the 1 GiB copy): " +
                   ", ".join(f"{c} x{v:.3f}" for c, v in calib.items()))
+        clock_table(rows, traces)
+
+
+def clock_table(rows, traces):
+    """Per-kernel range of the GPU clock and MFMA busy fraction over the
+    dispatches of a counter run that holds GRBM_GUI_ACTIVE (summed over the 8
+    XCDs) and SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs).  The
+    dispatch duration comes from the counter rows' own timestamps, else from
+    a kernel trace of the same run, joined by dispatch id."""
+    import collections
+    import csv
+    if not any(r["Counter_Name"] == "GRBM_GUI_ACTIVE" for r in rows):
+        return
+    disp = collections.defaultdict(dict)
+    for r in rows:
+        e = disp[(r["Kernel_Name"], r["Dispatch_Id"])]
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            e["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    ns = {}
+    for f in traces:
+        for r in csv.DictReader(open(f)):
+            ns[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    per = collections.defaultdict(list)
+    for (name, did), e in disp.items():
+        dur = e.get("ns") or ns.get(did)
+        if not dur or "GRBM_GUI_ACTIVE" not in e:
+            continue
+        cyc = e["GRBM_GUI_ACTIVE"] / 8.0
+        busy = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / cyc / 1024.0 if cyc else 0.0
+        per[short_kernel(name)].append((cyc / dur, busy))
+    if not per:
+        print("\n(no dispatch durations: run the counters with --kernel-trace for the clock table)")
+        return
+    print(f"\n{'kernel':42s} {'disp':>5s} {'clock GHz':>12s} {'MFMA busy':>11s} {'clock x busy':>12s}")
+    for k, v in sorted(per.items(), key=lambda kv: sum(b for _, b in kv[1]) / len(kv[1])):
+        ghz = [g for g, _ in v]
+        busy = [b for _, b in v]
+        prod = sum(g * b for g, b in v) / len(v)
+        print(f"{k[:42]:42s} {len(v):5d} {min(ghz):5.2f}-{max(ghz):5.2f}  {min(busy):4.2f}-{max(busy):5.2f} {prod:12.2f}")
 
 
 def traffic_for(kernel, workload):

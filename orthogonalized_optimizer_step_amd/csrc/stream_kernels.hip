@@ -10,6 +10,7 @@
 // Momentum: the summary's flow (输入输出流程) updates the momentum first; the
 // fp32 buffer is updated by two separately rounded fp32 operations.
 #include <cstring>
+#include <type_traits>
 
 #include "dion_internal.h"
 
@@ -63,6 +64,23 @@ __device__ __forceinline__ int mat_of_row(const MatDesc* descs, int nmat, int64_
 // weight of the smallest square; the lanes' integers are summed and the total
 // is rounded once.  Rows with an Inf or NaN get a NaN key.
 //
+// 16-bit inputs take a cheaper fast path.  The square of a value with p
+// significant bits (8 for bf16, 11 for fp16) is an integer multiple of
+// 2^(2 E - 254 - 2 (p - 1)), E its exponent in fp32 (at least 1), so every
+// square in a group of a lane's values, and every partial sum of them, is a
+// multiple of 2^L with L taken at the group's smallest nonzero exponent.  A
+// multiple of 2^L below 2^(L + 53) is a double, so the group's plain fp64 sum
+// is exact as long as its partial sums stay below that bound; they only
+// grow, and rounding is monotone, so the final sum is below the bound exactly
+// when none of them crossed it.  A group is the eight values of one 16-byte
+// load: it costs one fused multiply-add and one integer minimum per value,
+// and its exact sum enters the TwoSum pair as one term.  A group whose sum
+// reaches the bound (its squares spread over more than about 2^34 for bf16,
+// 2^28 for fp16: one value in some 10^5 of a Gaussian row) or is Inf or NaN
+// adds its values to the pair one at a time instead.  (Groups of 64 values
+// send too many rows to the integer fallback: a bf16 value 10^-5 times the
+// scale of its group is enough.)
+//
 // At row_frac = 1 no row is chosen by its key: the keys only give ||M||_F^2,
 // and the plain fp64 sum (EXACT = false) serves.
 
@@ -76,7 +94,9 @@ struct SqAcc {
   double hi = 0.0, lo = 0.0;
   unsigned bad = 0u;
   __device__ __forceinline__ void add(float x) {
-    const double q = __dmul_rn((double)x, (double)x);   // exact: 48 significant bits at most
+    add_exact(__dmul_rn((double)x, (double)x));         // exact: 48 significant bits at most
+  }
+  __device__ __forceinline__ void add_exact(double q) {
     double s, e, t, f;
     two_sum(hi, q, s, e);
     two_sum(lo, e, t, f);
@@ -251,7 +271,37 @@ __global__ __launch_bounds__(256) void k_rowkeys(const MatDesc* __restrict__ des
     key = wave_sum(s);
   } else {
     SqAcc A;
-    row_elems<InT>(d, r, lane, [&](float x) { A.add(x); });
+    const bool vec16 = sizeof(InT) == 2 && (d.C & 7) == 0 && ((uintptr_t)d.M & 15) == 0;
+    if (vec16) {
+      constexpr int p = std::is_same<InT, _Float16>::value ? 11 : 8;   // significant bits
+      const uint16_t* row = (const uint16_t*)d.M + r * d.C;
+      for (int c = lane * 8; c < d.C; c += 512) {
+        const uint4 v = *(const uint4*)(row + c);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float xs[8];
+        double s = 0.0;
+        uint32_t amin = 0xFFFFFFFFu;     // of (fp32 bits << 1) - 1: sign dropped, zeros wrap to the top
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          xs[q] = in16_to_f32<InT>(q & 1 ? w[q >> 1] >> 16 : w[q >> 1] & 0xFFFFu);
+          s = __fma_rn((double)xs[q], (double)xs[q], s);
+          amin = min(amin, (__float_as_uint(xs[q]) << 1) - 1u);
+        }
+        if (amin != 0xFFFFFFFFu) {
+          const int E = max((int)((amin + 1u) >> 24), 1);
+          const int L = 2 * E - 254 - 2 * (p - 1);
+          const double bound = __longlong_as_double((long long)(L + 53 + 1023) << 52);   // 2^(L + 53)
+          if (s < bound) {               // false for Inf and NaN too
+            A.add_exact(s);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) A.add(xs[q]);
+          }
+        }
+      }
+    } else {
+      row_elems<InT>(d, r, lane, [&](float x) { A.add(x); });
+    }
     A.wave();
     if (!A.bad) {
       key = __dadd_rn(A.hi, A.lo);

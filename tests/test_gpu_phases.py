@@ -146,6 +146,21 @@ def adversarial_matrix(dtype, cols, seed):
         else:                                    # equal to a tie row's key: ties to the lower row
             r[c[0]] = big
         rows.append(r)
+    # random rows with one value far below the others: for 16-bit inputs the
+    # eight values of its 16-byte load no longer sum exactly in one double, and
+    # are added one at a time
+    for e in ((16, 20) if dtype == "fp16" else (20, 40)):
+        r = rng.standard_normal(cols).astype(np.float32)
+        r[rng.integers(cols)] = np.float32(2.0 ** -e)
+        rows.append(r)
+    if cols > 4096:
+        # random rows whose columns from 4096 on are scaled by a power of two:
+        # each load holds values of one scale and sums exactly on its own, and
+        # the loads' sums, up to 2^52 apart, meet only in the exact pair
+        for e in ((6, 12) if dtype == "fp16" else (8, 14, 20, 26)):
+            r = rng.standard_normal(cols).astype(np.float32)
+            r[4096:] *= np.float32(2.0 ** -e)
+            rows.append(r)
     A = np.stack(rows)
     if dtype == "bf16":
         A = round_bf16(A)
@@ -155,12 +170,13 @@ def adversarial_matrix(dtype, cols, seed):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-@pytest.mark.parametrize("cols", [640, 333, 64, 5])
+@pytest.mark.parametrize("cols", [9216, 640, 333, 64, 5])
 def test_rowkeys_exact_rounding(dion, dtype, cols):
     """Keys bit-equal to the exact sum of squares rounded once, on rows built to
     defeat any fixed summation order (ties, a hair above a tie, squares hundreds
-    of bits apart): the first exercise the exact-pair fast path, the others the
-    exact integer fallback; 640 and 64 columns take 16-byte loads, 333 and 5 do not."""
+    of bits apart): the first exercise the exact fast paths, the others the
+    exact integer fallback; 9216, 640 and 64 columns take 16-byte loads (at 9216
+    eighteen per lane), 333 and 5 do not."""
     A = adversarial_matrix(dtype, cols, seed=cols)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
     for frac in (1.0 / 8, 0.5):
