@@ -43,8 +43,7 @@
  *     the caller's `workspace` (device memory, at least
  *     dion_workspace_size() bytes, 256-byte aligned).  The one exception is
  *     dion_orth_batched_noalloc, whose scratch is a fixed array that each
- *     device holds for the life of the process (and dion_lowrank_step's
- *     rocBLAS handle, see there).
+ *     device holds for the life of the process.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work on it and return without waiting for the device: the plan header
  *     goes up through a ring of pinned host buffers, each refilled only once
@@ -278,11 +277,12 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
  *             overwritten with the new one; must not overlap M[i]
  *   out[i]    device R x C of out_dtype; must not overlap M[i]
  *   rank      1 .. 512 (DION_E_UNSUPPORTED above)
- * The rank-r products run as batched rocBLAS GEMMs (one group per distinct
- * (R, C, r)), on the caller's stream with a 32 MiB slice of the workspace as
- * rocBLAS's workspace; the rocBLAS handle (one per thread and device, made at
- * the first call) holds rocBLAS's own state.  All other memory is the
- * caller's workspace.  Asynchronous on `stream`. */
+ * The rank-r products run in this library's GEMM kernel (one launch per
+ * distinct (R, C, r) and product, with device pointer arrays from the
+ * uploaded header): fp32 operands split exactly into three bf16 terms, six
+ * bf16 MFMA products of relative weight down to 2^-16 summed in fp32.  All
+ * memory is the caller's workspace; no handle or other state is kept.
+ * Asynchronous on `stream`. */
 typedef enum { DION_LOWRANK_QR = 0, DION_LOWRANK_COLNORM = 1 } dion_lowrank_mode;
 
 /* Bytes of workspace for dion_lowrank_step (0 on invalid arguments). */

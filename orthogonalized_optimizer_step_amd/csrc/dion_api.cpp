@@ -49,8 +49,6 @@ void launch_unpack(bool fp64_path, const MatDesc* descs, const int* prefix, int 
                    const MatScalars* scalars, float scale, bool use_nu2, hipStream_t s);
 void launch_scale_combine(MatScalars* scalars, int nmat, hipStream_t s);
 void launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
-void launch_lr_gemm(bool ta, bool tb, int m, int n, int k, float alpha, const float* const* A, const float* const* B,
-                    float beta, float* const* C, int count, hipStream_t s);
 void launch_tiny_gns(const MatDesc* descs, const int* ids, int ntiny, const MatScalars* scalars, const int* idx,
                      const double* coef, int K, unsigned long long restarts, int in_fmt, int out_fmt, int update,
                      float keep, hipStream_t s);
@@ -1610,14 +1608,17 @@ void make_update(Plan& P, int w_dtype, float weight_decay) {
 //   W = B^T P                              GEMM
 //   M = B - beta P W^T                     GEMM (beta = -beta, accumulate)
 //   Q = orth(W) or colnorm(W)              shifted CholeskyQR3, or k_lr_colnorm
-//   out = P Q^T                            GEMM (fp32, cast to bf16/fp16)
+//   out = P Q^T                            GEMM, written in the output dtype
 // orth is CholeskyQR run three times, the first on a shifted Gram matrix:
 // S = F^T F (GEMM), L = chol(S (+ shift)) and L^-1 in fp64 (k_lr_cholinv),
 // F <- F L^-T (GEMM); the triangular factor has a positive diagonal, the QR
 // convention of the oracle.  The rank-r products run in k_lr_gemm
-// (lowrank_gemm.hip), batched over the matrices of one shape.
+// (lowrank_gemm.hip), batched over the matrices of one shape, on two-term
+// fp16 operands whose scales come from the max slots (LrSlot) that each
+// operand's producer raises; the slots live in the uploaded header, so every
+// call starts them at zero (and Dion's normalized Q at one).
 constexpr int kMaxRank = 512;
-enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_N };
+enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_AM, LP_N };
 
 struct LrGroup {
   int R, C, r;
@@ -1631,8 +1632,8 @@ struct LrPlan {
   std::vector<int64_t> blk0;
   int64_t blocks = 0;
   bool out_fp32 = false;
-  size_t off_descs = 0, off_ptrs = 0, upload_bytes = 0, total = 0;
-  std::vector<size_t> off[LP_N];   // per matrix: X, Y, W, W2, S, L, A64 (in LP_D's place: D)
+  size_t off_descs = 0, off_ptrs = 0, off_amax = 0, off_blockmax = 0, upload_bytes = 0, total = 0;
+  std::vector<size_t> off[LP_N];   // per matrix: X, Y, W, W2, S, L
   std::vector<size_t> off_a64;
 };
 
@@ -1665,7 +1666,9 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
   P.off_ptrs = off;
   for (LrGroup& g : P.groups) { g.ptr_off = off; off += sizeof(float*) * LP_N * g.mats.size(); }
   off = align256(off);
+  P.off_amax = off; off = align256(off + sizeof(unsigned) * LS_N * batch);
   P.upload_bytes = off;
+  P.off_blockmax = off; off = align256(off + sizeof(float) * P.blocks);
   for (int k = 0; k < LP_N; ++k) P.off[k].assign(batch, 0);
   P.off_a64.assign(batch, 0);
   for (int i = 0; i < batch; ++i) {
@@ -1677,7 +1680,6 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
     P.off[LP_S][i] = off;  off = align256(off + 4 * r * r);
     P.off[LP_L][i] = off;  off = align256(off + 4 * r * r);
     P.off_a64[i] = off;    off = align256(off + 8 * r * r);
-    if (!P.out_fp32) { P.off[LP_D][i] = off; off = align256(off + 4 * R * C); }
   }
   P.total = off;
   return DION_OK;
@@ -1705,7 +1707,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     d.S = (float*)(ws + P.off[LP_S][i]);
     d.Linv = (float*)(ws + P.off[LP_L][i]);
     d.A64 = (double*)(ws + P.off_a64[i]);
-    d.D = P.out_fp32 ? (float*)out[i] : (float*)(ws + P.off[LP_D][i]);
+    d.amax = (unsigned*)(ws + P.off_amax) + (size_t)LS_N * i;
     d.elems = (int64_t)P.R[i] * P.C[i];
     d.blk0 = P.blk0[i];
     d.R = P.R[i];
@@ -1717,9 +1719,13 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     const size_t n = g.mats.size();
     for (size_t t = 0; t < n; ++t) {
       const LrDesc& d = descs[g.mats[t]];
-      float* const v[LP_N] = {d.M, d.Q, d.X, d.Y, d.W, d.W2, d.S, d.Linv, d.D};
+      float* const v[LP_N] = {d.M, d.Q, d.X, d.Y, d.W, d.W2, d.S, d.Linv, (float*)d.out, (float*)d.amax};
       for (int k = 0; k < LP_N; ++k) arr[k * n + t] = v[k];
     }
+  }
+  if (mode == DION_LOWRANK_COLNORM) {   // Dion's normalized columns: every |entry| at most one
+    unsigned* am = (unsigned*)(blob.data() + P.off_amax);
+    for (int i = 0; i < batch; ++i) am[(size_t)LS_N * i + LS_G2] = 0x3F800000u;
   }
   int rc = upload(blob.data(), P.upload_bytes, ws, stream);
   if (rc != DION_OK) return rc;
@@ -1747,32 +1753,49 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     return DION_OK;
   };
   // kernel instance names as profilers print them
-  auto gemm_name = [](bool ta, bool tb) {
-    return !ta ? (tb ? "dion::k_lr_gemm<true, true>" : "dion::k_lr_gemm<true, false>")
-               : (tb ? "dion::k_lr_gemm<false, true>" : "dion::k_lr_gemm<false, false>");
+  auto gemm_name = [](bool ta, bool tb, bool f16) {
+    static const char* names[8] = {
+        "dion::k_lr_gemm<true, false, false>", "dion::k_lr_gemm<true, true, false>",
+        "dion::k_lr_gemm<false, false, false>", "dion::k_lr_gemm<false, true, false>",
+        "dion::k_lr_gemm<true, false, true>",  "dion::k_lr_gemm<true, true, true>",
+        "dion::k_lr_gemm<false, false, true>",  "dion::k_lr_gemm<false, true, true>"};
+    return names[(f16 ? 4 : 0) + (ta ? 2 : 0) + (tb ? 1 : 0)];
   };
   bool any_small = false, any_large = false;
   for (int i = 0; i < batch; ++i) (P.r[i] <= LR_REG_RMAX ? any_small : any_large) = true;
   double elems = 0.0;
   for (int i = 0; i < batch; ++i) elems += (double)P.R[i] * P.C[i];
-  // product of one group: row-major C (m x n) = op(A) op(B) with inner dimension k
+  // product of one group: row-major C (m x n) = op(A) op(B) with inner dimension k;
+  // sa, sb: the operands' max slots, sc: the result's (-1: none).  Two-term
+  // fp16 operands, except for the power product B Q (three-term bf16), whose
+  // error the orthogonalization after it amplifies by the condition number
+  // of B Q
   auto gprod = [&](const char* name, const LrGroup& g, bool ta, bool tb, int m, int n, int k, float alpha,
-                   int A, int B, float beta_, int Cm, double bytes_each) -> int {
+                   int A, int B, float beta_, int Cm, int sa, int sb, int sc, int out_fmt,
+                   double bytes_each) -> int {
     const double cnt = (double)g.mats.size();
-    return phase(name, gemm_name(ta, tb), 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
-      launch_lr_gemm(ta, tb, m, n, k, alpha, (const float* const*)arrays(g, A), (const float* const*)arrays(g, B), beta_,
-                     arrays(g, Cm), (int)g.mats.size(), stream);
+    const bool f16 = sa != LS_B || sb != LS_QIN;
+    return phase(name, gemm_name(ta, tb, f16), 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
+      launch_lr_gemm(ta, tb, f16, m, n, k, alpha, (const float* const*)arrays(g, A), (const float* const*)arrays(g, B),
+                     beta_, (void* const*)arrays(g, Cm), (unsigned* const*)arrays(g, LP_AM), sa, sb, sc, out_fmt,
+                     (int)g.mats.size(), stream);
       return DION_OK;
     });
   };
 
   const double gsz = (double)dtype_bytes(grad_dtype);
   if ((rc = phase("lr_accumulate", "dion::k_lr_accumulate", 0.0, elems * (8.0 + gsz), [&]() {
-         launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, stream);
+         launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, (float*)(ws + P.off_blockmax), stream);
+         return DION_OK;
+       })) != DION_OK) return rc;
+  double cr_all = 0.0;
+  for (int i = 0; i < batch; ++i) cr_all += (double)P.C[i] * P.r[i];
+  if ((rc = phase("lr_absmax", "dion::k_lr_absmax", 0.0, cr_all * 4.0 + 4.0 * P.blocks, [&]() {
+         launch_lr_absmax(d_descs, nmat, (const float*)(ws + P.off_blockmax), stream);
          return DION_OK;
        })) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // Y = B Q
-    if ((rc = gprod("lr_power", g, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, 0.f, LP_Y,
+    if ((rc = gprod("lr_power", g, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, 0.f, LP_Y, LS_B, LS_QIN, LS_Y, 1,
                     4.0 * ((double)g.R * g.C + (double)g.C * g.r + (double)g.R * g.r))) != DION_OK) return rc;
   // shifted CholeskyQR3 of F (rows x r): F -> dst -> tmp -> dst (tmp may be F).
   // The first pass factors S + 1e-3 max_i S_ii I: an ill-conditioned F (its
@@ -1783,56 +1806,53 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   // and Yanagisawa, SIAM J. Sci. Comput. 2020, with a practical shift in
   // place of their worst-case one)
   constexpr float kShift = 1e-3f;
-  auto cholqr3 = [&](int F, int tmp, int dst, bool rows_are_R) -> int {
+  // F's max slot is s_in; pass p writes its factor L_p^-1 into slot s_l + p
+  // and its result into slot s_out + p
+  auto cholqr3 = [&](int F, int tmp, int dst, bool rows_are_R, int s_in, int s_l, int s_out) -> int {
     const int from[3] = {F, dst, tmp}, to[3] = {dst, tmp, dst};
     for (int pass = 0; pass < 3; ++pass) {
+      const int s_from = pass == 0 ? s_in : s_out + pass - 1;
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
         const int e = gprod("lr_orth", g, true, false, g.r, g.r, rows, 1.f, from[pass], from[pass], 0.f, LP_S,
-                            4.0 * ((double)rows * g.r + (double)g.r * g.r));
+                            s_from, s_from, -1, 1, 4.0 * ((double)rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
       double rr = 0.0;
       for (int i = 0; i < batch; ++i) rr += (double)P.r[i] * P.r[i];
       int e = phase("lr_cholinv", "dion::k_lr_cholinv", 0.0, rr * 8.0, [&]() {
-        launch_lr_cholinv(d_descs, nmat, any_small, any_large, pass == 0 ? kShift : 0.f, stream);
+        launch_lr_cholinv(d_descs, nmat, any_small, any_large, pass == 0 ? kShift : 0.f, s_l + pass, stream);
         return DION_OK;
       });
       if (e != DION_OK) return e;
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
-        e = gprod("lr_orth", g, false, true, rows, g.r, g.r, 1.f, from[pass], LP_L, 0.f, to[pass],
-                  4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
+        e = gprod("lr_orth", g, false, true, rows, g.r, g.r, 1.f, from[pass], LP_L, 0.f, to[pass], s_from, s_l + pass,
+                  s_out + pass, 1, 4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
     }
     return DION_OK;
   };
-  if ((rc = cholqr3(LP_Y, LP_Y, LP_X, true)) != DION_OK) return rc;   // P = orth(Y), in X
+  if ((rc = cholqr3(LP_Y, LP_Y, LP_X, true, LS_Y, LS_L0, LS_F0)) != DION_OK) return rc;   // P = orth(Y), in X
   for (const LrGroup& g : P.groups)   // W = B^T P
-    if ((rc = gprod("lr_right", g, true, false, g.C, g.r, g.R, 1.f, LP_M, LP_X, 0.f, LP_W,
+    if ((rc = gprod("lr_right", g, true, false, g.C, g.r, g.R, 1.f, LP_M, LP_X, 0.f, LP_W, LS_B, LS_F2, LS_W, 1,
                     4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // M = B - beta P W^T
-    if ((rc = gprod("lr_feedback", g, false, true, g.R, g.C, g.r, -beta, LP_X, LP_W, 1.f, LP_M,
+    if ((rc = gprod("lr_feedback", g, false, true, g.R, g.C, g.r, -beta, LP_X, LP_W, 1.f, LP_M, LS_F2, LS_W, -1, 1,
                     4.0 * (2.0 * g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   if (mode == DION_LOWRANK_QR) {
-    if ((rc = cholqr3(LP_W, LP_W2, LP_Q, false)) != DION_OK) return rc;
+    if ((rc = cholqr3(LP_W, LP_W2, LP_Q, false, LS_W, LS_L3, LS_G0)) != DION_OK) return rc;
   } else {
-    double cr = 0.0;
-    for (int i = 0; i < batch; ++i) cr += (double)P.C[i] * P.r[i];
-    if ((rc = phase("lr_colnorm", "dion::k_lr_colnorm", 0.0, cr * 8.0, [&]() {
+    if ((rc = phase("lr_colnorm", "dion::k_lr_colnorm", 0.0, cr_all * 8.0, [&]() {
            launch_lr_colnorm(d_descs, nmat, stream);
            return DION_OK;
          })) != DION_OK) return rc;
   }
-  for (const LrGroup& g : P.groups)   // D = P Q^T
-    if ((rc = gprod("lr_update", g, false, true, g.R, g.C, g.r, 1.f, LP_X, LP_Q, 0.f, LP_D,
-                    4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
-  if (!P.out_fp32)
-    if ((rc = phase("lr_cast", "dion::k_lr_cast", 0.0, elems * (4.0 + dtype_bytes(out_dtype)), [&]() {
-           launch_lr_cast(d_descs, nmat, P.blocks, out_dtype, stream);
-           return DION_OK;
-         })) != DION_OK) return rc;
+  const double ob = (double)dtype_bytes(out_dtype);
+  for (const LrGroup& g : P.groups)   // D = P Q^T, in the output dtype
+    if ((rc = gprod("lr_update", g, false, true, g.R, g.C, g.r, 1.f, LP_X, LP_Q, 0.f, LP_D, LS_F2, LS_G2, -1,
+                    out_dtype, ob * g.R * g.C + 4.0 * ((double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);
   return DION_OK;

@@ -7,18 +7,32 @@
 //   C = alpha op(A) op(B) + beta C      (row-major fp32, a batch of same-shape
 //                                        products given as device pointer arrays)
 //
-// fp32 accuracy from bf16 matrix cores.  Each fp32 value splits exactly into
-// three bf16 terms by truncation: h = x with its low 16 bits cleared, m the
-// same of x - h, l = x - h - m (24 significand bits = 8 + 8 + 8; bf16 keeps
-// fp32's exponent range, so no operand needs a scale).  A product sums the six
-// term products down to relative weight 2^-16 (hh; hm, mh; hl, lh, mm), small
-// ones first, in v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the three
-// dropped ones weigh 2^-24 and less, the size of fp32's own rounding.
+// fp32 accuracy from 16-bit matrix cores, in one of two operand formats:
+//  - F16 (two fp16 terms): each operand is scaled by a power of two s, chosen
+//    from its largest |value| (recorded by the operand's producer) so that the
+//    largest scaled value lies in [2^13, 2^14), and split as h = fp16(x s),
+//    l = fp16(x s - h) (x s - h is exact in fp32): x s = h + l to 22
+//    significant bits, or to 2^-24 absolute for the values far below the
+//    largest.  A product sums hl, lh and hh in v_mfma_f32_32x32x16_f16 (the
+//    dropped ll weighs 2^-22) and is scaled back by 2^-(la + lb), exactly.
+//  - BF16x3 (three bf16 terms, no scale): h = x with its low 16 bits cleared,
+//    m the same of x - h, l = x - h - m (8 + 8 + 8 significand bits, fp32's
+//    exponent range).  A product sums the six term products down to relative
+//    weight 2^-16 (mm, hl, lh; hm, mh; hh) in v_mfma_f32_32x32x16_bf16; the
+//    dropped ones weigh 2^-24 and less, fp32's own rounding.
+// Term products are summed smallest first, with fp32 accumulation.  F16 does
+// half the matrix-core work.  Its 22 bits suffice where the result's error
+// is not amplified afterwards; the power product B Q, whose result is
+// orthogonalized (its error grows with the condition number of B Q), takes
+// BF16x3.  In emulation against the fp64 oracle on the randomized low-rank
+// draws (ranks up to the full dimension), the worst error is 2.9e-5 with
+// BF16x3 everywhere, 7.0e-5 with F16 everywhere and 4.0e-5 with BF16x3 for
+// the power product only.
 //
 // Tiles of 128 x 128 outputs, four waves of 64 x 64 (2 x 2 MFMA blocks).  A
 // K-stage of 32 columns is loaded from global memory into registers (16-byte
 // loads when the rows allow, zeros outside the matrix) while the previous
-// stage is multiplied, then split and stored to LDS as [row][k] bf16 rows of
+// stage is multiplied, then split and stored to LDS as [row][k] fp16 rows of
 // four 16-byte chunks per term, the chunk order XOR-swizzled by row so that
 // the fragment reads of 32 lanes hit distinct banks.  Operands stored with K
 // contiguous are staged row by row; operands stored with M (or N) contiguous
@@ -27,36 +41,58 @@
 
 #include <cstdint>
 
+#include "lowrank_internal.h"
+
 namespace dion {
 
 namespace {
 
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int LG_TILE = 128;
 constexpr int LG_BK = 32;
-constexpr int LG_TERM = LG_TILE * LG_BK;   // bf16 elements of one operand term of one stage
+constexpr int LG_TERM = LG_TILE * LG_BK;   // fp16 elements of one operand term of one stage
 
 // chunk c (8 k values) of row r, swizzled; element offset inside a term
 __device__ __forceinline__ int lg_off(int r, int c) { return r * LG_BK + ((c ^ ((r >> 2) & 3)) << 3); }
 
-// x = h + m + l exactly; the three bf16 bit patterns
-__device__ __forceinline__ void lg_split(float x, uint32_t& h, uint32_t& m, uint32_t& l) {
-  const uint32_t u = __float_as_uint(x);
-  h = u >> 16;
-  const float r1 = x - __uint_as_float(u & 0xFFFF0000u);
-  const uint32_t v = __float_as_uint(r1);
-  m = v >> 16;
-  const float r2 = r1 - __uint_as_float(v & 0xFFFF0000u);
-  l = __float_as_uint(r2) >> 16;   // at most 8 significant bits: exact
+// log2 of the scale for an operand whose largest |value| has fp32 bits `bits`
+// (0 for an all-zero operand); clamped so that 2^l is a normal float
+__device__ __forceinline__ int lg_log2_scale(unsigned bits) {
+  if (bits == 0u) return 0;
+  const int e = (int)(bits >> 23) - 127;   // floor(log2 max) (-127 for a subnormal max)
+  return min(max(13 - e, -126), 126);
+}
+
+// The terms of x as 16-bit patterns: F16, x s = t[0] + t[1]; BF16x3,
+// x = t[0] + t[1] + t[2]
+template <bool F16>
+__device__ __forceinline__ void lg_split(float x, float s, uint32_t* t) {
+  if (F16) {
+    const float xs = x * s;
+    const _Float16 hh = (_Float16)xs;
+    const _Float16 ll = (_Float16)(xs - (float)hh);
+    t[0] = __builtin_bit_cast(uint16_t, hh);
+    t[1] = __builtin_bit_cast(uint16_t, ll);
+  } else {
+    const uint32_t u = __float_as_uint(x);
+    t[0] = u >> 16;
+    const float r1 = x - __uint_as_float(u & 0xFFFF0000u);
+    const uint32_t v = __float_as_uint(r1);
+    t[1] = v >> 16;
+    const float r2 = r1 - __uint_as_float(v & 0xFFFF0000u);
+    t[2] = __float_as_uint(r2) >> 16;   // at most 8 significant bits: exact
+  }
 }
 
 // A K-stage of one operand: LG_TILE rows (of op(X)'s M or N side) x LG_BK k,
 // 16 values per thread.  KC: stored with k contiguous (element (r, k) at
 // p[r * ld + k]); otherwise with r contiguous (element (r, k) at p[k * ld + r]).
-template <bool KC>
+template <bool KC, bool F16>
 struct LgStage {
+  static constexpr int NT = F16 ? 2 : 3;   // terms
   float v[16];
   __device__ __forceinline__ void load(const float* p, int ld, int rows, int ks, int r0, int k0, bool vec) {
     const int t = threadIdx.x;
@@ -84,23 +120,22 @@ struct LgStage {
       }
     }
   }
-  // split and store to the three term arrays at s (bf16 bits as uint16)
-  __device__ __forceinline__ void store(uint16_t* s) const {
+  // (scale,) split and store to the NT term arrays at s
+  __device__ __forceinline__ void store(uint16_t* s, float scale) const {
     const int t = threadIdx.x;
     if (KC) {
       const int r = t >> 1, c0 = (t & 1) * 2;   // chunks c0, c0 + 1
-      uint32_t w[3][8];
+      uint32_t w[NT][8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        uint32_t h0, m0, l0, h1, m1, l1;
-        lg_split(v[2 * i], h0, m0, l0);
-        lg_split(v[2 * i + 1], h1, m1, l1);
-        w[0][i] = h0 | (h1 << 16);
-        w[1][i] = m0 | (m1 << 16);
-        w[2][i] = l0 | (l1 << 16);
+        uint32_t a[3], b[3];
+        lg_split<F16>(v[2 * i], scale, a);
+        lg_split<F16>(v[2 * i + 1], scale, b);
+#pragma unroll
+        for (int u = 0; u < NT; ++u) w[u][i] = a[u] | (b[u] << 16);
       }
 #pragma unroll
-      for (int u = 0; u < 3; ++u)
+      for (int u = 0; u < NT; ++u)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           *(uint4*)(s + u * LG_TERM + lg_off(r, c0 + c)) = make_uint4(w[u][4 * c], w[u][4 * c + 1], w[u][4 * c + 2],
@@ -109,32 +144,43 @@ struct LgStage {
       const int r0 = (t & 31) * 4, k = (t >> 5) * 4;   // four rows, k .. k+3
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t h[4], m[4], l[4];
+        uint32_t w[4][3];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lg_split(v[4 * i + j], h[i], m[i], l[i]);
+        for (int i = 0; i < 4; ++i) lg_split<F16>(v[4 * i + j], scale, w[i]);
         const int r = r0 + j, o = lg_off(r, k >> 3) + (k & 7);
-        *(uint2*)(s + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        *(uint2*)(s + LG_TERM + o) = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
-        *(uint2*)(s + 2 * LG_TERM + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+          *(uint2*)(s + u * LG_TERM + o) = make_uint2(w[0][u] | (w[1][u] << 16), w[2][u] | (w[3][u] << 16));
       }
     }
   }
 };
+
+__device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
 
 }  // namespace
 
 // Row-major C (M x N) = alpha op(A) op(B) + beta C for batch entry z =
 // blockIdx.z.  A_KC: A is stored M x K (K contiguous, op = N), else K x M
 // (op = T).  B_KC: B is stored N x K (op = T), else K x N (op = N).
-template <bool A_KC, bool B_KC>
+template <bool A_KC, bool B_KC, bool F16>
 __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alpha, const float* const* __restrict__ As,
                                                  int lda, const float* const* __restrict__ Bs, int ldb, float beta,
-                                                 float* const* __restrict__ Cs, int ldc) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[3 * LG_TERM], sB[3 * LG_TERM];
+                                                 void* const* __restrict__ Cs, int ldc,
+                                                 unsigned* const* __restrict__ amax, int sa, int sb, int sc,
+                                                 int out_fmt) {
+  constexpr int NT = F16 ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) uint16_t sA[NT * LG_TERM], sB[NT * LG_TERM];
   const int z = blockIdx.z;
   const float* A = As[z];
   const float* B = Bs[z];
-  float* C = Cs[z];
+  unsigned* slots = amax[z];
+  const int la = F16 ? lg_log2_scale(slots[sa]) : 0, lb = F16 ? lg_log2_scale(slots[sb]) : 0;
+  const float scale_a = ldexpf(1.f, la), scale_b = ldexpf(1.f, lb);
   const int m0 = blockIdx.y * LG_TILE, n0 = blockIdx.x * LG_TILE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -149,15 +195,15 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  LgStage<A_KC> ga;
-  LgStage<B_KC> gb;
+  LgStage<A_KC, F16> ga;
+  LgStage<B_KC, F16> gb;
   const int nk = (K + LG_BK - 1) / LG_BK;
   ga.load(A, lda, M, K, m0, 0, veca);
   gb.load(B, ldb, N, K, n0, 0, vecb);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();   // every wave is done with the previous stage
-    ga.store(sA);
-    gb.store(sB);
+    ga.store(sA, scale_a);
+    gb.store(sB, scale_b);
     __syncthreads();
     if (kt + 1 < nk) {   // the next stage's loads fly while this one is multiplied
       ga.load(A, lda, M, K, m0, (kt + 1) * LG_BK, veca);
@@ -166,61 +212,104 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int chunk = kk * 2 + (lane >> 5);
-      bf16x8 fa[3][2], fb[3][2];
+      uint4 fa[NT][2], fb[NT][2];   // eight 16-bit values each
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const int ra = wm * 64 + f * 32 + (lane & 31), rb = wn * 64 + f * 32 + (lane & 31);
 #pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          fa[u][f] = *(const bf16x8*)(sA + u * LG_TERM + lg_off(ra, chunk));
-          fb[u][f] = *(const bf16x8*)(sB + u * LG_TERM + lg_off(rb, chunk));
+        for (int u = 0; u < NT; ++u) {
+          fa[u][f] = *(const uint4*)(sA + u * LG_TERM + lg_off(ra, chunk));
+          fb[u][f] = *(const uint4*)(sB + u * LG_TERM + lg_off(rb, chunk));
         }
       }
-      // term products from the smallest weight: mm, hl, lh (2^-16), hm, mh (2^-8), hh
-      constexpr int PA[6] = {1, 0, 2, 0, 1, 0}, PB[6] = {1, 2, 0, 1, 0, 0};
+      // term products from the smallest weight: F16 hl, lh (2^-11), hh;
+      // BF16x3 mm, hl, lh (2^-16), hm, mh (2^-8), hh
+      constexpr int NP = F16 ? 3 : 6;
+      constexpr int PA[6] = {F16 ? 0 : 1, F16 ? 1 : 0, F16 ? 0 : 2, 0, 1, 0};
+      constexpr int PB[6] = {1, F16 ? 0 : 2, 0, 1, 0, 0};
 #pragma unroll
-      for (int p = 0; p < 6; ++p)
+      for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[PA[p]][a], fb[PB[p]][b], acc[a][b], 0, 0, 0);
+          for (int b = 0; b < 2; ++b) {
+            if (F16)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, fa[PA[p]][a]),
+                                                                 __builtin_bit_cast(halfx8, fb[PB[p]][b]), acc[a][b], 0,
+                                                                 0, 0);
+            else
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[PA[p]][a]),
+                                                                  __builtin_bit_cast(bf16x8, fb[PB[p]][b]), acc[a][b],
+                                                                  0, 0, 0);
+          }
     }
   }
   // epilogue: lane holds column (lane & 31) of rows (e/4)*8 + (lane/32)*4 + e%4 of each block
+  const int lab = la + lb;
+  float mx = 0.f;
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int col = n0 + wn * 64 + b * 32 + (lane & 31);
-      if (col >= N) continue;
+      const int rbase = m0 + wm * 64 + a * 32 + (lane >> 5) * 4;
+      float cv[16];
+      if (out_fmt == 1 && beta != 0.f) {   // every read of C before any write: 16 loads in flight
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + (e >> 2) * 8 + (e & 3);
+          cv[e] = (col < N && row < M) ? ((const float*)Cs[z])[(size_t)row * ldc + col] : 0.f;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 64 + a * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-        if (row < M) {
-          float* c = C + (size_t)row * ldc + col;
-          const float v = alpha * acc[a][b][e];
-          *c = beta != 0.f ? v + beta * *c : v;
+        const int row = rbase + (e >> 2) * 8 + (e & 3);
+        if (col < N && row < M) {
+          const size_t o = (size_t)row * ldc + col;
+          float v = alpha * ldexpf(acc[a][b][e], -lab);
+          if (out_fmt == 1) {
+            if (beta != 0.f) v = v + beta * cv[e];
+            ((float*)Cs[z])[o] = v;
+          } else {
+            ((uint16_t*)Cs[z])[o] = out_fmt == 0 ? lg_bf16_rne(v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+          }
+          mx = fmaxf(mx, fabsf(v));
         }
       }
     }
+  if (sc >= 0) {   // the result's largest |value| for the products that read it: one atomic per block
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    if (tid == 0) {
+      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (m > 0.f) atomicMax(slots + sc, __float_as_uint(m));
+    }
+  }
 }
 
-// Row-major C (m x n) = alpha op(A) op(B) + beta C over `count` pointer
-// triples (device arrays): A is m x k (k x m when ta), B is k x n (n x k when
-// tb), as the BLAS conventions read in row-major order.
-void launch_lr_gemm(bool ta, bool tb, int m, int n, int k, float alpha, const float* const* A, const float* const* B,
-                    float beta, float* const* C, int count, hipStream_t s) {
+void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
+                    const float* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
+                    int out_fmt, int count, hipStream_t s) {
   const int lda = ta ? m : k, ldb = tb ? k : n, ldc = n;
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
-  if (!ta && tb)
-    hipLaunchKernelGGL((k_lr_gemm<true, true>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
-  else if (!ta && !tb)
-    hipLaunchKernelGGL((k_lr_gemm<true, false>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
-  else if (ta && !tb)
-    hipLaunchKernelGGL((k_lr_gemm<false, false>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
-  else
-    hipLaunchKernelGGL((k_lr_gemm<false, true>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc);
+#define DION_LRG(AK, BK, F)                                                                                          \
+  hipLaunchKernelGGL((k_lr_gemm<AK, BK, F>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,   \
+                     amax, sa, sb, sc, out_fmt)
+  if (f16) {
+    if (!ta && tb) DION_LRG(true, true, true);
+    else if (!ta && !tb) DION_LRG(true, false, true);
+    else if (ta && !tb) DION_LRG(false, false, true);
+    else DION_LRG(false, true, true);
+  } else {
+    if (!ta && tb) DION_LRG(true, true, false);
+    else if (!ta && !tb) DION_LRG(true, false, false);
+    else if (ta && !tb) DION_LRG(false, false, false);
+    else DION_LRG(false, true, false);
+  }
+#undef DION_LRG
 }
 
 }  // namespace dion

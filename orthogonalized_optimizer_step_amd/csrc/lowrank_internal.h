@@ -20,11 +20,29 @@ struct LrDesc {
   float* S;          // r x r  Gram of the factor being orthogonalized
   float* Linv;       // r x r  inverse of its Cholesky factor (lower)
   double* A64;       // r x r  fp64 scratch of the factorization
-  float* D;          // R x C  fp32 update before the cast (or == out)
+  unsigned* amax;    // LS_N slots: the largest |value| of each operand the
+                     // GEMMs read (fp32 bits; zero at the start of a call)
   int64_t elems;     // R * C
   int64_t blk0;      // first block of this matrix in the element-wise launches
   int R, C, r;
   int pad_;
+};
+
+// Operands of the step's products, each with a slot for its largest |value|,
+// from which the GEMM that reads it takes its fp16 scale.  The producer of
+// an operand raises its slot (atomicMax on the bits of a non-negative float):
+// the accumulation for B (through per-block maxima), a small pass for the
+// incoming Q, the GEMM epilogues for their outputs, the factorization for
+// L^-1.  CholeskyQR3 of
+// the power product: pass p reads F_{p-1} (F_-1 = Y) and L_p, writes F_p
+// (F_2 = P); of the right factor: pass p reads G_{p-1} (G_-1 = W) and L_{3+p},
+// writes G_p (G_2 = the new Q).  Dion's column normalization bounds the new
+// Q by one: its slot starts at 1.
+enum LrSlot {
+  LS_B, LS_QIN, LS_Y, LS_W,
+  LS_L0, LS_L1, LS_L2, LS_L3, LS_L4, LS_L5,
+  LS_F0, LS_F1, LS_F2, LS_G0, LS_G1, LS_G2,
+  LS_N
 };
 
 // element-wise launches: 256 threads x 8 elements per block
@@ -32,11 +50,28 @@ constexpr int LR_BLOCK_ELEMS = 2048;
 // ranks up to this factor their Gram matrix in registers (k_lr_cholinv_reg)
 constexpr int LR_REG_RMAX = 256;
 
-void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, hipStream_t s);
-void launch_lr_cast(const LrDesc* d, int nmat, int64_t blocks, int out_fmt, hipStream_t s);
+// blocks per matrix of k_lr_absmax
+constexpr int LR_ABSMAX_SPLIT = 16;
+
+// B = fl32(M + G) in place, each block's largest |B| to blockmax (one float
+// per element-wise block); then the LS_B slot from those, and the LS_QIN slot
+// of the incoming right factor
+void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, float* blockmax, hipStream_t s);
+void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStream_t s);
 // shift > 0: factor S + shift * (largest diagonal entry of S) * I (the first,
-// shifted pass of shifted CholeskyQR3)
-void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, hipStream_t s);
+// shifted pass of shifted CholeskyQR3); the largest |entry| of L^-1 raises
+// slot `amax_slot`
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, int amax_slot,
+                       hipStream_t s);
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
+// Row-major C (m x n) = alpha op(A) op(B) + beta C over `count` products
+// (device pointer arrays; amax: each product's matrix's LS_N slots), on
+// two-term fp16 operands (f16) or three-term bf16 ones.  The fp16 operands'
+// scales come from slots sa and sb; sc >= 0 raises slot sc with the result's
+// largest |value|.  out_fmt: 1 fp32 (with beta), 0 bf16 or 2 fp16 (beta must
+// be 0; round to nearest even).
+void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
+                    const float* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
+                    int out_fmt, int count, hipStream_t s);
 
 }  // namespace dion

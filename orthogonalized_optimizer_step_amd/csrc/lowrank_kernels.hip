@@ -1,12 +1,14 @@
 // Kernels of the low-rank (Dion / Orth-Dion) step (Orth-Dion explainer,
 // technical summary: power iteration, residual buffer, column normalization
 // in Dion and QR of the right factor in Orth-Dion).  The rank-r products run
-// as batched GEMMs in rocBLAS; what is here is the rest of the step:
+// in k_lr_gemm (lowrank_gemm.hip); what is here is the rest of the step:
 //   k_lr_accumulate  B = fl32(M + G) in place (the residual buffer)
+//   k_lr_absmax      the largest |value| of B and of the incoming right factor
 //   k_lr_cholinv     Cholesky factor of an r x r Gram matrix in fp64 and the
 //                    inverse of that factor, for CholeskyQR (A = P L^-T)
 //   k_lr_colnorm     Dion's column normalization of the right factor
-//   k_lr_cast        the fp32 update to bf16 or fp16, round to nearest even
+// The first, second and fourth raise the max slots that the GEMMs take their
+// operand scales from.
 #include <hip/hip_runtime.h>
 
 #include "lowrank_internal.h"
@@ -31,69 +33,94 @@ __device__ __forceinline__ float lr_in(const void* p, int64_t e, int fmt) {
   return (float)__builtin_bit_cast(_Float16, u);
 }
 
-__device__ __forceinline__ uint16_t lr_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// the largest value of a block of `nthreads` (at most 1024; every thread
+// calls), in thread 0
+template <int NTHREADS>
+__device__ __forceinline__ float lr_block_max(float mx) {
+  __shared__ float red[NTHREADS / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int w = 1; w < NTHREADS / 64; ++w) mx = fmaxf(mx, red[w]);
+  return mx;
+}
+
+// the block's largest value into *slot (non-negative floats order as their bits)
+template <int NTHREADS>
+__device__ __forceinline__ void lr_raise(unsigned* slot, float mx) {
+  mx = lr_block_max<NTHREADS>(mx);
+  if (threadIdx.x == 0 && mx > 0.f) atomicMax(slot, __float_as_uint(mx));
 }
 
 }  // namespace
 
-// B = fl32(M + G): one correctly rounded addition per element, 8 per thread.
-__global__ __launch_bounds__(256) void k_lr_accumulate(const LrDesc* __restrict__ descs, int nmat, int fmt) {
+// B = fl32(M + G): one correctly rounded addition per element, 8 per thread;
+// the block's largest |B| goes to blockmax[block] (k_lr_absmax reduces them:
+// atomics to one address per matrix from every block would serialize).
+__global__ __launch_bounds__(256) void k_lr_accumulate(const LrDesc* __restrict__ descs, int nmat, int fmt,
+                                                       float* __restrict__ blockmax) {
   const int64_t b = blockIdx.x;
   const LrDesc& d = descs[lr_mat_of_block(descs, nmat, b)];
   const int64_t e0 = (b - d.blk0) * LR_BLOCK_ELEMS + (int64_t)threadIdx.x * 8;
-  if (e0 >= d.elems) return;
-  float* M = d.M + e0;
-  if (e0 + 8 <= d.elems && ((uintptr_t)M & 31) == 0) {
-    float4 m0 = *(const float4*)M, m1 = *(const float4*)(M + 4);
-    float g[8];
-    if (fmt == 1 && ((uintptr_t)((const float*)d.G + e0) & 15) == 0) {
-      const float4 g0 = *(const float4*)((const float*)d.G + e0), g1 = *(const float4*)((const float*)d.G + e0 + 4);
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-    } else {
+  float mx = 0.f;
+  if (e0 < d.elems) {
+    float* M = d.M + e0;
+    if (e0 + 8 <= d.elems && ((uintptr_t)M & 31) == 0) {
+      float4 m0 = *(const float4*)M, m1 = *(const float4*)(M + 4);
+      float g[8];
+      if (fmt == 1 && ((uintptr_t)((const float*)d.G + e0) & 15) == 0) {
+        const float4 g0 = *(const float4*)((const float*)d.G + e0), g1 = *(const float4*)((const float*)d.G + e0 + 4);
+        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) g[i] = lr_in(d.G, e0 + i, fmt);
+        for (int i = 0; i < 8; ++i) g[i] = lr_in(d.G, e0 + i, fmt);
+      }
+      m0.x = __fadd_rn(m0.x, g[0]); m0.y = __fadd_rn(m0.y, g[1]); m0.z = __fadd_rn(m0.z, g[2]); m0.w = __fadd_rn(m0.w, g[3]);
+      m1.x = __fadd_rn(m1.x, g[4]); m1.y = __fadd_rn(m1.y, g[5]); m1.z = __fadd_rn(m1.z, g[6]); m1.w = __fadd_rn(m1.w, g[7]);
+      *(float4*)M = m0;
+      *(float4*)(M + 4) = m1;
+      mx = fmaxf(fmaxf(fmaxf(fabsf(m0.x), fabsf(m0.y)), fmaxf(fabsf(m0.z), fabsf(m0.w))),
+                 fmaxf(fmaxf(fabsf(m1.x), fabsf(m1.y)), fmaxf(fabsf(m1.z), fabsf(m1.w))));
+    } else {
+      for (int i = 0; i < 8 && e0 + i < d.elems; ++i) {
+        M[i] = __fadd_rn(M[i], lr_in(d.G, e0 + i, fmt));
+        mx = fmaxf(mx, fabsf(M[i]));
+      }
     }
-    m0.x = __fadd_rn(m0.x, g[0]); m0.y = __fadd_rn(m0.y, g[1]); m0.z = __fadd_rn(m0.z, g[2]); m0.w = __fadd_rn(m0.w, g[3]);
-    m1.x = __fadd_rn(m1.x, g[4]); m1.y = __fadd_rn(m1.y, g[5]); m1.z = __fadd_rn(m1.z, g[6]); m1.w = __fadd_rn(m1.w, g[7]);
-    *(float4*)M = m0;
-    *(float4*)(M + 4) = m1;
-  } else {
-    for (int i = 0; i < 8 && e0 + i < d.elems; ++i) M[i] = __fadd_rn(M[i], lr_in(d.G, e0 + i, fmt));
   }
+  mx = lr_block_max<256>(mx);
+  if (threadIdx.x == 0) blockmax[b] = mx;
 }
 
-// The fp32 update D to the output dtype (0 bf16, 2 fp16), 8 elements per thread.
-__global__ __launch_bounds__(256) void k_lr_cast(const LrDesc* __restrict__ descs, int nmat, int fmt) {
-  const int64_t b = blockIdx.x;
-  const LrDesc& d = descs[lr_mat_of_block(descs, nmat, b)];
-  const int64_t e0 = (b - d.blk0) * LR_BLOCK_ELEMS + (int64_t)threadIdx.x * 8;
-  if (e0 >= d.elems) return;
-  const float* D = d.D + e0;
-  uint16_t* o = (uint16_t*)d.out + e0;
-  const int n = e0 + 8 <= d.elems ? 8 : (int)(d.elems - e0);
-  float v[8];
-  if (n == 8 && ((uintptr_t)D & 15) == 0) {
-    *(float4*)&v[0] = *(const float4*)D;
-    *(float4*)&v[4] = *(const float4*)(D + 4);
+// Grid (LR_ABSMAX_SPLIT, matrices): block x of matrix i reduces its share of
+// the matrix's block maxima from k_lr_accumulate into the LS_B slot, and its
+// share of the incoming right factor Q (C x r, float4 loads when aligned)
+// into the LS_QIN slot.
+__global__ __launch_bounds__(256) void k_lr_absmax(const LrDesc* __restrict__ descs,
+                                                   const float* __restrict__ blockmax) {
+  const LrDesc& d = descs[blockIdx.y];
+  const int parts = gridDim.x, part = blockIdx.x, tid = threadIdx.x;
+  const int64_t nb = (d.elems + LR_BLOCK_ELEMS - 1) / LR_BLOCK_ELEMS;
+  float mb = 0.f;
+  for (int64_t e = (int64_t)part * 256 + tid; e < nb; e += (int64_t)parts * 256) mb = fmaxf(mb, blockmax[d.blk0 + e]);
+  lr_raise<256>(d.amax + LS_B, mb);
+  const int64_t n = (int64_t)d.C * d.r;
+  float mq = 0.f;
+  if (((uintptr_t)d.Q & 15) == 0) {
+    const int64_t n4 = n / 4;
+    const float4* q4 = (const float4*)d.Q;
+    for (int64_t e = (int64_t)part * 256 + tid; e < n4; e += (int64_t)parts * 256) {
+      const float4 v = q4[e];
+      mq = fmaxf(mq, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    for (int64_t e = n4 * 4 + part * 256 + tid; e < n; e += (int64_t)parts * 256) mq = fmaxf(mq, fabsf(d.Q[e]));
   } else {
-    for (int i = 0; i < n; ++i) v[i] = D[i];
+    for (int64_t e = (int64_t)part * 256 + tid; e < n; e += (int64_t)parts * 256) mq = fmaxf(mq, fabsf(d.Q[e]));
   }
-  uint16_t h[8];
-  for (int i = 0; i < n; ++i)
-    h[i] = fmt == 0 ? lr_bf16_rne(v[i]) : __builtin_bit_cast(uint16_t, (_Float16)v[i]);
-  if (n == 8 && ((uintptr_t)o & 15) == 0) {
-    uint4 pk;
-    pk.x = h[0] | ((uint32_t)h[1] << 16);
-    pk.y = h[2] | ((uint32_t)h[3] << 16);
-    pk.z = h[4] | ((uint32_t)h[5] << 16);
-    pk.w = h[6] | ((uint32_t)h[7] << 16);
-    *(uint4*)o = pk;
-  } else {
-    for (int i = 0; i < n; ++i) o[i] = h[i];
-  }
+  __syncthreads();   // lr_block_max's LDS is reused
+  lr_raise<256>(d.amax + LS_QIN, mq);
 }
 
 // One block per matrix.  From the Gram S = F^T F (r x r, fp32, symmetric) of
@@ -107,7 +134,7 @@ __global__ __launch_bounds__(256) void k_lr_cast(const LrDesc* __restrict__ desc
 // contract): its column of L^-1 and of the result is zero, which keeps every
 // value finite.  The inverse is column-wise forward substitution, one column
 // per thread, X = L^-1 kept transposed in the upper triangle of the scratch.
-__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, float shift) {
+__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, float shift, int amax_slot) {
   const LrDesc& d = descs[blockIdx.x];
   const int r = d.r;
   if (r <= LR_REG_RMAX) return;   // k_lr_cholinv_reg
@@ -169,10 +196,14 @@ __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ d
     }
   }
   __syncthreads();
+  float mxl = 0.f;
   for (int e = tid; e < r * r; e += 256) {
     const int i = e / r, c = e - (e / r) * r;
-    d.Linv[e] = i >= c ? (float)A[(size_t)c * r + i] : 0.f;
+    const float x = i >= c ? (float)A[(size_t)c * r + i] : 0.f;
+    d.Linv[e] = x;
+    mxl = fmaxf(mxl, fabsf(x));
   }
+  lr_raise<256>(d.amax + amax_slot, mxl);
 }
 
 // The same factorization for r <= 256 with the lower triangle held in
@@ -193,7 +224,8 @@ constexpr int LR_NB = LR_REG_RMAX / LR_GRID;
 constexpr int LR_SLOTS = LR_NB * (LR_NB + 1) / 2;
 static_assert(LR_GRID * LR_GRID == LR_REG_THREADS, "thread grid");
 
-__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, float shift) {
+__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, float shift,
+                                                          int amax_slot) {
   const LrDesc& d = descs[blockIdx.x];
   const int r = d.r;
   if (r > LR_REG_RMAX) return;    // k_lr_cholinv
@@ -269,7 +301,15 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
     const int i = e / r, c = e - (e / r) * r;
     if (c > i) d.Linv[e] = 0.f;
   }
-  LR_FOR_SLOTS({ if (own) d.Linv[(size_t)i * r + c] = (float)v[sl]; })
+  float mxl = 0.f;
+  LR_FOR_SLOTS({
+    if (own) {
+      const float x = (float)v[sl];
+      d.Linv[(size_t)i * r + c] = x;
+      mxl = fmaxf(mxl, fabsf(x));
+    }
+  })
+  lr_raise<LR_REG_THREADS>(d.amax + amax_slot, mxl);
 #undef LR_FOR_SLOTS
 }
 
@@ -289,15 +329,18 @@ __global__ __launch_bounds__(256) void k_lr_colnorm(const LrDesc* __restrict__ d
   }
 }
 
-void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, hipStream_t s) {
-  if (blocks > 0) hipLaunchKernelGGL(k_lr_accumulate, dim3((unsigned)blocks), dim3(256), 0, s, d, nmat, grad_fmt);
+void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, float* blockmax, hipStream_t s) {
+  if (blocks > 0)
+    hipLaunchKernelGGL(k_lr_accumulate, dim3((unsigned)blocks), dim3(256), 0, s, d, nmat, grad_fmt, blockmax);
 }
-void launch_lr_cast(const LrDesc* d, int nmat, int64_t blocks, int out_fmt, hipStream_t s) {
-  if (blocks > 0) hipLaunchKernelGGL(k_lr_cast, dim3((unsigned)blocks), dim3(256), 0, s, d, nmat, out_fmt);
+void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStream_t s) {
+  if (nmat > 0) hipLaunchKernelGGL(k_lr_absmax, dim3(LR_ABSMAX_SPLIT, nmat), dim3(256), 0, s, d, blockmax);
 }
-void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, hipStream_t s) {
-  if (nmat > 0 && any_small) hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, shift);
-  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, shift);
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, int amax_slot,
+                       hipStream_t s) {
+  if (nmat > 0 && any_small)
+    hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, shift, amax_slot);
+  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, shift, amax_slot);
 }
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s) {
   if (nmat > 0) hipLaunchKernelGGL(k_lr_colnorm, dim3(nmat), dim3(256), 0, s, d);
