@@ -1618,7 +1618,9 @@ void make_update(Plan& P, int w_dtype, float weight_decay) {
 // operand's producer raises; the slots live in the uploaded header, so every
 // call starts them at zero (and Dion's normalized Q at one).
 constexpr int kMaxRank = 512;
-enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_AM, LP_N };
+// pointer arrays per group: the matrices' buffers, the max slots, and the
+// split (fp16 hi and lo) copies of P, W and the new Q
+enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_AM, LP_XS, LP_WS, LP_QS, LP_N };
 
 struct LrGroup {
   int R, C, r;
@@ -1680,6 +1682,10 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
     P.off[LP_S][i] = off;  off = align256(off + 4 * r * r);
     P.off[LP_L][i] = off;  off = align256(off + 4 * r * r);
     P.off_a64[i] = off;    off = align256(off + 8 * r * r);
+    const size_t ldp = (r + 7) / 8 * 8;
+    P.off[LP_XS][i] = off; off = align256(off + 4 * R * ldp);
+    P.off[LP_WS][i] = off; off = align256(off + 4 * C * ldp);
+    P.off[LP_QS][i] = off; off = align256(off + 4 * C * ldp);
   }
   P.total = off;
   return DION_OK;
@@ -1719,7 +1725,10 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     const size_t n = g.mats.size();
     for (size_t t = 0; t < n; ++t) {
       const LrDesc& d = descs[g.mats[t]];
-      float* const v[LP_N] = {d.M, d.Q, d.X, d.Y, d.W, d.W2, d.S, d.Linv, (float*)d.out, (float*)d.amax};
+      const int i = g.mats[t];
+      float* const v[LP_N] = {d.M, d.Q, d.X, d.Y, d.W, d.W2, d.S, d.Linv, (float*)d.out, (float*)d.amax,
+                              (float*)(ws + P.off[LP_XS][i]), (float*)(ws + P.off[LP_WS][i]),
+                              (float*)(ws + P.off[LP_QS][i])};
       for (int k = 0; k < LP_N; ++k) arr[k * n + t] = v[k];
     }
   }
@@ -1754,11 +1763,12 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   };
   // kernel instance names as profilers print them
   auto gemm_name = [](bool ta, bool tb, bool f16) {
+    // <A layout, B layout, F16>: layout 0 r contiguous, 1 k contiguous, 2 split
     static const char* names[8] = {
-        "dion::k_lr_gemm<true, false, false>", "dion::k_lr_gemm<true, true, false>",
-        "dion::k_lr_gemm<false, false, false>", "dion::k_lr_gemm<false, true, false>",
-        "dion::k_lr_gemm<true, false, true>",  "dion::k_lr_gemm<true, true, true>",
-        "dion::k_lr_gemm<false, false, true>",  "dion::k_lr_gemm<false, true, true>"};
+        "dion::k_lr_gemm<1, 0, false>", "dion::k_lr_gemm<1, 1, false>",
+        "dion::k_lr_gemm<0, 0, false>", "dion::k_lr_gemm<0, 1, false>",
+        "dion::k_lr_gemm<1, 0, true>",  "dion::k_lr_gemm<1, 1, true>",
+        "dion::k_lr_gemm<0, 0, true>",  "dion::k_lr_gemm<0, 1, true>"};
     return names[(f16 ? 4 : 0) + (ta ? 2 : 0) + (tb ? 1 : 0)];
   };
   bool any_small = false, any_large = false;
@@ -1783,6 +1793,28 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     });
   };
 
+  // split copies of a group's rows x r operand (fp16 hi and lo, rows padded to ldp)
+  auto gsplit = [&](const LrGroup& g, int src, int dst, int rows, int slot) -> int {
+    const int ldp = (g.r + 7) / 8 * 8;
+    const double cnt = (double)g.mats.size();
+    return phase("lr_split", "dion::k_lr_split16", 0.0, cnt * rows * (4.0 * g.r + 4.0 * ldp), [&]() {
+      launch_lr_split16((const float* const*)arrays(g, src), (uint16_t* const*)arrays(g, dst), rows, g.r, ldp,
+                        (unsigned* const*)arrays(g, LP_AM), slot, (int)g.mats.size(), stream);
+      return DION_OK;
+    });
+  };
+  // C (R x C) = alpha P Z^T + beta C from the split P and Z (C x r), inner dimension r
+  auto gprod_split = [&](const char* name, const LrGroup& g, float alpha, int Z, float beta_, int Cm, int sz,
+                         int out_fmt, double bytes_each) -> int {
+    const int ldp = (g.r + 7) / 8 * 8;
+    const double cnt = (double)g.mats.size();
+    return phase(name, "dion::k_lr_gemm<2, 2, true>", 2.0 * g.R * g.C * g.r * cnt, bytes_each * cnt, [&]() {
+      launch_lr_gemm_split(g.R, g.C, g.r, ldp, alpha, (const uint16_t* const*)arrays(g, LP_XS),
+                           (const uint16_t* const*)arrays(g, Z), beta_, (void* const*)arrays(g, Cm),
+                           (unsigned* const*)arrays(g, LP_AM), LS_F2, sz, -1, out_fmt, (int)g.mats.size(), stream);
+      return DION_OK;
+    });
+  };
   const double gsz = (double)dtype_bytes(grad_dtype);
   if ((rc = phase("lr_accumulate", "dion::k_lr_accumulate", 0.0, elems * (8.0 + gsz), [&]() {
          launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, (float*)(ws + P.off_blockmax), stream);
@@ -1835,12 +1867,16 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     return DION_OK;
   };
   if ((rc = cholqr3(LP_Y, LP_Y, LP_X, true, LS_Y, LS_L0, LS_F0)) != DION_OK) return rc;   // P = orth(Y), in X
+  for (const LrGroup& g : P.groups)   // the split P, for the buffer update and the update
+    if ((rc = gsplit(g, LP_X, LP_XS, g.R, LS_F2)) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // W = B^T P
     if ((rc = gprod("lr_right", g, true, false, g.C, g.r, g.R, 1.f, LP_M, LP_X, 0.f, LP_W, LS_B, LS_F2, LS_W, 1,
                     4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
+  for (const LrGroup& g : P.groups)
+    if ((rc = gsplit(g, LP_W, LP_WS, g.C, LS_W)) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // M = B - beta P W^T
-    if ((rc = gprod("lr_feedback", g, false, true, g.R, g.C, g.r, -beta, LP_X, LP_W, 1.f, LP_M, LS_F2, LS_W, -1, 1,
-                    4.0 * (2.0 * g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
+    if ((rc = gprod_split("lr_feedback", g, -beta, LP_WS, 1.f, LP_M, LS_W, 1,
+                          4.0 * (2.0 * g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   if (mode == DION_LOWRANK_QR) {
     if ((rc = cholqr3(LP_W, LP_W2, LP_Q, false, LS_W, LS_L3, LS_G0)) != DION_OK) return rc;
   } else {
@@ -1849,10 +1885,12 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
            return DION_OK;
          })) != DION_OK) return rc;
   }
+  for (const LrGroup& g : P.groups)
+    if ((rc = gsplit(g, LP_Q, LP_QS, g.C, LS_G2)) != DION_OK) return rc;
   const double ob = (double)dtype_bytes(out_dtype);
   for (const LrGroup& g : P.groups)   // D = P Q^T, in the output dtype
-    if ((rc = gprod("lr_update", g, false, true, g.R, g.C, g.r, 1.f, LP_X, LP_Q, 0.f, LP_D, LS_F2, LS_G2, -1,
-                    out_dtype, ob * g.R * g.C + 4.0 * ((double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
+    if ((rc = gprod_split("lr_update", g, 1.f, LP_QS, 0.f, LP_D, LS_G2, out_dtype,
+                          ob * g.R * g.C + 4.0 * ((double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);
   return DION_OK;

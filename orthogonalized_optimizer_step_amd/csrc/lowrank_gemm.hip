@@ -29,6 +29,13 @@
 // BF16x3 everywhere, 7.0e-5 with F16 everywhere and 4.0e-5 with BF16x3 for
 // the power product only.
 //
+// A small F16 operand read by many blocks (P, W and the new Q in the buffer
+// update and the update, whose inner dimension is the rank) is split once by
+// k_lr_split16 into hi and lo arrays of fp16 rows (K contiguous, padded to a
+// multiple of 8 with zeros), and the GEMM copies its terms to LDS as they
+// are: the split of a 128-row operand tile would otherwise be repeated by
+// every block of the other dimension.
+//
 // Tiles of 128 x 128 outputs, four waves of 64 x 64 (2 x 2 MFMA blocks).  A
 // K-stage of 32 columns is loaded from global memory into registers (16-byte
 // loads when the rows allow, zeros outside the matrix) while the previous
@@ -87,11 +94,16 @@ __device__ __forceinline__ void lg_split(float x, float s, uint32_t* t) {
   }
 }
 
+// operand layouts: fp32 with r (the M or N index) contiguous, fp32 with k
+// contiguous, or split ahead into fp16 hi and lo rows with k contiguous
+enum { LG_RC = 0, LG_KC = 1, LG_PRE = 2 };
+
 // A K-stage of one operand: LG_TILE rows (of op(X)'s M or N side) x LG_BK k,
 // 16 values per thread.  KC: stored with k contiguous (element (r, k) at
 // p[r * ld + k]); otherwise with r contiguous (element (r, k) at p[k * ld + r]).
-template <bool KC, bool F16>
+template <int MODE, bool F16>
 struct LgStage {
+  static constexpr bool KC = MODE == LG_KC;
   static constexpr int NT = F16 ? 2 : 3;   // terms
   float v[16];
   __device__ __forceinline__ void load(const float* p, int ld, int rows, int ks, int r0, int k0, bool vec) {
@@ -122,6 +134,7 @@ struct LgStage {
   }
   // (scale,) split and store to the NT term arrays at s
   __device__ __forceinline__ void store(uint16_t* s, float scale) const {
+    static_assert(MODE != LG_PRE, "split operands have their own stage");
     const int t = threadIdx.x;
     if (KC) {
       const int r = t >> 1, c0 = (t & 1) * 2;   // chunks c0, c0 + 1
@@ -156,6 +169,34 @@ struct LgStage {
   }
 };
 
+// A K-stage of a split operand: hi rows at p, lo rows at p + term (fp16,
+// row length ld, a multiple of 8, zero beyond the operand's K); thread t
+// copies chunks (t&1)*2 and +1 of row t/2 of both terms, 16 bytes each.
+template <>
+struct LgStage<LG_PRE, true> {
+  uint4 v[4];
+  __device__ __forceinline__ void load(const uint16_t* p, int ld, int rows, int term, int r0, int k0) {
+    const int t = threadIdx.x;
+    const int r = r0 + (t >> 1), k = k0 + (t & 1) * 16;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int kc = k + 8 * c;
+        v[2 * u + c] = (r < rows && kc < ld) ? *(const uint4*)(p + (size_t)u * term + (size_t)r * ld + kc)
+                                              : make_uint4(0u, 0u, 0u, 0u);
+      }
+  }
+  __device__ __forceinline__ void store(uint16_t* s) const {
+    const int t = threadIdx.x;
+    const int r = t >> 1, c0 = (t & 1) * 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) *(uint4*)(s + u * LG_TERM + lg_off(r, c0 + c)) = v[2 * u + c];
+  }
+};
+
 __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -165,9 +206,11 @@ __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
 }  // namespace
 
 // Row-major C (M x N) = alpha op(A) op(B) + beta C for batch entry z =
-// blockIdx.z.  A_KC: A is stored M x K (K contiguous, op = N), else K x M
-// (op = T).  B_KC: B is stored N x K (op = T), else K x N (op = N).
-template <bool A_KC, bool B_KC, bool F16>
+// blockIdx.z.  A_MODE LG_KC: A is stored M x K (K contiguous, op = N); LG_RC:
+// K x M (op = T); LG_PRE: split fp16 rows M x K (ld = the padded row).
+// B_MODE LG_KC: B is stored N x K (op = T); LG_RC: K x N (op = N); LG_PRE:
+// split fp16 rows N x K.
+template <int A_MODE, int B_MODE, bool F16>
 __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alpha, const float* const* __restrict__ As,
                                                  int lda, const float* const* __restrict__ Bs, int ldb, float beta,
                                                  void* const* __restrict__ Cs, int ldc,
@@ -186,6 +229,7 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
   const int wm = wave >> 1, wn = wave & 1;
   const bool veca = (lda & 3) == 0 && ((uintptr_t)A & 15) == 0;
   const bool vecb = (ldb & 3) == 0 && ((uintptr_t)B & 15) == 0;
+  static_assert(F16 || (A_MODE != LG_PRE && B_MODE != LG_PRE), "split operands are fp16");
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -195,20 +239,24 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  LgStage<A_KC, F16> ga;
-  LgStage<B_KC, F16> gb;
+  LgStage<A_MODE, F16> ga;
+  LgStage<B_MODE, F16> gb;
   const int nk = (K + LG_BK - 1) / LG_BK;
-  ga.load(A, lda, M, K, m0, 0, veca);
-  gb.load(B, ldb, N, K, n0, 0, vecb);
+  auto load = [&](int k0) {
+    if constexpr (A_MODE == LG_PRE) ga.load((const uint16_t*)A, lda, M, M * lda, m0, k0);
+    else ga.load(A, lda, M, K, m0, k0, veca);
+    if constexpr (B_MODE == LG_PRE) gb.load((const uint16_t*)B, ldb, N, N * ldb, n0, k0);
+    else gb.load(B, ldb, N, K, n0, k0, vecb);
+  };
+  load(0);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();   // every wave is done with the previous stage
-    ga.store(sA, scale_a);
-    gb.store(sB, scale_b);
+    if constexpr (A_MODE == LG_PRE) ga.store(sA);
+    else ga.store(sA, scale_a);
+    if constexpr (B_MODE == LG_PRE) gb.store(sB);
+    else gb.store(sB, scale_b);
     __syncthreads();
-    if (kt + 1 < nk) {   // the next stage's loads fly while this one is multiplied
-      ga.load(A, lda, M, K, m0, (kt + 1) * LG_BK, veca);
-      gb.load(B, ldb, N, K, n0, (kt + 1) * LG_BK, vecb);
-    }
+    if (kt + 1 < nk) load((kt + 1) * LG_BK);   // the next stage's loads fly while this one is multiplied
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int chunk = kk * 2 + (lane >> 5);
@@ -299,17 +347,69 @@ void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha
   hipLaunchKernelGGL((k_lr_gemm<AK, BK, F>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,   \
                      amax, sa, sb, sc, out_fmt)
   if (f16) {
-    if (!ta && tb) DION_LRG(true, true, true);
-    else if (!ta && !tb) DION_LRG(true, false, true);
-    else if (ta && !tb) DION_LRG(false, false, true);
-    else DION_LRG(false, true, true);
+    if (!ta && tb) DION_LRG(LG_KC, LG_KC, true);
+    else if (!ta && !tb) DION_LRG(LG_KC, LG_RC, true);
+    else if (ta && !tb) DION_LRG(LG_RC, LG_RC, true);
+    else DION_LRG(LG_RC, LG_KC, true);
   } else {
-    if (!ta && tb) DION_LRG(true, true, false);
-    else if (!ta && !tb) DION_LRG(true, false, false);
-    else if (ta && !tb) DION_LRG(false, false, false);
-    else DION_LRG(false, true, false);
+    if (!ta && tb) DION_LRG(LG_KC, LG_KC, false);
+    else if (!ta && !tb) DION_LRG(LG_KC, LG_RC, false);
+    else if (ta && !tb) DION_LRG(LG_RC, LG_RC, false);
+    else DION_LRG(LG_RC, LG_KC, false);
   }
 #undef DION_LRG
+}
+
+void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint16_t* const* A, const uint16_t* const* B,
+                          float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc, int out_fmt,
+                          int count, hipStream_t s) {
+  const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
+  hipLaunchKernelGGL((k_lr_gemm<LG_PRE, LG_PRE, true>), grid, dim3(256), 0, s, m, n, k, alpha,
+                     (const float* const*)A, ldp, (const float* const*)B, ldp, beta, C, n, amax, sa, sb, sc, out_fmt);
+}
+
+// Split a batch of row-major fp32 matrices (rows x k) into fp16 hi and lo
+// rows of length ldp (k rounded up to 8, zeros beyond k) at dst (lo after
+// hi), with the scale that slot `slot` gives: the F16 operand format above.
+// Grid (blocks over rows * ldp / 8, count), 8 values per thread.
+__global__ __launch_bounds__(256) void k_lr_split16(const float* const* __restrict__ src, uint16_t* const* __restrict__ dst,
+                                                    int rows, int k, int ldp, unsigned* const* __restrict__ amax,
+                                                    int slot) {
+  const int z = blockIdx.y;
+  const int64_t e8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = ldp / 8;
+  if (e8 >= (int64_t)rows * cpr) return;
+  const int r = (int)(e8 / cpr), k0 = (int)(e8 - (int64_t)r * cpr) * 8;
+  const float scale = ldexpf(1.f, lg_log2_scale(amax[z][slot]));
+  const float* p = src[z] + (size_t)r * k + k0;
+  float v[8];
+  if (k0 + 8 <= k && (k & 3) == 0 && ((uintptr_t)src[z] & 15) == 0) {
+    *(float4*)&v[0] = *(const float4*)p;
+    *(float4*)&v[4] = *(const float4*)(p + 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = k0 + i < k ? p[i] : 0.f;
+  }
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t a[3], b[3];
+    lg_split<true>(v[2 * i], scale, a);
+    lg_split<true>(v[2 * i + 1], scale, b);
+    h[i] = a[0] | (b[0] << 16);
+    l[i] = a[1] | (b[1] << 16);
+  }
+  uint16_t* d = dst[z] + (size_t)r * ldp + k0;
+  *(uint4*)d = make_uint4(h[0], h[1], h[2], h[3]);
+  *(uint4*)(d + (size_t)rows * ldp) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+void launch_lr_split16(const float* const* src, uint16_t* const* dst, int rows, int k, int ldp,
+                       unsigned* const* amax, int slot, int count, hipStream_t s) {
+  const int64_t n8 = (int64_t)rows * (ldp / 8);
+  if (n8 > 0 && count > 0)
+    hipLaunchKernelGGL(k_lr_split16, dim3((unsigned)((n8 + 255) / 256), count), dim3(256), 0, s, src, dst, rows, k, ldp,
+                       amax, slot);
 }
 
 }  // namespace dion

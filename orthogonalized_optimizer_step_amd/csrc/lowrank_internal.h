@@ -73,5 +73,15 @@ void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
                     const float* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
                     int out_fmt, int count, hipStream_t s);
+// The same with both operands split ahead by launch_lr_split16: A as m rows
+// and B as n rows of k values (fp16 hi and lo, row length ldp), C = A B^T.
+void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint16_t* const* A, const uint16_t* const* B,
+                          float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc, int out_fmt,
+                          int count, hipStream_t s);
+// Split `count` row-major fp32 matrices (rows x k) with the scale of slot
+// `slot` into fp16 hi and lo rows of length ldp = k rounded up to 8 (zeros
+// beyond k; lo after hi): rows * ldp * 4 bytes at each dst.
+void launch_lr_split16(const float* const* src, uint16_t* const* dst, int rows, int k, int ldp,
+                       unsigned* const* amax, int slot, int count, hipStream_t s);
 
 }  // namespace dion
