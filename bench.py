@@ -343,7 +343,12 @@ def bench_lowrank(args, torch, dion):
     dom = max((k for k, v in kernels.items() if v["useful"] > 0), key=lambda k: kernels[k]["ms"])
     d = kernels[dom]
     avg_ms = d["ms"] / d["launches"]
-    achieved = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
+    useful_rate = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
+    # the products are fp32 GEMMs computed on 16-bit matrix cores: two fp16
+    # terms per operand (three MFMA products; template flag true) or three
+    # bf16 terms (six): priced as the MFMA work they execute
+    terms = 3 if dom.endswith("true>") else 6
+    achieved = useful_rate * terms
     useful = sum(v["useful"] for v in phases.values()) / args.steps
     params = sum(r * c for r, c in shapes)
     line = {
@@ -364,9 +369,11 @@ def bench_lowrank(args, torch, dion):
                    "matrices": len(shapes), "params": params, "rank": LOWRANK_RANK},
         "useful_tflops": useful / (ms_per_step * 1e-3) / 1e12,
         "host_wall_s": wall,
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_MFMA32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA32_TFLOPS, "traffic": None,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_MFMA16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA16_TFLOPS, "traffic": None,
                      "launch_ms": avg_ms, "useful_flops_per_launch": d["useful"] / d["launches"],
+                     "mfma_products_per_useful": terms,
+                     "useful_fp32_tflops": useful_rate, "fp32_matrix_peak": PEAK_MFMA32_TFLOPS,
                      "algorithmic_bytes_per_launch": d["bytes"] / d["launches"]},
         "phases": {n: {"ms_per_step": round(p["ms"] / args.steps, 3),
                        "launches_per_step": p["launches"] // args.steps,

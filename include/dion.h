@@ -279,10 +279,14 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
  *   rank      1 .. 512 (DION_E_UNSUPPORTED above)
  * The rank-r products run in this library's GEMM kernel (one launch per
  * distinct (R, C, r) and product, with device pointer arrays from the
- * uploaded header): fp32 operands split exactly into three bf16 terms, six
- * bf16 MFMA products of relative weight down to 2^-16 summed in fp32.  All
- * memory is the caller's workspace; no handle or other state is kept.
- * Asynchronous on `stream`. */
+ * uploaded header), with fp32 accumulation: B Q on fp32 operands split into
+ * three bf16 terms (six MFMA products, fp32 accuracy: its error is amplified
+ * by the orthogonalization that follows), every other product on two fp16
+ * terms under a power-of-two scale taken from the operand's largest |value|
+ * (three MFMA products, 22 significant bits).  The update is written in
+ * out_dtype by the last product (round to nearest even).  All memory is the
+ * caller's workspace; no handle or other state is kept.  Asynchronous on
+ * `stream`. */
 typedef enum { DION_LOWRANK_QR = 0, DION_LOWRANK_COLNORM = 1 } dion_lowrank_mode;
 
 /* Bytes of workspace for dion_lowrank_step (0 on invalid arguments). */

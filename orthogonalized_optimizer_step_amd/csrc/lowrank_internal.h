@@ -31,15 +31,15 @@ struct LrDesc {
 // Operands of the step's products, each with a slot for its largest |value|,
 // from which the GEMM that reads it takes its fp16 scale.  The producer of
 // an operand raises its slot (atomicMax on the bits of a non-negative float):
-// the accumulation for B (through per-block maxima), a small pass for the
-// incoming Q, the GEMM epilogues for their outputs, the factorization for
-// L^-1.  CholeskyQR3 of
+// the accumulation for B (through per-block maxima), the GEMM epilogues for
+// their outputs, the factorization for L^-1.  (The power product B Q takes
+// unscaled bf16 terms, so the incoming Q needs none.)  CholeskyQR3 of
 // the power product: pass p reads F_{p-1} (F_-1 = Y) and L_p, writes F_p
 // (F_2 = P); of the right factor: pass p reads G_{p-1} (G_-1 = W) and L_{3+p},
 // writes G_p (G_2 = the new Q).  Dion's column normalization bounds the new
 // Q by one: its slot starts at 1.
 enum LrSlot {
-  LS_B, LS_QIN, LS_Y, LS_W,
+  LS_B, LS_Y, LS_W,
   LS_L0, LS_L1, LS_L2, LS_L3, LS_L4, LS_L5,
   LS_F0, LS_F1, LS_F2, LS_G0, LS_G1, LS_G2,
   LS_N
@@ -54,8 +54,7 @@ constexpr int LR_REG_RMAX = 256;
 constexpr int LR_ABSMAX_SPLIT = 16;
 
 // B = fl32(M + G) in place, each block's largest |B| to blockmax (one float
-// per element-wise block); then the LS_B slot from those, and the LS_QIN slot
-// of the incoming right factor
+// per element-wise block); then the LS_B slot from those
 void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, float* blockmax, hipStream_t s);
 void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStream_t s);
 // shift > 0: factor S + shift * (largest diagonal entry of S) * I (the first,

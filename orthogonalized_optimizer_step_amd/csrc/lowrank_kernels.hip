@@ -3,11 +3,11 @@
 // in Dion and QR of the right factor in Orth-Dion).  The rank-r products run
 // in k_lr_gemm (lowrank_gemm.hip); what is here is the rest of the step:
 //   k_lr_accumulate  B = fl32(M + G) in place (the residual buffer)
-//   k_lr_absmax      the largest |value| of B and of the incoming right factor
+//   k_lr_absmax      the largest |value| of B, from k_lr_accumulate's block maxima
 //   k_lr_cholinv     Cholesky factor of an r x r Gram matrix in fp64 and the
 //                    inverse of that factor, for CholeskyQR (A = P L^-T)
 //   k_lr_colnorm     Dion's column normalization of the right factor
-// The first, second and fourth raise the max slots that the GEMMs take their
+// The second and third raise the max slots that the GEMMs take their fp16
 // operand scales from.
 #include <hip/hip_runtime.h>
 
@@ -95,9 +95,7 @@ __global__ __launch_bounds__(256) void k_lr_accumulate(const LrDesc* __restrict_
 }
 
 // Grid (LR_ABSMAX_SPLIT, matrices): block x of matrix i reduces its share of
-// the matrix's block maxima from k_lr_accumulate into the LS_B slot, and its
-// share of the incoming right factor Q (C x r, float4 loads when aligned)
-// into the LS_QIN slot.
+// the matrix's block maxima from k_lr_accumulate into the LS_B slot.
 __global__ __launch_bounds__(256) void k_lr_absmax(const LrDesc* __restrict__ descs,
                                                    const float* __restrict__ blockmax) {
   const LrDesc& d = descs[blockIdx.y];
@@ -106,21 +104,6 @@ __global__ __launch_bounds__(256) void k_lr_absmax(const LrDesc* __restrict__ de
   float mb = 0.f;
   for (int64_t e = (int64_t)part * 256 + tid; e < nb; e += (int64_t)parts * 256) mb = fmaxf(mb, blockmax[d.blk0 + e]);
   lr_raise<256>(d.amax + LS_B, mb);
-  const int64_t n = (int64_t)d.C * d.r;
-  float mq = 0.f;
-  if (((uintptr_t)d.Q & 15) == 0) {
-    const int64_t n4 = n / 4;
-    const float4* q4 = (const float4*)d.Q;
-    for (int64_t e = (int64_t)part * 256 + tid; e < n4; e += (int64_t)parts * 256) {
-      const float4 v = q4[e];
-      mq = fmaxf(mq, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    for (int64_t e = n4 * 4 + part * 256 + tid; e < n; e += (int64_t)parts * 256) mq = fmaxf(mq, fabsf(d.Q[e]));
-  } else {
-    for (int64_t e = (int64_t)part * 256 + tid; e < n; e += (int64_t)parts * 256) mq = fmaxf(mq, fabsf(d.Q[e]));
-  }
-  __syncthreads();   // lr_block_max's LDS is reused
-  lr_raise<256>(d.amax + LS_QIN, mq);
 }
 
 // One block per matrix.  From the Gram S = F^T F (r x r, fp32, symmetric) of

@@ -141,16 +141,16 @@ def llama70b_batch():
     """The Llama-3-70B-shaped stress as configured and as bench.py times it: 16
     matrices each of 8192x8192, 1024x8192, 28672x8192 and 8192x28672 (64 in one
     megabatched call), heavy-tailed spectrum k^-1/2 with random orthogonal
-    factors from seeded QR; K=6, restarts every 2, safety 1.05, top 1/4 of rows."""
+    factors from seeded QR (one pair per shape, each copy with its own order and
+    signs of the spectrum); K=6, restarts every 2, safety 1.05, top 1/4 of rows."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import orthogonalized_optimizer_step_amd as dion
-    from workloads import LLAMA3_70B_SHAPES, heavytail_torch
+    from workloads import LLAMA3_70B_SHAPES, heavytail_copies_torch
     wl = WORKLOADS["llama3_70b"]
     Ms = []
     for si, (r, c) in enumerate(LLAMA3_70B_SHAPES):
-        for cp in range(16):
-            Ms.append(heavytail_torch((5, si, cp), r, c))
+        Ms.extend(heavytail_copies_torch((5, si), r, c, 16))
         torch.cuda.synchronize()
         print(f"llama3_70b: generated 16 of {r}x{c}", flush=True)
     assert [tuple(M.shape) for M in Ms] == list(wl.shapes)

@@ -182,8 +182,13 @@ def lowrank_torch(key, rows, cols, rank, noise, log_scale=None, device="cuda", o
     return M.to(out_dtype or torch.bfloat16)
 
 
-def heavytail_torch(key, rows, cols, exponent=0.5, device="cuda", out_dtype=None):
-    """U diag(k^-exponent) V^T, U and V the Q factors of seeded Gaussians (fp32)."""
+def heavytail_copies_torch(key, rows, cols, copies, exponent=0.5, device="cuda", out_dtype=None):
+    """`copies` matrices U diag(d_c) V^T sharing U and V, the Q factors of
+    seeded Gaussians (fp32): d_c is the spectrum k^-exponent in a seeded
+    random order with random signs, so every copy has the same singular
+    values, assigned to different pairs of singular vectors.  (Two QRs per
+    shape rather than per copy: the QR of a 28672 x 8192 Gaussian takes
+    seconds.)"""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed_of(*key))
@@ -191,8 +196,13 @@ def heavytail_torch(key, rows, cols, exponent=0.5, device="cuda", out_dtype=None
     U, _ = torch.linalg.qr(torch.randn((rows, r), generator=g, device=device, dtype=torch.float32))
     V, _ = torch.linalg.qr(torch.randn((cols, r), generator=g, device=device, dtype=torch.float32))
     s = torch.arange(1, r + 1, device=device, dtype=torch.float32).pow(-exponent)
-    M = (U * s) @ V.t()
-    return M.to(out_dtype or torch.bfloat16)
+    out = []
+    for _ in range(copies):
+        perm = torch.randperm(r, generator=g, device=device)
+        sign = torch.randint(0, 2, (r,), generator=g, device=device).to(torch.float32).mul_(2.0).sub_(1.0)
+        out.append(((U * (s[perm] * sign)) @ V.t()).to(out_dtype or torch.bfloat16))
+    del U, V
+    return out
 
 
 def llama3_8b_torch(step=None, n_layers=32, device="cuda"):
@@ -206,8 +216,8 @@ def llama3_8b_torch(step=None, n_layers=32, device="cuda"):
 
 
 def llama3_70b_torch(copies=16, device="cuda"):
+    """The Llama-3-70B-shaped stress: `copies` heavy-tailed matrices of each shape."""
     mats = []
     for si, (r, c) in enumerate(LLAMA3_70B_SHAPES):
-        for cp in range(copies):
-            mats.append(heavytail_torch((5, si, cp), r, c, device=device))
+        mats.extend(heavytail_copies_torch((5, si), r, c, copies, device=device))
     return mats
