@@ -1679,7 +1679,8 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
     P.off[LP_Y][i] = off;  off = align256(off + 4 * R * r);
     P.off[LP_W][i] = off;  off = align256(off + 4 * C * r);
     P.off[LP_W2][i] = off; off = align256(off + 4 * C * r);
-    P.off[LP_S][i] = off;  off = align256(off + 4 * r * r);
+    const size_t parts = (size_t)std::max((R + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK, (C + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK);
+    P.off[LP_S][i] = off;  off = align256(off + 4 * r * r * parts);
     P.off[LP_L][i] = off;  off = align256(off + 4 * r * r);
     P.off_a64[i] = off;    off = align256(off + 8 * r * r);
     const size_t ldp = (r + 7) / 8 * 8;
@@ -1719,6 +1720,8 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     d.R = P.R[i];
     d.C = P.C[i];
     d.r = P.r[i];
+    d.parts_R = (P.R[i] + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK;
+    d.parts_C = (P.C[i] + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK;
   }
   for (const LrGroup& g : P.groups) {
     float** arr = (float**)(blob.data() + g.ptr_off);
@@ -1843,16 +1846,22 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     const int from[3] = {F, dst, tmp}, to[3] = {dst, tmp, dst};
     for (int pass = 0; pass < 3; ++pass) {
       const int s_from = pass == 0 ? s_in : s_out + pass - 1;
-      for (const LrGroup& g : P.groups) {
+      for (const LrGroup& g : P.groups) {   // S = F^T F, K split: lower tiles of each chunk's partial
         const int rows = rows_are_R ? g.R : g.C;
-        const int e = gprod("lr_orth", g, true, false, true, g.r, g.r, rows, 1.f, from[pass], from[pass], 0.f, LP_S,
-                            s_from, s_from, -1, 1, 4.0 * ((double)rows * g.r + (double)g.r * g.r));
+        const double cnt = (double)g.mats.size(), parts = (rows + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK;
+        const int e = phase("lr_orth", "dion::k_lr_gemm<0, 0, true>", 2.0 * g.r * g.r * rows * cnt,
+                            cnt * 4.0 * ((double)rows * g.r + parts * g.r * g.r), [&]() {
+                              launch_lr_gram(rows, g.r, (const float* const*)arrays(g, from[pass]), arrays(g, LP_S),
+                                             (unsigned* const*)arrays(g, LP_AM), s_from, (int)g.mats.size(), stream);
+                              return DION_OK;
+                            });
         if (e != DION_OK) return e;
       }
       double rr = 0.0;
       for (int i = 0; i < batch; ++i) rr += (double)P.r[i] * P.r[i];
       int e = phase("lr_cholinv", "dion::k_lr_cholinv", 0.0, rr * 8.0, [&]() {
-        launch_lr_cholinv(d_descs, nmat, any_small, any_large, pass == 0 ? kShift : 0.f, s_l + pass, stream);
+        launch_lr_cholinv(d_descs, nmat, any_small, any_large, rows_are_R, pass == 0 ? kShift : 0.f, s_l + pass,
+                          stream);
         return DION_OK;
       });
       if (e != DION_OK) return e;

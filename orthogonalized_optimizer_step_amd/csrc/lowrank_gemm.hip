@@ -215,10 +215,15 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
                                                  int lda, const float* const* __restrict__ Bs, int ldb, float beta,
                                                  void* const* __restrict__ Cs, int ldc,
                                                  unsigned* const* __restrict__ amax, int sa, int sb, int sc,
-                                                 int out_fmt) {
+                                                 int out_fmt, int kchunk, int lower_only) {
   constexpr int NT = F16 ? 2 : 3;
   __shared__ __attribute__((aligned(16))) uint16_t sA[NT * LG_TERM], sB[NT * LG_TERM];
-  const int z = blockIdx.z;
+  // kchunk > 0: K split into chunks, chunk p of product z in block z * parts
+  // + p, its partial result at C + p M N
+  const int parts = kchunk > 0 ? (K + kchunk - 1) / kchunk : 1;
+  const int z = blockIdx.z / parts, part = blockIdx.z - z * parts;
+  const int kbeg = part * kchunk, kend = kchunk > 0 ? min(K, kbeg + kchunk) : K;
+  if (lower_only && blockIdx.x > blockIdx.y) return;   // a tile wholly above the diagonal
   const float* A = As[z];
   const float* B = Bs[z];
   unsigned* slots = amax[z];
@@ -241,14 +246,14 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
 
   LgStage<A_MODE, F16> ga;
   LgStage<B_MODE, F16> gb;
-  const int nk = (K + LG_BK - 1) / LG_BK;
+  const int nk = (kend - kbeg + LG_BK - 1) / LG_BK;
   auto load = [&](int k0) {
     if constexpr (A_MODE == LG_PRE) ga.load((const uint16_t*)A, lda, M, M * lda, m0, k0);
-    else ga.load(A, lda, M, K, m0, k0, veca);
+    else ga.load(A, lda, M, kend, m0, k0, veca);
     if constexpr (B_MODE == LG_PRE) gb.load((const uint16_t*)B, ldb, N, N * ldb, n0, k0);
-    else gb.load(B, ldb, N, K, n0, k0, vecb);
+    else gb.load(B, ldb, N, kend, n0, k0, vecb);
   };
-  load(0);
+  load(kbeg);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();   // every wave is done with the previous stage
     if constexpr (A_MODE == LG_PRE) ga.store(sA);
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
     if constexpr (B_MODE == LG_PRE) gb.store(sB);
     else gb.store(sB, scale_b);
     __syncthreads();
-    if (kt + 1 < nk) load((kt + 1) * LG_BK);   // the next stage's loads fly while this one is multiplied
+    if (kt + 1 < nk) load(kbeg + (kt + 1) * LG_BK);   // the next stage's loads fly while this one is multiplied
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int chunk = kk * 2 + (lane >> 5);
@@ -306,14 +311,14 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = rbase + (e >> 2) * 8 + (e & 3);
-          cv[e] = (col < N && row < M) ? ((const float*)Cs[z])[(size_t)row * ldc + col] : 0.f;
+          cv[e] = (col < N && row < M) ? ((const float*)Cs[z])[(size_t)part * M * N + (size_t)row * ldc + col] : 0.f;
         }
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = rbase + (e >> 2) * 8 + (e & 3);
         if (col < N && row < M) {
-          const size_t o = (size_t)row * ldc + col;
+          const size_t o = (size_t)part * M * N + (size_t)row * ldc + col;
           float v = alpha * ldexpf(acc[a][b][e], -lab);
           if (out_fmt == 1) {
             if (beta != 0.f) v = v + beta * cv[e];
@@ -345,7 +350,7 @@ void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
 #define DION_LRG(AK, BK, F)                                                                                          \
   hipLaunchKernelGGL((k_lr_gemm<AK, BK, F>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,   \
-                     amax, sa, sb, sc, out_fmt)
+                     amax, sa, sb, sc, out_fmt, 0, 0)
   if (f16) {
     if (!ta && tb) DION_LRG(LG_KC, LG_KC, true);
     else if (!ta && !tb) DION_LRG(LG_KC, LG_RC, true);
@@ -365,7 +370,16 @@ void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint1
                           int count, hipStream_t s) {
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
   hipLaunchKernelGGL((k_lr_gemm<LG_PRE, LG_PRE, true>), grid, dim3(256), 0, s, m, n, k, alpha,
-                     (const float* const*)A, ldp, (const float* const*)B, ldp, beta, C, n, amax, sa, sb, sc, out_fmt);
+                     (const float* const*)A, ldp, (const float* const*)B, ldp, beta, C, n, amax, sa, sb, sc, out_fmt, 0,
+                     0);
+}
+
+void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, unsigned* const* amax, int sf, int count,
+                    hipStream_t s) {
+  const int parts = (rows + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK;
+  const dim3 grid((r + LG_TILE - 1) / LG_TILE, (r + LG_TILE - 1) / LG_TILE, count * parts);
+  hipLaunchKernelGGL((k_lr_gemm<LG_RC, LG_RC, true>), grid, dim3(256), 0, s, r, r, rows, 1.f, F, r, F, r, 0.f,
+                     (void* const*)S, r, amax, sf, sf, -1, 1, LR_GRAM_CHUNK, 1);
 }
 
 // Split a batch of row-major fp32 matrices (rows x k) into fp16 hi and lo

@@ -17,7 +17,8 @@ struct LrDesc {
   float* Y;          // R x r  B Q, then a CholeskyQR intermediate
   float* W;          // C x r  right factor before normalization
   float* W2;         // C x r  CholeskyQR intermediate of W
-  float* S;          // r x r  Gram of the factor being orthogonalized
+  float* S;          // r x r  Gram of the factor being orthogonalized, as
+                     // parts_R or parts_C partial sums (r x r each, K split)
   float* Linv;       // r x r  inverse of its Cholesky factor (lower)
   double* A64;       // r x r  fp64 scratch of the factorization
   unsigned* amax;    // LS_N slots: the largest |value| of each operand the
@@ -25,6 +26,7 @@ struct LrDesc {
   int64_t elems;     // R * C
   int64_t blk0;      // first block of this matrix in the element-wise launches
   int R, C, r;
+  int parts_R, parts_C;   // K chunks of the Gram of an R x r / C x r factor
   int pad_;
 };
 
@@ -52,16 +54,19 @@ constexpr int LR_REG_RMAX = 256;
 
 // blocks per matrix of k_lr_absmax
 constexpr int LR_ABSMAX_SPLIT = 16;
+// rows of the factor per K chunk of a CholeskyQR Gram product
+constexpr int LR_GRAM_CHUNK = 1024;
 
 // B = fl32(M + G) in place, each block's largest |B| to blockmax (one float
 // per element-wise block); then the LS_B slot from those
 void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, float* blockmax, hipStream_t s);
 void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStream_t s);
-// shift > 0: factor S + shift * (largest diagonal entry of S) * I (the first,
-// shifted pass of shifted CholeskyQR3); the largest |entry| of L^-1 raises
-// slot `amax_slot`
-void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, int amax_slot,
-                       hipStream_t s);
+// S is the sum of the parts_R (rows_are_R) or parts_C partial Grams, added
+// in order; shift > 0: factor S + shift * (largest diagonal entry of S) * I
+// (the first, shifted pass of shifted CholeskyQR3); the largest |entry| of
+// L^-1 raises slot `amax_slot`
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, bool rows_are_R, float shift,
+                       int amax_slot, hipStream_t s);
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
 // Row-major C (m x n) = alpha op(A) op(B) + beta C over `count` products
 // (device pointer arrays; amax: each product's matrix's LS_N slots), on
@@ -77,6 +82,12 @@ void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha
 void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint16_t* const* A, const uint16_t* const* B,
                           float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc, int out_fmt,
                           int count, hipStream_t s);
+// The Gram F^T F of `count` row-major fp32 factors F (rows x r, F16 terms
+// with the scale of slot sf): the rows split into chunks of LR_GRAM_CHUNK,
+// chunk p's r x r partial written at S + p r r (only the tiles on or below
+// the diagonal, all that the factorization reads).
+void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, unsigned* const* amax, int sf,
+                    int count, hipStream_t s);
 // Split `count` row-major fp32 matrices (rows x k) with the scale of slot
 // `slot` into fp16 hi and lo rows of length ldp = k rounded up to 8 (zeros
 // beyond k; lo after hi): rows * ldp * 4 bytes at each dst.

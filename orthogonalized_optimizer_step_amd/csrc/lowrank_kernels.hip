@@ -106,7 +106,16 @@ __global__ __launch_bounds__(256) void k_lr_absmax(const LrDesc* __restrict__ de
   lr_raise<256>(d.amax + LS_B, mb);
 }
 
-// One block per matrix.  From the Gram S = F^T F (r x r, fp32, symmetric) of
+// S[e], the sum of the partial Grams of the K chunks, added in order in fp64
+__device__ __forceinline__ double lr_gram_at(const LrDesc& d, int parts, size_t e) {
+  const size_t rr = (size_t)d.r * d.r;
+  double v = 0.0;
+  for (int p = 0; p < parts; ++p) v += (double)d.S[p * rr + e];
+  return v;
+}
+
+// One block per matrix.  From the Gram S = F^T F (r x r, fp32 partial sums
+// of its K chunks, symmetric; only the lower triangle is read) of
 // the factor F being orthogonalized: the lower Cholesky factor L of S, in
 // fp64, then Linv = L^-1 (fp32, lower; zero above the diagonal), so that
 // F L^-T has orthonormal columns (CholeskyQR; the triangular factor L^T has
@@ -117,8 +126,10 @@ __global__ __launch_bounds__(256) void k_lr_absmax(const LrDesc* __restrict__ de
 // contract): its column of L^-1 and of the result is zero, which keeps every
 // value finite.  The inverse is column-wise forward substitution, one column
 // per thread, X = L^-1 kept transposed in the upper triangle of the scratch.
-__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, float shift, int amax_slot) {
+__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, int rows_are_R, float shift,
+                                                    int amax_slot) {
   const LrDesc& d = descs[blockIdx.x];
+  const int parts = rows_are_R ? d.parts_R : d.parts_C;
   const int r = d.r;
   if (r <= LR_REG_RMAX) return;   // k_lr_cholinv_reg
   const int tid = threadIdx.x;
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ d
   double mx = 0.0;
   for (int e = tid; e < r * r; e += 256) {
     const int i = e / r, j = e - (e / r) * r;
-    const double v = j <= i ? (double)d.S[e] : 0.0;
+    const double v = j <= i ? lr_gram_at(d, parts, e) : 0.0;
     A[e] = v;
     if (i == j) mx = fmax(mx, v);
   }
@@ -207,9 +218,10 @@ constexpr int LR_NB = LR_REG_RMAX / LR_GRID;
 constexpr int LR_SLOTS = LR_NB * (LR_NB + 1) / 2;
 static_assert(LR_GRID * LR_GRID == LR_REG_THREADS, "thread grid");
 
-__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, float shift,
-                                                          int amax_slot) {
+__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, int rows_are_R,
+                                                          float shift, int amax_slot) {
   const LrDesc& d = descs[blockIdx.x];
+  const int parts = rows_are_R ? d.parts_R : d.parts_C;
   const int r = d.r;
   if (r > LR_REG_RMAX) return;    // k_lr_cholinv
   const int tid = threadIdx.x;
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
   }
   double mx = 0.0;
   LR_FOR_SLOTS({
-    v[sl] = own ? (double)d.S[(size_t)i * r + c] : 0.0;
+    v[sl] = own ? lr_gram_at(d, parts, (size_t)i * r + c) : 0.0;
     if (own && i == c) mx = fmax(mx, v[sl]);
   })
   for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
@@ -319,11 +331,12 @@ void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fm
 void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStream_t s) {
   if (nmat > 0) hipLaunchKernelGGL(k_lr_absmax, dim3(LR_ABSMAX_SPLIT, nmat), dim3(256), 0, s, d, blockmax);
 }
-void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, float shift, int amax_slot,
-                       hipStream_t s) {
+void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, bool rows_are_R, float shift,
+                       int amax_slot, hipStream_t s) {
+  const int rr = rows_are_R ? 1 : 0;
   if (nmat > 0 && any_small)
-    hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, shift, amax_slot);
-  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, shift, amax_slot);
+    hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, rr, shift, amax_slot);
+  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, rr, shift, amax_slot);
 }
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s) {
   if (nmat > 0) hipLaunchKernelGGL(k_lr_colnorm, dim3(nmat), dim3(256), 0, s, d);
