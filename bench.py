@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--summarize", metavar="DIR",
                     help="print a text summary of the rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--copy-ceiling", action="store_true",
-                    help="time plain device-to-device copies of 1, 4 and 16 GiB (the rate a streaming pass "
+                    help="time passes that read and write 1, 4 and 16 GiB once (runtime copy, elementwise kernel; the rate a streaming pass "
                          "that reads and writes each byte once can reach) and exit")
     ap.add_argument("--profile", action="store_true",
                     help="only run warmup + steps (for rocprofv3), no baseline; also runs one plain 1 GiB "
@@ -387,29 +387,32 @@ def bench_lowrank(args, torch, dion):
 
 
 def copy_ceiling(torch, reps=10):
-    """HBM rate of a plain device copy (the runtime's copy kernel), counting
-    the bytes read and written: the ceiling for a pass that moves each byte
-    once.  One JSON line per size, the median of `reps` timed copies."""
-    for gib in (1, 4, 16):
-        n = (gib << 30) // 4
-        src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        times = []
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            dst.copy_(src)
-            b.record()
-            b.synchronize()
-            times.append(a.elapsed_time(b))
-        times.sort()
-        ms = times[len(times) // 2]
-        print(json.dumps({"copy_ceiling": {"gib": gib, "bytes_moved": 2 * (gib << 30), "ms": ms,
-                                           "gbs": 2 * (gib << 30) / ms / 1e6, "min_ms": times[0]}}), flush=True)
-        del src, dst
-        torch.cuda.empty_cache()
+    """HBM rate of a pass that reads and writes each byte once, counting both:
+    the runtime's device copy (torch copy_, a hipMemcpy kernel) and PyTorch's
+    vectorized elementwise kernel (dst = src * 1).  One JSON line per kind
+    and size, the median of `reps` timed passes."""
+    for kind in ("copy", "elementwise"):
+        for gib in (1, 4, 16):
+            n = (gib << 30) // 4
+            src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+            dst = torch.empty_like(src)
+            op = (lambda: dst.copy_(src)) if kind == "copy" else (lambda: torch.mul(src, 1.0, out=dst))
+            for _ in range(2):
+                op()
+            times = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                op()
+                b.record()
+                b.synchronize()
+                times.append(a.elapsed_time(b))
+            times.sort()
+            ms = times[len(times) // 2]
+            print(json.dumps({"copy_ceiling": {"kind": kind, "gib": gib, "bytes_moved": 2 * (gib << 30), "ms": ms,
+                                               "gbs": 2 * (gib << 30) / ms / 1e6, "min_ms": times[0]}}), flush=True)
+            del src, dst
+            torch.cuda.empty_cache()
 
 
 def main():
