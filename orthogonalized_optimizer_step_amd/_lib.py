@@ -62,7 +62,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m orthogonalized_optimizer_step_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python orthogonalized_optimizer_step_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
     pp = ctypes.POINTER(ctypes.c_void_p)

@@ -1,6 +1,8 @@
 """Builds the HIP library in-tree: orthogonalized_optimizer_step_amd/libdion.so (gfx950).
 
-    python -m orthogonalized_optimizer_step_amd.build
+    python orthogonalized_optimizer_step_amd/build.py
+
+(run as a script: importing the package needs the library it builds)
 
 Every source is compiled with hipcc for gfx950 only.  The momentum kernel's
 two fp32 roundings rely on explicit round-to-nearest intrinsics; the
