@@ -345,9 +345,10 @@ def bench_lowrank(args, torch, dion):
     avg_ms = d["ms"] / d["launches"]
     useful_rate = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
     # the products are fp32 GEMMs computed on 16-bit matrix cores: two fp16
-    # terms per operand (three MFMA products; template flag true) or three
-    # bf16 terms (six): priced as the MFMA work they execute
-    terms = 3 if dom.endswith("true>") else 6
+    # terms per operand (three MFMA products) or, for the instances whose
+    # template flag is false, three bf16 terms (six): priced as the MFMA work
+    # they execute
+    terms = 6 if dom.endswith("false>") else 3
     achieved = useful_rate * terms
     useful = sum(v["useful"] for v in phases.values()) / args.steps
     params = sum(r * c for r, c in shapes)

@@ -1683,10 +1683,10 @@ int build_lr_plan(const dion_shape* shapes, int batch, int rank, int out_dtype, 
     P.off[LP_S][i] = off;  off = align256(off + 4 * r * r * parts);
     P.off[LP_L][i] = off;  off = align256(off + 4 * r * r);
     P.off_a64[i] = off;    off = align256(off + 8 * r * r);
-    const size_t ldp = (r + 7) / 8 * 8;
-    P.off[LP_XS][i] = off; off = align256(off + 4 * R * ldp);
-    P.off[LP_WS][i] = off; off = align256(off + 4 * C * ldp);
-    P.off[LP_QS][i] = off; off = align256(off + 4 * C * ldp);
+    const size_t ldp = (r + 31) / 32 * 32, Rp = (R + 127) / 128 * 128, Cp = (C + 127) / 128 * 128;
+    P.off[LP_XS][i] = off; off = align256(off + 4 * Rp * ldp);
+    P.off[LP_WS][i] = off; off = align256(off + 4 * Cp * ldp);
+    P.off[LP_QS][i] = off; off = align256(off + 4 * Cp * ldp);
   }
   P.total = off;
   return DION_OK;
@@ -1795,23 +1795,25 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     });
   };
 
-  // split copies of a group's rows x r operand (fp16 hi and lo, rows padded to ldp)
+  // split copies of a group's rows x r operand (fp16 hi and lo rows of ldp =
+  // r rounded up to 32, rows padded to a multiple of 128)
+  auto pad128 = [](int x) { return (x + 127) / 128 * 128; };
   auto gsplit = [&](const LrGroup& g, int src, int dst, int rows, int slot) -> int {
-    const int ldp = (g.r + 7) / 8 * 8;
+    const int ldp = (g.r + 31) / 32 * 32;
     const double cnt = (double)g.mats.size();
-    return phase("lr_split", "dion::k_lr_split16", 0.0, cnt * rows * (4.0 * g.r + 4.0 * ldp), [&]() {
-      launch_lr_split16((const float* const*)arrays(g, src), (uint16_t* const*)arrays(g, dst), rows, g.r, ldp,
-                        (unsigned* const*)arrays(g, LP_AM), slot, (int)g.mats.size(), stream);
+    return phase("lr_split", "dion::k_lr_split16", 0.0, cnt * (4.0 * rows * g.r + 4.0 * pad128(rows) * ldp), [&]() {
+      launch_lr_split16((const float* const*)arrays(g, src), (uint16_t* const*)arrays(g, dst), rows, pad128(rows), g.r,
+                        ldp, (unsigned* const*)arrays(g, LP_AM), slot, (int)g.mats.size(), stream);
       return DION_OK;
     });
   };
   // C (R x C) = alpha P Z^T + beta C from the split P and Z (C x r), inner dimension r
   auto gprod_split = [&](const char* name, const LrGroup& g, float alpha, int Z, float beta_, int Cm, int sz,
                          int out_fmt, double bytes_each) -> int {
-    const int ldp = (g.r + 7) / 8 * 8;
+    const int ldp = (g.r + 31) / 32 * 32;
     const double cnt = (double)g.mats.size();
-    return phase(name, "dion::k_lr_gemm<2, 2, true>", 2.0 * g.R * g.C * g.r * cnt, bytes_each * cnt, [&]() {
-      launch_lr_gemm_split(g.R, g.C, g.r, ldp, alpha, (const uint16_t* const*)arrays(g, LP_XS),
+    return phase(name, "dion::k_lr_gemm_dma", 2.0 * g.R * g.C * g.r * cnt, bytes_each * cnt, [&]() {
+      launch_lr_gemm_split(g.R, g.C, g.r, ldp, pad128(g.R), pad128(g.C), alpha, (const uint16_t* const*)arrays(g, LP_XS),
                            (const uint16_t* const*)arrays(g, Z), beta_, (void* const*)arrays(g, Cm),
                            (unsigned* const*)arrays(g, LP_AM), LS_F2, sz, -1, out_fmt, (int)g.mats.size(), stream);
       return DION_OK;

@@ -31,10 +31,12 @@
 //
 // A small F16 operand read by many blocks (P, W and the new Q in the buffer
 // update and the update, whose inner dimension is the rank) is split once by
-// k_lr_split16 into hi and lo arrays of fp16 rows (K contiguous, padded to a
-// multiple of 8 with zeros), and the GEMM copies its terms to LDS as they
-// are: the split of a 128-row operand tile would otherwise be repeated by
-// every block of the other dimension.
+// k_lr_split16 into hi and lo arrays of fp16 rows (K contiguous; rows padded
+// to a multiple of 128 and K to a multiple of 32, with zeros), and those two
+// products run in k_lr_gemm_dma: its stages go from global memory straight
+// into LDS (global_load_lds_dwordx4, each lane's 16 bytes placed where the
+// swizzled layout wants them) one stage ahead, with no register staging and
+// no split in the kernel.
 //
 // Tiles of 128 x 128 outputs, four waves of 64 x 64 (2 x 2 MFMA blocks).  A
 // K-stage of 32 columns is loaded from global memory into registers (16-byte
@@ -94,9 +96,8 @@ __device__ __forceinline__ void lg_split(float x, float s, uint32_t* t) {
   }
 }
 
-// operand layouts: fp32 with r (the M or N index) contiguous, fp32 with k
-// contiguous, or split ahead into fp16 hi and lo rows with k contiguous
-enum { LG_RC = 0, LG_KC = 1, LG_PRE = 2 };
+// operand layouts: fp32 with r (the M or N index) contiguous, or with k contiguous
+enum { LG_RC = 0, LG_KC = 1 };
 
 // A K-stage of one operand: LG_TILE rows (of op(X)'s M or N side) x LG_BK k,
 // 16 values per thread.  KC: stored with k contiguous (element (r, k) at
@@ -134,7 +135,6 @@ struct LgStage {
   }
   // (scale,) split and store to the NT term arrays at s
   __device__ __forceinline__ void store(uint16_t* s, float scale) const {
-    static_assert(MODE != LG_PRE, "split operands have their own stage");
     const int t = threadIdx.x;
     if (KC) {
       const int r = t >> 1, c0 = (t & 1) * 2;   // chunks c0, c0 + 1
@@ -169,34 +169,6 @@ struct LgStage {
   }
 };
 
-// A K-stage of a split operand: hi rows at p, lo rows at p + term (fp16,
-// row length ld, a multiple of 8, zero beyond the operand's K); thread t
-// copies chunks (t&1)*2 and +1 of row t/2 of both terms, 16 bytes each.
-template <>
-struct LgStage<LG_PRE, true> {
-  uint4 v[4];
-  __device__ __forceinline__ void load(const uint16_t* p, int ld, int rows, int term, int r0, int k0) {
-    const int t = threadIdx.x;
-    const int r = r0 + (t >> 1), k = k0 + (t & 1) * 16;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int kc = k + 8 * c;
-        v[2 * u + c] = (r < rows && kc < ld) ? *(const uint4*)(p + (size_t)u * term + (size_t)r * ld + kc)
-                                              : make_uint4(0u, 0u, 0u, 0u);
-      }
-  }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    const int t = threadIdx.x;
-    const int r = t >> 1, c0 = (t & 1) * 2;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) *(uint4*)(s + u * LG_TERM + lg_off(r, c0 + c)) = v[2 * u + c];
-  }
-};
-
 __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -205,11 +177,62 @@ __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
 
 }  // namespace
 
+// The epilogue of a 128 x 128 tile held by four waves of 64 x 64 (2 x 2 MFMA
+// blocks, lane = column (lane & 31) of rows (e/4)*8 + (lane/32)*4 + e%4 of
+// each block): C = alpha 2^-lab acc (+ beta C), written as out_fmt; with
+// slot >= 0, the block's largest |value| raises *slot.  Every thread calls.
+__device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab, float alpha,
+                                            float beta, void* Cp, int ldc, size_t coff, int out_fmt, unsigned* slot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  float mx = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = n0 + wn * 64 + b * 32 + (lane & 31);
+      const int rbase = m0 + wm * 64 + a * 32 + (lane >> 5) * 4;
+      float cv[16];
+      if (out_fmt == 1 && beta != 0.f) {   // every read of C before any write: 16 loads in flight
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + (e >> 2) * 8 + (e & 3);
+          cv[e] = (col < N && row < M) ? ((const float*)Cp)[coff + (size_t)row * ldc + col] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = rbase + (e >> 2) * 8 + (e & 3);
+        if (col < N && row < M) {
+          const size_t o = coff + (size_t)row * ldc + col;
+          float v = alpha * ldexpf(acc[a][b][e], -lab);
+          if (out_fmt == 1) {
+            if (beta != 0.f) v = v + beta * cv[e];
+            ((float*)Cp)[o] = v;
+          } else {
+            ((uint16_t*)Cp)[o] = out_fmt == 0 ? lg_bf16_rne(v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+          }
+          mx = fmaxf(mx, fabsf(v));
+        }
+      }
+    }
+  if (slot) {   // one atomic per block
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    if (tid == 0) {
+      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (m > 0.f) atomicMax(slot, __float_as_uint(m));
+    }
+  }
+}
+
 // Row-major C (M x N) = alpha op(A) op(B) + beta C for batch entry z =
 // blockIdx.z.  A_MODE LG_KC: A is stored M x K (K contiguous, op = N); LG_RC:
-// K x M (op = T); LG_PRE: split fp16 rows M x K (ld = the padded row).
-// B_MODE LG_KC: B is stored N x K (op = T); LG_RC: K x N (op = N); LG_PRE:
-// split fp16 rows N x K.
+// K x M (op = T).  B_MODE LG_KC: B is stored N x K (op = T); LG_RC: K x N
+// (op = N).
 template <int A_MODE, int B_MODE, bool F16>
 __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alpha, const float* const* __restrict__ As,
                                                  int lda, const float* const* __restrict__ Bs, int ldb, float beta,
@@ -234,7 +257,6 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
   const int wm = wave >> 1, wn = wave & 1;
   const bool veca = (lda & 3) == 0 && ((uintptr_t)A & 15) == 0;
   const bool vecb = (ldb & 3) == 0 && ((uintptr_t)B & 15) == 0;
-  static_assert(F16 || (A_MODE != LG_PRE && B_MODE != LG_PRE), "split operands are fp16");
 
   floatx16 acc[2][2];
 #pragma unroll
@@ -248,18 +270,14 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
   LgStage<B_MODE, F16> gb;
   const int nk = (kend - kbeg + LG_BK - 1) / LG_BK;
   auto load = [&](int k0) {
-    if constexpr (A_MODE == LG_PRE) ga.load((const uint16_t*)A, lda, M, M * lda, m0, k0);
-    else ga.load(A, lda, M, kend, m0, k0, veca);
-    if constexpr (B_MODE == LG_PRE) gb.load((const uint16_t*)B, ldb, N, N * ldb, n0, k0);
-    else gb.load(B, ldb, N, kend, n0, k0, vecb);
+    ga.load(A, lda, M, kend, m0, k0, veca);
+    gb.load(B, ldb, N, kend, n0, k0, vecb);
   };
   load(kbeg);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();   // every wave is done with the previous stage
-    if constexpr (A_MODE == LG_PRE) ga.store(sA);
-    else ga.store(sA, scale_a);
-    if constexpr (B_MODE == LG_PRE) gb.store(sB);
-    else gb.store(sB, scale_b);
+    ga.store(sA, scale_a);
+    gb.store(sB, scale_b);
     __syncthreads();
     if (kt + 1 < nk) load(kbeg + (kt + 1) * LG_BK);   // the next stage's loads fly while this one is multiplied
 #pragma unroll
@@ -297,50 +315,8 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
           }
     }
   }
-  // epilogue: lane holds column (lane & 31) of rows (e/4)*8 + (lane/32)*4 + e%4 of each block
-  const int lab = la + lb;
-  float mx = 0.f;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int col = n0 + wn * 64 + b * 32 + (lane & 31);
-      const int rbase = m0 + wm * 64 + a * 32 + (lane >> 5) * 4;
-      float cv[16];
-      if (out_fmt == 1 && beta != 0.f) {   // every read of C before any write: 16 loads in flight
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + (e >> 2) * 8 + (e & 3);
-          cv[e] = (col < N && row < M) ? ((const float*)Cs[z])[(size_t)part * M * N + (size_t)row * ldc + col] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = rbase + (e >> 2) * 8 + (e & 3);
-        if (col < N && row < M) {
-          const size_t o = (size_t)part * M * N + (size_t)row * ldc + col;
-          float v = alpha * ldexpf(acc[a][b][e], -lab);
-          if (out_fmt == 1) {
-            if (beta != 0.f) v = v + beta * cv[e];
-            ((float*)Cs[z])[o] = v;
-          } else {
-            ((uint16_t*)Cs[z])[o] = out_fmt == 0 ? lg_bf16_rne(v) : __builtin_bit_cast(uint16_t, (_Float16)v);
-          }
-          mx = fmaxf(mx, fabsf(v));
-        }
-      }
-    }
-  if (sc >= 0) {   // the result's largest |value| for the products that read it: one atomic per block
-    __shared__ float red[4];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    if (tid == 0) {
-      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      if (m > 0.f) atomicMax(slots + sc, __float_as_uint(m));
-    }
-  }
+  lg_epilogue(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], ldc, (size_t)part * M * N, out_fmt,
+              sc >= 0 ? slots + sc : nullptr);
 }
 
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
@@ -365,13 +341,149 @@ void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha
 #undef DION_LRG
 }
 
-void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint16_t* const* A, const uint16_t* const* B,
-                          float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc, int out_fmt,
-                          int count, hipStream_t s) {
+// ------------------------------------------------ split operands, LDS DMA
+// One 16-byte copy per lane from global memory straight into LDS: lane l's
+// bytes land at M0 + 16 l.  Completion is tracked by vmcnt, waited for
+// explicitly below (the instruction has no register result).
+__device__ __forceinline__ void lg_dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void lg_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// a barrier without __syncthreads' wait for every outstanding copy; the
+// wave's own LDS reads are waited for first
+__device__ __forceinline__ void lg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+__device__ __forceinline__ const void* lg_sgpr(const void* p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// Stages in LDS: two, so that two blocks share a CU (64 KB each).  Products
+// with inner dimension r = 256 have eight stages per tile, and a tile's
+// prologue and its store-bound epilogue stay exposed unless another block
+// runs beside it: four or three stages at one block per CU measured slower
+// (31.5 against 24.3 ms for the buffer update) than the register-staged
+// kernel, two stages at two blocks faster (22.1 ms).
+constexpr int LD_STAGES = 2;
+constexpr int LD_STAGE = 4 * LG_TERM * 2;     // bytes: A hi, A lo, B hi, B lo (8 KB each)
+constexpr int LD_COPIES = LD_STAGE / 1024 / 4;   // 1 KB copies per wave per stage (8)
+
+// C (M x N, row-major, ld N) = alpha A B^T (+ beta C) for product z =
+// blockIdx.z, with A (M x K) and B (N x K) split ahead: fp16 hi rows at
+// A[z], lo rows rows_a * ldp further on, row length ldp (a multiple of 32),
+// rows padded to rows_a (a multiple of 128); zeros in the padding.  Scales
+// from slots sa, sb (as k_lr_gemm's F16 operands); sc >= 0 raises slot sc.
+// A stage (32 k) of the 128 x 128 tile is 32 KB: four 8 KB term arrays of
+// 128 rows x 64 bytes in the swizzled row layout the fragments read.  Each
+// wave copies eight 1 KB pieces of it: piece q = 4 i + wave (i < 8) holds
+// term q / 8 and rows 16 (q % 8) .. +15, lane l row 16 (q % 8) + l / 4 and
+// the chunk whose swizzled position is l % 4.
+__global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int ldp, int rows_a, int rows_b,
+                                                        float alpha, const uint16_t* const* __restrict__ As,
+                                                        const uint16_t* const* __restrict__ Bs, float beta,
+                                                        void* const* __restrict__ Cs, unsigned* const* __restrict__ amax,
+                                                        int sa, int sb, int sc, int out_fmt) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[LD_STAGES * LD_STAGE / 2];
+  const int z = blockIdx.z;
+  unsigned* slots = amax[z];
+  const int la = lg_log2_scale(slots[sa]), lb = lg_log2_scale(slots[sb]);
+  const int m0 = blockIdx.y * LG_TILE, n0 = blockIdx.x * LG_TILE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+
+  // per-lane byte offsets (k = 0) of the eight pieces; the stage's k0 moves the scalar base
+  const char* baseA = (const char*)As[z];
+  const char* baseB = (const char*)Bs[z];
+  uint32_t voff[LD_COPIES];
+#pragma unroll
+  for (int i = 0; i < LD_COPIES; ++i) {
+    const int q = 4 * i + wave, term = q / 8;
+    const int row = 16 * (q % 8) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int r0 = term < 2 ? m0 : n0;
+    const size_t tstride = (size_t)(term < 2 ? rows_a : rows_b) * ldp;
+    voff[i] = (uint32_t)((((size_t)(term & 1) * tstride) + (size_t)(r0 + row) * ldp + 8 * c) * 2);
+  }
+  auto issue = [&](int kt) {   // the copies of stage kt into buffer kt % LD_STAGES
+    const uint32_t st = lds0 + (uint32_t)((kt % LD_STAGES) * LD_STAGE);
+#pragma unroll
+    for (int i = 0; i < LD_COPIES; ++i) {
+      const int q = 4 * i + wave;
+      const char* b = (q / 8 < 2 ? baseA : baseB) + (size_t)kt * LG_BK * 2;
+      lg_dma16(voff[i], lg_sgpr(b), (uint32_t)__builtin_amdgcn_readfirstlane(st + q * 1024));
+    }
+  };
+
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  const int nk = K / LG_BK;   // K = ldp, a multiple of 32
+#pragma unroll
+  for (int kt = 0; kt < LD_STAGES - 1; ++kt)
+    if (kt < nk) issue(kt);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most the later stages already issued are outstanding
+    const int later = min(nk, kt + LD_STAGES - 1) - kt - 1;
+    if (later >= 2) lg_wait_vmcnt<2 * LD_COPIES>();
+    else if (later == 1) lg_wait_vmcnt<LD_COPIES>();
+    else lg_wait_vmcnt<0>();
+    lg_barrier();   // every wave's copies of stage kt have landed, and every wave is done with stage kt - 1
+    if (kt + LD_STAGES - 1 < nk) issue(kt + LD_STAGES - 1);   // into stage kt - 1's buffer
+    const uint16_t* sbuf = smem + (kt % LD_STAGES) * (LD_STAGE / 2);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int chunk = kk * 2 + (lane >> 5);
+      halfx8 fa[2][2], fb[2][2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int ra = wm * 64 + f * 32 + (lane & 31), rb = wn * 64 + f * 32 + (lane & 31);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          fa[u][f] = *(const halfx8*)(sbuf + u * LG_TERM + lg_off(ra, chunk));
+          fb[u][f] = *(const halfx8*)(sbuf + (2 + u) * LG_TERM + lg_off(rb, chunk));
+        }
+      }
+      // hl, lh, then hh
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0][a], fb[1][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1][a], fb[0][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0][a], fb[0][b], acc[a][b], 0, 0, 0);
+    }
+  }
+  lg_epilogue(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], N, 0, out_fmt, sc >= 0 ? slots + sc : nullptr);
+}
+
+void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
+                          const uint16_t* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb,
+                          int sc, int out_fmt, int count, hipStream_t s) {
+  (void)k;
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
-  hipLaunchKernelGGL((k_lr_gemm<LG_PRE, LG_PRE, true>), grid, dim3(256), 0, s, m, n, k, alpha,
-                     (const float* const*)A, ldp, (const float* const*)B, ldp, beta, C, n, amax, sa, sb, sc, out_fmt, 0,
-                     0);
+  hipLaunchKernelGGL(k_lr_gemm_dma, grid, dim3(256), 0, s, m, n, ldp, ldp, rows_a, rows_b, alpha, A, B, beta, C, amax,
+                     sa, sb, sc, out_fmt);
 }
 
 void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, unsigned* const* amax, int sf, int count,
@@ -383,21 +495,25 @@ void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, uns
 }
 
 // Split a batch of row-major fp32 matrices (rows x k) into fp16 hi and lo
-// rows of length ldp (k rounded up to 8, zeros beyond k) at dst (lo after
-// hi), with the scale that slot `slot` gives: the F16 operand format above.
-// Grid (blocks over rows * ldp / 8, count), 8 values per thread.
+// rows of length ldp (k rounded up to 32) at dst, rows padded to rows_pad (a
+// multiple of 128), zeros in the padding, lo rows_pad * ldp after hi; with
+// the scale that slot `slot` gives: the F16 operand format above.  Grid
+// (blocks over rows_pad * ldp / 8, count), 8 values per thread.
 __global__ __launch_bounds__(256) void k_lr_split16(const float* const* __restrict__ src, uint16_t* const* __restrict__ dst,
-                                                    int rows, int k, int ldp, unsigned* const* __restrict__ amax,
-                                                    int slot) {
+                                                    int rows, int rows_pad, int k, int ldp,
+                                                    unsigned* const* __restrict__ amax, int slot) {
   const int z = blockIdx.y;
   const int64_t e8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int cpr = ldp / 8;
-  if (e8 >= (int64_t)rows * cpr) return;
+  if (e8 >= (int64_t)rows_pad * cpr) return;
   const int r = (int)(e8 / cpr), k0 = (int)(e8 - (int64_t)r * cpr) * 8;
   const float scale = ldexpf(1.f, lg_log2_scale(amax[z][slot]));
   const float* p = src[z] + (size_t)r * k + k0;
   float v[8];
-  if (k0 + 8 <= k && (k & 3) == 0 && ((uintptr_t)src[z] & 15) == 0) {
+  if (r >= rows) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  } else if (k0 + 8 <= k && (k & 3) == 0 && ((uintptr_t)src[z] & 15) == 0) {
     *(float4*)&v[0] = *(const float4*)p;
     *(float4*)&v[4] = *(const float4*)(p + 4);
   } else {
@@ -415,15 +531,15 @@ __global__ __launch_bounds__(256) void k_lr_split16(const float* const* __restri
   }
   uint16_t* d = dst[z] + (size_t)r * ldp + k0;
   *(uint4*)d = make_uint4(h[0], h[1], h[2], h[3]);
-  *(uint4*)(d + (size_t)rows * ldp) = make_uint4(l[0], l[1], l[2], l[3]);
+  *(uint4*)(d + (size_t)rows_pad * ldp) = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-void launch_lr_split16(const float* const* src, uint16_t* const* dst, int rows, int k, int ldp,
+void launch_lr_split16(const float* const* src, uint16_t* const* dst, int rows, int rows_pad, int k, int ldp,
                        unsigned* const* amax, int slot, int count, hipStream_t s) {
-  const int64_t n8 = (int64_t)rows * (ldp / 8);
+  const int64_t n8 = (int64_t)rows_pad * (ldp / 8);
   if (n8 > 0 && count > 0)
-    hipLaunchKernelGGL(k_lr_split16, dim3((unsigned)((n8 + 255) / 256), count), dim3(256), 0, s, src, dst, rows, k, ldp,
-                       amax, slot);
+    hipLaunchKernelGGL(k_lr_split16, dim3((unsigned)((n8 + 255) / 256), count), dim3(256), 0, s, src, dst, rows,
+                       rows_pad, k, ldp, amax, slot);
 }
 
 }  // namespace dion

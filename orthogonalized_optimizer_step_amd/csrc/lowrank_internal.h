@@ -77,11 +77,13 @@ void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
                     const float* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
                     int out_fmt, int count, hipStream_t s);
-// The same with both operands split ahead by launch_lr_split16: A as m rows
-// and B as n rows of k values (fp16 hi and lo, row length ldp), C = A B^T.
-void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint16_t* const* A, const uint16_t* const* B,
-                          float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc, int out_fmt,
-                          int count, hipStream_t s);
+// C (m x n, ld n) = alpha A B^T + beta C with both operands split ahead by
+// launch_lr_split16: A as m rows (padded to rows_a) and B as n rows (padded
+// to rows_b) of k values (fp16 hi and lo, row length ldp); out_fmt 1 fp32
+// (with beta), 0 bf16 or 2 fp16 (beta must be 0).
+void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
+                          const uint16_t* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb,
+                          int sc, int out_fmt, int count, hipStream_t s);
 // The Gram F^T F of `count` row-major fp32 factors F (rows x r, F16 terms
 // with the scale of slot sf): the rows split into chunks of LR_GRAM_CHUNK,
 // chunk p's r x r partial written at S + p r r (only the tiles on or below
@@ -89,9 +91,10 @@ void launch_lr_gemm_split(int m, int n, int k, int ldp, float alpha, const uint1
 void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, unsigned* const* amax, int sf,
                     int count, hipStream_t s);
 // Split `count` row-major fp32 matrices (rows x k) with the scale of slot
-// `slot` into fp16 hi and lo rows of length ldp = k rounded up to 8 (zeros
-// beyond k; lo after hi): rows * ldp * 4 bytes at each dst.
-void launch_lr_split16(const float* const* src, uint16_t* const* dst, int rows, int k, int ldp,
+// `slot` into fp16 hi and lo rows of length ldp = k rounded up to 32, rows
+// padded to rows_pad = rows rounded up to 128 (zeros in the padding; lo
+// after hi): rows_pad * ldp * 4 bytes at each dst.
+void launch_lr_split16(const float* const* src, uint16_t* const* dst, int rows, int rows_pad, int k, int ldp,
                        unsigned* const* amax, int slot, int count, hipStream_t s);
 
 }  // namespace dion

@@ -51,11 +51,12 @@ void launch_lr_gemm(bool, bool, bool, int, int, int, float, const float* const*,
                     unsigned* const*, int, int, int, int, int, hipStream_t) {
   std::abort();
 }
-void launch_lr_gemm_split(int, int, int, int, float, const uint16_t* const*, const uint16_t* const*, float, void* const*,
-                          unsigned* const*, int, int, int, int, int, hipStream_t) {
+void launch_lr_gemm_split(int, int, int, int, int, int, float, const uint16_t* const*, const uint16_t* const*, float,
+                          void* const*, unsigned* const*, int, int, int, int, int, hipStream_t) {
   std::abort();
 }
-void launch_lr_split16(const float* const*, uint16_t* const*, int, int, int, unsigned* const*, int, int, hipStream_t) {
+void launch_lr_split16(const float* const*, uint16_t* const*, int, int, int, int, unsigned* const*, int, int,
+                       hipStream_t) {
   std::abort();
 }
 }  // namespace dion

@@ -31,6 +31,21 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_no_internal_symbol_left_undefined():
+    """Every function of the library's own namespace is defined in it: a shared
+    library links with undefined symbols, which would fail only when loaded
+    lazily on first use."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", "-C", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    missing = [ln.strip() for ln in out.splitlines() if "dion::" in ln or " dion_" in ln]
+    assert not missing, missing
+
+
 def test_version():
     assert _lib.lib.dion_version() == 100
 
