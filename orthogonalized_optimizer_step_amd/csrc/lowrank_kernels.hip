@@ -204,14 +204,16 @@ __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ d
 // registers: 1024 threads as a 32 x 32 grid, thread (ty, tx) owning the
 // entries (ty + 32 a, tx + 32 b), a >= b, of the 8 x 8 block-cyclic layout (36
 // fp64 registers; an entry's row and column follow from its slot, so nothing
-// else is stored).  Both steps are right-looking eliminations with the pivot
+// else is stored).  Both are right-looking eliminations with the pivot
 // column (and, for the inverse, the finished row) broadcast through LDS:
 //   Cholesky, step k: L[k][k] = sqrt(A[k][k]); L[i][k] = A[i][k] / L[k][k];
 //     A[i][c] -= L[i][k] L[c][k] for k < c <= i;
 //   inverse of L X = I, step k: row k of X divided by L[k][k], then
 //     X[i][c] -= L[i][k] X[k][c] for i > k, c <= k.
-// L leaves the registers for the fp64 scratch (column-major, so that a
-// column is one contiguous read) before the inverse reuses them.
+// They run interleaved, step k of both at once: the inverse's step k needs
+// only column k of L, just broadcast, and the registers that held it take
+// column k of X.  (A first form stored L to fp64 scratch and reloaded one
+// column per inverse step, each step waiting on a global load.)
 constexpr int LR_REG_THREADS = 1024;
 constexpr int LR_GRID = 32;
 constexpr int LR_NB = LR_REG_RMAX / LR_GRID;
@@ -226,16 +228,18 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
   if (r > LR_REG_RMAX) return;    // k_lr_cholinv
   const int tid = threadIdx.x;
   const int ty = tid / LR_GRID, tx = tid % LR_GRID;
-  __shared__ double col[LR_REG_RMAX];
-  __shared__ double rowx[LR_REG_RMAX];
-  __shared__ double diag[LR_REG_RMAX];
+  __shared__ double u[LR_REG_RMAX];
   __shared__ double red[LR_REG_THREADS / 64];
   __shared__ double s_piv;
   double v[LR_SLOTS];
   // slot of (a, b), a >= b: a (a + 1) / 2 + b
-#define LR_FOR_SLOTS(BODY)                                            \
+#define LR_FOR_SLOTS(BODY) LR_FOR_SLOTS_IF(true, BODY)
+  // only the blocks (a, b) for which USE holds (a condition uniform over the
+  // block, so that the others are skipped by a scalar branch)
+#define LR_FOR_SLOTS_IF(USE, BODY)                                    \
   _Pragma("unroll") for (int a = 0; a < LR_NB; ++a)                   \
   _Pragma("unroll") for (int b = 0; b <= a; ++b) {                    \
+    if (!(USE)) continue;                                             \
     const int sl = a * (a + 1) / 2 + b;                               \
     const int i = ty + LR_GRID * a, c = tx + LR_GRID * b;             \
     const bool own = i < r && (a > b || ty >= tx);                    \
@@ -255,42 +259,32 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
   const double tiny = 1e-14 * big;
   if (shift > 0.f) LR_FOR_SLOTS({ if (own && i == c) v[sl] += (double)shift * big; })
 
+  // Step k finishes column k of L and, with it, row k of X = L^-1: once
+  // column k of L is broadcast its slots hold column k of X (zero below the
+  // diagonal before this step's update), and the slots of columns c <= k
+  // hold X from then on.  One LDS vector u carries both broadcasts, u[c] =
+  // X[k][c] for c <= k and L[c][k] for c > k, so that for every row i > k
+  // (whose multiplier L[i][k] is u[i]) both updates read
+  //   v[i][c] -= u[i] u[c]:
+  // the Cholesky trailing update for c > k, the elimination of X for c <= k.
   for (int k = 0; k < r; ++k) {
-    LR_FOR_SLOTS({ if (own && i == k && c == k) s_piv = v[sl]; })
+    const int kb = k / LR_GRID;   // the block row and column of k
+    LR_FOR_SLOTS_IF(a == kb && b == kb, { if (own && i == k && c == k) s_piv = v[sl]; })
     __syncthreads();
     const double piv = s_piv;
     const double dk = piv > tiny ? sqrt(piv) : 0.0;
     const double inv = dk > 0.0 ? 1.0 / dk : 0.0;
-    LR_FOR_SLOTS({
-      if (own && c == k) {
-        const double x = i == k ? dk : v[sl] * inv;
-        v[sl] = x;
-        col[i] = x;
-      }
-    })
-    if (tid == 0) diag[k] = dk;
-    __syncthreads();
-    LR_FOR_SLOTS({ if (own && c > k) v[sl] -= col[i] * col[c]; })
-  }
-  // L (column-major) to the scratch; X = I in the registers
-  double* Lc = d.A64;
-  LR_FOR_SLOTS({
-    if (own) Lc[(size_t)c * r + i] = v[sl];
-    v[sl] = (own && i == c) ? 1.0 : 0.0;
-  })
-  __syncthreads();
-  for (int k = 0; k < r; ++k) {
-    for (int i = k + 1 + tid; i < r; i += LR_REG_THREADS) col[i] = Lc[(size_t)k * r + i];
-    const double dinv = diag[k] > 0.0 ? 1.0 / diag[k] : 0.0;
-    LR_FOR_SLOTS({
-      if (own && i == k) {
-        v[sl] *= dinv;
-        rowx[c] = v[sl];
+    LR_FOR_SLOTS_IF(a == kb || b == kb, {
+      if (own && c == k) {   // column k of L out to LDS; X[k][k] = 1 / L[k][k], X[i][k] = 0 (i > k)
+        u[i] = i == k ? inv : v[sl] * inv;
+        v[sl] = i == k ? inv : 0.0;
+      } else if (own && i == k && c < k) {   // the rest of row k of X
+        v[sl] *= inv;
+        u[c] = v[sl];
       }
     })
     __syncthreads();
-    LR_FOR_SLOTS({ if (own && i > k && c <= k) v[sl] -= col[i] * rowx[c]; })
-    __syncthreads();
+    LR_FOR_SLOTS_IF(a >= kb, { if (own && i > k) v[sl] -= u[i] * u[c]; })   // rows above block kb are done
   }
   for (int e = tid; e < r * r; e += LR_REG_THREADS) {
     const int i = e / r, c = e - (e / r) * r;
@@ -306,6 +300,7 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
   })
   lr_raise<LR_REG_THREADS>(d.amax + amax_slot, mxl);
 #undef LR_FOR_SLOTS
+#undef LR_FOR_SLOTS_IF
 }
 
 // One block per matrix: Q[:, j] = W[:, j] / ||W[:, j]|| (fp64 norm), zero
