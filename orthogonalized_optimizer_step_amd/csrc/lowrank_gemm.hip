@@ -99,6 +99,13 @@ __device__ __forceinline__ void lg_split(float x, float s, uint32_t* t) {
 // operand layouts: fp32 with r (the M or N index) contiguous, or with k contiguous
 enum { LG_RC = 0, LG_KC = 1 };
 
+// Loads through generic pointers become flat loads, which also count against
+// the LDS wait counter: every wait for the fragment reads of a stage would
+// then wait for the next stage's loads from memory too.  Operand and result
+// accesses therefore go through global-address-space pointers (vmcnt only).
+#define LG_GLOBAL __attribute__((address_space(1)))
+typedef float lg_float4 __attribute__((ext_vector_type(4)));
+
 // A K-stage of one operand: LG_TILE rows (of op(X)'s M or N side) x LG_BK k,
 // 16 values per thread.  KC: stored with k contiguous (element (r, k) at
 // p[r * ld + k]); otherwise with r contiguous (element (r, k) at p[k * ld + r]).
@@ -107,14 +114,22 @@ struct LgStage {
   static constexpr bool KC = MODE == LG_KC;
   static constexpr int NT = F16 ? 2 : 3;   // terms
   float v[16];
+  // vec: 16-byte aligned rows.  A stage wholly inside the operand (every
+  // interior stage) takes 16-byte loads in every lane; the decision is the
+  // same for the whole block, so no lane waits on another's loads.
   __device__ __forceinline__ void load(const float* p, int ld, int rows, int ks, int r0, int k0, bool vec) {
     const int t = threadIdx.x;
+    const bool whole = vec && r0 + LG_TILE <= rows && k0 + LG_BK <= ks;
     if (KC) {   // row r0 + t/2, k0 + (t&1)*16 .. +15
       const int r = r0 + (t >> 1), k = k0 + (t & 1) * 16;
-      const float* q = p + (size_t)r * ld + k;
-      if (vec && r < rows && k + 16 <= ks) {
+      const float LG_GLOBAL* q = (const float LG_GLOBAL*)p + (size_t)r * ld + k;
+      if (whole) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(float4*)&v[4 * i] = ((const float4*)q)[i];
+        for (int i = 0; i < 4; ++i) {
+          const lg_float4 x = ((const lg_float4 LG_GLOBAL*)q)[i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[4 * i + j] = x[j];
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = (r < rows && k + i < ks) ? q[i] : 0.f;
@@ -123,9 +138,11 @@ struct LgStage {
       const int r = r0 + (t & 31) * 4, k = k0 + (t >> 5) * 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float* q = p + (size_t)(k + i) * ld + r;
-        if (vec && k + i < ks && r + 4 <= rows) {
-          *(float4*)&v[4 * i] = *(const float4*)q;
+        const float LG_GLOBAL* q = (const float LG_GLOBAL*)p + (size_t)(k + i) * ld + r;
+        if (whole) {
+          const lg_float4 x = *(const lg_float4 LG_GLOBAL*)q;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[4 * i + j] = x[j];
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) v[4 * i + j] = (k + i < ks && r + j < rows) ? q[j] : 0.f;
@@ -169,6 +186,30 @@ struct LgStage {
   }
 };
 
+// The block's tile (x, y) and batch entry z.  Blocks are dealt to the 8 XCDs
+// round-robin by linear id; they are renumbered so that each XCD runs a
+// contiguous run of tiles in (x, y, z) order, x fastest: the N tiles of one
+// row block, which read the same rows of A, then run at about the same time
+// in one XCD and share its L2 (the right product and the CholeskyQR products
+// gained 2-4% from this; the split-operand kernel below, whose blocks share
+// only small operands, lost 5-12% with it and keeps the plain order).
+struct LgBlock {
+  int x, y, z;
+};
+__device__ __forceinline__ LgBlock lg_block() {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int xcd = lin & 7, idx = lin >> 3;
+  const int base = total >> 3, rem = total & 7;
+  const int t = xcd * base + min(xcd, rem) + idx;
+  LgBlock b;
+  b.x = t % gx;
+  b.y = (t / gx) % gy;
+  b.z = t / (gx * gy);
+  return b;
+}
+
 __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -197,7 +238,7 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = rbase + (e >> 2) * 8 + (e & 3);
-          cv[e] = (col < N && row < M) ? ((const float*)Cp)[coff + (size_t)row * ldc + col] : 0.f;
+          cv[e] = (col < N && row < M) ? ((const float LG_GLOBAL*)Cp)[coff + (size_t)row * ldc + col] : 0.f;
         }
       }
 #pragma unroll
@@ -208,9 +249,9 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
           float v = alpha * ldexpf(acc[a][b][e], -lab);
           if (out_fmt == 1) {
             if (beta != 0.f) v = v + beta * cv[e];
-            ((float*)Cp)[o] = v;
+            ((float LG_GLOBAL*)Cp)[o] = v;
           } else {
-            ((uint16_t*)Cp)[o] = out_fmt == 0 ? lg_bf16_rne(v) : __builtin_bit_cast(uint16_t, (_Float16)v);
+            ((uint16_t LG_GLOBAL*)Cp)[o] = out_fmt == 0 ? lg_bf16_rne(v) : __builtin_bit_cast(uint16_t, (_Float16)v);
           }
           mx = fmaxf(mx, fabsf(v));
         }
@@ -229,8 +270,8 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
   }
 }
 
-// Row-major C (M x N) = alpha op(A) op(B) + beta C for batch entry z =
-// blockIdx.z.  A_MODE LG_KC: A is stored M x K (K contiguous, op = N); LG_RC:
+// Row-major C (M x N) = alpha op(A) op(B) + beta C for batch entry z of the
+// block (lg_block).  A_MODE LG_KC: A is stored M x K (K contiguous, op = N); LG_RC:
 // K x M (op = T).  B_MODE LG_KC: B is stored N x K (op = T); LG_RC: K x N
 // (op = N).
 template <int A_MODE, int B_MODE, bool F16>
@@ -241,18 +282,19 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
                                                  int out_fmt, int kchunk, int lower_only) {
   constexpr int NT = F16 ? 2 : 3;
   __shared__ __attribute__((aligned(16))) uint16_t sA[NT * LG_TERM], sB[NT * LG_TERM];
-  // kchunk > 0: K split into chunks, chunk p of product z in block z * parts
-  // + p, its partial result at C + p M N
+  // kchunk > 0: K split into chunks, chunk p of product z at batch index
+  // z * parts + p, its partial result at C + p M N
   const int parts = kchunk > 0 ? (K + kchunk - 1) / kchunk : 1;
-  const int z = blockIdx.z / parts, part = blockIdx.z - z * parts;
+  const LgBlock blk = lg_block();
+  const int z = blk.z / parts, part = blk.z - z * parts;
   const int kbeg = part * kchunk, kend = kchunk > 0 ? min(K, kbeg + kchunk) : K;
-  if (lower_only && blockIdx.x > blockIdx.y) return;   // a tile wholly above the diagonal
+  if (lower_only && blk.x > blk.y) return;   // a tile wholly above the diagonal
   const float* A = As[z];
   const float* B = Bs[z];
   unsigned* slots = amax[z];
   const int la = F16 ? lg_log2_scale(slots[sa]) : 0, lb = F16 ? lg_log2_scale(slots[sb]) : 0;
   const float scale_a = ldexpf(1.f, la), scale_b = ldexpf(1.f, lb);
-  const int m0 = blockIdx.y * LG_TILE, n0 = blockIdx.x * LG_TILE;
+  const int m0 = blk.y * LG_TILE, n0 = blk.x * LG_TILE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool veca = (lda & 3) == 0 && ((uintptr_t)A & 15) == 0;
