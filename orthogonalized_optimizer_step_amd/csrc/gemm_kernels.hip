@@ -196,6 +196,7 @@ __device__ __forceinline__ AT phase_alpha(const MatDesc& d, const PhaseArgs& pa,
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __host__ __device__ constexpr int epi_wave_bytes(int wt) {
   return 32 * (wt + 8) * 4;   // row-major strip 32 x (wt + 8) floats
@@ -321,31 +322,36 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
         const int rows_valid = pa.out_rows_are_m ? d.m : d.n;
         const int cols_valid = pa.out_rows_are_m ? d.n : d.m;
         if (gi < rows_valid && gj0 < cols_valid) {
-          const int orow = pa.idx ? pa.idx[d.sel0 + gi] : gi;
+          const int orow = pa.idx ? *to_global(pa.idx + d.sel0 + gi) : gi;
           const size_t o = (size_t)orow * d.C + gj0;
           const bool full = gj0 + 8 <= cols_valid;
+          // output (and weight) accesses through global pointers: flat ones
+          // would also count against the LDS wait counter of the next strip
           if (pa.out_update) {
             // the weight update: W <- fl32(fl32(W * keep) - fl32(alpha * u)),
             // rounded to W's dtype below (u = this fp32 output)
             float cur[8];
             if (pa.out_fp32) {
-              const float* wp = (const float*)d.out + o;
+              const float DION_GLOBAL* wp = to_global((const float*)d.out) + o;
               if (full && ((uintptr_t)wp & 15) == 0) {
-                *(float4*)&cur[0] = *(const float4*)wp;
-                *(float4*)&cur[4] = *(const float4*)(wp + 4);
+                const f32x4 c0 = *(const f32x4 DION_GLOBAL*)wp, c1 = *(const f32x4 DION_GLOBAL*)(wp + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  cur[i] = c0[i];
+                  cur[4 + i] = c1[i];
+                }
               } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) cur[i] = gj0 + i < cols_valid ? wp[i] : 0.f;
               }
             } else {
-              const uint16_t* wp = (const uint16_t*)d.out + o;
+              const uint16_t DION_GLOBAL* wp = to_global((const uint16_t*)d.out) + o;
               if (full && ((uintptr_t)wp & 15) == 0) {
-                const uint4 b = *(const uint4*)wp;
-                const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+                const u32x4 b = *(const u32x4 DION_GLOBAL*)wp;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                  cur[2 * i] = __uint_as_float(bw[i] << 16);
-                  cur[2 * i + 1] = __uint_as_float(bw[i] & 0xFFFF0000u);
+                  cur[2 * i] = __uint_as_float(b[i] << 16);
+                  cur[2 * i + 1] = __uint_as_float(b[i] & 0xFFFF0000u);
                 }
               } else {
 #pragma unroll
@@ -358,36 +364,36 @@ __device__ __forceinline__ void epilogue_strip(const MatDesc& d, const PhaseArgs
               w[i] = __fsub_rn(__fmul_rn(cur[i], pa.upd_keep), __fmul_rn(d.upd_alpha, w[i]));
           }
           if (pa.out_fp32) {
-            float* out = (float*)d.out + o;
+            float DION_GLOBAL* out = to_global_w((float*)d.out) + o;
             if (full && ((uintptr_t)out & 15) == 0) {
-              *(float4*)out = *(float4*)&w[0];
-              *(float4*)(out + 4) = *(float4*)&w[4];
+              *(f32x4 DION_GLOBAL*)out = f32x4{w[0], w[1], w[2], w[3]};
+              *(f32x4 DION_GLOBAL*)(out + 4) = f32x4{w[4], w[5], w[6], w[7]};
             } else {
 #pragma unroll
               for (int i = 0; i < 8; ++i)
                 if (gj0 + i < cols_valid) out[i] = w[i];
             }
           } else if (pa.out_f16) {
-            _Float16* out = (_Float16*)d.out + o;
+            _Float16 DION_GLOBAL* out = to_global_w((_Float16*)d.out) + o;
             if (full && ((uintptr_t)out & 15) == 0) {
               half8v pk;
 #pragma unroll
               for (int i = 0; i < 8; ++i) pk[i] = (_Float16)w[i];
-              *(half8v*)out = pk;
+              *(half8v DION_GLOBAL*)out = pk;
             } else {
 #pragma unroll
               for (int i = 0; i < 8; ++i)
                 if (gj0 + i < cols_valid) out[i] = (_Float16)w[i];
             }
           } else {
-            uint16_t* out = (uint16_t*)d.out + o;
+            uint16_t DION_GLOBAL* out = to_global_w((uint16_t*)d.out) + o;
             if (full && ((uintptr_t)out & 15) == 0) {
-              uint4 pk;
-              pk.x = (uint32_t)f32_to_bf16_rne(w[0]) | ((uint32_t)f32_to_bf16_rne(w[1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16_rne(w[2]) | ((uint32_t)f32_to_bf16_rne(w[3]) << 16);
-              pk.z = (uint32_t)f32_to_bf16_rne(w[4]) | ((uint32_t)f32_to_bf16_rne(w[5]) << 16);
-              pk.w = (uint32_t)f32_to_bf16_rne(w[6]) | ((uint32_t)f32_to_bf16_rne(w[7]) << 16);
-              *(uint4*)out = pk;
+              u32x4 pk;
+              pk[0] = (uint32_t)f32_to_bf16_rne(w[0]) | ((uint32_t)f32_to_bf16_rne(w[1]) << 16);
+              pk[1] = (uint32_t)f32_to_bf16_rne(w[2]) | ((uint32_t)f32_to_bf16_rne(w[3]) << 16);
+              pk[2] = (uint32_t)f32_to_bf16_rne(w[4]) | ((uint32_t)f32_to_bf16_rne(w[5]) << 16);
+              pk[3] = (uint32_t)f32_to_bf16_rne(w[6]) | ((uint32_t)f32_to_bf16_rne(w[7]) << 16);
+              *(u32x4 DION_GLOBAL*)out = pk;
             } else {
 #pragma unroll
               for (int i = 0; i < 8; ++i)
@@ -727,8 +733,8 @@ __global__ __launch_bounds__(256) void k_gemm64(const MatDesc* __restrict__ desc
   const int K = pa.k_is_n ? d.n_pad : d.m_pad;
   int ti, tj;
   decode_tile(SYM, t - prefix[j], arows, brows, BM, ti, tj);
-  const double* gA = (const double*)d.buf[pa.a_slot] + (size_t)ti * BM * K;
-  const double* gB = (const double*)d.buf[pa.b_slot] + (size_t)tj * BM * K;
+  const double DION_GLOBAL* gA = to_global((const double*)d.buf[pa.a_slot]) + (size_t)ti * BM * K;
+  const double DION_GLOBAL* gB = to_global((const double*)d.buf[pa.b_slot]) + (size_t)tj * BM * K;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   double acc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += BK) {

@@ -52,8 +52,9 @@ constexpr int LR_BLOCK_ELEMS = 2048;
 // ranks up to this factor their Gram matrix in registers (k_lr_cholinv_reg)
 constexpr int LR_REG_RMAX = 256;
 
-// blocks per matrix of k_lr_absmax
+// blocks per matrix of k_lr_absmax and of k_lr_gram_sum
 constexpr int LR_ABSMAX_SPLIT = 16;
+constexpr int LR_SUM_SPLIT = 256;
 // rows of the factor per K chunk of a CholeskyQR Gram product
 constexpr int LR_GRAM_CHUNK = 1024;
 
@@ -62,7 +63,7 @@ constexpr int LR_GRAM_CHUNK = 1024;
 void launch_lr_accumulate(const LrDesc* d, int nmat, int64_t blocks, int grad_fmt, float* blockmax, hipStream_t s);
 void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStream_t s);
 // S is the sum of the parts_R (rows_are_R) or parts_C partial Grams, added
-// in order; shift > 0: factor S + shift * (largest diagonal entry of S) * I
+// in order in fp64 into A64 (k_lr_gram_sum); shift > 0: factor S + shift * (largest diagonal entry of S) * I
 // (the first, shifted pass of shifted CholeskyQR3); the largest |entry| of
 // L^-1 raises slot `amax_slot`
 void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, bool rows_are_R, float shift,

@@ -4,6 +4,7 @@
 // in k_lr_gemm (lowrank_gemm.hip); what is here is the rest of the step:
 //   k_lr_accumulate  B = fl32(M + G) in place (the residual buffer)
 //   k_lr_absmax      the largest |value| of B, from k_lr_accumulate's block maxima
+//   k_lr_gram_sum    the Gram matrix from its K-chunk partial sums, in fp64
 //   k_lr_cholinv     Cholesky factor of an r x r Gram matrix in fp64 and the
 //                    inverse of that factor, for CholeskyQR (A = P L^-T)
 //   k_lr_colnorm     Dion's column normalization of the right factor
@@ -14,6 +15,12 @@
 #include "lowrank_internal.h"
 
 namespace dion {
+
+// Accesses to global memory through generic pointers become flat
+// instructions, which also count against the LDS wait counter; the
+// factorization's global loads and stores go through global-address-space
+// pointers so that its LDS waits do not wait for them.
+#define LR_GLOBAL __attribute__((address_space(1)))
 
 namespace {
 
@@ -106,17 +113,38 @@ __global__ __launch_bounds__(256) void k_lr_absmax(const LrDesc* __restrict__ de
   lr_raise<256>(d.amax + LS_B, mb);
 }
 
-// S[e], the sum of the partial Grams of the K chunks, added in order in fp64
-__device__ __forceinline__ double lr_gram_at(const LrDesc& d, int parts, size_t e) {
-  const size_t rr = (size_t)d.r * d.r;
-  double v = 0.0;
-  for (int p = 0; p < parts; ++p) v += (double)d.S[p * rr + e];
-  return v;
+// A64 = S in fp64: on and below the diagonal the sum of the partial Grams of
+// the K chunks (parts_R or parts_C of them), added in order; zero above it.
+// The input of both factorization kernels.  Grid (LR_SUM_SPLIT, matrices),
+// each thread a few entries (four partials' loads in flight at a time).
+__global__ __launch_bounds__(256) void k_lr_gram_sum(const LrDesc* __restrict__ descs, int rows_are_R) {
+  const LrDesc& d = descs[blockIdx.y];
+  const int parts = rows_are_R ? d.parts_R : d.parts_C;
+  const int r = d.r;
+  const size_t rr = (size_t)r * r;
+  const float LR_GLOBAL* S = (const float LR_GLOBAL*)d.S;
+  double LR_GLOBAL* A = (double LR_GLOBAL*)d.A64;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < rr; e += (size_t)gridDim.x * 256) {
+    const size_t i = e / r, j = e - i * r;
+    double v = 0.0;
+    if (j <= i) {
+      int p = 0;
+      for (; p + 4 <= parts; p += 4) {
+        const float a0 = S[p * rr + e], a1 = S[(p + 1) * rr + e], a2 = S[(p + 2) * rr + e], a3 = S[(p + 3) * rr + e];
+        v += (double)a0;
+        v += (double)a1;
+        v += (double)a2;
+        v += (double)a3;
+      }
+      for (; p < parts; ++p) v += (double)S[p * rr + e];
+    }
+    A[e] = v;
+  }
 }
 
-// One block per matrix.  From the Gram S = F^T F (r x r, fp32 partial sums
-// of its K chunks, symmetric; only the lower triangle is read) of
-// the factor F being orthogonalized: the lower Cholesky factor L of S, in
+// One block per matrix.  From the Gram S = F^T F (r x r, in A64 as
+// k_lr_gram_sum leaves it: fp64, lower triangle, zero above) of the factor
+// F being orthogonalized, factored in place: the lower Cholesky factor L of S, in
 // fp64, then Linv = L^-1 (fp32, lower; zero above the diagonal), so that
 // F L^-T has orthonormal columns (CholeskyQR; the triangular factor L^T has
 // a positive diagonal).  Left-looking: column j takes the dot products of
@@ -126,10 +154,8 @@ __device__ __forceinline__ double lr_gram_at(const LrDesc& d, int parts, size_t 
 // contract): its column of L^-1 and of the result is zero, which keeps every
 // value finite.  The inverse is column-wise forward substitution, one column
 // per thread, X = L^-1 kept transposed in the upper triangle of the scratch.
-__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, int rows_are_R, float shift,
-                                                    int amax_slot) {
+__global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ descs, float shift, int amax_slot) {
   const LrDesc& d = descs[blockIdx.x];
-  const int parts = rows_are_R ? d.parts_R : d.parts_C;
   const int r = d.r;
   if (r <= LR_REG_RMAX) return;   // k_lr_cholinv_reg
   const int tid = threadIdx.x;
@@ -139,12 +165,7 @@ __global__ __launch_bounds__(256) void k_lr_cholinv(const LrDesc* __restrict__ d
   __shared__ double red[256];
 
   double mx = 0.0;
-  for (int e = tid; e < r * r; e += 256) {
-    const int i = e / r, j = e - (e / r) * r;
-    const double v = j <= i ? lr_gram_at(d, parts, e) : 0.0;
-    A[e] = v;
-    if (i == j) mx = fmax(mx, v);
-  }
+  for (int i = tid; i < r; i += 256) mx = fmax(mx, A[(size_t)i * r + i]);   // A = S (k_lr_gram_sum)
   red[tid] = mx;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -220,10 +241,9 @@ constexpr int LR_NB = LR_REG_RMAX / LR_GRID;
 constexpr int LR_SLOTS = LR_NB * (LR_NB + 1) / 2;
 static_assert(LR_GRID * LR_GRID == LR_REG_THREADS, "thread grid");
 
-__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, int rows_are_R,
-                                                          float shift, int amax_slot) {
+__global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restrict__ descs, float shift,
+                                                          int amax_slot) {
   const LrDesc& d = descs[blockIdx.x];
-  const int parts = rows_are_R ? d.parts_R : d.parts_C;
   const int r = d.r;
   if (r > LR_REG_RMAX) return;    // k_lr_cholinv
   const int tid = threadIdx.x;
@@ -246,11 +266,15 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
     (void)sl; (void)own;                                              \
     BODY                                                              \
   }
-  double mx = 0.0;
+  // S from k_lr_gram_sum; every lane loads (entry 0 for the slots it does
+  // not own), so that no load is divergent and all 36 are in flight at once
+  const double LR_GLOBAL* S = (const double LR_GLOBAL*)d.A64;
   LR_FOR_SLOTS({
-    v[sl] = own ? lr_gram_at(d, parts, (size_t)i * r + c) : 0.0;
-    if (own && i == c) mx = fmax(mx, v[sl]);
+    const double x = S[own ? i * r + c : 0];   // 32-bit offsets from one base
+    v[sl] = own ? x : 0.0;
   })
+  double mx = 0.0;
+  LR_FOR_SLOTS({ if (own && i == c) mx = fmax(mx, v[sl]); })
   for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
@@ -286,15 +310,16 @@ __global__ __launch_bounds__(1024) void k_lr_cholinv_reg(const LrDesc* __restric
     __syncthreads();
     LR_FOR_SLOTS_IF(a >= kb, { if (own && i > k) v[sl] -= u[i] * u[c]; })   // rows above block kb are done
   }
+  float LR_GLOBAL* Linv = (float LR_GLOBAL*)d.Linv;
   for (int e = tid; e < r * r; e += LR_REG_THREADS) {
     const int i = e / r, c = e - (e / r) * r;
-    if (c > i) d.Linv[e] = 0.f;
+    if (c > i) Linv[e] = 0.f;
   }
   float mxl = 0.f;
   LR_FOR_SLOTS({
     if (own) {
       const float x = (float)v[sl];
-      d.Linv[(size_t)i * r + c] = x;
+      Linv[(size_t)i * r + c] = x;
       mxl = fmaxf(mxl, fabsf(x));
     }
   })
@@ -328,10 +353,10 @@ void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStrea
 }
 void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, bool rows_are_R, float shift,
                        int amax_slot, hipStream_t s) {
-  const int rr = rows_are_R ? 1 : 0;
-  if (nmat > 0 && any_small)
-    hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, rr, shift, amax_slot);
-  if (nmat > 0 && any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, rr, shift, amax_slot);
+  if (nmat <= 0) return;
+  hipLaunchKernelGGL(k_lr_gram_sum, dim3(LR_SUM_SPLIT, nmat), dim3(256), 0, s, d, rows_are_R ? 1 : 0);
+  if (any_small) hipLaunchKernelGGL(k_lr_cholinv_reg, dim3(nmat), dim3(LR_REG_THREADS), 0, s, d, shift, amax_slot);
+  if (any_large) hipLaunchKernelGGL(k_lr_cholinv, dim3(nmat), dim3(256), 0, s, d, shift, amax_slot);
 }
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s) {
   if (nmat > 0) hipLaunchKernelGGL(k_lr_colnorm, dim3(nmat), dim3(256), 0, s, d);

@@ -599,6 +599,9 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
 // as 8-column chunks straight from registers, ST through a 64 x 65 fp32 LDS
 // tile read as 8-row column chunks (both LDS passes are bank-conflict-free).
 typedef _Float16 half8s __attribute__((ext_vector_type(8)));
+typedef uint32_t pk_u32x4 __attribute__((ext_vector_type(4)));
+typedef float pk_f32x4 __attribute__((ext_vector_type(4)));
+#define DION_SGLOBAL __attribute__((address_space(1)))
 template <typename InT>
 __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ descs, const int* __restrict__ mats,
                                                 const int* __restrict__ prefix, int nmat, int total,
@@ -628,6 +631,9 @@ __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ desc
   const size_t ts = (size_t)k_pad * c_pad;
   const bool vec = (d.C & 7) == 0 && ((uintptr_t)d.M & 15) == 0;
 
+  // loads and stores through global pointers (flat ones would also count
+  // against the LDS wait counter), and every store after the barrier, so
+  // that neither the barrier nor an LDS wait waits for a store
   auto split_store = [&](_Float16* base, size_t off, const float* v, bool with_lo) {
     half8s h, l;
 #pragma unroll
@@ -635,49 +641,58 @@ __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ desc
       h[i] = (_Float16)v[i];
       l[i] = (_Float16)(v[i] - (float)h[i]);
     }
-    *(half8s*)(base + off) = h;
-    if (with_lo) *(half8s*)(base + off + ts) = l;
+    _Float16 DION_SGLOBAL* g = (_Float16 DION_SGLOBAL*)base + off;
+    *(half8s DION_SGLOBAL*)g = h;
+    if (with_lo) *(half8s DION_SGLOBAL*)(g + ts) = l;
   };
+  float v[2][8];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int q = threadIdx.x + 256 * j;
     const int row = q >> 3, cc = (q & 7) * 8;
     const int r = r0 + row, c = c0 + cc;
-    float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
     if (r < d.k && c < d.C) {
-      const int src = use_idx ? idx[r] : r;
-      const InT* p = (const InT*)d.M + (int64_t)src * d.C + c;
+      const int src = use_idx ? ((const int DION_SGLOBAL*)idx)[r] : r;
+      const InT DION_SGLOBAL* p = (const InT DION_SGLOBAL*)d.M + (int64_t)src * d.C + c;
       if (vec) {  // c + 8 <= C: C and c are multiples of 8
         if (sizeof(InT) == 2) {
-          const uint4 u = *(const uint4*)p;
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+          const pk_u32x4 u = *(const pk_u32x4 DION_SGLOBAL*)p;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[2 * i] = in16_to_f32<InT>(w4[i] & 0xFFFFu);
-            v[2 * i + 1] = in16_to_f32<InT>(w4[i] >> 16);
+            v[j][2 * i] = in16_to_f32<InT>(u[i] & 0xFFFFu);
+            v[j][2 * i + 1] = in16_to_f32<InT>(u[i] >> 16);
           }
         } else {
-          const float4 a = ((const float4*)p)[0], b = ((const float4*)p)[1];
-          v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-          v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+          const pk_f32x4 a = ((const pk_f32x4 DION_SGLOBAL*)p)[0], b = ((const pk_f32x4 DION_SGLOBAL*)p)[1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[j][i] = a[i];
+            v[j][4 + i] = b[i];
+          }
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (c + i < d.C)
-            v[i] = sizeof(InT) == 2 ? in16_to_f32<InT>(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+            v[j][i] = sizeof(InT) == 2 ? in16_to_f32<InT>(((const uint16_t DION_SGLOBAL*)p)[i])
+                                       : ((const float DION_SGLOBAL*)p)[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      v[i] *= scale;
-      tile[row][cc + i] = v[i];
+      v[j][i] *= scale;
+      tile[row][cc + i] = v[j][i];
     }
-    split_store(sl, blk_off(r, c, c_pad), v, sl_lo);      // SL row r, columns c..c+7
   }
   __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = threadIdx.x + 256 * j;
+    const int row = q >> 3, cc = (q & 7) * 8;
+    split_store(sl, blk_off(r0 + row, c0 + cc, c_pad), v[j], sl_lo);   // SL row r, columns c..c+7
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int q = threadIdx.x + 256 * j;
