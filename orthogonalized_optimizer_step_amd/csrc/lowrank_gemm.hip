@@ -105,6 +105,7 @@ enum { LG_RC = 0, LG_KC = 1 };
 // accesses therefore go through global-address-space pointers (vmcnt only).
 #define LG_GLOBAL __attribute__((address_space(1)))
 typedef float lg_float4 __attribute__((ext_vector_type(4)));
+typedef uint32_t lg_u32x2 __attribute__((ext_vector_type(2)));
 
 // A K-stage of one operand: LG_TILE rows (of op(X)'s M or N side) x LG_BK k,
 // 16 values per thread.  KC: stored with k contiguous (element (r, k) at
@@ -257,6 +258,94 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
         }
       }
     }
+  if (slot) {   // one atomic per block
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    if (tid == 0) {
+      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (m > 0.f) atomicMax(slot, __float_as_uint(m));
+    }
+  }
+}
+
+// The same epilogue for accumulators of C^T (the MFMA operands swapped:
+// block (a, b) holds rows m0 + wm 64 + a 32 + (lane & 31) and, in elements
+// 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g +
+// 4 (lane / 32) .. + 3), so that a lane reads and writes four columns of a
+// row at once; ld of C is N.  Every read of C is issued before any write.
+__device__ __forceinline__ void lg_epilogue_t(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab,
+                                              float alpha, float beta, void* Cp, int out_fmt, unsigned* slot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool vec = (N & 3) == 0 && ((uintptr_t)Cp & 15) == 0;
+  const bool readc = out_fmt == 1 && beta != 0.f;
+  float LG_GLOBAL* C32 = (float LG_GLOBAL*)Cp;
+  uint16_t LG_GLOBAL* C16 = (uint16_t LG_GLOBAL*)Cp;
+  float cv[2][2][16];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = m0 + wm * 64 + a * 32 + (lane & 31);
+        const int col = n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane >> 5);
+        const size_t o = (size_t)row * N + col;
+        if (!readc) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cv[a][b][4 * g + j] = 0.f;
+        } else if (vec && row < M && col + 4 <= N) {
+          const lg_float4 x = *(const lg_float4 LG_GLOBAL*)(C32 + o);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cv[a][b][4 * g + j] = x[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cv[a][b][4 * g + j] = (row < M && col + j < N) ? C32[o + j] : 0.f;
+        }
+      }
+  float mx = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = m0 + wm * 64 + a * 32 + (lane & 31);
+        const int col = n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane >> 5);
+        const size_t o = (size_t)row * N + col;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = alpha * ldexpf(acc[a][b][4 * g + j], -lab);
+          if (readc) v[j] = v[j] + beta * cv[a][b][4 * g + j];
+          if (row < M && col + j < N) mx = fmaxf(mx, fabsf(v[j]));
+        }
+        if (row >= M) continue;
+        if (out_fmt == 1) {
+          if (vec && col + 4 <= N) {
+            *(lg_float4 LG_GLOBAL*)(C32 + o) = lg_float4{v[0], v[1], v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (col + j < N) C32[o + j] = v[j];
+          }
+        } else {
+          uint32_t h[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            h[j] = out_fmt == 0 ? lg_bf16_rne(v[j]) : __builtin_bit_cast(uint16_t, (_Float16)v[j]);
+          if (vec && col + 4 <= N) {
+            *(lg_u32x2 LG_GLOBAL*)(C16 + o) = lg_u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (col + j < N) C16[o + j] = (uint16_t)h[j];
+          }
+        }
+      }
   if (slot) {   // one atomic per block
     __shared__ float red[4];
 #pragma unroll
@@ -505,18 +594,18 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0][a], fb[1][b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[1][b], fa[0][a], acc[a][b], 0, 0, 0);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[1][a], fb[0][b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[0][b], fa[1][a], acc[a][b], 0, 0, 0);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[0][a], fb[0][b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[0][b], fa[0][a], acc[a][b], 0, 0, 0);
     }
   }
-  lg_epilogue(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], N, 0, out_fmt, sc >= 0 ? slots + sc : nullptr);
+  lg_epilogue_t(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], out_fmt, sc >= 0 ? slots + sc : nullptr);
 }
 
 void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
