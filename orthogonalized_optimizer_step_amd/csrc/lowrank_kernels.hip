@@ -18,9 +18,11 @@ namespace dion {
 
 // Accesses to global memory through generic pointers become flat
 // instructions, which also count against the LDS wait counter; the
-// factorization's global loads and stores go through global-address-space
-// pointers so that its LDS waits do not wait for them.
+// factorization's and the accumulation's global accesses go through
+// global-address-space pointers so that their LDS waits do not wait for them.
 #define LR_GLOBAL __attribute__((address_space(1)))
+typedef float lr_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t lr_u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -73,23 +75,35 @@ __global__ __launch_bounds__(256) void k_lr_accumulate(const LrDesc* __restrict_
   const int64_t e0 = (b - d.blk0) * LR_BLOCK_ELEMS + (int64_t)threadIdx.x * 8;
   float mx = 0.f;
   if (e0 < d.elems) {
-    float* M = d.M + e0;
-    if (e0 + 8 <= d.elems && ((uintptr_t)M & 31) == 0) {
-      float4 m0 = *(const float4*)M, m1 = *(const float4*)(M + 4);
+    float LR_GLOBAL* M = (float LR_GLOBAL*)d.M + e0;
+    const char LR_GLOBAL* G = (const char LR_GLOBAL*)d.G + e0 * (fmt == 1 ? 4 : 2);
+    // 16-byte accesses: M's 8 values as two, G's as one (16-bit) or two (fp32)
+    if (e0 + 8 <= d.elems && ((uintptr_t)M & 31) == 0 && ((uintptr_t)G & 15) == 0) {
+      const lr_f32x4 m0 = ((const lr_f32x4 LR_GLOBAL*)M)[0], m1 = ((const lr_f32x4 LR_GLOBAL*)M)[1];
+      float m[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
       float g[8];
-      if (fmt == 1 && ((uintptr_t)((const float*)d.G + e0) & 15) == 0) {
-        const float4 g0 = *(const float4*)((const float*)d.G + e0), g1 = *(const float4*)((const float*)d.G + e0 + 4);
-        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-      } else {
+      if (fmt == 1) {
+        const lr_f32x4 g0 = ((const lr_f32x4 LR_GLOBAL*)G)[0], g1 = ((const lr_f32x4 LR_GLOBAL*)G)[1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) g[i] = lr_in(d.G, e0 + i, fmt);
+        for (int i = 0; i < 4; ++i) {
+          g[i] = g0[i];
+          g[4 + i] = g1[i];
+        }
+      } else {
+        const lr_u32x4 u = *(const lr_u32x4 LR_GLOBAL*)G;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t h = (u[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+          g[i] = fmt == 0 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+        }
       }
-      m0.x = __fadd_rn(m0.x, g[0]); m0.y = __fadd_rn(m0.y, g[1]); m0.z = __fadd_rn(m0.z, g[2]); m0.w = __fadd_rn(m0.w, g[3]);
-      m1.x = __fadd_rn(m1.x, g[4]); m1.y = __fadd_rn(m1.y, g[5]); m1.z = __fadd_rn(m1.z, g[6]); m1.w = __fadd_rn(m1.w, g[7]);
-      *(float4*)M = m0;
-      *(float4*)(M + 4) = m1;
-      mx = fmaxf(fmaxf(fmaxf(fabsf(m0.x), fabsf(m0.y)), fmaxf(fabsf(m0.z), fabsf(m0.w))),
-                 fmaxf(fmaxf(fabsf(m1.x), fabsf(m1.y)), fmaxf(fabsf(m1.z), fabsf(m1.w))));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        m[i] = __fadd_rn(m[i], g[i]);
+        mx = fmaxf(mx, fabsf(m[i]));
+      }
+      ((lr_f32x4 LR_GLOBAL*)M)[0] = lr_f32x4{m[0], m[1], m[2], m[3]};
+      ((lr_f32x4 LR_GLOBAL*)M)[1] = lr_f32x4{m[4], m[5], m[6], m[7]};
     } else {
       for (int i = 0; i < 8 && e0 + i < d.elems; ++i) {
         M[i] = __fadd_rn(M[i], lr_in(d.G, e0 + i, fmt));
