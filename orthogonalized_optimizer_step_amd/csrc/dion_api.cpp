@@ -1784,12 +1784,12 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   // whose error the orthogonalization after it amplifies by the condition
   // number of B Q
   auto gprod = [&](const char* name, const LrGroup& g, bool ta, bool tb, bool f16, int m, int n, int k, float alpha,
-                   int A, int B, float beta_, int Cm, int sa, int sb, int sc, int out_fmt,
+                   int A, int B, int Cm, int sa, int sb, int sc, int out_fmt,
                    double bytes_each) -> int {
     const double cnt = (double)g.mats.size();
     return phase(name, gemm_name(ta, tb, f16), 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
       launch_lr_gemm(ta, tb, f16, m, n, k, alpha, (const float* const*)arrays(g, A), (const float* const*)arrays(g, B),
-                     beta_, (void* const*)arrays(g, Cm), (unsigned* const*)arrays(g, LP_AM), sa, sb, sc, out_fmt,
+                     (void* const*)arrays(g, Cm), (unsigned* const*)arrays(g, LP_AM), sa, sb, sc, out_fmt,
                      (int)g.mats.size(), stream);
       return DION_OK;
     });
@@ -1831,7 +1831,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
          return DION_OK;
        })) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // Y = B Q
-    if ((rc = gprod("lr_power", g, false, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, 0.f, LP_Y, LS_B, LS_B, LS_Y, 1,
+    if ((rc = gprod("lr_power", g, false, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, LP_Y, LS_B, LS_B, LS_Y, 1,
                     4.0 * ((double)g.R * g.C + (double)g.C * g.r + (double)g.R * g.r))) != DION_OK) return rc;
   // shifted CholeskyQR3 of F (rows x r): F -> dst -> tmp -> dst (tmp may be F).
   // The first pass factors S + 1e-3 max_i S_ii I: an ill-conditioned F (its
@@ -1869,7 +1869,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
       if (e != DION_OK) return e;
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
-        e = gprod("lr_orth", g, false, true, true, rows, g.r, g.r, 1.f, from[pass], LP_L, 0.f, to[pass], s_from, s_l + pass,
+        e = gprod("lr_orth", g, false, true, true, rows, g.r, g.r, 1.f, from[pass], LP_L, to[pass], s_from, s_l + pass,
                   s_out + pass, 1, 4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
@@ -1880,7 +1880,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   for (const LrGroup& g : P.groups)   // the split P, for the buffer update and the update
     if ((rc = gsplit(g, LP_X, LP_XS, g.R, LS_F2)) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // W = B^T P
-    if ((rc = gprod("lr_right", g, true, false, true, g.C, g.r, g.R, 1.f, LP_M, LP_X, 0.f, LP_W, LS_B, LS_F2, LS_W, 1,
+    if ((rc = gprod("lr_right", g, true, false, true, g.C, g.r, g.R, 1.f, LP_M, LP_X, LP_W, LS_B, LS_F2, LS_W, 1,
                     4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)
     if ((rc = gsplit(g, LP_W, LP_WS, g.C, LS_W)) != DION_OK) return rc;

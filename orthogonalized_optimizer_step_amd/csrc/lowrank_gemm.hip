@@ -220,71 +220,26 @@ __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
 }  // namespace
 
 // The epilogue of a 128 x 128 tile held by four waves of 64 x 64 (2 x 2 MFMA
-// blocks, lane = column (lane & 31) of rows (e/4)*8 + (lane/32)*4 + e%4 of
-// each block): C = alpha 2^-lab acc (+ beta C), written as out_fmt; with
-// slot >= 0, the block's largest |value| raises *slot.  Every thread calls.
-__device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab, float alpha,
-                                            float beta, void* Cp, int ldc, size_t coff, int out_fmt, unsigned* slot) {
+// blocks), whose MFMAs take the B operand first so that the accumulators
+// hold C^T: block (a, b) holds row m0 + wm 64 + a 32 + (lane & 31) and, in
+// elements 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g
+// + 4 (lane / 32) .. + 3; a lane thus reads and writes four columns of a row
+// at once.  C (ld ldc, from element coff) = alpha 2^-lab acc (+ beta C with
+// READC, fp32 only), written as out_fmt; every read of C is issued before
+// any write.  With slot, the block's largest |value| raises *slot.  Every
+// thread calls.
+template <bool READC>
+__device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab,
+                                            float alpha, float beta, void* Cp, int ldc, size_t coff, int out_fmt,
+                                            unsigned* slot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  float mx = 0.f;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int col = n0 + wn * 64 + b * 32 + (lane & 31);
-      const int rbase = m0 + wm * 64 + a * 32 + (lane >> 5) * 4;
-      float cv[16];
-      if (out_fmt == 1 && beta != 0.f) {   // every read of C before any write: 16 loads in flight
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + (e >> 2) * 8 + (e & 3);
-          cv[e] = (col < N && row < M) ? ((const float LG_GLOBAL*)Cp)[coff + (size_t)row * ldc + col] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = rbase + (e >> 2) * 8 + (e & 3);
-        if (col < N && row < M) {
-          const size_t o = coff + (size_t)row * ldc + col;
-          float v = alpha * ldexpf(acc[a][b][e], -lab);
-          if (out_fmt == 1) {
-            if (beta != 0.f) v = v + beta * cv[e];
-            ((float LG_GLOBAL*)Cp)[o] = v;
-          } else {
-            ((uint16_t LG_GLOBAL*)Cp)[o] = out_fmt == 0 ? lg_bf16_rne(v) : __builtin_bit_cast(uint16_t, (_Float16)v);
-          }
-          mx = fmaxf(mx, fabsf(v));
-        }
-      }
-    }
-  if (slot) {   // one atomic per block
-    __shared__ float red[4];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    if (tid == 0) {
-      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      if (m > 0.f) atomicMax(slot, __float_as_uint(m));
-    }
-  }
-}
-
-// The same epilogue for accumulators of C^T (the MFMA operands swapped:
-// block (a, b) holds rows m0 + wm 64 + a 32 + (lane & 31) and, in elements
-// 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g +
-// 4 (lane / 32) .. + 3), so that a lane reads and writes four columns of a
-// row at once; ld of C is N.  Every read of C is issued before any write.
-__device__ __forceinline__ void lg_epilogue_t(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab,
-                                              float alpha, float beta, void* Cp, int out_fmt, unsigned* slot) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const bool vec = (N & 3) == 0 && ((uintptr_t)Cp & 15) == 0;
-  const bool readc = out_fmt == 1 && beta != 0.f;
-  float LG_GLOBAL* C32 = (float LG_GLOBAL*)Cp;
-  uint16_t LG_GLOBAL* C16 = (uint16_t LG_GLOBAL*)Cp;
+  const bool vec = (N & 3) == 0 && (ldc & 3) == 0 && ((uintptr_t)Cp & 15) == 0 && (coff & 3) == 0;
+  const bool readc = READC && out_fmt == 1 && beta != 0.f;
+  float LG_GLOBAL* C32 = (float LG_GLOBAL*)Cp + coff;
+  uint16_t LG_GLOBAL* C16 = (uint16_t LG_GLOBAL*)Cp + coff;
   float cv[2][2][16];
+  if (READC)
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -293,7 +248,7 @@ __device__ __forceinline__ void lg_epilogue_t(floatx16 (&acc)[2][2], int M, int 
       for (int g = 0; g < 4; ++g) {
         const int row = m0 + wm * 64 + a * 32 + (lane & 31);
         const int col = n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane >> 5);
-        const size_t o = (size_t)row * N + col;
+        const size_t o = (size_t)row * ldc + col;
         if (!readc) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) cv[a][b][4 * g + j] = 0.f;
@@ -315,7 +270,7 @@ __device__ __forceinline__ void lg_epilogue_t(floatx16 (&acc)[2][2], int M, int 
       for (int g = 0; g < 4; ++g) {
         const int row = m0 + wm * 64 + a * 32 + (lane & 31);
         const int col = n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane >> 5);
-        const size_t o = (size_t)row * N + col;
+        const size_t o = (size_t)row * ldc + col;
         float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -359,13 +314,13 @@ __device__ __forceinline__ void lg_epilogue_t(floatx16 (&acc)[2][2], int M, int 
   }
 }
 
-// Row-major C (M x N) = alpha op(A) op(B) + beta C for batch entry z of the
+// Row-major C (M x N) = alpha op(A) op(B) for batch entry z of the
 // block (lg_block).  A_MODE LG_KC: A is stored M x K (K contiguous, op = N); LG_RC:
 // K x M (op = T).  B_MODE LG_KC: B is stored N x K (op = T); LG_RC: K x N
 // (op = N).
 template <int A_MODE, int B_MODE, bool F16>
 __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alpha, const float* const* __restrict__ As,
-                                                 int lda, const float* const* __restrict__ Bs, int ldb, float beta,
+                                                 int lda, const float* const* __restrict__ Bs, int ldb,
                                                  void* const* __restrict__ Cs, int ldc,
                                                  unsigned* const* __restrict__ amax, int sa, int sb, int sc,
                                                  int out_fmt, int kchunk, int lower_only) {
@@ -435,28 +390,28 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
         for (int a = 0; a < 2; ++a)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            if (F16)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, fa[PA[p]][a]),
-                                                                 __builtin_bit_cast(halfx8, fb[PB[p]][b]), acc[a][b], 0,
+            if (F16)   // B operand first: the accumulators hold C^T (lg_epilogue)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, fb[PB[p]][b]),
+                                                                 __builtin_bit_cast(halfx8, fa[PA[p]][a]), acc[a][b], 0,
                                                                  0, 0);
             else
-              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[PA[p]][a]),
-                                                                  __builtin_bit_cast(bf16x8, fb[PB[p]][b]), acc[a][b],
+              acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[PB[p]][b]),
+                                                                  __builtin_bit_cast(bf16x8, fa[PA[p]][a]), acc[a][b],
                                                                   0, 0, 0);
           }
     }
   }
-  lg_epilogue(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], ldc, (size_t)part * M * N, out_fmt,
+  lg_epilogue<false>(acc, M, N, m0, n0, la + lb, alpha, 0.f, Cs[z], ldc, (size_t)part * M * N, out_fmt,
               sc >= 0 ? slots + sc : nullptr);
 }
 
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
-                    const float* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
+                    const float* const* B, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
                     int out_fmt, int count, hipStream_t s) {
   const int lda = ta ? m : k, ldb = tb ? k : n, ldc = n;
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
 #define DION_LRG(AK, BK, F)                                                                                          \
-  hipLaunchKernelGGL((k_lr_gemm<AK, BK, F>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,   \
+  hipLaunchKernelGGL((k_lr_gemm<AK, BK, F>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, C, ldc,   \
                      amax, sa, sb, sc, out_fmt, 0, 0)
   if (f16) {
     if (!ta && tb) DION_LRG(LG_KC, LG_KC, true);
@@ -605,7 +560,7 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
         for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[0][b], fa[0][a], acc[a][b], 0, 0, 0);
     }
   }
-  lg_epilogue_t(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], out_fmt, sc >= 0 ? slots + sc : nullptr);
+  lg_epilogue<true>(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], N, 0, out_fmt, sc >= 0 ? slots + sc : nullptr);
 }
 
 void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
@@ -621,7 +576,7 @@ void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, uns
                     hipStream_t s) {
   const int parts = (rows + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK;
   const dim3 grid((r + LG_TILE - 1) / LG_TILE, (r + LG_TILE - 1) / LG_TILE, count * parts);
-  hipLaunchKernelGGL((k_lr_gemm<LG_RC, LG_RC, true>), grid, dim3(256), 0, s, r, r, rows, 1.f, F, r, F, r, 0.f,
+  hipLaunchKernelGGL((k_lr_gemm<LG_RC, LG_RC, true>), grid, dim3(256), 0, s, r, r, rows, 1.f, F, r, F, r,
                      (void* const*)S, r, amax, sf, sf, -1, 1, LR_GRAM_CHUNK, 1);
 }
 

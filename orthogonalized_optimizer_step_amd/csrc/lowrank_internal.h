@@ -69,14 +69,13 @@ void launch_lr_absmax(const LrDesc* d, int nmat, const float* blockmax, hipStrea
 void launch_lr_cholinv(const LrDesc* d, int nmat, bool any_small, bool any_large, bool rows_are_R, float shift,
                        int amax_slot, hipStream_t s);
 void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
-// Row-major C (m x n) = alpha op(A) op(B) + beta C over `count` products
-// (device pointer arrays; amax: each product's matrix's LS_N slots), on
-// two-term fp16 operands (f16) or three-term bf16 ones.  The fp16 operands'
-// scales come from slots sa and sb; sc >= 0 raises slot sc with the result's
-// largest |value|.  out_fmt: 1 fp32 (with beta), 0 bf16 or 2 fp16 (beta must
-// be 0; round to nearest even).
+// Row-major C (m x n) = alpha op(A) op(B) over `count` products (device
+// pointer arrays; amax: each product's matrix's LS_N slots), on two-term
+// fp16 operands (f16) or three-term bf16 ones.  The fp16 operands' scales
+// come from slots sa and sb; sc >= 0 raises slot sc with the result's
+// largest |value|.  out_fmt: 1 fp32, 0 bf16 or 2 fp16 (round to nearest even).
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
-                    const float* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
+                    const float* const* B, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
                     int out_fmt, int count, hipStream_t s);
 // C (m x n, ld n) = alpha A B^T + beta C with both operands split ahead by
 // launch_lr_split16: A as m rows (padded to rows_a) and B as n rows (padded

@@ -47,7 +47,7 @@ void launch_lr_absmax(const LrDesc*, int, const float*, hipStream_t) { std::abor
 void launch_lr_cholinv(const LrDesc*, int, bool, bool, bool, float, int, hipStream_t) { std::abort(); }
 void launch_lr_gram(int, int, const float* const*, float* const*, unsigned* const*, int, int, hipStream_t) { std::abort(); }
 void launch_lr_colnorm(const LrDesc*, int, hipStream_t) { std::abort(); }
-void launch_lr_gemm(bool, bool, bool, int, int, int, float, const float* const*, const float* const*, float, void* const*,
+void launch_lr_gemm(bool, bool, bool, int, int, int, float, const float* const*, const float* const*, void* const*,
                     unsigned* const*, int, int, int, int, int, hipStream_t) {
   std::abort();
 }
