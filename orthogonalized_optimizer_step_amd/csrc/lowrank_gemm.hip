@@ -4,8 +4,9 @@
 // B - beta P W^T, the update P Q'^T, and the Gram and apply products of
 // CholeskyQR) runs here.
 //
-//   C = alpha op(A) op(B) + beta C      (row-major fp32, a batch of same-shape
-//                                        products given as device pointer arrays)
+//   C = alpha op(A) op(B) (+ beta C)    (row-major fp32, a batch of same-shape
+//                                        products given as device pointer arrays;
+//                                        beta C in the split-operand kernel)
 //
 // fp32 accuracy from 16-bit matrix cores, in one of two operand formats:
 //  - F16 (two fp16 terms): each operand is scaled by a power of two s, chosen
@@ -40,12 +41,14 @@
 //
 // Tiles of 128 x 128 outputs, four waves of 64 x 64 (2 x 2 MFMA blocks).  A
 // K-stage of 32 columns is loaded from global memory into registers (16-byte
-// loads when the rows allow, zeros outside the matrix) while the previous
-// stage is multiplied, then split and stored to LDS as [row][k] fp16 rows of
-// four 16-byte chunks per term, the chunk order XOR-swizzled by row so that
-// the fragment reads of 32 lanes hit distinct banks.  Operands stored with K
-// contiguous are staged row by row; operands stored with M (or N) contiguous
-// are staged four K-rows at a time and written as 8-byte column pieces.
+// loads for every stage inside the matrix, zeros outside it) while the
+// previous stage is multiplied, then split and stored to LDS as [row][k] fp16
+// rows of four 16-byte chunks per term, the chunk order XOR-swizzled by row
+// so that the fragment reads of 32 lanes hit distinct banks.  Operands stored
+// with K contiguous are staged row by row; operands stored with M (or N)
+// contiguous are staged four K-rows at a time and written as 8-byte column
+// pieces.  The MFMAs take the B operand first, so that the accumulators hold
+// C^T and each lane writes four consecutive columns of a row of C at once.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
