@@ -10,9 +10,13 @@
 // a few rows, whose fp16 rounding a Gram side of a few rows cannot average
 // out.  Here one workgroup per matrix
 // runs the whole iteration in fp64: the m x m matrices G, P, Q and a temporary
-// live in LDS (four 64 x 64 fp64 buffers, 128 KB, plus a 16 KB staging chunk
-// for the Gram), the iterate X (m x n, fp64) in two workspace buffers that
-// alternate at restarts.
+// live in LDS (four 64 x 64 fp64 buffers, rows padded to 65 so that a column
+// of 16 rows spreads over the banks, 133 KB, plus a 16 KB staging chunk for
+// the Gram), the iterate X (m x n, fp64) in two workspace buffers that
+// alternate at restarts.  The m x m products and the Gram run on the matrix
+// cores (v_mfma_f64_16x16x4_f64): each of the 16 waves owns one 16 x 16 tile
+// of the 64 x 64 result.  Entries beyond m stay zero in every buffer, so the
+// products can run over whole tiles.
 #include <hip/hip_runtime.h>
 
 #include "dion_internal.h"
@@ -20,7 +24,10 @@
 namespace dion {
 
 constexpr int TINY_M = 64;
+constexpr int TINY_LD = TINY_M + 1;   // row stride of the LDS matrices
 constexpr int TINY_THREADS = 1024;
+typedef double tiny_d4 __attribute__((ext_vector_type(4)));
+#define TINY_GLOBAL __attribute__((address_space(1)))
 
 namespace {
 
@@ -80,9 +87,10 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
   const int tid = threadIdx.x;
   const double nu2 = scalars[mi].nu2;                // ||S||_F^2 from the selection
   const double s = nu2 > 0.0 ? 1.0 / sqrt(nu2) : 0.0;
-  __shared__ double buf[4][TINY_M * TINY_M];          // row-major, ld TINY_M
-  double* X = (double*)d.buf[SLOT_X];                 // m x n, ld n
-  double* X2 = (double*)d.buf[SLOT_XT0];
+  __shared__ double buf[4][TINY_M * TINY_LD];         // row-major, ld TINY_LD
+  double TINY_GLOBAL* X = (double TINY_GLOBAL*)d.buf[SLOT_X];     // m x n, ld n
+  double TINY_GLOBAL* X2 = (double TINY_GLOBAL*)d.buf[SLOT_XT0];
+  for (int e = tid; e < 4 * TINY_M * TINY_LD; e += TINY_THREADS) (&buf[0][0])[e] = 0.0;
   auto src_row = [&](int j) { return idx ? idx[d.sel0 + j] : j; };
 
   // X = S / nu, oriented so that m <= n (S^T when the block is tall)
@@ -93,51 +101,54 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
   }
   __syncthreads();
 
-  // G = X X^T from 32-column chunks of X staged transposed in LDS; thread
-  // (i0, j) sums rows i0, i0 + 16, i0 + 32, i0 + 48 of column j along the long
-  // side in order (so G[i][j] and G[j][i] take the same sum)
+  // The MFMA tiles: wave w owns rows 16 (w / 4) .. + 15 and columns 16 (w %
+  // 4) .. + 15 of a 64 x 64 result.  v_mfma_f64_16x16x4_f64 takes lane l's
+  // A[l % 16][l / 16] and B[l / 16][l % 16] and accumulates D[l / 16 +
+  // 4 v][l % 16] in its element v (rows interleaved by four; checked on the
+  // device against a host product).  Tiles wholly beyond m are zero.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ti = wave >> 2, tj = wave & 3;
+  const bool live = ti * 16 < m && tj * 16 < m;
+  auto tile_store = [&](double* C, const tiny_d4& acc) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) C[(ti * 16 + (lane >> 4) + 4 * v) * TINY_LD + tj * 16 + (lane & 15)] = acc[v];
+  };
+  // G = X X^T from 32-column chunks of X staged transposed in LDS (xc[k][row]);
+  // G[i][j] and G[j][i] take the same products in the same order
   __shared__ double xc[32 * TINY_M];
   auto gram = [&](double* G) {
-    const int j = tid & 63, i0 = tid >> 6;
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    tiny_d4 acc = {0.0, 0.0, 0.0, 0.0};
     for (int l0 = 0; l0 < n; l0 += 32) {
       for (int e = tid; e < 32 * TINY_M; e += TINY_THREADS) {
         const int row = e >> 5, k = e & 31;
         xc[k * TINY_M + row] = (row < m && l0 + k < n) ? X[(size_t)row * n + l0 + k] : 0.0;
       }
       __syncthreads();
-      if (j < m) {
-        for (int k = 0; k < 32; ++k) {
-          const double bk = xc[k * TINY_M + j];
+      if (live) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] += xc[k * TINY_M + i0 + 16 * r] * bk;
+        for (int k0 = 0; k0 < 32; k0 += 4) {
+          const int k = k0 + (lane >> 4);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xc[k * TINY_M + ti * 16 + (lane & 15)],
+                                                     xc[k * TINY_M + tj * 16 + (lane & 15)], acc, 0, 0, 0);
         }
       }
       __syncthreads();
     }
-    if (j < m) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i0 + 16 * r < m) G[(i0 + 16 * r) * TINY_M + j] = acc[r];
-    }
+    tile_store(G, acc);
     __syncthreads();
   };
-  // C = A B (m x m): thread (i0, j) forms rows i0, i0 + 16, i0 + 32, i0 + 48 of
-  // column j, sharing each B[k][j] (rows past m are computed from in-bounds
-  // LDS and dropped)
+  // C = A B (m x m, zero beyond m); C is neither A nor B
+  const int kmax = (m + 3) & ~3;
   auto mm = [&](double* C, const double* A, const double* B) {
-    const int j = tid & 63, i0 = tid >> 6;
-    if (j < m) {
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int k = 0; k < m; ++k) {
-        const double bk = B[k * TINY_M + j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += A[(i0 + 16 * r) * TINY_M + k] * bk;
+    tiny_d4 acc = {0.0, 0.0, 0.0, 0.0};
+    if (live) {
+      for (int k0 = 0; k0 < kmax; k0 += 4) {
+        const int k = k0 + (lane >> 4);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(A[(ti * 16 + (lane & 15)) * TINY_LD + k],
+                                                   B[k * TINY_LD + tj * 16 + (lane & 15)], acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (i0 + 16 * r < m) C[(i0 + 16 * r) * TINY_M + j] = acc[r];
     }
+    tile_store(C, acc);
     __syncthreads();
   };
   // (Q X)[i][l] for every (i, l), or X when Q == NULL: each work item is one
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
         for (int k = 0; k < m; ++k) {
           const double x = X[(size_t)k * n + l];
 #pragma unroll
-          for (int r = 0; r < 8; ++r) acc[r] += Q[(i0 + r < TINY_M ? i0 + r : 0) * TINY_M + k] * x;
+          for (int r = 0; r < 8; ++r) acc[r] += Q[(i0 + r < TINY_M ? i0 + r : 0) * TINY_LD + k] * x;
         }
       } else {
 #pragma unroll
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
     mm(buf[t], buf[g], buf[g]);                        // G G
     for (int e = tid; e < m * m; e += TINY_THREADS) {  // P = a I + b G + c G G
       const int i = e / m, j = e - (e / m) * m;
-      const int o = i * TINY_M + j;
+      const int o = i * TINY_LD + j;
       buf[p][o] = (i == j ? a : 0.0) + b * buf[g][o] + c * buf[t][o];
     }
     __syncthreads();
@@ -190,7 +201,7 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
     if ((restarts >> (k - 1)) & 1ull) {                // X <- Q X, G <- X X^T, Q <- I
       apply(buf[q], [&](int i, int l, double v) { X2[(size_t)i * n + l] = v; });
       __syncthreads();
-      double* tmp = X;
+      double TINY_GLOBAL* tmp = X;
       X = X2;
       X2 = tmp;
       gram(buf[g]);
