@@ -151,30 +151,34 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
     tile_store(C, acc);
     __syncthreads();
   };
-  // (Q X)[i][l] for every (i, l), or X when Q == NULL: each work item is one
-  // column l and 8 consecutive rows, so the loads of X[k][l] are coalesced
-  // across the lanes and Q[i][k] is the same address for all of them
+  // (Q X)[i][l] for every (i, l), or X when Q == NULL: each wave takes 16 x 16
+  // output tiles in turn, the products on the matrix cores with X's values
+  // loaded straight from global memory (lane l: row k0 + l / 16, column l % 16)
   auto apply = [&](const double* Q, auto&& sink) {
-    const int groups = (m + 7) / 8;
-    for (int it = tid; it < groups * n; it += TINY_THREADS) {
-      const int rg = it / n, l = it - (it / n) * n;
-      const int i0 = rg * 8;
-      double acc[8];
+    const int tiles_l = (n + 15) / 16, tiles = ((m + 15) / 16) * tiles_l;
+    for (int tt = wave; tt < tiles; tt += TINY_THREADS / 64) {
+      const int ai = tt / tiles_l, al = tt - (tt / tiles_l) * tiles_l;
+      const int col = al * 16 + (lane & 15);
+      tiny_d4 acc = {0.0, 0.0, 0.0, 0.0};
       if (Q) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r] = 0.0;
-        for (int k = 0; k < m; ++k) {
-          const double x = X[(size_t)k * n + l];
-#pragma unroll
-          for (int r = 0; r < 8; ++r) acc[r] += Q[(i0 + r < TINY_M ? i0 + r : 0) * TINY_LD + k] * x;
+#pragma unroll 4
+        for (int k0 = 0; k0 < kmax; k0 += 4) {
+          const int k = k0 + (lane >> 4);
+          const double x = (k < m && col < n) ? X[(size_t)k * n + col] : 0.0;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(Q[(ai * 16 + (lane & 15)) * TINY_LD + k], x, acc, 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) acc[r] = i0 + r < m ? X[(size_t)(i0 + r) * n + l] : 0.0;
+        for (int v = 0; v < 4; ++v) {
+          const int i = ai * 16 + (lane >> 4) + 4 * v;
+          acc[v] = (i < m && col < n) ? X[(size_t)i * n + col] : 0.0;
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (i0 + r < m) sink(i0 + r, l, acc[r]);
+      for (int v = 0; v < 4; ++v) {
+        const int i = ai * 16 + (lane >> 4) + 4 * v;
+        if (i < m && col < n) sink(i, col, acc[v]);
+      }
     }
   };
 
