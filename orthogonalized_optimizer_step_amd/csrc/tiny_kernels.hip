@@ -151,6 +151,25 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
     tile_store(C, acc);
     __syncthreads();
   };
+  // P = a I + b G + c G G, the polynomial formed from G G's tiles as they
+  // leave the matrix cores (zero beyond m)
+  auto mm_poly = [&](double* P, const double* G, double a, double b, double c) {
+    tiny_d4 acc = {0.0, 0.0, 0.0, 0.0};
+    if (live) {
+      for (int k0 = 0; k0 < kmax; k0 += 4) {
+        const int k = k0 + (lane >> 4);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(G[(ti * 16 + (lane & 15)) * TINY_LD + k],
+                                                   G[k * TINY_LD + tj * 16 + (lane & 15)], acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ti * 16 + (lane >> 4) + 4 * v, j = tj * 16 + (lane & 15);
+      const int o = i * TINY_LD + j;
+      P[o] = (i < m && j < m) ? (i == j ? a : 0.0) + b * G[o] + c * acc[v] : 0.0;
+    }
+    __syncthreads();
+  };
   // (Q X)[i][l] for every (i, l), or X when Q == NULL: each wave takes 16 x 16
   // output tiles in turn, the products on the matrix cores with X's values
   // loaded straight from global memory (lane l: row k0 + l / 16, column l % 16)
@@ -187,17 +206,11 @@ __global__ __launch_bounds__(TINY_THREADS) void k_tiny_gns(const MatDesc* __rest
   for (int k = 1; k <= K; ++k) {
     const double a = coef[3 * (k - 1)], b = coef[3 * (k - 1) + 1], c = coef[3 * (k - 1) + 2];
     const int p = tiny_free(g, q, -1);
-    const int t = tiny_free(g, q, p);
-    mm(buf[t], buf[g], buf[g]);                        // G G
-    for (int e = tid; e < m * m; e += TINY_THREADS) {  // P = a I + b G + c G G
-      const int i = e / m, j = e - (e / m) * m;
-      const int o = i * TINY_LD + j;
-      buf[p][o] = (i == j ? a : 0.0) + b * buf[g][o] + c * buf[t][o];
-    }
-    __syncthreads();
+    mm_poly(buf[p], buf[g], a, b, c);                  // P = a I + b G + c G G
     if (q < 0) {
       q = p;                                           // Q = P at a segment's first iteration
     } else {
+      const int t = tiny_free(g, q, p);
       mm(buf[t], buf[p], buf[q]);                      // Q <- P Q
       q = t;
     }
