@@ -1603,7 +1603,8 @@ void make_update(Plan& P, int w_dtype, float weight_decay) {
 // previous right factor, the residual (error-feedback) buffer, and the right
 // factor normalized by columns (Dion) or by QR (Orth-Dion).  Per matrix,
 // with r = min(rank, R, C):
-//   B = fl32(M + G)                        k_lr_accumulate (M in place)
+//   B = fl32(M + G)                        formed where read (16-bit G), or
+//                                          k_lr_accumulate (M in place)
 //   P = orth(B Q)                          GEMM, then shifted CholeskyQR3
 //   W = B^T P                              GEMM
 //   M = B - beta P W^T                     GEMM (beta = -beta, accumulate)
@@ -1618,9 +1619,9 @@ void make_update(Plan& P, int w_dtype, float weight_decay) {
 // operand's producer raises; the slots live in the uploaded header, so every
 // call starts them at zero (and Dion's normalized Q at one).
 constexpr int kMaxRank = 512;
-// pointer arrays per group: the matrices' buffers, the max slots, and the
-// split (fp16 hi and lo) copies of P, W and the new Q
-enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_AM, LP_XS, LP_WS, LP_QS, LP_N };
+// pointer arrays per group: the matrices' buffers, the max slots, the split
+// (fp16 hi and lo) copies of P, W and the new Q, and the gradients
+enum { LP_M, LP_Q, LP_X, LP_Y, LP_W, LP_W2, LP_S, LP_L, LP_D, LP_AM, LP_XS, LP_WS, LP_QS, LP_G, LP_N };
 
 struct LrGroup {
   int R, C, r;
@@ -1731,7 +1732,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
       const int i = g.mats[t];
       float* const v[LP_N] = {d.M, d.Q, d.X, d.Y, d.W, d.W2, d.S, d.Linv, (float*)d.out, (float*)d.amax,
                               (float*)(ws + P.off[LP_XS][i]), (float*)(ws + P.off[LP_WS][i]),
-                              (float*)(ws + P.off[LP_QS][i])};
+                              (float*)(ws + P.off[LP_QS][i]), (float*)d.G};
       for (int k = 0; k < LP_N; ++k) arr[k * n + t] = v[k];
     }
   }
@@ -1783,13 +1784,16 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   // fp16 operands (f16), or three-term bf16 ones for the power product B Q,
   // whose error the orthogonalization after it amplifies by the condition
   // number of B Q
+  // withg: A is the buffer M and the operand B = fl32(M + G) (gslot >= 0:
+  // raise that slot with its largest |value|)
   auto gprod = [&](const char* name, const LrGroup& g, bool ta, bool tb, bool f16, int m, int n, int k, float alpha,
-                   int A, int B, int Cm, int sa, int sb, int sc, int out_fmt,
+                   int A, int B, int Cm, int sa, int sb, int sc, int out_fmt, bool withg, int gslot,
                    double bytes_each) -> int {
     const double cnt = (double)g.mats.size();
     return phase(name, gemm_name(ta, tb, f16), 2.0 * m * n * k * cnt, bytes_each * cnt, [&]() {
       launch_lr_gemm(ta, tb, f16, m, n, k, alpha, (const float* const*)arrays(g, A), (const float* const*)arrays(g, B),
                      (void* const*)arrays(g, Cm), (unsigned* const*)arrays(g, LP_AM), sa, sb, sc, out_fmt,
+                     withg ? (const uint16_t* const*)arrays(g, LP_G) : nullptr, grad_dtype, gslot,
                      (int)g.mats.size(), stream);
       return DION_OK;
     });
@@ -1809,30 +1813,42 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   };
   // C (R x C) = alpha P Z^T + beta C from the split P and Z (C x r), inner dimension r
   auto gprod_split = [&](const char* name, const LrGroup& g, float alpha, int Z, float beta_, int Cm, int sz,
-                         int out_fmt, double bytes_each) -> int {
+                         int out_fmt, bool withg, double bytes_each) -> int {
     const int ldp = (g.r + 31) / 32 * 32;
     const double cnt = (double)g.mats.size();
     return phase(name, "dion::k_lr_gemm_dma", 2.0 * g.R * g.C * g.r * cnt, bytes_each * cnt, [&]() {
       launch_lr_gemm_split(g.R, g.C, g.r, ldp, pad128(g.R), pad128(g.C), alpha, (const uint16_t* const*)arrays(g, LP_XS),
                            (const uint16_t* const*)arrays(g, Z), beta_, (void* const*)arrays(g, Cm),
-                           (unsigned* const*)arrays(g, LP_AM), LS_F2, sz, -1, out_fmt, (int)g.mats.size(), stream);
+                           (unsigned* const*)arrays(g, LP_AM), LS_F2, sz, -1, out_fmt,
+                           withg ? (const uint16_t* const*)arrays(g, LP_G) : nullptr, grad_dtype,
+                           (int)g.mats.size(), stream);
       return DION_OK;
     });
   };
   const double gsz = (double)dtype_bytes(grad_dtype);
-  if ((rc = phase("lr_accumulate", "dion::k_lr_accumulate", 0.0, elems * (8.0 + gsz), [&]() {
-         launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, (float*)(ws + P.off_blockmax), stream);
-         return DION_OK;
-       })) != DION_OK) return rc;
   double cr_all = 0.0;
   for (int i = 0; i < batch; ++i) cr_all += (double)P.C[i] * P.r[i];
-  if ((rc = phase("lr_absmax", "dion::k_lr_absmax", 0.0, 4.0 * P.blocks, [&]() {
-         launch_lr_absmax(d_descs, nmat, (const float*)(ws + P.off_blockmax), stream);
-         return DION_OK;
-       })) != DION_OK) return rc;
+  // With 16-bit gradients the buffer B = fl32(M + G) is never stored: the
+  // power product, the right factor and the buffer update form it as they
+  // read M and G (the power product also raising B's max slot), and M takes
+  // the updated buffer in the last of them.  fp32 gradients take a pass that
+  // stores B into M first.
+  const bool fused = grad_dtype != DION_FP32;
+  if (!fused) {
+    if ((rc = phase("lr_accumulate", "dion::k_lr_accumulate", 0.0, elems * (8.0 + gsz), [&]() {
+           launch_lr_accumulate(d_descs, nmat, P.blocks, grad_dtype, (float*)(ws + P.off_blockmax), stream);
+           return DION_OK;
+         })) != DION_OK) return rc;
+    if ((rc = phase("lr_absmax", "dion::k_lr_absmax", 0.0, 4.0 * P.blocks, [&]() {
+           launch_lr_absmax(d_descs, nmat, (const float*)(ws + P.off_blockmax), stream);
+           return DION_OK;
+         })) != DION_OK) return rc;
+  }
+  const double bsz = fused ? 4.0 + gsz : 4.0;   // bytes read per element of B
   for (const LrGroup& g : P.groups)   // Y = B Q
     if ((rc = gprod("lr_power", g, false, false, false, g.R, g.r, g.C, 1.f, LP_M, LP_Q, LP_Y, LS_B, LS_B, LS_Y, 1,
-                    4.0 * ((double)g.R * g.C + (double)g.C * g.r + (double)g.R * g.r))) != DION_OK) return rc;
+                    fused, fused ? LS_B : -1,
+                    bsz * g.R * g.C + 4.0 * ((double)g.C * g.r + (double)g.R * g.r))) != DION_OK) return rc;
   // shifted CholeskyQR3 of F (rows x r): F -> dst -> tmp -> dst (tmp may be F).
   // The first pass factors S + 1e-3 max_i S_ii I: an ill-conditioned F (its
   // fp32 Gram matrix losing the small directions to rounding) then still
@@ -1870,7 +1886,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
       for (const LrGroup& g : P.groups) {
         const int rows = rows_are_R ? g.R : g.C;
         e = gprod("lr_orth", g, false, true, true, rows, g.r, g.r, 1.f, from[pass], LP_L, to[pass], s_from, s_l + pass,
-                  s_out + pass, 1, 4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
+                  s_out + pass, 1, false, -1, 4.0 * (2.0 * rows * g.r + (double)g.r * g.r));
         if (e != DION_OK) return e;
       }
     }
@@ -1881,12 +1897,12 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     if ((rc = gsplit(g, LP_X, LP_XS, g.R, LS_F2)) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // W = B^T P
     if ((rc = gprod("lr_right", g, true, false, true, g.C, g.r, g.R, 1.f, LP_M, LP_X, LP_W, LS_B, LS_F2, LS_W, 1,
-                    4.0 * ((double)g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
+                    fused, -1, bsz * g.R * g.C + 4.0 * ((double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)
     if ((rc = gsplit(g, LP_W, LP_WS, g.C, LS_W)) != DION_OK) return rc;
   for (const LrGroup& g : P.groups)   // M = B - beta P W^T
-    if ((rc = gprod_split("lr_feedback", g, -beta, LP_WS, 1.f, LP_M, LS_W, 1,
-                          4.0 * (2.0 * g.R * g.C + (double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
+    if ((rc = gprod_split("lr_feedback", g, -beta, LP_WS, 1.f, LP_M, LS_W, 1, fused,
+                          (bsz + 4.0) * g.R * g.C + 4.0 * ((double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   if (mode == DION_LOWRANK_QR) {
     if ((rc = cholqr3(LP_W, LP_W2, LP_Q, false, LS_W, LS_L3, LS_G0)) != DION_OK) return rc;
   } else {
@@ -1899,7 +1915,7 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
     if ((rc = gsplit(g, LP_Q, LP_QS, g.C, LS_G2)) != DION_OK) return rc;
   const double ob = (double)dtype_bytes(out_dtype);
   for (const LrGroup& g : P.groups)   // D = P Q^T, in the output dtype
-    if ((rc = gprod_split("lr_update", g, 1.f, LP_QS, 0.f, LP_D, LS_G2, out_dtype,
+    if ((rc = gprod_split("lr_update", g, 1.f, LP_QS, 0.f, LP_D, LS_G2, out_dtype, false,
                           ob * g.R * g.C + 4.0 * ((double)g.R * g.r + (double)g.C * g.r))) != DION_OK) return rc;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail("kernel launch", e);

@@ -109,6 +109,7 @@ enum { LG_RC = 0, LG_KC = 1 };
 #define LG_GLOBAL __attribute__((address_space(1)))
 typedef float lg_float4 __attribute__((ext_vector_type(4)));
 typedef uint32_t lg_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t lg_u32x4 __attribute__((ext_vector_type(4)));
 
 // A K-stage of one operand: LG_TILE rows (of op(X)'s M or N side) x LG_BK k,
 // 16 values per thread.  KC: stored with k contiguous (element (r, k) at
@@ -190,6 +191,67 @@ struct LgStage {
   }
 };
 
+// The 16-bit gradient G (bf16, gfmt 0, or fp16, gfmt 2) of the residual
+// buffer B = fl32(M + G), loaded beside a stage of M in LgStage's element
+// order, so that the products that read B take M and G instead of a stored B
+// (same rounding: one fl32 addition per element).
+template <int MODE>
+struct LgGrad {
+  static constexpr bool KC = MODE == LG_KC;
+  uint32_t w[8];   // two values per word, element i in half i & 1 of word i / 2
+  __device__ __forceinline__ void load(const uint16_t* g, int ld, int rows, int ks, int r0, int k0, bool vec) {
+    const int t = threadIdx.x;
+    const bool whole = vec && r0 + LG_TILE <= rows && k0 + LG_BK <= ks;
+    if (KC) {   // row r0 + t/2, k0 + (t&1)*16 .. +15 (16-byte aligned rows: ld a multiple of 8)
+      const int r = r0 + (t >> 1), k = k0 + (t & 1) * 16;
+      const uint16_t LG_GLOBAL* q = (const uint16_t LG_GLOBAL*)g + (size_t)r * ld + k;
+      if (whole) {
+        const lg_u32x4 a = ((const lg_u32x4 LG_GLOBAL*)q)[0], b = ((const lg_u32x4 LG_GLOBAL*)q)[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w[i] = a[i];
+          w[4 + i] = b[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t lo = (r < rows && k + 2 * i < ks) ? q[2 * i] : 0u;
+          const uint32_t hi = (r < rows && k + 2 * i + 1 < ks) ? q[2 * i + 1] : 0u;
+          w[i] = lo | (hi << 16);
+        }
+      }
+    } else {    // rows k0 + (t>>5)*4 + i, columns r0 + (t&31)*4 .. +3 (8-byte aligned: ld a multiple of 4)
+      const int r = r0 + (t & 31) * 4, k = k0 + (t >> 5) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t LG_GLOBAL* q = (const uint16_t LG_GLOBAL*)g + (size_t)(k + i) * ld + r;
+        if (whole) {
+          const lg_u32x2 x = *(const lg_u32x2 LG_GLOBAL*)q;
+          w[2 * i] = x[0];
+          w[2 * i + 1] = x[1];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t lo = (k + i < ks && r + 2 * j < rows) ? q[2 * j] : 0u;
+            const uint32_t hi = (k + i < ks && r + 2 * j + 1 < rows) ? q[2 * j + 1] : 0u;
+            w[2 * i + j] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+  }
+  // v <- fl32(v + G), and the largest |v| into mx
+  __device__ __forceinline__ void add(float (&v)[16], int gfmt, float& mx) const {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const float g = gfmt == 0 ? __uint_as_float(h << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+      v[i] = __fadd_rn(v[i], g);
+      mx = fmaxf(mx, fabsf(v[i]));
+    }
+  }
+};
+
 // The block's tile (x, y) and batch entry z.  Blocks are dealt to the 8 XCDs
 // round-robin by linear id; they are renumbered so that each XCD runs a
 // contiguous run of tiles in (x, y, z) order, x fastest: the N tiles of one
@@ -228,13 +290,13 @@ __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
 // elements 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g
 // + 4 (lane / 32) .. + 3; a lane thus reads and writes four columns of a row
 // at once.  C (ld ldc, from element coff) = alpha 2^-lab acc (+ beta C with
-// READC, fp32 only), written as out_fmt; every read of C is issued before
-// any write.  With slot, the block's largest |value| raises *slot.  Every
-// thread calls.
+// READC, fp32 only; with G, beta fl32(C + G) for the 16-bit G laid out as C),
+// written as out_fmt; every read of C is issued before any write.  With
+// slot, the block's largest |value| raises *slot.  Every thread calls.
 template <bool READC>
 __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab,
                                             float alpha, float beta, void* Cp, int ldc, size_t coff, int out_fmt,
-                                            unsigned* slot) {
+                                            unsigned* slot, const uint16_t* G, int gfmt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool vec = (N & 3) == 0 && (ldc & 3) == 0 && ((uintptr_t)Cp & 15) == 0 && (coff & 3) == 0;
@@ -262,6 +324,21 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j) cv[a][b][4 * g + j] = (row < M && col + j < N) ? C32[o + j] : 0.f;
+        }
+        if (readc && G) {   // C <- fl32(C + G): the buffer B formed from M and G
+          uint32_t h[4];
+          const uint16_t LG_GLOBAL* gp = (const uint16_t LG_GLOBAL*)G + coff + o;
+          if (vec && ((uintptr_t)G & 7) == 0 && row < M && col + 4 <= N) {
+            const lg_u32x2 x = *(const lg_u32x2 LG_GLOBAL*)gp;
+            h[0] = x[0] & 0xFFFFu; h[1] = x[0] >> 16; h[2] = x[1] & 0xFFFFu; h[3] = x[1] >> 16;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = (row < M && col + j < N) ? gp[j] : 0u;
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            cv[a][b][4 * g + j] = __fadd_rn(cv[a][b][4 * g + j], gfmt == 0 ? __uint_as_float(h[j] << 16)
+                                                                           : (float)__builtin_bit_cast(_Float16, (uint16_t)h[j]));
         }
       }
   float mx = 0.f;
@@ -326,7 +403,8 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
                                                  int lda, const float* const* __restrict__ Bs, int ldb,
                                                  void* const* __restrict__ Cs, int ldc,
                                                  unsigned* const* __restrict__ amax, int sa, int sb, int sc,
-                                                 int out_fmt, int kchunk, int lower_only) {
+                                                 int out_fmt, int kchunk, int lower_only,
+                                                 const uint16_t* const* __restrict__ Gs, int gfmt, int gslot) {
   constexpr int NT = F16 ? 2 : 3;
   __shared__ __attribute__((aligned(16))) uint16_t sA[NT * LG_TERM], sB[NT * LG_TERM];
   // kchunk > 0: K split into chunks, chunk p of product z at batch index
@@ -357,14 +435,21 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
 
   LgStage<A_MODE, F16> ga;
   LgStage<B_MODE, F16> gb;
+  // with Gs, A is M and the operand is B = fl32(M + G), formed as loaded
+  const uint16_t* G = Gs ? Gs[z] : nullptr;
+  const bool vecg = (lda & (A_MODE == LG_KC ? 7 : 3)) == 0 && ((uintptr_t)G & 15) == 0;
+  LgGrad<A_MODE> gg;
+  float bmax = 0.f;
   const int nk = (kend - kbeg + LG_BK - 1) / LG_BK;
   auto load = [&](int k0) {
     ga.load(A, lda, M, kend, m0, k0, veca);
+    if (G) gg.load(G, lda, M, kend, m0, k0, vecg);
     gb.load(B, ldb, N, kend, n0, k0, vecb);
   };
   load(kbeg);
   for (int kt = 0; kt < nk; ++kt) {
     __syncthreads();   // every wave is done with the previous stage
+    if (G) gg.add(ga.v, gfmt, bmax);
     ga.store(sA, scale_a);
     gb.store(sB, scale_b);
     __syncthreads();
@@ -405,17 +490,28 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
     }
   }
   lg_epilogue<false>(acc, M, N, m0, n0, la + lb, alpha, 0.f, Cs[z], ldc, (size_t)part * M * N, out_fmt,
-              sc >= 0 ? slots + sc : nullptr);
+              sc >= 0 ? slots + sc : nullptr, nullptr, 0);
+  if (G && gslot >= 0) {   // the largest |B| over this block's share of it
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o, 64));
+    if (lane == 0) red[wave] = bmax;
+    __syncthreads();
+    if (tid == 0) {
+      const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (m > 0.f) atomicMax(slots + gslot, __float_as_uint(m));
+    }
+  }
 }
 
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
                     const float* const* B, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
-                    int out_fmt, int count, hipStream_t s) {
+                    int out_fmt, const uint16_t* const* G, int gfmt, int gslot, int count, hipStream_t s) {
   const int lda = ta ? m : k, ldb = tb ? k : n, ldc = n;
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
 #define DION_LRG(AK, BK, F)                                                                                          \
   hipLaunchKernelGGL((k_lr_gemm<AK, BK, F>), grid, dim3(256), 0, s, m, n, k, alpha, A, lda, B, ldb, C, ldc,   \
-                     amax, sa, sb, sc, out_fmt, 0, 0)
+                     amax, sa, sb, sc, out_fmt, 0, 0, G, gfmt, gslot)
   if (f16) {
     if (!ta && tb) DION_LRG(LG_KC, LG_KC, true);
     else if (!ta && !tb) DION_LRG(LG_KC, LG_RC, true);
@@ -480,7 +576,8 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
                                                         float alpha, const uint16_t* const* __restrict__ As,
                                                         const uint16_t* const* __restrict__ Bs, float beta,
                                                         void* const* __restrict__ Cs, unsigned* const* __restrict__ amax,
-                                                        int sa, int sb, int sc, int out_fmt) {
+                                                        int sa, int sb, int sc, int out_fmt,
+                                                        const uint16_t* const* __restrict__ Gs, int gfmt) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[LD_STAGES * LD_STAGE / 2];
   const int z = blockIdx.z;
   unsigned* slots = amax[z];
@@ -563,16 +660,17 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
         for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[0][b], fa[0][a], acc[a][b], 0, 0, 0);
     }
   }
-  lg_epilogue<true>(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], N, 0, out_fmt, sc >= 0 ? slots + sc : nullptr);
+  lg_epilogue<true>(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], N, 0, out_fmt, sc >= 0 ? slots + sc : nullptr,
+                    Gs ? Gs[z] : nullptr, gfmt);
 }
 
 void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
                           const uint16_t* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb,
-                          int sc, int out_fmt, int count, hipStream_t s) {
+                          int sc, int out_fmt, const uint16_t* const* G, int gfmt, int count, hipStream_t s) {
   (void)k;
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
   hipLaunchKernelGGL(k_lr_gemm_dma, grid, dim3(256), 0, s, m, n, ldp, ldp, rows_a, rows_b, alpha, A, B, beta, C, amax,
-                     sa, sb, sc, out_fmt);
+                     sa, sb, sc, out_fmt, G, gfmt);
 }
 
 void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, unsigned* const* amax, int sf, int count,
@@ -580,7 +678,7 @@ void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, uns
   const int parts = (rows + LR_GRAM_CHUNK - 1) / LR_GRAM_CHUNK;
   const dim3 grid((r + LG_TILE - 1) / LG_TILE, (r + LG_TILE - 1) / LG_TILE, count * parts);
   hipLaunchKernelGGL((k_lr_gemm<LG_RC, LG_RC, true>), grid, dim3(256), 0, s, r, r, rows, 1.f, F, r, F, r,
-                     (void* const*)S, r, amax, sf, sf, -1, 1, LR_GRAM_CHUNK, 1);
+                     (void* const*)S, r, amax, sf, sf, -1, 1, LR_GRAM_CHUNK, 1, nullptr, 0, -1);
 }
 
 // Split a batch of row-major fp32 matrices (rows x k) into fp16 hi and lo

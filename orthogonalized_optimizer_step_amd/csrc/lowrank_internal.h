@@ -74,16 +74,20 @@ void launch_lr_colnorm(const LrDesc* d, int nmat, hipStream_t s);
 // fp16 operands (f16) or three-term bf16 ones.  The fp16 operands' scales
 // come from slots sa and sb; sc >= 0 raises slot sc with the result's
 // largest |value|.  out_fmt: 1 fp32, 0 bf16 or 2 fp16 (round to nearest even).
+// With G (16-bit gradients laid out as A, gfmt 0 bf16 or 2 fp16), the A
+// operand is fl32(A + G), and gslot >= 0 raises slot gslot with its largest
+// |value|.
 void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha, const float* const* A,
                     const float* const* B, void* const* C, unsigned* const* amax, int sa, int sb, int sc,
-                    int out_fmt, int count, hipStream_t s);
+                    int out_fmt, const uint16_t* const* G, int gfmt, int gslot, int count, hipStream_t s);
 // C (m x n, ld n) = alpha A B^T + beta C with both operands split ahead by
 // launch_lr_split16: A as m rows (padded to rows_a) and B as n rows (padded
 // to rows_b) of k values (fp16 hi and lo, row length ldp); out_fmt 1 fp32
-// (with beta), 0 bf16 or 2 fp16 (beta must be 0).
+// (with beta), 0 bf16 or 2 fp16 (beta must be 0).  With G (16-bit, laid out
+// as C), beta C is beta fl32(C + G).
 void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
                           const uint16_t* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb,
-                          int sc, int out_fmt, int count, hipStream_t s);
+                          int sc, int out_fmt, const uint16_t* const* G, int gfmt, int count, hipStream_t s);
 // The Gram F^T F of `count` row-major fp32 factors F (rows x r, F16 terms
 // with the scale of slot sf): the rows split into chunks of LR_GRAM_CHUNK,
 // chunk p's r x r partial written at S + p r r (only the tiles on or below

@@ -48,11 +48,12 @@ void launch_lr_cholinv(const LrDesc*, int, bool, bool, bool, float, int, hipStre
 void launch_lr_gram(int, int, const float* const*, float* const*, unsigned* const*, int, int, hipStream_t) { std::abort(); }
 void launch_lr_colnorm(const LrDesc*, int, hipStream_t) { std::abort(); }
 void launch_lr_gemm(bool, bool, bool, int, int, int, float, const float* const*, const float* const*, void* const*,
-                    unsigned* const*, int, int, int, int, int, hipStream_t) {
+                    unsigned* const*, int, int, int, int, const uint16_t* const*, int, int, int, hipStream_t) {
   std::abort();
 }
 void launch_lr_gemm_split(int, int, int, int, int, int, float, const uint16_t* const*, const uint16_t* const*, float,
-                          void* const*, unsigned* const*, int, int, int, int, int, hipStream_t) {
+                          void* const*, unsigned* const*, int, int, int, int, const uint16_t* const*, int, int,
+                          hipStream_t) {
   std::abort();
 }
 void launch_lr_split16(const float* const*, uint16_t* const*, int, int, int, int, unsigned* const*, int, int,
