@@ -290,13 +290,45 @@ __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
 // elements 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g
 // + 4 (lane / 32) .. + 3; a lane thus reads and writes four columns of a row
 // at once.  C (ld ldc, from element coff) = alpha 2^-lab acc (+ beta C with
-// READC, fp32 only; with G, beta fl32(C + G) for the 16-bit G laid out as C),
+// READC, fp32 only; with useg, beta fl32(C + G) for the 16-bit G values gw
+// that lg_read_g read),
 // written as out_fmt; every read of C is issued before any write.  With
 // slot, the block's largest |value| raises *slot.  Every thread calls.
+// The 16-bit G values under the tile in the accumulator layout (the four
+// columns of group (a, b, g) in two words), read ahead by the split-operand
+// kernel so that their latency hides behind its main loop.
+typedef uint32_t LgGradTile[2][2][4][2];
+__device__ __forceinline__ void lg_read_g(LgGradTile& gw, int M, int N, int m0, int n0, const uint16_t* G) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool vec = (N & 3) == 0 && ((uintptr_t)G & 7) == 0;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = m0 + wm * 64 + a * 32 + (lane & 31);
+        const int col = n0 + wn * 64 + b * 32 + 8 * g + 4 * (lane >> 5);
+        const uint16_t LG_GLOBAL* gp = (const uint16_t LG_GLOBAL*)G + (size_t)row * N + col;
+        if (vec && row < M && col + 4 <= N) {
+          const lg_u32x2 x = *(const lg_u32x2 LG_GLOBAL*)gp;
+          gw[a][b][g][0] = x[0];
+          gw[a][b][g][1] = x[1];
+        } else {
+          uint32_t h[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) h[j] = (row < M && col + j < N) ? gp[j] : 0u;
+          gw[a][b][g][0] = h[0] | (h[1] << 16);
+          gw[a][b][g][1] = h[2] | (h[3] << 16);
+        }
+      }
+}
+
 template <bool READC>
 __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab,
                                             float alpha, float beta, void* Cp, int ldc, size_t coff, int out_fmt,
-                                            unsigned* slot, const uint16_t* G, int gfmt) {
+                                            unsigned* slot, const LgGradTile& gw, bool useg, int gfmt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const bool vec = (N & 3) == 0 && (ldc & 3) == 0 && ((uintptr_t)Cp & 15) == 0 && (coff & 3) == 0;
@@ -325,20 +357,13 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
 #pragma unroll
           for (int j = 0; j < 4; ++j) cv[a][b][4 * g + j] = (row < M && col + j < N) ? C32[o + j] : 0.f;
         }
-        if (readc && G) {   // C <- fl32(C + G): the buffer B formed from M and G
-          uint32_t h[4];
-          const uint16_t LG_GLOBAL* gp = (const uint16_t LG_GLOBAL*)G + coff + o;
-          if (vec && ((uintptr_t)G & 7) == 0 && row < M && col + 4 <= N) {
-            const lg_u32x2 x = *(const lg_u32x2 LG_GLOBAL*)gp;
-            h[0] = x[0] & 0xFFFFu; h[1] = x[0] >> 16; h[2] = x[1] & 0xFFFFu; h[3] = x[1] >> 16;
-          } else {
+        if (readc && useg) {   // C <- fl32(C + G): the buffer B formed from M and G
 #pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = (row < M && col + j < N) ? gp[j] : 0u;
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t h = (gw[a][b][g][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            cv[a][b][4 * g + j] = __fadd_rn(cv[a][b][4 * g + j], gfmt == 0 ? __uint_as_float(h << 16)
+                                                                           : (float)__builtin_bit_cast(_Float16, (uint16_t)h));
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            cv[a][b][4 * g + j] = __fadd_rn(cv[a][b][4 * g + j], gfmt == 0 ? __uint_as_float(h[j] << 16)
-                                                                           : (float)__builtin_bit_cast(_Float16, (uint16_t)h[j]));
         }
       }
   float mx = 0.f;
@@ -399,7 +424,7 @@ __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N,
 // K x M (op = T).  B_MODE LG_KC: B is stored N x K (op = T); LG_RC: K x N
 // (op = N).
 template <int A_MODE, int B_MODE, bool F16>
-__global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alpha, const float* const* __restrict__ As,
+__global__ __launch_bounds__(256, 3) void k_lr_gemm(int M, int N, int K, float alpha, const float* const* __restrict__ As,
                                                  int lda, const float* const* __restrict__ Bs, int ldb,
                                                  void* const* __restrict__ Cs, int ldc,
                                                  unsigned* const* __restrict__ amax, int sa, int sb, int sc,
@@ -489,8 +514,9 @@ __global__ __launch_bounds__(256) void k_lr_gemm(int M, int N, int K, float alph
           }
     }
   }
+  const LgGradTile gnone = {};
   lg_epilogue<false>(acc, M, N, m0, n0, la + lb, alpha, 0.f, Cs[z], ldc, (size_t)part * M * N, out_fmt,
-              sc >= 0 ? slots + sc : nullptr, nullptr, 0);
+              sc >= 0 ? slots + sc : nullptr, gnone, false, 0);
   if (G && gslot >= 0) {   // the largest |B| over this block's share of it
     __shared__ float red[4];
 #pragma unroll
@@ -620,6 +646,11 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
   const int nk = K / LG_BK;   // K = ldp, a multiple of 32
+  // G (the buffer update's B = fl32(C + G)) read first: the loads complete
+  // while the main loop runs (the first stage's wait covers them)
+  const bool pg = Gs && out_fmt == 1 && beta != 0.f;
+  LgGradTile gw;
+  if (pg) lg_read_g(gw, M, N, m0, n0, Gs[z]);
 #pragma unroll
   for (int kt = 0; kt < LD_STAGES - 1; ++kt)
     if (kt < nk) issue(kt);
@@ -661,7 +692,7 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
     }
   }
   lg_epilogue<true>(acc, M, N, m0, n0, la + lb, alpha, beta, Cs[z], N, 0, out_fmt, sc >= 0 ? slots + sc : nullptr,
-                    Gs ? Gs[z] : nullptr, gfmt);
+                    gw, pg, gfmt);
 }
 
 void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
