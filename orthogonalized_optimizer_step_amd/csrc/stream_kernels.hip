@@ -16,6 +16,13 @@
 
 namespace dion {
 
+// Global-address-space pointers (vmcnt only; flat accesses also count
+// against the LDS wait counter) and native vector types for them.
+#define DION_SGLOBAL __attribute__((address_space(1)))
+typedef uint32_t pk_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t pk_u32x4 __attribute__((ext_vector_type(4)));
+typedef float pk_f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint16_t bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -341,8 +348,12 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
   if (g >= total_rows) return;
   const MatDesc& d = descs[mat_of_row(descs, nmat, g)];
   const int64_t r = g - d.row0;
-  float* E = (float*)d.M + r * d.C;
-  uint16_t* out = (uint16_t*)d.out + r * d.C;
+  // global-address-space accesses: flat ones would also count against the
+  // LDS wait counter, so the row's closing reduction would wait for its stores
+  float DION_SGLOBAL* E = (float DION_SGLOBAL*)d.M + r * d.C;
+  uint16_t DION_SGLOBAL* out = (uint16_t DION_SGLOBAL*)d.out + r * d.C;
+  const uint16_t DION_SGLOBAL* G16 = (const uint16_t DION_SGLOBAL*)d.grad + r * d.C;
+  const float DION_SGLOBAL* G32 = (const float DION_SGLOBAL*)d.grad + r * d.C;
   double s = 0.0;
   SqAcc A;
   auto key_of = [&](float m) {
@@ -352,36 +363,34 @@ __global__ __launch_bounds__(256) void k_momentum_keys(const MatDesc* __restrict
   const bool vec = (d.C & 3) == 0;
   if (vec) {
     for (int c = lane * 4; c < d.C; c += 256) {
-      float4 e = *(float4*)(E + c);
+      const pk_f32x4 e = *(const pk_f32x4 DION_SGLOBAL*)(E + c);
       float gv[4];
       if (sizeof(GT) == 2) {
-        const uint2 b = *(const uint2*)((const uint16_t*)d.grad + r * d.C + c);
-        gv[0] = __uint_as_float(b.x << 16);
-        gv[1] = __uint_as_float(b.x & 0xFFFF0000u);
-        gv[2] = __uint_as_float(b.y << 16);
-        gv[3] = __uint_as_float(b.y & 0xFFFF0000u);
+        const pk_u32x2 b = *(const pk_u32x2 DION_SGLOBAL*)(G16 + c);
+        gv[0] = __uint_as_float(b[0] << 16);
+        gv[1] = __uint_as_float(b[0] & 0xFFFF0000u);
+        gv[2] = __uint_as_float(b[1] << 16);
+        gv[3] = __uint_as_float(b[1] & 0xFFFF0000u);
       } else {
-        const float4 b = *(const float4*)((const float*)d.grad + r * d.C + c);
-        gv[0] = b.x; gv[1] = b.y; gv[2] = b.z; gv[3] = b.w;
+        const pk_f32x4 b = *(const pk_f32x4 DION_SGLOBAL*)(G32 + c);
+        gv[0] = b[0]; gv[1] = b[1]; gv[2] = b[2]; gv[3] = b[3];
       }
-      float m[4] = {__fadd_rn(__fmul_rn(beta, e.x), gv[0]), __fadd_rn(__fmul_rn(beta, e.y), gv[1]),
-                    __fadd_rn(__fmul_rn(beta, e.z), gv[2]), __fadd_rn(__fmul_rn(beta, e.w), gv[3])};
-      *(float4*)(E + c) = make_float4(m[0], m[1], m[2], m[3]);
+      float m[4] = {__fadd_rn(__fmul_rn(beta, e[0]), gv[0]), __fadd_rn(__fmul_rn(beta, e[1]), gv[1]),
+                    __fadd_rn(__fmul_rn(beta, e[2]), gv[2]), __fadd_rn(__fmul_rn(beta, e[3]), gv[3])};
+      *(pk_f32x4 DION_SGLOBAL*)(E + c) = pk_f32x4{m[0], m[1], m[2], m[3]};
       if (write_out == 1) {
-        uint2 o;
-        o.x = (uint32_t)bf16_rne(m[0]) | ((uint32_t)bf16_rne(m[1]) << 16);
-        o.y = (uint32_t)bf16_rne(m[2]) | ((uint32_t)bf16_rne(m[3]) << 16);
-        *(uint2*)(out + c) = o;
+        const pk_u32x2 o = {(uint32_t)bf16_rne(m[0]) | ((uint32_t)bf16_rne(m[1]) << 16),
+                            (uint32_t)bf16_rne(m[2]) | ((uint32_t)bf16_rne(m[3]) << 16)};
+        *(pk_u32x2 DION_SGLOBAL*)(out + c) = o;
       } else if (write_out == 2) {
-        *(uint2*)(out + c) = make_uint2(0u, 0u);
+        *(pk_u32x2 DION_SGLOBAL*)(out + c) = pk_u32x2{0u, 0u};
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) key_of(m[q]);
     }
   } else {
     for (int c = lane; c < d.C; c += 64) {
-      const float gv = sizeof(GT) == 2 ? bf16_to_f32(((const uint16_t*)d.grad)[r * d.C + c])
-                                       : ((const float*)d.grad)[r * d.C + c];
+      const float gv = sizeof(GT) == 2 ? bf16_to_f32(G16[c]) : G32[c];
       const float m = __fadd_rn(__fmul_rn(beta, E[c]), gv);
       E[c] = m;
       if (write_out) out[c] = write_out == 1 ? bf16_rne(m) : (uint16_t)0;
@@ -599,9 +608,6 @@ __global__ __launch_bounds__(256) void k_pack(const MatDesc* __restrict__ descs,
 // as 8-column chunks straight from registers, ST through a 64 x 65 fp32 LDS
 // tile read as 8-row column chunks (both LDS passes are bank-conflict-free).
 typedef _Float16 half8s __attribute__((ext_vector_type(8)));
-typedef uint32_t pk_u32x4 __attribute__((ext_vector_type(4)));
-typedef float pk_f32x4 __attribute__((ext_vector_type(4)));
-#define DION_SGLOBAL __attribute__((address_space(1)))
 template <typename InT>
 __global__ __launch_bounds__(256) void k_pack16(const MatDesc* __restrict__ descs, const int* __restrict__ mats,
                                                 const int* __restrict__ prefix, int nmat, int total,
