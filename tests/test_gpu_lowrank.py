@@ -93,6 +93,26 @@ def test_lowrank_buffer_bit_exact_beta0(dion):
 
 
 @pytest.mark.parametrize("mode", ["qr", "colnorm"])
+@pytest.mark.parametrize("grad_dtype", [torch.bfloat16, torch.float16])
+def test_lowrank_formed_buffer_matches_stored_buffer(dion, mode, grad_dtype):
+    """16-bit gradients have B = fl32(M + G) formed where it is read; fp32
+    gradients have it stored by a pass first.  The same gradient values given
+    both ways must give bit-identical buffers, right factors and updates (the
+    ragged shapes take the masked loads, the 256-multiples the vector ones)."""
+    shapes = SHAPES + [(512, 384), (384, 512), (1024, 256)]
+    Ms, Gs, Qs = make(shapes, 64, 14, grad_dtype)
+    G32 = [g.float() for g in Gs]   # exact: every 16-bit value is an fp32 value
+    for beta in (0.1, 1.0):
+        a = run(dion, Ms, Gs, Qs, beta, mode, out_dtype=torch.bfloat16)
+        b = run(dion, Ms, G32, Qs, beta, mode, out_dtype=torch.bfloat16)
+        for x, y in zip(a, b):
+            for i, s in enumerate(shapes):
+                assert torch.equal(x[i].view(torch.int16) if x[i].dtype == torch.bfloat16 else x[i].view(torch.int32),
+                                   y[i].view(torch.int16) if y[i].dtype == torch.bfloat16 else y[i].view(torch.int32)), \
+                    (s, beta, mode, grad_dtype)
+
+
+@pytest.mark.parametrize("mode", ["qr", "colnorm"])
 def test_lowrank_bf16_output_and_partial_isometry(dion, mode):
     shapes = [(300, 200), (200, 300), (512, 512)]
     Ms, Gs, Qs = make(shapes, 24, 13)
