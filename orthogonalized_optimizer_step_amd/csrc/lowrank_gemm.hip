@@ -284,19 +284,10 @@ __device__ __forceinline__ uint16_t lg_bf16_rne(float v) {
 
 }  // namespace
 
-// The epilogue of a 128 x 128 tile held by four waves of 64 x 64 (2 x 2 MFMA
-// blocks), whose MFMAs take the B operand first so that the accumulators
-// hold C^T: block (a, b) holds row m0 + wm 64 + a 32 + (lane & 31) and, in
-// elements 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g
-// + 4 (lane / 32) .. + 3; a lane thus reads and writes four columns of a row
-// at once.  C (ld ldc, from element coff) = alpha 2^-lab acc (+ beta C with
-// READC, fp32 only; with useg, beta fl32(C + G) for the 16-bit G values gw
-// that lg_read_g read),
-// written as out_fmt; every read of C is issued before any write.  With
-// slot, the block's largest |value| raises *slot.  Every thread calls.
-// The 16-bit G values under the tile in the accumulator layout (the four
-// columns of group (a, b, g) in two words), read ahead by the split-operand
-// kernel so that their latency hides behind its main loop.
+// The 16-bit G values (laid out as C, ld N) under a 128 x 128 tile in the
+// accumulator layout of lg_epilogue below (the four columns of group (a, b, g)
+// in two words), read ahead by the split-operand kernel so that their latency
+// hides behind its main loop.
 typedef uint32_t LgGradTile[2][2][4][2];
 __device__ __forceinline__ void lg_read_g(LgGradTile& gw, int M, int N, int m0, int n0, const uint16_t* G) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -325,6 +316,16 @@ __device__ __forceinline__ void lg_read_g(LgGradTile& gw, int M, int N, int m0, 
       }
 }
 
+// The epilogue of a 128 x 128 tile held by four waves of 64 x 64 (2 x 2 MFMA
+// blocks), whose MFMAs take the B operand first so that the accumulators
+// hold C^T: block (a, b) holds row m0 + wm 64 + a 32 + (lane & 31) and, in
+// elements 4g .. 4g + 3, the four consecutive columns n0 + wn 64 + b 32 + 8g
+// + 4 (lane / 32) .. + 3; a lane thus reads and writes four columns of a row
+// at once.  C (ld ldc, from element coff) = alpha 2^-lab acc (+ beta C with
+// READC, fp32 only; with useg, beta fl32(C + G) for the 16-bit G values gw
+// that lg_read_g read), written as out_fmt; every read of C is issued before
+// any write.  With slot, the block's largest |value| raises *slot.  Every
+// thread calls.
 template <bool READC>
 __device__ __forceinline__ void lg_epilogue(floatx16 (&acc)[2][2], int M, int N, int m0, int n0, int lab,
                                             float alpha, float beta, void* Cp, int ldc, size_t coff, int out_fmt,
