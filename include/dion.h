@@ -272,7 +272,8 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
  * method's contract (the factor is not unique): the output is finite but
  * unspecified.
  *   M[i]      device R x C fp32 buffer, updated in place
- *   grad[i]   device R x C of grad_dtype (bf16, fp32 or fp16), read only
+ *   grad[i]   device R x C of grad_dtype (bf16, fp32 or fp16), read only;
+ *             must not overlap M[i]
  *   Q[i]      device C x r fp32 right factor: read as the previous one,
  *             overwritten with the new one; must not overlap M[i]
  *   out[i]    device R x C of out_dtype; must not overlap M[i]
@@ -283,8 +284,11 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
  * three bf16 terms (six MFMA products, fp32 accuracy: its error is amplified
  * by the orthogonalization that follows), every other product on two fp16
  * terms under a power-of-two scale taken from the operand's largest |value|
- * (three MFMA products, 22 significant bits).  The update is written in
- * out_dtype by the last product (round to nearest even).  All memory is the
+ * (three MFMA products, 22 significant bits).  With a 16-bit gradient, B is
+ * never stored: the products that read it add M and G as they load them
+ * (the same single rounding), and M takes the new buffer in the last of
+ * them.  The update is written in out_dtype by the last product (round to
+ * nearest even).  All memory is the
  * caller's workspace; no handle or other state is kept.  Asynchronous on
  * `stream`. */
 typedef enum { DION_LOWRANK_QR = 0, DION_LOWRANK_COLNORM = 1 } dion_lowrank_mode;

@@ -2307,6 +2307,9 @@ int dion_lowrank_step(float* const* M, const void* const* grad, float* const* Q,
     const size_t n = (size_t)P.R[i] * P.C[i];
     if (overlaps(out[i], n * oes, M[i], n * 4)) return fail(DION_E_INVAL, "out must not overlap M");
     if (overlaps(Q[i], (size_t)P.C[i] * P.r[i] * 4, M[i], n * 4)) return fail(DION_E_INVAL, "Q must not overlap M");
+    // M is rewritten while the gradient is still read (by other blocks)
+    if (overlaps(grad[i], n * dtype_bytes(grad_dtype), M[i], n * 4))
+      return fail(DION_E_INVAL, "grad must not overlap M");
   }
   return run_lr(P, M, grad, Q, out, batch, grad_dtype, out_dtype, beta, mode, workspace, workspace_bytes,
                 (hipStream_t)stream);

@@ -209,6 +209,7 @@ def test_lowrank_validation_errors_before_launch():
     assert call(batch=0) == -1
     assert call(O=ptrs(0x10000, 0x80000)) == -1          # out overlaps M
     assert call(Q=ptrs(0x10000 + 64, 0x60000)) == -1     # Q overlaps M
+    assert call(G=ptrs(0x10000 + 128, 0x40000)) == -1    # grad overlaps M
     assert call(M=ptrs(0, 0x20000)) == -1                # NULL matrix
     assert call(nbytes=need - 1) == -3                   # workspace too small
     assert call(ws=0x100001) == -3                       # misaligned
