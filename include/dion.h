@@ -88,10 +88,12 @@ typedef enum { DION_BF16 = 0, DION_FP32 = 1, DION_FP16 = 2 } dion_dtype;
  *     (about 1.4e-2 at 12 and 2e-2 at 16 iterations on small blocks).  A
  *     call that would run a matrix on this path with more than 12 iterations,
  *     with slopes a_k / s multiplying to more than 3.4445^12, or with
- *     keep_schedule and a run of more than 5 iterations between restarts is
- *     refused (DION_E_UNSUPPORTED); DION_PREC_FP64 takes it.  Matrices with a
- *     Gram side of at most 64 and a long side of at most 1024, or a Gram side
- *     of at most 16, run in fp64 in one launch on every precision setting.
+ *     keep_schedule and a run of more than two iterations between restarts
+ *     where a run is longer than 5 iterations or the slopes multiply to more
+ *     than 3.4445^6 is refused (DION_E_UNSUPPORTED); DION_PREC_FP64 takes
+ *     it.  Matrices with a Gram side of at most 64 and a long side of at
+ *     most 1024, or a Gram side of at most 16, run in fp64 in one launch on
+ *     every precision setting.
  *   DION_PREC_FP64: fp64 arithmetic throughout (error ~1e-12; gate 1e-4).
  *   DION_PREC_AUTO: FP64 for DION_FP32 inputs of dion_orth_batched, MFMA16
  *     otherwise (bf16 and fp16). */
@@ -139,7 +141,11 @@ typedef struct {
  *                 1: run the schedule as given; runs longer than two
  *                 iterations take two-term operands (about 1e-3 without
  *                 restarts, at about three times the MFMA work of those
- *                 runs).  dion_restart_points and the useful-FLOP count
+ *                 runs).  Two terms hold the rounding of such a run only
+ *                 while few iterations follow it: the slopes a_k / s of the
+ *                 whole schedule must multiply to at most 3.4445^6 (six
+ *                 iterations of the fixed quintic) and no run may exceed 5
+ *                 iterations, else the call is refused.  dion_restart_points and the useful-FLOP count
  *                 follow the schedule as given either way. */
 typedef struct {
   const float* ns_coeffs;

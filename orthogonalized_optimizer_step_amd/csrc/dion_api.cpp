@@ -75,10 +75,14 @@ constexpr int kMaxIter = 64;
 // rounding in the small singular directions by its slope a_k (safety folded
 // in).  Its 2e-2 gate is established up to twelve iterations whose slopes
 // multiply to at most the fixed quintic's 3.4445^12 and, for schedules kept as
-// given, runs of at most five iterations between restarts; calls that would put
-// a matrix on that path beyond this are refused (the FP64 path takes them).
+// given with a run of more than two iterations, runs of at most five
+// iterations between restarts and slopes multiplying to at most 3.4445^6 (a
+// kept run ahead of further iterations reached 2.5-3.2e-2 at eight iterations
+// of the fixed quintic, where the cut schedule stays under 7e-3); calls that
+// would put a matrix on that path beyond this are refused (the FP64 path takes
+// them).
 constexpr int kMfmaMaxIter = 12, kMfmaMaxKeptRun = 5;
-const double kMfmaMaxGain = std::pow(3.4445, 12);
+const double kMfmaMaxGain = std::pow(3.4445, 12), kMfmaMaxKeptGain = std::pow(3.4445, 6);
 
 // ------------------------------------------------------------ parameters
 struct Params {
@@ -418,9 +422,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     if (K > kMfmaMaxIter || gain > kMfmaMaxGain * (1.0 + 1e-9))
       return fail(DION_E_UNSUPPORTED, "the MFMA16 path holds its error bound up to 12 iterations with slopes a_k "
                                       "multiplying to at most 3.4445^12; use DION_PREC_FP64");
-    if (prm.keep_schedule && longest > kMfmaMaxKeptRun)
-      return fail(DION_E_UNSUPPORTED, "keep_schedule: runs of more than 5 iterations between restarts are outside "
-                                      "the MFMA16 path's error bound");
+    if (prm.keep_schedule && longest > 2 &&
+        (longest > kMfmaMaxKeptRun || gain > kMfmaMaxKeptGain * (1.0 + 1e-9)))
+      return fail(DION_E_UNSUPPORTED, "keep_schedule: a run of more than 5 iterations between restarts, or a kept "
+                                      "run in a schedule whose slopes a_k multiply to more than 3.4445^6, is "
+                                      "outside the MFMA16 path's error bound; use keep_schedule = 0 or DION_PREC_FP64");
   }
 
   // tables of the GEMM phases, over mf

@@ -270,7 +270,8 @@ def _orth_rc(shapes, dtype=_lib.DION_BF16, **kw):
 def test_mfma16_iteration_range_guard():
     """The MFMA16 path refuses schedules beyond the range its 2e-2 error bound is
     established for (more than 12 iterations, slopes multiplying to more than
-    3.4445^12, or kept runs of more than 5 iterations between restarts), with
+    3.4445^12, or a kept run of more than two iterations where a run exceeds 5
+    iterations or the slopes multiply to more than 3.4445^6), with
     DION_E_UNSUPPORTED before any launch; the FP64 path and matrices that take
     the one-launch fp64 kernel (Gram side <= 64 and long side <= 1024, or Gram
     side <= 16) accept them."""
@@ -279,7 +280,9 @@ def test_mfma16_iteration_range_guard():
     ws = -3   # DION_E_WORKSPACE: the plan was accepted, the (absent) workspace was not
     assert _orth_rc(big, n_iter=12, restart_every=2) == ws
     for kw in (dict(n_iter=13, restart_every=2), dict(n_iter=20), dict(coeffs=(5.0, -6.0, 2.0), n_iter=10),
-               dict(n_iter=6, keep_schedule=True), dict(n_iter=8, restart_mask=0b1, keep_schedule=True)):
+               dict(n_iter=6, keep_schedule=True), dict(n_iter=8, restart_mask=0b1, keep_schedule=True),
+               dict(n_iter=8, restart_mask=0b100100, keep_schedule=True),
+               dict(n_iter=7, restart_mask=0b10000, keep_schedule=True)):
         assert _orth_rc(big, **kw) == -2, kw
         assert _orth_rc(big, precision="fp64", **kw) == ws, kw
         assert _orth_rc(tiny, **kw) == ws, kw
@@ -290,6 +293,11 @@ def test_mfma16_iteration_range_guard():
     assert _orth_rc(big, coeffs=(3.6, -4.8, 2.0), n_iter=12, safety=1.05) == ws
     assert _orth_rc(big, coeffs=(3.6, -4.8, 2.0), n_iter=12) == -2
     assert _orth_rc(big, n_iter=5, keep_schedule=True) == ws
+    # kept runs: accepted up to six iterations of the fixed quintic, with lower
+    # slopes, or where no run is longer than two (keep changes nothing)
+    assert _orth_rc(big, n_iter=6, restart_mask=0b1, keep_schedule=True) == ws
+    assert _orth_rc(big, coeffs=(1.5, -0.5, 0.0), n_iter=8, restart_mask=0b100100, keep_schedule=True) == ws
+    assert _orth_rc(big, n_iter=8, restart_every=2, keep_schedule=True) == ws
     # the row-subset step (MFMA16 only) refuses the same schedules
     p, keep = dion._params(dion.QUINTIC, 13, 2, 0, 1.0, 0.125, "mfma16")
     fake = (ctypes.c_void_p * 1)(0x10000)

@@ -97,7 +97,7 @@ def test_small_ragged_mfma16(dion, sched):
 
 
 @pytest.mark.parametrize("sched", [dict(), dict(restart_mask=0b10, safety=1.01), dict(n_iter=6, restart_mask=0b1),
-                                   dict(n_iter=7, restart_threshold=1e5)])
+                                   dict(n_iter=6, restart_threshold=1e5)])
 def test_long_runs_cut_or_kept(dion, sched):
     """Schedules with runs of more than two iterations between restarts: cut by extra
     restarts (the default) or run as given with two-term operands (keep_schedule).  Both
