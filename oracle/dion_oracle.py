@@ -61,11 +61,11 @@ formula, selection criterion or worked example.  The readings taken here are:
       a_k^2.  A restart is taken after the iteration at which the product of
       these factors since the last restart first reaches tau.
 
-Parity unpinned by the pages: readings R4 (where the safety factor acts),
+Readings without a formula on the pages: R4 (where the safety factor acts),
 R8 and R14 (the error-feedback form), R11 (the weight update and its shape
-scale) and R12 (what the restart threshold measures) are readings of pages
-that state no formula; the functions implementing them are pinned against
-the mathematics below, not against a value the pages print.
+scale) and R12 (what the restart threshold measures).  The pages print no
+value to check them against; the functions implementing them are pinned
+against the mathematics below (closed forms, identities, scalar emulation).
 
 Parity pins (in tests/): SVD closed form U f^K(Sigma) V^T, textbook polar
 factor via the cubic Newton-Schulz map, the NS band invariant, equivalence with

@@ -36,9 +36,10 @@ The pages print no formula for the step.  The readings taken here are:
       r = min(rank, R, C).  Inputs of rank below r (B Q or W rank-deficient)
       are outside the method's contract: the factorization is not unique.
 
-Parity unpinned by the pages: D1 and D4 (the buffer's accumulation and the
-error-feedback form) and D5's QR sign convention are readings; the functions
-are pinned against the mathematics below.
+Readings without a formula on the pages: D1 and D4 (the buffer's
+accumulation and the error-feedback form) and D5's QR sign convention.  The
+pages print no value to check them against; the functions are pinned against
+the mathematics below.
 
 Parity pins (in tests/test_orthdion_pins.py): orthonormal factors and the
 positive-diagonal QR convention against LAPACK, exact recovery of the rank-r
