@@ -274,9 +274,12 @@ int dion_rowsubset_step_update(float* const* E, const void* const* grad, void* c
  * inverse in fp64; the first of three passes factors the Gram matrix plus
  * 1e-3 times its largest diagonal entry), which keeps the factor
  * orthonormal to working precision for F of condition number up to about
- * 1e7, where plain CholeskyQR2 in fp32 needs about 4e3 at most.  Inputs for which B Q or W has rank below r are outside the
- * method's contract (the factor is not unique): the output is finite but
- * unspecified.
+ * 1e7, where plain CholeskyQR2 in fp32 needs about 4e3 at most.  The
+ * factor itself is fixed by fp32-accurate data only to about
+ * cond(F) * 2^-24 (relative error about 1e-6 for a well-conditioned F; a
+ * first step from a square random Q can reach cond(B Q) = 1e5).  Inputs for
+ * which B Q or W has rank below r are outside the method's contract (the
+ * factor is not unique): the output is finite but unspecified.
  *   M[i]      device R x C fp32 buffer, updated in place
  *   grad[i]   device R x C of grad_dtype (bf16, fp32 or fp16), read only;
  *             must not overlap M[i]

@@ -125,3 +125,30 @@ def test_rank_clamped_and_modes_checked():
     assert P.shape == (5, 5) and Qn.shape == (9, 5)
     with pytest.raises(ValueError):
         L.lowrank_step(M, G, Q, beta=1.0, mode="svd")
+
+
+@pytest.mark.parametrize("cond", [1e1, 1e3, 1e5])
+def test_qr_factor_sensitivity_to_fp32_accurate_data(cond):
+    """The orthogonal QR factor of F moves by up to about cond(F) * u under a relative
+    perturbation u of F (QR perturbation theory), so data that is only fp32-accurate
+    (u = 2^-24) determines P = orth(B Q) to about cond(B Q) * 2^-24: at cond 1e5 that
+    exceeds 1e-4 even with every later step exact.  This is why the randomized low-rank
+    sweep gates the factor and the update at max(1e-4, cond * 2^-24)."""
+    rng = np.random.default_rng(int(np.log10(cond)))
+    R, C = 300, 12
+    U, _ = np.linalg.qr(rng.standard_normal((R, C)))
+    V, _ = np.linalg.qr(rng.standard_normal((C, C)))
+    F = (U * np.logspace(0, -np.log10(cond), C)) @ V.T
+    assert np.isclose(np.linalg.cond(F), cond, rtol=1e-6)
+    P = L.qr_positive(F)
+    u = 2.0 ** -24
+    worst = 0.0
+    for t in range(20):
+        E = rng.standard_normal(F.shape)
+        E *= u * np.linalg.norm(F) / np.linalg.norm(E)
+        d = np.linalg.norm(L.qr_positive(F + E) - P) / np.linalg.norm(P)
+        worst = max(worst, d)
+    assert worst <= 4 * cond * u            # bounded by the condition number ...
+    assert worst >= 0.01 * cond * u         # ... and that bound is attained in order of magnitude
+    if cond >= 1e5:
+        assert worst > 1e-4
