@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="time passes that read and write 1, 4 and 16 GiB once (runtime copy, elementwise kernel; the rate a streaming pass "
                          "that reads and writes each byte once can reach) and exit")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time the vendor library's dense GEMMs (torch.matmul: hipBLASLt/rocBLAS) in fp16 and "
+                         "bf16 on random and on constant operands at the Llama-3-8B product shapes, each "
+                         "sustained for about two seconds (the power limit's steady state), and exit")
     ap.add_argument("--profile", action="store_true",
                     help="only run warmup + steps (for rocprofv3), no baseline; also runs one plain 1 GiB "
                          "device copy so byte counters can be calibrated against a known size")
@@ -447,6 +451,60 @@ def copy_ceiling(torch, reps=10):
             torch.cuda.empty_cache()
 
 
+def gemm_ceiling(torch, seconds=2.0):
+    """Dense-GEMM throughput of the vendor library on this machine, as a same-box
+    ceiling for the hand-written kernels: torch.matmul (hipBLASLt / rocBLAS,
+    fp32 accumulate) in fp16 and bf16, on N(0,1) operands (full-entropy
+    significands, like the iterates) and on constant operands (few toggling
+    bits), at the products of the Llama-3-8B set: 4096^3 (an m x m chain
+    product), 4096 x 4096 x 14336 (a Gram with a long reduction) and
+    4096 x 14336 x 4096 (a tall apply).  Each shape runs back to back for about
+    `seconds` so that the board reaches its power limit; the rate is the
+    median over ten equal slices of that run, timed with hipEvents on the
+    current stream.  One JSON line per dtype, data and shape."""
+    shapes = [(4096, 4096, 4096), (4096, 14336, 4096), (4096, 4096, 14336)]
+    for dt_name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        for data in ("random", "constant"):
+            for (m, k, n) in shapes:
+                g = torch.Generator(device="cuda").manual_seed(7)
+                if data == "random":
+                    a = torch.randn((m, k), generator=g, device="cuda").to(dt)
+                    b = torch.randn((k, n), generator=g, device="cuda").to(dt)
+                else:
+                    a = torch.full((m, k), 0.5, device="cuda", dtype=dt)
+                    b = torch.full((k, n), 0.25, device="cuda", dtype=dt)
+                c = torch.empty((m, n), device="cuda", dtype=dt)
+                flop = 2.0 * m * n * k
+                for _ in range(3):
+                    torch.matmul(a, b, out=c)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                torch.matmul(a, b, out=c)
+                e1.record()
+                e1.synchronize()
+                per = max(e0.elapsed_time(e1), 1e-3)
+                reps = max(1, int(seconds * 1e3 / per / 10))
+                times = []
+                for _ in range(10):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        torch.matmul(a, b, out=c)
+                    e1.record()
+                    e1.synchronize()
+                    times.append(e0.elapsed_time(e1) / reps)
+                first = times[0]
+                times.sort()
+                ms = times[len(times) // 2]
+                print(json.dumps({"gemm_ceiling": {"dtype": dt_name, "data": data, "m": m, "k": k, "n": n,
+                                                   "ms": ms, "tflops": flop / ms / 1e9,
+                                                   "first_slice_tflops": flop / first / 1e9,
+                                                   "frac_of_dense_peak": flop / ms / 1e9 / 2516.6,
+                                                   "reps_per_slice": reps}}), flush=True)
+                del a, b, c
+                torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -459,6 +517,9 @@ def main():
     import torch
     if args.copy_ceiling:
         copy_ceiling(torch)
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling(torch)
         return
     import orthogonalized_optimizer_step_amd as dion
     from workloads import WORKLOADS

@@ -365,6 +365,28 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   int n_restarts = 0;
   for (int r : xr) n_restarts += (r != 0);
   const bool any_restart = n_restarts > 0;
+  // The one-term chain's symmetric-in-exact-arithmetic products (Q <- P Q,
+  // and the accumulated restart factor S = Q_2 Q_1) are mirrored when the
+  // slopes of the whole schedule multiply to at most six iterations of the
+  // fixed quintic's (every configured workload): the mirrored triangle's
+  // rounding is then amplified by few iterations afterwards.
+  double gain_all = 1.0;
+  for (int k = 0; k < K; ++k) gain_all *= std::max(1.0, std::fabs(prm.a[k]));
+  const bool mirror_q = !P.fp64 && gain_all <= std::pow(3.4445, 6) * (1.0 + 1e-9);
+  // S is mirrored only where every run between restarts is short (at most two
+  // iterations, the default cut): a kept longer run gives Q_1 the gain of
+  // every one of its iterations, and the mirror's wrong-side rounding with it
+  // (a kept five-iteration run, K = 8: 3.3e-2 mirrored, within the gate full)
+  bool all_short = true;
+  {
+    int k0 = 0;
+    for (int k = 1; k <= K; ++k)
+      if (k == K || xr[k - 1]) {
+        if (k - k0 > 2) all_short = false;
+        k0 = k;
+      }
+  }
+  const bool mirror_s = mirror_q && all_short;
   const size_t es = P.fp64 ? 8 : 2;
   const size_t mm_terms = P.fp64 ? 1 : 2;
   const size_t xt_terms = P.fp64 ? 1 : 2;
@@ -392,7 +414,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     // with more restarts its rounding compounds (emulation, K = 7 or 8 with
     // restarts every 2 or every iteration: 1.0-2.4e-2 against 1.8-7.8e-3
     // restarting from the two-term iterate).
-    mp.acc = !P.fp64 && P.xterms0 == 1 && n_restarts == 2 && 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m;
+    // Cost per matrix: S as a full product (2m^3) plus the one-term apply
+    // (2m^2 n) against the two-term apply (4m^2 n), i.e. n >= 1.5m; a
+    // mirrored S costs m^3, which pays for every shape (n >= m).
+    mp.acc = !P.fp64 && P.xterms0 == 1 && n_restarts == 2 &&
+             (mirror_s || 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m);
     P.total_rows += R;
     P.total_sel += mp.k;
   }
@@ -491,6 +517,12 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   const int t_xtq_acc = add_table(P, accs, rect_counts(accs, bm_xtq, true));
   const int t_xtq_nacc = add_table(P, naccs, rect_counts(naccs, bm_xtq, true));
   const int t_full_acc = add_table(P, accs, sub_full(accs, bm_full));
+  auto sub_sym = [&](const std::vector<int>& ms, int bm) {
+    std::vector<int> c;
+    for (int i : ms) { int T = P.mats[i].m_pad / bm; c.push_back(T * (T + 1) / 2); }
+    return c;
+  };
+  const int t_sym_acc = add_table(P, accs, sub_sym(accs, bm_sym));
   const int t_full_nacc = add_table(P, naccs, sub_full(naccs, bm_full));
   // pack and transpose tables over the MFMA matrices (the kernels look the
   // matrices up through the table's list)
@@ -717,9 +749,6 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
   // ... or mirrored, when the schedule's slopes multiply to at most six
   // iterations of the fixed quintic's (every configured workload): the
   // mirrored triangle's rounding is amplified by fewer iterations afterwards
-  double gain_all = 1.0;
-  for (int k = 0; k < K; ++k) gain_all *= std::max(1.0, std::fabs(prm.a[k]));
-  const bool mirror_q = !P.fp64 && gain_all <= std::pow(3.4445, 6) * (1.0 + 1e-9);
   for (int k = 1; k <= K; ++k) {
     const double a = prm.a[k - 1], b = prm.b[k - 1], c = prm.c[k - 1];
     if (q_slot < 0) {
@@ -865,7 +894,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pq.b_slot = qat_slot;
         pq.c_slot = qa_new;
         pq.alpha = sQAn / (sQ * sQA);
-        gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
+        if (mirror_s) {   // Q_1 and Q_2 are mirrored, S is symmetric in exact arithmetic
+          gemm(t_sym_acc, bm_sym, true, 1, 1, EPI_SYM, pq, "acc_product", false, false);
+        } else {
+          gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
+        }
         freel.push_back(qa_slot);
         if (qat_slot != qa_slot) freel.push_back(qat_slot);
         qa_slot = qat_slot = qa_new;
