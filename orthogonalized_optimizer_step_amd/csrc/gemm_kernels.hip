@@ -544,7 +544,7 @@ template <int NA, int NB> struct Prods {
 // stage k carry the reads of half 1, and the copies of stage k+S-1 ride in
 // between, one per two MFMAs over both halves.
 template <int BM, int NA, int NB, int EPI, bool SYM>
-__global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ descs,
+__global__ __launch_bounds__(256, (BM == 128 && NA + NB == 2) ? 3 : 1) void k_gemm16(const MatDesc* __restrict__ descs,
                                                    const int* __restrict__ mats,
                                                    const int* __restrict__ prefix, int nmat,
                                                    const int* __restrict__ ranges, PhaseArgs pa) {
@@ -554,7 +554,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm16(const MatDesc* __restrict__ d
   constexpr int RPW = 128 / BK;              // stage rows per 256-byte bank window
   constexpr int TERM_BYTES = BM * BK * 2;    // one operand term of one stage
   constexpr int STAGE_BYTES = NT * TERM_BYTES;
-  constexpr int S = 4 * STAGE_BYTES <= 160 * 1024 ? 4 : (3 * STAGE_BYTES <= 160 * 1024 ? 3 : 2);
+  constexpr int S = (BM == 128 && NT == 2) ? 3
+                  : (4 * STAGE_BYTES <= 160 * 1024 ? 4 : (3 * STAGE_BYTES <= 160 * 1024 ? 3 : 2));
   constexpr int IPW = TERM_BYTES / 4096;     // 1 KB copies per wave per term per stage
   constexpr int WT = BM / 2;                 // wave tile
   constexpr int F = WT / 32;                 // MFMA blocks per wave dim
