@@ -225,6 +225,7 @@ struct Table {  // a (matrix list, prefix) pair inside the int blob
 struct MatPlan {
   int R, C, k, m, n, m_pad, n_pad, tall;
   bool acc;  // restarts after the first start from X0 with the accumulated factor
+  bool acc_sym = false;  // ... with S = Q_2 Q_1 as a mirrored product
   bool tiny = false;  // runs in the one-workgroup fp64 kernel
   size_t off[N_SLOTS];
   size_t bytes = 0;   // its buffers in the workspace
@@ -416,9 +417,13 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     // restarting from the two-term iterate).
     // Cost per matrix: S as a full product (2m^3) plus the one-term apply
     // (2m^2 n) against the two-term apply (4m^2 n), i.e. n >= 1.5m; a
-    // mirrored S costs m^3, which pays for every shape (n >= m).
+    // mirrored S costs m^3, which pays for every shape (n >= m).  Gram sides
+    // below 128 rows keep the full product: they average out the mirror's
+    // wrong-side rounding least, and its saving there is negligible.
+    mp.acc_sym = mirror_s && mp.m >= 128;
     mp.acc = !P.fp64 && P.xterms0 == 1 && n_restarts == 2 &&
-             (mirror_s || 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m);
+             (mp.acc_sym || 2 * (int64_t)mp.n >= 3 * (int64_t)mp.m);
+    mp.acc_sym = mp.acc_sym && mp.acc;
     P.total_rows += R;
     P.total_sel += mp.k;
   }
@@ -522,7 +527,10 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
     for (int i : ms) { int T = P.mats[i].m_pad / bm; c.push_back(T * (T + 1) / 2); }
     return c;
   };
-  const int t_sym_acc = add_table(P, accs, sub_sym(accs, bm_sym));
+  std::vector<int> accs_sym, accs_full;   // S mirrored, or run in full
+  for (int i : accs) (P.mats[i].acc_sym ? accs_sym : accs_full).push_back(i);
+  const int t_sym_acc = add_table(P, accs_sym, sub_sym(accs_sym, bm_sym));
+  const int t_full_acc_s = add_table(P, accs_full, sub_full(accs_full, bm_full));
   const int t_full_nacc = add_table(P, naccs, sub_full(naccs, bm_full));
   // pack and transpose tables over the MFMA matrices (the kernels look the
   // matrices up through the table's list)
@@ -894,11 +902,9 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         pq.b_slot = qat_slot;
         pq.c_slot = qa_new;
         pq.alpha = sQAn / (sQ * sQA);
-        if (mirror_s) {   // Q_1 and Q_2 are mirrored, S is symmetric in exact arithmetic
-          gemm(t_sym_acc, bm_sym, true, 1, 1, EPI_SYM, pq, "acc_product", false, false);
-        } else {
-          gemm(t_full_acc, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
-        }
+        // where Q_1 and Q_2 are mirrored, S is symmetric in exact arithmetic
+        if (P.tabs[t_sym_acc].nmat) gemm(t_sym_acc, bm_sym, true, 1, 1, EPI_SYM, pq, "acc_product", false, false);
+        if (P.tabs[t_full_acc_s].nmat) gemm(t_full_acc_s, bm_full, false, 1, 1, EPI_RECT, pq, "acc_product", false, false);
         freel.push_back(qa_slot);
         if (qat_slot != qa_slot) freel.push_back(qat_slot);
         qa_slot = qat_slot = qa_new;
