@@ -366,7 +366,7 @@ def bench_lowrank(args, torch, dion):
         return
     ms_plain = time_plain(torch, call, args.steps)
     phases, kernels = {}, {}
-    for name, kern, ms, u, r, b in recs:
+    for name, kern, ms, u, r, b, a in recs:
         for key, tab in ((name, phases), (kern, kernels)):
             e = tab.setdefault(key, {"ms": 0.0, "launches": 0, "useful": 0.0, "bytes": 0.0})
             e["ms"] += ms
@@ -585,7 +585,7 @@ def main():
     useful = orth.useful_flops()
     # per-phase aggregation
     phases = {}
-    for name, kern, ms, u, r, b in recs:
+    for name, kern, ms, u, r, b, a in recs:
         ph = phases.setdefault(name, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0,
                                       "kernels": set()})
         ph["kernels"].add(kern)
@@ -597,20 +597,25 @@ def main():
     # the roofline entry is for the kernel instance with the most GPU time:
     # an MFMA kernel against the matrix peak, a streaming pass against HBM
     kernels = {}
-    for name, kern, ms, u, r, b in recs:
-        k = kernels.setdefault(kern, {"ms": 0.0, "launches": 0, "useful": 0.0, "mfma": 0.0, "bytes": 0.0,
-                                      "phases": set()})
+    for name, kern, ms, u, r, b, a in recs:
+        k = kernels.setdefault(kern, {"ms": 0.0, "launches": 0, "useful": 0.0, "alg": 0.0, "mfma": 0.0,
+                                      "bytes": 0.0, "phases": set()})
         k["phases"].add(name)
         k["ms"] += ms
         k["launches"] += 1
         k["useful"] += u
+        k["alg"] += a
         k["mfma"] += r
         k["bytes"] += b
     dom_kernel = max(kernels, key=lambda k: kernels[k]["ms"])
     d = kernels[dom_kernel]
     avg_ms = d["ms"] / d["launches"]
     compute = d["mfma"] > 0
-    achieved = ((d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12 if compute else
+    # an MFMA kernel is priced by its algorithmic FLOPs: the per-unit formulas
+    # of the useful count over every product its launches run (the useful count
+    # leaves out the accumulated restart factor and the restarts a cut
+    # schedule adds, which this kernel instance also runs)
+    achieved = ((d["alg"] / d["launches"]) / (avg_ms * 1e-3) / 1e12 if compute else
                 (d["bytes"] / d["launches"]) / (avg_ms * 1e-3) / 1e9)
     # algorithmic HBM bytes per launch, from the plan: each operand term read
     # once and the result written once
@@ -654,7 +659,9 @@ def main():
                       "phase": "+".join(sorted(d["phases"])), "achieved": achieved,
                       "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                       "traffic": traffic, "launch_ms": avg_ms,
+                      "algorithmic_flops_per_launch": d["alg"] / d["launches"],
                       "useful_flops_per_launch": d["useful"] / d["launches"],
+                      "useful_tflops": d["useful"] / d["launches"] / (avg_ms * 1e-3) / 1e12,
                       "mfma_tflops": d["mfma"] / d["launches"] / (avg_ms * 1e-3) / 1e12,
                       "algorithmic_bytes_per_launch": alg_bytes} if compute else
                      {"bound": "hbm", "kernel": dom_kernel, "phase": "+".join(sorted(d["phases"])),

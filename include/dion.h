@@ -404,6 +404,15 @@ int dion_profile_enable(int enable);
 int dion_profile_count(void);
 int dion_profile_get(int index, const char** name, const char** kernel, float* ms,
                      double* useful_flops, double* mfma_flops, double* bytes);
+/* Algorithmic FLOPs of record `index`: the per-unit formulas of its useful
+ * count (Gram n m (m+1), m x m chain product m^2 (m+1), apply 2 m^2 n) over
+ * every product the launch runs, including those outside the caller's
+ * schedule (the accumulated restart factor S = Q_2 Q_1 of a restart from X0,
+ * and the applies and Grams of the restarts the planner adds to cut long
+ * runs), which the useful count leaves out.  Diagonal tiles, padding and
+ * split terms are not counted.  Does not wait for the device.  NULL output
+ * allowed; DION_E_INVAL for an index out of range. */
+int dion_profile_get_algorithmic(int index, double* algorithmic_flops);
 
 /* Static message for a status code. */
 const char* dion_strerror(int status);

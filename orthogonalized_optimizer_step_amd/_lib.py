@@ -44,6 +44,7 @@ EXPORTS = (
     "dion_profile_get", "dion_phase_workspace_size", "dion_rowkeys_topk_batched", "dion_syrk_batched",
     "dion_sympoly_batched", "dion_apply_batched", "dion_rowsubset_step_update", "dion_restart_points",
     "dion_lowrank_workspace_size", "dion_lowrank_step", "dion_orth_batched_noalloc", "dion_workspace_size_capped",
+    "dion_profile_get_algorithmic",
 )
 
 
@@ -103,6 +104,8 @@ def _load():
     lib.dion_profile_get.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_char_p),
                                      ctypes.POINTER(ctypes.c_float), dp, dp, dp]
     lib.dion_profile_get.restype = ctypes.c_int
+    lib.dion_profile_get_algorithmic.argtypes = [ctypes.c_int, dp]
+    lib.dion_profile_get_algorithmic.restype = ctypes.c_int
     lib.dion_version.argtypes = []
     lib.dion_version.restype = ctypes.c_int
     fp = ctypes.POINTER(ctypes.c_float)

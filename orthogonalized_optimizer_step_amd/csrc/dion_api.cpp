@@ -212,9 +212,12 @@ struct Step {
   int grid = 0;          // ST_GEMM: blocks launched
   float scale = 1.f;     // ST_UNPACK: value scale (times nu^2 when use_nu2)
   bool use_nu2 = false;
-  // accounting for profiles: name, useful FLOPs, executed MFMA FLOPs, algorithmic bytes
+  // accounting for profiles: name, useful FLOPs (the caller's schedule, by the
+  // per-unit formulas), algorithmic FLOPs (the same formulas over every product
+  // the plan runs: also the accumulated restart factor and the restarts a cut
+  // schedule adds), executed MFMA FLOPs, algorithmic bytes
   const char* name = "";
-  double useful = 0, raw = 0, bytes = 0;
+  double useful = 0, alg = 0, raw = 0, bytes = 0;
 };
 
 struct Table {  // a (matrix list, prefix) pair inside the int blob
@@ -629,7 +632,7 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
         }
       st.bytes += 2.0 * mp.k * mp.C * in_es;
     }
-    st.raw = st.useful;
+    st.raw = st.alg = st.useful;
     P.steps.push_back(st);
   }
   P.carry = step_mode && prm.carry;
@@ -677,10 +680,11 @@ int build_plan(const dion_shape* shapes, int batch, int dtype, const Params& prm
       g.raw += (double)tiles * bm * bm * K * 2.0 * nprod;
       // an m x m chain product counts as the symmetric half however it is run
       const bool mxm = !pa.k_is_n && !pa.a_rows_is_n && !pa.b_rows_is_n && epi != EPI_OUT;
-      if (!counts_useful) {}                                     // extra work of the execution
-      else if (sym && pa.k_is_n) g.useful += n * m * (m + 1);   // Gram
-      else if (mxm) g.useful += m * m * (m + 1);                 // m x m chain
-      else g.useful += 2.0 * m * m * n;                          // apply / final
+      const double f = (sym && pa.k_is_n) ? n * m * (m + 1)      // Gram
+                       : mxm ? m * m * (m + 1)                    // m x m chain
+                       : 2.0 * m * m * n;                         // apply / final
+      g.alg += f;
+      if (counts_useful) g.useful += f;                           // else extra work of the execution
       // algorithmic HBM bytes on the padded layout: every operand term read
       // once, the result written once (both triangles of a symmetric one)
       const double ar = pa.a_rows_is_n ? mp.n_pad : mp.m_pad, br = pa.b_rows_is_n ? mp.n_pad : mp.m_pad;
@@ -1298,7 +1302,7 @@ struct ProfRec {
   const char* name;
   const char* kernel;
   hipEvent_t a, b;
-  double useful, raw, bytes;
+  double useful, raw, bytes, alg;
 };
 
 // Name of the kernel instance a step launches, as the profiler prints it
@@ -1441,7 +1445,7 @@ int run(const Plan& P, const void* const* M, void* const* out, const void* const
   const int fmt = P.fmt;
 
   for (const Step& st : P.steps) {
-    ProfRec rec{st.name, nullptr, nullptr, nullptr, st.useful, st.raw, st.bytes};
+    ProfRec rec{st.name, nullptr, nullptr, nullptr, st.useful, st.raw, st.bytes, st.alg};
     if (g_prof.on) {
       rec.a = g_prof.get();
       rec.b = g_prof.get();
@@ -1798,11 +1802,11 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
   auto arrays = [&](const LrGroup& g, int k) { return (float* const*)(ws + g.ptr_off) + k * g.mats.size(); };
   const int nmat = batch;
 
-  // each launch (or batched rocBLAS call) as one profiling record, with its
-  // useful FLOPs (2 m n k per product) and algorithmic bytes
+  // each launch as one profiling record, with its useful FLOPs (2 m n k per
+  // product; also its algorithmic FLOPs) and algorithmic bytes
   auto phase = [&](const char* name, const char* kernel, double useful, double bytes,
                    const std::function<int()>& fn) -> int {
-    ProfRec rec{name, kernel, nullptr, nullptr, useful, useful, bytes};
+    ProfRec rec{name, kernel, nullptr, nullptr, useful, useful, bytes, useful};
     if (g_prof.on) {
       rec.a = g_prof.get();
       rec.b = g_prof.get();
@@ -2321,6 +2325,12 @@ int dion_profile_get(int i, const char** name, const char** kernel, float* ms, d
   if (useful_flops) *useful_flops = r.useful;
   if (mfma_flops) *mfma_flops = r.raw;
   if (bytes) *bytes = r.bytes;
+  return DION_OK;
+}
+
+int dion_profile_get_algorithmic(int i, double* algorithmic_flops) {
+  if (i < 0 || i >= (int)g_prof.recs.size()) return fail(DION_E_INVAL, "profile record out of range");
+  if (algorithmic_flops) *algorithmic_flops = g_prof.recs[i].alg;
   return DION_OK;
 }
 

@@ -46,6 +46,18 @@ def test_no_internal_symbol_left_undefined():
     assert not missing, missing
 
 
+def test_profile_get_algorithmic_index_checked():
+    """The algorithmic-FLOP query rejects an index outside the records."""
+    lib = _lib.lib
+    lib.dion_profile_enable(1)
+    lib.dion_profile_enable(0)
+    v = ctypes.c_double(-1.0)
+    assert lib.dion_profile_count() == 0
+    assert lib.dion_profile_get_algorithmic(0, ctypes.byref(v)) == -1
+    assert lib.dion_profile_get_algorithmic(-1, None) == -1
+    assert v.value == -1.0
+
+
 def test_version():
     assert _lib.lib.dion_version() == 100
 

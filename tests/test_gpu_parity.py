@@ -121,6 +121,31 @@ def test_long_runs_cut_or_kept(dion, sched):
     print("long runs", sched, f"cut {worst[False]:.2e} kept {worst[True]:.2e}", flush=True)
 
 
+def test_profile_algorithmic_flops(dion):
+    """Per-launch FLOP accounting of a two-restart schedule (K = 5, restarts after 2
+    and 4), against counts written out from the shapes: useful FLOPs over the call
+    equal dion_useful_flops; every launch's algorithmic FLOPs equal its useful ones
+    except the accumulated restart factor's, which counts m^2 (m + 1) per matrix
+    restarting from X0 in the algorithmic figure and nothing in the useful one."""
+    shapes = [(256, 640), (640, 256), (384, 384), (1024, 512)]
+    Ms = [round_bf16(lowrank_np((33, i), r, c, 16, 0.1)) for i, (r, c) in enumerate(shapes)]
+    dev = [to_dev_bf16(M) for M in Ms]
+    dion.profile_enable(True)
+    dion.orth_batched(dev, restart_every=2)
+    recs = dion.profile_records()
+    dion.profile_enable(False)
+    useful = sum(r[3] for r in recs)
+    assert useful == pytest.approx(dion.useful_flops(shapes, restart_every=2), rel=1e-12)
+    acc = [r for r in recs if r[0] == "acc_product"]
+    assert len(acc) == 1, [r[0] for r in recs]
+    assert acc[0][3] == 0.0
+    # every matrix here has a Gram side of at least 128 and restarts from X0
+    assert acc[0][6] == pytest.approx(sum(float(min(r, c)) ** 2 * (min(r, c) + 1) for r, c in shapes), rel=1e-12)
+    for r in recs:
+        if r[0] != "acc_product":
+            assert r[6] == pytest.approx(r[3], rel=1e-12), r
+
+
 def test_keep_schedule_no_effect_on_short_runs(dion):
     """Runs of at most two iterations are never cut: the same plan, bit-identical outputs."""
     dev = [to_dev_bf16(M) for M in small_batch(16)]
