@@ -379,9 +379,9 @@ def bench_lowrank(args, torch, dion):
     useful_rate = (d["useful"] / d["launches"]) / (avg_ms * 1e-3) / 1e12
     # the products are fp32 GEMMs computed on 16-bit matrix cores: two fp16
     # terms per operand (three MFMA products) or, for the instances whose
-    # template flag is false, three bf16 terms (six): priced as the MFMA work
-    # they execute
-    terms = 6 if dom.endswith("false>") else 3
+    # template flag is false, three bf16 terms (six); the bf16 update reads
+    # one fp16 term (one product): priced as the MFMA work they execute
+    terms = 6 if dom.endswith("false>") else (1 if dom.endswith("dma<1>") else 3)
     achieved = useful_rate * terms
     useful = sum(v["useful"] for v in phases.values()) / args.steps
     params = sum(r * c for r, c in shapes)

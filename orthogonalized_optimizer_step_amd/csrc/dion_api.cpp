@@ -1872,7 +1872,8 @@ int run_lr(const LrPlan& P, float* const* M, const void* const* G, float* const*
                          int out_fmt, bool withg, double bytes_each) -> int {
     const int ldp = (g.r + 31) / 32 * 32;
     const double cnt = (double)g.mats.size();
-    return phase(name, "dion::k_lr_gemm_dma", 2.0 * g.R * g.C * g.r * cnt, bytes_each * cnt, [&]() {
+    return phase(name, out_fmt == 0 ? "dion::k_lr_gemm_dma<1>" : "dion::k_lr_gemm_dma<2>", 2.0 * g.R * g.C * g.r * cnt,
+                 bytes_each * cnt, [&]() {
       launch_lr_gemm_split(g.R, g.C, g.r, ldp, pad128(g.R), pad128(g.C), alpha, (const uint16_t* const*)arrays(g, LP_XS),
                            (const uint16_t* const*)arrays(g, Z), beta_, (void* const*)arrays(g, Cm),
                            (unsigned* const*)arrays(g, LP_AM), LS_F2, sz, -1, out_fmt,

@@ -585,9 +585,14 @@ __device__ __forceinline__ const void* lg_sgpr(const void* p) {
 // runs beside it: four or three stages at one block per CU measured slower
 // (31.5 against 24.3 ms for the buffer update) than the register-staged
 // kernel, two stages at two blocks faster (22.1 ms).
-constexpr int LD_STAGES = 2;
-constexpr int LD_STAGE = 4 * LG_TERM * 2;     // bytes: A hi, A lo, B hi, B lo (8 KB each)
-constexpr int LD_COPIES = LD_STAGE / 1024 / 4;   // 1 KB copies per wave per stage (8)
+// With one term per operand (hi only: the update written in bf16, whose
+// rounding is eight times the one-term product's) a stage is half as large,
+// and four of them fill the same 64 KB.
+template <int NT> struct LdCfg {
+  static constexpr int STAGES = NT == 2 ? 2 : 4;
+  static constexpr int STAGE = 2 * NT * LG_TERM * 2;   // bytes: A hi (, A lo), B hi (, B lo): 8 KB each
+  static constexpr int COPIES = STAGE / 1024 / 4;      // 1 KB copies per wave per stage (8 or 4)
+};
 
 // C (M x N, row-major, ld N) = alpha A B^T (+ beta C) for product z =
 // blockIdx.z, with A (M x K) and B (N x K) split ahead: fp16 hi rows at
@@ -599,12 +604,14 @@ constexpr int LD_COPIES = LD_STAGE / 1024 / 4;   // 1 KB copies per wave per sta
 // wave copies eight 1 KB pieces of it: piece q = 4 i + wave (i < 8) holds
 // term q / 8 and rows 16 (q % 8) .. +15, lane l row 16 (q % 8) + l / 4 and
 // the chunk whose swizzled position is l % 4.
+template <int NT>
 __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int ldp, int rows_a, int rows_b,
                                                         float alpha, const uint16_t* const* __restrict__ As,
                                                         const uint16_t* const* __restrict__ Bs, float beta,
                                                         void* const* __restrict__ Cs, unsigned* const* __restrict__ amax,
                                                         int sa, int sb, int sc, int out_fmt,
                                                         const uint16_t* const* __restrict__ Gs, int gfmt) {
+  constexpr int LD_STAGES = LdCfg<NT>::STAGES, LD_STAGE = LdCfg<NT>::STAGE, LD_COPIES = LdCfg<NT>::COPIES;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[LD_STAGES * LD_STAGE / 2];
   const int z = blockIdx.z;
   unsigned* slots = amax[z];
@@ -621,19 +628,19 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
   uint32_t voff[LD_COPIES];
 #pragma unroll
   for (int i = 0; i < LD_COPIES; ++i) {
-    const int q = 4 * i + wave, term = q / 8;
+    const int q = 4 * i + wave, term = q / 8;   // term array: operand term / NT, its term % NT
     const int row = 16 * (q % 8) + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
-    const int r0 = term < 2 ? m0 : n0;
-    const size_t tstride = (size_t)(term < 2 ? rows_a : rows_b) * ldp;
-    voff[i] = (uint32_t)((((size_t)(term & 1) * tstride) + (size_t)(r0 + row) * ldp + 8 * c) * 2);
+    const int r0 = term < NT ? m0 : n0;
+    const size_t tstride = (size_t)(term < NT ? rows_a : rows_b) * ldp;
+    voff[i] = (uint32_t)((((size_t)(term % NT) * tstride) + (size_t)(r0 + row) * ldp + 8 * c) * 2);
   }
   auto issue = [&](int kt) {   // the copies of stage kt into buffer kt % LD_STAGES
     const uint32_t st = lds0 + (uint32_t)((kt % LD_STAGES) * LD_STAGE);
 #pragma unroll
     for (int i = 0; i < LD_COPIES; ++i) {
       const int q = 4 * i + wave;
-      const char* b = (q / 8 < 2 ? baseA : baseB) + (size_t)kt * LG_BK * 2;
+      const char* b = (q / 8 < NT ? baseA : baseB) + (size_t)kt * LG_BK * 2;
       lg_dma16(voff[i], lg_sgpr(b), (uint32_t)__builtin_amdgcn_readfirstlane(st + q * 1024));
     }
   };
@@ -658,7 +665,7 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed once at most the later stages already issued are outstanding
     const int later = min(nk, kt + LD_STAGES - 1) - kt - 1;
-    if (later >= 2) lg_wait_vmcnt<2 * LD_COPIES>();
+    if (later >= 2) lg_wait_vmcnt<2 * LD_COPIES>();   // at most LD_STAGES - 2 = 2
     else if (later == 1) lg_wait_vmcnt<LD_COPIES>();
     else lg_wait_vmcnt<0>();
     lg_barrier();   // every wave's copies of stage kt have landed, and every wave is done with stage kt - 1
@@ -667,25 +674,27 @@ __global__ __launch_bounds__(256, 2) void k_lr_gemm_dma(int M, int N, int K, int
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int chunk = kk * 2 + (lane >> 5);
-      halfx8 fa[2][2], fb[2][2];
+      halfx8 fa[NT][2], fb[NT][2];
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         const int ra = wm * 64 + f * 32 + (lane & 31), rb = wn * 64 + f * 32 + (lane & 31);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NT; ++u) {
           fa[u][f] = *(const halfx8*)(sbuf + u * LG_TERM + lg_off(ra, chunk));
-          fb[u][f] = *(const halfx8*)(sbuf + (2 + u) * LG_TERM + lg_off(rb, chunk));
+          fb[u][f] = *(const halfx8*)(sbuf + (NT + u) * LG_TERM + lg_off(rb, chunk));
         }
       }
-      // hl, lh, then hh
+      // hl, lh (two terms), then hh
+      if constexpr (NT == 2) {
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[1][b], fa[0][a], acc[a][b], 0, 0, 0);
+          for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[1][b], fa[0][a], acc[a][b], 0, 0, 0);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[0][b], fa[1][a], acc[a][b], 0, 0, 0);
+          for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[0][b], fa[1][a], acc[a][b], 0, 0, 0);
+      }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -701,8 +710,12 @@ void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, 
                           int sc, int out_fmt, const uint16_t* const* G, int gfmt, int count, hipStream_t s) {
   (void)k;
   const dim3 grid((n + LG_TILE - 1) / LG_TILE, (m + LG_TILE - 1) / LG_TILE, count);
-  hipLaunchKernelGGL(k_lr_gemm_dma, grid, dim3(256), 0, s, m, n, ldp, ldp, rows_a, rows_b, alpha, A, B, beta, C, amax,
-                     sa, sb, sc, out_fmt, G, gfmt);
+  if (out_fmt == 0)   // a bf16 result: the hi terms alone
+    hipLaunchKernelGGL(k_lr_gemm_dma<1>, grid, dim3(256), 0, s, m, n, ldp, ldp, rows_a, rows_b, alpha, A, B, beta, C,
+                       amax, sa, sb, sc, out_fmt, G, gfmt);
+  else
+    hipLaunchKernelGGL(k_lr_gemm_dma<2>, grid, dim3(256), 0, s, m, n, ldp, ldp, rows_a, rows_b, alpha, A, B, beta, C,
+                       amax, sa, sb, sc, out_fmt, G, gfmt);
 }
 
 void launch_lr_gram(int rows, int r, const float* const* F, float* const* S, unsigned* const* amax, int sf, int count,

@@ -84,7 +84,9 @@ void launch_lr_gemm(bool ta, bool tb, bool f16, int m, int n, int k, float alpha
 // launch_lr_split16: A as m rows (padded to rows_a) and B as n rows (padded
 // to rows_b) of k values (fp16 hi and lo, row length ldp); out_fmt 1 fp32
 // (with beta), 0 bf16 or 2 fp16 (beta must be 0).  With G (16-bit, laid out
-// as C), beta C is beta fl32(C + G).
+// as C), beta C is beta fl32(C + G).  A bf16 result reads the hi terms only
+// (one product, k_lr_gemm_dma<1>): its rounding, 2^-9 relative, is eight
+// times the one-term product's; the others read both terms (three products).
 void launch_lr_gemm_split(int m, int n, int k, int ldp, int rows_a, int rows_b, float alpha, const uint16_t* const* A,
                           const uint16_t* const* B, float beta, void* const* C, unsigned* const* amax, int sa, int sb,
                           int sc, int out_fmt, const uint16_t* const* G, int gfmt, int count, hipStream_t s);
