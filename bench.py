@@ -123,6 +123,10 @@ def cpu_baseline(wl, Ms, seconds, torch):
 # the kernels and the plan that decides what each launch of them covers
 KERNEL_SOURCES = ("orthogonalized_optimizer_step_amd/csrc/gemm_kernels.hip",
                   "orthogonalized_optimizer_step_amd/csrc/stream_kernels.hip",
+                  "orthogonalized_optimizer_step_amd/csrc/tiny_kernels.hip",
+                  "orthogonalized_optimizer_step_amd/csrc/lowrank_gemm.hip",
+                  "orthogonalized_optimizer_step_amd/csrc/lowrank_kernels.hip",
+                  "orthogonalized_optimizer_step_amd/csrc/lowrank_internal.h",
                   "orthogonalized_optimizer_step_amd/csrc/dion_api.cpp",
                   "orthogonalized_optimizer_step_amd/csrc/dion_internal.h")
 # counter summaries per workload (the TRAFFIC lines of a file hold only for the workload it was taken on)
