@@ -456,8 +456,8 @@ def copy_ceiling(torch, reps=10):
 
 
 def gemm_ceiling(torch, seconds=2.0):
-    """Dense-GEMM throughput of the vendor library on this machine, as a same-box
-    ceiling for the hand-written kernels: torch.matmul (hipBLASLt / rocBLAS,
+    """Dense-GEMM throughput of the vendor library on the GPU it runs on, as a
+    ceiling for the hand-written kernels measured on the same device: torch.matmul (hipBLASLt / rocBLAS,
     fp32 accumulate) in fp16 and bf16, on N(0,1) operands (full-entropy
     significands, like the iterates) and on constant operands (few toggling
     bits), at the products of the Llama-3-8B set: 4096^3 (an m x m chain
