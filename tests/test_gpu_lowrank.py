@@ -125,6 +125,33 @@ def test_lowrank_bf16_output_and_partial_isometry(dion, mode):
             assert np.abs(sv[:24] - 1.0).max() < 2e-2 and sv[24] < 2e-2
 
 
+@pytest.mark.parametrize("mode", ["qr", "colnorm"])
+@pytest.mark.parametrize("beta", [1.0, 0.1])
+def test_lowrank_bf16_update_from_hi_terms(dion, mode, beta):
+    """A bf16 update is computed from the fp16 hi terms of P and Q' alone (one
+    product).  Against the oracle its error may exceed the bf16 rounding of the
+    exact update by at most a quarter (the one-term product's error is about a
+    tenth of it), on ragged shapes and at ranks 16 and 64; the buffer and the
+    right factor are those of the fp32-output call, bit for bit."""
+    shapes = SHAPES + [(512, 384), (384, 512), (1024, 256)]
+    for rank, seed in ((16, 21), (64, 22)):
+        Ms, Gs, Qs = make(shapes, rank, seed)
+        dM, dQ, outs = run(dion, Ms, Gs, Qs, beta, mode, out_dtype=torch.bfloat16)
+        dM32, dQ32, _ = run(dion, Ms, Gs, Qs, beta, mode, out_dtype=torch.float32)
+        worst = 0.0
+        for i, s in enumerate(shapes):
+            assert torch.equal(dM[i].view(torch.int32), dM32[i].view(torch.int32)), s
+            assert torch.equal(dQ[i].view(torch.int32), dQ32[i].view(torch.int32)), s
+            _, _, _, D_ref = L.lowrank_step(Ms[i], Gs[i].float().numpy(), Qs[i], beta, mode)
+            rounded = torch.from_numpy(D_ref.astype(np.float32)).to(torch.bfloat16).float().numpy()
+            e_round = rel_frobenius(rounded.astype(np.float64), D_ref)
+            e = rel_frobenius(as64(outs[i]), D_ref)
+            worst = max(worst, e / max(e_round, 1e-300))
+            assert e <= 1.25 * e_round + 1e-6, (s, rank, e, e_round)
+        print(f"lowrank bf16 update {mode} beta {beta} rank {rank}: error / bf16 rounding at most {worst:.3f}",
+              flush=True)
+
+
 def test_lowrank_exact_recovery(dion):
     """With Q = the top-r right singular vectors of B, the update is U_r V_r^T."""
     shapes = [(120, 80), (80, 120)]
@@ -163,16 +190,24 @@ def test_lowrank_three_steps(dion):
 
 
 def test_lowrank_full_size(dion):
-    """Llama-3-8B MLP shapes at rank 256, fp32 update: every element against the oracle."""
+    """Llama-3-8B MLP shapes at rank 256, fp32 update: every element against the
+    oracle; and the bf16 update from the hi terms (the benchmarked form) within a
+    quarter above the bf16 rounding of the exact update."""
     shapes = [(4096, 14336), (14336, 4096)]
     Ms, Gs, Qs = make(shapes, 256, 17)
     dM, dQ, outs = run(dion, Ms, Gs, Qs, 1.0, "qr")
+    _, _, outs16 = run(dion, Ms, Gs, Qs, 1.0, "qr", out_dtype=torch.bfloat16)
     for i, s in enumerate(shapes):
         M_ref, Q_ref, _, D_ref = L.lowrank_step(Ms[i], Gs[i].float().numpy(), Qs[i], 1.0, "qr")
         e = (buf_err(as64(dM[i]), M_ref, Ms[i], Gs[i].float().numpy()), rel_frobenius(as64(dQ[i]), Q_ref),
              rel_frobenius(as64(outs[i]), D_ref))
-        print("lowrank full", s, " ".join(f"{x:.2e}" for x in e), flush=True)
+        rounded = torch.from_numpy(D_ref.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        e_round = rel_frobenius(rounded.astype(np.float64), D_ref)
+        e16 = rel_frobenius(as64(outs16[i]), D_ref)
+        print("lowrank full", s, " ".join(f"{x:.2e}" for x in e), f"bf16 {e16:.3e} (rounding {e_round:.3e})",
+              flush=True)
         assert max(e) <= TOL, (s, e)
+        assert e16 <= 1.25 * e_round + 1e-6, (s, e16, e_round)
 
 
 def test_lowrank_zero_input_is_finite(dion):
